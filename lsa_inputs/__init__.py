@@ -1,0 +1,288 @@
+"""Seeded synthetic inputs for the LSA decode hot path.
+
+This module only draws numbers and lays them out in memory.  It holds none of
+the method's arithmetic: no score, no selection, no LRU, no attention.  Both
+the CPU oracle (``oracle/``) and the HIP library (``learned_sparse_kv_amd``)
+are fed from here, so that the two sides see bit-identical inputs.
+
+Values are drawn on the 1/8 grid (multiples of 2**-3) so that every dot
+product and weighted head sum the scorer forms is exactly representable in
+fp32 whatever the summation order.  The shapes follow the pages'
+configuration: a 128-token sliding window plus compressed entries of width
+512 (FlashMemory 1M context doc, "Memory Layout" in the technical-details
+section), compressed capacity ceil(ctx / ratio) for ratios 4 and 128 (same
+doc, pinned-memory formula), three memory indexers combined by max or mean
+(same doc, FlashMemory configuration), and KVSwap's grouped low-rank keys
+(KVSwap article, sections 2.2 and 2.3).
+"""
+from __future__ import annotations
+
+import dataclasses
+import zlib
+from typing import Optional, Tuple
+
+import numpy as np
+
+GRID = 0.125  # 1/8
+
+
+# --------------------------------------------------------------------------
+# random streams
+# --------------------------------------------------------------------------
+def rng_for(base_seed: int, tag: str, *idx: int) -> np.random.Generator:
+    """A PCG64 stream keyed by (base seed, tensor tag, indices...)."""
+    key = [int(base_seed) & 0xFFFFFFFF, zlib.crc32(tag.encode())]
+    key += [int(i) & 0xFFFFFFFF for i in idx]
+    return np.random.default_rng(np.random.SeedSequence(key))
+
+
+def _fill_chunks(out: np.ndarray, draw, chunk: int = 1 << 23) -> np.ndarray:
+    flat = out.reshape(-1)
+    for s in range(0, flat.size, chunk):
+        e = min(flat.size, s + chunk)
+        flat[s:e] = draw(e - s)
+    return out
+
+
+def grid_uniform(rng: np.random.Generator, shape, lo: float = -1.0, hi: float = 1.0,
+                 step: float = GRID, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Uniform over the points lo, lo+step, ..., hi (inclusive), float32."""
+    n_lo = int(round(lo / step))
+    n_hi = int(round(hi / step))
+    if out is None:
+        out = np.empty(shape, dtype=np.float32)
+    st = np.float32(step)
+
+    def draw(n):
+        return rng.integers(n_lo, n_hi + 1, size=n, dtype=np.int16).astype(np.float32) * st
+
+    return _fill_chunks(out, draw)
+
+
+def grid_gauss(rng: np.random.Generator, shape, sigma: float, lo: float = -1.0,
+               hi: float = 1.0, step: float = GRID) -> np.ndarray:
+    """Gaussian N(0, sigma^2) rounded to the grid and clamped to [lo, hi]."""
+    z = rng.standard_normal(size=shape) * sigma
+    v = np.clip(np.round(z / step) * step, lo, hi)
+    return v.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# dtype encodings (exact for grid values; they refuse anything else)
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    if np.any(u & 0xFFFF):
+        raise ValueError("value not exactly representable in bfloat16")
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    h = np.asarray(x, dtype=np.float32).astype(np.float16)
+    if not np.array_equal(h.astype(np.float32), np.asarray(x, dtype=np.float32)):
+        raise ValueError("value not exactly representable in float16")
+    return h.view(np.uint16)
+
+
+DTYPE_CODES = {"f32": 0, "bf16": 1, "f16": 2}
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Store float32 grid values in the named storage dtype (f32 / bf16 / f16 bits)."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return f32_to_f16_bits(x)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+def compressed_cap(ctx: int, ratio: int) -> int:
+    return (ctx + ratio - 1) // ratio
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One decode-step workload: a shared ratio-``src_ratio`` source layer that
+    is scored, and ``layer_ratios`` sparse layers that stage and attend."""
+    name: str
+    base_seed: int
+    ctx: int
+    batch: int
+    src_ratio: int
+    layer_ratios: Tuple[int, ...]
+    gpu_chunks: int
+    cold: str            # "hbm" or "host"
+    dk: int
+    n_idx: int
+    heads: int
+    key_dtype: str
+    kv_dtype: str
+    mode: str            # "topk" or "threshold"
+    k: int               # top-k, or the cap in threshold mode
+    ensemble: str = "max"
+    tau: Optional[float] = None
+    steps: int = 16
+    window: int = 128
+    kv_dim: int = 512
+    hq: int = 16
+    dist: str = "uniform"     # "uniform" or "planted"
+    drift: Optional[float] = None  # fraction of indexer-query coordinates redrawn per step
+
+    @property
+    def n_src(self) -> int:
+        return compressed_cap(self.ctx, self.src_ratio)
+
+    def layer_cap(self, layer: int) -> int:
+        return compressed_cap(self.ctx, self.layer_ratios[layer])
+
+    @property
+    def n_layers(self) -> int:
+        return len(self.layer_ratios)
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.kv_dim))
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# Threshold for the 256K workload: sigmoid of the midpoint between the 1311th and
+# 1312th distinct largest step-0 scores pooled over the batch (0.5% of 4 x 65536),
+# and the per-step redraw fraction of the 1M workload, chosen so that consecutive
+# top-512 sets overlap by about 80%.  Both written by oracle/calibrate_workloads.py.
+THRESH_256K_TAU = None
+SWAP_1M_DRIFT = None
+
+WORKLOADS = {
+    # tiny single-layer step: 8K ctx, ratio 4, 1 indexer x 4 heads x 64, top-64
+    "tiny_8k": Workload(
+        name="tiny_8k", base_seed=1001, ctx=8192, batch=1, src_ratio=4, layer_ratios=(4,),
+        gpu_chunks=2048, cold="hbm", dk=64, n_idx=1, heads=4, key_dtype="f32", kv_dtype="f32",
+        mode="topk", k=64, steps=16),
+    # 8K ctx, 3-indexer ensemble, ratio-4 + ratio-128 layers, 512-slot LRU pool
+    "ens_8k": Workload(
+        name="ens_8k", base_seed=1002, ctx=8192, batch=1, src_ratio=4, layer_ratios=(4, 128),
+        gpu_chunks=512, cold="hbm", dk=128, n_idx=3, heads=8, key_dtype="f32", kv_dtype="f32",
+        mode="topk", k=512, ensemble="max", steps=64),
+    # 256K ctx, threshold mode, bf16, batch 4, planted high-score clusters, fully resident
+    "thresh_256k": Workload(
+        name="thresh_256k", base_seed=1003, ctx=262144, batch=4, src_ratio=4, layer_ratios=(4, 128),
+        gpu_chunks=65536, cold="hbm", dk=128, n_idx=3, heads=8, key_dtype="bf16", kv_dtype="bf16",
+        mode="threshold", k=512, ensemble="max", tau=THRESH_256K_TAU, steps=64, dist="planted"),
+    # 1M ctx, 4 x (ratio-4 + ratio-128) layers, pinned-host cold pools, 1024-slot LRU
+    "swap_1m": Workload(
+        name="swap_1m", base_seed=1004, ctx=1048576, batch=1, src_ratio=4,
+        layer_ratios=(4, 128, 4, 128, 4, 128, 4, 128),
+        gpu_chunks=1024, cold="host", dk=128, n_idx=3, heads=8, key_dtype="f32", kv_dtype="f32",
+        mode="topk", k=512, ensemble="max", steps=256, drift=SWAP_1M_DRIFT),
+}
+
+
+# --------------------------------------------------------------------------
+# per-tensor generators
+# --------------------------------------------------------------------------
+PLANT_RUN = 32        # planted clusters are runs of 32 consecutive entries
+PLANT_FRACTION = 0.02  # ... covering 2% of the source entries
+
+
+def _topic(wl: Workload, b: int) -> np.ndarray:
+    return grid_uniform(rng_for(wl.base_seed, "topic", b), (wl.dk,))
+
+
+def planted_runs(wl: Workload, b: int) -> np.ndarray:
+    """Start indices (ascending) of the planted runs of sequence b."""
+    n_blocks = wl.n_src // PLANT_RUN
+    n_runs = int(round(PLANT_FRACTION * wl.n_src / PLANT_RUN))
+    rng = rng_for(wl.base_seed, "runs", b)
+    blocks = np.sort(rng.choice(n_blocks, size=n_runs, replace=False))
+    return blocks * PLANT_RUN
+
+
+def indexer_keys_f32(wl: Workload, b: int) -> np.ndarray:
+    """Compressed indexer keys of the source layer, [n_src][dk], float32 grid values."""
+    rng = rng_for(wl.base_seed, "keys", b)
+    if wl.dist == "uniform":
+        return grid_uniform(rng, (wl.n_src, wl.dk))
+    keys = grid_gauss(rng, (wl.n_src, wl.dk), sigma=0.35)
+    topic = _topic(wl, b)
+    rng_p = rng_for(wl.base_seed, "plant", b)
+    for s in planted_runs(wl, b):
+        half = rng_p.random((PLANT_RUN, wl.dk)) < 0.5
+        blk = keys[s:s + PLANT_RUN]
+        blk[half] = np.broadcast_to(topic, blk.shape)[half]
+    return keys
+
+
+def indexer_keys(wl: Workload, b: int) -> np.ndarray:
+    return encode(indexer_keys_f32(wl, b), wl.key_dtype)
+
+
+def indexer_query(wl: Workload, b: int, step: int, prev: Optional[np.ndarray] = None):
+    """Indexer queries q [n_idx][H][dk] and head weights w [n_idx][H] for one step.
+
+    With ``wl.drift`` set, step t > 0 keeps q of step t-1 and redraws a fraction
+    ``drift`` of its coordinates (pass the previous q as ``prev``); w is drawn
+    once per sequence."""
+    shape_q = (wl.n_idx, wl.heads, wl.dk)
+    shape_w = (wl.n_idx, wl.heads)
+    if wl.dist == "planted":
+        topic = _topic(wl, b)
+        noise = grid_gauss(rng_for(wl.base_seed, "qnoise", b, step), shape_q, sigma=0.25)
+        q = np.clip(topic[None, None, :] + noise, -1.0, 1.0).astype(np.float32)
+        w = grid_uniform(rng_for(wl.base_seed, "w", b, step), shape_w,
+                         lo=1.0 / 64, hi=1.0 / 8, step=1.0 / 64)
+        return q, w
+    if wl.drift is None:
+        q = grid_uniform(rng_for(wl.base_seed, "q", b, step), shape_q)
+        w = grid_uniform(rng_for(wl.base_seed, "w", b, step), shape_w)
+        return q, w
+    w = grid_uniform(rng_for(wl.base_seed, "w", b, 0), shape_w)
+    if step == 0:
+        return grid_uniform(rng_for(wl.base_seed, "q", b, 0), shape_q), w
+    if prev is None:
+        raise ValueError("a drifting query needs the previous step's q")
+    rng = rng_for(wl.base_seed, "q", b, step)
+    redraw = rng.random(shape_q) < wl.drift
+    fresh = grid_uniform(rng, shape_q)
+    return np.where(redraw, fresh, prev).astype(np.float32), w
+
+
+def window_rows(wl: Workload, layer: int, b: int) -> np.ndarray:
+    """Sliding-window KV rows [W][D] (float32 grid values)."""
+    return grid_uniform(rng_for(wl.base_seed, "window", layer, b), (wl.window, wl.kv_dim))
+
+
+def cold_rows(wl: Workload, layer: int, b: int, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """All compressed KV entries of one sparse layer [cap][D] (float32 grid values).
+    ``out`` may be any float32 buffer of that shape (e.g. pinned host memory)."""
+    cap = wl.layer_cap(layer)
+    return grid_uniform(rng_for(wl.base_seed, "cold", layer, b), (cap, wl.kv_dim), out=out)
+
+
+def attn_query(wl: Workload, layer: int, b: int, step: int) -> np.ndarray:
+    """Attention queries [Hq][D] of one sparse layer for one step."""
+    return grid_uniform(rng_for(wl.base_seed, "aq", layer, b, step), (wl.hq, wl.kv_dim))
+
+
+def indexer_query_steps(wl: Workload, b: int, steps: int):
+    """Indexer queries of steps 0..steps-1, as (q [steps][n_idx][H][dk], w [steps][n_idx][H])."""
+    qs, ws = [], []
+    prev = None
+    for t in range(steps):
+        q, w = indexer_query(wl, b, t, prev)
+        qs.append(q)
+        ws.append(w)
+        prev = q
+    return np.stack(qs), np.stack(ws)

@@ -1,0 +1,276 @@
+"""CPU oracle of the LSA decode hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library
+(``learned_sparse_kv_amd``) never imports, links or calls it, and this package
+never imports the product library.  The arithmetic lives in the plain C++ file
+``lsa_oracle.cpp`` (double accumulation, one entry at a time); this module only
+marshals numpy arrays and chains the steps in the pages' order:
+score -> select -> (per sparse layer) ratio map -> stage -> attend.
+
+Parity pins for every function are in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lsa_oracle.cpp")
+_BUILD = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD, "liblsa_oracle.so")
+
+DT = {"f32": 0, "bf16": 1, "f16": 2}
+ENS = {"max": 0, "mean": 1}
+MODE = {"topk": 0, "threshold": 1}
+ST_NOT_STORED = 4
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with g++ (no HIP headers, no GPU)."""
+    os.makedirs(_BUILD, exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(["g++", "-std=c++17", "-O2", "-shared", "-fPIC", _SRC, "-o", tmp])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i32, i64, u64, f32, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_double
+        sig = {
+            "oracle_compressed_cap": (i64, [i64, i32]),
+            "oracle_pinned_bytes": (u64, [i64, P, i32, i32, i32]),
+            "oracle_max_capacity": (i32, [i32, i32]),
+            "oracle_swap_enabled": (i32, [i64, i32]),
+            "oracle_score": (None, [P, i32, i64, i32, P, P, i32, i32, i32, P]),
+            "oracle_threshold_float": (f32, [f64]),
+            "oracle_select": (i32, [P, i64, i32, i32, f64, P]),
+            "oracle_ratio_map": (i32, [P, i32, i32, i32, P]),
+            "oracle_pool_new": (P, [i64, i32, i32, i64]),
+            "oracle_pool_free": (None, [P]),
+            "oracle_pool_store": (None, [P, i64, i64]),
+            "oracle_pool_stage": (i32, [P, P, i32, P, P, P, P]),
+            "oracle_pool_stats": (None, [P, P]),
+            "oracle_pool_state": (i32, [P, P, P]),
+            "oracle_attend": (None, [P, i32, i32, P, i32, P, i32, P, i32, f32, P]),
+            "oracle_lowrank_score": (None, [P, i64, i32, P, P, i32, P, P]),
+            "oracle_attend_kv": (None, [P, i32, P, P, i32, i64, P, i32, f32, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(_lib, name)
+            fn.restype = res
+            fn.argtypes = args
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _kv(a: np.ndarray, dtype: str) -> np.ndarray:
+    return _c(a, np.float32 if dtype == "f32" else np.uint16)
+
+
+# ------------------------------------------------------------------ sizing --
+def compressed_cap(ctx: int, ratio: int) -> int:
+    return int(lib().oracle_compressed_cap(ctx, ratio))
+
+
+def pinned_bytes(ctx: int, ratios: Sequence[int], kv_dim: int, elem_bytes: int) -> int:
+    r = _c(list(ratios), np.int32)
+    return int(lib().oracle_pinned_bytes(ctx, _p(r), len(r), kv_dim, elem_bytes))
+
+
+def max_capacity(window: int, gpu_chunks: int) -> int:
+    return int(lib().oracle_max_capacity(window, gpu_chunks))
+
+
+def swap_enabled(cap: int, gpu_chunks: int) -> bool:
+    return bool(lib().oracle_swap_enabled(cap, gpu_chunks))
+
+
+# ------------------------------------------------------------------- score --
+def score(keys: np.ndarray, key_dtype: str, q: np.ndarray, w: np.ndarray,
+          ensemble: str = "max", n_valid: Optional[int] = None) -> np.ndarray:
+    """keys [N][dk] (f32 or 16-bit codes), q [n_idx][H][dk], w [n_idx][H] -> e [n_valid] f32."""
+    keys = _kv(keys, key_dtype)
+    q = _c(q, np.float32)
+    w = _c(w, np.float32)
+    n_idx, H, dk = q.shape
+    n = keys.shape[0] if n_valid is None else int(n_valid)
+    e = np.zeros(n, np.float32)
+    lib().oracle_score(_p(keys), DT[key_dtype], n, dk, _p(q), _p(w), n_idx, H, ENS[ensemble], _p(e))
+    return e
+
+
+# ------------------------------------------------------------------ select --
+def threshold_float(tau: float) -> np.float32:
+    return np.float32(lib().oracle_threshold_float(float(tau)))
+
+
+def select(e: np.ndarray, mode: str, k: int, tau: float = 0.5,
+           n_valid: Optional[int] = None) -> np.ndarray:
+    e = _c(e, np.float32)
+    n = e.shape[0] if n_valid is None else int(n_valid)
+    out = np.zeros(max(1, min(k, n)), np.int32)
+    c = lib().oracle_select(_p(e), n, MODE[mode], k, float(tau), _p(out))
+    return out[:c].copy()
+
+
+def ratio_map(sel: np.ndarray, src_ratio: int, layer_ratio: int) -> np.ndarray:
+    sel = _c(sel, np.int32)
+    out = np.zeros(max(1, sel.size), np.int32)
+    c = lib().oracle_ratio_map(_p(sel), sel.size, src_ratio, layer_ratio, _p(out))
+    return out[:c].copy()
+
+
+# ------------------------------------------------------------------- stage --
+class Pool:
+    """One sparse layer's slot pool for one sequence (the page's LRU struct)."""
+
+    def __init__(self, cap: int, gpu_chunks: int, window: int, row_bytes: int):
+        self.cap, self.gpu_chunks, self.window = cap, gpu_chunks, window
+        self._h = lib().oracle_pool_new(cap, gpu_chunks, window, row_bytes)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib().oracle_pool_free(h)
+            self._h = None
+
+    def store(self, first: int, count: int) -> None:
+        lib().oracle_pool_store(self._h, first, count)
+
+    def stage(self, sel: np.ndarray):
+        """-> (status, phys [W+n], misses [(logical, slot)] in processing order)."""
+        sel = _c(sel, np.int32)
+        n = sel.size
+        phys = np.zeros(self.window + n, np.int32)
+        ml = np.zeros(max(1, n), np.int32)
+        ms = np.zeros(max(1, n), np.int32)
+        nm = ctypes.c_int32(0)
+        st = lib().oracle_pool_stage(self._h, _p(sel), n, _p(phys), _p(ml), _p(ms), ctypes.byref(nm))
+        return int(st), phys, list(zip(ml[:nm.value].tolist(), ms[:nm.value].tolist()))
+
+    def stats(self) -> dict:
+        out = np.zeros(4, np.uint64)
+        lib().oracle_pool_stats(self._h, _p(out))
+        return dict(hits=int(out[0]), misses=int(out[1]), h2d_bytes=int(out[2]), d2h_bytes=int(out[3]))
+
+    def state(self):
+        """-> (slot_logical [S], lru slot ids most- to least-recent)."""
+        sl = np.zeros(self.gpu_chunks, np.int32)
+        lru = np.zeros(self.gpu_chunks, np.int32)
+        n = lib().oracle_pool_state(self._h, _p(sl), _p(lru))
+        return sl, lru[:n].copy()
+
+
+# ------------------------------------------------------------------ attend --
+def attend(q: np.ndarray, window: np.ndarray, store: np.ndarray, kv_dtype: str,
+           sel: np.ndarray, scale: float) -> np.ndarray:
+    """q [Hq][D]; window [W][D]; store [cap][D]; sel [n] logical IDs -> out [Hq][D] f32."""
+    q = _c(q, np.float32)
+    Hq, D = q.shape
+    window = _kv(window, kv_dtype)
+    store = _kv(store, kv_dtype)
+    sel = _c(sel, np.int32)
+    W = window.shape[0] if window.size else 0
+    out = np.zeros((Hq, D), np.float32)
+    lib().oracle_attend(_p(q), Hq, D, _p(window), W, _p(store), DT[kv_dtype], _p(sel), sel.size,
+                        float(scale), _p(out))
+    return out
+
+
+# ------------------------------------------------------------------ KVSwap --
+def lowrank_score(U: np.ndarray, S: np.ndarray, V: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """U [T][r] f16 codes, S [r] f32, V [C][r] f16 codes, q [C] f32 -> score [T] f32."""
+    U = _c(U, np.uint16)
+    V = _c(V, np.uint16)
+    S = _c(S, np.float32)
+    q = _c(q, np.float32)
+    T, r = U.shape
+    C = V.shape[0]
+    out = np.zeros(T, np.float32)
+    lib().oracle_lowrank_score(_p(U), T, r, _p(S), _p(V), C, _p(q), _p(out))
+    return out
+
+
+def attend_kv(q: np.ndarray, K: np.ndarray, V: np.ndarray, kv_dtype: str, row_stride: int,
+              pos: np.ndarray, scale: float) -> np.ndarray:
+    """One head: q [dh]; K, V flat arrays where position p starts at p*row_stride."""
+    q = _c(q, np.float32)
+    K = _kv(K, kv_dtype)
+    V = _kv(V, kv_dtype)
+    pos = _c(pos, np.int32)
+    out = np.zeros(q.size, np.float32)
+    lib().oracle_attend_kv(_p(q), q.size, _p(K), _p(V), DT[kv_dtype], row_stride, _p(pos), pos.size,
+                           float(scale), _p(out))
+    return out
+
+
+# ------------------------------------------------------------- decode step --
+class DecodeState:
+    """Oracle of whole decode steps for one workload: per sparse layer and
+    sequence an LRU pool; all rows stored up front."""
+
+    def __init__(self, wl, window_rows: List[List[np.ndarray]], store_rows: List[List[np.ndarray]]):
+        # window_rows[layer][b] : [W][D]; store_rows[layer][b] : [cap][D] (kv dtype storage)
+        self.wl = wl
+        self.window_rows = window_rows
+        self.store_rows = store_rows
+        row_bytes = wl.kv_dim * (4 if wl.kv_dtype == "f32" else 2)
+        self.pools = []
+        for l in range(wl.n_layers):
+            cap = wl.layer_cap(l)
+            per_b = []
+            for b in range(wl.batch):
+                p = Pool(cap, wl.gpu_chunks, wl.window, row_bytes)
+                p.store(0, cap)
+                per_b.append(p)
+            self.pools.append(per_b)
+
+    def step(self, keys: Sequence[np.ndarray], q_idx: np.ndarray, w_idx: np.ndarray,
+             q_attn: np.ndarray, k: Optional[int] = None) -> dict:
+        """keys[b] [N][dk]; q_idx [B][n_idx][H][dk]; w_idx [B][n_idx][H]; q_attn [L][B][Hq][D]."""
+        wl = self.wl
+        k = wl.k if k is None else k
+        res = dict(scores=[], sel=[], layer_sel=[], phys=[], misses=[], out=[])
+        for b in range(wl.batch):
+            e = score(keys[b], wl.key_dtype, q_idx[b], w_idx[b], wl.ensemble)
+            s = select(e, wl.mode, k, wl.tau if wl.tau is not None else 0.5)
+            res["scores"].append(e)
+            res["sel"].append(s)
+        for l in range(wl.n_layers):
+            lsel, lphys, lmiss, lout = [], [], [], []
+            for b in range(wl.batch):
+                sl = ratio_map(res["sel"][b], wl.src_ratio, wl.layer_ratios[l])
+                st, phys, miss = self.pools[l][b].stage(sl)
+                if st != 0:
+                    raise RuntimeError(f"oracle stage status {st}")
+                out = attend(q_attn[l][b], self.window_rows[l][b], self.store_rows[l][b],
+                             wl.kv_dtype, sl, wl.scale)
+                lsel.append(sl)
+                lphys.append(phys)
+                lmiss.append(miss)
+                lout.append(out)
+            res["layer_sel"].append(lsel)
+            res["phys"].append(lphys)
+            res["misses"].append(lmiss)
+            res["out"].append(lout)
+        return res

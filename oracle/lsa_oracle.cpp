@@ -1,0 +1,427 @@
+// Plain CPU oracle of the LSA decode hot path (score -> select -> stage ->
+// attend) and of KVSwap's grouped low-rank prediction.
+//
+// TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+// or calls this file; only the test-suite, the package smoke check and the
+// benchmark's CPU-baseline leg load it (through oracle/__init__.py).  It shares
+// no code, header, table or constant with the HIP library.
+//
+// Every step is written the slow, obvious way: double accumulation, one entry
+// at a time, std::stable_sort for ordering, and for the slot pool the literal
+// structure of page 1 (a std::list LRU plus an unordered_map).  Each function
+// names the passage of the source pages it follows.  The pages are:
+//   [P1] "FlashMemory 1M 上下文显存优化使用文档" (PocketLLM performance doc)
+//   [P2] article on "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long
+//        Context via Lookahead Sparse Attention"
+//   [P4] "KVSwap：大模型推理中的KV缓存优化技术"
+// Where the pages leave a step open, the reading taken is stated inline.
+//
+// Build: g++ -std=c++17 -O2 -shared -fPIC lsa_oracle.cpp -o liblsa_oracle.so
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <list>
+#include <numeric>
+#include <set>
+#include <unordered_map>
+#include <vector>
+
+namespace {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+enum { ENS_MAX = 0, ENS_MEAN = 1 };
+enum { SEL_TOPK = 0, SEL_THRESHOLD = 1 };
+enum { ST_OK = 0, ST_NOT_STORED = 4 };
+
+// IEEE binary16 -> double, from the format's definition (1 sign, 5 exponent
+// bits with bias 15, 10 fraction bits; exponent 0 = subnormal).
+double half_to_double(uint16_t h) {
+    const int sign = h >> 15;
+    const int expo = (h >> 10) & 31;
+    const int frac = h & 1023;
+    double v;
+    if (expo == 0) {
+        v = std::ldexp((double)frac, -24);
+    } else if (expo == 31) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = std::ldexp((double)(1024 + frac), expo - 25);
+    }
+    return sign ? -v : v;
+}
+
+// bfloat16 is the upper half of an IEEE binary32.
+double bf16_to_double(uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+double elem(const void* base, int dtype, int64_t i) {
+    if (dtype == DT_F32) {
+        float f;
+        std::memcpy(&f, (const char*)base + 4 * i, 4);
+        return f;
+    }
+    uint16_t h;
+    std::memcpy(&h, (const char*)base + 2 * i, 2);
+    return dtype == DT_BF16 ? bf16_to_double(h) : half_to_double(h);
+}
+
+// Total order of the selector: higher score first, lower index first among
+// equal scores.  Reading: the pages give no tie rule; the lowest index wins.
+// -0 and +0 compare equal here, so they tie.
+struct ByScoreThenIndex {
+    const float* e;
+    bool operator()(int32_t a, int32_t b) const {
+        if (e[a] != e[b]) return e[a] > e[b];
+        return a < b;
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+// ---------------------------------------------------------------- sizing ---
+// [P1] "POCKETLLM_GGUF_KV_SWAP_PINNED_MIB" tuning section: per layer
+// compressed_cap = (context_length + ratio - 1) / ratio and the pinned bytes
+// are the sum over sparse layers of compressed_cap * kv_dim * sizeof(element).
+int64_t oracle_compressed_cap(int64_t ctx, int32_t ratio) {
+    return (ctx + ratio - 1) / ratio;
+}
+
+uint64_t oracle_pinned_bytes(int64_t ctx, const int32_t* ratios, int32_t n_layers,
+                             int32_t kv_dim, int32_t elem_bytes) {
+    uint64_t total = 0;
+    for (int32_t l = 0; l < n_layers; ++l)
+        total += (uint64_t)oracle_compressed_cap(ctx, ratios[l]) * (uint64_t)kv_dim *
+                 (uint64_t)elem_bytes;
+    return total;
+}
+
+// [P1] expected-log section: max_capacity = window(128) + gpu_chunks(512).
+int32_t oracle_max_capacity(int32_t window, int32_t gpu_chunks) { return window + gpu_chunks; }
+
+// [P1] troubleshooting, "gguf_kv_swap=0 reason=no_layer_with_compressed_cap_gt_gpu_chunks":
+// a layer whose compressed_cap <= gpu_chunks is kept fully resident (no swap).
+int32_t oracle_swap_enabled(int64_t cap, int32_t gpu_chunks) { return cap > gpu_chunks ? 1 : 0; }
+
+// ----------------------------------------------------------------- score ---
+// [P1] architecture overview: the hidden state feeds 3 scorers which read the
+// shared indexer_kv_cache and are combined by an ensemble (max or mean).
+// [P2] "LSA 让模型预判 KV chunk": memory-indexer queries are matched against the
+// compressed indexer keys by dot-product similarity.
+// Reading (the pages give no head formula): indexer i scores entry j as
+//     s_i[j] = sum_h w[i,h] * ReLU( q[i,h,:] . key[j,:] )
+// kept as a float; the max ensemble takes the largest s_i[j], the mean ensemble
+// rounds the sum of the float s_i[j] to float and divides once by n_idx in
+// IEEE single precision.  -0 is written as +0.
+//
+// keys: [n_valid][dk] in key_dtype; q: [n_idx][H][dk]; w: [n_idx][H]; e: [n_valid].
+void oracle_score(const void* keys, int32_t key_dtype, int64_t n_valid, int32_t dk,
+                  const float* q, const float* w, int32_t n_idx, int32_t H,
+                  int32_t ensemble, float* e) {
+    std::vector<double> key(dk);
+    std::vector<float> s(n_idx);
+    for (int64_t j = 0; j < n_valid; ++j) {
+        for (int32_t t = 0; t < dk; ++t) key[t] = elem(keys, key_dtype, j * dk + t);
+        for (int32_t i = 0; i < n_idx; ++i) {
+            double acc = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                const float* qh = q + ((int64_t)i * H + h) * dk;
+                double d = 0.0;
+                for (int32_t t = 0; t < dk; ++t) d += (double)qh[t] * key[t];
+                const double relu = d > 0.0 ? d : 0.0;
+                acc += (double)w[(int64_t)i * H + h] * relu;
+            }
+            s[i] = (float)acc + 0.0f;
+        }
+        float r;
+        if (ensemble == ENS_MAX) {
+            r = s[0];
+            for (int32_t i = 1; i < n_idx; ++i)
+                if (s[i] > r) r = s[i];
+        } else {
+            double sum = 0.0;
+            for (int32_t i = 0; i < n_idx; ++i) sum += (double)s[i];
+            const float sum_f = (float)sum;
+            r = sum_f / (float)n_idx;
+        }
+        e[j] = r + 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------- select ---
+// [P2] "Recall / Threshold Selector": an entry is recalled when the sigmoid of
+// its score exceeds a threshold tau.  Over the reals sigmoid(e) > tau holds
+// exactly when e > logit(tau) = ln(tau / (1 - tau)); for a float e that is
+// e > t_f with t_f the largest float not above logit(tau).
+float oracle_threshold_float(double tau) {
+    const double t = std::log(tau / (1.0 - tau));
+    float tf = (float)t;
+    if ((double)tf > t) tf = std::nextafterf(tf, -INFINITY);
+    return tf;
+}
+
+// Top-k mode: [P1] "global top-k (512 chunks)", index_topk = global_keep_cap.
+// Threshold mode: [P2] sigmoid threshold, capped at k ([P1] log line
+// "global_keep_cap=512").  Reading: when more than k entries pass, the first k
+// of the total order are kept; fewer than k valid entries means all of them.
+// The selected indices are returned in ascending order.
+int32_t oracle_select(const float* e, int64_t n_valid, int32_t mode, int32_t k, double tau,
+                      int32_t* sel) {
+    std::vector<int32_t> order(n_valid);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), ByScoreThenIndex{e});
+
+    std::vector<int32_t> chosen;
+    if (mode == SEL_TOPK) {
+        for (int64_t r = 0; r < n_valid && (int64_t)chosen.size() < k; ++r)
+            chosen.push_back(order[r]);
+    } else {
+        const float tf = oracle_threshold_float(tau);
+        std::vector<int32_t> pass;
+        for (int64_t r = 0; r < n_valid; ++r)
+            if (e[order[r]] > tf) pass.push_back(order[r]);
+        for (size_t r = 0; r < pass.size() && (int64_t)chosen.size() < k; ++r)
+            chosen.push_back(pass[r]);
+    }
+    std::sort(chosen.begin(), chosen.end());
+    std::copy(chosen.begin(), chosen.end(), sel);
+    return (int32_t)chosen.size();
+}
+
+// ------------------------------------------------------------- ratio map ---
+// [P1] FlashMemory vs native indexer table and the log line "source_ratio=4":
+// one global selection over the ratio-4 source layer is reused by every sparse
+// layer, including the ratio-128 ones.  Reading (the pages do not say how):
+// source entry j covers tokens [j*r_src, (j+1)*r_src), which lie in entry
+// floor(j*r_src / r_layer) of a layer whose ratio is a multiple of r_src; the
+// layer's list is the ascending set of those entries, duplicates removed.
+int32_t oracle_ratio_map(const int32_t* sel, int32_t count, int32_t src_ratio,
+                         int32_t layer_ratio, int32_t* out) {
+    std::set<int64_t> s;
+    for (int32_t i = 0; i < count; ++i) s.insert((int64_t)sel[i] * src_ratio / layer_ratio);
+    int32_t n = 0;
+    for (int64_t v : s) out[n++] = (int32_t)v;
+    return n;
+}
+
+// ----------------------------------------------------------------- stage ---
+// [P1] "KV_SWAP 实现细节": the per-layer state is this struct, and swap-in of
+// the selected logical IDs works per ID: a hit touches the entry (moves it to
+// the LRU front) and counts a hit; a miss evicts the LRU back (pop_back),
+// takes that slot, copies the host row into it and counts a miss; the ID is
+// then rewritten to the physical row window + slot.  A selected chunk that was
+// never stored is an error ("selected chunk before it was stored").
+// Readings: (a) the doc gives no order among the IDs of one step: hits are
+// processed first, then misses, each group in ascending logical order, so a
+// step never evicts a chunk it selected; (b) while a slot was never used, a
+// miss takes the lowest-numbered unused slot instead of evicting.
+struct OracleSwapLayerState {
+    int64_t compressed_cap;
+    int32_t gpu_chunks;
+    int32_t window;
+    int64_t row_bytes;
+    std::vector<uint8_t> host_ready;          // [compressed_cap]
+    std::vector<int> gpu_slot_logical;        // [gpu_chunks], -1 = unused
+    std::unordered_map<int, int> slot_by_logical;
+    std::list<int> slot_lru;                  // slot ids, front = most recently used
+    uint64_t hits = 0, misses = 0, h2d_bytes = 0, d2h_bytes = 0;
+};
+
+void* oracle_pool_new(int64_t cap, int32_t gpu_chunks, int32_t window, int64_t row_bytes) {
+    auto* p = new OracleSwapLayerState;
+    p->compressed_cap = cap;
+    p->gpu_chunks = gpu_chunks;
+    p->window = window;
+    p->row_bytes = row_bytes;
+    p->host_ready.assign(cap, 0);
+    p->gpu_slot_logical.assign(gpu_chunks, -1);
+    return p;
+}
+
+void oracle_pool_free(void* pool) { delete static_cast<OracleSwapLayerState*>(pool); }
+
+// [P1] store flow: the row is copied device-to-host and host_ready is set.
+void oracle_pool_store(void* pool, int64_t first, int64_t count) {
+    auto* p = static_cast<OracleSwapLayerState*>(pool);
+    for (int64_t l = first; l < first + count; ++l) p->host_ready[l] = 1;
+    p->d2h_bytes += (uint64_t)count * (uint64_t)p->row_bytes;
+}
+
+// sel: ascending unique logical IDs of this layer (n of them).
+// phys: [window + n]; rows 0..window-1 are the window, then one row per ID.
+// miss_logical / miss_slot: [n]; the misses in processing order.
+// Returns 0, or 4 when a selected ID was never stored (nothing is changed then).
+int32_t oracle_pool_stage(void* pool, const int32_t* sel, int32_t n, int32_t* phys,
+                          int32_t* miss_logical, int32_t* miss_slot, int32_t* n_miss) {
+    auto* p = static_cast<OracleSwapLayerState*>(pool);
+    for (int32_t i = 0; i < n; ++i)
+        if (!p->host_ready[sel[i]]) return ST_NOT_STORED;
+    for (int32_t r = 0; r < p->window; ++r) phys[r] = r;
+    *n_miss = 0;
+    if (p->compressed_cap <= p->gpu_chunks) {   // swap disabled: fully resident
+        for (int32_t i = 0; i < n; ++i) phys[p->window + i] = p->window + sel[i];
+        return ST_OK;
+    }
+    std::vector<int32_t> missed;
+    for (int32_t i = 0; i < n; ++i) {           // hits, ascending
+        auto it = p->slot_by_logical.find(sel[i]);
+        if (it == p->slot_by_logical.end()) {
+            missed.push_back(sel[i]);
+            continue;
+        }
+        const int slot = it->second;
+        p->slot_lru.remove(slot);
+        p->slot_lru.push_front(slot);
+        p->hits++;
+    }
+    for (int32_t l : missed) {                  // misses, ascending
+        int slot = -1;
+        for (int s = 0; s < p->gpu_chunks; ++s)
+            if (p->gpu_slot_logical[s] < 0) { slot = s; break; }
+        if (slot < 0) {
+            slot = p->slot_lru.back();
+            p->slot_lru.pop_back();
+            p->slot_by_logical.erase(p->gpu_slot_logical[slot]);
+        }
+        p->gpu_slot_logical[slot] = l;
+        p->slot_by_logical[l] = slot;
+        p->slot_lru.push_front(slot);
+        p->misses++;
+        p->h2d_bytes += (uint64_t)p->row_bytes;
+        miss_logical[*n_miss] = l;
+        miss_slot[*n_miss] = slot;
+        (*n_miss)++;
+    }
+    for (int32_t i = 0; i < n; ++i) phys[p->window + i] = p->window + p->slot_by_logical[sel[i]];
+    return ST_OK;
+}
+
+// stats: hits, misses, h2d_bytes, d2h_bytes
+void oracle_pool_stats(void* pool, uint64_t* out) {
+    auto* p = static_cast<OracleSwapLayerState*>(pool);
+    out[0] = p->hits;
+    out[1] = p->misses;
+    out[2] = p->h2d_bytes;
+    out[3] = p->d2h_bytes;
+}
+
+// slot_logical: [gpu_chunks] logical ID held by each slot (-1 unused);
+// lru: slot ids from most to least recently used; returns their number.
+int32_t oracle_pool_state(void* pool, int32_t* slot_logical, int32_t* lru) {
+    auto* p = static_cast<OracleSwapLayerState*>(pool);
+    for (int s = 0; s < p->gpu_chunks; ++s) slot_logical[s] = p->gpu_slot_logical[s];
+    int32_t n = 0;
+    for (int s : p->slot_lru) lru[n++] = s;
+    return n;
+}
+
+// ---------------------------------------------------------------- attend ---
+// [P1] "Two-tier KV cache" and the per-layer sparse attention
+// (indexed_cached_attention over window + selected): one decode query per head
+// attends over the window rows and then the selected compressed entries.
+// Readings: each compressed entry serves as both key and value (kv_dim 512);
+// softmax(scale * q.row) with no mask and no sink; rows are taken in list order
+// (window 0..W-1, then the selected entries in ascending logical order), read
+// from the full store by logical ID -- staging only moves rows, so this is also
+// the answer with swapping switched off.  With no rows the output is 0.
+//
+// q: [Hq][D] f32; window: [W][D]; store: [cap][D] (kv_dtype); sel: [n]; out: [Hq][D].
+void oracle_attend(const float* q, int32_t Hq, int32_t D, const void* window, int32_t W,
+                   const void* store, int32_t kv_dtype, const int32_t* sel, int32_t n,
+                   float scale, float* out) {
+    const int32_t rows = W + n;
+    std::vector<double> kv((size_t)rows * D);
+    for (int32_t r = 0; r < rows; ++r)
+        for (int32_t d = 0; d < D; ++d)
+            kv[(size_t)r * D + d] = r < W ? elem(window, kv_dtype, (int64_t)r * D + d)
+                                          : elem(store, kv_dtype, (int64_t)sel[r - W] * D + d);
+    std::vector<double> z(rows);
+    for (int32_t h = 0; h < Hq; ++h) {
+        if (rows == 0) {
+            for (int32_t d = 0; d < D; ++d) out[(size_t)h * D + d] = 0.0f;
+            continue;
+        }
+        double m = -INFINITY;
+        for (int32_t r = 0; r < rows; ++r) {
+            double dot = 0.0;
+            for (int32_t d = 0; d < D; ++d) dot += (double)q[(size_t)h * D + d] * kv[(size_t)r * D + d];
+            z[r] = (double)scale * dot;
+            m = std::max(m, z[r]);
+        }
+        double den = 0.0;
+        for (int32_t r = 0; r < rows; ++r) {
+            z[r] = std::exp(z[r] - m);
+            den += z[r];
+        }
+        for (int32_t d = 0; d < D; ++d) {
+            double num = 0.0;
+            for (int32_t r = 0; r < rows; ++r) num += z[r] * kv[(size_t)r * D + d];
+            out[(size_t)h * D + d] = (float)(num / den);
+        }
+    }
+}
+
+// ------------------------------------------------------- KVSwap variant ---
+// [P4] §2.3.1-2.3.2: K is kept as low-rank factors K ~ U diag(S) V^T and
+// rebuilt on demand (reconstruct_K = U @ diag(S) @ V.T); §2.2.1: the
+// prediction scores are q @ K^T followed by top-k with k = MG = 400; §2.2.2:
+// heads are grouped (G = 4) and a group shares one selection.
+// Reading: a group's key at position t is the concatenation of its heads'
+// keys (width C = G * head_dim); its query is the concatenation of the heads'
+// queries; score[t] = q . K[t,:] with K[t,:] = sum_x U[t,x] S[x] V[:,x].
+//
+// U: [T][r] f16; S: [r] f32; V: [C][r] f16; q: [C] f32; score: [T].
+void oracle_lowrank_score(const uint16_t* U, int64_t T, int32_t r, const float* S,
+                          const uint16_t* V, int32_t C, const float* q, float* score) {
+    std::vector<double> krow(C);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t c = 0; c < C; ++c) {
+            double k = 0.0;
+            for (int32_t x = 0; x < r; ++x)
+                k += half_to_double(U[t * r + x]) * (double)S[x] * half_to_double(V[(int64_t)c * r + x]);
+            krow[c] = k;
+        }
+        double dot = 0.0;
+        for (int32_t c = 0; c < C; ++c) dot += (double)q[c] * krow[c];
+        score[t] = (float)dot + 0.0f;
+    }
+}
+
+// Per-head attention of the KVSwap variant over separate full-precision K and
+// V rows of the selected positions (no window).  K, V: position p of this head
+// starts at element p * row_stride; q: [dh]; out: [dh].
+void oracle_attend_kv(const float* q, int32_t dh, const void* K, const void* V, int32_t kv_dtype,
+                      int64_t row_stride, const int32_t* pos, int32_t n, float scale, float* out) {
+    if (n == 0) {
+        for (int32_t d = 0; d < dh; ++d) out[d] = 0.0f;
+        return;
+    }
+    std::vector<double> z(n);
+    double m = -INFINITY;
+    for (int32_t i = 0; i < n; ++i) {
+        double dot = 0.0;
+        for (int32_t d = 0; d < dh; ++d)
+            dot += (double)q[d] * elem(K, kv_dtype, (int64_t)pos[i] * row_stride + d);
+        z[i] = (double)scale * dot;
+        m = std::max(m, z[i]);
+    }
+    double den = 0.0;
+    for (int32_t i = 0; i < n; ++i) {
+        z[i] = std::exp(z[i] - m);
+        den += z[i];
+    }
+    for (int32_t d = 0; d < dh; ++d) {
+        double num = 0.0;
+        for (int32_t i = 0; i < n; ++i) num += z[i] * elem(V, kv_dtype, (int64_t)pos[i] * row_stride + d);
+        out[d] = (float)(num / den);
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+"""Pins of oracle.score (indexer scoring + ensemble) against a hand-worked
+example, exact rational brute force, and special cases with closed forms."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import lsa_inputs as L
+import oracle
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "score_hand.json")))
+
+
+def round_f32(x: Fraction) -> np.float32:
+    """Round a rational to the nearest float32 (ties to even), exactly."""
+    f = np.float32(float(x))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - x), int(np.float32(c).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def brute_score(keys, q, w, ens):
+    """Exact rational score of every key; the mean is the float sum divided once."""
+    n_idx, H, dk = q.shape
+    out = []
+    for k in keys:
+        s = []
+        for i in range(n_idx):
+            acc = Fraction(0)
+            for h in range(H):
+                d = sum(Fraction(float(q[i, h, t])) * Fraction(float(k[t])) for t in range(dk))
+                acc += Fraction(float(w[i, h])) * max(d, Fraction(0))
+            s.append(round_f32(acc))
+        if ens == "max":
+            out.append(max(s))
+        else:
+            tot = round_f32(sum(Fraction(float(v)) for v in s))
+            out.append(round_f32(Fraction(float(tot)) / n_idx))
+    return np.array(out, np.float32)
+
+
+def test_hand_example():
+    keys = np.array(GOLD["keys"], np.float32)
+    q = np.array(GOLD["q"], np.float32)
+    w = np.array(GOLD["w"], np.float32)
+    for ens in ("max", "mean"):
+        e = oracle.score(keys, "f32", q, w, ens)
+        assert e.tolist() == GOLD[ens], ens
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_grid(seed):
+    rng = np.random.default_rng(seed)
+    n_idx, H, dk, N = rng.integers(1, 4), rng.integers(1, 4), rng.integers(1, 9), rng.integers(1, 25)
+    keys = L.grid_uniform(rng, (N, dk))
+    q = L.grid_uniform(rng, (n_idx, H, dk))
+    w = L.grid_uniform(rng, (n_idx, H))
+    for ens in ("max", "mean"):
+        got = oracle.score(keys, "f32", q, w, ens)
+        want = brute_score(keys, q, w, ens)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), ens
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_brute_force_general_floats(seed):
+    # arbitrary fp32 inputs: the double-accumulated oracle is within one float ulp
+    # of the exact rational result
+    rng = np.random.default_rng(100 + seed)
+    n_idx, H, dk, N = 3, 3, 7, 16
+    keys = rng.standard_normal((N, dk)).astype(np.float32)
+    q = rng.standard_normal((n_idx, H, dk)).astype(np.float32)
+    w = rng.standard_normal((n_idx, H)).astype(np.float32)
+    for ens in ("max", "mean"):
+        got = oracle.score(keys, "f32", q, w, ens)
+        want = brute_score(keys, q, w, ens)
+        ulp = np.spacing(np.abs(want)).astype(np.float64)
+        assert np.all(np.abs(got.astype(np.float64) - want) <= ulp + 1e-30)
+
+
+def test_single_positive_head_is_matmul():
+    # one indexer, one head, weight 1, all-positive operands: the score is q.k,
+    # i.e. a matrix-vector product
+    rng = np.random.default_rng(7)
+    keys = L.grid_uniform(rng, (300, 64), lo=0.125, hi=1.0)
+    q = L.grid_uniform(rng, (1, 1, 64), lo=0.125, hi=1.0)
+    w = np.ones((1, 1), np.float32)
+    got = oracle.score(keys, "f32", q, w)
+    want = (keys.astype(np.float64) @ q[0, 0].astype(np.float64)).astype(np.float32)
+    assert np.array_equal(got, want)
+
+
+def test_relu_clips_negative_dots():
+    # all dots negative -> every head contributes 0 -> score +0 (sign bit clear)
+    rng = np.random.default_rng(8)
+    keys = L.grid_uniform(rng, (50, 16), lo=0.125, hi=1.0)
+    q = -L.grid_uniform(rng, (2, 3, 16), lo=0.125, hi=1.0)
+    w = -np.ones((2, 3), np.float32)  # negative weights times 0 give -0
+    for ens in ("max", "mean"):
+        e = oracle.score(keys, "f32", q, w, ens)
+        assert np.all(e.view(np.uint32) == 0), ens
+
+
+def test_identical_indexers_ensemble_agree():
+    rng = np.random.default_rng(9)
+    keys = L.grid_uniform(rng, (200, 32))
+    q1 = L.grid_uniform(rng, (1, 4, 32))
+    w1 = L.grid_uniform(rng, (1, 4))
+    one = oracle.score(keys, "f32", q1, w1)
+    q3, w3 = np.repeat(q1, 3, 0), np.repeat(w1, 3, 0)
+    assert np.array_equal(oracle.score(keys, "f32", q3, w3, "max"), one)
+    assert np.array_equal(oracle.score(keys, "f32", q3, w3, "mean"), one)
+
+
+def test_max_ensemble_is_max_of_single_indexers():
+    rng = np.random.default_rng(10)
+    keys = L.grid_uniform(rng, (200, 32))
+    q = L.grid_uniform(rng, (3, 4, 32))
+    w = L.grid_uniform(rng, (3, 4))
+    singles = np.stack([oracle.score(keys, "f32", q[i:i + 1], w[i:i + 1]) for i in range(3)])
+    assert np.array_equal(oracle.score(keys, "f32", q, w, "max"), singles.max(0) + np.float32(0))
+    mean = ((singles[0] + singles[1]) + singles[2]) / np.float32(3)  # exact sums on the grid
+    assert np.array_equal(oracle.score(keys, "f32", q, w, "mean"), mean.astype(np.float32))
+
+
+def test_weights_scale_linearly():
+    rng = np.random.default_rng(11)
+    keys = L.grid_uniform(rng, (100, 16))
+    q = L.grid_uniform(rng, (2, 3, 16))
+    w = L.grid_uniform(rng, (2, 3))
+    assert np.array_equal(oracle.score(keys, "f32", q, 2 * w), 2 * oracle.score(keys, "f32", q, w))
+
+
+def test_key_permutation_permutes_scores():
+    rng = np.random.default_rng(12)
+    keys = L.grid_uniform(rng, (120, 16))
+    q = L.grid_uniform(rng, (3, 2, 16))
+    w = L.grid_uniform(rng, (3, 2))
+    perm = rng.permutation(120)
+    assert np.array_equal(oracle.score(keys[perm], "f32", q, w), oracle.score(keys, "f32", q, w)[perm])
+
+
+def test_bf16_and_f16_storage_decode():
+    rng = np.random.default_rng(13)
+    keys = L.grid_uniform(rng, (64, 16))
+    q = L.grid_uniform(rng, (3, 8, 16))
+    w = L.grid_uniform(rng, (3, 8))
+    ref = oracle.score(keys, "f32", q, w)
+    assert np.array_equal(oracle.score(L.f32_to_bf16_bits(keys), "bf16", q, w), ref)
+    assert np.array_equal(oracle.score(L.f32_to_f16_bits(keys), "f16", q, w), ref)
+    # f16 decode incl. subnormals: one positive key element, q = w = 1 -> the value itself
+    vals = np.array([6.1e-5, 5.96e-8, 1.0, 0.333, 65504.0, 2.0 ** -20], np.float16)
+    e = oracle.score(vals.view(np.uint16).reshape(-1, 1), "f16", np.ones((1, 1, 1), np.float32),
+                     np.ones((1, 1), np.float32))
+    assert np.array_equal(e, vals.astype(np.float32))
+
+
+def test_n_valid_prefix():
+    rng = np.random.default_rng(14)
+    keys = L.grid_uniform(rng, (100, 16))
+    q = L.grid_uniform(rng, (1, 2, 16))
+    w = L.grid_uniform(rng, (1, 2))
+    assert np.array_equal(oracle.score(keys, "f32", q, w, n_valid=37), oracle.score(keys[:37], "f32", q, w))
