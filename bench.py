@@ -1,0 +1,204 @@
+"""Benchmark of the LSA decode hot path on one MI355X.
+
+One step = score (every compressed indexer key of the source layer) -> select
+-> per sparse layer: ratio map -> LRU stage + gather of missed rows -> attend,
+i.e. one lsa_decode_step.  Default workload: 1M-token context, ratio-4 source
+layer of 262144 entries, 4 x (ratio-4 + ratio-128) sparse layers with pinned
+host cold pools and 1024-slot LRU pools, top-512, 3 indexers x 8 heads x 128.
+
+Prints ONE JSON line.  Per-kernel times come from HIP events recorded on the
+launch stream inside the timed region; the CPU baseline is the plain oracle
+timed on a bounded sample of the same steps.
+
+    python bench.py [--steps K] [--warmup W] [--workload swap_1m|thresh_256k|ens_8k|tiny_8k]
+                    [--no-cpu-baseline] [--copy-calibration]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LSA decode steps/s (score+select+attend) at 256K/1M ctx; % of HBM peak"
+HBM_PEAK_GBS = 8000.0
+KERNELS = ["score", "select", "stage", "gather", "attend", "combine"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(name):
+    with open(os.path.join(ROOT, "learned_sparse_kv_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload, score_src_hash):
+    """HBM bytes per fm_score launch from the committed rocprofv3 counter summary,
+    or None when absent or taken on a different fm_score source."""
+    path = os.path.join(ROOT, "profiles", f"fm_score_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"fm_score\.hip sha256\[:16\]:\s*([0-9a-f]+)", txt)
+    m_bytes = re.search(r"hbm_bytes_per_dispatch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != score_src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 256 << 20
+    a = torch.empty(n // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 5 copies of {n} bytes (read {n}, write {n} per dispatch)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="swap_1m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-steps", type=int, default=12)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the decode path on a single MI355X "
+              "(the multi-GPU sharding is a design, not code); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import lsa_inputs as L
+    from learned_sparse_kv_amd import lsa
+    from learned_sparse_kv_amd.workload import DeviceWorkload
+
+    wl = L.WORKLOADS[args.workload]
+    K, Wm = args.steps, args.warmup
+    log(f"workload {wl.name}: ctx={wl.ctx} B={wl.batch} N={wl.n_src} layers={wl.layer_ratios} "
+        f"k={wl.k} S={wl.gpu_chunks} cold={wl.cold} keys={wl.key_dtype} kv={wl.kv_dtype}")
+    t0 = time.time()
+    dw = DeviceWorkload(wl, keep_host=not args.no_cpu_baseline, log=log)
+    dw.make_steps(Wm + K)
+    log(f"set-up {time.time() - t0:.1f}s")
+
+    for t in range(Wm):
+        dw.step(t)
+    torch.cuda.synchronize()
+    stats0 = [p.stats() for p in dw.pools]
+
+    # ---- timed region: K steps, HIP events around every kernel on the launch stream
+    dw.ctx.set_timing(True)
+    dw.ctx.timing_read()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for t in range(Wm, Wm + K):
+        dw.step(t)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ktimes = dw.ctx.timing_read()
+    dw.ctx.set_timing(False)
+    ms_per_step = (t_end - t_start) * 1e3 / K
+    value = 1e3 / ms_per_step
+    stats1 = [p.stats() for p in dw.pools]
+
+    # ---- algorithmic bytes (per launch)
+    key_b = 4 if wl.key_dtype == "f32" else 2
+    kv_b = 4 if wl.kv_dtype == "f32" else 2
+    score_bytes = wl.batch * wl.n_src * (wl.dk * key_b + 4)
+    avg = {k: (ktimes[k][0] / ktimes[k][1] if ktimes[k][1] else 0.0) for k in KERNELS}
+    score_gbs = score_bytes / (avg["score"] * 1e-3) / 1e9
+    hits = sum(s1["hits"] - s0["hits"] for s0, s1 in zip(stats0, stats1))
+    misses = sum(s1["misses"] - s0["misses"] for s0, s1 in zip(stats0, stats1))
+    # attention bytes: window + staged rows of every layer and sequence, read once
+    n_rows = dw.n_rows.cpu().numpy()
+    attend_bytes = float(n_rows.sum()) * wl.kv_dim * kv_b
+    sa_ms = avg["score"] + avg["attend"] + avg["combine"]
+    sa_frac = (score_bytes + attend_bytes) / (sa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+
+    src_hash = kernel_source_hash("fm_score.hip")
+    traffic = stored_traffic(wl.name, src_hash)
+    roofline = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "fm_score",
+                "algorithmic_bytes_per_launch": score_bytes, "avg_launch_us": round(avg["score"] * 1e3, 2)}
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same steps, and a
+    # parity check of the GPU on those steps (pools reset on both sides)
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n_s = max(1, min(args.cpu_sample_steps, Wm + K))
+        ref = oracle.DecodeState(wl, dw.windows, dw.stores)
+        dw.reset_pools()
+        sel_ok, max_err = True, 0.0
+        tc0 = time.perf_counter()
+        cpu_s = 0.0
+        for t in range(n_s):
+            dw.step(t)
+            torch.cuda.synchronize()
+            c0 = time.perf_counter()
+            want = ref.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t])
+            cpu_s += time.perf_counter() - c0
+            cnt = dw.count.cpu().numpy()
+            sel = dw.sel.cpu().numpy()
+            out = dw.out.cpu().numpy()
+            phys = dw.phys.cpu().numpy()
+            for b in range(wl.batch):
+                sel_ok &= bool(np.array_equal(sel[b, :cnt[b]], want["sel"][b]))
+                for l in range(wl.n_layers):
+                    w_ = want["out"][l][b]
+                    den = np.maximum(np.abs(w_).max(axis=1), 1e-30)
+                    max_err = max(max_err, float((np.abs(out[l, b] - w_).max(axis=1) / den).max()))
+                    n = want["phys"][l][b].size
+                    sel_ok &= bool(np.array_equal(phys[l, b, :n], want["phys"][l][b]))
+        tol = 1e-5 if wl.kv_dtype == "f32" else 2e-2
+        parity = {"steps": n_s, "selected_sets_and_rows_identical": sel_ok, "max_rel_err": max_err,
+                  "tolerance": tol, "pass": bool(sel_ok and max_err <= tol)}
+        cpu = {"value": round(n_s / cpu_s, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_s} full decode steps (steps 0..{n_s - 1}) of {wl.name}: score of all "
+                         f"{wl.batch}x{wl.n_src} entries, select, {wl.n_layers} layers of stage + attend; "
+                         f"single-threaded C++ oracle, {cpu_s:.1f}s"}
+        log(f"cpu baseline {cpu['value']} steps/s over {n_s} steps ({time.perf_counter() - tc0:.1f}s incl. GPU replay)")
+
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.kv_dtype if wl.kv_dtype == wl.key_dtype else f"{wl.key_dtype}/{wl.kv_dtype}",
+        "data": "synthetic (seeded 1/8-grid values)",
+        "config": {"workload": wl.name, "ctx": wl.ctx, "batch": wl.batch, "src_entries": wl.n_src,
+                   "sparse_layer_ratios": list(wl.layer_ratios), "indexers": f"{wl.n_idx}x{wl.heads}x{wl.dk}",
+                   "select": f"{wl.mode} k={wl.k}", "gpu_chunks": wl.gpu_chunks, "cold_pool": wl.cold,
+                   "window": wl.window, "kv_dim": wl.kv_dim, "attn_heads": wl.hq,
+                   "step": "score+select+stage+gather+attend (full lsa_decode_step)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_us": {k: round(avg[k] * 1e3, 2) for k in KERNELS},
+        "score_attend_hbm_frac": round(sa_frac, 4),
+        "hit_rate": round(hits / max(1, hits + misses), 4),
+        "parity": parity,
+        "fm_score_src": src_hash,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,293 @@
+/*
+ * liblsa -- the per-decode-step hot path of Lookahead Sparse Attention (LSA)
+ * and of the KV swap around it, for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step is: score every compressed indexer key with the memory
+ * indexers (lsa_score), keep the query-critical chunks (lsa_select), stage
+ * them into a bounded slot pool managed as an LRU over a larger cold pool
+ * (lsa_stage), and attend over a sliding window plus the staged entries
+ * (lsa_attend).  lsa_decode_step chains the four for a stack of sparse layers.
+ *
+ * Sources (cited by title and section; the pages are public web text):
+ *   [P1] PocketLLM, "FlashMemory 1M 上下文显存优化使用文档": overview (two-tier
+ *        KV cache), configuration flags, GPU_CHUNKS / PINNED_MIB tuning
+ *        (closed-form sizing), expected logs, troubleshooting (errors 1-4,
+ *        swap auto-disable), technical details (architecture, memory layout,
+ *        GgufKvSwapLayerState, swap-in and store flows).
+ *   [P2] article on "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long
+ *        Context via Lookahead Sparse Attention": LSA section (memory indexer
+ *        queries vs compressed indexer keys; sigmoid threshold selector), the
+ *        placement section (three indexers, OR-mode routing).
+ *   [P4] "KVSwap：大模型推理中的KV缓存优化技术": §2.2 grouped KV prediction,
+ *        §2.3 low-rank K, §3.2 ring buffer of 400 groups.
+ *
+ * Conventions for every entry point:
+ *   - Pointers documented "device" are HBM addresses on the current HIP device
+ *     (e.g. torch tensors' data_ptr()); "host" pointers are ordinary CPU memory.
+ *     The caller owns every pointer it passes; liblsa owns only what its own
+ *     *_create functions allocate (context workspace, pool tables, cold pools).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns; outputs are valid once that stream has synchronised.
+ *     Counts produced on the device stay on the device.
+ *   - Every call returns an lsa_status.  On failure nothing is enqueued and
+ *     lsa_last_error() (thread-local) holds a one-line explanation.
+ *   - No entry point calls hipMalloc/hipFree on the step path, except that a
+ *     context grows its workspace the first time a larger problem is seen
+ *     (lsa_ctx_reserve pre-sizes it).
+ *   - Scores must not be NaN.  Arguments outside the documented ranges return
+ *     LSA_ERR_INVALID_ARG, unsupported shapes LSA_ERR_UNSUPPORTED.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSA_ABI_VERSION 1
+#define LSA_MAX_LAYERS 16
+#define LSA_MAX_BATCH 64
+
+typedef enum lsa_status {
+    LSA_OK = 0,
+    LSA_ERR_INVALID_ARG = 1,
+    LSA_ERR_SLOTS_LT_TOPK = 2,   /* [P1] error 2: GPU_CHUNKS must be >= index_topk */
+    LSA_ERR_PINNED_CAP = 3,      /* [P1] error 3: pinned cache exceeds cap */
+    LSA_ERR_NOT_STORED = 4,      /* [P1] error 4: selected chunk before it was stored */
+    LSA_ERR_HIP = 5,             /* a HIP runtime call failed */
+    LSA_ERR_NO_MEMORY = 6,       /* device or pinned allocation failed */
+    LSA_ERR_UNSUPPORTED = 7      /* a valid shape this build has no kernel for */
+} lsa_status;
+
+typedef enum lsa_dtype { LSA_F32 = 0, LSA_BF16 = 1, LSA_F16 = 2 } lsa_dtype;
+typedef enum lsa_ensemble { LSA_ENSEMBLE_MAX = 0, LSA_ENSEMBLE_MEAN = 1 } lsa_ensemble;
+typedef enum lsa_select_mode { LSA_SELECT_TOPK = 0, LSA_SELECT_THRESHOLD = 1 } lsa_select_mode;
+typedef enum lsa_cold_kind { LSA_COLD_HBM = 0, LSA_COLD_HOST = 1 } lsa_cold_kind;
+
+typedef void* lsa_stream_t; /* hipStream_t */
+
+/* ----------------------------------------------------------- closed forms --
+ * [P1] PINNED_MIB tuning: compressed_cap = (context_length + ratio - 1) / ratio;
+ * required pinned bytes = sum over sparse layers of compressed_cap * kv_dim *
+ * sizeof(element).  [P1] expected logs: max_capacity = window + gpu_chunks.
+ * Invalid arguments (ctx < 0, ratio <= 0, ...) give 0 / -1. */
+int64_t  lsa_compressed_cap(int64_t ctx, int32_t ratio);
+uint64_t lsa_pinned_bytes(int64_t ctx, const int32_t* ratios /* host [n_layers] */,
+                          int32_t n_layers, int32_t kv_dim, lsa_dtype dtype);
+int32_t  lsa_max_capacity(int32_t window, int32_t gpu_chunks);
+/* [P1] PINNED_MIB: LSA_ERR_PINNED_CAP, with "required_mib=X cap_mib=Y" in
+ * lsa_last_error(), when the layers' pinned bytes exceed cap_bytes. */
+lsa_status lsa_check_pinned(int64_t ctx, const int32_t* ratios, int32_t n_layers, int32_t kv_dim,
+                            lsa_dtype dtype, uint64_t cap_bytes);
+/* logit threshold used by threshold selection: the largest float t_f with
+ * t_f <= ln(tau / (1 - tau)); an entry passes when score > t_f, i.e. exactly
+ * when sigmoid(score) > tau over the reals.  NaN for tau outside (0, 1). */
+float lsa_threshold_logit(double tau);
+
+const char* lsa_status_string(lsa_status s);
+const char* lsa_last_error(void);
+int32_t     lsa_abi_version(void);
+
+/* ---------------------------------------------------------------- context --
+ * Owns the device workspace of lsa_select / lsa_attend / lsa_decode_step and
+ * optional per-kernel timing events.  One context per device and thread of
+ * use; calls on one context must not overlap.  `device` becomes current. */
+typedef struct lsa_ctx lsa_ctx;
+lsa_status lsa_ctx_create(lsa_ctx** out, int32_t device);
+void       lsa_ctx_destroy(lsa_ctx* ctx);
+lsa_status lsa_ctx_reserve(lsa_ctx* ctx, uint64_t bytes);
+
+/* Kernel timing: when on, lsa_decode_step / lsa_score / lsa_attend record HIP
+ * events around their launches on the launch stream.  lsa_ctx_timing_read
+ * waits for the last event, returns for each kernel kind (LSA_K_*) the summed
+ * milliseconds and launch count since the previous read, and resets them. */
+enum { LSA_K_SCORE = 0, LSA_K_SELECT = 1, LSA_K_STAGE = 2, LSA_K_GATHER = 3,
+       LSA_K_ATTEND = 4, LSA_K_COMBINE = 5, LSA_K_COUNT = 6 };
+lsa_status lsa_ctx_set_timing(lsa_ctx* ctx, int32_t on);
+lsa_status lsa_ctx_timing_read(lsa_ctx* ctx, double* ms /* host [LSA_K_COUNT] */,
+                               int64_t* launches /* host [LSA_K_COUNT] */);
+
+/* ------------------------------------------------------------------ score --
+ * [P1] architecture: 3 scorers read the shared indexer keys and are combined
+ * by an ensemble (FLASHMEMORY_ENSEMBLE=max|mean); [P2] LSA section: memory
+ * indexer queries are matched against the compressed indexer keys by dot
+ * product.  For every sequence b and valid entry j < n_valid[b]:
+ *     s_i[j]   = sum_h w[b,i,h] * ReLU( q[b,i,h,:] . keys[b,j,:] )   (fp32)
+ *     score[j] = max_i s_i[j]                (LSA_ENSEMBLE_MAX), or
+ *                (sum_i s_i[j]) / n_idx      (LSA_ENSEMBLE_MEAN, one IEEE division)
+ * with -0 written as +0.  Accumulation is fp32 in an unspecified order, so the
+ * result is exact whenever every partial sum is representable in fp32.
+ *   keys   device [batch][n_keys][dk], key_dtype LSA_F32 or LSA_BF16, rows contiguous
+ *   n_valid host [batch] (0 <= n_valid[b] <= n_keys) or NULL for n_keys each
+ *   q      device f32 [batch][n_idx][heads][dk]
+ *   w      device f32 [batch][n_idx][heads]
+ *   scores device f32 [batch][n_keys]; entries j >= n_valid[b] are not written
+ * Supported: dk in {32, 64, 128}; 1 <= n_idx <= 4; 1 <= heads <= 8;
+ * 1 <= batch <= LSA_MAX_BATCH; n_keys * dk * sizeof(key) < 2^32 per sequence. */
+lsa_status lsa_score(const void* keys, lsa_dtype key_dtype, int32_t batch, int64_t n_keys,
+                     const int64_t* n_valid, int32_t dk, const float* q, const float* w,
+                     int32_t n_idx, int32_t heads, lsa_ensemble ensemble, float* scores,
+                     lsa_stream_t stream);
+
+/* ----------------------------------------------------------------- select --
+ * [P1] "global top-k (512 chunks)" with index_topk = global_keep_cap; [P2]
+ * Recall / Threshold Selector: recall entries whose sigmoid(score) exceeds
+ * tau.  Order: higher score first, lower index first among equal scores
+ * (+0 and -0 are equal).
+ *   LSA_SELECT_TOPK:      the first min(k, n_valid) entries of that order;
+ *   LSA_SELECT_THRESHOLD: the entries with sigmoid(score) > tau (computed as
+ *                         score > lsa_threshold_logit(tau)); if more than k
+ *                         pass, the first k of them in the order.
+ *   scores device f32 [n_seg][n_keys]; n_valid host [n_seg] or NULL (for
+ *          n_seg > LSA_MAX_BATCH the values must all be equal)
+ *   sel    device i32 [n_seg][k]: selected indices ascending, then -1 padding
+ *   count  device i32 [n_seg]: number selected
+ * Supported: 1 <= k <= 4096, n_seg >= 1, n_keys <= 2^31 - 1 and
+ * ceil(n_keys / 32768) * k <= 32768; tau in (0, 1) for threshold mode. */
+lsa_status lsa_select(lsa_ctx* ctx, const float* scores, int32_t n_seg, int64_t n_keys,
+                      const int64_t* n_valid, lsa_select_mode mode, int32_t k, double tau,
+                      int32_t* sel, int32_t* count, lsa_stream_t stream);
+
+/* ------------------------------------------------------------------ pools --
+ * [P1] technical details, GgufKvSwapLayerState and swap-in flow: per sparse
+ * layer, all compressed rows live in a cold pool ([P1]: pinned host; here also
+ * HBM) and `gpu_chunks` GPU slots stage the selected ones, managed as an LRU.
+ * One pool serves one sparse layer for `batch` independent sequences.
+ *
+ * kv_buf is the caller's device buffer [batch][lsa_pool_rows(desc)][kv_dim]
+ * (sequence b at element offset b * kv_stride_b): rows 0..window-1 hold the
+ * sliding window (the caller writes them), the rest are slots.  A layer with
+ * compressed_cap <= gpu_chunks is fully resident ([P1] troubleshooting,
+ * swap auto-disable): its rows window + j hold entry j and nothing swaps.
+ *
+ * lsa_pool_create errors: gpu_chunks < topk without allow_topk_reduction ->
+ * LSA_ERR_SLOTS_LT_TOPK ([P1] error 2); a host cold pool above
+ * pinned_cap_bytes (0 = no cap) -> LSA_ERR_PINNED_CAP ([P1] error 3).
+ * With allow_topk_reduction and gpu_chunks < topk, at most gpu_chunks chunks
+ * may be staged per step ([P1] TEST_ALLOW_TOPK_REDUCTION). */
+typedef struct lsa_pool_desc {
+    int64_t ctx;                /* context length in tokens */
+    int32_t ratio;              /* this layer's compression ratio (a multiple of the source ratio) */
+    int32_t window;             /* sliding-window rows, [P1]: 128 */
+    int32_t gpu_chunks;         /* staging slots S, [P1]: 512 or 1024; S >= 1, and S <= 4096 when it swaps */
+    int32_t topk;               /* index_topk the selection may produce, <= 1024 */
+    int32_t kv_dim;             /* D, [P1]: 512 */
+    int32_t batch;              /* sequences, 1 <= batch <= LSA_MAX_BATCH */
+    lsa_dtype dtype;            /* row storage: LSA_F32 or LSA_BF16 */
+    lsa_cold_kind cold;         /* where the full store lives */
+    uint64_t pinned_cap_bytes;  /* [P1] PINNED_MIB, 0 = unlimited */
+    int32_t allow_topk_reduction;
+    void* kv_buf;               /* device, caller-owned */
+    int64_t kv_stride_b;        /* elements between sequences of kv_buf */
+} lsa_pool_desc;
+
+typedef struct lsa_pool_stats_t {
+    uint64_t hits, misses;      /* [P1] gguf_kv_swap_stats hits= misses= */
+    uint64_t h2d_bytes;         /* rows moved cold -> slots */
+    uint64_t d2h_bytes;         /* rows stored into the pool */
+    int64_t compressed_cap;
+    int32_t swap_enabled;       /* 0: fully resident ([P1] gguf_kv_swap=0 reason=...) */
+    int32_t resident;           /* slots in use, summed over sequences */
+} lsa_pool_stats_t;
+
+typedef struct lsa_pool lsa_pool;
+/* rows per sequence that kv_buf must hold: window + (swap ? gpu_chunks : cap) */
+int64_t    lsa_pool_rows(const lsa_pool_desc* desc);
+lsa_status lsa_pool_create(lsa_pool** out, const lsa_pool_desc* desc);
+void       lsa_pool_destroy(lsa_pool* pool);
+/* [P1] store flow: copy `count` rows (host or device memory, [count][kv_dim]
+ * in the pool dtype) into entries first..first+count-1 of sequence b and mark
+ * them stored; a staged copy of such an entry is refreshed.  Asynchronous. */
+lsa_status lsa_pool_store(lsa_pool* pool, int32_t b, int64_t first, int64_t count,
+                          const void* rows, lsa_stream_t stream);
+/* Host address of the pinned cold pool of sequence b (LSA_COLD_HOST only),
+ * [cap][kv_dim]; rows written there directly must be declared with
+ * lsa_pool_mark_stored. NULL otherwise. */
+void*      lsa_pool_host_rows(lsa_pool* pool, int32_t b);
+lsa_status lsa_pool_mark_stored(lsa_pool* pool, int32_t b, int64_t first, int64_t count,
+                                lsa_stream_t stream);
+/* empty every slot (stored rows stay stored) and zero hits/misses/h2d. */
+lsa_status lsa_pool_reset(lsa_pool* pool, lsa_stream_t stream);
+/* Synchronises `stream`, then reports counters.  Returns LSA_ERR_NOT_STORED
+ * ([P1] error 4) if a step since the last call selected an entry that was never
+ * stored (such an entry is staged from whatever its cold row holds). */
+lsa_status lsa_pool_stats(lsa_pool* pool, lsa_pool_stats_t* out, lsa_stream_t stream);
+/* Test hook ([P1] KV_SWAP_VALIDATE): copies the slot table of sequence b to
+ * host: slot_logical [gpu_chunks] (-1 = unused) and lru [gpu_chunks] (slot ids
+ * from most to least recently used); returns the number of used slots in
+ * *n_used.  Synchronises `stream`. */
+lsa_status lsa_pool_state(lsa_pool* pool, int32_t b, int32_t* slot_logical, int32_t* lru,
+                          int32_t* n_used, lsa_stream_t stream);
+
+/* ------------------------------------------------------------------ stage --
+ * [P1] swap-in flow: for the chunks selected on the ratio-src_ratio source
+ * layer, map them to this pool's ratio (entry j -> floor(j * src_ratio /
+ * ratio), duplicates removed, ascending), then per entry: a hit moves it to
+ * the LRU front; a miss takes the lowest unused slot, else evicts the least
+ * recently used one, and its row is copied cold -> slot.  Hits are handled
+ * before misses, each in ascending order, so no selected chunk is evicted in
+ * the step that selects it.  Writes the physical row list the attention reads:
+ * phys[b][0..window-1] = 0..window-1, then window + slot of each entry in
+ * ascending entry order; n_rows[b] = window + entries.
+ *   sel   device i32 [batch][sel_stride] ascending source-layer indices
+ *   count device i32 [batch]
+ *   phys  device i32 [batch][phys_stride], phys_stride >= window + sel_stride
+ *   n_rows device i32 [batch]
+ * sel_stride must not exceed the pool's gpu_chunks when it swaps (it is the
+ * most entries a step can stage), nor 1024. */
+lsa_status lsa_stage(lsa_pool* pool, const int32_t* sel, const int32_t* count, int32_t sel_stride,
+                     int32_t src_ratio, int32_t* phys, int32_t phys_stride, int32_t* n_rows,
+                     lsa_stream_t stream);
+
+/* ----------------------------------------------------------------- attend --
+ * [P1] overview "Two-tier KV cache" and indexed_cached_attention (window +
+ * selected): per sequence b and head h, with rows r = phys[b][0..n_rows[b]-1]
+ * of kv (each row serves as key and value):
+ *     out[b,h,:] = sum_r softmax_r(scale * q[b,h,:] . kv[r,:]) * kv[r,:]
+ * accumulated in fp32; out = 0 when n_rows[b] == 0.  The split over rows
+ * depends only on n_rows[b], so the result does not depend on which physical
+ * rows hold the entries (swap on and off give identical bits).
+ *   q    device f32 [batch][hq][kv_dim];  out device f32 [batch][hq][kv_dim]
+ *   kv   device [batch] x rows x kv_dim (dtype F32 or BF16), sequence b at
+ *        element offset b * kv_stride_b
+ *   kv_rows rows per sequence of kv: phys entries outside [0, kv_rows) read
+ *        as zero rows (a malformed list cannot read past the buffer)
+ *   phys device i32 [batch][phys_stride]; n_rows device i32 [batch], values
+ *        clamped to [0, phys_stride]
+ * Supported: 1 <= hq <= 16, kv_dim in {128, 256, 512}, 1 <= batch <= LSA_MAX_BATCH. */
+lsa_status lsa_attend(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dtype,
+                      int64_t kv_stride_b, int64_t kv_rows, const int32_t* phys,
+                      int32_t phys_stride, const int32_t* n_rows, int32_t batch, int32_t hq,
+                      int32_t kv_dim, float scale, float* out, lsa_stream_t stream);
+
+/* ------------------------------------------------------------ decode step --
+ * [P1] architecture overview: score once on the shared source layer, one
+ * global selection, then for every sparse layer the swap-in and the attention
+ * over window + selected.  All layers' pools must share `batch`. */
+typedef struct lsa_step_desc {
+    /* scoring of the shared source layer (see lsa_score) */
+    const void* keys; lsa_dtype key_dtype; int64_t n_keys; const int64_t* n_valid; int32_t dk;
+    const float* q_idx; const float* w_idx; int32_t n_idx; int32_t heads; lsa_ensemble ensemble;
+    /* selection (see lsa_select); k is lowered to the smallest swapping pool's
+       gpu_chunks when that pool allows top-k reduction */
+    lsa_select_mode mode; int32_t k; double tau; int32_t src_ratio;
+    float* scores;              /* device f32 [batch][n_keys] */
+    int32_t* sel;               /* device i32 [batch][k] */
+    int32_t* count;             /* device i32 [batch] */
+    /* sparse layers */
+    int32_t n_layers;           /* 1..LSA_MAX_LAYERS */
+    lsa_pool* const* pools;     /* host [n_layers] */
+    const float* q_attn;        /* device f32 [n_layers][batch][hq][kv_dim] */
+    float* out;                 /* device f32 [n_layers][batch][hq][kv_dim] */
+    int32_t* phys;              /* device i32 [n_layers][batch][window + k] or NULL (workspace) */
+    int32_t* n_rows;            /* device i32 [n_layers][batch] or NULL (workspace) */
+    int32_t hq; float scale; int32_t batch;
+} lsa_step_desc;
+lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSA_H */

@@ -1,0 +1,212 @@
+// kv_stage: ratio map + LRU slot assignment + gather of missed rows.
+//
+// [P1] technical details, swap-in flow of gguf_kv_swap_in_selected: each
+// selected logical chunk is looked up in the slot table; a hit is moved to the
+// LRU front and counted; a miss evicts the LRU back, takes its slot, has its
+// row copied from the cold pool, and is counted; then every chunk's index is
+// rewritten to the physical row window + slot.  [P1] store flow / error 4: a
+// chunk that was never stored must not be selected.  [P1] troubleshooting: a
+// layer whose compressed_cap <= gpu_chunks does not swap (rows = window + j).
+//
+// Readings shared with the CPU oracle: a source chunk j maps to chunk
+// floor(j * src_ratio / ratio) of this layer (duplicates dropped); hits are
+// handled before misses, each in ascending chunk order; a miss takes the
+// lowest never-used slot before it evicts.
+//
+// Design (gfx950): one 1024-thread workgroup per (layer, sequence) replaces
+// the host-side std::list walk with prefix sums.  The LRU list is kept as an
+// array `lru` of used slots, most recent first.  With h hits and m misses in
+// a step, the page's sequential loop leaves the list as
+//     [misses, last processed first] [hits, last processed first]
+//     [untouched slots in their old order, minus the evicted ones]
+// and the evicted slots are exactly the last (m - free) untouched entries of
+// the old list, taken from the back.  Slots are handed out lowest-first and
+// never freed, so the unused ones are always used..S-1.  A second kernel with
+// one wave per missed row copies cold -> slot (HBM cold pools, or pinned host
+// memory read directly over PCIe, so no host round trip sits in the step).
+#include "lsa_internal.hpp"
+
+namespace lsa {
+
+namespace {
+
+constexpr int kNT = 1024;
+constexpr int kMaxSlots = 4096;
+
+__global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
+    const StageLayer& L = a.L[blockIdx.y];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+
+    __shared__ int s_scan[kNT / 64 + 1];
+    __shared__ int s_sel[kNT];
+    __shared__ int s_victim[kNT];
+    __shared__ int s_order[kMaxSlots];
+    __shared__ uint8_t s_hit[kMaxSlots];
+
+    // 1. source selection -> this layer's ascending unique chunk list
+    int n_src = L.count[b];
+    n_src = n_src < 0 ? 0 : (n_src > L.sel_stride ? L.sel_stride : n_src);
+    const int32_t* sel = L.sel + (int64_t)b * L.sel_stride;
+    bool keep = false;
+    int m = -1;
+    if (tid < n_src) {
+        m = (int)((int64_t)sel[tid] * L.src_ratio / L.ratio);
+        keep = tid == 0 || m != (int)((int64_t)sel[tid - 1] * L.src_ratio / L.ratio);
+    }
+    int n_l;
+    const int pos = block_excl_scan<kNT>(keep ? 1 : 0, s_scan, &n_l);
+    if (keep) s_sel[pos] = m;
+    __syncthreads();
+
+    int32_t* phys = L.phys + (int64_t)b * L.phys_stride;
+    for (int r = tid; r < L.window; r += kNT) phys[r] = r;
+    if (tid == 0) L.n_rows[b] = L.window + n_l;
+    // entries outside [0, cap) (a malformed selection) are flagged and read
+    // window row 0 instead, so no access leaves the pool's buffers
+    int l = tid < n_l ? s_sel[tid] : -1;
+    if (tid < n_l && (l < 0 || l >= L.cap)) {
+        atomicOr(&L.meta[b * 4 + 1], 2);
+        phys[L.window + tid] = 0;
+        l = -1;
+    }
+    if (l >= 0 && !L.ready[(int64_t)b * L.cap + l]) atomicOr(&L.meta[b * 4 + 1], 1);
+
+    if (!L.swap) {
+        if (l >= 0) phys[L.window + tid] = L.window + l;
+        if (tid == 0) L.n_miss[b] = 0;
+        return;
+    }
+
+    int32_t* slot_of = L.slot_of + (int64_t)b * L.cap;
+    int32_t* logical_of = L.logical_of + (int64_t)b * L.S;
+    int32_t* lru = L.lru + (int64_t)b * L.S;
+    const int S = L.S;
+    const int n_used = L.meta[b * 4 + 0];
+
+    for (int i = tid; i < S; i += kNT) s_hit[i] = 0;
+    for (int i = tid; i < n_used; i += kNT) s_order[i] = lru[i];
+    __syncthreads();
+
+    // 2. hits and misses, ranked in ascending chunk order
+    int slot = l >= 0 ? slot_of[l] : -1;
+    const bool hit = slot >= 0;
+    const bool miss = l >= 0 && !hit;
+    if (hit) s_hit[slot] = 1;
+    int tot;
+    const int packed = block_excl_scan<kNT>((hit ? 1 : 0) | (miss ? 1 << 16 : 0), s_scan, &tot);
+    const int hit_rank = packed & 0xFFFF, miss_rank = packed >> 16;
+    const int n_hit = tot & 0xFFFF, n_miss = tot >> 16;
+    const int free_slots = S - n_used;
+    const int n_evict = n_miss > free_slots ? n_miss - free_slots : 0;
+
+    // 3. untouched used slots in old list order; the last n_evict are evicted
+    constexpr int kPer = kMaxSlots / kNT;
+    bool untouched[kPer];
+    int c_untouched = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int p = tid * kPer + q;
+        untouched[q] = p < n_used && s_hit[s_order[p]] == 0;
+        c_untouched += untouched[q] ? 1 : 0;
+    }
+    int n_untouched;
+    int before = block_excl_scan<kNT>(c_untouched, s_scan, &n_untouched);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        if (!untouched[q]) continue;
+        const int p = tid * kPer + q;
+        const int after = n_untouched - before - 1;
+        if (after < n_evict) {
+            s_victim[after] = s_order[p];           // victim 0 = least recently used
+        } else {
+            lru[n_miss + n_hit + before] = s_order[p];
+        }
+        ++before;
+    }
+    __syncthreads();
+
+    // 4. slots for the misses; the evicted chunks leave the table
+    if (miss) slot = miss_rank < free_slots ? n_used + miss_rank : s_victim[miss_rank - free_slots];
+    int old = -1;
+    if (tid < n_evict) old = logical_of[s_victim[tid]];
+    __syncthreads();
+    if (old >= 0) slot_of[old] = -1;
+    if (miss) {
+        slot_of[l] = slot;
+        logical_of[slot] = l;
+        int32_t* mrec = L.miss + ((int64_t)b * L.sel_stride + miss_rank) * 2;
+        mrec[0] = l;
+        mrec[1] = slot;
+        lru[n_miss - 1 - miss_rank] = slot;
+    }
+    if (hit) lru[n_miss + n_hit - 1 - hit_rank] = slot;
+    if (l >= 0) phys[L.window + tid] = L.window + slot;
+    if (tid == 0) {
+        L.meta[b * 4 + 0] = n_used + (n_miss < free_slots ? n_miss : free_slots);
+        L.n_miss[b] = n_miss;
+        uint64_t* st = L.stats + (int64_t)b * 4;
+        st[0] += (uint64_t)n_hit;
+        st[1] += (uint64_t)n_miss;
+        st[2] += (uint64_t)n_miss * (uint64_t)L.row_bytes;
+    }
+}
+
+constexpr int kGatherWaves = 4;
+
+// one wave per missed row: cold[entry] -> kv[window + slot]
+__global__ __launch_bounds__(kGatherWaves * 64) void kv_gather_kernel(const StageArgs a) {
+    const StageLayer& L = a.L[blockIdx.z];
+    if (!L.swap) return;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = blockIdx.x * kGatherWaves + wave;
+    if (m >= L.n_miss[b]) return;
+    const int32_t* mrec = L.miss + ((int64_t)b * L.sel_stride + m) * 2;
+    const int l = mrec[0], slot = mrec[1];
+    const char* src = static_cast<const char*>(L.cold) + b * L.cold_stride_b + (int64_t)l * L.row_bytes;
+    char* dst = static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes + (int64_t)(L.window + slot) * L.row_bytes;
+    for (int off = lane * 16; off < L.row_bytes; off += 64 * 16)
+        *reinterpret_cast<f32x4*>(dst + off) = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + off));
+}
+
+__global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L, int b, int64_t first, int64_t count) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t i = (int64_t)blockIdx.x * 4 + wave;
+    if (i >= count) return;
+    const int64_t l = first + i;
+    const int slot = L.slot_of[(int64_t)b * L.cap + l];
+    if (slot < 0) return;
+    const char* src = static_cast<const char*>(L.cold) + b * L.cold_stride_b + l * L.row_bytes;
+    char* dst = static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes + (int64_t)(L.window + slot) * L.row_bytes;
+    for (int off = lane * 16; off < L.row_bytes; off += 64 * 16)
+        *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(src + off);
+}
+
+}  // namespace
+
+hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(kv_stage_kernel, dim3(a.batch, a.n_layers), dim3(kNT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_gather(const StageArgs& a, hipStream_t s) {
+    int max_stride = 0, any_swap = 0;
+    for (int i = 0; i < a.n_layers; ++i) {
+        if (a.L[i].sel_stride > max_stride) max_stride = a.L[i].sel_stride;
+        any_swap |= a.L[i].swap;
+    }
+    if (!any_swap || max_stride == 0) return hipSuccess;
+    const dim3 grid((max_stride + kGatherWaves - 1) / kGatherWaves, a.batch, a.n_layers);
+    hipLaunchKernelGGL(kv_gather_kernel, grid, dim3(kGatherWaves * 64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_refresh_staged(const StageLayer& L, int b, int64_t first, int64_t count, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((count + 3) / 4));
+    hipLaunchKernelGGL(refresh_staged_kernel, grid, dim3(256), 0, s, L, b, first, count);
+    return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -1,0 +1,827 @@
+// liblsa host side: the C ABI of include/lsa.h -- argument validation, the
+// page's closed forms and error conditions, context workspace, slot pools,
+// per-kernel timing, and the decode-step composition.  All arithmetic of the
+// step runs in the kernels of fm_score.hip, fm_select.hip, kv_stage.hip and
+// lsa_attend.hip.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "lsa_internal.hpp"
+
+using namespace lsa;
+
+namespace {
+
+thread_local std::string g_err;
+
+lsa_status fail(lsa_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+#define HIPTRY(call)                                                                     \
+    do {                                                                                 \
+        hipError_t e_ = (call);                                                          \
+        if (e_ != hipSuccess) return fail(LSA_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+int elem_bytes(lsa_dtype d) { return d == LSA_F32 ? 4 : 2; }
+bool row_dtype_ok(lsa_dtype d) { return d == LSA_F32 || d == LSA_BF16; }
+
+int n_cu_current() {
+    static int cache[128] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 128) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+// ------------------------------------------------------------------ context
+struct lsa_ctx {
+    int device = 0;
+    int n_cu = 256;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    bool timing = false;
+    struct Pending {
+        int kind;
+        hipEvent_t a, b;
+    };
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> spare;
+};
+
+namespace {
+
+lsa_status ws_ensure(lsa_ctx* c, size_t bytes) {
+    if (bytes <= c->ws_bytes) return LSA_OK;
+    size_t want = align_up(bytes, (size_t)1 << 20);
+    if (c->ws) {
+        HIPTRY(hipDeviceSynchronize());
+        HIPTRY(hipFree(c->ws));
+        c->ws = nullptr;
+        c->ws_bytes = 0;
+    }
+    if (hipMalloc(&c->ws, want) != hipSuccess) {
+        (void)hipGetLastError();
+        c->ws = nullptr;
+        return fail(LSA_ERR_NO_MEMORY, "workspace allocation of %zu bytes failed", want);
+    }
+    c->ws_bytes = want;
+    return LSA_OK;
+}
+
+hipEvent_t ev_take(lsa_ctx* c) {
+    if (!c->spare.empty()) {
+        hipEvent_t e = c->spare.back();
+        c->spare.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Records an event before construction and one at end(); nothing when timing is off.
+struct Timed {
+    lsa_ctx* c;
+    int kind;
+    hipStream_t s;
+    hipEvent_t a = nullptr;
+    Timed(lsa_ctx* c_, int kind_, hipStream_t s_) : c(c_), kind(kind_), s(s_) {
+        if (c && c->timing) {
+            a = ev_take(c);
+            if (a) (void)hipEventRecord(a, s);
+        }
+    }
+    void end() {
+        if (!a) return;
+        hipEvent_t b = ev_take(c);
+        if (!b) return;
+        (void)hipEventRecord(b, s);
+        c->pending.push_back({kind, a, b});
+        a = nullptr;
+    }
+};
+
+}  // namespace
+
+// ------------------------------------------------------------------- pools
+struct lsa_pool {
+    lsa_pool_desc d;
+    int device = 0;
+    int64_t cap = 0;
+    int swap = 0;
+    int row_bytes = 0;
+    int64_t rows_per_seq = 0;
+    void* tables = nullptr;
+    int32_t* slot_of = nullptr;
+    int32_t* logical_of = nullptr;
+    int32_t* lru = nullptr;
+    int32_t* meta = nullptr;
+    uint64_t* stats = nullptr;
+    uint8_t* ready = nullptr;
+    int32_t* miss = nullptr;
+    int32_t* n_miss = nullptr;
+    void* cold_dev = nullptr;   // device address of the cold pool (HBM, or mapped pinned host)
+    void* cold_host = nullptr;  // host address when pinned
+    int64_t cold_stride_b = 0;  // bytes
+    uint64_t d2h_bytes = 0;
+};
+
+extern "C" {
+
+// ------------------------------------------------------------ closed forms
+int64_t lsa_compressed_cap(int64_t ctx, int32_t ratio) {
+    if (ctx < 0 || ratio <= 0) return -1;
+    return (ctx + ratio - 1) / ratio;
+}
+
+uint64_t lsa_pinned_bytes(int64_t ctx, const int32_t* ratios, int32_t n_layers, int32_t kv_dim,
+                          lsa_dtype dtype) {
+    if (!ratios || n_layers < 0 || kv_dim <= 0 || ctx < 0) return 0;
+    uint64_t tot = 0;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const int64_t cap = lsa_compressed_cap(ctx, ratios[l]);
+        if (cap < 0) return 0;
+        tot += (uint64_t)cap * (uint64_t)kv_dim * (uint64_t)elem_bytes(dtype);
+    }
+    return tot;
+}
+
+int32_t lsa_max_capacity(int32_t window, int32_t gpu_chunks) {
+    if (window < 0 || gpu_chunks < 0) return -1;
+    return window + gpu_chunks;
+}
+
+lsa_status lsa_check_pinned(int64_t ctx, const int32_t* ratios, int32_t n_layers, int32_t kv_dim,
+                            lsa_dtype dtype, uint64_t cap_bytes) {
+    if (!ratios || n_layers <= 0 || kv_dim <= 0 || ctx < 0)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_check_pinned: invalid arguments");
+    const uint64_t need = lsa_pinned_bytes(ctx, ratios, n_layers, kv_dim, dtype);
+    if (need > cap_bytes)
+        return fail(LSA_ERR_PINNED_CAP, "pinned cache exceeds cap: required_mib=%llu cap_mib=%llu",
+                    (unsigned long long)((need + (1u << 20) - 1) >> 20),
+                    (unsigned long long)(cap_bytes >> 20));
+    return LSA_OK;
+}
+
+float lsa_threshold_logit(double tau) {
+    if (!(tau > 0.0 && tau < 1.0)) return NAN;
+    const double t = log(tau / (1.0 - tau));
+    float tf = (float)t;
+    if ((double)tf > t) tf = nextafterf(tf, -INFINITY);
+    return tf;
+}
+
+const char* lsa_status_string(lsa_status s) {
+    switch (s) {
+        case LSA_OK: return "ok";
+        case LSA_ERR_INVALID_ARG: return "invalid argument";
+        case LSA_ERR_SLOTS_LT_TOPK: return "gpu_chunks must be >= index_topk";
+        case LSA_ERR_PINNED_CAP: return "pinned cache exceeds cap";
+        case LSA_ERR_NOT_STORED: return "selected chunk before it was stored";
+        case LSA_ERR_HIP: return "HIP runtime error";
+        case LSA_ERR_NO_MEMORY: return "out of memory";
+        case LSA_ERR_UNSUPPORTED: return "unsupported shape";
+    }
+    return "unknown status";
+}
+
+const char* lsa_last_error(void) { return g_err.c_str(); }
+int32_t lsa_abi_version(void) { return LSA_ABI_VERSION; }
+
+// ----------------------------------------------------------------- context
+lsa_status lsa_ctx_create(lsa_ctx** out, int32_t device) {
+    if (!out) return fail(LSA_ERR_INVALID_ARG, "lsa_ctx_create: out is NULL");
+    *out = nullptr;
+    int n = 0;
+    HIPTRY(hipGetDeviceCount(&n));
+    if (device < 0 || device >= n) return fail(LSA_ERR_INVALID_ARG, "device %d of %d", device, n);
+    HIPTRY(hipSetDevice(device));
+    lsa_ctx* c = new lsa_ctx;
+    c->device = device;
+    c->n_cu = n_cu_current();
+    *out = c;
+    return LSA_OK;
+}
+
+void lsa_ctx_destroy(lsa_ctx* c) {
+    if (!c) return;
+    (void)hipDeviceSynchronize();
+    if (c->ws) (void)hipFree(c->ws);
+    for (auto& p : c->pending) {
+        (void)hipEventDestroy(p.a);
+        (void)hipEventDestroy(p.b);
+    }
+    for (auto e : c->spare) (void)hipEventDestroy(e);
+    delete c;
+}
+
+lsa_status lsa_ctx_reserve(lsa_ctx* c, uint64_t bytes) {
+    if (!c) return fail(LSA_ERR_INVALID_ARG, "ctx is NULL");
+    return ws_ensure(c, (size_t)bytes);
+}
+
+lsa_status lsa_ctx_set_timing(lsa_ctx* c, int32_t on) {
+    if (!c) return fail(LSA_ERR_INVALID_ARG, "ctx is NULL");
+    c->timing = on != 0;
+    return LSA_OK;
+}
+
+lsa_status lsa_ctx_timing_read(lsa_ctx* c, double* ms, int64_t* launches) {
+    if (!c || !ms || !launches) return fail(LSA_ERR_INVALID_ARG, "lsa_ctx_timing_read: NULL argument");
+    for (int k = 0; k < LSA_K_COUNT; ++k) {
+        ms[k] = 0.0;
+        launches[k] = 0;
+    }
+    if (!c->pending.empty()) HIPTRY(hipEventSynchronize(c->pending.back().b));
+    for (auto& p : c->pending) {
+        float t = 0.f;
+        HIPTRY(hipEventElapsedTime(&t, p.a, p.b));
+        ms[p.kind] += t;
+        launches[p.kind] += 1;
+        c->spare.push_back(p.a);
+        c->spare.push_back(p.b);
+    }
+    c->pending.clear();
+    return LSA_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ score
+namespace {
+
+lsa_status score_args(const void* keys, lsa_dtype key_dtype, int32_t batch, int64_t n_keys,
+                      const int64_t* n_valid, int32_t dk, const float* q, const float* w, int32_t n_idx,
+                      int32_t heads, lsa_ensemble ens, float* scores, ScoreArgs* a) {
+    if (batch < 1 || batch > LSA_MAX_BATCH) return fail(LSA_ERR_INVALID_ARG, "batch %d not in [1, %d]", batch, LSA_MAX_BATCH);
+    if (n_keys < 0 || n_keys > INT32_MAX) return fail(LSA_ERR_INVALID_ARG, "n_keys %lld out of range", (long long)n_keys);
+    if (!keys || !q || !w || !scores) return fail(LSA_ERR_INVALID_ARG, "lsa_score: NULL pointer");
+    if (ens != LSA_ENSEMBLE_MAX && ens != LSA_ENSEMBLE_MEAN) return fail(LSA_ERR_INVALID_ARG, "ensemble %d", (int)ens);
+    if (dk <= 0 || n_idx <= 0 || heads <= 0) return fail(LSA_ERR_INVALID_ARG, "dk, n_idx and heads must be positive");
+    if (key_dtype != LSA_F32 && key_dtype != LSA_BF16) return fail(LSA_ERR_UNSUPPORTED, "key dtype %d", (int)key_dtype);
+    if (dk != 32 && dk != 64 && dk != 128) return fail(LSA_ERR_UNSUPPORTED, "dk %d (supported: 32, 64, 128)", dk);
+    if (n_idx > 4 || heads > 8) return fail(LSA_ERR_UNSUPPORTED, "n_idx %d x heads %d (supported: <= 4 x <= 8)", n_idx, heads);
+    if ((uint64_t)n_keys * (uint64_t)dk * (uint64_t)elem_bytes(key_dtype) >= ((uint64_t)1 << 32))
+        return fail(LSA_ERR_UNSUPPORTED, "a sequence's keys exceed 4 GiB");
+    memset(a, 0, sizeof(*a));
+    a->keys = keys;
+    a->q = q;
+    a->w = w;
+    a->scores = scores;
+    a->n_keys = n_keys;
+    a->batch = batch;
+    a->n_idx = n_idx;
+    a->heads = heads;
+    a->ensemble = ens;
+    int tiles = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t nv = n_valid ? n_valid[b] : n_keys;
+        if (nv < 0 || nv > n_keys) return fail(LSA_ERR_INVALID_ARG, "n_valid[%d] = %lld not in [0, n_keys]", b, (long long)nv);
+        a->n_valid[b] = (int32_t)nv;
+        a->tile_start[b] = tiles;
+        tiles += (int)((nv + 127) / 128);
+    }
+    a->tile_start[batch] = tiles;
+    return LSA_OK;
+}
+
+lsa_status select_setup(lsa_ctx* c, const float* scores, int32_t n_seg, int64_t n_keys, const int64_t* n_valid,
+                        lsa_select_mode mode, int32_t k, int32_t stride, double tau, int32_t* sel, int32_t* count,
+                        SelectArgs* a, size_t* ws_need) {
+    if (!scores || !sel || !count) return fail(LSA_ERR_INVALID_ARG, "lsa_select: NULL pointer");
+    if (n_seg < 1) return fail(LSA_ERR_INVALID_ARG, "n_seg %d", n_seg);
+    if (n_keys < 0 || n_keys > INT32_MAX) return fail(LSA_ERR_INVALID_ARG, "n_keys out of range");
+    if (mode != LSA_SELECT_TOPK && mode != LSA_SELECT_THRESHOLD) return fail(LSA_ERR_INVALID_ARG, "mode %d", (int)mode);
+    if (k < 1 || k > 4096) return fail(LSA_ERR_INVALID_ARG, "k %d not in [1, 4096]", k);
+    if (mode == LSA_SELECT_THRESHOLD && !(tau > 0.0 && tau < 1.0))
+        return fail(LSA_ERR_INVALID_ARG, "tau %g not in (0, 1)", tau);
+    memset(a, 0, sizeof(*a));
+    a->scores = scores;
+    a->n_keys = n_keys;
+    a->n_seg = n_seg;
+    a->k = k;
+    a->stride = stride;
+    a->mode = mode;
+    a->t_f = mode == LSA_SELECT_THRESHOLD ? lsa_threshold_logit(tau) : 0.0f;
+    a->sel = sel;
+    a->count = count;
+    a->n_valid_uniform = (int32_t)n_keys;
+    if (n_valid) {
+        bool uniform = true;
+        for (int s = 0; s < n_seg; ++s) {
+            if (n_valid[s] < 0 || n_valid[s] > n_keys)
+                return fail(LSA_ERR_INVALID_ARG, "n_valid[%d] = %lld not in [0, n_keys]", s, (long long)n_valid[s]);
+            uniform = uniform && n_valid[s] == n_valid[0];
+        }
+        if (uniform) {
+            a->n_valid_uniform = (int32_t)n_valid[0];
+        } else {
+            if (n_seg > LSA_MAX_BATCH)
+                return fail(LSA_ERR_UNSUPPORTED, "per-segment n_valid needs n_seg <= %d", LSA_MAX_BATCH);
+            a->has_n_valid = 1;
+            for (int s = 0; s < n_seg; ++s) a->n_valid[s] = (int32_t)n_valid[s];
+        }
+    }
+    size_t need = select_workspace_bytes(n_seg, n_keys, k, &a->nblk, &a->e1, &a->e2);
+    if (need == 0) return fail(LSA_ERR_UNSUPPORTED, "ceil(n_keys / 32768) * k must be <= 32768");
+    *ws_need = a->nblk > 1 ? need : 0;
+    return LSA_OK;
+}
+
+void select_bind_ws(SelectArgs* a, char* ws) {
+    if (a->nblk <= 1) return;
+    const size_t n = (size_t)a->n_seg * a->nblk * a->k;
+    a->cand_key = reinterpret_cast<uint32_t*>(ws);
+    a->cand_idx = reinterpret_cast<int32_t*>(ws + align_up(n * 4, 256));
+    a->cand_n = reinterpret_cast<int32_t*>(ws + 2 * align_up(n * 4, 256));
+}
+
+size_t select_ws_span(const SelectArgs& a) {
+    if (a.nblk <= 1) return 0;
+    const size_t n = (size_t)a.n_seg * a.nblk * a.k;
+    return 2 * align_up(n * 4, 256) + align_up((size_t)a.n_seg * a.nblk * 4, 256);
+}
+
+StageLayer stage_layer(const lsa_pool* p, const int32_t* sel, const int32_t* count, int32_t sel_stride,
+                       int32_t src_ratio, int32_t* phys, int32_t phys_stride, int32_t* n_rows) {
+    StageLayer L;
+    memset(&L, 0, sizeof(L));
+    L.slot_of = p->slot_of;
+    L.logical_of = p->logical_of;
+    L.lru = p->lru;
+    L.meta = p->meta;
+    L.stats = p->stats;
+    L.ready = p->ready;
+    L.sel = sel;
+    L.count = count;
+    L.phys = phys;
+    L.n_rows = n_rows;
+    L.miss = p->miss;
+    L.n_miss = p->n_miss;
+    L.cold = p->cold_dev;
+    L.kv = p->d.kv_buf;
+    L.cap = p->cap;
+    L.cold_stride_b = p->cold_stride_b;
+    L.kv_stride_b_bytes = p->d.kv_stride_b * (int64_t)elem_bytes(p->d.dtype);
+    L.ratio = p->d.ratio;
+    L.src_ratio = src_ratio;
+    L.S = p->d.gpu_chunks;
+    L.window = p->d.window;
+    L.swap = p->swap;
+    L.sel_stride = sel_stride;
+    L.phys_stride = phys_stride;
+    L.row_bytes = p->row_bytes;
+    return L;
+}
+
+lsa_status stage_check(const lsa_pool* p, int32_t sel_stride, int32_t src_ratio, int32_t phys_stride) {
+    if (sel_stride < 1 || sel_stride > 1024) return fail(LSA_ERR_INVALID_ARG, "sel_stride %d not in [1, 1024]", sel_stride);
+    if (p->swap && sel_stride > p->d.gpu_chunks)
+        return fail(LSA_ERR_SLOTS_LT_TOPK, "a step may select %d chunks but the pool has %d gpu_chunks",
+                    sel_stride, p->d.gpu_chunks);
+    if (src_ratio < 1 || p->d.ratio % src_ratio != 0)
+        return fail(LSA_ERR_INVALID_ARG, "pool ratio %d is not a multiple of src_ratio %d", p->d.ratio, src_ratio);
+    if (phys_stride < p->d.window + sel_stride)
+        return fail(LSA_ERR_INVALID_ARG, "phys_stride %d < window + sel_stride (%d)", phys_stride, p->d.window + sel_stride);
+    return LSA_OK;
+}
+
+
+// attention split + combine, timed as two intervals when timing is on
+lsa_status attend_timed(lsa_ctx* ctx, const AttendArgs& a, hipStream_t s) {
+    Timed t(ctx, LSA_K_ATTEND, s);
+    hipEvent_t mid = t.a ? ev_take(ctx) : nullptr;
+    HIPTRY(launch_lsa_attend(a, s, mid));
+    if (mid) {
+        ctx->pending.push_back({LSA_K_ATTEND, t.a, mid});
+        t.a = nullptr;
+        hipEvent_t e = ev_take(ctx);
+        if (e) {
+            (void)hipEventRecord(e, s);
+            ctx->pending.push_back({LSA_K_COMBINE, mid, e});
+        }
+    } else {
+        t.end();
+    }
+    return LSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lsa_status lsa_score(const void* keys, lsa_dtype key_dtype, int32_t batch, int64_t n_keys,
+                     const int64_t* n_valid, int32_t dk, const float* q, const float* w, int32_t n_idx,
+                     int32_t heads, lsa_ensemble ensemble, float* scores, lsa_stream_t stream) {
+    ScoreArgs a;
+    lsa_status st = score_args(keys, key_dtype, batch, n_keys, n_valid, dk, q, w, n_idx, heads, ensemble, scores, &a);
+    if (st != LSA_OK) return st;
+    HIPTRY(launch_fm_score(a, key_dtype, dk, n_cu_current(), (hipStream_t)stream));
+    return LSA_OK;
+}
+
+lsa_status lsa_select(lsa_ctx* ctx, const float* scores, int32_t n_seg, int64_t n_keys, const int64_t* n_valid,
+                      lsa_select_mode mode, int32_t k, double tau, int32_t* sel, int32_t* count,
+                      lsa_stream_t stream) {
+    if (!ctx) return fail(LSA_ERR_INVALID_ARG, "ctx is NULL");
+    SelectArgs a;
+    size_t need = 0;
+    lsa_status st = select_setup(ctx, scores, n_seg, n_keys, n_valid, mode, k, k, tau, sel, count, &a, &need);
+    if (st != LSA_OK) return st;
+    if (need) {
+        st = ws_ensure(ctx, select_ws_span(a));
+        if (st != LSA_OK) return st;
+        select_bind_ws(&a, static_cast<char*>(ctx->ws));
+    }
+    Timed t(ctx, LSA_K_SELECT, (hipStream_t)stream);
+    HIPTRY(launch_fm_select(a, (hipStream_t)stream));
+    t.end();
+    return LSA_OK;
+}
+
+// ------------------------------------------------------------------- pools
+int64_t lsa_pool_rows(const lsa_pool_desc* d) {
+    if (!d) return -1;
+    const int64_t cap = lsa_compressed_cap(d->ctx, d->ratio);
+    if (cap < 0 || d->window < 0 || d->gpu_chunks < 1) return -1;
+    return d->window + (cap > d->gpu_chunks ? d->gpu_chunks : cap);
+}
+
+void lsa_pool_destroy(lsa_pool* p) {
+    if (!p) return;
+    (void)hipDeviceSynchronize();
+    if (p->tables) (void)hipFree(p->tables);
+    if (p->cold_host) (void)hipHostFree(p->cold_host);
+    else if (p->cold_dev) (void)hipFree(p->cold_dev);
+    delete p;
+}
+
+lsa_status lsa_pool_create(lsa_pool** out, const lsa_pool_desc* d) {
+    if (!out || !d) return fail(LSA_ERR_INVALID_ARG, "lsa_pool_create: NULL argument");
+    *out = nullptr;
+    if (d->ctx < 0 || d->ratio < 1) return fail(LSA_ERR_INVALID_ARG, "ctx %lld, ratio %d", (long long)d->ctx, d->ratio);
+    if (d->window < 0 || d->window > 4096) return fail(LSA_ERR_INVALID_ARG, "window %d not in [0, 4096]", d->window);
+    if (d->gpu_chunks < 1) return fail(LSA_ERR_INVALID_ARG, "gpu_chunks %d < 1", d->gpu_chunks);
+    if (d->topk < 1 || d->topk > 1024) return fail(LSA_ERR_INVALID_ARG, "topk %d not in [1, 1024]", d->topk);
+    if (d->batch < 1 || d->batch > LSA_MAX_BATCH) return fail(LSA_ERR_INVALID_ARG, "batch %d", d->batch);
+    if (!row_dtype_ok(d->dtype)) return fail(LSA_ERR_UNSUPPORTED, "row dtype %d", (int)d->dtype);
+    if (d->kv_dim < 8 || (d->kv_dim * elem_bytes(d->dtype)) % 16 != 0)
+        return fail(LSA_ERR_UNSUPPORTED, "kv_dim %d: rows must be a multiple of 16 bytes", d->kv_dim);
+    if (d->cold != LSA_COLD_HBM && d->cold != LSA_COLD_HOST) return fail(LSA_ERR_INVALID_ARG, "cold kind %d", (int)d->cold);
+    if (!d->kv_buf) return fail(LSA_ERR_INVALID_ARG, "kv_buf is NULL");
+    const int64_t cap = lsa_compressed_cap(d->ctx, d->ratio);
+    if (cap > INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "compressed_cap %lld", (long long)cap);
+    const int swap = cap > d->gpu_chunks ? 1 : 0;
+    if (swap && d->gpu_chunks > 4096)
+        return fail(LSA_ERR_UNSUPPORTED, "a swapping pool supports at most 4096 gpu_chunks (got %d)", d->gpu_chunks);
+    const int64_t rows = lsa_pool_rows(d);
+    if (d->batch > 1 && d->kv_stride_b < rows * d->kv_dim)
+        return fail(LSA_ERR_INVALID_ARG, "kv_stride_b %lld < rows * kv_dim (%lld)", (long long)d->kv_stride_b,
+                    (long long)(rows * d->kv_dim));
+    if (swap && d->gpu_chunks < d->topk && !d->allow_topk_reduction)
+        return fail(LSA_ERR_SLOTS_LT_TOPK, "gpu_chunks (%d) must be >= index_topk (%d)", d->gpu_chunks, d->topk);
+    const int row_bytes = d->kv_dim * elem_bytes(d->dtype);
+    const uint64_t cold_bytes = swap ? (uint64_t)d->batch * (uint64_t)cap * (uint64_t)row_bytes : 0;
+    if (swap && d->cold == LSA_COLD_HOST && d->pinned_cap_bytes && cold_bytes > d->pinned_cap_bytes)
+        return fail(LSA_ERR_PINNED_CAP, "pinned cache exceeds cap: required_mib=%llu cap_mib=%llu",
+                    (unsigned long long)((cold_bytes + (1u << 20) - 1) >> 20),
+                    (unsigned long long)(d->pinned_cap_bytes >> 20));
+
+    lsa_pool* p = new lsa_pool;
+    p->d = *d;
+    HIPTRY(hipGetDevice(&p->device));
+    p->cap = cap;
+    p->swap = swap;
+    p->row_bytes = row_bytes;
+    p->rows_per_seq = rows;
+    const int64_t B = d->batch, S = swap ? d->gpu_chunks : 1, C = cap;
+    const size_t sz_slot = align_up((size_t)(swap ? B * C : 1) * 4, 256);
+    const size_t sz_lo = align_up((size_t)(B * S) * 4, 256);
+    const size_t sz_meta = align_up((size_t)B * 16, 256);
+    const size_t sz_stats = align_up((size_t)B * 32, 256);
+    const size_t sz_ready = align_up((size_t)(B * C), 256);
+    const size_t sz_miss = align_up((size_t)B * 1024 * 8, 256);
+    const size_t sz_nmiss = align_up((size_t)B * 4, 256);
+    const size_t total = sz_slot + 2 * sz_lo + sz_meta + sz_stats + sz_ready + sz_miss + sz_nmiss;
+    if (hipMalloc(&p->tables, total) != hipSuccess) {
+        (void)hipGetLastError();
+        delete p;
+        return fail(LSA_ERR_NO_MEMORY, "pool tables (%zu bytes)", total);
+    }
+    char* t = static_cast<char*>(p->tables);
+    p->slot_of = reinterpret_cast<int32_t*>(t); t += sz_slot;
+    p->logical_of = reinterpret_cast<int32_t*>(t); t += sz_lo;
+    p->lru = reinterpret_cast<int32_t*>(t); t += sz_lo;
+    p->meta = reinterpret_cast<int32_t*>(t); t += sz_meta;
+    p->stats = reinterpret_cast<uint64_t*>(t); t += sz_stats;
+    p->ready = reinterpret_cast<uint8_t*>(t); t += sz_ready;
+    p->miss = reinterpret_cast<int32_t*>(t); t += sz_miss;
+    p->n_miss = reinterpret_cast<int32_t*>(t);
+    hipError_t e = hipMemset(p->tables, 0, total);
+    if (e == hipSuccess) e = hipMemset(p->slot_of, 0xFF, sz_slot + 2 * sz_lo);
+    if (e == hipSuccess && swap) {
+        p->cold_stride_b = (int64_t)C * row_bytes;
+        if (d->cold == LSA_COLD_HBM) {
+            e = hipMalloc(&p->cold_dev, cold_bytes);
+        } else {
+            e = hipHostMalloc(&p->cold_host, cold_bytes, hipHostMallocDefault);
+            if (e == hipSuccess) e = hipHostGetDevicePointer(&p->cold_dev, p->cold_host, 0);
+        }
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            lsa_pool_destroy(p);
+            return fail(LSA_ERR_NO_MEMORY, "cold pool of %llu bytes (%s)", (unsigned long long)cold_bytes,
+                        d->cold == LSA_COLD_HBM ? "HBM" : "pinned host");
+        }
+    }
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        lsa_pool_destroy(p);
+        return fail(LSA_ERR_HIP, "pool initialisation: %s", hipGetErrorString(e));
+    }
+    *out = p;
+    return LSA_OK;
+}
+
+void* lsa_pool_host_rows(lsa_pool* p, int32_t b) {
+    if (!p || !p->cold_host || b < 0 || b >= p->d.batch) return nullptr;
+    return static_cast<char*>(p->cold_host) + (int64_t)b * p->cold_stride_b;
+}
+
+static lsa_status mark_ready(lsa_pool* p, int32_t b, int64_t first, int64_t count, hipStream_t s) {
+    HIPTRY(hipMemsetAsync(p->ready + (int64_t)b * p->cap + first, 1, (size_t)count, s));
+    if (p->swap) {
+        StageLayer L = stage_layer(p, nullptr, nullptr, 1, 1, nullptr, 0, nullptr);
+        HIPTRY(launch_refresh_staged(L, b, first, count, s));
+    }
+    p->d2h_bytes += (uint64_t)count * (uint64_t)p->row_bytes;
+    return LSA_OK;
+}
+
+lsa_status lsa_pool_store(lsa_pool* p, int32_t b, int64_t first, int64_t count, const void* rows,
+                          lsa_stream_t stream) {
+    if (!p) return fail(LSA_ERR_INVALID_ARG, "pool is NULL");
+    if (b < 0 || b >= p->d.batch || first < 0 || count < 0 || first + count > p->cap)
+        return fail(LSA_ERR_INVALID_ARG, "store of entries [%lld, %lld) of sequence %d outside [0, %lld)",
+                    (long long)first, (long long)(first + count), b, (long long)p->cap);
+    if (count == 0) return LSA_OK;
+    if (!rows) return fail(LSA_ERR_INVALID_ARG, "rows is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    const size_t bytes = (size_t)count * p->row_bytes;
+    void* dst;
+    if (p->swap) {
+        char* base = static_cast<char*>(p->cold_host ? p->cold_host : p->cold_dev);
+        dst = base + (int64_t)b * p->cold_stride_b + first * p->row_bytes;
+    } else {
+        dst = static_cast<char*>(p->d.kv_buf) +
+              ((int64_t)b * p->d.kv_stride_b + (p->d.window + first) * (int64_t)p->d.kv_dim) * elem_bytes(p->d.dtype);
+    }
+    HIPTRY(hipMemcpyAsync(dst, rows, bytes, hipMemcpyDefault, s));
+    return mark_ready(p, b, first, count, s);
+}
+
+lsa_status lsa_pool_mark_stored(lsa_pool* p, int32_t b, int64_t first, int64_t count, lsa_stream_t stream) {
+    if (!p) return fail(LSA_ERR_INVALID_ARG, "pool is NULL");
+    if (b < 0 || b >= p->d.batch || first < 0 || count < 0 || first + count > p->cap)
+        return fail(LSA_ERR_INVALID_ARG, "entries [%lld, %lld) outside [0, %lld)", (long long)first,
+                    (long long)(first + count), (long long)p->cap);
+    if (count == 0) return LSA_OK;
+    return mark_ready(p, b, first, count, (hipStream_t)stream);
+}
+
+lsa_status lsa_pool_reset(lsa_pool* p, lsa_stream_t stream) {
+    if (!p) return fail(LSA_ERR_INVALID_ARG, "pool is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t B = p->d.batch;
+    if (p->swap) {
+        HIPTRY(hipMemsetAsync(p->slot_of, 0xFF, (size_t)(B * p->cap) * 4, s));
+        HIPTRY(hipMemsetAsync(p->logical_of, 0xFF, (size_t)(B * p->d.gpu_chunks) * 4, s));
+    }
+    HIPTRY(hipMemsetAsync(p->meta, 0, (size_t)B * 16, s));
+    HIPTRY(hipMemsetAsync(p->stats, 0, (size_t)B * 32, s));
+    return LSA_OK;
+}
+
+lsa_status lsa_pool_stats(lsa_pool* p, lsa_pool_stats_t* out, lsa_stream_t stream) {
+    if (!p || !out) return fail(LSA_ERR_INVALID_ARG, "lsa_pool_stats: NULL argument");
+    HIPTRY(hipStreamSynchronize((hipStream_t)stream));
+    const int B = p->d.batch;
+    std::vector<uint64_t> st((size_t)B * 4);
+    std::vector<int32_t> meta((size_t)B * 4);
+    HIPTRY(hipMemcpy(st.data(), p->stats, st.size() * 8, hipMemcpyDeviceToHost));
+    HIPTRY(hipMemcpy(meta.data(), p->meta, meta.size() * 4, hipMemcpyDeviceToHost));
+    memset(out, 0, sizeof(*out));
+    int flags = 0;
+    for (int b = 0; b < B; ++b) {
+        out->hits += st[b * 4 + 0];
+        out->misses += st[b * 4 + 1];
+        out->h2d_bytes += st[b * 4 + 2];
+        out->resident += meta[b * 4 + 0];
+        flags |= meta[b * 4 + 1];
+        meta[b * 4 + 1] = 0;
+    }
+    out->d2h_bytes = p->d2h_bytes;
+    out->compressed_cap = p->cap;
+    out->swap_enabled = p->swap;
+    if (flags) {
+        HIPTRY(hipMemcpy(p->meta, meta.data(), meta.size() * 4, hipMemcpyHostToDevice));
+        if (flags & 2) return fail(LSA_ERR_INVALID_ARG, "a step selected an entry outside [0, compressed_cap)");
+        return fail(LSA_ERR_NOT_STORED, "selected chunk before it was stored");
+    }
+    return LSA_OK;
+}
+
+lsa_status lsa_pool_state(lsa_pool* p, int32_t b, int32_t* slot_logical, int32_t* lru, int32_t* n_used,
+                          lsa_stream_t stream) {
+    if (!p || !slot_logical || !lru || !n_used) return fail(LSA_ERR_INVALID_ARG, "lsa_pool_state: NULL argument");
+    if (b < 0 || b >= p->d.batch) return fail(LSA_ERR_INVALID_ARG, "sequence %d", b);
+    HIPTRY(hipStreamSynchronize((hipStream_t)stream));
+    const int S = p->d.gpu_chunks;
+    if (!p->swap) {
+        for (int i = 0; i < S; ++i) slot_logical[i] = -1;
+        *n_used = 0;
+        return LSA_OK;
+    }
+    int32_t meta[4];
+    HIPTRY(hipMemcpy(meta, p->meta + b * 4, 16, hipMemcpyDeviceToHost));
+    HIPTRY(hipMemcpy(slot_logical, p->logical_of + (int64_t)b * S, (size_t)S * 4, hipMemcpyDeviceToHost));
+    HIPTRY(hipMemcpy(lru, p->lru + (int64_t)b * S, (size_t)S * 4, hipMemcpyDeviceToHost));
+    *n_used = meta[0];
+    return LSA_OK;
+}
+
+// ------------------------------------------------------------------- stage
+lsa_status lsa_stage(lsa_pool* p, const int32_t* sel, const int32_t* count, int32_t sel_stride, int32_t src_ratio,
+                     int32_t* phys, int32_t phys_stride, int32_t* n_rows, lsa_stream_t stream) {
+    if (!p || !sel || !count || !phys || !n_rows) return fail(LSA_ERR_INVALID_ARG, "lsa_stage: NULL argument");
+    lsa_status st = stage_check(p, sel_stride, src_ratio, phys_stride);
+    if (st != LSA_OK) return st;
+    StageArgs a;
+    memset(&a, 0, sizeof(a));
+    a.n_layers = 1;
+    a.batch = p->d.batch;
+    a.L[0] = stage_layer(p, sel, count, sel_stride, src_ratio, phys, phys_stride, n_rows);
+    hipStream_t s = (hipStream_t)stream;
+    HIPTRY(launch_kv_stage(a, s));
+    HIPTRY(launch_kv_gather(a, s));
+    return LSA_OK;
+}
+
+// ------------------------------------------------------------------ attend
+lsa_status lsa_attend(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dtype, int64_t kv_stride_b,
+                      int64_t kv_rows, const int32_t* phys, int32_t phys_stride, const int32_t* n_rows,
+                      int32_t batch, int32_t hq, int32_t kv_dim, float scale, float* out, lsa_stream_t stream) {
+    if (!ctx || !q || !kv || !phys || !n_rows || !out) return fail(LSA_ERR_INVALID_ARG, "lsa_attend: NULL argument");
+    if (batch < 1 || batch > LSA_MAX_BATCH) return fail(LSA_ERR_INVALID_ARG, "batch %d", batch);
+    if (hq < 1 || phys_stride < 1 || kv_rows < 0 || !isfinite(scale))
+        return fail(LSA_ERR_INVALID_ARG, "hq %d, phys_stride %d, kv_rows %lld, scale %g", hq, phys_stride,
+                    (long long)kv_rows, (double)scale);
+    if (batch > 1 && kv_stride_b < kv_rows * kv_dim) return fail(LSA_ERR_INVALID_ARG, "kv_stride_b < kv_rows * kv_dim");
+    if (!row_dtype_ok(dtype)) return fail(LSA_ERR_UNSUPPORTED, "row dtype %d", (int)dtype);
+    if (hq > 16 || (kv_dim != 128 && kv_dim != 256 && kv_dim != 512))
+        return fail(LSA_ERR_UNSUPPORTED, "hq %d, kv_dim %d (supported: hq <= 16, kv_dim 128/256/512)", hq, kv_dim);
+    AttendArgs a;
+    memset(&a, 0, sizeof(a));
+    a.n_layers = 1;
+    a.batch = batch;
+    a.hq = hq;
+    a.D = kv_dim;
+    a.dtype = dtype;
+    a.max_splits = (phys_stride + kAttendRows - 1) / kAttendRows;
+    a.scale = scale;
+    const size_t need = attend_workspace_bytes(1, batch, kv_dim, phys_stride);
+    lsa_status st = ws_ensure(ctx, need);
+    if (st != LSA_OK) return st;
+    a.part_acc = static_cast<float*>(ctx->ws);
+    a.part_ml = a.part_acc + (size_t)batch * a.max_splits * 16 * kv_dim;
+    a.L[0] = AttendLayer{q, kv, phys, n_rows, out, kv_stride_b, kv_rows, phys_stride};
+    return attend_timed(ctx, a, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------- decode step
+lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
+    if (!ctx || !d) return fail(LSA_ERR_INVALID_ARG, "lsa_decode_step: NULL argument");
+    if (d->n_layers < 1 || d->n_layers > LSA_MAX_LAYERS)
+        return fail(LSA_ERR_INVALID_ARG, "n_layers %d not in [1, %d]", d->n_layers, LSA_MAX_LAYERS);
+    if (!d->pools || !d->q_attn || !d->out || !d->scores || !d->sel || !d->count)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_decode_step: NULL pointer in the step");
+    const lsa_pool* p0 = d->pools[0];
+    if (!p0) return fail(LSA_ERR_INVALID_ARG, "pool 0 is NULL");
+    const int B = d->batch, D = p0->d.kv_dim, W = p0->d.window;
+    const lsa_dtype dt = p0->d.dtype;
+    if (d->hq < 1 || d->hq > 16) return fail(LSA_ERR_UNSUPPORTED, "hq %d (supported 1..16)", d->hq);
+    if (D != 128 && D != 256 && D != 512) return fail(LSA_ERR_UNSUPPORTED, "kv_dim %d", D);
+    if (!isfinite(d->scale)) return fail(LSA_ERR_INVALID_ARG, "scale");
+    int k_eff = d->k;
+    for (int l = 0; l < d->n_layers; ++l) {
+        const lsa_pool* p = d->pools[l];
+        if (!p) return fail(LSA_ERR_INVALID_ARG, "pool %d is NULL", l);
+        if (p->d.batch != B || p->d.kv_dim != D || p->d.window != W || p->d.dtype != dt)
+            return fail(LSA_ERR_INVALID_ARG, "pool %d: batch, kv_dim, window and dtype must match the step", l);
+        if (p->swap && p->d.gpu_chunks < k_eff) {
+            if (!p->d.allow_topk_reduction)
+                return fail(LSA_ERR_SLOTS_LT_TOPK, "pool %d: gpu_chunks (%d) must be >= index_topk (%d)", l,
+                            p->d.gpu_chunks, d->k);
+            k_eff = p->d.gpu_chunks;
+        }
+    }
+    ScoreArgs sa;
+    lsa_status st = score_args(d->keys, d->key_dtype, B, d->n_keys, d->n_valid, d->dk, d->q_idx, d->w_idx, d->n_idx,
+                               d->heads, d->ensemble, d->scores, &sa);
+    if (st != LSA_OK) return st;
+    SelectArgs se;
+    size_t sel_need = 0;
+    st = select_setup(ctx, d->scores, B, d->n_keys, d->n_valid, d->mode, k_eff, d->k, d->tau, d->sel, d->count, &se,
+                      &sel_need);
+    if (st != LSA_OK) return st;
+    const int phys_stride = W + d->k;
+    for (int l = 0; l < d->n_layers; ++l) {
+        st = stage_check(d->pools[l], k_eff, d->src_ratio, phys_stride);
+        if (st != LSA_OK) return st;
+    }
+    // workspace: select candidates | attend partials | phys | n_rows
+    const size_t off_att = align_up(select_ws_span(se), 256);
+    const size_t att_bytes = attend_workspace_bytes(d->n_layers, B, D, phys_stride);
+    const size_t off_phys = off_att + align_up(att_bytes, 256);
+    const size_t phys_bytes = d->phys ? 0 : align_up((size_t)d->n_layers * B * phys_stride * 4, 256);
+    const size_t off_nrows = off_phys + phys_bytes;
+    const size_t nrows_bytes = d->n_rows ? 0 : align_up((size_t)d->n_layers * B * 4, 256);
+    st = ws_ensure(ctx, off_nrows + nrows_bytes);
+    if (st != LSA_OK) return st;
+    char* ws = static_cast<char*>(ctx->ws);
+    select_bind_ws(&se, ws);
+    int32_t* phys = d->phys ? d->phys : reinterpret_cast<int32_t*>(ws + off_phys);
+    int32_t* n_rows = d->n_rows ? d->n_rows : reinterpret_cast<int32_t*>(ws + off_nrows);
+
+    StageArgs ga;
+    memset(&ga, 0, sizeof(ga));
+    ga.n_layers = d->n_layers;
+    ga.batch = B;
+    AttendArgs aa;
+    memset(&aa, 0, sizeof(aa));
+    aa.n_layers = d->n_layers;
+    aa.batch = B;
+    aa.hq = d->hq;
+    aa.D = D;
+    aa.dtype = dt;
+    aa.max_splits = (phys_stride + kAttendRows - 1) / kAttendRows;
+    aa.scale = d->scale;
+    aa.part_acc = reinterpret_cast<float*>(ws + off_att);
+    aa.part_ml = aa.part_acc + (size_t)d->n_layers * B * aa.max_splits * 16 * D;
+    for (int l = 0; l < d->n_layers; ++l) {
+        const lsa_pool* p = d->pools[l];
+        int32_t* ph = phys + (size_t)l * B * phys_stride;
+        int32_t* nr = n_rows + (size_t)l * B;
+        ga.L[l] = stage_layer(p, d->sel, d->count, d->k, d->src_ratio, ph, phys_stride, nr);
+        aa.L[l] = AttendLayer{d->q_attn + (size_t)l * B * d->hq * D, p->d.kv_buf, ph, nr,
+                              d->out + (size_t)l * B * d->hq * D, p->d.kv_stride_b, p->rows_per_seq, phys_stride};
+    }
+
+    hipStream_t s = (hipStream_t)stream;
+    {
+        Timed t(ctx, LSA_K_SCORE, s);
+        HIPTRY(launch_fm_score(sa, d->key_dtype, d->dk, ctx->n_cu, s));
+        t.end();
+    }
+    {
+        Timed t(ctx, LSA_K_SELECT, s);
+        HIPTRY(launch_fm_select(se, s));
+        t.end();
+    }
+    {
+        Timed t(ctx, LSA_K_STAGE, s);
+        HIPTRY(launch_kv_stage(ga, s));
+        t.end();
+    }
+    {
+        Timed t(ctx, LSA_K_GATHER, s);
+        HIPTRY(launch_kv_gather(ga, s));
+        t.end();
+    }
+    st = attend_timed(ctx, aa, s);
+    if (st != LSA_OK) return st;
+    return LSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+// lsa_attend: decode attention over the sliding window plus the staged
+// compressed entries, every row used as both key and value.
+//
+// [P1] overview "Two-tier KV cache" and per-layer indexed_cached_attention
+// (window + selected), reading d_kv_cache[physical_id]:
+//   out[h,:] = sum_r softmax_r(scale * q[h,:] . kv[phys[r],:]) * kv[phys[r],:]
+//
+// Design (gfx950): flash-decode split over rows.  All heads share the rows
+// (MQA-like), so a workgroup loads one 32-row tile into LDS once and computes
+// the 16-head x 32-row score block and the 16-head x D output block with
+// v_mfma_f32_16x16x4f32: QK^T splits the rows over 2 waves and the D
+// (contraction) dimension over 2 waves, PV splits D over 4 waves.  Each split
+// writes its running max, softmax denominator and unnormalised output; a
+// second kernel merges the splits in split order.  Split s always covers list
+// rows [32 s, 32 s + 32), so the arithmetic depends only on the list length
+// and the row contents -- not on which physical rows hold them.
+#include "lsa_internal.hpp"
+
+namespace lsa {
+
+namespace {
+
+constexpr int kR = kAttendRows;   // rows per split
+constexpr int kThreads = 256;
+
+template <typename KT>
+__device__ inline float ld_elem(const char* p);
+template <>
+__device__ inline float ld_elem<float>(const char* p) { return *reinterpret_cast<const float*>(p); }
+template <>
+__device__ inline float ld_elem<uint16_t>(const char* p) {
+    return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16);
+}
+
+template <typename KT>
+__device__ inline void unpack(const uint4& u, float* out);
+template <>
+__device__ inline void unpack<float>(const uint4& u, float* out) {
+    out[0] = __uint_as_float(u.x);
+    out[1] = __uint_as_float(u.y);
+    out[2] = __uint_as_float(u.z);
+    out[3] = __uint_as_float(u.w);
+}
+template <>
+__device__ inline void unpack<uint16_t>(const uint4& u, float* out) {
+    out[0] = bf16_lo(u.x);
+    out[1] = bf16_hi(u.x);
+    out[2] = bf16_lo(u.y);
+    out[3] = bf16_hi(u.y);
+    out[4] = bf16_lo(u.z);
+    out[5] = bf16_hi(u.z);
+    out[6] = bf16_lo(u.w);
+    out[7] = bf16_hi(u.w);
+}
+
+template <int D, typename KT>
+__global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendArgs a) {
+    constexpr int RB = D * (int)sizeof(KT);          // row bytes
+    constexpr int LS = RB + 16;                      // LDS row stride
+    constexpr int CPR = RB / 16;                     // 16-byte chunks per row
+    constexpr int QK_STEPS = D / 8;                  // per lane: D/2 per wave-half, /4 k-lanes
+    constexpr int PER_READ = 16 / (int)sizeof(KT);
+    constexpr int NB = D / 64;                       // 16-wide output blocks per wave in PV
+
+    __shared__ __attribute__((aligned(16))) char tile[kR * LS];
+    __shared__ float sS[2][16][kR];
+    __shared__ float sP[16][kR];
+    __shared__ int s_ph[kR];
+
+    const AttendLayer& L = a.L[blockIdx.z];
+    const int b = blockIdx.y, split = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int n = L.n_rows[b];
+    n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
+    const int r0 = split * kR;
+    if (r0 >= n) return;
+    const int cnt = n - r0 < kR ? n - r0 : kR;
+    const int pair = blockIdx.z * a.batch + b;
+
+    if (tid < kR) {
+        int p = tid < cnt ? L.phys[(int64_t)b * L.phys_stride + r0 + tid] : -1;
+        s_ph[tid] = (p >= 0 && p < L.kv_rows) ? p : -1;
+    }
+    __syncthreads();
+    const char* kvb = static_cast<const char*>(L.kv) + (int64_t)b * L.kv_stride_b * (int64_t)sizeof(KT);
+    for (int c = tid; c < kR * CPR; c += kThreads) {
+        const int r = c / CPR, cc = c % CPR;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (s_ph[r] >= 0) v = *reinterpret_cast<const uint4*>(kvb + (int64_t)s_ph[r] * RB + cc * 16);
+        *reinterpret_cast<uint4*>(tile + r * LS + cc * 16) = v;
+    }
+
+    // ---- scores: S[h][r] = q[h] . row[r]; wave = (row block nb, D half kh)
+    {
+        const int nb = wave & 1, kh = wave >> 1;
+        const int h = lane & 15, g = lane >> 4;
+        const int e0 = kh * (D / 2) + g * QK_STEPS;
+        float qa[QK_STEPS];
+        const float* qp = L.q + ((int64_t)b * a.hq + (h < a.hq ? h : 0)) * D + e0;
+#pragma unroll
+        for (int s = 0; s < QK_STEPS; s += 4) {
+            f32x4 v = h < a.hq ? *reinterpret_cast<const f32x4*>(qp + s) : f32x4{0.f, 0.f, 0.f, 0.f};
+            qa[s] = v[0];
+            qa[s + 1] = v[1];
+            qa[s + 2] = v[2];
+            qa[s + 3] = v[3];
+        }
+        __syncthreads();   // tile complete
+        const char* rowp = tile + (nb * 16 + (lane & 15)) * LS + e0 * (int)sizeof(KT);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rd = 0; rd < QK_STEPS / PER_READ; ++rd) {
+            float kb[PER_READ];
+            unpack<KT>(*reinterpret_cast<const uint4*>(rowp + rd * 16), kb);
+#pragma unroll
+            for (int e = 0; e < PER_READ; ++e)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[rd * PER_READ + e], kb[e], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sS[kh][4 * g + r][nb * 16 + (lane & 15)] = acc[r];
+    }
+    __syncthreads();
+
+    // ---- per-head softmax over this split's rows
+    float* ml = a.part_ml + ((int64_t)pair * a.max_splits + split) * 32;
+    if (tid < 16) {
+        const int h = tid;
+        float m = -INFINITY;
+        for (int r = 0; r < cnt; ++r) {
+            const float z = (sS[0][h][r] + sS[1][h][r]) * a.scale;
+            sS[0][h][r] = z;
+            m = fmaxf(m, z);
+        }
+        float l = 0.0f;
+        for (int r = 0; r < kR; ++r) {
+            const float p = r < cnt ? expf(sS[0][h][r] - m) : 0.0f;
+            sP[h][r] = p;
+            l += p;
+        }
+        ml[h] = m;
+        ml[16 + h] = l;
+    }
+    __syncthreads();
+
+    // ---- unnormalised output O[h][d] = sum_r P[h][r] row[r][d]; wave = D quarter
+    {
+        const int h = lane & 15, g = lane >> 4;
+        const int d0 = wave * (D / 4);
+        f32x4 acc[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kR / 4; ++s) {
+            const int r = 4 * s + g;
+            const float pa = sP[h][r];
+            const char* rp = tile + r * LS;
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const float vb = ld_elem<KT>(rp + (d0 + 16 * i + h) * (int)sizeof(KT));
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, acc[i], 0, 0, 0);
+            }
+        }
+        float* po = a.part_acc + ((int64_t)pair * a.max_splits + split) * 16 * D;
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) po[(4 * g + r) * D + d0 + 16 * i + h] = acc[i][r];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a) {
+    const AttendLayer& L = a.L[blockIdx.z];
+    const int b = blockIdx.y;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int h = idx / D, d = idx % D;
+    if (h >= a.hq) return;
+    int n = L.n_rows[b];
+    n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
+    const int ns = (n + kR - 1) / kR;
+    const int pair = blockIdx.z * a.batch + b;
+    float* out = L.out + ((int64_t)b * a.hq + h) * D + d;
+    if (ns == 0) {
+        *out = 0.0f;
+        return;
+    }
+    const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * 32 + h]);
+    float den = 0.0f, num = 0.0f;
+    const float* po = a.part_acc + (int64_t)pair * a.max_splits * 16 * D + h * D + d;
+    for (int s = 0; s < ns; ++s) {
+        const float f = expf(ml[s * 32 + h] - M);
+        den += f * ml[s * 32 + 16 + h];
+        num += f * po[(int64_t)s * 16 * D];
+    }
+    *out = num / den;
+}
+
+template <int D, typename KT>
+hipError_t launch_t(const AttendArgs& a, hipStream_t s, hipEvent_t mid) {
+    const dim3 g1(a.max_splits, a.batch, a.n_layers);
+    hipLaunchKernelGGL((attend_split_kernel<D, KT>), g1, dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (mid) {
+        e = hipEventRecord(mid, s);
+        if (e != hipSuccess) return e;
+    }
+    const dim3 g2((16 * D + 255) / 256, a.batch, a.n_layers);
+    hipLaunchKernelGGL((attend_combine_kernel<D>), g2, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows) {
+    const size_t splits = (size_t)((max_rows + kR - 1) / kR);
+    return (size_t)n_layers * batch * splits * (16 * (size_t)D + 32) * sizeof(float);
+}
+
+hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid) {
+    if (a.max_splits == 0) return hipSuccess;
+    if (a.dtype == LSA_F32) {
+        if (a.D == 128) return launch_t<128, float>(a, s, mid);
+        if (a.D == 256) return launch_t<256, float>(a, s, mid);
+        if (a.D == 512) return launch_t<512, float>(a, s, mid);
+    } else if (a.dtype == LSA_BF16) {
+        if (a.D == 128) return launch_t<128, uint16_t>(a, s, mid);
+        if (a.D == 256) return launch_t<256, uint16_t>(a, s, mid);
+        if (a.D == 512) return launch_t<512, uint16_t>(a, s, mid);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lsa

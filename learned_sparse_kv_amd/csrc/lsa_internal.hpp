@@ -1,0 +1,167 @@
+// Internal declarations shared by the liblsa HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lsa.h"
+
+namespace lsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ device helpers
+// Buffer resource for raw buffer loads: reads at byte offsets >= num_records
+// return zero, which is how ragged tails are padded without branches.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_records) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records,
+                                             0x00020000);
+}
+
+// The builtin returns four uint32 lanes; keep that type (assigning it to a
+// float vector would convert values instead of moving bits).
+__device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ inline float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ inline float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0 is first turned into +0 so the two compare equal.
+__device__ inline uint32_t order_key(float x) {
+    x = x + 0.0f;
+    const uint32_t b = __float_as_uint(x);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ inline int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+
+// Exclusive block-wide prefix sum for blockDim.x == NT (multiple of 64);
+// `smem` needs NT/64 + 1 ints.  Returns the exclusive prefix; *total = sum.
+template <int NT>
+__device__ inline int block_excl_scan(int v, int* smem, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int NW = NT / 64;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) smem[wave] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < NW; ++w) {
+            const int t = smem[w];
+            smem[w] = run;
+            run += t;
+        }
+        smem[NW] = run;
+    }
+    __syncthreads();
+    const int res = smem[wave] + incl - v;
+    *total = smem[NW];
+    __syncthreads();
+    return res;
+}
+
+// ------------------------------------------------------------------ launchers
+struct ScoreArgs {
+    const void* keys;
+    const float* q;
+    const float* w;
+    float* scores;
+    int64_t n_keys;
+    int32_t batch, n_idx, heads, ensemble;
+    int32_t n_valid[LSA_MAX_BATCH];
+    int32_t tile_start[LSA_MAX_BATCH + 1];   // prefix of 128-key tiles per sequence
+};
+hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, hipStream_t s);
+
+struct SelectArgs {
+    const float* scores;
+    int64_t n_keys;
+    int32_t n_seg, k, stride, mode;   // k: most entries kept; stride: row length of sel
+    float t_f;                  // threshold mode: pass if score > t_f
+    int32_t n_valid_uniform;    // used when has_n_valid == 0
+    int32_t has_n_valid;
+    int32_t n_valid[LSA_MAX_BATCH];
+    int32_t* sel;
+    int32_t* count;
+    // two-stage workspace
+    uint32_t* cand_key;         // [n_seg][nblk][k]
+    int32_t* cand_idx;          // [n_seg][nblk][k]
+    int32_t* cand_n;            // [n_seg][nblk]
+    int32_t nblk, e1, e2;
+};
+size_t select_workspace_bytes(int n_seg, int64_t n_keys, int k, int* nblk, int* e1, int* e2);
+hipError_t launch_fm_select(const SelectArgs& a, hipStream_t s);
+
+struct StageLayer {
+    int32_t* slot_of;           // [batch][cap] slot or -1
+    int32_t* logical_of;        // [batch][S] entry or -1
+    int32_t* lru;               // [batch][S] slot ids, most recent first
+    int32_t* meta;              // [batch][4]: used slots, not-stored flag
+    uint64_t* stats;            // [batch][4]: hits, misses, h2d bytes
+    const uint8_t* ready;       // [batch][cap]
+    const int32_t* sel;         // [batch][sel_stride]
+    const int32_t* count;       // [batch]
+    int32_t* phys;              // [batch][phys_stride]
+    int32_t* n_rows;            // [batch]
+    int32_t* miss;              // [batch][sel_stride][2]: (entry, slot)
+    int32_t* n_miss;            // [batch]
+    const void* cold;           // cold rows, sequence b at b * cold_stride_b bytes
+    void* kv;                   // kv_buf
+    int64_t cap, cold_stride_b, kv_stride_b_bytes;
+    int32_t ratio, src_ratio, S, window, swap, sel_stride, phys_stride, row_bytes;
+};
+struct StageArgs {
+    int32_t n_layers, batch;
+    StageLayer L[LSA_MAX_LAYERS];
+};
+hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s);
+hipError_t launch_kv_gather(const StageArgs& a, hipStream_t s);
+// copy the rows of entries [first, first+count) of sequence b that are staged
+// from the cold pool into their slots
+hipError_t launch_refresh_staged(const StageLayer& L, int b, int64_t first, int64_t count,
+                                 hipStream_t s);
+
+struct AttendLayer {
+    const float* q;             // [batch][hq][D]
+    const void* kv;
+    const int32_t* phys;
+    const int32_t* n_rows;
+    float* out;                 // [batch][hq][D]
+    int64_t kv_stride_b;        // elements
+    int64_t kv_rows;            // rows per sequence; phys entries outside read as zero rows
+    int32_t phys_stride;
+};
+struct AttendArgs {
+    int32_t n_layers, batch, hq, D, dtype, max_splits;
+    float scale;
+    float* part_acc;            // [layer][b][split][16][D]
+    float* part_ml;             // [layer][b][split][2][16]
+    AttendLayer L[LSA_MAX_LAYERS];
+};
+constexpr int kAttendRows = 32;
+size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows);
+hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid = nullptr);
+
+}  // namespace lsa

@@ -1,0 +1,117 @@
+"""Device set-up of a decode-step workload from the seeded generators.
+
+Builds, for a ``lsa_inputs.Workload``: the source layer's indexer keys in HBM,
+one ``lsa.Pool`` per sparse layer (window rows in the KV buffer, every
+compressed row stored in the cold pool -- pinned host memory is filled in
+place), the per-step indexer and attention queries, and the output buffers of
+``lsa.decode_step``.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+import lsa_inputs as L
+
+from . import lsa
+
+
+def to_device(x: np.ndarray, dtype: str, dev) -> torch.Tensor:
+    """Upload values already encoded for `dtype` (f32 array, or bf16/f16 16-bit codes)."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+    t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+def torch_dtype(dtype: str):
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+
+
+class DeviceWorkload:
+    def __init__(self, wl: L.Workload, device: int = 0, keep_host: bool = False, ctx: Optional[lsa.Ctx] = None,
+                 log=None):
+        self.wl = wl
+        self.dev = torch.device(f"cuda:{device}")
+        self.ctx = ctx if ctx is not None else lsa.Ctx(device)
+        self.keep_host = keep_host
+        say = log or (lambda *_: None)
+        B, D, W = wl.batch, wl.kv_dim, wl.window
+        keys_np = [L.indexer_keys(wl, b) for b in range(B)]
+        self.keys = to_device(np.stack(keys_np), wl.key_dtype, self.dev)
+        self.keys_np = keys_np if keep_host else None
+        say(f"keys {tuple(self.keys.shape)} {wl.key_dtype}")
+        self.pools: List[lsa.Pool] = []
+        self.kv: List[torch.Tensor] = []
+        self.windows: List[List[np.ndarray]] = []
+        self.stores: List[List[np.ndarray]] = []
+        np_row = np.float32 if wl.kv_dtype == "f32" else np.uint16
+        for l in range(wl.n_layers):
+            rows = lsa.Pool.rows_needed(wl.ctx, wl.layer_ratios[l], W, wl.gpu_chunks)
+            kv = torch.zeros((B, rows, D), dtype=torch_dtype(wl.kv_dtype), device=self.dev)
+            pool = lsa.Pool(wl.ctx, wl.layer_ratios[l], kv, W, wl.gpu_chunks, wl.k, D, B, cold=wl.cold)
+            wins, stores = [], []
+            for b in range(B):
+                win = L.encode(L.window_rows(wl, l, b), wl.kv_dtype)
+                kv[b, :W] = to_device(win, wl.kv_dtype, self.dev)
+                host = pool.host_rows(b, np_row)
+                if host is not None and wl.kv_dtype == "f32":
+                    L.cold_rows(wl, l, b, out=host)
+                    pool.mark_stored(b, 0, pool.cap)
+                    store = host
+                elif host is not None:
+                    host[:] = L.encode(L.cold_rows(wl, l, b), wl.kv_dtype)
+                    pool.mark_stored(b, 0, pool.cap)
+                    store = host
+                else:
+                    store = L.encode(L.cold_rows(wl, l, b), wl.kv_dtype)
+                    pool.store(b, 0, store)
+                wins.append(win)
+                stores.append(store if keep_host else None)
+            self.pools.append(pool)
+            self.kv.append(kv)
+            self.windows.append(wins)
+            self.stores.append(stores)
+            say(f"layer {l}: ratio {wl.layer_ratios[l]} cap {pool.cap} swap {pool.swap} cold {wl.cold}")
+        torch.cuda.synchronize()
+        nL, k = wl.n_layers, wl.k
+        self.scores = torch.zeros((B, wl.n_src), dtype=torch.float32, device=self.dev)
+        self.sel = torch.zeros((B, k), dtype=torch.int32, device=self.dev)
+        self.count = torch.zeros((B,), dtype=torch.int32, device=self.dev)
+        self.out = torch.zeros((nL, B, wl.hq, D), dtype=torch.float32, device=self.dev)
+        self.phys = torch.zeros((nL, B, W + k), dtype=torch.int32, device=self.dev)
+        self.n_rows = torch.zeros((nL, B), dtype=torch.int32, device=self.dev)
+        self.q_idx = self.w_idx = self.q_attn = None
+        self.q_idx_np = self.w_idx_np = self.q_attn_np = None
+
+    def make_steps(self, steps: int) -> None:
+        """Draw the indexer and attention queries of `steps` steps and upload them."""
+        wl = self.wl
+        B, nL = wl.batch, wl.n_layers
+        qs, ws = [], []
+        for b in range(B):
+            q, w = L.indexer_query_steps(wl, b, steps)
+            qs.append(q)
+            ws.append(w)
+        self.q_idx_np = np.stack(qs, axis=1)          # [steps][B][n_idx][H][dk]
+        self.w_idx_np = np.stack(ws, axis=1)          # [steps][B][n_idx][H]
+        self.q_attn_np = np.stack([np.stack([np.stack([L.attn_query(wl, l, b, t) for b in range(B)])
+                                             for l in range(nL)]) for t in range(steps)])
+        self.q_idx = torch.from_numpy(self.q_idx_np).to(self.dev)
+        self.w_idx = torch.from_numpy(self.w_idx_np).to(self.dev)
+        self.q_attn = torch.from_numpy(self.q_attn_np).to(self.dev)
+
+    def step(self, t: int, stream=None) -> None:
+        wl = self.wl
+        lsa.decode_step(self.ctx, keys=self.keys, q_idx=self.q_idx[t], w_idx=self.w_idx[t], pools=self.pools,
+                        q_attn=self.q_attn[t], out=self.out, scores=self.scores, sel=self.sel, count=self.count,
+                        k=wl.k, src_ratio=wl.src_ratio, scale=wl.scale, ensemble=wl.ensemble, mode=wl.mode,
+                        tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys, n_rows=self.n_rows,
+                        stream=stream)
+
+    def reset_pools(self) -> None:
+        for p in self.pools:
+            p.reset()
+        torch.cuda.synchronize()

@@ -162,8 +162,8 @@ class Workload:
 # 1312th distinct largest step-0 scores pooled over the batch (0.5% of 4 x 65536),
 # and the per-step redraw fraction of the 1M workload, chosen so that consecutive
 # top-512 sets overlap by about 80%.  Both written by oracle/calibrate_workloads.py.
-THRESH_256K_TAU = None
-SWAP_1M_DRIFT = None
+THRESH_256K_TAU = 0.9999999942439965
+SWAP_1M_DRIFT = 0.01875
 
 WORKLOADS = {
     # tiny single-layer step: 8K ctx, ratio 4, 1 indexer x 4 heads x 64, top-64

@@ -1,0 +1,107 @@
+"""GPU parity of lsa_attend with oracle.attend (fp32 1e-5, bf16 2e-2 relative),
+and bit-identical outputs for the same rows in different physical places."""
+import numpy as np
+import pytest
+import torch
+
+import lsa_inputs as L
+import oracle
+from learned_sparse_kv_amd import lsa
+from learned_sparse_kv_amd.workload import to_device
+
+from gpu_util import DEV, RTOL, rel_err_rows, say
+
+pytestmark = pytest.mark.gpu
+_CTX = None
+
+
+def ctx():
+    global _CTX
+    if _CTX is None:
+        _CTX = lsa.Ctx(0)
+    return _CTX
+
+
+def attend_case(rng, B, hq, D, W, n_sel, cap, dtype, stride_extra=3):
+    q = L.grid_uniform(rng, (B, hq, D))
+    wins = [L.encode(L.grid_uniform(rng, (W, D)), dtype) for _ in range(B)]
+    stores = [L.encode(L.grid_uniform(rng, (cap, D)), dtype) for _ in range(B)]
+    sels = [np.sort(rng.choice(cap, size=n, replace=False)).astype(np.int32) for n in n_sel]
+    # physical buffer: window rows, then the store rows at a shifted place
+    rows = W + cap + 5
+    kv = np.zeros((B, rows) + (D,), stores[0].dtype)
+    phys = np.full((B, W + max(n_sel) + stride_extra), -1, np.int32)
+    for b in range(B):
+        kv[b, :W] = wins[b]
+        kv[b, W + 5:] = stores[b]
+        phys[b, :W] = np.arange(W)
+        phys[b, W:W + n_sel[b]] = W + 5 + sels[b]
+    nrows = np.array([W + n for n in n_sel], np.int32)
+    out = torch.full((B, hq, D), float("nan"), device=DEV)
+    lsa.attend(ctx(), torch.from_numpy(q).to(DEV), to_device(kv, dtype, DEV), torch.from_numpy(phys).to(DEV),
+               torch.from_numpy(nrows).to(DEV), out, 1 / np.sqrt(D))
+    got = out.cpu().numpy()
+    for b in range(B):
+        want = oracle.attend(q[b], wins[b], stores[b], dtype, sels[b], 1 / np.sqrt(D))
+        err = rel_err_rows(got[b], want)
+        assert err <= RTOL[dtype], f"seq {b}: rel err {err}"
+    return got
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [512, 256, 128])
+def test_attend_matches_oracle(dtype, D):
+    say(f"attend D={D} {dtype}")
+    rng = np.random.default_rng(D + (dtype == "bf16"))
+    attend_case(rng, 4, 16, D, 128, [512, 0, 33, 1], 2048, dtype)
+
+
+@pytest.mark.parametrize("W,n", [(0, 1), (0, 31), (0, 32), (0, 33), (5, 0), (128, 64), (1, 639)])
+def test_attend_row_counts(W, n):
+    rng = np.random.default_rng(W * 1000 + n)
+    attend_case(rng, 1, 5, 512, W, [n], 700, "f32")
+
+
+def test_no_rows_gives_zero():
+    out = torch.full((1, 16, 512), float("nan"), device=DEV)
+    lsa.attend(ctx(), torch.zeros((1, 16, 512), device=DEV), torch.zeros((1, 4, 512), device=DEV),
+               torch.zeros((1, 4), dtype=torch.int32, device=DEV), torch.zeros((1,), dtype=torch.int32, device=DEV),
+               out, 0.1)
+    assert torch.all(out == 0)
+
+
+def test_physical_placement_does_not_change_bits():
+    # page 1 (swap output invariance) / page 3 (residency only changes occupancy):
+    # the same row list read from two different physical layouts gives the same bits
+    rng = np.random.default_rng(11)
+    D, W, n = 512, 128, 300
+    q = torch.from_numpy(L.grid_uniform(rng, (1, 16, D))).to(DEV)
+    rows = L.grid_uniform(rng, (W + n, D))
+    perm = rng.permutation(W + n + 50)[: W + n]
+    kv_a = torch.from_numpy(rows[None]).to(DEV)
+    big = np.zeros((W + n + 50, D), np.float32)
+    big[perm] = rows
+    kv_b = torch.from_numpy(big[None]).to(DEV)
+    pa = torch.arange(W + n, dtype=torch.int32, device=DEV)[None]
+    pb = torch.from_numpy(perm.astype(np.int32)[None]).to(DEV)
+    nr = torch.tensor([W + n], dtype=torch.int32, device=DEV)
+    oa = torch.zeros((1, 16, D), device=DEV)
+    ob = torch.zeros((1, 16, D), device=DEV)
+    lsa.attend(ctx(), q, kv_a, pa, nr, oa, 0.05)
+    lsa.attend(ctx(), q, kv_b, pb, nr, ob, 0.05)
+    assert torch.equal(oa.view(torch.int32), ob.view(torch.int32))
+
+
+def test_all_chunks_is_dense_attention():
+    rng = np.random.default_rng(12)
+    D, W, cap = 512, 128, 512
+    q = L.grid_uniform(rng, (1, 16, D))
+    rows = L.grid_uniform(rng, (W + cap, D))
+    out = torch.zeros((1, 16, D), device=DEV)
+    lsa.attend(ctx(), torch.from_numpy(q).to(DEV), torch.from_numpy(rows[None]).to(DEV),
+               torch.arange(W + cap, dtype=torch.int32, device=DEV)[None],
+               torch.tensor([W + cap], dtype=torch.int32, device=DEV), out, 1 / np.sqrt(D))
+    z = (q[0].astype(np.float64) @ rows.T.astype(np.float64)) / np.sqrt(D)
+    p = np.exp(z - z.max(1, keepdims=True))
+    want = (p / p.sum(1, keepdims=True)) @ rows.astype(np.float64)
+    assert rel_err_rows(out[0].cpu().numpy(), want) <= 1e-5
