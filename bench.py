@@ -33,9 +33,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(name):
-    with open(os.path.join(ROOT, "learned_sparse_kv_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(*names):
+    """sha256[:16] over the named csrc files (the kernel and the header it includes)."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "learned_sparse_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(workload, score_src_hash):
@@ -45,7 +49,7 @@ def stored_traffic(workload, score_src_hash):
     if not os.path.exists(path):
         return None
     txt = open(path).read()
-    m_hash = re.search(r"fm_score\.hip sha256\[:16\]:\s*([0-9a-f]+)", txt)
+    m_hash = re.search(r"fm_score\.hip\+lsa_internal\.hpp sha256\[:16\]:\s*([0-9a-f]+)", txt)
     m_bytes = re.search(r"hbm_bytes_per_dispatch:\s*([0-9.eE+]+)", txt)
     if not m_hash or not m_bytes or m_hash.group(1) != score_src_hash:
         return None
@@ -134,7 +138,7 @@ def main():
     sa_ms = avg["score"] + avg["attend"] + avg["combine"]
     sa_frac = (score_bytes + attend_bytes) / (sa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
 
-    src_hash = kernel_source_hash("fm_score.hip")
+    src_hash = kernel_source_hash("fm_score.hip", "lsa_internal.hpp")
     traffic = stored_traffic(wl.name, src_hash)
     roofline = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "fm_score",
