@@ -116,8 +116,10 @@ def main():
     t_start = time.perf_counter()
     for t in range(Wm, Wm + K):
         dw.step(t)
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t_end = time.perf_counter()
+    log(f"host enqueue {(t_enq - t_start) * 1e6 / K:.1f} us/step, wall {(t_end - t_start) * 1e6 / K:.1f} us/step")
     ktimes = dw.ctx.timing_read()
     dw.ctx.set_timing(False)
     ms_per_step = (t_end - t_start) * 1e3 / K

@@ -256,7 +256,8 @@ lsa_status lsa_stage(lsa_pool* pool, const int32_t* sel, const int32_t* count, i
  *        as zero rows (a malformed list cannot read past the buffer)
  *   phys device i32 [batch][phys_stride]; n_rows device i32 [batch], values
  *        clamped to [0, phys_stride]
- * Supported: 1 <= hq <= 16, kv_dim in {128, 256, 512}, 1 <= batch <= LSA_MAX_BATCH. */
+ * Supported: 1 <= hq <= 16, kv_dim in {128, 256, 512}, 1 <= batch <= LSA_MAX_BATCH,
+ * phys_stride <= 5120. */
 lsa_status lsa_attend(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dtype,
                       int64_t kv_stride_b, int64_t kv_rows, const int32_t* phys,
                       int32_t phys_stride, const int32_t* n_rows, int32_t batch, int32_t hq,

@@ -109,7 +109,6 @@ __global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a
     };
 
     load_tile(t, pre);
-
     while (t < total) {
         const int b = seq_of(t);
         if (b != cur_b) {

@@ -7,19 +7,29 @@
 // out on the host), then caps at k by the same order.  Output: the chosen
 // indices in ascending order, -1 padding, and the count.
 //
-// Design (gfx950): scores become order-preserving 32-bit keys (-0 folded into
-// +0).  A 1024-thread workgroup holds up to 32768 keys in registers (E per
-// thread, contiguous indices per thread so thread order is index order) and
-// finds the K-th largest key T by four 8-bit radix passes over LDS
-// histograms (one histogram per wave; each wave first adds the lanes that
-// share the first active lane's digit with one atomic, which takes the
-// contention out of the clustered high digits).  The chosen set is every key
-// > T plus the lowest-indexed (K - #greater) keys equal to T: two block
-// scans (ties by index, then output positions) compact it in index order.
-// Long segments run two stages: blocks of 1024*E entries emit their own
-// top-k candidates in index order; one workgroup per segment then selects
-// from the concatenated candidates.  The global top-k is always inside the
-// union of per-block top-k sets, so the result is exact.
+// Design (gfx950).  Scores become order-preserving 32-bit keys (-0 folded
+// into +0).  Two paths:
+//
+// * Segments of at most 32768 entries: one 1024-thread workgroup holds the
+//   keys in registers (contiguous indices per thread, so thread order is index
+//   order), finds the K-th largest key T with four 8-bit radix passes over an
+//   LDS histogram, and compacts {key > T} plus the lowest-indexed keys equal to
+//   T with two block scans.  Histogram atomics are pre-aggregated per wave:
+//   the lanes sharing the first active lane's digit add with one atomic, which
+//   removes the contention of clustered high digits.
+//
+// * Longer segments: (1) every 4096-entry block builds an 11-bit key histogram
+//   in LDS and adds it to a per-segment global histogram; (2) every 1024-entry
+//   block finds the boundary bucket b* holding the K-th largest key from that
+//   histogram and keeps, in index order (block scan, no atomics), its entries
+//   in buckets >= b*; (3) one workgroup per segment gathers the kept entries in
+//   block order -- which is global index order -- resolves b* with radix
+//   passes over the 21 key bits below the bucket, and compacts {above b*} +
+//   {candidates > T} + {the first candidates equal to T}: ties fall to the
+//   lowest index because the list is in index order, and the output is
+//   already ascending.  If more than 8192 entries are kept, step (3) falls back
+//   to an exact streaming select over the whole segment.  Step (3) leaves the
+//   histogram zeroed for the next call.
 #include "lsa_internal.hpp"
 
 namespace lsa {
@@ -28,62 +38,62 @@ namespace {
 
 constexpr int kNT = 1024;
 constexpr int kNW = kNT / 64;
+constexpr int kBlk = 4096;          // entries per block of the histogram kernel
+constexpr int kColBlk = 1024;       // entries per block of the collect kernel
+constexpr int kBitmapEntries = 262144;               // segments up to this length sort via a bitmap
+constexpr int kBitmapWords = kBitmapEntries / 32;
+constexpr int kBlkThreads = 256;
 
-struct SelShared {
-    uint32_t hist[kNW][256];
+struct KthShared {
+    uint32_t hist[256];
     int scan[kNW + 1];
     uint32_t digit;
     int above;
 };
 
+__device__ inline int seg_valid(const SelectArgs& a, int seg) {
+    return a.has_n_valid ? a.n_valid[seg] : a.n_valid_uniform;
+}
+
+// Given a 256-bin histogram of the digits of the still-tied keys, finds the
+// digit d holding the rem-th largest key; sh.digit = d, sh.above = keys with a
+// larger digit.  Threads tid < 256 own digit 255 - tid.
+__device__ inline void find_digit(const uint32_t* hist, int rem, KthShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t d = 255u - (uint32_t)(tid & 255);
+    const int cnt = tid < 256 ? (int)hist[d] : 0;
+    const int incl = wave_incl_scan(cnt);
+    if (tid < 256 && lane == 63) sh.scan[wave] = incl;
+    __syncthreads();
+    if (tid < 256) {
+        int off = 0;
+        for (int w = 0; w < wave; ++w) off += sh.scan[w];
+        const int ge = off + incl;
+        if (ge >= rem && ge - cnt < rem) {
+            sh.digit = d;
+            sh.above = ge - cnt;
+        }
+    }
+    __syncthreads();
+}
+
 // K-th largest key among the valid ones (1 <= K <= #valid).  Returns T and the
 // number of keys equal to T that belong to the top K.
 template <int E>
-__device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int K, SelShared& sh,
+__device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int K, KthShared& sh,
                           uint32_t* T_out, int* need_eq_out) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t prefix = 0, mask = 0;
     int rem = K;
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        for (int i = tid; i < kNW * 256; i += kNT) (&sh.hist[0][0])[i] = 0u;
+        if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0u;
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const bool act = valid[e] && (key[e] & mask) == prefix;
-            const uint32_t dg = (key[e] >> shift) & 255u;
-            const uint64_t am = __ballot(act);
-            if (am) {
-                const int first = __ffsll((unsigned long long)am) - 1;
-                const uint32_t d0 = __shfl(dg, first, 64);
-                const uint64_t same = __ballot(act && dg == d0);
-                if (lane == first) atomicAdd(&sh.hist[wave][d0], (uint32_t)__popcll(same));
-                if (act && dg != d0) atomicAdd(&sh.hist[wave][dg], 1u);
-            }
-        }
+        for (int e = 0; e < E; ++e)
+            hist_add(sh.hist, valid[e] && (key[e] & mask) == prefix, (key[e] >> shift) & 255u);
         __syncthreads();
-        // thread tid < 256 owns digit 255 - tid, so an inclusive scan over tid
-        // counts the keys whose digit is >= that digit
-        const uint32_t d = 255u - (uint32_t)(tid & 255);
-        int cnt = 0;
-        if (tid < 256) {
-#pragma unroll
-            for (int w = 0; w < kNW; ++w) cnt += (int)sh.hist[w][d];
-        }
-        const int incl = wave_incl_scan(cnt);
-        if (tid < 256 && lane == 63) sh.scan[wave] = incl;
-        __syncthreads();
-        if (tid < 256) {
-            int off = 0;
-            for (int w = 0; w < wave; ++w) off += sh.scan[w];
-            const int ge = off + incl;
-            if (ge >= rem && ge - cnt < rem) {
-                sh.digit = d;
-                sh.above = ge - cnt;
-            }
-        }
-        __syncthreads();
+        find_digit(sh.hist, rem, sh);
         prefix |= sh.digit << shift;
         mask |= 255u << shift;
         rem -= sh.above;
@@ -93,11 +103,11 @@ __device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int 
     *need_eq_out = rem;
 }
 
-// Marks the chosen keys (all > T, plus the first need_eq equal to T in index
-// order) and returns each chosen key's output position in index order.
+// Marks the chosen keys (all > T, plus the first need_eq equal to T in thread
+// order = index order) and returns the first output position of this thread.
 template <int E>
 __device__ void block_choose(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t T, int need_eq,
-                             SelShared& sh, bool (&take)[E], int* pos0) {
+                             KthShared& sh, bool (&take)[E], int* pos0) {
     int c_eq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) c_eq += (valid[e] && key[e] == T) ? 1 : 0;
@@ -116,88 +126,48 @@ __device__ void block_choose(const uint32_t (&key)[E], const bool (&valid)[E], u
 }
 
 template <int E>
-__global__ __launch_bounds__(kNT) void select_stage1(const SelectArgs a) {
-    __shared__ SelShared sh;
-    const int tid = threadIdx.x;
-    const int seg = blockIdx.y, blk = blockIdx.x;
-    const int n_valid = a.has_n_valid ? a.n_valid[seg] : a.n_valid_uniform;
-    const int64_t base = (int64_t)blk * (kNT * E) + (int64_t)tid * E;
-    const float* sc = a.scores + (int64_t)seg * a.n_keys;
-
-    uint32_t key[E];
-    bool valid[E];
-    int c_valid = 0;
+__device__ inline void load_scores(const float* sc, int64_t base, int n_valid, float (&x)[E], bool (&v)[E]) {
+    const bool vec = E >= 4 && (((uintptr_t)(sc + base)) & 15u) == 0 && base + E <= n_valid;
+    if (vec) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int64_t j = base + e;
-        bool v = j < n_valid;
-        const float x = v ? sc[j] : 0.0f;
-        if (a.mode == LSA_SELECT_THRESHOLD) v = v && (x > a.t_f);
-        key[e] = order_key(x);
-        valid[e] = v;
-        c_valid += v ? 1 : 0;
-    }
-    int n_ok;
-    block_excl_scan<kNT>(c_valid, sh.scan, &n_ok);
-    const int K = n_ok < a.k ? n_ok : a.k;
-
-    const bool final_stage = a.nblk == 1;
-    int32_t* out_sel = a.sel + (int64_t)seg * a.stride;
-    if (K == 0) {
-        if (final_stage) {
-            for (int i = tid; i < a.stride; i += kNT) out_sel[i] = -1;
-            if (tid == 0) a.count[seg] = 0;
-        } else if (tid == 0) {
-            a.cand_n[seg * a.nblk + blk] = 0;
+        for (int e = 0; e < E; e += 4) {
+            const f32x4 q = *reinterpret_cast<const f32x4*>(sc + base + e);
+            x[e] = q[0];
+            x[e + 1] = q[1];
+            x[e + 2] = q[2];
+            x[e + 3] = q[3];
         }
-        return;
-    }
-    uint32_t T;
-    int need_eq;
-    block_kth<E>(key, valid, K, sh, &T, &need_eq);
-    bool take[E];
-    int pos;
-    block_choose<E>(key, valid, T, need_eq, sh, take, &pos);
-    if (final_stage) {
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (take[e] && pos < a.stride) out_sel[pos++] = (int32_t)(base + e);
-        for (int i = K + tid; i < a.stride; i += kNT) out_sel[i] = -1;
-        if (tid == 0) a.count[seg] = K;
+        for (int e = 0; e < E; ++e) v[e] = true;
     } else {
-        const int64_t cb = ((int64_t)seg * a.nblk + blk) * a.k;
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (take[e] && pos < a.k) {
-                a.cand_key[cb + pos] = key[e];
-                a.cand_idx[cb + pos] = (int32_t)(base + e);
-                ++pos;
-            }
-        if (tid == 0) a.cand_n[seg * a.nblk + blk] = K;
+        for (int e = 0; e < E; ++e) {
+            v[e] = base + e < n_valid;
+            x[e] = v[e] ? sc[base + e] : 0.0f;
+        }
     }
 }
 
+// ---------------------------------------------------------------- path 0
 template <int E>
-__global__ __launch_bounds__(kNT) void select_stage2(const SelectArgs a) {
-    __shared__ SelShared sh;
+__global__ __launch_bounds__(kNT) void select_single(const SelectArgs a) {
+    __shared__ KthShared sh;
     const int tid = threadIdx.x;
     const int seg = blockIdx.x;
-    const int slots = a.nblk * a.k;
-    const int64_t cb = (int64_t)seg * slots;
+    const int n_valid = seg_valid(a, seg);
+    const int64_t base = (int64_t)tid * E;
+    const float* sc = a.scores + (int64_t)seg * a.n_keys;
 
-    uint32_t key[E];
-    int32_t idx[E];
+    float x[E];
     bool valid[E];
+    load_scores<E>(sc, base, n_valid, x, valid);
+    uint32_t key[E];
     int c_valid = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const int p = tid * E + e;
-        bool v = p < slots;
-        if (v) v = (p % a.k) < a.cand_n[seg * a.nblk + p / a.k];
-        key[e] = v ? a.cand_key[cb + p] : 0u;
-        idx[e] = v ? a.cand_idx[cb + p] : 0;
-        valid[e] = v;
-        c_valid += v ? 1 : 0;
+        if (a.mode == LSA_SELECT_THRESHOLD) valid[e] = valid[e] && (x[e] > a.t_f);
+        key[e] = order_key(x[e]);
+        c_valid += valid[e] ? 1 : 0;
     }
     int n_ok;
     block_excl_scan<kNT>(c_valid, sh.scan, &n_ok);
@@ -216,9 +186,278 @@ __global__ __launch_bounds__(kNT) void select_stage2(const SelectArgs a) {
     block_choose<E>(key, valid, T, need_eq, sh, take, &pos);
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        if (take[e] && pos < a.stride) out_sel[pos++] = idx[e];
+        if (take[e] && pos < a.stride) out_sel[pos++] = (int32_t)(base + e);
     for (int i = K + tid; i < a.stride; i += kNT) out_sel[i] = -1;
     if (tid == 0) a.count[seg] = K;
+}
+
+// ---------------------------------------------------------------- path 1
+__device__ inline bool entry(const SelectArgs& a, const float* sc, int64_t j, int n_valid, uint32_t* key) {
+    bool v = j < n_valid;
+    const float x = v ? sc[j] : 0.0f;
+    if (a.mode == LSA_SELECT_THRESHOLD) v = v && (x > a.t_f);
+    *key = order_key(x);
+    return v;
+}
+
+__global__ __launch_bounds__(kBlkThreads) void sel_hist_kernel(const SelectArgs a) {
+    constexpr int PER = kBlk / kBlkThreads;
+    __shared__ uint32_t h[kSelBins];
+    const int tid = threadIdx.x, seg = blockIdx.y;
+    const int64_t base = (int64_t)blockIdx.x * kBlk;
+    const int n_valid = seg_valid(a, seg);
+    const float* sc = a.scores + (int64_t)seg * a.n_keys;
+    // all loads first: one memory latency per block instead of one per entry
+    float x[PER];
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int64_t j = base + it * kBlkThreads + tid;
+        x[it] = j < n_valid ? sc[j] : 0.0f;
+    }
+    for (int i = tid; i < kSelBins; i += kBlkThreads) h[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int64_t j = base + it * kBlkThreads + tid;
+        bool v = j < n_valid;
+        if (a.mode == LSA_SELECT_THRESHOLD) v = v && (x[it] > a.t_f);
+        hist_add(h, v, order_key(x[it]) >> kSelShift);
+    }
+    __syncthreads();
+    uint32_t* g = a.hist + (int64_t)seg * kSelBins;
+    for (int i = tid; i < kSelBins; i += kBlkThreads) {
+        const uint32_t c = h[i];
+        if (c) atomicAdd(&g[i], c);
+    }
+}
+
+// From the segment histogram: out[0] = boundary bucket b* (-1 if nothing is
+// chosen), out[1] = entries in buckets above b*, out[2] = valid entries.
+template <int NT>
+__device__ void find_boundary(const uint32_t* g, int k, int* s_scan, int* out) {
+    constexpr int PER = kSelBins / NT;
+    const int t = threadIdx.x;
+    uint32_t c[PER];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        c[i] = g[kSelBins - 1 - PER * t - i];
+        local += (int)c[i];
+    }
+    int total;
+    int run = block_excl_scan<NT>(local, s_scan, &total);
+    const int K = total < k ? total : k;
+    if (t == 0) {
+        out[0] = -1;
+        out[1] = 0;
+        out[2] = total;
+    }
+    __syncthreads();
+    if (K > 0) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (run < K && run + (int)c[i] >= K) {
+                out[0] = kSelBins - 1 - PER * t - i;
+                out[1] = run;
+            }
+            run += (int)c[i];
+        }
+    }
+    __syncthreads();
+}
+
+// Every 1024-entry block keeps, in index order, its entries in buckets >= b*
+// (those above b* are chosen for sure; those in b* are the candidates), with
+// their keys; the top index bit marks a candidate.
+__global__ __launch_bounds__(kBlkThreads) void sel_collect_kernel(const SelectArgs a) {
+    constexpr int PER = kColBlk / kBlkThreads;   // 4 consecutive entries per thread
+    __shared__ int s_scan[kBlkThreads / 64 + 1];
+    __shared__ int s_b[3];
+    const int tid = threadIdx.x, seg = blockIdx.y, blk = blockIdx.x;
+    const int n_valid = seg_valid(a, seg);
+    const float* sc = a.scores + (int64_t)seg * a.n_keys;
+    const int64_t base = (int64_t)blk * kColBlk + tid * PER;
+    float x[PER];
+    bool v[PER];
+    load_scores<PER>(sc, base, n_valid, x, v);
+    find_boundary<kBlkThreads>(a.hist + (int64_t)seg * kSelBins, a.k, s_scan, s_b);
+    const int bstar = s_b[0];
+    uint32_t key[PER];
+    int keep[PER];
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        if (a.mode == LSA_SELECT_THRESHOLD) v[e] = v[e] && (x[e] > a.t_f);
+        key[e] = order_key(x[e]);
+        const int bin = (int)(key[e] >> kSelShift);
+        keep[e] = (bstar >= 0 && v[e] && bin >= bstar) ? (bin == bstar ? 2 : 1) : 0;
+        c += keep[e] ? 1 : 0;
+    }
+    int tot;
+    int pos = block_excl_scan<kBlkThreads>(c, s_scan, &tot);
+    const int64_t ob = ((int64_t)seg * a.nblk + blk) * kColBlk;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        if (!keep[e]) continue;
+        a.blk_idx[ob + pos] = (int32_t)(base + e) | (keep[e] == 2 ? (int32_t)0x80000000 : 0);
+        a.blk_key[ob + pos] = key[e];
+        ++pos;
+    }
+    if (tid == 0) a.blk_count[(int64_t)seg * a.nblk + blk] = tot;
+}
+
+// Exact selection straight from the scores by one workgroup: four radix passes
+// over the whole segment, then an index-ordered compaction.  Used when the
+// boundary bucket overflows the candidate list.
+__device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid, int K, KthShared& sh,
+                              int32_t* out_sel) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, mask = 0;
+    int rem = K;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        if (tid < 256) sh.hist[tid] = 0u;
+        __syncthreads();
+        for (int64_t c = 0; c < n_valid; c += kNT) {
+            uint32_t key;
+            const bool v = entry(a, sc, c + tid, n_valid, &key);
+            hist_add(sh.hist, v && (key & mask) == prefix, (key >> shift) & 255u);
+        }
+        __syncthreads();
+        find_digit(sh.hist, rem, sh);
+        prefix |= sh.digit << shift;
+        mask |= 255u << shift;
+        rem -= sh.above;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;
+    const int need_eq = rem;
+    constexpr int E = 8;
+    int run_eq = 0, run_out = 0;
+    for (int64_t c = 0; c < n_valid; c += (int64_t)kNT * E) {
+        uint32_t key[E];
+        bool v[E];
+        int c_eq = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            v[e] = entry(a, sc, c + (int64_t)tid * E + e, n_valid, &key[e]);
+            c_eq += (v[e] && key[e] == T) ? 1 : 0;
+        }
+        int tot_eq;
+        int r = run_eq + block_excl_scan<kNT>(c_eq, sh.scan, &tot_eq);
+        bool take[E];
+        int c_take = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool eq = v[e] && key[e] == T;
+            take[e] = (v[e] && key[e] > T) || (eq && r < need_eq);
+            r += eq ? 1 : 0;
+            c_take += take[e] ? 1 : 0;
+        }
+        int tot_take;
+        int pos = run_out + block_excl_scan<kNT>(c_take, sh.scan, &tot_take);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (take[e] && pos < a.stride) out_sel[pos++] = (int32_t)(c + (int64_t)tid * E + e);
+        run_eq += tot_eq;
+        run_out += tot_take;
+    }
+}
+
+// One workgroup per segment: gathers the blocks' kept entries (global index
+// order), resolves the boundary bucket with radix passes over the 21 key bits
+// below it, and writes the chosen indices (already ascending).
+__global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
+    __shared__ KthShared sh;
+    __shared__ int s_b[3];
+    __shared__ int32_t s_idx[kSelKeepCap];
+    __shared__ uint32_t s_key[kSelKeepCap];
+    const int tid = threadIdx.x, seg = blockIdx.x;
+    uint32_t* g = a.hist + (int64_t)seg * kSelBins;
+    find_boundary<kNT>(g, a.k, sh.scan, s_b);
+    const int total = s_b[2];
+    const int K = total < a.k ? total : a.k;
+    const int bstar = s_b[0];
+    const int above = s_b[1];
+    int32_t* out_sel = a.sel + (int64_t)seg * a.stride;
+
+    // block offsets: thread t owns blocks [t*PB, (t+1)*PB)
+    const int nb = a.nblk;
+    const int PB = (nb + kNT - 1) / kNT;
+    const int32_t* cnt = a.blk_count + (int64_t)seg * nb;
+    int mine = 0;
+    for (int q = 0; q < PB; ++q) {
+        const int bi = tid * PB + q;
+        if (bi < nb && K > 0) mine += cnt[bi];
+    }
+    int n_keep;
+    int off = block_excl_scan<kNT>(mine, sh.scan, &n_keep);
+    if (K > 0 && n_keep <= kSelKeepCap) {
+        for (int q = 0; q < PB; ++q) {
+            const int bi = tid * PB + q;
+            if (bi >= nb) break;
+            const int c = cnt[bi];
+            const int64_t ob = ((int64_t)seg * nb + bi) * kColBlk;
+            for (int i = 0; i < c; ++i) {
+                s_idx[off + i] = a.blk_idx[ob + i];
+                s_key[off + i] = a.blk_key[ob + i];
+            }
+            off += c;
+        }
+        __syncthreads();
+        // radix passes over bits 20..0 of the candidates' keys (bucket b* fixes the rest)
+        const int need = K - above;
+        uint32_t prefix = (uint32_t)bstar << kSelShift, mask = ~((1u << kSelShift) - 1u);
+        int rem = need;
+        const int shifts[3] = {13, 5, 0};
+        const int widths[3] = {8, 8, 5};
+#pragma unroll 1
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = shifts[pass];
+            const uint32_t dmask = (1u << widths[pass]) - 1u;
+            if (tid < 256) sh.hist[tid] = 0u;
+            __syncthreads();
+            for (int p0 = 0; p0 < n_keep; p0 += kNT) {
+                const int p = p0 + tid;
+                const bool act = p < n_keep && s_idx[p] < 0 && (s_key[p] & mask) == prefix;
+                hist_add(sh.hist, act, p < n_keep ? (s_key[p] >> shift) & dmask : 0u);
+            }
+            __syncthreads();
+            find_digit(sh.hist, rem, sh);
+            prefix |= sh.digit << shift;
+            mask |= dmask << shift;
+            rem -= sh.above;
+            __syncthreads();
+        }
+        const uint32_t T = prefix;
+        const int need_eq = rem;
+        // index-ordered compaction: all entries above b*, candidates > T, and
+        // the first need_eq candidates equal to T
+        int run_eq = 0, run_out = 0;
+        for (int p0 = 0; p0 < n_keep; p0 += kNT) {
+            const int p = p0 + tid;
+            const bool in = p < n_keep;
+            const int32_t raw = in ? s_idx[p] : 0;
+            const uint32_t k2 = in ? s_key[p] : 0u;
+            const bool cand = in && raw < 0;
+            const bool eq = cand && k2 == T;
+            int tot_eq;
+            const int r = run_eq + block_excl_scan<kNT>(eq ? 1 : 0, sh.scan, &tot_eq);
+            const bool take = in && (!cand || k2 > T || (eq && r < need_eq));
+            int tot_take;
+            const int pos = run_out + block_excl_scan<kNT>(take ? 1 : 0, sh.scan, &tot_take);
+            if (take && pos < a.stride) out_sel[pos] = raw & 0x7FFFFFFF;
+            run_eq += tot_eq;
+            run_out += tot_take;
+        }
+    } else if (K > 0) {
+        stream_select(a, a.scores + (int64_t)seg * a.n_keys, seg_valid(a, seg), K, sh, out_sel);
+    }
+    for (int i = K + tid; i < a.stride; i += kNT) out_sel[i] = -1;
+    if (tid == 0) a.count[seg] = K;
+    __syncthreads();
+    for (int i = tid; i < kSelBins; i += kNT) g[i] = 0u;
 }
 
 int next_pow2(int x) {
@@ -227,62 +466,62 @@ int next_pow2(int x) {
     return p;
 }
 
-hipError_t launch_s1(const SelectArgs& a, hipStream_t s) {
-    const dim3 grid(a.nblk, a.n_seg), block(kNT);
-    switch (a.e1) {
-        case 1: hipLaunchKernelGGL(select_stage1<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(select_stage1<2>, grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL(select_stage1<4>, grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL(select_stage1<8>, grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL(select_stage1<16>, grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL(select_stage1<32>, grid, block, 0, s, a); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_s2(const SelectArgs& a, hipStream_t s) {
-    const dim3 grid(a.n_seg), block(kNT);
-    switch (a.e2) {
-        case 1: hipLaunchKernelGGL(select_stage2<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(select_stage2<2>, grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL(select_stage2<4>, grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL(select_stage2<8>, grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL(select_stage2<16>, grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL(select_stage2<32>, grid, block, 0, s, a); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
 }  // namespace
 
-// Chooses the stage shapes; returns 0 when the problem is out of range.
-size_t select_workspace_bytes(int n_seg, int64_t n_keys, int k, int* nblk, int* e1, int* e2) {
-    if (n_keys <= 32768) {
-        *nblk = 1;
-        *e1 = next_pow2((int)((n_keys + kNT - 1) / kNT));
-        if (*e1 < 1) *e1 = 1;
-        *e2 = 0;
-        return 1;
+bool select_plan(SelectArgs* a, size_t* zero_bytes, size_t* ws_bytes) {
+    if (a->k > 4096) return false;
+    if (a->n_keys <= kSelSingle) {
+        a->path = 0;
+        a->e1 = next_pow2((int)((a->n_keys + kNT - 1) / kNT));
+        if (a->e1 < 1) a->e1 = 1;
+        a->nblk = 0;
+        *zero_bytes = 0;
+        *ws_bytes = 0;
+        return true;
     }
-    int E = 8;
-    int64_t nb = (n_keys + (int64_t)kNT * E - 1) / ((int64_t)kNT * E);
-    while (nb * k > 32768 && E < 32) {
-        E *= 2;
-        nb = (n_keys + (int64_t)kNT * E - 1) / ((int64_t)kNT * E);
-    }
-    if (nb * k > 32768) return 0;
-    *nblk = (int)nb;
-    *e1 = E;
-    *e2 = next_pow2((int)((nb * k + kNT - 1) / kNT));
-    return (size_t)n_seg * nb * k * 8 + (size_t)n_seg * nb * 4 + 256;
+    a->path = 1;
+    a->e1 = 0;
+    a->nblk = (int)((a->n_keys + kColBlk - 1) / kColBlk);
+    *zero_bytes = (size_t)a->n_seg * kSelBins * 4;
+    const size_t nb = (size_t)a->n_seg * a->nblk;
+    *ws_bytes = nb * 4 + 256 + nb * kColBlk * 8 + 256;
+    return true;
+}
+
+void select_bind(SelectArgs* a, void* zero_region, void* ws) {
+    if (a->path != 1) return;
+    a->hist = static_cast<uint32_t*>(zero_region);
+    char* w = static_cast<char*>(ws);
+    const size_t nb = (size_t)a->n_seg * a->nblk;
+    a->blk_count = reinterpret_cast<int32_t*>(w);
+    w += (nb * 4 + 255) / 256 * 256;
+    a->blk_idx = reinterpret_cast<int32_t*>(w);
+    a->blk_key = reinterpret_cast<uint32_t*>(w + nb * kColBlk * 4);
 }
 
 hipError_t launch_fm_select(const SelectArgs& a, hipStream_t s) {
-    hipError_t e = launch_s1(a, s);
-    if (e != hipSuccess || a.nblk == 1) return e;
-    return launch_s2(a, s);
+    if (a.path == 0) {
+        const dim3 grid(a.n_seg), block(kNT);
+        switch (a.e1) {
+            case 1: hipLaunchKernelGGL(select_single<1>, grid, block, 0, s, a); break;
+            case 2: hipLaunchKernelGGL(select_single<2>, grid, block, 0, s, a); break;
+            case 4: hipLaunchKernelGGL(select_single<4>, grid, block, 0, s, a); break;
+            case 8: hipLaunchKernelGGL(select_single<8>, grid, block, 0, s, a); break;
+            case 16: hipLaunchKernelGGL(select_single<16>, grid, block, 0, s, a); break;
+            case 32: hipLaunchKernelGGL(select_single<32>, grid, block, 0, s, a); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    const dim3 gh((unsigned)((a.n_keys + kBlk - 1) / kBlk), a.n_seg);
+    hipLaunchKernelGGL(sel_hist_kernel, gh, dim3(kBlkThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sel_collect_kernel, dim3(a.nblk, a.n_seg), dim3(kBlkThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sel_final_kernel, dim3(a.n_seg), dim3(kNT), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace lsa

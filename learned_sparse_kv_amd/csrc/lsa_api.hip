@@ -60,6 +60,8 @@ struct lsa_ctx {
     int n_cu = 256;
     void* ws = nullptr;
     size_t ws_bytes = 0;
+    void* zero = nullptr;       // select histogram: zero between calls
+    size_t zero_bytes = 0;
     bool timing = false;
     struct Pending {
         int kind;
@@ -86,6 +88,28 @@ lsa_status ws_ensure(lsa_ctx* c, size_t bytes) {
         return fail(LSA_ERR_NO_MEMORY, "workspace allocation of %zu bytes failed", want);
     }
     c->ws_bytes = want;
+    return LSA_OK;
+}
+
+// The zero region is left zeroed by the kernels that use it; a new or grown
+// region is zeroed here.
+lsa_status zero_ensure(lsa_ctx* c, size_t bytes) {
+    if (bytes <= c->zero_bytes) return LSA_OK;
+    size_t want = align_up(bytes, (size_t)1 << 16);
+    if (c->zero) {
+        HIPTRY(hipDeviceSynchronize());
+        HIPTRY(hipFree(c->zero));
+        c->zero = nullptr;
+        c->zero_bytes = 0;
+    }
+    if (hipMalloc(&c->zero, want) != hipSuccess) {
+        (void)hipGetLastError();
+        c->zero = nullptr;
+        return fail(LSA_ERR_NO_MEMORY, "select workspace allocation of %zu bytes failed", want);
+    }
+    HIPTRY(hipMemset(c->zero, 0, want));
+    HIPTRY(hipDeviceSynchronize());
+    c->zero_bytes = want;
     return LSA_OK;
 }
 
@@ -228,6 +252,7 @@ void lsa_ctx_destroy(lsa_ctx* c) {
     if (!c) return;
     (void)hipDeviceSynchronize();
     if (c->ws) (void)hipFree(c->ws);
+    if (c->zero) (void)hipFree(c->zero);
     for (auto& p : c->pending) {
         (void)hipEventDestroy(p.a);
         (void)hipEventDestroy(p.b);
@@ -343,24 +368,13 @@ lsa_status select_setup(lsa_ctx* c, const float* scores, int32_t n_seg, int64_t 
             for (int s = 0; s < n_seg; ++s) a->n_valid[s] = (int32_t)n_valid[s];
         }
     }
-    size_t need = select_workspace_bytes(n_seg, n_keys, k, &a->nblk, &a->e1, &a->e2);
-    if (need == 0) return fail(LSA_ERR_UNSUPPORTED, "ceil(n_keys / 32768) * k must be <= 32768");
-    *ws_need = a->nblk > 1 ? need : 0;
+    size_t zero_bytes = 0;
+    if (!select_plan(a, &zero_bytes, ws_need)) return fail(LSA_ERR_UNSUPPORTED, "selection shape out of range");
+    if (zero_bytes) {
+        lsa_status st = zero_ensure(c, zero_bytes);
+        if (st != LSA_OK) return st;
+    }
     return LSA_OK;
-}
-
-void select_bind_ws(SelectArgs* a, char* ws) {
-    if (a->nblk <= 1) return;
-    const size_t n = (size_t)a->n_seg * a->nblk * a->k;
-    a->cand_key = reinterpret_cast<uint32_t*>(ws);
-    a->cand_idx = reinterpret_cast<int32_t*>(ws + align_up(n * 4, 256));
-    a->cand_n = reinterpret_cast<int32_t*>(ws + 2 * align_up(n * 4, 256));
-}
-
-size_t select_ws_span(const SelectArgs& a) {
-    if (a.nblk <= 1) return 0;
-    const size_t n = (size_t)a.n_seg * a.nblk * a.k;
-    return 2 * align_up(n * 4, 256) + align_up((size_t)a.n_seg * a.nblk * 4, 256);
 }
 
 StageLayer stage_layer(const lsa_pool* p, const int32_t* sel, const int32_t* count, int32_t sel_stride,
@@ -449,11 +463,9 @@ lsa_status lsa_select(lsa_ctx* ctx, const float* scores, int32_t n_seg, int64_t 
     size_t need = 0;
     lsa_status st = select_setup(ctx, scores, n_seg, n_keys, n_valid, mode, k, k, tau, sel, count, &a, &need);
     if (st != LSA_OK) return st;
-    if (need) {
-        st = ws_ensure(ctx, select_ws_span(a));
-        if (st != LSA_OK) return st;
-        select_bind_ws(&a, static_cast<char*>(ctx->ws));
-    }
+    st = ws_ensure(ctx, need);
+    if (st != LSA_OK) return st;
+    select_bind(&a, ctx->zero, ctx->ws);
     Timed t(ctx, LSA_K_SELECT, (hipStream_t)stream);
     HIPTRY(launch_fm_select(a, (hipStream_t)stream));
     t.end();
@@ -701,6 +713,8 @@ lsa_status lsa_attend(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dt
     if (!row_dtype_ok(dtype)) return fail(LSA_ERR_UNSUPPORTED, "row dtype %d", (int)dtype);
     if (hq > 16 || (kv_dim != 128 && kv_dim != 256 && kv_dim != 512))
         return fail(LSA_ERR_UNSUPPORTED, "hq %d, kv_dim %d (supported: hq <= 16, kv_dim 128/256/512)", hq, kv_dim);
+    if (phys_stride > kAttendMaxRows)
+        return fail(LSA_ERR_UNSUPPORTED, "phys_stride %d > %d rows", phys_stride, kAttendMaxRows);
     AttendArgs a;
     memset(&a, 0, sizeof(a));
     a.n_layers = 1;
@@ -756,12 +770,14 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
                       &sel_need);
     if (st != LSA_OK) return st;
     const int phys_stride = W + d->k;
+    if (phys_stride > kAttendMaxRows)
+        return fail(LSA_ERR_UNSUPPORTED, "window + k = %d > %d rows", phys_stride, kAttendMaxRows);
     for (int l = 0; l < d->n_layers; ++l) {
         st = stage_check(d->pools[l], k_eff, d->src_ratio, phys_stride);
         if (st != LSA_OK) return st;
     }
     // workspace: select candidates | attend partials | phys | n_rows
-    const size_t off_att = align_up(select_ws_span(se), 256);
+    const size_t off_att = align_up(sel_need, 256);
     const size_t att_bytes = attend_workspace_bytes(d->n_layers, B, D, phys_stride);
     const size_t off_phys = off_att + align_up(att_bytes, 256);
     const size_t phys_bytes = d->phys ? 0 : align_up((size_t)d->n_layers * B * phys_stride * 4, 256);
@@ -770,7 +786,7 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
     st = ws_ensure(ctx, off_nrows + nrows_bytes);
     if (st != LSA_OK) return st;
     char* ws = static_cast<char*>(ctx->ws);
-    select_bind_ws(&se, ws);
+    select_bind(&se, ctx->zero, ws);
     int32_t* phys = d->phys ? d->phys : reinterpret_cast<int32_t*>(ws + off_phys);
     int32_t* n_rows = d->n_rows ? d->n_rows : reinterpret_cast<int32_t*>(ws + off_nrows);
 

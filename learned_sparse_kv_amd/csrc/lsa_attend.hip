@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kR = kAttendRows;   // rows per split
 constexpr int kThreads = 256;
+constexpr int kMaxSplits = kAttendMaxRows / kAttendRows;
 
 template <typename KT>
 __device__ inline float ld_elem(const char* p);
@@ -168,33 +169,56 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
     }
 }
 
+// One workgroup per (layer, sequence, 32-column slice of D): the splits'
+// maxima and denominators are staged in LDS once, every thread then merges
+// two outputs over the splits in split order with independent loads.
+constexpr int kCombCols = 32;
+
 template <int D>
 __global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a) {
+    __shared__ float s_w[kMaxSplits][16];   // exp(m_s - M_h)
+    __shared__ float s_inv[16];             // 1 / sum_s exp(m_s - M_h) l_s
     const AttendLayer& L = a.L[blockIdx.z];
     const int b = blockIdx.y;
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    const int h = idx / D, d = idx % D;
-    if (h >= a.hq) return;
+    const int tid = threadIdx.x;
     int n = L.n_rows[b];
     n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
     const int ns = (n + kR - 1) / kR;
     const int pair = blockIdx.z * a.batch + b;
-    float* out = L.out + ((int64_t)b * a.hq + h) * D + d;
+    const int d0 = blockIdx.x * kCombCols;
+    const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
+    if (tid < 16) {
+        const int h = tid;
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * 32 + h]);
+        float den = 0.0f;
+        for (int s = 0; s < ns; ++s) {
+            const float f = expf(ml[s * 32 + h] - M);
+            s_w[s][h] = f;
+            den += f * ml[s * 32 + 16 + h];
+        }
+        s_inv[h] = 1.0f / den;
+    }
+    __syncthreads();
+    // thread -> (head h, columns d0 + c and d0 + c + 16)
+    const int h = tid >> 4, c = tid & 15;
+    if (h >= a.hq) return;
+    float* out = L.out + ((int64_t)b * a.hq + h) * D + d0;
     if (ns == 0) {
-        *out = 0.0f;
+        out[c] = 0.0f;
+        out[c + 16] = 0.0f;
         return;
     }
-    const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * 32 + h]);
-    float den = 0.0f, num = 0.0f;
-    const float* po = a.part_acc + (int64_t)pair * a.max_splits * 16 * D + h * D + d;
+    const float* po = a.part_acc + (int64_t)pair * a.max_splits * 16 * D + (int64_t)h * D + d0;
+    float n0 = 0.0f, n1 = 0.0f;
+#pragma unroll 4
     for (int s = 0; s < ns; ++s) {
-        const float f = expf(ml[s * 32 + h] - M);
-        den += f * ml[s * 32 + 16 + h];
-        num += f * po[(int64_t)s * 16 * D];
+        const float f = s_w[s][h];
+        n0 += f * po[(int64_t)s * 16 * D + c];
+        n1 += f * po[(int64_t)s * 16 * D + c + 16];
     }
-    *out = num / den;
+    out[c] = n0 * s_inv[h];
+    out[c + 16] = n1 * s_inv[h];
 }
 
 template <int D, typename KT>
@@ -207,7 +231,7 @@ hipError_t launch_t(const AttendArgs& a, hipStream_t s, hipEvent_t mid) {
         e = hipEventRecord(mid, s);
         if (e != hipSuccess) return e;
     }
-    const dim3 g2((16 * D + 255) / 256, a.batch, a.n_layers);
+    const dim3 g2(D / kCombCols, a.batch, a.n_layers);
     hipLaunchKernelGGL((attend_combine_kernel<D>), g2, dim3(256), 0, s, a);
     return hipGetLastError();
 }

@@ -57,6 +57,21 @@ __device__ inline int wave_sum(int v) {
     return v;
 }
 
+// Adds 1 to hist[dg] for every active lane of the wave; the lanes sharing the
+// first active lane's value are added with one atomic (clustered keys would
+// otherwise serialise on one LDS address).  Call with the whole wave.
+__device__ inline void hist_add(uint32_t* hist, bool act, uint32_t dg) {
+    const uint64_t am = __ballot(act);
+    if (am) {
+        const int lane = threadIdx.x & 63;
+        const int first = __ffsll((unsigned long long)am) - 1;
+        const uint32_t d0 = __shfl(dg, first, 64);
+        const uint64_t same = __ballot(act && dg == d0);
+        if (lane == first) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+        if (act && dg != d0) atomicAdd(&hist[dg], 1u);
+    }
+}
+
 // Exclusive block-wide prefix sum for blockDim.x == NT (multiple of 64);
 // `smem` needs NT/64 + 1 ints.  Returns the exclusive prefix; *total = sum.
 template <int NT>
@@ -83,6 +98,11 @@ __device__ inline int block_excl_scan(int v, int* smem, int* total) {
 }
 
 // ------------------------------------------------------------------ launchers
+constexpr int kSelBins = 2048;        // 11-bit key histogram of the long-segment path
+constexpr int kSelShift = 21;         // bin = order_key(score) >> kSelShift
+constexpr int kSelKeepCap = 8192;     // entries (above + in the boundary bucket) resolved in LDS
+constexpr int kSelSingle = 32768;     // segments up to this length use one workgroup
+
 struct ScoreArgs {
     const void* keys;
     const float* q;
@@ -105,13 +125,19 @@ struct SelectArgs {
     int32_t n_valid[LSA_MAX_BATCH];
     int32_t* sel;
     int32_t* count;
-    // two-stage workspace
-    uint32_t* cand_key;         // [n_seg][nblk][k]
-    int32_t* cand_idx;          // [n_seg][nblk][k]
-    int32_t* cand_n;            // [n_seg][nblk]
-    int32_t nblk, e1, e2;
+    int32_t path;               // 0: one workgroup per segment, 1: histogram path
+    int32_t e1;                 // path 0: keys per thread
+    int32_t nblk;               // path 1: 1024-entry blocks per segment
+    // path 1 workspace.  hist is zero on entry and left zero on exit.
+    uint32_t* hist;             // [n_seg][kSelBins]
+    int32_t* blk_count;         // [n_seg][nblk] entries each block kept
+    int32_t* blk_idx;           // [n_seg][nblk][1024] kept indices (top bit: boundary bucket)
+    uint32_t* blk_key;          // [n_seg][nblk][1024] their keys
 };
-size_t select_workspace_bytes(int n_seg, int64_t n_keys, int k, int* nblk, int* e1, int* e2);
+// Fills the shape fields; returns false when out of range.  *zero_bytes is the
+// size of the zero-initialised region (hist + counters), *ws_bytes the rest.
+bool select_plan(SelectArgs* a, size_t* zero_bytes, size_t* ws_bytes);
+void select_bind(SelectArgs* a, void* zero_region, void* ws);
 hipError_t launch_fm_select(const SelectArgs& a, hipStream_t s);
 
 struct StageLayer {
@@ -161,6 +187,7 @@ struct AttendArgs {
     AttendLayer L[LSA_MAX_LAYERS];
 };
 constexpr int kAttendRows = 32;
+constexpr int kAttendMaxRows = 5120;    // longest row list (window + entries) of one attention
 size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows);
 hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid = nullptr);
 
