@@ -40,8 +40,7 @@ constexpr int kNT = 1024;
 constexpr int kNW = kNT / 64;
 constexpr int kBlk = 4096;          // entries per block of the histogram kernel
 constexpr int kColBlk = 1024;       // entries per block of the collect kernel
-constexpr int kBitmapEntries = 262144;               // segments up to this length sort via a bitmap
-constexpr int kBitmapWords = kBitmapEntries / 32;
+constexpr int kMaxBlocks = 4096;    // collect blocks whose lists the final kernel gathers in LDS
 constexpr int kBlkThreads = 256;
 
 struct KthShared {
@@ -373,6 +372,7 @@ __global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
     __shared__ int s_b[3];
     __shared__ int32_t s_idx[kSelKeepCap];
     __shared__ uint32_t s_key[kSelKeepCap];
+    __shared__ int s_start[kMaxBlocks + 1];
     const int tid = threadIdx.x, seg = blockIdx.x;
     uint32_t* g = a.hist + (int64_t)seg * kSelBins;
     find_boundary<kNT>(g, a.k, sh.scan, s_b);
@@ -393,17 +393,26 @@ __global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
     }
     int n_keep;
     int off = block_excl_scan<kNT>(mine, sh.scan, &n_keep);
-    if (K > 0 && n_keep <= kSelKeepCap) {
+    if (K > 0 && n_keep <= kSelKeepCap && nb <= kMaxBlocks) {
+        // every block's first position in the gathered list
         for (int q = 0; q < PB; ++q) {
             const int bi = tid * PB + q;
             if (bi >= nb) break;
-            const int c = cnt[bi];
-            const int64_t ob = ((int64_t)seg * nb + bi) * kColBlk;
-            for (int i = 0; i < c; ++i) {
-                s_idx[off + i] = a.blk_idx[ob + i];
-                s_key[off + i] = a.blk_key[ob + i];
+            s_start[bi] = off;
+            off += cnt[bi];
+        }
+        if (tid == 0) s_start[nb] = n_keep;
+        __syncthreads();
+        // all threads copy: entry p belongs to the last block starting at or before p
+        for (int p = tid; p < n_keep; p += kNT) {
+            int lo = 0, hi = nb - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_start[mid] <= p) lo = mid; else hi = mid - 1;
             }
-            off += c;
+            const int64_t src = ((int64_t)seg * nb + lo) * kColBlk + (p - s_start[lo]);
+            s_idx[p] = a.blk_idx[src];
+            s_key[p] = a.blk_key[src];
         }
         __syncthreads();
         // radix passes over bits 20..0 of the candidates' keys (bucket b* fixes the rest)

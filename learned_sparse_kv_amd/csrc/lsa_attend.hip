@@ -6,10 +6,11 @@
 //   out[h,:] = sum_r softmax_r(scale * q[h,:] . kv[phys[r],:]) * kv[phys[r],:]
 //
 // Design (gfx950): flash-decode split over rows.  All heads share the rows
-// (MQA-like), so a workgroup loads one 32-row tile into LDS once and computes
-// the 16-head x 32-row score block and the 16-head x D output block with
-// v_mfma_f32_16x16x4f32: QK^T splits the rows over 2 waves and the D
-// (contraction) dimension over 2 waves, PV splits D over 4 waves.  Each split
+// (MQA-like), so a workgroup of 8 waves issues every load of one 32-row tile
+// at once, stages it in LDS, and computes the 16-head x 32-row score block and
+// the 16-head x D output block with v_mfma_f32_16x16x4f32: QK^T splits the rows
+// over 2 waves and the D (contraction) dimension over 4, the softmax runs on
+// 32 lanes per head, PV splits D over the 8 waves.  Each split
 // writes its running max, softmax denominator and unnormalised output; a
 // second kernel merges the splits in split order.  Split s always covers list
 // rows [32 s, 32 s + 32), so the arithmetic depends only on the list length
@@ -21,7 +22,7 @@ namespace lsa {
 namespace {
 
 constexpr int kR = kAttendRows;   // rows per split
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kMaxSplits = kAttendMaxRows / kAttendRows;
 
 template <typename KT>
@@ -59,12 +60,15 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
     constexpr int RB = D * (int)sizeof(KT);          // row bytes
     constexpr int LS = RB + 16;                      // LDS row stride
     constexpr int CPR = RB / 16;                     // 16-byte chunks per row
-    constexpr int QK_STEPS = D / 8;                  // per lane: D/2 per wave-half, /4 k-lanes
+    constexpr int LOADS = kR * CPR / kThreads;       // 16-byte row loads per thread
+    constexpr int RSTEP = kThreads / CPR;            // rows covered by one round of loads
+    constexpr int QK_STEPS = D / 16;                 // per lane: a quarter of D over 4 k-lanes
     constexpr int PER_READ = 16 / (int)sizeof(KT);
-    constexpr int NB = D / 64;                       // 16-wide output blocks per wave in PV
+    constexpr int NB = D / 128;                      // 16-wide output blocks per wave in PV
+    static_assert(LOADS >= 1 && (kR * CPR) % kThreads == 0, "tile must split evenly");
 
     __shared__ __attribute__((aligned(16))) char tile[kR * LS];
-    __shared__ float sS[2][16][kR];
+    __shared__ float sS[4][16][kR];
     __shared__ float sP[16][kR];
     __shared__ int s_ph[kR];
 
@@ -83,31 +87,36 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
         s_ph[tid] = (p >= 0 && p < L.kv_rows) ? p : -1;
     }
     __syncthreads();
+    // every row load of the tile is issued before any is used
     const char* kvb = static_cast<const char*>(L.kv) + (int64_t)b * L.kv_stride_b * (int64_t)sizeof(KT);
-    for (int c = tid; c < kR * CPR; c += kThreads) {
-        const int r = c / CPR, cc = c % CPR;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (s_ph[r] >= 0) v = *reinterpret_cast<const uint4*>(kvb + (int64_t)s_ph[r] * RB + cc * 16);
-        *reinterpret_cast<uint4*>(tile + r * LS + cc * 16) = v;
+    const int cc = tid % CPR, rr = tid / CPR;
+    uint4 v[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int p = s_ph[rr + i * RSTEP];
+        v[i] = p >= 0 ? *reinterpret_cast<const uint4*>(kvb + (int64_t)p * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
     }
-
-    // ---- scores: S[h][r] = q[h] . row[r]; wave = (row block nb, D half kh)
+    // scores: S[h][r] = q[h] . row[r]; wave = (row block nb, quarter kq of D)
+    const int nb = wave & 1, kq = wave >> 1;
+    const int h = lane & 15, g = lane >> 4;
+    const int e0 = kq * (D / 4) + g * QK_STEPS;
+    float qa[QK_STEPS];
     {
-        const int nb = wave & 1, kh = wave >> 1;
-        const int h = lane & 15, g = lane >> 4;
-        const int e0 = kh * (D / 2) + g * QK_STEPS;
-        float qa[QK_STEPS];
         const float* qp = L.q + ((int64_t)b * a.hq + (h < a.hq ? h : 0)) * D + e0;
 #pragma unroll
         for (int s = 0; s < QK_STEPS; s += 4) {
-            f32x4 v = h < a.hq ? *reinterpret_cast<const f32x4*>(qp + s) : f32x4{0.f, 0.f, 0.f, 0.f};
-            qa[s] = v[0];
-            qa[s + 1] = v[1];
-            qa[s + 2] = v[2];
-            qa[s + 3] = v[3];
+            f32x4 q4 = h < a.hq ? *reinterpret_cast<const f32x4*>(qp + s) : f32x4{0.f, 0.f, 0.f, 0.f};
+            qa[s] = q4[0];
+            qa[s + 1] = q4[1];
+            qa[s + 2] = q4[2];
+            qa[s + 3] = q4[3];
         }
-        __syncthreads();   // tile complete
-        const char* rowp = tile + (nb * 16 + (lane & 15)) * LS + e0 * (int)sizeof(KT);
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) *reinterpret_cast<uint4*>(tile + (rr + i * RSTEP) * LS + cc * 16) = v[i];
+    __syncthreads();
+    {
+        const char* rowp = tile + (nb * 16 + h) * LS + e0 * (int)sizeof(KT);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rd = 0; rd < QK_STEPS / PER_READ; ++rd) {
@@ -118,35 +127,34 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[rd * PER_READ + e], kb[e], acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sS[kh][4 * g + r][nb * 16 + (lane & 15)] = acc[r];
+        for (int r = 0; r < 4; ++r) sS[kq][4 * g + r][nb * 16 + h] = acc[r];
     }
     __syncthreads();
 
-    // ---- per-head softmax over this split's rows
+    // softmax over this split's rows: 32 lanes per head, fixed-pattern reductions
     float* ml = a.part_ml + ((int64_t)pair * a.max_splits + split) * 32;
-    if (tid < 16) {
-        const int h = tid;
-        float m = -INFINITY;
-        for (int r = 0; r < cnt; ++r) {
-            const float z = (sS[0][h][r] + sS[1][h][r]) * a.scale;
-            sS[0][h][r] = z;
-            m = fmaxf(m, z);
+    {
+        const int hh = tid >> 5, r = tid & 31;
+        const bool in = r < cnt;
+        const float z = in ? (((sS[0][hh][r] + sS[1][hh][r]) + sS[2][hh][r]) + sS[3][hh][r]) * a.scale : -INFINITY;
+        float m = z;
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+        const float p = in ? expf(z - m) : 0.0f;
+        float l = p;
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) l += __shfl_xor(l, o, 32);
+        sP[hh][r] = p;
+        if (r == 0) {
+            ml[hh] = m;
+            ml[16 + hh] = l;
         }
-        float l = 0.0f;
-        for (int r = 0; r < kR; ++r) {
-            const float p = r < cnt ? expf(sS[0][h][r] - m) : 0.0f;
-            sP[h][r] = p;
-            l += p;
-        }
-        ml[h] = m;
-        ml[16 + h] = l;
     }
     __syncthreads();
 
-    // ---- unnormalised output O[h][d] = sum_r P[h][r] row[r][d]; wave = D quarter
+    // unnormalised output O[h][d] = sum_r P[h][r] row[r][d]; wave = D/8 columns
     {
-        const int h = lane & 15, g = lane >> 4;
-        const int d0 = wave * (D / 4);
+        const int d0 = wave * (D / 8);
         f32x4 acc[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -170,12 +178,14 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
 }
 
 // One workgroup per (layer, sequence, 32-column slice of D): the splits'
-// maxima and denominators are staged in LDS once, every thread then merges
-// two outputs over the splits in split order with independent loads.
+// maxima and denominators are staged in LDS with one parallel load, every
+// thread then merges two outputs over the splits in split order, eight
+// splits' loads in flight at a time.
 constexpr int kCombCols = 32;
 
 template <int D>
 __global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a) {
+    __shared__ float s_ml[kMaxSplits * 32];
     __shared__ float s_w[kMaxSplits][16];   // exp(m_s - M_h)
     __shared__ float s_inv[16];             // 1 / sum_s exp(m_s - M_h) l_s
     const AttendLayer& L = a.L[blockIdx.z];
@@ -187,17 +197,19 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a)
     const int pair = blockIdx.z * a.batch + b;
     const int d0 = blockIdx.x * kCombCols;
     const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
+    for (int i = tid; i < ns * 32; i += 256) s_ml[i] = ml[i];
+    __syncthreads();
     if (tid < 16) {
-        const int h = tid;
+        const int hh = tid;
         float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * 32 + h]);
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, s_ml[s * 32 + hh]);
         float den = 0.0f;
         for (int s = 0; s < ns; ++s) {
-            const float f = expf(ml[s * 32 + h] - M);
-            s_w[s][h] = f;
-            den += f * ml[s * 32 + 16 + h];
+            const float f = expf(s_ml[s * 32 + hh] - M);
+            s_w[s][hh] = f;
+            den += f * s_ml[s * 32 + 16 + hh];
         }
-        s_inv[h] = 1.0f / den;
+        s_inv[hh] = 1.0f / den;
     }
     __syncthreads();
     // thread -> (head h, columns d0 + c and d0 + c + 16)
@@ -211,11 +223,22 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a)
     }
     const float* po = a.part_acc + (int64_t)pair * a.max_splits * 16 * D + (int64_t)h * D + d0;
     float n0 = 0.0f, n1 = 0.0f;
-#pragma unroll 4
-    for (int s = 0; s < ns; ++s) {
-        const float f = s_w[s][h];
-        n0 += f * po[(int64_t)s * 16 * D + c];
-        n1 += f * po[(int64_t)s * 16 * D + c + 16];
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+        float x0[8], x1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool in = s0 + j < ns;
+            x0[j] = in ? po[(int64_t)(s0 + j) * 16 * D + c] : 0.0f;
+            x1[j] = in ? po[(int64_t)(s0 + j) * 16 * D + c + 16] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (s0 + j < ns) {
+                const float f = s_w[s0 + j][h];
+                n0 += f * x0[j];
+                n1 += f * x1[j];
+            }
+        }
     }
     out[c] = n0 * s_inv[h];
     out[c + 16] = n1 * s_inv[h];
