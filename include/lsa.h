@@ -102,7 +102,9 @@ lsa_status lsa_ctx_reserve(lsa_ctx* ctx, uint64_t bytes);
 /* Kernel timing: when on, lsa_decode_step / lsa_score / lsa_attend record HIP
  * events around their launches on the launch stream.  lsa_ctx_timing_read
  * waits for the last event, returns for each kernel kind (LSA_K_*) the summed
- * milliseconds and launch count since the previous read, and resets them. */
+ * milliseconds and launch count since the previous read, and resets them.
+ * LSA_K_STAGE covers the LRU update together with the copy of missed rows;
+ * LSA_K_GATHER is kept for layout and reads 0. */
 enum { LSA_K_SCORE = 0, LSA_K_SELECT = 1, LSA_K_STAGE = 2, LSA_K_GATHER = 3,
        LSA_K_ATTEND = 4, LSA_K_COMBINE = 5, LSA_K_COUNT = 6 };
 lsa_status lsa_ctx_set_timing(lsa_ctx* ctx, int32_t on);

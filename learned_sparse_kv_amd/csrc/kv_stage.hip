@@ -21,8 +21,8 @@
 //     [untouched slots in their old order, minus the evicted ones]
 // and the evicted slots are exactly the last (m - free) untouched entries of
 // the old list, taken from the back.  Slots are handed out lowest-first and
-// never freed, so the unused ones are always used..S-1.  A second kernel with
-// one wave per missed row copies cold -> slot (HBM cold pools, or pinned host
+// never freed, so the unused ones are always used..S-1.  The same workgroup
+// then copies its missed rows cold -> slot (HBM cold pools, or pinned host
 // memory read directly over PCIe, so no host round trip sits in the step).
 #include "lsa_internal.hpp"
 
@@ -43,6 +43,8 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
     __shared__ int s_victim[kNT];
     __shared__ int s_order[kMaxSlots];
     __shared__ uint8_t s_hit[kMaxSlots];
+    __shared__ int s_mlog[kNT];     // missed entries and their slots, by miss rank
+    __shared__ int s_mslot[kNT];
 
     // 1. source selection -> this layer's ascending unique chunk list
     int n_src = L.count[b];
@@ -72,9 +74,13 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
     }
     if (l >= 0 && !L.ready[(int64_t)b * L.cap + l]) atomicOr(&L.meta[b * 4 + 1], 1);
 
+    int32_t* src = L.defer_copy ? L.src + (int64_t)b * L.phys_stride : nullptr;
+    if (src) {
+        for (int r = tid; r < L.window; r += kNT) src[r] = -1;
+        if (tid < n_l) src[L.window + tid] = -1;
+    }
     if (!L.swap) {
         if (l >= 0) phys[L.window + tid] = L.window + l;
-        if (tid == 0) L.n_miss[b] = 0;
         return;
     }
 
@@ -135,39 +141,49 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
     if (miss) {
         slot_of[l] = slot;
         logical_of[slot] = l;
-        int32_t* mrec = L.miss + ((int64_t)b * L.sel_stride + miss_rank) * 2;
-        mrec[0] = l;
-        mrec[1] = slot;
+        s_mlog[miss_rank] = l;
+        s_mslot[miss_rank] = slot;
         lru[n_miss - 1 - miss_rank] = slot;
+        if (src) src[L.window + tid] = l;
     }
     if (hit) lru[n_miss + n_hit - 1 - hit_rank] = slot;
     if (l >= 0) phys[L.window + tid] = L.window + slot;
     if (tid == 0) {
         L.meta[b * 4 + 0] = n_used + (n_miss < free_slots ? n_miss : free_slots);
-        L.n_miss[b] = n_miss;
         uint64_t* st = L.stats + (int64_t)b * 4;
         st[0] += (uint64_t)n_hit;
         st[1] += (uint64_t)n_miss;
         st[2] += (uint64_t)n_miss * (uint64_t)L.row_bytes;
     }
-}
+    if (src) return;   // the attention reads the missed rows and fills their slots
+    __syncthreads();
 
-constexpr int kGatherWaves = 4;
-
-// one wave per missed row: cold[entry] -> kv[window + slot]
-__global__ __launch_bounds__(kGatherWaves * 64) void kv_gather_kernel(const StageArgs a) {
-    const StageLayer& L = a.L[blockIdx.z];
-    if (!L.swap) return;
-    const int b = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int m = blockIdx.x * kGatherWaves + wave;
-    if (m >= L.n_miss[b]) return;
-    const int32_t* mrec = L.miss + ((int64_t)b * L.sel_stride + m) * 2;
-    const int l = mrec[0], slot = mrec[1];
-    const char* src = static_cast<const char*>(L.cold) + b * L.cold_stride_b + (int64_t)l * L.row_bytes;
-    char* dst = static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes + (int64_t)(L.window + slot) * L.row_bytes;
-    for (int off = lane * 16; off < L.row_bytes; off += 64 * 16)
-        *reinterpret_cast<f32x4*>(dst + off) = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + off));
+    // 5. copy the missed rows cold -> slot (pinned host rows are read over PCIe
+    //    directly); kBatch 16-byte loads per thread are in flight at a time
+    const int cpr = L.row_bytes / 16;
+    const int chunks = n_miss * cpr;
+    const char* cold = static_cast<const char*>(L.cold) + b * L.cold_stride_b;
+    char* kv = static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes;
+    constexpr int kBatch = 8;
+    for (int c0 = 0; c0 < chunks; c0 += kNT * kBatch) {
+        uint4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int c = c0 + u * kNT + tid;
+            if (c < chunks) {
+                const int m = c / cpr, off = (c - m * cpr) * 16;
+                v[u] = *reinterpret_cast<const uint4*>(cold + (int64_t)s_mlog[m] * L.row_bytes + off);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int c = c0 + u * kNT + tid;
+            if (c < chunks) {
+                const int m = c / cpr, off = (c - m * cpr) * 16;
+                *reinterpret_cast<uint4*>(kv + (int64_t)(L.window + s_mslot[m]) * L.row_bytes + off) = v[u];
+            }
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L, int b, int64_t first, int64_t count) {
@@ -187,18 +203,6 @@ __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L,
 
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(kv_stage_kernel, dim3(a.batch, a.n_layers), dim3(kNT), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_kv_gather(const StageArgs& a, hipStream_t s) {
-    int max_stride = 0, any_swap = 0;
-    for (int i = 0; i < a.n_layers; ++i) {
-        if (a.L[i].sel_stride > max_stride) max_stride = a.L[i].sel_stride;
-        any_swap |= a.L[i].swap;
-    }
-    if (!any_swap || max_stride == 0) return hipSuccess;
-    const dim3 grid((max_stride + kGatherWaves - 1) / kGatherWaves, a.batch, a.n_layers);
-    hipLaunchKernelGGL(kv_gather_kernel, grid, dim3(kGatherWaves * 64), 0, s, a);
     return hipGetLastError();
 }
 

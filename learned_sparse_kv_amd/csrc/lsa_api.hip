@@ -163,8 +163,6 @@ struct lsa_pool {
     int32_t* meta = nullptr;
     uint64_t* stats = nullptr;
     uint8_t* ready = nullptr;
-    int32_t* miss = nullptr;
-    int32_t* n_miss = nullptr;
     void* cold_dev = nullptr;   // device address of the cold pool (HBM, or mapped pinned host)
     void* cold_host = nullptr;  // host address when pinned
     int64_t cold_stride_b = 0;  // bytes
@@ -391,8 +389,6 @@ StageLayer stage_layer(const lsa_pool* p, const int32_t* sel, const int32_t* cou
     L.count = count;
     L.phys = phys;
     L.n_rows = n_rows;
-    L.miss = p->miss;
-    L.n_miss = p->n_miss;
     L.cold = p->cold_dev;
     L.kv = p->d.kv_buf;
     L.cap = p->cap;
@@ -533,9 +529,7 @@ lsa_status lsa_pool_create(lsa_pool** out, const lsa_pool_desc* d) {
     const size_t sz_meta = align_up((size_t)B * 16, 256);
     const size_t sz_stats = align_up((size_t)B * 32, 256);
     const size_t sz_ready = align_up((size_t)(B * C), 256);
-    const size_t sz_miss = align_up((size_t)B * 1024 * 8, 256);
-    const size_t sz_nmiss = align_up((size_t)B * 4, 256);
-    const size_t total = sz_slot + 2 * sz_lo + sz_meta + sz_stats + sz_ready + sz_miss + sz_nmiss;
+    const size_t total = sz_slot + 2 * sz_lo + sz_meta + sz_stats + sz_ready;
     if (hipMalloc(&p->tables, total) != hipSuccess) {
         (void)hipGetLastError();
         delete p;
@@ -547,9 +541,7 @@ lsa_status lsa_pool_create(lsa_pool** out, const lsa_pool_desc* d) {
     p->lru = reinterpret_cast<int32_t*>(t); t += sz_lo;
     p->meta = reinterpret_cast<int32_t*>(t); t += sz_meta;
     p->stats = reinterpret_cast<uint64_t*>(t); t += sz_stats;
-    p->ready = reinterpret_cast<uint8_t*>(t); t += sz_ready;
-    p->miss = reinterpret_cast<int32_t*>(t); t += sz_miss;
-    p->n_miss = reinterpret_cast<int32_t*>(t);
+    p->ready = reinterpret_cast<uint8_t*>(t);
     hipError_t e = hipMemset(p->tables, 0, total);
     if (e == hipSuccess) e = hipMemset(p->slot_of, 0xFF, sz_slot + 2 * sz_lo);
     if (e == hipSuccess && swap) {
@@ -696,7 +688,6 @@ lsa_status lsa_stage(lsa_pool* p, const int32_t* sel, const int32_t* count, int3
     a.L[0] = stage_layer(p, sel, count, sel_stride, src_ratio, phys, phys_stride, n_rows);
     hipStream_t s = (hipStream_t)stream;
     HIPTRY(launch_kv_stage(a, s));
-    HIPTRY(launch_kv_gather(a, s));
     return LSA_OK;
 }
 
@@ -729,7 +720,7 @@ lsa_status lsa_attend(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dt
     if (st != LSA_OK) return st;
     a.part_acc = static_cast<float*>(ctx->ws);
     a.part_ml = a.part_acc + (size_t)batch * a.max_splits * 16 * kv_dim;
-    a.L[0] = AttendLayer{q, kv, phys, n_rows, out, kv_stride_b, kv_rows, phys_stride};
+    a.L[0] = AttendLayer{q, kv, phys, n_rows, out, kv_stride_b, kv_rows, phys_stride, nullptr, nullptr, nullptr, 0, 0};
     return attend_timed(ctx, a, (hipStream_t)stream);
 }
 
@@ -783,12 +774,15 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
     const size_t phys_bytes = d->phys ? 0 : align_up((size_t)d->n_layers * B * phys_stride * 4, 256);
     const size_t off_nrows = off_phys + phys_bytes;
     const size_t nrows_bytes = d->n_rows ? 0 : align_up((size_t)d->n_layers * B * 4, 256);
-    st = ws_ensure(ctx, off_nrows + nrows_bytes);
+    const size_t off_src = off_nrows + nrows_bytes;
+    const size_t src_bytes = align_up((size_t)d->n_layers * B * phys_stride * 4, 256);
+    st = ws_ensure(ctx, off_src + src_bytes);
     if (st != LSA_OK) return st;
     char* ws = static_cast<char*>(ctx->ws);
     select_bind(&se, ctx->zero, ws);
     int32_t* phys = d->phys ? d->phys : reinterpret_cast<int32_t*>(ws + off_phys);
     int32_t* n_rows = d->n_rows ? d->n_rows : reinterpret_cast<int32_t*>(ws + off_nrows);
+    int32_t* srcs = reinterpret_cast<int32_t*>(ws + off_src);
 
     StageArgs ga;
     memset(&ga, 0, sizeof(ga));
@@ -809,9 +803,15 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
         const lsa_pool* p = d->pools[l];
         int32_t* ph = phys + (size_t)l * B * phys_stride;
         int32_t* nr = n_rows + (size_t)l * B;
+        int32_t* sr = srcs + (size_t)l * B * phys_stride;
         ga.L[l] = stage_layer(p, d->sel, d->count, d->k, d->src_ratio, ph, phys_stride, nr);
+        ga.L[l].defer_copy = 1;
+        ga.L[l].src = sr;
+        // a swapping layer's missed rows are read from the cold pool by the
+        // attention, which also fills their slots
         aa.L[l] = AttendLayer{d->q_attn + (size_t)l * B * d->hq * D, p->d.kv_buf, ph, nr,
-                              d->out + (size_t)l * B * d->hq * D, p->d.kv_stride_b, p->rows_per_seq, phys_stride};
+                              d->out + (size_t)l * B * d->hq * D, p->d.kv_stride_b, p->rows_per_seq, phys_stride,
+                              p->swap ? sr : nullptr, p->d.kv_buf, p->cold_dev, p->cold_stride_b, p->cap};
     }
 
     hipStream_t s = (hipStream_t)stream;
@@ -828,11 +828,6 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
     {
         Timed t(ctx, LSA_K_STAGE, s);
         HIPTRY(launch_kv_stage(ga, s));
-        t.end();
-    }
-    {
-        Timed t(ctx, LSA_K_GATHER, s);
-        HIPTRY(launch_kv_gather(ga, s));
         t.end();
     }
     st = attend_timed(ctx, aa, s);

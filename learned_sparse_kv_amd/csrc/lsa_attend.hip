@@ -71,6 +71,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
     __shared__ float sS[4][16][kR];
     __shared__ float sP[16][kR];
     __shared__ int s_ph[kR];
+    __shared__ int s_src[kR];
 
     const AttendLayer& L = a.L[blockIdx.z];
     const int b = blockIdx.y, split = blockIdx.x;
@@ -85,16 +86,30 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
     if (tid < kR) {
         int p = tid < cnt ? L.phys[(int64_t)b * L.phys_stride + r0 + tid] : -1;
         s_ph[tid] = (p >= 0 && p < L.kv_rows) ? p : -1;
+        int sr = (L.src && tid < cnt) ? L.src[(int64_t)b * L.phys_stride + r0 + tid] : -1;
+        s_src[tid] = (sr >= 0 && sr < L.cold_rows && s_ph[tid] >= 0) ? sr : -1;
     }
     __syncthreads();
-    // every row load of the tile is issued before any is used
+    // every row load of the tile is issued before any is used; a row staged
+    // in this step comes from the cold pool and is written into its slot
     const char* kvb = static_cast<const char*>(L.kv) + (int64_t)b * L.kv_stride_b * (int64_t)sizeof(KT);
+    const char* cb = static_cast<const char*>(L.cold) + (int64_t)b * L.cold_stride_b;
     const int cc = tid % CPR, rr = tid / CPR;
     uint4 v[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-        const int p = s_ph[rr + i * RSTEP];
-        v[i] = p >= 0 ? *reinterpret_cast<const uint4*>(kvb + (int64_t)p * RB + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+        const int r = rr + i * RSTEP;
+        const int p = s_ph[r], sr = s_src[r];
+        const char* from = sr >= 0 ? cb + (int64_t)sr * RB : kvb + (int64_t)p * RB;
+        v[i] = p >= 0 ? *reinterpret_cast<const uint4*>(from + cc * 16) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (L.src) {
+        char* kvw = static_cast<char*>(L.kv_w) + (int64_t)b * L.kv_stride_b * (int64_t)sizeof(KT);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int r = rr + i * RSTEP;
+            if (s_src[r] >= 0) *reinterpret_cast<uint4*>(kvw + (int64_t)s_ph[r] * RB + cc * 16) = v[i];
+        }
     }
     // scores: S[h][r] = q[h] . row[r]; wave = (row block nb, quarter kq of D)
     const int nb = wave & 1, kq = wave >> 1;

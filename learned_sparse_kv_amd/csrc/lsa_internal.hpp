@@ -151,19 +151,21 @@ struct StageLayer {
     const int32_t* count;       // [batch]
     int32_t* phys;              // [batch][phys_stride]
     int32_t* n_rows;            // [batch]
-    int32_t* miss;              // [batch][sel_stride][2]: (entry, slot)
-    int32_t* n_miss;            // [batch]
     const void* cold;           // cold rows, sequence b at b * cold_stride_b bytes
     void* kv;                   // kv_buf
     int64_t cap, cold_stride_b, kv_stride_b_bytes;
     int32_t ratio, src_ratio, S, window, swap, sel_stride, phys_stride, row_bytes;
+    // defer_copy: instead of copying missed rows, write src[b][r] = cold entry
+    // of list row r for a miss, -1 otherwise; the attention then reads the
+    // missed rows from the cold pool and fills their slots
+    int32_t defer_copy;
+    int32_t* src;               // [batch][phys_stride]
 };
 struct StageArgs {
     int32_t n_layers, batch;
     StageLayer L[LSA_MAX_LAYERS];
 };
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s);
-hipError_t launch_kv_gather(const StageArgs& a, hipStream_t s);
 // copy the rows of entries [first, first+count) of sequence b that are staged
 // from the cold pool into their slots
 hipError_t launch_refresh_staged(const StageLayer& L, int b, int64_t first, int64_t count,
@@ -178,6 +180,13 @@ struct AttendLayer {
     int64_t kv_stride_b;        // elements
     int64_t kv_rows;            // rows per sequence; phys entries outside read as zero rows
     int32_t phys_stride;
+    // optional (deferred staging): list row r with src[b][r] >= 0 is read from
+    // cold entry src and written into kv row phys[b][r]
+    const int32_t* src;
+    void* kv_w;                 // writable alias of kv
+    const void* cold;
+    int64_t cold_stride_b;      // bytes
+    int64_t cold_rows;          // entries per sequence of the cold pool
 };
 struct AttendArgs {
     int32_t n_layers, batch, hq, D, dtype, max_splits;

@@ -111,6 +111,22 @@ class DeviceWorkload:
                         tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys, n_rows=self.n_rows,
                         stream=stream)
 
+    def capture(self, steps) -> None:
+        """Capture each listed step as a HIP graph (torch.cuda.CUDAGraph around
+        one lsa.decode_step).  The step enqueues only kernel launches, so the
+        graph replays exactly the eager work; run one eager step first so the
+        context workspace is already sized."""
+        self.graphs = {}
+        for t in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(t)
+            self.graphs[t] = g
+        torch.cuda.synchronize()
+
+    def replay(self, t: int) -> None:
+        self.graphs[t].replay()
+
     def reset_pools(self) -> None:
         for p in self.pools:
             p.reset()
