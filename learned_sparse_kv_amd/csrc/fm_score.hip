@@ -8,38 +8,43 @@
 //
 // Design (gfx950): the key scan is the only O(context) traffic of a decode
 // step, so keys are read from HBM exactly once, in coalesced 16-byte buffer
-// loads, and every query is applied to each key while it sits in LDS.  The
-// (n_idx*H <= 32) x dk query block stays in registers as the A operand of
-// v_mfma_f32_32x32x2f32; a wave multiplies it by 32 keys at a time (B
-// operand), so one MFMA chain yields all 32x32 dot products of the tile.
-// Query row i of the MFMA is indexer i/8, head i%8; with that layout each
-// lane's 16 accumulators hold 4 heads of each of 4 indexers for one key, so
-// the ReLU/weight/head-sum epilogue is in-lane plus one cross-half exchange.
-// The k dimension is permuted so that a lane reads one contiguous half-row
-// from LDS (lane half 0 takes elements 0..dk/2-1, half 1 the rest); A uses
-// the same permutation, so the products are unchanged.  LDS rows are padded by
-// 16 bytes so that 8 consecutive rows start in different bank groups.
-// A workgroup (4 waves) owns a 128-key tile; the next tile's global loads are
-// issued before the MFMAs of the current one (register double buffering).
+// loads (out-of-range tails read as zero), and every query is applied to a
+// key while it sits in LDS.  The (n_idx*H <= 32) x dk query block stays in
+// registers as the A operand of v_mfma_f32_32x32x2f32; a wave multiplies it by
+// 32 keys at a time (B operand), so one MFMA chain yields all 32x32 dot
+// products of its tile.  Query row i of the MFMA is indexer i/8, head i%8;
+// with that layout each lane's 16 accumulators hold 4 heads of each of 4
+// indexers for one key, so the ReLU/weight/head-sum/ensemble epilogue is
+// in-lane plus one cross-half exchange.  The k dimension is permuted so that a
+// lane reads one contiguous half-row from LDS (lane half 0 takes elements
+// 0..dk/2-1, half 1 the rest); A uses the same permutation, so the products
+// are unchanged.  LDS rows are padded by 16 bytes so that 8 consecutive rows
+// start in different bank groups.
+// Every wave works on its own 32-key tiles and LDS region with wave-scope
+// fences only -- no workgroup barriers -- and issues the next tile's loads
+// before the MFMAs of the current one, so one wave's memory phase overlaps
+// another's MFMAs.  The grid is one 4-wave workgroup per CU (fewer when the
+// scan is short), which keeps every wave's share of tiles equal.
 #include "lsa_internal.hpp"
 
 namespace lsa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTile = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTile = 32;          // keys per wave tile
 
 template <int DK, typename KT>
 struct Cfg {
     static constexpr int kRowBytes = DK * (int)sizeof(KT);
     static constexpr int kLdsStride = kRowBytes + 16;
     static constexpr int kTileBytes = kTile * kRowBytes;
-    static constexpr int kLoads = kTileBytes / (kThreads * 16);
+    static constexpr int kLoads = kTileBytes / (64 * 16);      // 16-byte loads per lane
     static constexpr int kHalf = DK / 2;                     // MFMA k-steps
     static constexpr int kHalfBytes = kHalf * (int)sizeof(KT);
     static constexpr int kReads = kHalfBytes / 16;           // ds_read_b128 per lane
-    static_assert(kTileBytes % (kThreads * 16) == 0, "tile must split into 16-byte loads");
+    static_assert(kTileBytes % (64 * 16) == 0, "tile must split into 16-byte loads");
     static_assert(kHalfBytes % 16 == 0, "half row must be 16-byte aligned");
 };
 
@@ -70,16 +75,17 @@ template <int DK, typename KT>
 __global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a) {
     using C = Cfg<DK, KT>;
     constexpr int kPerRead = 16 / (int)sizeof(KT);
-    __shared__ __attribute__((aligned(16))) char lds[kTile * C::kLdsStride];
+    __shared__ __attribute__((aligned(16))) char lds[kWaves][kTile * C::kLdsStride];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int col = lane & 31;      // key within the wave's 32 (B/D column); query row for A
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps tile state in SGPRs
+    const int col = lane & 31;      // key within the tile (B/D column); query row for A
     const int half = lane >> 5;     // which half of dk this lane feeds
 
     const int total = a.tile_start[a.batch];
-    int t = blockIdx.x;
+    const int stride = gridDim.x * kWaves;
+    int t = blockIdx.x * kWaves + wave;
     if (t >= total) return;
 
     auto seq_of = [&](int tile) {
@@ -87,28 +93,23 @@ __global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a
         while (tile >= a.tile_start[b + 1]) ++b;
         return b;
     };
+    const char* kbase = static_cast<const char*>(a.keys);
+    auto load_tile = [&](int tile, uint4 (&dst)[C::kLoads]) {
+        const int b = seq_of(tile);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(kbase + (int64_t)b * a.n_keys * C::kRowBytes,
+                                                   (uint32_t)a.n_valid[b] * (uint32_t)C::kRowBytes);
+        const uint32_t base = (uint32_t)(tile - a.tile_start[b]) * (uint32_t)C::kTileBytes;
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i) dst[i] = buffer_load16(r, base + (uint32_t)(i * 64 + lane) * 16u);
+    };
 
     int cur_b = -1;
     float qa[C::kHalf];
     float wr[16];
-    __amdgpu_buffer_rsrc_t rsrc;
-    const char* kbase = static_cast<const char*>(a.keys);
-
-    auto rsrc_for = [&](int b) {
-        return make_rsrc(kbase + (int64_t)b * a.n_keys * C::kRowBytes,
-                         (uint32_t)a.n_valid[b] * (uint32_t)C::kRowBytes);
-    };
-
+    char* my = lds[wave];
     uint4 pre[C::kLoads];
-    auto load_tile = [&](int tile, uint4 (&dst)[C::kLoads]) {
-        const int b = seq_of(tile);
-        const __amdgpu_buffer_rsrc_t r = rsrc_for(b);
-        const uint32_t base = (uint32_t)(tile - a.tile_start[b]) * (uint32_t)C::kTileBytes;
-#pragma unroll
-        for (int i = 0; i < C::kLoads; ++i) dst[i] = buffer_load16(r, base + (uint32_t)(i * kThreads + tid) * 16u);
-    };
-
     load_tile(t, pre);
+
     while (t < total) {
         const int b = seq_of(t);
         if (b != cur_b) {
@@ -134,21 +135,22 @@ __global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a
         }
         const int tile_in_seq = t - a.tile_start[b];
 
-        __syncthreads();   // previous tile's LDS reads are done
 #pragma unroll
         for (int i = 0; i < C::kLoads; ++i) {
-            const int off = (i * kThreads + tid) * 16;
-            const int row = off / C::kRowBytes, cb = off % C::kRowBytes;
-            *reinterpret_cast<uint4*>(lds + row * C::kLdsStride + cb) = pre[i];
+            const int off = (i * 64 + lane) * 16;
+            *reinterpret_cast<uint4*>(my + (off / C::kRowBytes) * C::kLdsStride + off % C::kRowBytes) = pre[i];
         }
-        __syncthreads();
+        // the wave's LDS writes are visible to all its lanes past this point
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        const int t_next = t + gridDim.x;
+        const int t_next = t + stride;
         if (t_next < total) load_tile(t_next, pre);
 
-        // 32 keys of this wave x 32 query rows, k = DK
+        // 32 keys x 32 query rows, k = DK
         f32x16 acc = {};
-        const char* myrow = lds + (wave * 32 + col) * C::kLdsStride + half * C::kHalfBytes;
+        const char* myrow = my + col * C::kLdsStride + half * C::kHalfBytes;
 #pragma unroll
         for (int rd = 0; rd < C::kReads; ++rd) {
             const uint4 u = *reinterpret_cast<const uint4*>(myrow + rd * 16);
@@ -158,6 +160,10 @@ __global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a
             for (int e = 0; e < kPerRead; ++e)
                 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[rd * kPerRead + e], kb[e], acc, 0, 0, 0);
         }
+        // all lanes' LDS reads of this tile are done before the next tile is written
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // epilogue: per indexer, this lane's 4 heads; then the other half's 4 heads
         float s[4];
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a
             for (int gi = 1; gi < a.n_idx; ++gi) sum += s[gi];
             e = sum / (float)a.n_idx;
         }
-        const int key = tile_in_seq * kTile + wave * 32 + col;
+        const int key = tile_in_seq * kTile + col;
         if (half == 0 && key < a.n_valid[b]) a.scores[(int64_t)b * a.n_keys + key] = e + 0.0f;
 
         t = t_next;
@@ -190,8 +196,8 @@ template <int DK, typename KT>
 hipError_t launch_t(const ScoreArgs& a, int n_cu, hipStream_t s) {
     const int total = a.tile_start[a.batch];
     if (total == 0) return hipSuccess;
-    int grid = n_cu * 2;
-    if (grid > total) grid = total;
+    int grid = (total + kWaves - 1) / kWaves;
+    if (grid > n_cu) grid = n_cu;
     hipLaunchKernelGGL((fm_score_kernel<DK, KT>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

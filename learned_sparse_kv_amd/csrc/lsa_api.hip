@@ -323,7 +323,7 @@ lsa_status score_args(const void* keys, lsa_dtype key_dtype, int32_t batch, int6
         if (nv < 0 || nv > n_keys) return fail(LSA_ERR_INVALID_ARG, "n_valid[%d] = %lld not in [0, n_keys]", b, (long long)nv);
         a->n_valid[b] = (int32_t)nv;
         a->tile_start[b] = tiles;
-        tiles += (int)((nv + 127) / 128);
+        tiles += (int)((nv + 31) / 32);
     }
     a->tile_start[batch] = tiles;
     return LSA_OK;

@@ -111,7 +111,7 @@ struct ScoreArgs {
     int64_t n_keys;
     int32_t batch, n_idx, heads, ensemble;
     int32_t n_valid[LSA_MAX_BATCH];
-    int32_t tile_start[LSA_MAX_BATCH + 1];   // prefix of 128-key tiles per sequence
+    int32_t tile_start[LSA_MAX_BATCH + 1];   // prefix of 32-key tiles per sequence
 };
 hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, hipStream_t s);
 
