@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LSA_ABI_VERSION 1
+#define LSA_ABI_VERSION 2
 #define LSA_MAX_LAYERS 16
 #define LSA_MAX_BATCH 64
 
@@ -177,12 +177,17 @@ typedef struct lsa_pool_desc {
     int32_t topk;               /* index_topk the selection may produce, <= 1024 */
     int32_t kv_dim;             /* D, [P1]: 512 */
     int32_t batch;              /* sequences, 1 <= batch <= LSA_MAX_BATCH */
-    lsa_dtype dtype;            /* row storage: LSA_F32 or LSA_BF16 */
+    lsa_dtype dtype;            /* row storage: LSA_F32, LSA_BF16 or LSA_F16 */
     lsa_cold_kind cold;         /* where the full store lives */
     uint64_t pinned_cap_bytes;  /* [P1] PINNED_MIB, 0 = unlimited */
     int32_t allow_topk_reduction;
     void* kv_buf;               /* device, caller-owned */
     int64_t kv_stride_b;        /* elements between sequences of kv_buf */
+    /* Optional caller-owned cold store (LSA_COLD_HBM only): when non-NULL the
+       pool allocates none and uses cold_buf + b * cold_stride_b (bytes) as the
+       [cap][kv_dim] rows of sequence b.  Several pools may share one store. */
+    void* cold_buf;
+    int64_t cold_stride_b;      /* bytes between sequences of cold_buf */
 } lsa_pool_desc;
 
 typedef struct lsa_pool_stats_t {
@@ -289,6 +294,71 @@ typedef struct lsa_step_desc {
     int32_t hq; float scale; int32_t batch;
 } lsa_step_desc;
 lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
+
+/* ---------------------------------------------------------------- KVSwap --
+ * KVSwap article, sections 2.2-2.3 and 3.2: keys of a head group are kept as
+ * low-rank factors K ~ U diag(S) V^T; the group's query scores every position,
+ * the top positions are staged into a bounded slot buffer and each head of the
+ * group attends over full-precision K and V rows of those positions.
+ * A segment is one head group of one sequence and layer; rows of the slot
+ * buffer hold [K of the group's heads | V of the group's heads].
+ *
+ * lsa_score_lowrank: for every segment s and position t < T,
+ *     scores[s][t] = q[s] . (U[s] diag(S[s]) V[s]^T)[t,:] = U[s][t,:] . p[s],
+ *     p[s] = diag(S[s]) V[s]^T q[s]     (fp32 accumulation)
+ *   U device f16 [n_seg][T][rank], S device f32 [n_seg][rank],
+ *   V device f16 [n_seg][C][rank], q device f32 [n_seg][C],
+ *   scores device f32 [n_seg][T].  rank in {16, 32, 64}; 1 <= C <= 4096;
+ *   T * rank * 2 < 4 GiB; n_seg <= 65535.  Uses the context workspace
+ *   (n_seg * rank floats). */
+lsa_status lsa_score_lowrank(lsa_ctx* ctx, const void* U, lsa_dtype factor_dtype, int32_t n_seg, int64_t T,
+                             int32_t rank, const float* S, const void* V, int32_t C, const float* q,
+                             float* scores, lsa_stream_t stream);
+
+/* lsa_attend_kv: for segment s and head h < heads, over rows
+ * r = phys[s][0..n_rows[s]-1] of the segment's slot rows,
+ *     out[s,h,:] = sum_r softmax_r(scale * q[s,h,:] . K_h[r,:]) * V_h[r,:]
+ * with K_h[r,:] = row r elements [h*dh, (h+1)*dh) and V_h[r,:] = row r
+ * elements [(heads+h)*dh, (heads+h+1)*dh); fp32 accumulation; out = 0 when
+ * n_rows[s] == 0.
+ *   q   device f32 [n_seg][heads][dh];  out device f32 [n_seg][heads][dh]
+ *   kv  device, dtype F16 or BF16, segment s at element offset s * kv_stride_seg,
+ *       kv_rows rows of 2 * heads * dh elements; phys entries outside
+ *       [0, kv_rows) read as zero rows
+ *   phys device i32 [n_seg][phys_stride]; n_rows device i32 [n_seg], clamped
+ *       to [0, phys_stride]
+ * Supported: 1 <= heads <= 8, dh in {64, 128}, phys_stride <= 4096 and
+ * heads * phys_stride <= 16384. */
+lsa_status lsa_attend_kv(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dtype, int64_t kv_stride_seg,
+                         int64_t kv_rows, int32_t heads, int32_t head_dim, const int32_t* phys,
+                         int32_t phys_stride, const int32_t* n_rows, int32_t n_seg, float scale, float* out,
+                         lsa_stream_t stream);
+
+/* lsa_kvswap_step: one decode step of the KVSwap variant over n_pools pools of
+ * `batch` sequences each (segment s = pool * batch + b): lsa_score_lowrank over
+ * all segments, top-k per segment (lsa_select rules: ties to the lowest
+ * position, output ascending), lsa_stage of every pool (window 0, positions
+ * used as entries directly), then lsa_attend_kv over the staged rows.
+ * Every pool must have window 0, ratio 1, compressed_cap == T, the same batch,
+ * dtype and kv_dim == 2 * heads * head_dim, and their kv_buf must be laid out
+ * back to back: pool p's kv_buf == pool 0's + p * batch * kv_stride_b elements. */
+typedef struct lsa_kvswap_desc {
+    const void* U; const float* S; const void* V; lsa_dtype factor_dtype;
+    int64_t T; int32_t rank;
+    const float* q;             /* device f32 [n_seg][heads * head_dim] */
+    int32_t heads, head_dim;
+    int32_t k;                  /* positions kept per segment, <= 1024 */
+    float* scores;              /* device f32 [n_seg][T] */
+    int32_t* sel;               /* device i32 [n_seg][k] */
+    int32_t* count;             /* device i32 [n_seg] */
+    int32_t n_pools;
+    lsa_pool* const* pools;     /* host [n_pools] */
+    int32_t* phys;              /* device i32 [n_seg][k] */
+    int32_t* n_rows;            /* device i32 [n_seg] */
+    float scale;
+    float* out;                 /* device f32 [n_seg][heads][head_dim] */
+} lsa_kvswap_desc;
+lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ lsa_status fail(lsa_status s, const char* fmt, ...) {
     } while (0)
 
 int elem_bytes(lsa_dtype d) { return d == LSA_F32 ? 4 : 2; }
-bool row_dtype_ok(lsa_dtype d) { return d == LSA_F32 || d == LSA_BF16; }
+bool row_dtype_ok(lsa_dtype d) { return d == LSA_F32 || d == LSA_BF16 || d == LSA_F16; }
 
 int n_cu_current() {
     static int cache[128] = {0};
@@ -166,6 +166,7 @@ struct lsa_pool {
     void* cold_dev = nullptr;   // device address of the cold pool (HBM, or mapped pinned host)
     void* cold_host = nullptr;  // host address when pinned
     int64_t cold_stride_b = 0;  // bytes
+    bool cold_owned = false;    // false: the caller's cold_buf
     uint64_t d2h_bytes = 0;
 };
 
@@ -481,7 +482,7 @@ void lsa_pool_destroy(lsa_pool* p) {
     (void)hipDeviceSynchronize();
     if (p->tables) (void)hipFree(p->tables);
     if (p->cold_host) (void)hipHostFree(p->cold_host);
-    else if (p->cold_dev) (void)hipFree(p->cold_dev);
+    else if (p->cold_dev && p->cold_owned) (void)hipFree(p->cold_dev);
     delete p;
 }
 
@@ -511,6 +512,11 @@ lsa_status lsa_pool_create(lsa_pool** out, const lsa_pool_desc* d) {
         return fail(LSA_ERR_SLOTS_LT_TOPK, "gpu_chunks (%d) must be >= index_topk (%d)", d->gpu_chunks, d->topk);
     const int row_bytes = d->kv_dim * elem_bytes(d->dtype);
     const uint64_t cold_bytes = swap ? (uint64_t)d->batch * (uint64_t)cap * (uint64_t)row_bytes : 0;
+    if (d->cold_buf && d->cold != LSA_COLD_HBM)
+        return fail(LSA_ERR_INVALID_ARG, "a caller-owned cold_buf must be device memory (LSA_COLD_HBM)");
+    if (d->cold_buf && d->batch > 1 && d->cold_stride_b < cap * (int64_t)row_bytes)
+        return fail(LSA_ERR_INVALID_ARG, "cold_stride_b %lld < compressed_cap * row bytes (%lld)",
+                    (long long)d->cold_stride_b, (long long)(cap * (int64_t)row_bytes));
     if (swap && d->cold == LSA_COLD_HOST && d->pinned_cap_bytes && cold_bytes > d->pinned_cap_bytes)
         return fail(LSA_ERR_PINNED_CAP, "pinned cache exceeds cap: required_mib=%llu cap_mib=%llu",
                     (unsigned long long)((cold_bytes + (1u << 20) - 1) >> 20),
@@ -546,8 +552,12 @@ lsa_status lsa_pool_create(lsa_pool** out, const lsa_pool_desc* d) {
     if (e == hipSuccess) e = hipMemset(p->slot_of, 0xFF, sz_slot + 2 * sz_lo);
     if (e == hipSuccess && swap) {
         p->cold_stride_b = (int64_t)C * row_bytes;
-        if (d->cold == LSA_COLD_HBM) {
+        if (d->cold_buf) {
+            p->cold_dev = d->cold_buf;
+            if (d->batch > 1) p->cold_stride_b = d->cold_stride_b;
+        } else if (d->cold == LSA_COLD_HBM) {
             e = hipMalloc(&p->cold_dev, cold_bytes);
+            p->cold_owned = true;
         } else {
             e = hipHostMalloc(&p->cold_host, cold_bytes, hipHostMallocDefault);
             if (e == hipSuccess) e = hipHostGetDevicePointer(&p->cold_dev, p->cold_host, 0);
@@ -832,6 +842,193 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
     }
     st = attend_timed(ctx, aa, s);
     if (st != LSA_OK) return st;
+    return LSA_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ KVSwap
+namespace {
+
+lsa_status lowrank_args(const void* U, lsa_dtype fdt, int32_t n_seg, int64_t T, int32_t rank, const float* S,
+                        const void* V, int32_t C, const float* q, float* scores, LowrankArgs* a) {
+    if (!U || !S || !V || !q || !scores) return fail(LSA_ERR_INVALID_ARG, "lsa_score_lowrank: NULL pointer");
+    if (fdt != LSA_F16) return fail(LSA_ERR_UNSUPPORTED, "factor dtype %d (supported: F16)", (int)fdt);
+    if (n_seg < 0 || T < 0) return fail(LSA_ERR_INVALID_ARG, "n_seg %d, T %lld", n_seg, (long long)T);
+    if (n_seg > 65535) return fail(LSA_ERR_UNSUPPORTED, "n_seg %d > 65535", n_seg);
+    if (rank != 16 && rank != 32 && rank != 64) return fail(LSA_ERR_UNSUPPORTED, "rank %d (supported: 16, 32, 64)", rank);
+    if (C < 1 || C > 4096) return fail(LSA_ERR_UNSUPPORTED, "C %d not in [1, 4096]", C);
+    if ((uint64_t)T * (uint64_t)rank * 2u >= ((uint64_t)1 << 32)) return fail(LSA_ERR_UNSUPPORTED, "U of a segment exceeds 4 GiB");
+    memset(a, 0, sizeof(*a));
+    a->U = static_cast<const uint16_t*>(U);
+    a->S = S;
+    a->V = static_cast<const uint16_t*>(V);
+    a->q = q;
+    a->scores = scores;
+    a->T = T;
+    a->n_seg = n_seg;
+    a->rank = rank;
+    a->C = C;
+    a->rows_per_block = 2048;
+    return LSA_OK;
+}
+
+lsa_status attend_kv_args(const float* q, const void* kv, lsa_dtype dt, int64_t kv_stride_seg, int64_t kv_rows,
+                          int32_t heads, int32_t dh, const int32_t* phys, int32_t phys_stride, const int32_t* n_rows,
+                          int32_t n_seg, float scale, float* out, AttendKVArgs* a) {
+    if (!q || !kv || !phys || !n_rows || !out) return fail(LSA_ERR_INVALID_ARG, "lsa_attend_kv: NULL pointer");
+    if (dt != LSA_F16 && dt != LSA_BF16) return fail(LSA_ERR_UNSUPPORTED, "K/V dtype %d (supported: F16, BF16)", (int)dt);
+    if (heads < 1 || heads > 8) return fail(LSA_ERR_UNSUPPORTED, "heads %d not in [1, 8]", heads);
+    if (dh != 64 && dh != 128) return fail(LSA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", dh);
+    if (n_seg < 0 || phys_stride < 1 || phys_stride > kAttendKVMaxRows || kv_rows < 0 || !isfinite(scale))
+        return fail(LSA_ERR_INVALID_ARG, "n_seg %d, phys_stride %d, kv_rows %lld", n_seg, phys_stride, (long long)kv_rows);
+    if ((int64_t)heads * phys_stride * 4 > 65536)
+        return fail(LSA_ERR_UNSUPPORTED, "heads * phys_stride = %d exceeds the 16384 scores one workgroup keeps in LDS",
+                    heads * phys_stride);
+    const int64_t row_elems = 2LL * heads * dh;
+    if ((uint64_t)kv_rows * (uint64_t)row_elems * 2u >= ((uint64_t)1 << 32))
+        return fail(LSA_ERR_UNSUPPORTED, "a segment's rows exceed 4 GiB");
+    if (n_seg > 1 && kv_stride_seg < kv_rows * row_elems)
+        return fail(LSA_ERR_INVALID_ARG, "kv_stride_seg %lld < kv_rows * row elements", (long long)kv_stride_seg);
+    memset(a, 0, sizeof(*a));
+    a->q = q;
+    a->kv = kv;
+    a->kv_stride_seg = kv_stride_seg;
+    a->kv_rows = kv_rows;
+    a->phys = phys;
+    a->n_rows = n_rows;
+    a->out = out;
+    a->phys_stride = phys_stride;
+    a->n_seg = n_seg;
+    a->heads = heads;
+    a->head_dim = dh;
+    a->dtype = dt;
+    a->scale = scale;
+    return LSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lsa_status lsa_score_lowrank(lsa_ctx* ctx, const void* U, lsa_dtype factor_dtype, int32_t n_seg, int64_t T,
+                             int32_t rank, const float* S, const void* V, int32_t C, const float* q,
+                             float* scores, lsa_stream_t stream) {
+    if (!ctx) return fail(LSA_ERR_INVALID_ARG, "ctx is NULL");
+    LowrankArgs a;
+    lsa_status st = lowrank_args(U, factor_dtype, n_seg, T, rank, S, V, C, q, scores, &a);
+    if (st != LSA_OK) return st;
+    st = ws_ensure(ctx, align_up((size_t)n_seg * rank * 4, 256));
+    if (st != LSA_OK) return st;
+    a.p = static_cast<float*>(ctx->ws);
+    hipStream_t s = (hipStream_t)stream;
+    Timed t(ctx, LSA_K_SCORE, s);
+    HIPTRY(launch_lowrank_score(a, s));
+    t.end();
+    return LSA_OK;
+}
+
+lsa_status lsa_attend_kv(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dtype, int64_t kv_stride_seg,
+                         int64_t kv_rows, int32_t heads, int32_t head_dim, const int32_t* phys,
+                         int32_t phys_stride, const int32_t* n_rows, int32_t n_seg, float scale, float* out,
+                         lsa_stream_t stream) {
+    if (!ctx) return fail(LSA_ERR_INVALID_ARG, "ctx is NULL");
+    AttendKVArgs a;
+    lsa_status st = attend_kv_args(q, kv, dtype, kv_stride_seg, kv_rows, heads, head_dim, phys, phys_stride, n_rows,
+                                   n_seg, scale, out, &a);
+    if (st != LSA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    Timed t(ctx, LSA_K_ATTEND, s);
+    HIPTRY(launch_attend_kv(a, s));
+    t.end();
+    return LSA_OK;
+}
+
+lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t stream) {
+    if (!ctx || !d) return fail(LSA_ERR_INVALID_ARG, "lsa_kvswap_step: NULL argument");
+    if (d->n_pools < 1 || !d->pools || !d->pools[0]) return fail(LSA_ERR_INVALID_ARG, "no pools");
+    if (!d->sel || !d->count || !d->phys || !d->n_rows || !d->out)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_kvswap_step: NULL pointer in the step");
+    const lsa_pool* p0 = d->pools[0];
+    const int B = p0->d.batch;
+    const int64_t n_seg64 = (int64_t)d->n_pools * B;
+    if (n_seg64 > INT32_MAX / 2) return fail(LSA_ERR_UNSUPPORTED, "too many segments");
+    const int n_seg = (int)n_seg64;
+    const int64_t row_elems = 2LL * d->heads * d->head_dim;
+    const int eb = elem_bytes(p0->d.dtype);
+    for (int i = 0; i < d->n_pools; ++i) {
+        const lsa_pool* p = d->pools[i];
+        if (!p) return fail(LSA_ERR_INVALID_ARG, "pool %d is NULL", i);
+        if (p->d.batch != B || p->d.dtype != p0->d.dtype || p->d.kv_dim != row_elems || p->d.window != 0 ||
+            p->d.ratio != 1 || p->cap != d->T || p->d.kv_stride_b != p0->d.kv_stride_b ||
+            p->d.gpu_chunks != p0->d.gpu_chunks)
+            return fail(LSA_ERR_INVALID_ARG,
+                        "pool %d: needs window 0, ratio 1, compressed_cap T, kv_dim 2*heads*head_dim and the "
+                        "batch, dtype, gpu_chunks and kv_stride_b of pool 0", i);
+        const char* want = static_cast<const char*>(p0->d.kv_buf) + (int64_t)i * B * p0->d.kv_stride_b * eb;
+        if (p->d.kv_buf != want) return fail(LSA_ERR_INVALID_ARG, "pool %d: kv_buf is not pool 0's + %d * batch * kv_stride_b", i, i);
+        if (p->swap && p->d.gpu_chunks < d->k)
+            return fail(LSA_ERR_SLOTS_LT_TOPK, "pool %d: gpu_chunks (%d) must be >= k (%d)", i, p->d.gpu_chunks, d->k);
+    }
+    LowrankArgs la;
+    lsa_status st = lowrank_args(d->U, d->factor_dtype, n_seg, d->T, d->rank, d->S, d->V, d->heads * d->head_dim, d->q,
+                                 d->scores, &la);
+    if (st != LSA_OK) return st;
+    if (d->T > INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "T %lld", (long long)d->T);
+    SelectArgs se;
+    size_t sel_need = 0;
+    st = select_setup(ctx, d->scores, n_seg, d->T, nullptr, LSA_SELECT_TOPK, d->k, d->k, 0.5, d->sel, d->count, &se,
+                      &sel_need);
+    if (st != LSA_OK) return st;
+    for (int i = 0; i < d->n_pools; ++i) {
+        st = stage_check(d->pools[i], d->k, 1, d->k);
+        if (st != LSA_OK) return st;
+    }
+    AttendKVArgs ka;
+    st = attend_kv_args(d->q, p0->d.kv_buf, p0->d.dtype, p0->d.kv_stride_b, p0->rows_per_seq, d->heads, d->head_dim,
+                        d->phys, d->k, d->n_rows, n_seg, d->scale, d->out, &ka);
+    if (st != LSA_OK) return st;
+    // workspace: select candidates | p
+    const size_t off_p = align_up(sel_need, 256);
+    st = ws_ensure(ctx, off_p + align_up((size_t)n_seg * d->rank * 4, 256));
+    if (st != LSA_OK) return st;
+    char* ws = static_cast<char*>(ctx->ws);
+    select_bind(&se, ctx->zero, ws);
+    la.p = reinterpret_cast<float*>(ws + off_p);
+
+    hipStream_t s = (hipStream_t)stream;
+    {
+        Timed t(ctx, LSA_K_SCORE, s);
+        HIPTRY(launch_lowrank_score(la, s));
+        t.end();
+    }
+    {
+        Timed t(ctx, LSA_K_SELECT, s);
+        HIPTRY(launch_fm_select(se, s));
+        t.end();
+    }
+    {
+        Timed t(ctx, LSA_K_STAGE, s);
+        for (int i0 = 0; i0 < d->n_pools; i0 += LSA_MAX_LAYERS) {
+            StageArgs ga;
+            memset(&ga, 0, sizeof(ga));
+            ga.batch = B;
+            ga.n_layers = d->n_pools - i0 < LSA_MAX_LAYERS ? d->n_pools - i0 : LSA_MAX_LAYERS;
+            for (int j = 0; j < ga.n_layers; ++j) {
+                const int i = i0 + j;
+                const size_t seg0 = (size_t)i * B;
+                ga.L[j] = stage_layer(d->pools[i], d->sel + seg0 * d->k, d->count + seg0, d->k, 1,
+                                      d->phys + seg0 * d->k, d->k, d->n_rows + seg0);
+            }
+            HIPTRY(launch_kv_stage(ga, s));
+        }
+        t.end();
+    }
+    {
+        Timed t(ctx, LSA_K_ATTEND, s);
+        HIPTRY(launch_attend_kv(ka, s));
+        t.end();
+    }
     return LSA_OK;
 }
 

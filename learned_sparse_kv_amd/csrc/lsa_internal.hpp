@@ -201,3 +201,37 @@ size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows);
 hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid = nullptr);
 
 }  // namespace lsa
+
+namespace lsa {
+
+// --------------------------------------------------------- KVSwap variant
+__device__ inline float f16_to_f32(uint16_t bits) { return (float)__builtin_bit_cast(_Float16, bits); }
+
+struct LowrankArgs {
+    const uint16_t* U;      // [n_seg][T][rank] f16
+    const float* S;         // [n_seg][rank]
+    const uint16_t* V;      // [n_seg][C][rank] f16
+    const float* q;         // [n_seg][C]
+    float* p;               // [n_seg][rank] workspace: S * (V^T q)
+    float* scores;          // [n_seg][T]
+    int64_t T;
+    int32_t n_seg, rank, C;
+    int32_t rows_per_block;
+};
+hipError_t launch_lowrank_score(const LowrankArgs& a, hipStream_t s, hipEvent_t mid = nullptr);
+
+struct AttendKVArgs {
+    const float* q;         // [n_seg][heads * head_dim]
+    const void* kv;         // segment s rows at element s * kv_stride_seg; row = [K heads | V heads]
+    int64_t kv_stride_seg;  // elements
+    int64_t kv_rows;
+    const int32_t* phys;    // [n_seg][phys_stride]
+    const int32_t* n_rows;  // [n_seg]
+    float* out;             // [n_seg][heads][head_dim]
+    int32_t phys_stride, n_seg, heads, head_dim, dtype;
+    float scale;
+};
+constexpr int kAttendKVMaxRows = 4096;
+hipError_t launch_attend_kv(const AttendKVArgs& a, hipStream_t s);
+
+}  // namespace lsa

@@ -42,7 +42,8 @@ class LsaError(RuntimeError):
 class PoolDesc(ctypes.Structure):
     _fields_ = [("ctx", i64), ("ratio", i32), ("window", i32), ("gpu_chunks", i32), ("topk", i32),
                 ("kv_dim", i32), ("batch", i32), ("dtype", i32), ("cold", i32), ("pinned_cap_bytes", u64),
-                ("allow_topk_reduction", i32), ("kv_buf", P), ("kv_stride_b", i64)]
+                ("allow_topk_reduction", i32), ("kv_buf", P), ("kv_stride_b", i64),
+                ("cold_buf", P), ("cold_stride_b", i64)]
 
 
 class PoolStats(ctypes.Structure):
@@ -58,6 +59,15 @@ class StepDesc(ctypes.Structure):
                 ("n_layers", i32), ("pools", P), ("q_attn", P), ("out", P), ("phys", P), ("n_rows", P),
                 ("hq", i32), ("scale", f32), ("batch", i32)]
 
+
+class KVSwapDesc(ctypes.Structure):
+    _fields_ = [("U", P), ("S", P), ("V", P), ("factor_dtype", i32), ("T", i64), ("rank", i32),
+                ("q", P), ("heads", i32), ("head_dim", i32), ("k", i32),
+                ("scores", P), ("sel", P), ("count", P), ("n_pools", i32), ("pools", P),
+                ("phys", P), ("n_rows", P), ("scale", f32), ("out", P)]
+
+
+ABI_VERSION = 2
 
 _SIGS = {
     "lsa_compressed_cap": (i64, [i64, i32]),
@@ -87,6 +97,9 @@ _SIGS = {
     "lsa_stage": (i32, [P, P, P, i32, i32, P, i32, P, P]),
     "lsa_attend": (i32, [P, P, P, i32, i64, i64, P, i32, P, i32, i32, i32, f32, P, P]),
     "lsa_decode_step": (i32, [P, ctypes.POINTER(StepDesc), P]),
+    "lsa_score_lowrank": (i32, [P, P, i32, i32, i64, i32, P, P, i32, P, P, P]),
+    "lsa_attend_kv": (i32, [P, P, P, i32, i64, i64, i32, i32, P, i32, P, i32, f32, P, P]),
+    "lsa_kvswap_step": (i32, [P, ctypes.POINTER(KVSwapDesc), P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -233,7 +246,10 @@ class Pool:
 
     def __init__(self, ctx: int, ratio: int, kv_buf, window: int, gpu_chunks: int, topk: int,
                  kv_dim: int = 512, batch: int = 1, cold: str = "hbm", pinned_cap_bytes: int = 0,
-                 allow_topk_reduction: bool = False, kv_stride_b: Optional[int] = None):
+                 allow_topk_reduction: bool = False, kv_stride_b: Optional[int] = None,
+                 cold_buf=None, cold_stride_b: int = 0):
+        """cold_buf: optional caller-owned device tensor holding the cold rows of
+        every sequence (sequence b at byte offset b * cold_stride_b)."""
         _dev(kv_buf, "kv_buf")
         d = PoolDesc()
         d.ctx, d.ratio, d.window, d.gpu_chunks, d.topk = ctx, ratio, window, gpu_chunks, topk
@@ -241,6 +257,11 @@ class Pool:
         d.pinned_cap_bytes = pinned_cap_bytes
         d.allow_topk_reduction = 1 if allow_topk_reduction else 0
         d.kv_buf = _ptr(kv_buf)
+        if cold_buf is not None:
+            if not cold_buf.is_cuda:
+                raise ValueError("cold_buf must be a device tensor")
+            d.cold_buf, d.cold_stride_b = cold_buf.data_ptr(), cold_stride_b
+        self.cold_buf = cold_buf  # keep the caller's buffer alive
         rows = int(lib().lsa_pool_rows(ctypes.byref(d)))
         d.kv_stride_b = kv_stride_b if kv_stride_b is not None else rows * kv_dim
         if kv_buf.numel() < batch * d.kv_stride_b and batch > 0:
@@ -366,3 +387,47 @@ def decode_step(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, 
     d.n_rows = _ptr(n_rows) if n_rows is not None else None
     d.hq, d.scale, d.batch = hq, float(scale), B
     _check(lib().lsa_decode_step(ctx.h, ctypes.byref(d), _stream(stream)))
+
+
+# ---------------------------------------------------------------- KVSwap
+def score_lowrank(ctx: Ctx, U, S, V, q, scores, stream=None) -> None:
+    """U [n_seg][T][r] f16, S [n_seg][r] f32, V [n_seg][C][r] f16, q [n_seg][C] f32 -> scores [n_seg][T] f32."""
+    for t, n in ((U, "U"), (S, "S"), (V, "V"), (q, "q"), (scores, "scores")):
+        _dev(t, n)
+    n_seg, T, r = U.shape
+    C = V.shape[1]
+    _check(lib().lsa_score_lowrank(ctx.h, _ptr(U), row_dtype_code(U), n_seg, T, r, _ptr(S), _ptr(V), C, _ptr(q),
+                                   _ptr(scores), _stream(stream)))
+
+
+def attend_kv(ctx: Ctx, q, kv, phys, n_rows, out, scale: float, kv_rows: Optional[int] = None,
+              kv_stride_seg: Optional[int] = None, stream=None) -> None:
+    """q [n_seg][heads][dh] f32; kv [n_seg][rows][2*heads*dh] f16/bf16; phys [n_seg][stride] i32;
+    n_rows [n_seg] i32 -> out [n_seg][heads][dh] f32."""
+    for t, n in ((q, "q"), (kv, "kv"), (phys, "phys"), (n_rows, "n_rows"), (out, "out")):
+        _dev(t, n)
+    n_seg, heads, dh = q.shape
+    rows = kv.shape[1] if kv_rows is None else kv_rows
+    stride = kv.shape[1] * kv.shape[2] if kv_stride_seg is None else kv_stride_seg
+    _check(lib().lsa_attend_kv(ctx.h, _ptr(q), _ptr(kv), row_dtype_code(kv), stride, rows, heads, dh, _ptr(phys),
+                               phys.shape[1], _ptr(n_rows), n_seg, float(scale), _ptr(out), _stream(stream)))
+
+
+def kvswap_step(ctx: Ctx, *, U, S, V, q, pools: Sequence[Pool], k: int, heads: int, head_dim: int, scores, sel,
+                count, phys, n_rows, out, scale: float, stream=None) -> None:
+    """One KVSwap decode step (lsa_kvswap_step); segment s = pool * batch + b.
+
+    U [n_seg][T][r] f16; S [n_seg][r]; V [n_seg][C][r] f16; q [n_seg][C] f32; scores [n_seg][T] f32;
+    sel / phys [n_seg][k] i32; count / n_rows [n_seg] i32; out [n_seg][heads][head_dim] f32."""
+    for t, n in ((U, "U"), (S, "S"), (V, "V"), (q, "q"), (scores, "scores"), (sel, "sel"), (count, "count"),
+                 (phys, "phys"), (n_rows, "n_rows"), (out, "out")):
+        _dev(t, n)
+    n_seg, T, r = U.shape
+    d = KVSwapDesc()
+    pool_arr = (P * len(pools))(*[p.h for p in pools])
+    d.U, d.S, d.V, d.factor_dtype, d.T, d.rank = _ptr(U), _ptr(S), _ptr(V), row_dtype_code(U), T, r
+    d.q, d.heads, d.head_dim, d.k = _ptr(q), heads, head_dim, k
+    d.scores, d.sel, d.count = _ptr(scores), _ptr(sel), _ptr(count)
+    d.n_pools, d.pools = len(pools), ctypes.cast(pool_arr, P)
+    d.phys, d.n_rows, d.scale, d.out = _ptr(phys), _ptr(n_rows), float(scale), _ptr(out)
+    _check(lib().lsa_kvswap_step(ctx.h, ctypes.byref(d), _stream(stream)))

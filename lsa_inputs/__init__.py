@@ -286,3 +286,151 @@ def indexer_query_steps(wl: Workload, b: int, steps: int):
         ws.append(w)
         prev = q
     return np.stack(qs), np.stack(ws)
+
+
+# --------------------------------------------------------------------------
+# KVSwap grouped low-rank keys (KVSwap article, sections 2.2-2.3 and 3.2)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class KVSwapWorkload:
+    """Grouped low-rank key prediction: ``layers`` x ``groups`` groups of
+    ``group_heads`` KV heads of width ``head_dim`` per sequence; a group's keys
+    over ``ctx`` positions are given as factors U [ctx][rank], S [rank],
+    V [C][rank] (C = group_heads * head_dim); top ``k`` positions per group are
+    staged into a ``slots``-slot LRU pool and attended per head over full K/V.
+
+    Segment s = (layer * groups + group) * batch + b.  The cold K/V rows of a
+    (group, sequence) are shared by all layers (one synthetic store; see the
+    design notes), each row being [K of the group's heads | V of the group's
+    heads] in f16."""
+    name: str
+    base_seed: int
+    ctx: int
+    batch: int
+    layers: int
+    groups: int
+    k: int
+    slots: int
+    group_heads: int = 4
+    head_dim: int = 128
+    rank: int = 32
+    kv_dtype: str = "f16"
+    steps: int = 8
+    drift: Optional[float] = None
+
+    @property
+    def C(self) -> int:
+        return self.group_heads * self.head_dim
+
+    @property
+    def n_pools(self) -> int:
+        return self.layers * self.groups
+
+    @property
+    def n_seg(self) -> int:
+        return self.n_pools * self.batch
+
+    @property
+    def row_elems(self) -> int:
+        return 2 * self.C
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.head_dim))
+
+    def seg(self, layer: int, group: int, b: int) -> int:
+        return (layer * self.groups + group) * self.batch + b
+
+    def replace(self, **kw) -> "KVSwapWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+KVSWAP_WORKLOADS = {
+    # small case the oracle finishes in seconds: 2 sequences x 2 layers x 2 groups
+    "kvswap_small": KVSwapWorkload(name="kvswap_small", base_seed=1005, ctx=2048, batch=2, layers=2, groups=2,
+                                   k=400, slots=400, steps=6, drift=0.05),
+    # the article's shape: 32K ctx, batch 16, 32 layers x 8 groups of 4 heads x 128, rank 32, top-400
+    "kvswap_32k": KVSwapWorkload(name="kvswap_32k", base_seed=1006, ctx=32768, batch=16, layers=32, groups=8,
+                                 k=400, slots=400, steps=16, drift=0.05),
+}
+
+HALF = 0.5
+
+
+def grid_codes(rng: np.random.Generator, shape, n_points: int) -> np.ndarray:
+    """uint8 codes uniform on 0..n_points-1 (n_points a power of two <= 256),
+    taken from the low bits of raw random bytes; much cheaper than
+    ``grid_uniform`` for the multi-GiB KVSwap tensors."""
+    assert n_points & (n_points - 1) == 0 and 2 <= n_points <= 256
+    n = int(np.prod(shape))
+    return (np.frombuffer(rng.bytes(n), dtype=np.uint8) & np.uint8(n_points - 1)).reshape(shape)
+
+
+# KVSwap tensors are stored as codes: value = (code - offset) / 8
+U_POINTS, U_OFFSET = 8, 4          # U, V on {-1/2, ..., 3/8}
+KV_POINTS, KV_OFFSET = 16, 8       # cold K/V on {-1, ..., 7/8}
+
+
+def codes_to_f32(codes: np.ndarray, offset: int) -> np.ndarray:
+    return (codes.astype(np.float32) - np.float32(offset)) * np.float32(GRID)
+
+
+def code_table_f16(n_points: int, offset: int) -> np.ndarray:
+    """f16 bit patterns of the code values, indexed by code."""
+    return f32_to_f16_bits((np.arange(n_points, dtype=np.float32) - offset) * np.float32(GRID))
+
+
+def lowrank_U_codes(wl: KVSwapWorkload, layer: int, group: int, b: int) -> np.ndarray:
+    return grid_codes(rng_for(wl.base_seed, "U", layer, group, b), (wl.ctx, wl.rank), U_POINTS)
+
+
+def lowrank_U(wl: KVSwapWorkload, layer: int, group: int, b: int) -> np.ndarray:
+    """U [ctx][rank], 1/8 grid on [-1/2, 3/8] (float32 values)."""
+    return codes_to_f32(lowrank_U_codes(wl, layer, group, b), U_OFFSET)
+
+
+def lowrank_S(wl: KVSwapWorkload, layer: int, group: int, b: int) -> np.ndarray:
+    """Singular values S [rank] on the 1/8 grid in [0, 1/2], float32."""
+    return grid_uniform(rng_for(wl.base_seed, "S", layer, group, b), (wl.rank,), lo=0.0, hi=HALF)
+
+
+def lowrank_V_codes(wl: KVSwapWorkload, layer: int, group: int, b: int) -> np.ndarray:
+    return grid_codes(rng_for(wl.base_seed, "V", layer, group, b), (wl.C, wl.rank), U_POINTS)
+
+
+def lowrank_V(wl: KVSwapWorkload, layer: int, group: int, b: int) -> np.ndarray:
+    """V [C][rank], 1/8 grid on [-1/2, 3/8] (float32 values)."""
+    return codes_to_f32(lowrank_V_codes(wl, layer, group, b), U_OFFSET)
+
+
+def kvswap_query(wl: KVSwapWorkload, layer: int, group: int, b: int, step: int,
+                 prev: Optional[np.ndarray] = None) -> np.ndarray:
+    """The group's query [C] (its heads' queries concatenated), 1/8 grid in
+    [-1/2, 1/2].  With ``wl.drift`` set, step t > 0 redraws that fraction of the
+    previous step's coordinates."""
+    rng = rng_for(wl.base_seed, "kq", layer, group, b, step)
+    fresh = grid_uniform(rng, (wl.C,), lo=-HALF, hi=HALF)
+    if wl.drift is None or step == 0:
+        return fresh
+    if prev is None:
+        raise ValueError("a drifting query needs the previous step's q")
+    redraw = rng.random(wl.C) < wl.drift
+    return np.where(redraw, fresh, prev).astype(np.float32)
+
+
+def kvswap_query_steps(wl: KVSwapWorkload, layer: int, group: int, b: int, steps: int) -> np.ndarray:
+    out, prev = [], None
+    for t in range(steps):
+        prev = kvswap_query(wl, layer, group, b, t, prev)
+        out.append(prev)
+    return np.stack(out)
+
+
+def kvswap_cold_codes(wl: KVSwapWorkload, group: int, b: int) -> np.ndarray:
+    return grid_codes(rng_for(wl.base_seed, "kvcold", group, b), (wl.ctx, wl.row_elems), KV_POINTS)
+
+
+def kvswap_cold(wl: KVSwapWorkload, group: int, b: int) -> np.ndarray:
+    """Full-precision K/V rows of one (group, sequence) [ctx][2*C] (float32 values
+    on the 1/8 grid in [-1, 7/8]): the group's heads' keys, then their values."""
+    return codes_to_f32(kvswap_cold_codes(wl, group, b), KV_OFFSET)

@@ -274,3 +274,39 @@ class DecodeState:
             res["misses"].append(lmiss)
             res["out"].append(lout)
         return res
+
+
+# ------------------------------------------------------------ KVSwap step --
+class KVSwapState:
+    """Oracle of KVSwap decode steps for chosen segments (layer, group, b):
+    low-rank score over all positions -> top-k (ties to the lowest position)
+    -> the segment's LRU slot pool (window 0) -> per head attention over the
+    full-precision K/V rows of the selected positions (read from the cold
+    store by position, so it is also the reference with swapping off)."""
+
+    def __init__(self, wl, segs):
+        self.wl = wl
+        self.segs = list(segs)
+        row_bytes = wl.row_elems * 2
+        self.pools = {}
+        for seg in self.segs:
+            p = Pool(wl.ctx, wl.slots, 0, row_bytes)
+            p.store(0, wl.ctx)
+            self.pools[seg] = p
+
+    def step(self, seg, U, S, V, q, cold) -> dict:
+        """U [T][r] f16 codes, S [r] f32, V [C][r] f16 codes, q [C] f32, cold [T][2C] f16 codes
+        -> dict(score, sel, phys, misses, out [heads][dh])."""
+        wl = self.wl
+        e = lowrank_score(U, S, V, q)
+        sel = select(e, "topk", wl.k)
+        st, phys, miss = self.pools[seg].stage(sel)
+        if st != 0:
+            raise RuntimeError(f"oracle stage status {st}")
+        flat = np.ascontiguousarray(cold, dtype=np.uint16).reshape(-1)
+        H, dh, C = wl.group_heads, wl.head_dim, wl.C
+        out = np.zeros((H, dh), np.float32)
+        for h in range(H):
+            out[h] = attend_kv(q[h * dh:(h + 1) * dh], flat[h * dh:], flat[C + h * dh:], "f16", 2 * C, sel,
+                               wl.scale)
+        return dict(score=e, sel=sel, phys=phys, misses=miss, out=out)

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(lsa.EXPORTS)
-    assert L.lsa_abi_version() == 1
+    assert L.lsa_abi_version() == lsa.ABI_VERSION == 2
 
 
 def test_closed_forms_match_oracle():
@@ -87,7 +87,41 @@ def test_pool_validation_errors_before_any_device_call():
     assert _create(_desc(ctx=1 << 20, gpu_chunks=5000, topk=512))[0] == 7
     assert _create(_desc(topk=2000))[0] == 1
     assert _create(_desc(batch=0))[0] == 1
-    assert _create(_desc(dtype=2))[0] == 7
+    assert _create(_desc(dtype=9))[0] == 7
+    # a caller-owned cold store must be device memory and hold every sequence
+    assert _create(_desc(cold=1, cold_buf=0x2000))[0] == 1
+    st, msg = _create(_desc(batch=2, kv_stride_b=1 << 20, cold_buf=0x2000, cold_stride_b=1024))
+    assert st == 1 and "cold_stride_b" in msg
+
+
+def test_kvswap_argument_checks():
+    L = lsa.lib()
+    ctx = 0x10   # never dereferenced: every call below is rejected before using it
+    # lsa_score_lowrank(ctx, U, dtype, n_seg, T, rank, S, V, C, q, scores, stream)
+    assert L.lsa_score_lowrank(None, 0x10, 2, 1, 64, 32, 0x10, 0x10, 512, 0x10, 0x10, None) == 1
+    assert L.lsa_score_lowrank(ctx, None, 2, 1, 64, 32, 0x10, 0x10, 512, 0x10, 0x10, None) == 1
+    assert L.lsa_score_lowrank(ctx, 0x10, 0, 1, 64, 32, 0x10, 0x10, 512, 0x10, 0x10, None) == 7
+    assert L.lsa_score_lowrank(ctx, 0x10, 2, 1, 64, 24, 0x10, 0x10, 512, 0x10, 0x10, None) == 7
+    assert L.lsa_score_lowrank(ctx, 0x10, 2, 1, 64, 32, 0x10, 0x10, 5000, 0x10, 0x10, None) == 7
+    assert L.lsa_score_lowrank(ctx, 0x10, 2, 1, 1 << 27, 32, 0x10, 0x10, 512, 0x10, 0x10, None) == 7
+    # lsa_attend_kv(ctx, q, kv, dtype, kv_stride_seg, kv_rows, heads, dh, phys, phys_stride, n_rows, n_seg, scale, out, s)
+    args = [ctx, 0x10, 0x10, 2, 1 << 20, 400, 4, 128, 0x10, 400, 0x10, 2, 0.1, 0x10, None]
+
+    def akv(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.lsa_attend_kv(*a)
+    assert akv(a0=None) == 1
+    assert akv(a3=0) == 7            # f32 rows
+    assert akv(a6=9) == 7            # heads
+    assert akv(a7=96) == 7           # head_dim
+    assert akv(a9=5000) == 1         # phys_stride
+    assert akv(a4=1000) == 1         # kv_stride_seg below kv_rows * row elements
+    assert akv(a12=float("nan")) == 1
+    assert L.lsa_kvswap_step(None, None, None) == 1
+    d = lsa.KVSwapDesc()
+    assert L.lsa_kvswap_step(ctx, ctypes.byref(d), None) == 1   # no pools
 
 
 def test_pool_rows_swap_auto_disable():

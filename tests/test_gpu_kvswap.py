@@ -1,0 +1,122 @@
+"""GPU parity of the KVSwap variant (KVSwap article, sections 2.2-2.3 and 3.2)
+with the oracle: low-rank scores bit-identical (exact on the grid), identical
+top-k sets and slot rows, per-head attention within 1e-5 per row (both sides
+read the same f16 values; only fp32 vs double accumulation differs)."""
+import numpy as np
+import pytest
+import torch
+
+import lsa_inputs as L
+import oracle
+from learned_sparse_kv_amd import lsa
+from learned_sparse_kv_amd.kvswap_workload import DeviceKVSwap
+
+from gpu_util import DEV, bits, rel_err_rows, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    return lsa.Ctx(0)
+
+
+def _rand_codes(rng, shape, pts, off):
+    return L.codes_to_f32(rng.integers(0, pts, size=shape, dtype=np.uint8), off)
+
+
+@pytest.mark.parametrize("n_seg,T,rank,C", [(1, 1, 32, 512), (3, 2047, 32, 512), (2, 5000, 16, 256),
+                                            (2, 4096, 64, 128), (5, 2048, 32, 8)])
+def test_score_lowrank_bit_identical(ctx, n_seg, T, rank, C):
+    say(f"score_lowrank n_seg={n_seg} T={T} rank={rank} C={C}")
+    rng = np.random.default_rng(T + rank)
+    U = _rand_codes(rng, (n_seg, T, rank), 8, 4)
+    V = _rand_codes(rng, (n_seg, C, rank), 8, 4)
+    S = _rand_codes(rng, (n_seg, rank), 8, 4) + np.float32(0.5)
+    q = _rand_codes(rng, (n_seg, C), 8, 4)
+    Ub, Vb = L.f32_to_f16_bits(U), L.f32_to_f16_bits(V)
+    to16 = lambda a: torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.float16)
+    sc = torch.full((n_seg, T), 7.0, device=DEV)
+    lsa.score_lowrank(ctx, to16(Ub), torch.from_numpy(S).to(DEV), to16(Vb), torch.from_numpy(q).to(DEV), sc)
+    got = sc.cpu().numpy()
+    for s in range(n_seg):
+        want = oracle.lowrank_score(Ub[s], S[s], Vb[s], q[s])
+        assert np.array_equal(bits(got[s]), bits(want)), f"segment {s}"
+
+
+@pytest.mark.parametrize("heads,dh,dtype", [(4, 128, "f16"), (1, 64, "f16"), (8, 128, "bf16"), (3, 64, "bf16")])
+def test_attend_kv_matches_oracle(ctx, heads, dh, dtype):
+    say(f"attend_kv heads={heads} dh={dh} {dtype}")
+    rng = np.random.default_rng(heads * dh)
+    n_seg, rows, stride = 6, 450, 420
+    row_elems = 2 * heads * dh
+    kv = _rand_codes(rng, (n_seg, rows, row_elems), 16, 8)
+    enc = L.f32_to_f16_bits(kv) if dtype == "f16" else L.f32_to_bf16_bits(kv)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    kv_dev = torch.from_numpy(enc.view(np.int16)).to(DEV).view(tdt)
+    q = rng.standard_normal((n_seg, heads, dh)).astype(np.float32)
+    n_rows = np.array([0, 1, 37, 400, 420, 64], np.int32)
+    phys = np.stack([rng.permutation(rows)[:stride] for _ in range(n_seg)]).astype(np.int32)
+    phys[5, 3] = rows + 7          # outside the segment: reads as a zero row
+    out = torch.full((n_seg, heads, dh), 9.0, device=DEV)
+    lsa.attend_kv(ctx, torch.from_numpy(q).to(DEV), kv_dev, torch.from_numpy(phys).to(DEV),
+                  torch.from_numpy(n_rows).to(DEV), out, 1.0 / np.sqrt(dh))
+    got = out.cpu().numpy()
+    zero_row = np.zeros((1, row_elems), enc.dtype)
+    for s in range(n_seg):
+        n = n_rows[s]
+        if n == 0:
+            assert np.all(got[s] == 0)
+            continue
+        store = np.concatenate([enc[s], zero_row])
+        pos = np.where(phys[s, :n] < rows, phys[s, :n], rows).astype(np.int32)
+        flat = store.reshape(-1)
+        for h in range(heads):
+            want = oracle.attend_kv(q[s, h], flat[h * dh:], flat[(heads + h) * dh:], dtype, row_elems, pos,
+                                    1.0 / np.sqrt(dh))
+            err = rel_err_rows(got[s, h], want)
+            assert err <= TOL, f"segment {s} head {h}: rel err {err}"
+
+
+def run_kvswap(wl, steps, segs=None):
+    say(f"kvswap {wl.name}: {steps} steps, n_seg={wl.n_seg}, T={wl.ctx}, k={wl.k}, slots={wl.slots}")
+    dw = DeviceKVSwap(wl, log=say)
+    dw.make_steps(steps)
+    segs = list(range(wl.n_seg)) if segs is None else segs
+    ref = oracle.KVSwapState(wl, segs)
+    inputs = {s: dw.host_inputs(s, 0) for s in segs}
+    misses = {s: 0 for s in segs}
+    for t in range(steps):
+        dw.step(t)
+        torch.cuda.synchronize()
+        sc, sel, cnt = dw.scores.cpu().numpy(), dw.sel.cpu().numpy(), dw.count.cpu().numpy()
+        phys, nrows, out = dw.phys.cpu().numpy(), dw.n_rows.cpu().numpy(), dw.out.cpu().numpy()
+        for s in segs:
+            U, S, V, _, cold = inputs[s]
+            want = ref.step(s, U, S, V, dw.q_np[t, s], cold)
+            assert np.array_equal(bits(sc[s]), bits(want["score"])), f"step {t} seg {s}: scores"
+            n = want["sel"].size
+            assert cnt[s] == n and np.array_equal(sel[s, :n], want["sel"]), f"step {t} seg {s}: selection"
+            assert nrows[s] == n and np.array_equal(phys[s, :n], want["phys"]), f"step {t} seg {s}: slot rows"
+            err = rel_err_rows(out[s], want["out"])
+            assert err <= TOL, f"step {t} seg {s}: rel err {err}"
+            misses[s] += len(want["misses"])
+        say(f"  step {t} ok")
+    B = wl.batch
+    for p, pool in enumerate(dw.pools):
+        st = pool.stats()
+        covered = [s for s in range(p * B, (p + 1) * B) if s in misses]
+        if len(covered) == B:
+            assert st["misses"] == sum(misses[s] for s in covered), f"pool {p} misses"
+    return dw
+
+
+def test_kvswap_small_all_segments():
+    run_kvswap(L.KVSWAP_WORKLOADS["kvswap_small"], 6)
+
+
+def test_kvswap_32k_full_size_sampled_segments():
+    wl = L.KVSWAP_WORKLOADS["kvswap_32k"]
+    segs = [0, 1, wl.seg(13, 5, 7), wl.n_seg - 1]
+    run_kvswap(wl, 2, segs)
