@@ -328,7 +328,7 @@ lsa_status lsa_score_lowrank(lsa_ctx* ctx, const void* U, lsa_dtype factor_dtype
  *   phys device i32 [n_seg][phys_stride]; n_rows device i32 [n_seg], clamped
  *       to [0, phys_stride]
  * Supported: 1 <= heads <= 8, dh in {64, 128}, phys_stride <= 4096 and
- * heads * phys_stride <= 16384. */
+ * (heads + 2) * phys_stride <= 16384. */
 lsa_status lsa_attend_kv(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dtype, int64_t kv_stride_seg,
                          int64_t kv_rows, int32_t heads, int32_t head_dim, const int32_t* phys,
                          int32_t phys_stride, const int32_t* n_rows, int32_t n_seg, float scale, float* out,

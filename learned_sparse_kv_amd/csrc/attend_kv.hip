@@ -50,31 +50,76 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
     constexpr int kLpr = DH * 2 / 16;       // lanes per row slice
     constexpr int kRpi = 64 / kLpr;         // rows per wave load
     constexpr int kUnroll = 4;
-    extern __shared__ float sz[];           // [heads][phys_stride]
+    // LDS: per list row its slot byte offset and cold row (-1: none), then per head the scores
+    extern __shared__ int32_t lds[];
     const int s = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (h >= a.heads) return;
     const int sub = lane % kLpr, rg = lane / kLpr;
-    float* z = sz + h * a.phys_stride;
     int n = a.n_rows[s];
     n = n < 0 ? 0 : (n > a.phys_stride ? a.phys_stride : n);
     float* out = a.out + ((int64_t)s * a.heads + h) * DH;
-    if (n == 0) {
+    if (n == 0) {   // uniform over the workgroup
         if (lane < kLpr)
             for (int e = 0; e < 8; ++e) out[lane * 8 + e] = 0.0f;
         return;
     }
+    uint32_t* s_off = reinterpret_cast<uint32_t*>(lds);
+    int32_t* s_src = lds + a.phys_stride;
+    float* z = reinterpret_cast<float*>(lds + 2 * a.phys_stride) + h * a.phys_stride;
+
     const uint32_t row_bytes = (uint32_t)(2 * a.heads * DH * 2);
     const uint32_t nrec = (uint32_t)a.kv_rows * row_bytes;
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc(static_cast<const char*>(a.kv) + a.kv_stride_seg * 2 * s, nrec);
     const int32_t* ph = a.phys + (int64_t)s * a.phys_stride;
-    auto row_off = [&](int i) -> uint32_t {
-        const int32_t p = i < n ? ph[i] : -1;
-        // rows outside [0, kv_rows) read as zero
-        return ((uint32_t)p < (uint32_t)a.kv_rows) ? (uint32_t)p * row_bytes : nrec;
+    const int32_t* srcs = a.src ? a.src + (int64_t)s * a.phys_stride : nullptr;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int32_t p = ph[i];
+        // rows outside [0, kv_rows) read as zero (offset past the buffer)
+        s_off[i] = ((uint32_t)p < (uint32_t)a.kv_rows) ? (uint32_t)p * row_bytes : nrec;
+        s_src[i] = srcs ? srcs[i] : -1;
+    }
+    __syncthreads();
+
+    // deferred staging: a missed row is read from the cold store and this
+    // head's K (pass 1) or V (pass 2) slice is written into its slot.  Every
+    // lane issues both a slot load and a cold load; the one it does not need
+    // is pointed past its buffer, reads zero and moves no data, so the loads of
+    // a batch stay branch-free and in flight together.
+    const uint32_t cold_rec = srcs ? (uint32_t)a.cold_rows * row_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(srcs ? reinterpret_cast<const void*>(a.seg_cold[s]) : a.kv, cold_rec);
+    auto load_batch = [&](int i0, uint32_t slice, uint4* v) {
+        int32_t c[kUnroll];
+        uint32_t off[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = i0 + u * kRpi + rg;
+            off[u] = i < n ? s_off[i] : nrec;
+            c[u] = i < n ? s_src[i] : -1;
+        }
+        if (!srcs) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) v[u] = buffer_load16(r, off[u] + slice);
+            return;
+        }
+        uint4 w[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const bool cold = (uint32_t)c[u] < (uint32_t)a.cold_rows;
+            v[u] = buffer_load16(r, (cold ? nrec : off[u]) + slice);
+            w[u] = buffer_load16(rc, cold ? (uint32_t)c[u] * row_bytes + slice : cold_rec);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const bool cold = (uint32_t)c[u] < (uint32_t)a.cold_rows;
+            v[u] = make_uint4(v[u].x | w[u].x, v[u].y | w[u].y, v[u].z | w[u].z, v[u].w | w[u].w);
+            const u32x4 d = {v[u].x, v[u].y, v[u].z, v[u].w};
+            // the slot write goes past the buffer (dropped) unless this row was missed
+            __builtin_amdgcn_raw_buffer_store_b128(d, r, (cold && off[u] < nrec) ? off[u] + slice : nrec, 0, 0);
+        }
     };
+
     float qv[8];
     {
         const float* qh = a.q + ((int64_t)s * a.heads + h) * DH + sub * 8;
@@ -87,8 +132,7 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
     // pass 1: z_i = scale * q . K_i
     for (int i0 = 0; i0 < n; i0 += kRpi * kUnroll) {
         uint4 kv[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) kv[u] = buffer_load16(r, row_off(i0 + u * kRpi + rg) + k_off);
+        load_batch(i0, k_off, kv);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             float f[8];
@@ -127,8 +171,7 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < n; i0 += kRpi * kUnroll) {
         uint4 vv[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) vv[u] = buffer_load16(r, row_off(i0 + u * kRpi + rg) + v_off);
+        load_batch(i0, v_off, vv);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int i = i0 + u * kRpi + rg;
@@ -152,7 +195,7 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
 
 template <int DH>
 hipError_t launch_dh(const AttendKVArgs& a, hipStream_t s) {
-    const size_t lds = (size_t)a.heads * a.phys_stride * sizeof(float);
+    const size_t lds = (size_t)(a.heads + 2) * a.phys_stride * sizeof(float);
     if (a.dtype == LSA_F16)
         hipLaunchKernelGGL((attend_kv_kernel<DH, uint16_t>), dim3(a.n_seg), dim3(64 * a.heads), lds, s, a);
     else if (a.dtype == LSA_BF16)

@@ -74,6 +74,8 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
     }
     if (l >= 0 && !L.ready[(int64_t)b * L.cap + l]) atomicOr(&L.meta[b * 4 + 1], 1);
 
+    if (L.seg_cold && tid == 0)
+        L.seg_cold[b] = (uint64_t)(static_cast<const char*>(L.cold) + b * L.cold_stride_b);
     int32_t* src = L.defer_copy ? L.src + (int64_t)b * L.phys_stride : nullptr;
     if (src) {
         for (int r = tid; r < L.window; r += kNT) src[r] = -1;

@@ -882,9 +882,9 @@ lsa_status attend_kv_args(const float* q, const void* kv, lsa_dtype dt, int64_t 
     if (dh != 64 && dh != 128) return fail(LSA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", dh);
     if (n_seg < 0 || phys_stride < 1 || phys_stride > kAttendKVMaxRows || kv_rows < 0 || !isfinite(scale))
         return fail(LSA_ERR_INVALID_ARG, "n_seg %d, phys_stride %d, kv_rows %lld", n_seg, phys_stride, (long long)kv_rows);
-    if ((int64_t)heads * phys_stride * 4 > 65536)
-        return fail(LSA_ERR_UNSUPPORTED, "heads * phys_stride = %d exceeds the 16384 scores one workgroup keeps in LDS",
-                    heads * phys_stride);
+    if ((int64_t)(heads + 2) * phys_stride * 4 > 65536)
+        return fail(LSA_ERR_UNSUPPORTED, "(heads + 2) * phys_stride = %d exceeds the 16384 words one workgroup keeps in LDS",
+                    (heads + 2) * phys_stride);
     const int64_t row_elems = 2LL * heads * dh;
     if ((uint64_t)kv_rows * (uint64_t)row_elems * 2u >= ((uint64_t)1 << 32))
         return fail(LSA_ERR_UNSUPPORTED, "a segment's rows exceed 4 GiB");
@@ -974,7 +974,8 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     lsa_status st = lowrank_args(d->U, d->factor_dtype, n_seg, d->T, d->rank, d->S, d->V, d->heads * d->head_dim, d->q,
                                  d->scores, &la);
     if (st != LSA_OK) return st;
-    if (d->T > INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "T %lld", (long long)d->T);
+    if (d->T > INT32_MAX || (uint64_t)d->T * (uint64_t)row_elems * (uint64_t)eb >= ((uint64_t)1 << 32))
+        return fail(LSA_ERR_UNSUPPORTED, "T %lld: a sequence's cold rows must stay below 4 GiB", (long long)d->T);
     SelectArgs se;
     size_t sel_need = 0;
     st = select_setup(ctx, d->scores, n_seg, d->T, nullptr, LSA_SELECT_TOPK, d->k, d->k, 0.5, d->sel, d->count, &se,
@@ -988,13 +989,21 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     st = attend_kv_args(d->q, p0->d.kv_buf, p0->d.dtype, p0->d.kv_stride_b, p0->rows_per_seq, d->heads, d->head_dim,
                         d->phys, d->k, d->n_rows, n_seg, d->scale, d->out, &ka);
     if (st != LSA_OK) return st;
-    // workspace: select candidates | p
+    // workspace: select candidates | p | src | seg_cold
     const size_t off_p = align_up(sel_need, 256);
-    st = ws_ensure(ctx, off_p + align_up((size_t)n_seg * d->rank * 4, 256));
+    const size_t off_src = off_p + align_up((size_t)n_seg * d->rank * 4, 256);
+    const size_t off_cold = off_src + align_up((size_t)n_seg * d->k * 4, 256);
+    st = ws_ensure(ctx, off_cold + align_up((size_t)n_seg * 8, 256));
     if (st != LSA_OK) return st;
     char* ws = static_cast<char*>(ctx->ws);
     select_bind(&se, ctx->zero, ws);
     la.p = reinterpret_cast<float*>(ws + off_p);
+    int32_t* srcs = reinterpret_cast<int32_t*>(ws + off_src);
+    uint64_t* seg_cold = reinterpret_cast<uint64_t*>(ws + off_cold);
+    // missed rows are read from the cold store by the attention, which also fills their slots
+    ka.src = srcs;
+    ka.seg_cold = seg_cold;
+    ka.cold_rows = d->T;
 
     hipStream_t s = (hipStream_t)stream;
     {
@@ -1019,6 +1028,9 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
                 const size_t seg0 = (size_t)i * B;
                 ga.L[j] = stage_layer(d->pools[i], d->sel + seg0 * d->k, d->count + seg0, d->k, 1,
                                       d->phys + seg0 * d->k, d->k, d->n_rows + seg0);
+                ga.L[j].defer_copy = 1;
+                ga.L[j].src = srcs + seg0 * d->k;
+                ga.L[j].seg_cold = seg_cold + seg0;
             }
             HIPTRY(launch_kv_stage(ga, s));
         }

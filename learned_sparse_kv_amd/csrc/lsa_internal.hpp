@@ -160,6 +160,9 @@ struct StageLayer {
     // missed rows from the cold pool and fills their slots
     int32_t defer_copy;
     int32_t* src;               // [batch][phys_stride]
+    // optional: seg_cold[b] = address of sequence b's cold rows (written by the
+    // stage, so a later kernel can find a missed row without the pool)
+    uint64_t* seg_cold;         // [batch]
 };
 struct StageArgs {
     int32_t n_layers, batch;
@@ -230,6 +233,12 @@ struct AttendKVArgs {
     float* out;             // [n_seg][heads][head_dim]
     int32_t phys_stride, n_seg, heads, head_dim, dtype;
     float scale;
+    // optional (deferred staging): list row i with src[s][i] >= 0 is read from
+    // cold row src of the segment's cold store (address seg_cold[s]) and
+    // written into its slot row phys[s][i]
+    const int32_t* src;         // [n_seg][phys_stride]
+    const uint64_t* seg_cold;   // [n_seg]
+    int64_t cold_rows;          // rows of each segment's cold store
 };
 constexpr int kAttendKVMaxRows = 4096;
 hipError_t launch_attend_kv(const AttendKVArgs& a, hipStream_t s);
