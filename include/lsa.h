@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LSA_ABI_VERSION 2
+#define LSA_ABI_VERSION 3
 #define LSA_MAX_LAYERS 16
 #define LSA_MAX_BATCH 64
 
@@ -294,6 +294,34 @@ typedef struct lsa_step_desc {
     int32_t hq; float scale; int32_t batch;
 } lsa_step_desc;
 lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
+
+/* ------------------------------------------------------ lookahead schedule --
+ * [P2] LSA section: the memory indexer predicts, ahead of time, which chunks
+ * the coming decoding window will use, and only those are recalled to the GPU;
+ * [P1] limitations and future work: global scoring runs synchronously in the
+ * reference and overlapping it is listed as future work.
+ * Here the prediction for the next step overlaps the current step:
+ *   lsa_lookahead_prime(ctx, d, s): score d->q_idx / d->w_idx, select and stage
+ *     every layer on stream s: the rows of the first step (their missed rows
+ *     are copied by the first lsa_lookahead_step).
+ *   lsa_lookahead_step(ctx, d, s): for the current step, copy its missed rows
+ *     into their slots and attend d->q_attn over its staged rows (writing
+ *     d->out); for the NEXT step, score d->q_idx / d->w_idx (the indexer query
+ *     that predicts it), select and stage.  Five launches on s, each pairing
+ *     independent work of the two steps (row copy with the key scan, attention
+ *     with the selection histogram, attention combine with the selection's
+ *     candidate pass), then the select's last pass and the stage.
+ * The outputs equal lsa_decode_step's when step t's call carries the indexer
+ * query of step t+1: every kernel body is the same, and the stage of step t+1
+ * runs after step t's attention has finished.
+ * d->phys / d->n_rows, when given, hold two buffers: [2][n_layers][batch][window + k]
+ * and [2][n_layers][batch]; the context alternates between them (the rows of
+ * the coming step are in buffer lsa_lookahead_buffer(ctx)).  Calls that
+ * overlap on one context race; a captured step replays correctly only in the
+ * order it was captured. */
+lsa_status lsa_lookahead_prime(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
+lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
+int32_t    lsa_lookahead_buffer(const lsa_ctx* ctx);
 
 /* ---------------------------------------------------------------- KVSwap --
  * KVSwap article, sections 2.2-2.3 and 3.2: keys of a head group are kept as

@@ -30,6 +30,7 @@
 namespace lsa {
 
 namespace {
+namespace score_k {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -72,7 +73,7 @@ __device__ inline void unpack16<uint16_t>(const uint4& u, float* out) {
 }
 
 template <int DK, typename KT>
-__global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a) {
+__device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, const int gx) {
     using C = Cfg<DK, KT>;
     constexpr int kPerRead = 16 / (int)sizeof(KT);
     __shared__ __attribute__((aligned(16))) char lds[kWaves][kTile * C::kLdsStride];
@@ -84,8 +85,8 @@ __global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a
     const int half = lane >> 5;     // which half of dk this lane feeds
 
     const int total = a.tile_start[a.batch];
-    const int stride = gridDim.x * kWaves;
-    int t = blockIdx.x * kWaves + wave;
+    const int stride = gx * kWaves;
+    int t = bx * kWaves + wave;
     if (t >= total) return;
 
     auto seq_of = [&](int tile) {
@@ -193,6 +194,11 @@ __global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a
 }
 
 template <int DK, typename KT>
+__global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a) {
+    fm_score_body<DK, KT>(a, blockIdx.x, gridDim.x);
+}
+
+template <int DK, typename KT>
 hipError_t launch_t(const ScoreArgs& a, int n_cu, hipStream_t s) {
     const int total = a.tile_start[a.batch];
     if (total == 0) return hipSuccess;
@@ -202,8 +208,13 @@ hipError_t launch_t(const ScoreArgs& a, int n_cu, hipStream_t s) {
     return hipGetLastError();
 }
 
+}  // namespace score_k
+#ifndef LSA_BODIES_ONLY
+using namespace score_k;
+#endif
 }  // namespace
 
+#ifndef LSA_BODIES_ONLY
 hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, hipStream_t s) {
     if (key_dtype == LSA_F32) {
         if (dk == 32) return launch_t<32, float>(a, n_cu, s);
@@ -216,5 +227,7 @@ hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, 
     }
     return hipErrorInvalidValue;
 }
+
+#endif  // LSA_BODIES_ONLY
 
 }  // namespace lsa

@@ -35,6 +35,7 @@
 namespace lsa {
 
 namespace {
+namespace select_k {
 
 constexpr int kNT = 1024;
 constexpr int kNW = kNT / 64;
@@ -199,35 +200,40 @@ __device__ inline bool entry(const SelectArgs& a, const float* sc, int64_t j, in
     return v;
 }
 
-__global__ __launch_bounds__(kBlkThreads) void sel_hist_kernel(const SelectArgs a) {
-    constexpr int PER = kBlk / kBlkThreads;
+template <int NT>
+__device__ __forceinline__ void sel_hist_body(const SelectArgs& a, const int bx, const int by) {
+    constexpr int PER = kBlk / NT;
     __shared__ uint32_t h[kSelBins];
-    const int tid = threadIdx.x, seg = blockIdx.y;
-    const int64_t base = (int64_t)blockIdx.x * kBlk;
+    const int tid = threadIdx.x, seg = by;
+    const int64_t base = (int64_t)bx * kBlk;
     const int n_valid = seg_valid(a, seg);
     const float* sc = a.scores + (int64_t)seg * a.n_keys;
     // all loads first: one memory latency per block instead of one per entry
     float x[PER];
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-        const int64_t j = base + it * kBlkThreads + tid;
+        const int64_t j = base + it * NT + tid;
         x[it] = j < n_valid ? sc[j] : 0.0f;
     }
-    for (int i = tid; i < kSelBins; i += kBlkThreads) h[i] = 0u;
+    for (int i = tid; i < kSelBins; i += NT) h[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-        const int64_t j = base + it * kBlkThreads + tid;
+        const int64_t j = base + it * NT + tid;
         bool v = j < n_valid;
         if (a.mode == LSA_SELECT_THRESHOLD) v = v && (x[it] > a.t_f);
         hist_add(h, v, order_key(x[it]) >> kSelShift);
     }
     __syncthreads();
     uint32_t* g = a.hist + (int64_t)seg * kSelBins;
-    for (int i = tid; i < kSelBins; i += kBlkThreads) {
+    for (int i = tid; i < kSelBins; i += NT) {
         const uint32_t c = h[i];
         if (c) atomicAdd(&g[i], c);
     }
+}
+
+__global__ __launch_bounds__(kBlkThreads) void sel_hist_kernel(const SelectArgs a) {
+    sel_hist_body<kBlkThreads>(a, blockIdx.x, blockIdx.y);
 }
 
 // From the segment histogram: out[0] = boundary bucket b* (-1 if nothing is
@@ -268,11 +274,11 @@ __device__ void find_boundary(const uint32_t* g, int k, int* s_scan, int* out) {
 // Every 1024-entry block keeps, in index order, its entries in buckets >= b*
 // (those above b* are chosen for sure; those in b* are the candidates), with
 // their keys; the top index bit marks a candidate.
-__global__ __launch_bounds__(kBlkThreads) void sel_collect_kernel(const SelectArgs a) {
+__device__ __forceinline__ void sel_collect_body(const SelectArgs& a, const int bx, const int by) {
     constexpr int PER = kColBlk / kBlkThreads;   // 4 consecutive entries per thread
     __shared__ int s_scan[kBlkThreads / 64 + 1];
     __shared__ int s_b[3];
-    const int tid = threadIdx.x, seg = blockIdx.y, blk = blockIdx.x;
+    const int tid = threadIdx.x, seg = by, blk = bx;
     const int n_valid = seg_valid(a, seg);
     const float* sc = a.scores + (int64_t)seg * a.n_keys;
     const int64_t base = (int64_t)blk * kColBlk + tid * PER;
@@ -303,6 +309,10 @@ __global__ __launch_bounds__(kBlkThreads) void sel_collect_kernel(const SelectAr
         ++pos;
     }
     if (tid == 0) a.blk_count[(int64_t)seg * a.nblk + blk] = tot;
+}
+
+__global__ __launch_bounds__(kBlkThreads) void sel_collect_kernel(const SelectArgs a) {
+    sel_collect_body(a, blockIdx.x, blockIdx.y);
 }
 
 // Exact selection straight from the scores by one workgroup: four radix passes
@@ -475,8 +485,13 @@ int next_pow2(int x) {
     return p;
 }
 
+}  // namespace select_k
+#ifndef LSA_BODIES_ONLY
+using namespace select_k;
+#endif
 }  // namespace
 
+#ifndef LSA_BODIES_ONLY
 bool select_plan(SelectArgs* a, size_t* zero_bytes, size_t* ws_bytes) {
     if (a->k > 4096) return false;
     if (a->n_keys <= kSelSingle) {
@@ -508,6 +523,12 @@ void select_bind(SelectArgs* a, void* zero_region, void* ws) {
     a->blk_key = reinterpret_cast<uint32_t*>(w + nb * kColBlk * 4);
 }
 
+hipError_t launch_fm_select_final(const SelectArgs& a, hipStream_t s) {
+    if (a.path == 0) return launch_fm_select(a, s);
+    hipLaunchKernelGGL(sel_final_kernel, dim3(a.n_seg), dim3(kNT), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_fm_select(const SelectArgs& a, hipStream_t s) {
     if (a.path == 0) {
         const dim3 grid(a.n_seg), block(kNT);
@@ -532,5 +553,7 @@ hipError_t launch_fm_select(const SelectArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(sel_final_kernel, dim3(a.n_seg), dim3(kNT), 0, s, a);
     return hipGetLastError();
 }
+
+#endif  // LSA_BODIES_ONLY
 
 }  // namespace lsa

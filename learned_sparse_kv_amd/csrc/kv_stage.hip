@@ -29,9 +29,54 @@
 namespace lsa {
 
 namespace {
+namespace stage_k {
 
 constexpr int kNT = 1024;
 constexpr int kMaxSlots = 4096;
+
+// Copies `chunks` 16-byte chunks (cpr per row) of the rows src_row[m] of
+// `cold` to rows dst_row_off + dst_row[m] of `kv`, eight chunks in flight per
+// thread.  The loads are unconditional (a chunk past the end re-reads the last
+// one) and the batch is held in named registers; only the stores are
+// predicated.
+template <int NT>
+__device__ inline void copy_rows(const char* cold, char* kv, int row_bytes, int chunks, int cpr, const int* src_row,
+                                 const int* dst_row, int dst_row_off) {
+    const int tid = threadIdx.x;
+    auto addr = [&](int c, int64_t& from, int64_t& to) {
+        const int cc = c < chunks ? c : chunks - 1;
+        const int m = cc / cpr, off = (cc - m * cpr) * 16;
+        from = (int64_t)src_row[m] * row_bytes + off;
+        to = (int64_t)(dst_row_off + dst_row[m]) * row_bytes + off;
+    };
+    for (int c0 = 0; c0 < chunks; c0 += NT * 8) {
+        int64_t f0, f1, f2, f3, f4, f5, f6, f7, t0, t1, t2, t3, t4, t5, t6, t7;
+        addr(c0 + 0 * NT + tid, f0, t0);
+        addr(c0 + 1 * NT + tid, f1, t1);
+        addr(c0 + 2 * NT + tid, f2, t2);
+        addr(c0 + 3 * NT + tid, f3, t3);
+        addr(c0 + 4 * NT + tid, f4, t4);
+        addr(c0 + 5 * NT + tid, f5, t5);
+        addr(c0 + 6 * NT + tid, f6, t6);
+        addr(c0 + 7 * NT + tid, f7, t7);
+        const uint4 v0 = *reinterpret_cast<const uint4*>(cold + f0);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(cold + f1);
+        const uint4 v2 = *reinterpret_cast<const uint4*>(cold + f2);
+        const uint4 v3 = *reinterpret_cast<const uint4*>(cold + f3);
+        const uint4 v4 = *reinterpret_cast<const uint4*>(cold + f4);
+        const uint4 v5 = *reinterpret_cast<const uint4*>(cold + f5);
+        const uint4 v6 = *reinterpret_cast<const uint4*>(cold + f6);
+        const uint4 v7 = *reinterpret_cast<const uint4*>(cold + f7);
+        if (c0 + 0 * NT + tid < chunks) *reinterpret_cast<uint4*>(kv + t0) = v0;
+        if (c0 + 1 * NT + tid < chunks) *reinterpret_cast<uint4*>(kv + t1) = v1;
+        if (c0 + 2 * NT + tid < chunks) *reinterpret_cast<uint4*>(kv + t2) = v2;
+        if (c0 + 3 * NT + tid < chunks) *reinterpret_cast<uint4*>(kv + t3) = v3;
+        if (c0 + 4 * NT + tid < chunks) *reinterpret_cast<uint4*>(kv + t4) = v4;
+        if (c0 + 5 * NT + tid < chunks) *reinterpret_cast<uint4*>(kv + t5) = v5;
+        if (c0 + 6 * NT + tid < chunks) *reinterpret_cast<uint4*>(kv + t6) = v6;
+        if (c0 + 7 * NT + tid < chunks) *reinterpret_cast<uint4*>(kv + t7) = v7;
+    }
+}
 
 __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
     const StageLayer& L = a.L[blockIdx.y];
@@ -166,26 +211,7 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
     const int chunks = n_miss * cpr;
     const char* cold = static_cast<const char*>(L.cold) + b * L.cold_stride_b;
     char* kv = static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes;
-    constexpr int kBatch = 8;
-    for (int c0 = 0; c0 < chunks; c0 += kNT * kBatch) {
-        uint4 v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int c = c0 + u * kNT + tid;
-            if (c < chunks) {
-                const int m = c / cpr, off = (c - m * cpr) * 16;
-                v[u] = *reinterpret_cast<const uint4*>(cold + (int64_t)s_mlog[m] * L.row_bytes + off);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int c = c0 + u * kNT + tid;
-            if (c < chunks) {
-                const int m = c / cpr, off = (c - m * cpr) * 16;
-                *reinterpret_cast<uint4*>(kv + (int64_t)(L.window + s_mslot[m]) * L.row_bytes + off) = v[u];
-            }
-        }
-    }
+    copy_rows<kNT>(cold, kv, L.row_bytes, chunks, cpr, s_mlog, s_mslot, L.window);
 }
 
 __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L, int b, int64_t first, int64_t count) {
@@ -201,7 +227,57 @@ __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L,
         *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(src + off);
 }
 
+// Copies the rows a stage recorded as missed (src[b][r] >= 0: cold entry of
+// list row r) from the cold pool into their slots.  One workgroup per 32 list
+// rows of one (layer, sequence); every load of a batch is issued before any
+// store, so reads of pinned host rows keep many PCIe requests in flight.
+constexpr int kFetchRows = 32;
+constexpr int kFetchNT = 256;
+__device__ __forceinline__ void fetch_missed_body(const StageArgs& a, const int bx, const int by, const int bz) {
+    const StageLayer& L = a.L[bz];
+    const int b = by, r0 = bx * kFetchRows;
+    if (!L.swap || r0 >= L.phys_stride) return;
+    __shared__ int s_src[kFetchRows], s_dst[kFetchRows];
+    __shared__ int s_n;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    if (tid < kFetchRows) {
+        const int r = r0 + tid;
+        const int n = L.n_rows[b];
+        const int sr = (r < n && r < L.phys_stride) ? L.src[(int64_t)b * L.phys_stride + r] : -1;
+        const int ph = (r < n && r < L.phys_stride) ? L.phys[(int64_t)b * L.phys_stride + r] : -1;
+        // only rows the stage itself recorded: a cold entry below cap and a slot row
+        if (sr >= 0 && sr < L.cap && ph >= L.window && ph < L.window + L.S) {
+            const int i = atomicAdd(&s_n, 1);
+            s_src[i] = sr;
+            s_dst[i] = ph;
+        }
+    }
+    __syncthreads();
+    const int cpr = L.row_bytes / 16;
+    const int chunks = s_n * cpr;
+    const char* cold = static_cast<const char*>(L.cold) + b * L.cold_stride_b;
+    char* kv = static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes;
+    copy_rows<kFetchNT>(cold, kv, L.row_bytes, chunks, cpr, s_src, s_dst, 0);
+}
+
+__global__ __launch_bounds__(kFetchNT) void fetch_missed_kernel(const StageArgs a) {
+    fetch_missed_body(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+}  // namespace stage_k
+#ifndef LSA_BODIES_ONLY
+using namespace stage_k;
+#endif
 }  // namespace
+
+#ifndef LSA_BODIES_ONLY
+hipError_t launch_fetch_missed(const StageArgs& a, int phys_stride, hipStream_t s) {
+    const dim3 grid((unsigned)((phys_stride + kFetchRows - 1) / kFetchRows), a.batch, a.n_layers);
+    hipLaunchKernelGGL(fetch_missed_kernel, grid, dim3(kFetchNT), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(kv_stage_kernel, dim3(a.batch, a.n_layers), dim3(kNT), 0, s, a);
@@ -214,5 +290,7 @@ hipError_t launch_refresh_staged(const StageLayer& L, int b, int64_t first, int6
     hipLaunchKernelGGL(refresh_staged_kernel, grid, dim3(256), 0, s, L, b, first, count);
     return hipGetLastError();
 }
+
+#endif  // LSA_BODIES_ONLY
 
 }  // namespace lsa

@@ -69,6 +69,9 @@ struct lsa_ctx {
     };
     std::vector<Pending> pending;
     std::vector<hipEvent_t> spare;
+    // lookahead schedule: which of the two row-list buffers holds the rows of
+    // the coming step
+    int la_cur = 0;
 };
 
 namespace {
@@ -735,18 +738,36 @@ lsa_status lsa_attend(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dt
 }
 
 // ------------------------------------------------------------- decode step
-lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
-    if (!ctx || !d) return fail(LSA_ERR_INVALID_ARG, "lsa_decode_step: NULL argument");
+}  // extern "C"
+
+namespace {
+
+// Everything one decode step launches, validated and bound to the workspace.
+// n_buf row-list buffers are laid out (2 for the lookahead schedule).
+struct StepPlan {
+    ScoreArgs sa;
+    SelectArgs se;
+    StageArgs ga;           // per layer; phys / n_rows / src point at buffer 0
+    AttendArgs aa;
+    int B = 0, D = 0, W = 0, L = 0, k_eff = 0, phys_stride = 0;
+    int32_t* phys = nullptr;     // [n_buf][L][B][phys_stride]
+    int32_t* n_rows = nullptr;   // [n_buf][L][B]
+    int32_t* srcs = nullptr;     // [n_buf][L][B][phys_stride]
+};
+
+lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* P) {
+    if (!ctx || !d) return fail(LSA_ERR_INVALID_ARG, "decode step: NULL argument");
     if (d->n_layers < 1 || d->n_layers > LSA_MAX_LAYERS)
         return fail(LSA_ERR_INVALID_ARG, "n_layers %d not in [1, %d]", d->n_layers, LSA_MAX_LAYERS);
     if (!d->pools || !d->q_attn || !d->out || !d->scores || !d->sel || !d->count)
-        return fail(LSA_ERR_INVALID_ARG, "lsa_decode_step: NULL pointer in the step");
+        return fail(LSA_ERR_INVALID_ARG, "decode step: NULL pointer in the step");
     const lsa_pool* p0 = d->pools[0];
     if (!p0) return fail(LSA_ERR_INVALID_ARG, "pool 0 is NULL");
     const int B = d->batch, D = p0->d.kv_dim, W = p0->d.window;
     const lsa_dtype dt = p0->d.dtype;
     if (d->hq < 1 || d->hq > 16) return fail(LSA_ERR_UNSUPPORTED, "hq %d (supported 1..16)", d->hq);
     if (D != 128 && D != 256 && D != 512) return fail(LSA_ERR_UNSUPPORTED, "kv_dim %d", D);
+    if (dt != LSA_F32 && dt != LSA_BF16) return fail(LSA_ERR_UNSUPPORTED, "row dtype %d (supported: F32, BF16)", (int)dt);
     if (!isfinite(d->scale)) return fail(LSA_ERR_INVALID_ARG, "scale");
     int k_eff = d->k;
     for (int l = 0; l < d->n_layers; ++l) {
@@ -761,13 +782,11 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
             k_eff = p->d.gpu_chunks;
         }
     }
-    ScoreArgs sa;
     lsa_status st = score_args(d->keys, d->key_dtype, B, d->n_keys, d->n_valid, d->dk, d->q_idx, d->w_idx, d->n_idx,
-                               d->heads, d->ensemble, d->scores, &sa);
+                               d->heads, d->ensemble, d->scores, &P->sa);
     if (st != LSA_OK) return st;
-    SelectArgs se;
     size_t sel_need = 0;
-    st = select_setup(ctx, d->scores, B, d->n_keys, d->n_valid, d->mode, k_eff, d->k, d->tau, d->sel, d->count, &se,
+    st = select_setup(ctx, d->scores, B, d->n_keys, d->n_valid, d->mode, k_eff, d->k, d->tau, d->sel, d->count, &P->se,
                       &sel_need);
     if (st != LSA_OK) return st;
     const int phys_stride = W + d->k;
@@ -777,71 +796,164 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
         st = stage_check(d->pools[l], k_eff, d->src_ratio, phys_stride);
         if (st != LSA_OK) return st;
     }
-    // workspace: select candidates | attend partials | phys | n_rows
+    const int L = d->n_layers;
+    // workspace: select candidates | attend partials | phys | n_rows | src
     const size_t off_att = align_up(sel_need, 256);
-    const size_t att_bytes = attend_workspace_bytes(d->n_layers, B, D, phys_stride);
+    const size_t att_bytes = attend_workspace_bytes(L, B, D, phys_stride);
     const size_t off_phys = off_att + align_up(att_bytes, 256);
-    const size_t phys_bytes = d->phys ? 0 : align_up((size_t)d->n_layers * B * phys_stride * 4, 256);
+    const size_t phys_bytes = d->phys ? 0 : align_up((size_t)n_buf * L * B * phys_stride * 4, 256);
     const size_t off_nrows = off_phys + phys_bytes;
-    const size_t nrows_bytes = d->n_rows ? 0 : align_up((size_t)d->n_layers * B * 4, 256);
+    const size_t nrows_bytes = d->n_rows ? 0 : align_up((size_t)n_buf * L * B * 4, 256);
     const size_t off_src = off_nrows + nrows_bytes;
-    const size_t src_bytes = align_up((size_t)d->n_layers * B * phys_stride * 4, 256);
+    const size_t src_bytes = align_up((size_t)n_buf * L * B * phys_stride * 4, 256);
     st = ws_ensure(ctx, off_src + src_bytes);
     if (st != LSA_OK) return st;
     char* ws = static_cast<char*>(ctx->ws);
-    select_bind(&se, ctx->zero, ws);
-    int32_t* phys = d->phys ? d->phys : reinterpret_cast<int32_t*>(ws + off_phys);
-    int32_t* n_rows = d->n_rows ? d->n_rows : reinterpret_cast<int32_t*>(ws + off_nrows);
-    int32_t* srcs = reinterpret_cast<int32_t*>(ws + off_src);
+    select_bind(&P->se, ctx->zero, ws);
+    P->phys = d->phys ? d->phys : reinterpret_cast<int32_t*>(ws + off_phys);
+    P->n_rows = d->n_rows ? d->n_rows : reinterpret_cast<int32_t*>(ws + off_nrows);
+    P->srcs = reinterpret_cast<int32_t*>(ws + off_src);
+    P->B = B;
+    P->D = D;
+    P->W = W;
+    P->L = L;
+    P->k_eff = k_eff;
+    P->phys_stride = phys_stride;
 
-    StageArgs ga;
-    memset(&ga, 0, sizeof(ga));
-    ga.n_layers = d->n_layers;
-    ga.batch = B;
-    AttendArgs aa;
-    memset(&aa, 0, sizeof(aa));
-    aa.n_layers = d->n_layers;
-    aa.batch = B;
-    aa.hq = d->hq;
-    aa.D = D;
-    aa.dtype = dt;
-    aa.max_splits = (phys_stride + kAttendRows - 1) / kAttendRows;
-    aa.scale = d->scale;
-    aa.part_acc = reinterpret_cast<float*>(ws + off_att);
-    aa.part_ml = aa.part_acc + (size_t)d->n_layers * B * aa.max_splits * 16 * D;
-    for (int l = 0; l < d->n_layers; ++l) {
+    memset(&P->ga, 0, sizeof(P->ga));
+    P->ga.n_layers = L;
+    P->ga.batch = B;
+    memset(&P->aa, 0, sizeof(P->aa));
+    P->aa.n_layers = L;
+    P->aa.batch = B;
+    P->aa.hq = d->hq;
+    P->aa.D = D;
+    P->aa.dtype = dt;
+    P->aa.max_splits = (phys_stride + kAttendRows - 1) / kAttendRows;
+    P->aa.scale = d->scale;
+    P->aa.part_acc = reinterpret_cast<float*>(ws + off_att);
+    P->aa.part_ml = P->aa.part_acc + (size_t)L * B * P->aa.max_splits * 16 * D;
+    for (int l = 0; l < L; ++l) {
         const lsa_pool* p = d->pools[l];
-        int32_t* ph = phys + (size_t)l * B * phys_stride;
-        int32_t* nr = n_rows + (size_t)l * B;
-        int32_t* sr = srcs + (size_t)l * B * phys_stride;
-        ga.L[l] = stage_layer(p, d->sel, d->count, d->k, d->src_ratio, ph, phys_stride, nr);
-        ga.L[l].defer_copy = 1;
-        ga.L[l].src = sr;
-        // a swapping layer's missed rows are read from the cold pool by the
-        // attention, which also fills their slots
-        aa.L[l] = AttendLayer{d->q_attn + (size_t)l * B * d->hq * D, p->d.kv_buf, ph, nr,
-                              d->out + (size_t)l * B * d->hq * D, p->d.kv_stride_b, p->rows_per_seq, phys_stride,
-                              p->swap ? sr : nullptr, p->d.kv_buf, p->cold_dev, p->cold_stride_b, p->cap};
+        int32_t* ph = P->phys + (size_t)l * B * phys_stride;
+        int32_t* nr = P->n_rows + (size_t)l * B;
+        int32_t* sr = P->srcs + (size_t)l * B * phys_stride;
+        P->ga.L[l] = stage_layer(p, d->sel, d->count, d->k, d->src_ratio, ph, phys_stride, nr);
+        P->ga.L[l].defer_copy = 1;
+        P->ga.L[l].src = sr;
+        P->aa.L[l] = AttendLayer{d->q_attn + (size_t)l * B * d->hq * D, p->d.kv_buf, ph, nr,
+                                 d->out + (size_t)l * B * d->hq * D, p->d.kv_stride_b, p->rows_per_seq, phys_stride,
+                                 nullptr, p->d.kv_buf, p->cold_dev, p->cold_stride_b, p->cap};
     }
+    return LSA_OK;
+}
 
-    hipStream_t s = (hipStream_t)stream;
+// Point the stage and attention of a plan at row-list buffer `buf`.
+void plan_use_buffer(StepPlan* P, int buf) {
+    const size_t per_buf = (size_t)P->L * P->B;
+    for (int l = 0; l < P->L; ++l) {
+        int32_t* ph = P->phys + (buf * per_buf + (size_t)l * P->B) * P->phys_stride;
+        int32_t* nr = P->n_rows + buf * per_buf + (size_t)l * P->B;
+        P->ga.L[l].phys = ph;
+        P->ga.L[l].n_rows = nr;
+        P->ga.L[l].src = P->srcs + (buf * per_buf + (size_t)l * P->B) * P->phys_stride;
+        P->aa.L[l].phys = ph;
+        P->aa.L[l].n_rows = nr;
+    }
+}
+
+lsa_status launch_predict(lsa_ctx* ctx, const StepPlan& P, const lsa_step_desc* d, hipStream_t s, bool fetch) {
     {
         Timed t(ctx, LSA_K_SCORE, s);
-        HIPTRY(launch_fm_score(sa, d->key_dtype, d->dk, ctx->n_cu, s));
+        HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s));
         t.end();
     }
     {
         Timed t(ctx, LSA_K_SELECT, s);
-        HIPTRY(launch_fm_select(se, s));
+        HIPTRY(launch_fm_select(P.se, s));
         t.end();
     }
     {
         Timed t(ctx, LSA_K_STAGE, s);
-        HIPTRY(launch_kv_stage(ga, s));
+        HIPTRY(launch_kv_stage(P.ga, s));
         t.end();
     }
-    st = attend_timed(ctx, aa, s);
+    if (fetch) {
+        Timed t(ctx, LSA_K_GATHER, s);
+        HIPTRY(launch_fetch_missed(P.ga, P.phys_stride, s));
+        t.end();
+    }
+    return LSA_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
+    StepPlan P;
+    lsa_status st = step_plan(ctx, d, 1, &P);
     if (st != LSA_OK) return st;
+    // a swapping layer's missed rows are read from the cold pool by the
+    // attention, which also fills their slots
+    for (int l = 0; l < P.L; ++l)
+        if (d->pools[l]->swap) P.aa.L[l].src = P.ga.L[l].src;
+    hipStream_t s = (hipStream_t)stream;
+    st = launch_predict(ctx, P, d, s, false);
+    if (st != LSA_OK) return st;
+    return attend_timed(ctx, P.aa, s);
+}
+
+int32_t lsa_lookahead_buffer(const lsa_ctx* ctx) { return ctx ? ctx->la_cur : 0; }
+
+lsa_status lsa_lookahead_prime(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
+    StepPlan P;
+    lsa_status st = step_plan(ctx, d, 2, &P);
+    if (st != LSA_OK) return st;
+    ctx->la_cur = 0;
+    plan_use_buffer(&P, 0);
+    // the first step's rows are staged; its lookahead step copies the missed ones
+    return launch_predict(ctx, P, d, (hipStream_t)stream, false);
+}
+
+// Step t (rows in buffer cur) and the prediction of step t+1 (into buffer
+// nxt), as five launches on one stream; see lookahead.hip.
+lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
+    StepPlan P;
+    lsa_status st = step_plan(ctx, d, 2, &P);
+    if (st != LSA_OK) return st;
+    const int cur = ctx->la_cur, nxt = cur ^ 1;
+    hipStream_t s = (hipStream_t)stream;
+    plan_use_buffer(&P, cur);
+    const StageArgs fetch_cur = P.ga;   // the rows step t reads, and its recorded misses
+    {
+        Timed t(ctx, LSA_K_SCORE, s);
+        HIPTRY(launch_la_fetch_score(P.sa, fetch_cur, P.phys_stride, d->key_dtype, d->dk, ctx->n_cu, s));
+        t.end();
+    }
+    {
+        Timed t(ctx, LSA_K_ATTEND, s);
+        HIPTRY(launch_la_attend_hist(P.aa, P.se, s));
+        t.end();
+    }
+    {
+        Timed t(ctx, LSA_K_COMBINE, s);
+        HIPTRY(launch_la_combine_collect(P.aa, P.se, s));
+        t.end();
+    }
+    {
+        Timed t(ctx, LSA_K_SELECT, s);
+        HIPTRY(launch_fm_select_final(P.se, s));
+        t.end();
+    }
+    plan_use_buffer(&P, nxt);
+    {
+        Timed t(ctx, LSA_K_STAGE, s);
+        HIPTRY(launch_kv_stage(P.ga, s));
+        t.end();
+    }
+    ctx->la_cur = nxt;
     return LSA_OK;
 }
 

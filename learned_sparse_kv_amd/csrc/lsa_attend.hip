@@ -20,6 +20,7 @@
 namespace lsa {
 
 namespace {
+namespace attend_k {
 
 constexpr int kR = kAttendRows;   // rows per split
 constexpr int kThreads = 512;
@@ -56,7 +57,7 @@ __device__ inline void unpack<uint16_t>(const uint4& u, float* out) {
 }
 
 template <int D, typename KT>
-__global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendArgs a) {
+__device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int bx, const int by, const int bz) {
     constexpr int RB = D * (int)sizeof(KT);          // row bytes
     constexpr int LS = RB + 16;                      // LDS row stride
     constexpr int CPR = RB / 16;                     // 16-byte chunks per row
@@ -73,15 +74,15 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
     __shared__ int s_ph[kR];
     __shared__ int s_src[kR];
 
-    const AttendLayer& L = a.L[blockIdx.z];
-    const int b = blockIdx.y, split = blockIdx.x;
+    const AttendLayer& L = a.L[bz];
+    const int b = by, split = bx;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int n = L.n_rows[b];
     n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
     const int r0 = split * kR;
     if (r0 >= n) return;
     const int cnt = n - r0 < kR ? n - r0 : kR;
-    const int pair = blockIdx.z * a.batch + b;
+    const int pair = bz * a.batch + b;
 
     if (tid < kR) {
         int p = tid < cnt ? L.phys[(int64_t)b * L.phys_stride + r0 + tid] : -1;
@@ -192,6 +193,11 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
     }
 }
 
+template <int D, typename KT>
+__global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendArgs a) {
+    attend_split_body<D, KT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
 // One workgroup per (layer, sequence, 32-column slice of D): the splits'
 // maxima and denominators are staged in LDS with one parallel load, every
 // thread then merges two outputs over the splits in split order, eight
@@ -199,18 +205,18 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
 constexpr int kCombCols = 32;
 
 template <int D>
-__global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a) {
+__device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const int bx, const int by, const int bz) {
     __shared__ float s_ml[kMaxSplits * 32];
     __shared__ float s_w[kMaxSplits][16];   // exp(m_s - M_h)
     __shared__ float s_inv[16];             // 1 / sum_s exp(m_s - M_h) l_s
-    const AttendLayer& L = a.L[blockIdx.z];
-    const int b = blockIdx.y;
+    const AttendLayer& L = a.L[bz];
+    const int b = by;
     const int tid = threadIdx.x;
     int n = L.n_rows[b];
     n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
     const int ns = (n + kR - 1) / kR;
-    const int pair = blockIdx.z * a.batch + b;
-    const int d0 = blockIdx.x * kCombCols;
+    const int pair = bz * a.batch + b;
+    const int d0 = bx * kCombCols;
     const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
     for (int i = tid; i < ns * 32; i += 256) s_ml[i] = ml[i];
     __syncthreads();
@@ -259,6 +265,11 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a)
     out[c + 16] = n1 * s_inv[h];
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a) {
+    attend_combine_body<D>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
 template <int D, typename KT>
 hipError_t launch_t(const AttendArgs& a, hipStream_t s, hipEvent_t mid) {
     const dim3 g1(a.max_splits, a.batch, a.n_layers);
@@ -274,8 +285,13 @@ hipError_t launch_t(const AttendArgs& a, hipStream_t s, hipEvent_t mid) {
     return hipGetLastError();
 }
 
+}  // namespace attend_k
+#ifndef LSA_BODIES_ONLY
+using namespace attend_k;
+#endif
 }  // namespace
 
+#ifndef LSA_BODIES_ONLY
 size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows) {
     const size_t splits = (size_t)((max_rows + kR - 1) / kR);
     return (size_t)n_layers * batch * splits * (16 * (size_t)D + 32) * sizeof(float);
@@ -294,5 +310,7 @@ hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid)
     }
     return hipErrorInvalidValue;
 }
+
+#endif  // LSA_BODIES_ONLY
 
 }  // namespace lsa

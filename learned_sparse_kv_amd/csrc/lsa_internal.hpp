@@ -169,6 +169,10 @@ struct StageArgs {
     StageLayer L[LSA_MAX_LAYERS];
 };
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s);
+// copy the rows a deferred stage recorded in src[] from the cold pool into their slots
+hipError_t launch_fetch_missed(const StageArgs& a, int phys_stride, hipStream_t s);
+// the select's last launch alone (path 1: the final kernel; path 0: the whole select)
+hipError_t launch_fm_select_final(const SelectArgs& a, hipStream_t s);
 // copy the rows of entries [first, first+count) of sequence b that are staged
 // from the cold pool into their slots
 hipError_t launch_refresh_staged(const StageLayer& L, int b, int64_t first, int64_t count,
@@ -202,6 +206,11 @@ constexpr int kAttendRows = 32;
 constexpr int kAttendMaxRows = 5120;    // longest row list (window + entries) of one attention
 size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows);
 hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid = nullptr);
+// fused launches of the lookahead schedule
+hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
+                                 int n_cu, hipStream_t s);
+hipError_t launch_la_attend_hist(const AttendArgs& aa, const SelectArgs& se, hipStream_t s);
+hipError_t launch_la_combine_collect(const AttendArgs& aa, const SelectArgs& se, hipStream_t s);
 
 }  // namespace lsa
 

@@ -67,7 +67,7 @@ class KVSwapDesc(ctypes.Structure):
                 ("phys", P), ("n_rows", P), ("scale", f32), ("out", P)]
 
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _SIGS = {
     "lsa_compressed_cap": (i64, [i64, i32]),
@@ -97,6 +97,9 @@ _SIGS = {
     "lsa_stage": (i32, [P, P, P, i32, i32, P, i32, P, P]),
     "lsa_attend": (i32, [P, P, P, i32, i64, i64, P, i32, P, i32, i32, i32, f32, P, P]),
     "lsa_decode_step": (i32, [P, ctypes.POINTER(StepDesc), P]),
+    "lsa_lookahead_prime": (i32, [P, ctypes.POINTER(StepDesc), P]),
+    "lsa_lookahead_step": (i32, [P, ctypes.POINTER(StepDesc), P]),
+    "lsa_lookahead_buffer": (i32, [P]),
     "lsa_score_lowrank": (i32, [P, P, i32, i32, i64, i32, P, P, i32, P, P, P]),
     "lsa_attend_kv": (i32, [P, P, P, i32, i64, i64, i32, i32, P, i32, P, i32, f32, P, P]),
     "lsa_kvswap_step": (i32, [P, ctypes.POINTER(KVSwapDesc), P]),
@@ -356,6 +359,70 @@ def attend(ctx: Ctx, q, kv, phys, n_rows, out, scale: float, kv_rows: Optional[i
     stride = kv.shape[1] * kv.shape[2] if kv_stride_b is None else kv_stride_b
     _check(lib().lsa_attend(ctx.h, _ptr(q), _ptr(kv), row_dtype_code(kv), stride, rows, _ptr(phys), phys.shape[1],
                             _ptr(n_rows), B, hq, D, float(scale), _ptr(out), _stream(stream)))
+
+
+def _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble="max",
+               mode="topk", tau=0.5, n_valid=None, phys=None, n_rows=None):
+    for t, n in ((keys, "keys"), (q_idx, "q_idx"), (w_idx, "w_idx"), (q_attn, "q_attn"), (out, "out"),
+                 (scores, "scores"), (sel, "sel"), (count, "count")):
+        _dev(t, n)
+    B, N, dk = keys.shape
+    _, n_idx, H, _ = q_idx.shape
+    L, _, hq, D = q_attn.shape
+    if L != len(pools):
+        raise ValueError("q_attn's first dimension must equal the number of pools")
+    d = StepDesc()
+    nv = _host_i64(n_valid)
+    pool_arr = (P * len(pools))(*[p.h for p in pools])
+    d.keys, d.key_dtype, d.n_keys, d.n_valid, d.dk = _ptr(keys), row_dtype_code(keys), N, \
+        (ctypes.cast(nv, P) if nv else None), dk
+    d.q_idx, d.w_idx, d.n_idx, d.heads, d.ensemble = _ptr(q_idx), _ptr(w_idx), n_idx, H, ENS[ensemble]
+    d.mode, d.k, d.tau, d.src_ratio = MODE[mode], k, float(tau), src_ratio
+    d.scores, d.sel, d.count = _ptr(scores), _ptr(sel), _ptr(count)
+    d.n_layers, d.pools, d.q_attn, d.out = len(pools), ctypes.cast(pool_arr, P), _ptr(q_attn), _ptr(out)
+    d.phys = _ptr(phys) if phys is not None else None
+    d.n_rows = _ptr(n_rows) if n_rows is not None else None
+    d.hq, d.scale, d.batch = hq, float(scale), B
+    return d, (nv, pool_arr)
+
+
+def lookahead_prime(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,
+                    k: int, src_ratio: int, scale: float, ensemble: str = "max", mode: str = "topk",
+                    tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None) -> None:
+    """Stage the rows of the first lookahead step (lsa_lookahead_prime); arguments as decode_step,
+    with phys [2][L][B][window + k] and n_rows [2][L][B] when given."""
+    d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
+                         mode, tau, n_valid, phys, n_rows)
+    _check(lib().lsa_lookahead_prime(ctx.h, ctypes.byref(d), _stream(stream)))
+
+
+def lookahead_step(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,
+                   k: int, src_ratio: int, scale: float, ensemble: str = "max", mode: str = "topk",
+                   tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None) -> None:
+    """Attend this step (q_attn -> out) while predicting and staging the next one from q_idx / w_idx
+    (lsa_lookahead_step)."""
+    d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
+                         mode, tau, n_valid, phys, n_rows)
+    _check(lib().lsa_lookahead_step(ctx.h, ctypes.byref(d), _stream(stream)))
+
+
+class PreparedStep:
+    """A step descriptor marshalled once and launched many times (the tensors it
+    points at must stay alive and keep their addresses)."""
+
+    def __init__(self, fn_name: str, ctx: Ctx, stream=None, **kw):
+        self.desc, self._keep = _step_desc(**kw)
+        self._fn = getattr(lib(), fn_name)
+        self._ctx = ctx.h
+        self._ref = ctypes.byref(self.desc)
+        self._stream = _stream(stream)
+
+    def __call__(self) -> None:
+        _check(self._fn(self._ctx, self._ref, self._stream))
+
+
+def lookahead_buffer(ctx: Ctx) -> int:
+    return int(lib().lsa_lookahead_buffer(ctx.h))
 
 
 def decode_step(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,

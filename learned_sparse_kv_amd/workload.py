@@ -111,6 +111,46 @@ class DeviceWorkload:
                         tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys, n_rows=self.n_rows,
                         stream=stream)
 
+    # ---- lookahead schedule: step t attends with the rows staged during step
+    # t-1 (or by prime) and predicts step t+1 from q_idx[t+1]
+    def _la_buffers(self):
+        if getattr(self, "phys2", None) is None:
+            wl = self.wl
+            self.phys2 = torch.zeros((2, wl.n_layers, wl.batch, wl.window + wl.k), dtype=torch.int32, device=self.dev)
+            self.n_rows2 = torch.zeros((2, wl.n_layers, wl.batch), dtype=torch.int32, device=self.dev)
+
+    def _la_args(self, t_idx: int, t_attn: int):
+        wl = self.wl
+        self._la_buffers()
+        return dict(keys=self.keys, q_idx=self.q_idx[t_idx], w_idx=self.w_idx[t_idx], pools=self.pools,
+                    q_attn=self.q_attn[t_attn], out=self.out, scores=self.scores, sel=self.sel, count=self.count,
+                    k=wl.k, src_ratio=wl.src_ratio, scale=wl.scale, ensemble=wl.ensemble, mode=wl.mode,
+                    tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys2, n_rows=self.n_rows2)
+
+    def lookahead_prime(self, t: int = 0, stream=None) -> None:
+        lsa.lookahead_prime(self.ctx, stream=stream, **self._la_args(t, t))
+
+    def lookahead_step(self, t: int, stream=None) -> None:
+        """Attend step t and stage step t+1 (needs the queries of step t+1)."""
+        lsa.lookahead_step(self.ctx, stream=stream, **self._la_args(t + 1, t))
+
+    def prepare_lookahead(self, steps) -> None:
+        """Marshal the descriptors of the listed lookahead steps once (launch with run_prepared)."""
+        self.prepared = {t: lsa.PreparedStep("lsa_lookahead_step", self.ctx, **self._la_args(t + 1, t))
+                         for t in steps}
+
+    def run_prepared(self, t: int) -> None:
+        self.prepared[t]()
+
+    def capture_lookahead(self, steps) -> None:
+        self.graphs = {}
+        for t in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.lookahead_step(t)
+            self.graphs[t] = g
+        torch.cuda.synchronize()
+
     def capture(self, steps) -> None:
         """Capture each listed step as a HIP graph (torch.cuda.CUDAGraph around
         one lsa.decode_step).  The step enqueues only kernel launches, so the
