@@ -20,11 +20,20 @@
 // 0..dk/2-1, half 1 the rest); A uses the same permutation, so the products
 // are unchanged.  LDS rows are padded by 16 bytes so that 8 consecutive rows
 // start in different bank groups.
-// Every wave works on its own 32-key tiles and LDS region with wave-scope
-// fences only -- no workgroup barriers -- and issues the next tile's loads
-// before the MFMAs of the current one, so one wave's memory phase overlaps
-// another's MFMAs.  The grid is one 4-wave workgroup per CU (fewer when the
-// scan is short), which keeps every wave's share of tiles equal.
+// Every wave works on its own 32-key tiles (tiles wave, wave + 4*grid, ...)
+// and its own two LDS tile buffers, with wave-scope fences only -- no
+// workgroup barriers.  The tile loop is software-pipelined: while the MFMA
+// chain reads tile t from one buffer, each of its 16-byte read steps also
+// writes one piece of tile t+1 (held in registers) into the other buffer and
+// issues the load of the same piece of tile t+2, so a full tile of loads stays
+// in flight under the MFMAs and no separate copy phase remains.  On gfx950 a
+// wave's VALU instructions do not overlap its own f32 MFMAs (measured: each
+// adds its issue time to the chain), so the loop keeps VALU work to the
+// epilogue: integer-max ReLU, head weights, a permlane32 swap for the other
+// half's heads, and the ensemble.  Tiles are taken per sequence, so the
+// queries, weights and buffer resources stay fixed in the inner loop.  The
+// grid is one 4-wave workgroup per CU (fewer when the scan is short), which
+// keeps every wave's share of tiles equal.
 #include "lsa_internal.hpp"
 
 namespace lsa {
@@ -72,129 +81,171 @@ __device__ inline void unpack16<uint16_t>(const uint4& u, float* out) {
     out[7] = bf16_hi(u.w);
 }
 
+// max(x, 0) for finite x in one integer max: a set sign bit makes the pattern
+// a negative int32 (-0 becomes +0)
+__device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Buffer resource of one tile: base at the tile, records = bytes of the
+// sequence's valid keys from there on, so every read of the tile stays inside
+// the sequence and rows >= n_valid read as zero.  A sequence has
+// ceil(n_valid / 32) tiles, so a tile's first row is valid: tile_off < seq_bytes.
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char* seq, uint32_t seq_bytes, uint32_t tile_off) {
+    return make_rsrc(seq + tile_off, seq_bytes - tile_off);
+}
+
+__device__ inline void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int DK, typename KT>
 __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, const int gx) {
     using C = Cfg<DK, KT>;
     constexpr int kPerRead = 16 / (int)sizeof(KT);
-    __shared__ __attribute__((aligned(16))) char lds[kWaves][kTile * C::kLdsStride];
+    constexpr int kSteps = C::kReads;                     // 16-byte reads per lane per tile
+    static_assert(C::kReads == C::kLoads, "one tile load per read step");
+    static_assert(1024 % C::kRowBytes == 0, "a 64-lane load covers whole rows");
+    constexpr int kBuf = kTile * C::kLdsStride;
+    constexpr int kLoadStride = (1024 / C::kRowBytes) * C::kLdsStride;   // LDS bytes per 64-lane load
+    __shared__ __attribute__((aligned(16))) char lds[kWaves][2][kBuf];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps tile state in SGPRs
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps tile state in SGPRs
     const int col = lane & 31;      // key within the tile (B/D column); query row for A
     const int half = lane >> 5;     // which half of dk this lane feeds
-
     const int total = a.tile_start[a.batch];
     const int stride = gx * kWaves;
     int t = bx * kWaves + wave;
-    if (t >= total) return;
 
-    auto seq_of = [&](int tile) {
-        int b = 0;
-        while (tile >= a.tile_start[b + 1]) ++b;
-        return b;
-    };
     const char* kbase = static_cast<const char*>(a.keys);
-    auto load_tile = [&](int tile, uint4 (&dst)[C::kLoads]) {
-        const int b = seq_of(tile);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(kbase + (int64_t)b * a.n_keys * C::kRowBytes,
-                                                   (uint32_t)a.n_valid[b] * (uint32_t)C::kRowBytes);
-        const uint32_t base = (uint32_t)(tile - a.tile_start[b]) * (uint32_t)C::kTileBytes;
+    const __amdgpu_buffer_rsrc_t zero_r = make_rsrc(kbase, 0u);     // every read returns zero
+    // LDS byte offset of this lane's 16-byte piece of load i: woff + i * kLoadStride
+    const int woff = (lane * 16 / C::kRowBytes) * C::kLdsStride + (lane * 16) % C::kRowBytes;
+    const int roff = col * C::kLdsStride + half * C::kHalfBytes;
+    // byte offset of load i of a tile: vo[i / 4] + (i % 4) * 1024 (the constant goes to the
+    // instruction's offset field)
+    uint32_t vo[(kSteps + 3) / 4];
 #pragma unroll
-        for (int i = 0; i < C::kLoads; ++i) dst[i] = buffer_load16(r, base + (uint32_t)(i * 64 + lane) * 16u);
-    };
+    for (int k = 0; k < (kSteps + 3) / 4; ++k) vo[k] = (uint32_t)lane * 16u + (uint32_t)k * 4096u;
+    char* const my0 = lds[wave][0];
 
-    int cur_b = -1;
-    float qa[C::kHalf];
-    float wr[16];
-    char* my = lds[wave];
-    uint4 pre[C::kLoads];
-    load_tile(t, pre);
-
+    int b = 0;
     while (t < total) {
-        const int b = seq_of(t);
-        if (b != cur_b) {
-            cur_b = b;
-            // A operand: query row `col` (indexer col/8, head col%8), elements half*DK/2 + s
+        // one run of this wave's tiles that belong to sequence b
+        while (t >= a.tile_start[b + 1]) ++b;
+        const int lo = a.tile_start[b], hi = a.tile_start[b + 1];
+        const int nv = a.n_valid[b];
+        const char* const seq = kbase + (int64_t)b * a.n_keys * C::kRowBytes;
+        const uint32_t seq_bytes = (uint32_t)nv * (uint32_t)C::kRowBytes;
+        // scores of keys >= n_valid, and every store of lane half 1 (offset 2^31), are dropped
+        const __amdgpu_buffer_rsrc_t so = make_rsrc(a.scores + (int64_t)b * a.n_keys, (uint32_t)nv * 4u);
+
+        // prologue: tile t into LDS buffer 0, tile t + stride in flight in registers; the
+        // queries and weights load behind the first tile
+        uint4 pre[kSteps];
+        const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(seq, seq_bytes, (uint32_t)(t - lo) * (uint32_t)C::kTileBytes);
+#pragma unroll
+        for (int i = 0; i < kSteps; ++i) pre[i] = buffer_load16(r0, vo[i >> 2] + (uint32_t)(i & 3) * 1024u);
+        __builtin_amdgcn_sched_barrier(0);
+        // A operand: query row `col` (indexer col/8, head col%8), elements half*DK/2 + s
+        float qa[C::kHalf];
+        {
             const int g = col >> 3, hd = col & 7;
             const bool qv = g < a.n_idx && hd < a.heads;
             const float* qrow = a.q + (((int64_t)b * a.n_idx + (qv ? g : 0)) * a.heads + (qv ? hd : 0)) * DK + half * C::kHalf;
 #pragma unroll
-            for (int s = 0; s < C::kHalf; s += 4) {
-                f32x4 v = qv ? *reinterpret_cast<const f32x4*>(qrow + s) : f32x4{0.f, 0.f, 0.f, 0.f};
-                qa[s] = v[0];
-                qa[s + 1] = v[1];
-                qa[s + 2] = v[2];
-                qa[s + 3] = v[3];
-            }
-            // epilogue weights: accumulator r is query row 8*(r/4) + 4*half + r%4
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int gi = r >> 2, hi = 4 * half + (r & 3);
-                wr[r] = (gi < a.n_idx && hi < a.heads) ? a.w[((int64_t)b * a.n_idx + gi) * a.heads + hi] : 0.0f;
+            for (int e = 0; e < C::kHalf; e += 4) {
+                const f32x4 v = qv ? *reinterpret_cast<const f32x4*>(qrow + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+                qa[e] = v[0];
+                qa[e + 1] = v[1];
+                qa[e + 2] = v[2];
+                qa[e + 3] = v[3];
             }
         }
-        const int tile_in_seq = t - a.tile_start[b];
-
+        // epilogue weights: accumulator r is query row 8*(r/4) + 4*half + r%4
+        float wr[16];
 #pragma unroll
-        for (int i = 0; i < C::kLoads; ++i) {
-            const int off = (i * 64 + lane) * 16;
-            *reinterpret_cast<uint4*>(my + (off / C::kRowBytes) * C::kLdsStride + off % C::kRowBytes) = pre[i];
+        for (int r = 0; r < 16; ++r) {
+            const int gi = r >> 2, hi_ = 4 * half + (r & 3);
+            wr[r] = (gi < a.n_idx && hi_ < a.heads) ? a.w[((int64_t)b * a.n_idx + gi) * a.heads + hi_] : 0.0f;
         }
-        // the wave's LDS writes are visible to all its lanes past this point
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        const int t_next = t + stride;
-        if (t_next < total) load_tile(t_next, pre);
-
-        // 32 keys x 32 query rows, k = DK
-        f32x16 acc = {};
-        const char* myrow = my + col * C::kLdsStride + half * C::kHalfBytes;
+        __builtin_amdgcn_sched_barrier(0);
+        {
 #pragma unroll
-        for (int rd = 0; rd < C::kReads; ++rd) {
-            const uint4 u = *reinterpret_cast<const uint4*>(myrow + rd * 16);
-            float kb[kPerRead];
-            unpack16<KT>(u, kb);
+            for (int i = 0; i < kSteps; ++i) *reinterpret_cast<uint4*>(my0 + woff + i * kLoadStride) = pre[i];
+            const int tn = t + stride;
+            const __amdgpu_buffer_rsrc_t rn =
+                tn < hi ? tile_rsrc(seq, seq_bytes, (uint32_t)(tn - lo) * (uint32_t)C::kTileBytes) : zero_r;
 #pragma unroll
-            for (int e = 0; e < kPerRead; ++e)
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[rd * kPerRead + e], kb[e], acc, 0, 0, 0);
+            for (int i = 0; i < kSteps; ++i) pre[i] = buffer_load16(rn, vo[i >> 2] + (uint32_t)(i & 3) * 1024u);
         }
-        // all lanes' LDS reads of this tile are done before the next tile is written
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_sync();
 
-        // epilogue: per indexer, this lane's 4 heads; then the other half's 4 heads
-        float s[4];
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-            float v = 0.0f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) v += wr[4 * gi + c] * fmaxf(acc[4 * gi + c], 0.0f);
-            s[gi] = v;
-        }
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) s[gi] = (s[gi] + __shfl_xor(s[gi], 32, 64)) + 0.0f;
-        float e;
-        if (a.ensemble == LSA_ENSEMBLE_MAX) {
-            e = s[0];
-            for (int gi = 1; gi < a.n_idx; ++gi) e = fmaxf(e, s[gi]);
-        } else {
-            float sum = s[0];
-            for (int gi = 1; gi < a.n_idx; ++gi) sum += s[gi];
-            e = sum / (float)a.n_idx;
-        }
-        const int key = tile_in_seq * kTile + col;
-        if (half == 0 && key < a.n_valid[b]) a.scores[(int64_t)b * a.n_keys + key] = e + 0.0f;
+        int cur = 0;
+        for (; t < hi; t += stride) {
+            // LDS buffer `cur` holds tile t; `pre` holds tile t + stride (in flight).  Each
+            // MFMA step also moves one piece of `pre` into the other buffer and refills it
+            // with tile t + 2*stride, so loads stay in flight under the MFMA chain.
+            const int t2 = t + 2 * stride;
+            const __amdgpu_buffer_rsrc_t r2 =
+                t2 < hi ? tile_rsrc(seq, seq_bytes, (uint32_t)(t2 - lo) * (uint32_t)C::kTileBytes) : zero_r;
+            const char* rd = my0 + cur * kBuf + roff;
+            char* wrb = my0 + (cur ^ 1) * kBuf + woff;
 
-        t = t_next;
+            f32x16 acc = {};
+            uint4 u = *reinterpret_cast<const uint4*>(rd);
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                const uint4 un = s + 1 < kSteps ? *reinterpret_cast<const uint4*>(rd + (s + 1) * 16) : u;
+                *reinterpret_cast<uint4*>(wrb + s * kLoadStride) = pre[s];
+                pre[s] = buffer_load16(r2, vo[s >> 2] + (uint32_t)(s & 3) * 1024u);
+                float kb[kPerRead];
+                unpack16<KT>(u, kb);
+#pragma unroll
+                for (int e = 0; e < kPerRead; ++e)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[s * kPerRead + e], kb[e], acc, 0, 0, 0);
+                u = un;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the other buffer is complete and this one's reads are done
+            wave_sync();
+
+            // epilogue: per indexer, this lane's 4 heads; then the other half's 4 heads
+            float sv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                if (gi >= a.n_idx) break;   // uniform
+                float v = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v += wr[4 * gi + c] * relu(acc[4 * gi + c]);
+                // lanes 0..31 receive lane l+32's value in r[1]
+                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                sv[gi] = (v + __uint_as_float(r[1])) + 0.0f;
+            }
+            float e;
+            if (a.ensemble == LSA_ENSEMBLE_MAX) {
+                e = sv[0];
+                if (a.n_idx > 1) e = fmaxf(e, sv[1]);
+                if (a.n_idx > 2) e = fmaxf(e, sv[2]);
+                if (a.n_idx > 3) e = fmaxf(e, sv[3]);
+            } else {
+                float sum = sv[0];
+                if (a.n_idx > 1) sum += sv[1];
+                if (a.n_idx > 2) sum += sv[2];
+                if (a.n_idx > 3) sum += sv[3];
+                e = sum / (float)a.n_idx;
+            }
+            const uint32_t off = half ? 0x80000000u : (uint32_t)((t - lo) * kTile + col) * 4u;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e + 0.0f), so, off, 0, 0);
+            cur ^= 1;
+        }
     }
 }
 
 template <int DK, typename KT>
-__global__ __launch_bounds__(kThreads, 2) void fm_score_kernel(const ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fm_score_kernel(const ScoreArgs a) {
     fm_score_body<DK, KT>(a, blockIdx.x, gridDim.x);
 }
 

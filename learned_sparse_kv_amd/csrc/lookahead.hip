@@ -41,10 +41,17 @@ struct Split {
 // The copy wave of a score workgroup: copies the missed rows recorded in the
 // list rows wg, wg + n_wg, wg + 2 n_wg, ... of the flattened (layer, sequence,
 // row) space from the cold pool into their slots.  Its misses go to LDS in
-// rank order, then every lane copies 16-byte chunks of them with eight loads
-// in flight (loads unconditional on clamped indices, stores predicated, so
-// the batch stays in registers).  The wave has its own load counter, so its long
-// PCIe reads never hold up the score waves.
+// rank order, then every lane copies 16-byte chunks of them, kCopyInFlight
+// loads at a time (loads unconditional on clamped indices, stores predicated,
+// so the batch stays in registers).  The wave has its own load counter, so the
+// score waves never wait on its loads; on a pinned-host cold pool the PCIe
+// reads still slow down while the score streams keys from HBM (measured: the
+// fused launch takes about the score time plus the fetch time).
+#ifndef LSA_COPY_IN_FLIGHT
+#define LSA_COPY_IN_FLIGHT 4
+#endif
+constexpr int kCopyInFlight = LSA_COPY_IN_FLIGHT;
+
 struct CopyRow {
     int64_t from;   // byte offset in the layer's cold pool
     int64_t to;     // byte offset in the layer's KV buffer
@@ -91,34 +98,18 @@ __device__ inline void copy_wave(const StageArgs& ga, int phys_stride, int wg, i
             from = static_cast<const char*>(ga.L[r.layer].cold) + r.from + off;
             to = static_cast<char*>(ga.L[r.layer].kv) + r.to + off;
         };
-        for (int c0 = 0; c0 < chunks; c0 += 64 * 8) {
-            // eight chunks per lane in flight, held in named registers
-            const char *f0, *f1, *f2, *f3, *f4, *f5, *f6, *f7;
-            char *t0, *t1, *t2, *t3, *t4, *t5, *t6, *t7;
-            at(c0 + 0 * 64 + lane, f0, t0);
-            at(c0 + 1 * 64 + lane, f1, t1);
-            at(c0 + 2 * 64 + lane, f2, t2);
-            at(c0 + 3 * 64 + lane, f3, t3);
-            at(c0 + 4 * 64 + lane, f4, t4);
-            at(c0 + 5 * 64 + lane, f5, t5);
-            at(c0 + 6 * 64 + lane, f6, t6);
-            at(c0 + 7 * 64 + lane, f7, t7);
-            const uint4 v0 = *reinterpret_cast<const uint4*>(f0);
-            const uint4 v1 = *reinterpret_cast<const uint4*>(f1);
-            const uint4 v2 = *reinterpret_cast<const uint4*>(f2);
-            const uint4 v3 = *reinterpret_cast<const uint4*>(f3);
-            const uint4 v4 = *reinterpret_cast<const uint4*>(f4);
-            const uint4 v5 = *reinterpret_cast<const uint4*>(f5);
-            const uint4 v6 = *reinterpret_cast<const uint4*>(f6);
-            const uint4 v7 = *reinterpret_cast<const uint4*>(f7);
-            if (c0 + 0 * 64 + lane < chunks) *reinterpret_cast<uint4*>(t0) = v0;
-            if (c0 + 1 * 64 + lane < chunks) *reinterpret_cast<uint4*>(t1) = v1;
-            if (c0 + 2 * 64 + lane < chunks) *reinterpret_cast<uint4*>(t2) = v2;
-            if (c0 + 3 * 64 + lane < chunks) *reinterpret_cast<uint4*>(t3) = v3;
-            if (c0 + 4 * 64 + lane < chunks) *reinterpret_cast<uint4*>(t4) = v4;
-            if (c0 + 5 * 64 + lane < chunks) *reinterpret_cast<uint4*>(t5) = v5;
-            if (c0 + 6 * 64 + lane < chunks) *reinterpret_cast<uint4*>(t6) = v6;
-            if (c0 + 7 * 64 + lane < chunks) *reinterpret_cast<uint4*>(t7) = v7;
+        for (int c0 = 0; c0 < chunks; c0 += 64 * kCopyInFlight) {
+            // kCopyInFlight chunks per lane in flight
+            const char* f[kCopyInFlight];
+            char* to[kCopyInFlight];
+            uint4 v[kCopyInFlight];
+#pragma unroll
+            for (int u = 0; u < kCopyInFlight; ++u) at(c0 + u * 64 + lane, f[u], to[u]);
+#pragma unroll
+            for (int u = 0; u < kCopyInFlight; ++u) v[u] = *reinterpret_cast<const uint4*>(f[u]);
+#pragma unroll
+            for (int u = 0; u < kCopyInFlight; ++u)
+                if (c0 + u * 64 + lane < chunks) *reinterpret_cast<uint4*>(to[u]) = v[u];
         }
         // the next pass may reuse the list entries
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
