@@ -121,6 +121,7 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
 
     if (L.seg_cold && tid == 0)
         L.seg_cold[b] = (uint64_t)(static_cast<const char*>(L.cold) + b * L.cold_stride_b);
+    if (L.n_miss && tid == 0) L.n_miss[b] = 0;   // a swapping layer overwrites it below
     int32_t* src = L.defer_copy ? L.src + (int64_t)b * L.phys_stride : nullptr;
     if (src) {
         for (int r = tid; r < L.window; r += kNT) src[r] = -1;
@@ -192,6 +193,12 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
         s_mslot[miss_rank] = slot;
         lru[n_miss - 1 - miss_rank] = slot;
         if (src) src[L.window + tid] = l;
+        if (L.miss) {
+            uint64_t* e = L.miss + ((int64_t)b * L.phys_stride + miss_rank) * 2;
+            e[0] = (uint64_t)(static_cast<const char*>(L.cold) + b * L.cold_stride_b + (int64_t)l * L.row_bytes);
+            e[1] = (uint64_t)(static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes +
+                              (int64_t)(L.window + slot) * L.row_bytes);
+        }
     }
     if (hit) lru[n_miss + n_hit - 1 - hit_rank] = slot;
     if (l >= 0) phys[L.window + tid] = L.window + slot;
@@ -201,6 +208,7 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
         st[0] += (uint64_t)n_hit;
         st[1] += (uint64_t)n_miss;
         st[2] += (uint64_t)n_miss * (uint64_t)L.row_bytes;
+        if (L.n_miss) L.n_miss[b] = n_miss;
     }
     if (src) return;   // the attention reads the missed rows and fills their slots
     __syncthreads();

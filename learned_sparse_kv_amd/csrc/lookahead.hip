@@ -38,93 +38,89 @@ struct Split {
     int x2;        // second body's x extent (y = rest)
 };
 
-// The copy wave of a score workgroup: copies the missed rows recorded in the
-// list rows wg, wg + n_wg, wg + 2 n_wg, ... of the flattened (layer, sequence,
-// row) space from the cold pool into their slots.  Its misses go to LDS in
-// rank order, then every lane copies 16-byte chunks of them, kCopyInFlight
-// loads at a time (loads unconditional on clamped indices, stores predicated,
-// so the batch stays in registers).  The wave has its own load counter, so the
-// score waves never wait on its loads; on a pinned-host cold pool the PCIe
-// reads still slow down while the score streams keys from HBM (measured: the
-// fused launch takes about the score time plus the fetch time).
-#ifndef LSA_COPY_IN_FLIGHT
-#define LSA_COPY_IN_FLIGHT 4
-#endif
-constexpr int kCopyInFlight = LSA_COPY_IN_FLIGHT;
-
-struct CopyRow {
-    int64_t from;   // byte offset in the layer's cold pool
-    int64_t to;     // byte offset in the layer's KV buffer
-    int layer, row_bytes;
+// The missed rows a deferring stage listed for the step, as the copy wave reads
+// them: the lists and counts of every (layer, sequence) segment lie back to
+// back, segment s = layer * batch + b.
+struct CopyArgs {
+    const uint64_t* miss;     // [n_seg][phys_stride][2]: cold row address, slot row address
+    const int32_t* n_miss;    // [n_seg]
+    int32_t n_seg, phys_stride, row_bytes;
 };
 
-__device__ inline void copy_wave(const StageArgs& ga, int phys_stride, int wg, int n_wg, CopyRow* rows) {
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+
+// 16-byte chunks each copy lane has in flight per pass
+constexpr int kCopyInFlight = 8;
+
+// The copy wave of a score workgroup.  All missed rows of the step are split
+// into 16-byte chunks, numbered row by row in segment order, and lane `lane`
+// of copy wave `wg` (of n_wg) takes chunks wg*64 + lane + u*G for G = 64*n_wg:
+// every copy lane of the launch gets the same share, whatever the miss count of
+// its own rows, and one pass of kCopyInFlight loads per lane covers the step's
+// misses on the 1M-context workload, so all of its PCIe reads are in flight at
+// once.  A chunk finds its segment by binary search of the prefix of the miss
+// counts (in LDS).  Loads are unconditional on a clamped chunk index and stores
+// are predicated, so a pass stays in registers.  The wave has its own load
+// counter: the score waves never wait on its reads.
+__device__ inline void copy_wave(const CopyArgs& ca, const int wg, const int n_wg, int* s_pre) {
     const int lane = threadIdx.x & 63;
-    const int per_layer = ga.batch * phys_stride;
-    const int total = ga.n_layers * per_layer;
-    for (int k0 = 0; wg + k0 * n_wg < total; k0 += 64) {
-        const int i = wg + (k0 + lane) * n_wg;
-        bool miss = false;
-        CopyRow cr{0, 0, 0, 0};
-        if (i < total) {
-            const int layer = i / per_layer, b = (i / phys_stride) % ga.batch, r = i % phys_stride;
-            const StageLayer& L = ga.L[layer];
-            if (L.swap && r < L.n_rows[b]) {
-                const int sr = L.src[(int64_t)b * phys_stride + r];
-                const int ph = L.phys[(int64_t)b * phys_stride + r];
-                if (sr >= 0 && sr < L.cap && ph >= L.window && ph < L.window + L.S) {
-                    miss = true;
-                    cr.from = b * L.cold_stride_b + (int64_t)sr * L.row_bytes;
-                    cr.to = b * L.kv_stride_b_bytes + (int64_t)ph * L.row_bytes;
-                    cr.layer = layer;
-                    cr.row_bytes = L.row_bytes;
-                }
-            }
+    // exclusive prefix of the per-segment miss counts
+    int carry = 0;
+    for (int s0 = 0; s0 < ca.n_seg; s0 += 64) {
+        const int sg = s0 + lane;
+        const int c = sg < ca.n_seg ? ca.n_miss[sg] : 0;
+        int v = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(v, d, 64);
+            if (lane >= d) v += o;
         }
-        const uint64_t m = __ballot(miss);
-        const int n = __popcll(m);
-        if (n == 0) continue;
-        if (miss) rows[__popcll(m & ((1ull << lane) - 1ull))] = cr;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int cpr = rows[0].row_bytes / 16;   // one row size per step (every layer shares kv_dim)
-        const int chunks = n * cpr;
-        // source and destination of chunk c (clamped to the last chunk)
-        auto at = [&](int c, const char*& from, char*& to) {
-            const int cc = c < chunks ? c : chunks - 1;
-            const int j = cc / cpr, off = (cc - j * cpr) * 16;
-            const CopyRow& r = rows[j];
-            from = static_cast<const char*>(ga.L[r.layer].cold) + r.from + off;
-            to = static_cast<char*>(ga.L[r.layer].kv) + r.to + off;
-        };
-        for (int c0 = 0; c0 < chunks; c0 += 64 * kCopyInFlight) {
-            // kCopyInFlight chunks per lane in flight
-            const char* f[kCopyInFlight];
-            char* to[kCopyInFlight];
-            uint4 v[kCopyInFlight];
-#pragma unroll
-            for (int u = 0; u < kCopyInFlight; ++u) at(c0 + u * 64 + lane, f[u], to[u]);
-#pragma unroll
-            for (int u = 0; u < kCopyInFlight; ++u) v[u] = *reinterpret_cast<const uint4*>(f[u]);
-#pragma unroll
-            for (int u = 0; u < kCopyInFlight; ++u)
-                if (c0 + u * 64 + lane < chunks) *reinterpret_cast<uint4*>(to[u]) = v[u];
+        if (sg < ca.n_seg) s_pre[sg] = carry + v - c;
+        carry += __shfl(v, 63, 64);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const int shift = __builtin_ctz((unsigned)(ca.row_bytes / 16));   // row_bytes / 16 is a power of two
+    const int cpr_mask = (ca.row_bytes / 16) - 1;
+    const int chunks = carry << shift;
+    const int G = n_wg * 64;
+    for (int base = wg * 64; base < chunks; base += G * kCopyInFlight) {
+        uint64_t from[kCopyInFlight], to[kCopyInFlight];
+#pragma clang loop unroll(full)
+        for (int u = 0; u < kCopyInFlight; ++u) {
+            int c = base + lane + u * G;
+            c = c < chunks ? c : chunks - 1;
+            const int m = c >> shift;                    // missed row, in segment order
+            // last segment starting at or before m: a fixed-step binary search
+            int lo = 0;
+#pragma clang loop unroll(full)
+            for (int step = LSA_MAX_LAYERS * LSA_MAX_BATCH / 2; step > 0; step >>= 1)
+                if (lo + step < ca.n_seg && s_pre[lo + step] <= m) lo += step;
+            const uint64_t* e = ca.miss + ((int64_t)lo * ca.phys_stride + (m - s_pre[lo])) * 2;
+            const uint64_t off = (uint64_t)(c & cpr_mask) * 16u;
+            from[u] = e[0] + off;
+            to[u] = e[1] + off;
         }
-        // the next pass may reuse the list entries
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // global (not generic) accesses: their completion counts in order, so all
+        // loads of the pass are issued before the first wait
+        u32x4 v[kCopyInFlight];
+#pragma clang loop unroll(full)
+        for (int u = 0; u < kCopyInFlight; ++u) v[u] = *reinterpret_cast<const global_u32x4*>(from[u]);
+#pragma clang loop unroll(full)
+        for (int u = 0; u < kCopyInFlight; ++u)
+            if (base + lane + u * G < chunks) *reinterpret_cast<global_u32x4*>(to[u]) = v[u];
     }
 }
 
 // Workgroup = 4 score waves (fm_score) + 1 copy wave.
 template <int DK, typename KT>
-__global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, const StageArgs ga, const int phys_stride) {
-    __shared__ CopyRow s_rows[64];
+__global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, const CopyArgs ca) {
+    __shared__ int s_pre[LSA_MAX_LAYERS * LSA_MAX_BATCH];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave == 4) {
-        copy_wave(ga, phys_stride, blockIdx.x, gridDim.x, s_rows);
+        copy_wave(ca, blockIdx.x, gridDim.x, s_pre);
         return;
     }
     score_k::fm_score_body<DK, KT>(sa, blockIdx.x, gridDim.x);
@@ -153,12 +149,12 @@ __global__ __launch_bounds__(256) void la_combine_collect(const AttendArgs aa, c
 }
 
 template <int DK, typename KT>
-hipError_t launch_a(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int n_cu, hipStream_t s) {
+hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, int n_cu, hipStream_t s) {
     const int total = sa.tile_start[sa.batch];
     int grid = (total + score_k::kWaves - 1) / score_k::kWaves;
     if (grid > n_cu) grid = n_cu;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((la_score_copy<DK, KT>), dim3(grid), dim3(320), 0, s, sa, ga, phys_stride);
+    hipLaunchKernelGGL((la_score_copy<DK, KT>), dim3(grid), dim3(320), 0, s, sa, ca);
     return hipGetLastError();
 }
 
@@ -198,14 +194,27 @@ hipError_t launch_c(const AttendArgs& aa, const SelectArgs& se, hipStream_t s) {
 
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
                                  int n_cu, hipStream_t s) {
+    // the copy reads the stage's miss lists through one base pointer: they must
+    // lie back to back over (layer, sequence), with one row size
+    const StageLayer& L0 = ga.L[0];
+    if (!L0.miss || !L0.n_miss || ga.n_layers < 1 || ga.batch < 1) return hipErrorInvalidValue;
+    for (int l = 0; l < ga.n_layers; ++l) {
+        const StageLayer& L = ga.L[l];
+        if (L.miss != L0.miss + (size_t)l * ga.batch * phys_stride * 2 || L.n_miss != L0.n_miss + (size_t)l * ga.batch ||
+            L.row_bytes != L0.row_bytes || L.phys_stride != phys_stride)
+            return hipErrorInvalidValue;
+    }
+    const int cpr = L0.row_bytes / 16;
+    if (L0.row_bytes % 16 != 0 || cpr < 1 || (cpr & (cpr - 1)) != 0) return hipErrorInvalidValue;
+    const CopyArgs ca{L0.miss, L0.n_miss, ga.n_layers * ga.batch, phys_stride, L0.row_bytes};
     if (key_dtype == LSA_F32) {
-        if (dk == 32) return launch_a<32, float>(sa, ga, phys_stride, n_cu, s);
-        if (dk == 64) return launch_a<64, float>(sa, ga, phys_stride, n_cu, s);
-        if (dk == 128) return launch_a<128, float>(sa, ga, phys_stride, n_cu, s);
+        if (dk == 32) return launch_a<32, float>(sa, ca, n_cu, s);
+        if (dk == 64) return launch_a<64, float>(sa, ca, n_cu, s);
+        if (dk == 128) return launch_a<128, float>(sa, ca, n_cu, s);
     } else if (key_dtype == LSA_BF16) {
-        if (dk == 32) return launch_a<32, uint16_t>(sa, ga, phys_stride, n_cu, s);
-        if (dk == 64) return launch_a<64, uint16_t>(sa, ga, phys_stride, n_cu, s);
-        if (dk == 128) return launch_a<128, uint16_t>(sa, ga, phys_stride, n_cu, s);
+        if (dk == 32) return launch_a<32, uint16_t>(sa, ca, n_cu, s);
+        if (dk == 64) return launch_a<64, uint16_t>(sa, ca, n_cu, s);
+        if (dk == 128) return launch_a<128, uint16_t>(sa, ca, n_cu, s);
     }
     return hipErrorInvalidValue;
 }

@@ -753,6 +753,8 @@ struct StepPlan {
     int32_t* phys = nullptr;     // [n_buf][L][B][phys_stride]
     int32_t* n_rows = nullptr;   // [n_buf][L][B]
     int32_t* srcs = nullptr;     // [n_buf][L][B][phys_stride]
+    uint64_t* miss = nullptr;    // [n_buf][L][B][phys_stride][2]
+    int32_t* n_miss = nullptr;   // [n_buf][L][B]
 };
 
 lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* P) {
@@ -797,7 +799,7 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
         if (st != LSA_OK) return st;
     }
     const int L = d->n_layers;
-    // workspace: select candidates | attend partials | phys | n_rows | src
+    // workspace: select candidates | attend partials | phys | n_rows | src | miss lists | miss counts
     const size_t off_att = align_up(sel_need, 256);
     const size_t att_bytes = attend_workspace_bytes(L, B, D, phys_stride);
     const size_t off_phys = off_att + align_up(att_bytes, 256);
@@ -806,13 +808,19 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
     const size_t nrows_bytes = d->n_rows ? 0 : align_up((size_t)n_buf * L * B * 4, 256);
     const size_t off_src = off_nrows + nrows_bytes;
     const size_t src_bytes = align_up((size_t)n_buf * L * B * phys_stride * 4, 256);
-    st = ws_ensure(ctx, off_src + src_bytes);
+    const size_t off_miss = off_src + src_bytes;
+    const size_t miss_bytes = align_up((size_t)n_buf * L * B * phys_stride * 16, 256);
+    const size_t off_nmiss = off_miss + miss_bytes;
+    const size_t nmiss_bytes = align_up((size_t)n_buf * L * B * 4, 256);
+    st = ws_ensure(ctx, off_nmiss + nmiss_bytes);
     if (st != LSA_OK) return st;
     char* ws = static_cast<char*>(ctx->ws);
     select_bind(&P->se, ctx->zero, ws);
     P->phys = d->phys ? d->phys : reinterpret_cast<int32_t*>(ws + off_phys);
     P->n_rows = d->n_rows ? d->n_rows : reinterpret_cast<int32_t*>(ws + off_nrows);
     P->srcs = reinterpret_cast<int32_t*>(ws + off_src);
+    P->miss = reinterpret_cast<uint64_t*>(ws + off_miss);
+    P->n_miss = reinterpret_cast<int32_t*>(ws + off_nmiss);
     P->B = B;
     P->D = D;
     P->W = W;
@@ -841,6 +849,8 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
         P->ga.L[l] = stage_layer(p, d->sel, d->count, d->k, d->src_ratio, ph, phys_stride, nr);
         P->ga.L[l].defer_copy = 1;
         P->ga.L[l].src = sr;
+        P->ga.L[l].miss = P->miss + (size_t)l * B * phys_stride * 2;
+        P->ga.L[l].n_miss = P->n_miss + (size_t)l * B;
         P->aa.L[l] = AttendLayer{d->q_attn + (size_t)l * B * d->hq * D, p->d.kv_buf, ph, nr,
                                  d->out + (size_t)l * B * d->hq * D, p->d.kv_stride_b, p->rows_per_seq, phys_stride,
                                  nullptr, p->d.kv_buf, p->cold_dev, p->cold_stride_b, p->cap};
@@ -857,6 +867,8 @@ void plan_use_buffer(StepPlan* P, int buf) {
         P->ga.L[l].phys = ph;
         P->ga.L[l].n_rows = nr;
         P->ga.L[l].src = P->srcs + (buf * per_buf + (size_t)l * P->B) * P->phys_stride;
+        P->ga.L[l].miss = P->miss + (buf * per_buf + (size_t)l * P->B) * P->phys_stride * 2;
+        P->ga.L[l].n_miss = P->n_miss + buf * per_buf + (size_t)l * P->B;
         P->aa.L[l].phys = ph;
         P->aa.L[l].n_rows = nr;
     }

@@ -163,6 +163,11 @@ struct StageLayer {
     // optional: seg_cold[b] = address of sequence b's cold rows (written by the
     // stage, so a later kernel can find a missed row without the pool)
     uint64_t* seg_cold;         // [batch]
+    // optional: the misses of a deferring stage as a compact list,
+    // miss[b][rank] = {address of the cold row, address of its slot row}, and
+    // n_miss[b] = their number (0 for a resident layer)
+    uint64_t* miss;             // [batch][phys_stride][2]
+    int32_t* n_miss;            // [batch]
 };
 struct StageArgs {
     int32_t n_layers, batch;
@@ -206,7 +211,9 @@ constexpr int kAttendRows = 32;
 constexpr int kAttendMaxRows = 5120;    // longest row list (window + entries) of one attention
 size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows);
 hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid = nullptr);
-// fused launches of the lookahead schedule
+// fused launches of the lookahead schedule.  launch_la_fetch_score scores and,
+// in the same launch, copies the rows in the miss lists of `ga` (a deferring
+// stage's output, laid out back to back over (layer, sequence)) into their slots.
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
                                  int n_cu, hipStream_t s);
 hipError_t launch_la_attend_hist(const AttendArgs& aa, const SelectArgs& se, hipStream_t s);
