@@ -82,7 +82,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=12)
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--graph", type=int, default=1, help="time HIP-graph replays (1) or eager launches (0)")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="time eager launches (0, the default: faster here, the host keeps ahead of the GPU) "
+                         "or HIP-graph replays, one graph per step (1)")
     ap.add_argument("--schedule", choices=["lookahead", "sync"], default="lookahead",
                     help="lookahead: each step's row copy and attention share launches with the next step's "
                          "score and selection; sync: score, select, stage and attend one after another")
@@ -119,9 +121,10 @@ def main():
     dw.make_steps(Wm + K + 2)
     log(f"set-up {time.time() - t0:.1f}s")
 
-    def timed_region(schedule):
-        """Warm up, capture K steps of the schedule as HIP graphs (one per step), and time
-        their replays; the pools start empty.  Returns (ms per step, LRU stats before, after)."""
+    def timed_region(schedule, use_graph):
+        """Warm up, then time K steps of the schedule, launched eagerly or as HIP-graph
+        replays (one graph per step); the pools start empty.  Returns (ms per step, LRU
+        stats before, after)."""
         dw.reset_pools()
         la = schedule == "lookahead"
         if la:
@@ -130,7 +133,6 @@ def main():
         for t in range(Wm):
             eager(t)
         torch.cuda.synchronize()
-        use_graph = args.graph != 0
         if use_graph:
             if la:
                 dw.capture_lookahead(range(Wm, Wm + K))
@@ -150,17 +152,20 @@ def main():
         t_enq = time.perf_counter()
         torch.cuda.synchronize()
         t_end = time.perf_counter()
-        log(f"{schedule}: host enqueue {(t_enq - t_start) * 1e6 / K:.1f} us/step, "
-            f"wall {(t_end - t_start) * 1e6 / K:.1f} us/step")
+        log(f"{schedule} ({'graph' if use_graph else 'eager'}): host enqueue {(t_enq - t_start) * 1e6 / K:.1f} "
+            f"us/step, wall {(t_end - t_start) * 1e6 / K:.1f} us/step")
         s1 = [p.stats() for p in dw.pools]
         dw.graphs = {}
         return (t_end - t_start) * 1e3 / K, s0, s1
 
-    # ---- timed regions: K steps of each schedule (HIP-graph replays by default);
+    # ---- timed regions: K steps of each schedule, launched as --graph says; the
+    # chosen schedule is also timed with the other launch mode, for context.
     # `value` is the chosen schedule's
     other = "sync" if args.schedule == "lookahead" else "lookahead"
-    other_ms, _, _ = timed_region(other)
-    ms_per_step, stats0, stats1 = timed_region(args.schedule)
+    use_graph = args.graph != 0
+    other_ms, _, _ = timed_region(other, use_graph)
+    alt_ms, _, _ = timed_region(args.schedule, not use_graph)
+    ms_per_step, stats0, stats1 = timed_region(args.schedule, use_graph)
     value = 1e3 / ms_per_step
 
     # ---- kernel-timed region: the same K steps of the synchronous schedule
@@ -299,8 +304,10 @@ def main():
                    "window": wl.window, "kv_dim": wl.kv_dim, "attn_heads": wl.hq,
                    "step": "score+select+stage+fetch+attend",
                    "schedule": args.schedule,
-                   "launch": "hip graph per step" if args.graph else "eager"},
+                   "launch": "hip graph per step" if use_graph else "eager"},
         other + "_schedule": {"value": round(1e3 / other_ms, 2), "ms_per_step": round(other_ms, 5)},
+        ("graph" if not use_graph else "eager") + "_launch": {"value": round(1e3 / alt_ms, 2),
+                                                             "ms_per_step": round(alt_ms, 5)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_us_events": {k: round(avg[k] * 1e3, 2) for k in KERNELS},
