@@ -49,16 +49,18 @@ struct CopyArgs {
 
 typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 
-// 16-byte chunks each copy lane has in flight per pass
-constexpr int kCopyInFlight = 8;
+// 16-byte chunks each copy lane has in flight per pass.  One is fastest on the
+// 1M-context workload (72.4 us per step against 73.7 / 75.7 / 76.7 us for 2 / 4 /
+// 8): with 256 copy waves it keeps 256 KB of PCIe reads outstanding, which the
+// link drains at its full rate, while deeper queues sit in the memory path in
+// front of the score waves' key loads and slow both.
+constexpr int kCopyInFlight = 1;
 
 // The copy wave of a score workgroup.  All missed rows of the step are split
 // into 16-byte chunks, numbered row by row in segment order, and lane `lane`
 // of copy wave `wg` (of n_wg) takes chunks wg*64 + lane + u*G for G = 64*n_wg:
 // every copy lane of the launch gets the same share, whatever the miss count of
-// its own rows, and one pass of kCopyInFlight loads per lane covers the step's
-// misses on the 1M-context workload, so all of its PCIe reads are in flight at
-// once.  A chunk finds its segment by binary search of the prefix of the miss
+// its own rows, so the PCIe reads stay spread evenly over the launch.  A chunk finds its segment by binary search of the prefix of the miss
 // counts (in LDS).  Loads are unconditional on a clamped chunk index and stores
 // are predicated, so a pass stays in registers.  The wave has its own load
 // counter: the score waves never wait on its reads.
