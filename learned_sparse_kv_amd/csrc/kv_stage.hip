@@ -85,25 +85,59 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
 
     __shared__ int s_scan[kNT / 64 + 1];
     __shared__ int s_sel[kNT];
+    __shared__ int s_slot[kNT];     // slot of s_sel[i] before this step (-1: none)
+    __shared__ uint8_t s_rdy[kNT];  // ready flag of s_sel[i]
     __shared__ int s_victim[kNT];
     __shared__ int s_order[kMaxSlots];
+    __shared__ int s_logical[kMaxSlots];   // logical_of before this step
     __shared__ uint8_t s_hit[kMaxSlots];
     __shared__ int s_mlog[kNT];     // missed entries and their slots, by miss rank
     __shared__ int s_mslot[kNT];
 
-    // 1. source selection -> this layer's ascending unique chunk list
-    int n_src = L.count[b];
-    n_src = n_src < 0 ? 0 : (n_src > L.sel_stride ? L.sel_stride : n_src);
+    // Loads come in two dependent rounds: the selection together with the LRU
+    // state (order, slot occupants, used count), then the slot-table entry and
+    // ready flag of each source entry's chunk.  The tables are not written
+    // before they are read below.
+    const bool sw = L.swap != 0;
+    int32_t* slot_of = L.slot_of + (int64_t)b * L.cap;
+    int32_t* logical_of = L.logical_of + (int64_t)b * L.S;
+    int32_t* lru = L.lru + (int64_t)b * L.S;
+    const int S = L.S;
     const int32_t* sel = L.sel + (int64_t)b * L.sel_stride;
+    const int n_src_raw = L.count[b];
+    const int sv = tid < L.sel_stride ? sel[tid] : 0;
+    const int sp = (tid >= 1 && tid <= L.sel_stride) ? sel[tid - 1] : 0;
+    int n_used = 0;
+    if (sw) {
+        n_used = L.meta[b * 4 + 0];
+        for (int i = tid; i < S; i += kNT) {
+            s_order[i] = lru[i];
+            s_logical[i] = logical_of[i];
+            s_hit[i] = 0;
+        }
+    }
+
+    // 1. source selection -> this layer's ascending unique chunk list
+    const int n_src = n_src_raw < 0 ? 0 : (n_src_raw > L.sel_stride ? L.sel_stride : n_src_raw);
     bool keep = false;
     int m = -1;
     if (tid < n_src) {
-        m = (int)((int64_t)sel[tid] * L.src_ratio / L.ratio);
-        keep = tid == 0 || m != (int)((int64_t)sel[tid - 1] * L.src_ratio / L.ratio);
+        m = (int)((int64_t)sv * L.src_ratio / L.ratio);
+        keep = tid == 0 || m != (int)((int64_t)sp * L.src_ratio / L.ratio);
+    }
+    int my_slot = -1;
+    uint8_t my_rdy = 1;
+    if (keep && m >= 0 && m < L.cap) {
+        my_rdy = L.ready[(int64_t)b * L.cap + m];
+        if (sw) my_slot = slot_of[m];
     }
     int n_l;
     const int pos = block_excl_scan<kNT>(keep ? 1 : 0, s_scan, &n_l);
-    if (keep) s_sel[pos] = m;
+    if (keep) {
+        s_sel[pos] = m;
+        s_slot[pos] = my_slot;
+        s_rdy[pos] = my_rdy;
+    }
     __syncthreads();
 
     int32_t* phys = L.phys + (int64_t)b * L.phys_stride;
@@ -117,7 +151,7 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
         phys[L.window + tid] = 0;
         l = -1;
     }
-    if (l >= 0 && !L.ready[(int64_t)b * L.cap + l]) atomicOr(&L.meta[b * 4 + 1], 1);
+    if (l >= 0 && !s_rdy[tid]) atomicOr(&L.meta[b * 4 + 1], 1);
 
     if (L.seg_cold && tid == 0)
         L.seg_cold[b] = (uint64_t)(static_cast<const char*>(L.cold) + b * L.cold_stride_b);
@@ -127,23 +161,13 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
         for (int r = tid; r < L.window; r += kNT) src[r] = -1;
         if (tid < n_l) src[L.window + tid] = -1;
     }
-    if (!L.swap) {
+    if (!sw) {
         if (l >= 0) phys[L.window + tid] = L.window + l;
         return;
     }
 
-    int32_t* slot_of = L.slot_of + (int64_t)b * L.cap;
-    int32_t* logical_of = L.logical_of + (int64_t)b * L.S;
-    int32_t* lru = L.lru + (int64_t)b * L.S;
-    const int S = L.S;
-    const int n_used = L.meta[b * 4 + 0];
-
-    for (int i = tid; i < S; i += kNT) s_hit[i] = 0;
-    for (int i = tid; i < n_used; i += kNT) s_order[i] = lru[i];
-    __syncthreads();
-
     // 2. hits and misses, ranked in ascending chunk order
-    int slot = l >= 0 ? slot_of[l] : -1;
+    int slot = l >= 0 ? s_slot[tid] : -1;
     const bool hit = slot >= 0;
     const bool miss = l >= 0 && !hit;
     if (hit) s_hit[slot] = 1;
@@ -183,7 +207,7 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
     // 4. slots for the misses; the evicted chunks leave the table
     if (miss) slot = miss_rank < free_slots ? n_used + miss_rank : s_victim[miss_rank - free_slots];
     int old = -1;
-    if (tid < n_evict) old = logical_of[s_victim[tid]];
+    if (tid < n_evict) old = s_logical[s_victim[tid]];
     __syncthreads();
     if (old >= 0) slot_of[old] = -1;
     if (miss) {
