@@ -23,8 +23,8 @@
 //   block finds the boundary bucket b* holding the K-th largest key from that
 //   histogram and keeps, in index order (block scan, no atomics), its entries
 //   in buckets >= b*; (3) one workgroup per segment gathers the kept entries in
-//   block order -- which is global index order -- resolves b* with radix
-//   passes over the 21 key bits below the bucket, and compacts {above b*} +
+//   block order -- which is global index order -- resolves b* with two radix
+//   passes (11 + 10 bits) over the 21 key bits below the bucket, and places {above b*} +
 //   {candidates > T} + {the first candidates equal to T}: ties fall to the
 //   lowest index because the list is in index order, and the output is
 //   already ascending.  If more than 8192 entries are kept, step (3) falls back
@@ -374,15 +374,47 @@ __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid,
     }
 }
 
+// Over hist[0, NB) taken from the top bin down: the bin holding the rem-th
+// largest entry (1 <= rem <= the histogram's total); *bin = it, *above =
+// entries in the bins above it.  Thread t of the kNT owns bins NB-1-PER*t-i.
+template <int NB>
+__device__ void find_bin(const uint32_t* hist, int rem, int* scan, int* out, int* bin, int* above) {
+    constexpr int PER = NB / kNT;
+    static_assert(PER >= 1 && NB % kNT == 0, "bins per thread");
+    const int t = threadIdx.x;
+    int c[PER];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        c[i] = (int)hist[NB - 1 - PER * t - i];
+        local += c[i];
+    }
+    int tot;
+    int run = block_excl_scan<kNT>(local, scan, &tot);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (run < rem && run + c[i] >= rem) {
+            out[0] = NB - 1 - PER * t - i;
+            out[1] = run;
+        }
+        run += c[i];
+    }
+    __syncthreads();
+    *bin = out[0];
+    *above = out[1];
+    __syncthreads();
+}
+
 // One workgroup per segment: gathers the blocks' kept entries (global index
-// order), resolves the boundary bucket with radix passes over the 21 key bits
-// below it, and writes the chosen indices (already ascending).
+// order), resolves the boundary bucket with two radix passes over the 21 key
+// bits below it, and writes the chosen indices (already ascending).
 __global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
     __shared__ KthShared sh;
     __shared__ int s_b[3];
     __shared__ int32_t s_idx[kSelKeepCap];
     __shared__ uint32_t s_key[kSelKeepCap];
     __shared__ int s_start[kMaxBlocks + 1];
+    __shared__ uint32_t s_h2[2048];
     const int tid = threadIdx.x, seg = blockIdx.x;
     uint32_t* g = a.hist + (int64_t)seg * kSelBins;
     find_boundary<kNT>(g, a.k, sh.scan, s_b);
@@ -425,50 +457,63 @@ __global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
             s_key[p] = a.blk_key[src];
         }
         __syncthreads();
-        // radix passes over bits 20..0 of the candidates' keys (bucket b* fixes the rest)
+        // two radix passes over bits 20..0 of the candidates' keys (bucket b* fixes
+        // the rest): bits 20..10, then bits 9..0 of the candidates in the bin found
         const int need = K - above;
-        uint32_t prefix = (uint32_t)bstar << kSelShift, mask = ~((1u << kSelShift) - 1u);
-        int rem = need;
-        const int shifts[3] = {13, 5, 0};
-        const int widths[3] = {8, 8, 5};
-#pragma unroll 1
-        for (int pass = 0; pass < 3; ++pass) {
-            const int shift = shifts[pass];
-            const uint32_t dmask = (1u << widths[pass]) - 1u;
-            if (tid < 256) sh.hist[tid] = 0u;
-            __syncthreads();
-            for (int p0 = 0; p0 < n_keep; p0 += kNT) {
-                const int p = p0 + tid;
-                const bool act = p < n_keep && s_idx[p] < 0 && (s_key[p] & mask) == prefix;
-                hist_add(sh.hist, act, p < n_keep ? (s_key[p] >> shift) & dmask : 0u);
-            }
-            __syncthreads();
-            find_digit(sh.hist, rem, sh);
-            prefix |= sh.digit << shift;
-            mask |= dmask << shift;
-            rem -= sh.above;
-            __syncthreads();
-        }
-        const uint32_t T = prefix;
-        const int need_eq = rem;
-        // index-ordered compaction: all entries above b*, candidates > T, and
-        // the first need_eq candidates equal to T
-        int run_eq = 0, run_out = 0;
+        for (int i = tid; i < 2048; i += kNT) s_h2[i] = 0u;
+        __syncthreads();
         for (int p0 = 0; p0 < n_keep; p0 += kNT) {
             const int p = p0 + tid;
-            const bool in = p < n_keep;
-            const int32_t raw = in ? s_idx[p] : 0;
-            const uint32_t k2 = in ? s_key[p] : 0u;
-            const bool cand = in && raw < 0;
-            const bool eq = cand && k2 == T;
-            int tot_eq;
-            const int r = run_eq + block_excl_scan<kNT>(eq ? 1 : 0, sh.scan, &tot_eq);
-            const bool take = in && (!cand || k2 > T || (eq && r < need_eq));
-            int tot_take;
-            const int pos = run_out + block_excl_scan<kNT>(take ? 1 : 0, sh.scan, &tot_take);
-            if (take && pos < a.stride) out_sel[pos] = raw & 0x7FFFFFFF;
-            run_eq += tot_eq;
-            run_out += tot_take;
+            const bool act = p < n_keep && s_idx[p] < 0;
+            hist_add(s_h2, act, p < n_keep ? (s_key[p] >> 10) & 2047u : 0u);
+        }
+        __syncthreads();
+        int bin, bin_above;
+        find_bin<2048>(s_h2, need, sh.scan, s_b, &bin, &bin_above);
+        const uint32_t d1 = (uint32_t)bin;
+        int rem = need - bin_above;
+        for (int i = tid; i < 1024; i += kNT) s_h2[i] = 0u;
+        __syncthreads();
+        for (int p0 = 0; p0 < n_keep; p0 += kNT) {
+            const int p = p0 + tid;
+            const bool act = p < n_keep && s_idx[p] < 0 && ((s_key[p] >> 10) & 2047u) == d1;
+            hist_add(s_h2, act, p < n_keep ? s_key[p] & 1023u : 0u);
+        }
+        __syncthreads();
+        find_bin<1024>(s_h2, rem, sh.scan, s_b, &bin, &bin_above);
+        const uint32_t T = ((uint32_t)bstar << kSelShift) | (d1 << 10) | (uint32_t)bin;
+        const int need_eq = rem - bin_above;
+        // index-ordered placement with one scan: thread t takes entries [t*E2, t*E2 + E2);
+        // an entry above T (every entry above b*, and candidates > T) goes to
+        // (entries above T before it) + min(candidates equal to T before it, need_eq),
+        // and the first need_eq candidates equal to T fill in between
+        const int E2 = (n_keep + kNT - 1) / kNT;   // <= kSelKeepCap / kNT
+        const int q0 = tid * E2;
+        int c_gt = 0, c_eq = 0;
+        for (int e = 0; e < E2; ++e) {
+            const int p = q0 + e;
+            if (p >= n_keep) break;
+            const int32_t raw = s_idx[p];
+            const uint32_t k2 = s_key[p];
+            if (raw >= 0 || k2 > T) ++c_gt;
+            else if (k2 == T) ++c_eq;
+        }
+        int tot;
+        const int packed = block_excl_scan<kNT>(c_gt | (c_eq << 16), sh.scan, &tot);
+        int n_gt = packed & 0xFFFF, n_eq = packed >> 16;
+        for (int e = 0; e < E2; ++e) {
+            const int p = q0 + e;
+            if (p >= n_keep) break;
+            const int32_t raw = s_idx[p];
+            const uint32_t k2 = s_key[p];
+            if (raw >= 0 || k2 > T) {
+                const int pos = n_gt + (n_eq < need_eq ? n_eq : need_eq);
+                if (pos < a.stride) out_sel[pos] = raw & 0x7FFFFFFF;
+                ++n_gt;
+            } else if (k2 == T) {
+                if (n_eq < need_eq && n_gt + n_eq < a.stride) out_sel[n_gt + n_eq] = raw & 0x7FFFFFFF;
+                ++n_eq;
+            }
         }
     } else if (K > 0) {
         stream_select(a, a.scores + (int64_t)seg * a.n_keys, seg_valid(a, seg), K, sh, out_sel);
