@@ -318,6 +318,7 @@ __global__ __launch_bounds__(kBlkThreads) void sel_collect_kernel(const SelectAr
 // Exact selection straight from the scores by one workgroup: four radix passes
 // over the whole segment, then an index-ordered compaction.  Used when the
 // boundary bucket overflows the candidate list.
+template <int NT>
 __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid, int K, KthShared& sh,
                               int32_t* out_sel) {
     const int tid = threadIdx.x;
@@ -328,7 +329,7 @@ __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid,
         const int shift = 24 - 8 * pass;
         if (tid < 256) sh.hist[tid] = 0u;
         __syncthreads();
-        for (int64_t c = 0; c < n_valid; c += kNT) {
+        for (int64_t c = 0; c < n_valid; c += NT) {
             uint32_t key;
             const bool v = entry(a, sc, c + tid, n_valid, &key);
             hist_add(sh.hist, v && (key & mask) == prefix, (key >> shift) & 255u);
@@ -344,7 +345,7 @@ __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid,
     const int need_eq = rem;
     constexpr int E = 8;
     int run_eq = 0, run_out = 0;
-    for (int64_t c = 0; c < n_valid; c += (int64_t)kNT * E) {
+    for (int64_t c = 0; c < n_valid; c += (int64_t)NT * E) {
         uint32_t key[E];
         bool v[E];
         int c_eq = 0;
@@ -354,7 +355,7 @@ __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid,
             c_eq += (v[e] && key[e] == T) ? 1 : 0;
         }
         int tot_eq;
-        int r = run_eq + block_excl_scan<kNT>(c_eq, sh.scan, &tot_eq);
+        int r = run_eq + block_excl_scan<NT>(c_eq, sh.scan, &tot_eq);
         bool take[E];
         int c_take = 0;
 #pragma unroll
@@ -365,7 +366,7 @@ __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid,
             c_take += take[e] ? 1 : 0;
         }
         int tot_take;
-        int pos = run_out + block_excl_scan<kNT>(c_take, sh.scan, &tot_take);
+        int pos = run_out + block_excl_scan<NT>(c_take, sh.scan, &tot_take);
 #pragma unroll
         for (int e = 0; e < E; ++e)
             if (take[e] && pos < a.stride) out_sel[pos++] = (int32_t)(c + (int64_t)tid * E + e);
@@ -376,11 +377,11 @@ __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid,
 
 // Over hist[0, NB) taken from the top bin down: the bin holding the rem-th
 // largest entry (1 <= rem <= the histogram's total); *bin = it, *above =
-// entries in the bins above it.  Thread t of the kNT owns bins NB-1-PER*t-i.
-template <int NB>
+// entries in the bins above it.  Thread t of the NT owns bins NB-1-PER*t-i.
+template <int NB, int NT>
 __device__ void find_bin(const uint32_t* hist, int rem, int* scan, int* out, int* bin, int* above) {
-    constexpr int PER = NB / kNT;
-    static_assert(PER >= 1 && NB % kNT == 0, "bins per thread");
+    constexpr int PER = NB / NT;
+    static_assert(PER >= 1 && NB % NT == 0, "bins per thread");
     const int t = threadIdx.x;
     int c[PER];
     int local = 0;
@@ -390,7 +391,7 @@ __device__ void find_bin(const uint32_t* hist, int rem, int* scan, int* out, int
         local += c[i];
     }
     int tot;
-    int run = block_excl_scan<kNT>(local, scan, &tot);
+    int run = block_excl_scan<NT>(local, scan, &tot);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         if (run < rem && run + c[i] >= rem) {
@@ -405,37 +406,41 @@ __device__ void find_bin(const uint32_t* hist, int rem, int* scan, int* out, int
     __syncthreads();
 }
 
-// One workgroup per segment: gathers the blocks' kept entries (global index
+// One workgroup of NT threads per segment: gathers the blocks' kept entries (global index
 // order), resolves the boundary bucket with two radix passes over the 21 key
 // bits below it, and writes the chosen indices (already ascending).
-__global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
+template <int NT, int MAXB = kMaxBlocks>
+__device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int seg) {
     __shared__ KthShared sh;
     __shared__ int s_b[3];
     __shared__ int32_t s_idx[kSelKeepCap];
     __shared__ uint32_t s_key[kSelKeepCap];
-    __shared__ int s_start[kMaxBlocks + 1];
+    __shared__ int s_start[MAXB + 1];
     __shared__ uint32_t s_h2[2048];
-    const int tid = threadIdx.x, seg = blockIdx.x;
+    const int tid = threadIdx.x;
     uint32_t* g = a.hist + (int64_t)seg * kSelBins;
-    find_boundary<kNT>(g, a.k, sh.scan, s_b);
+    // the blocks' counts are loaded before the histogram is scanned (thread t
+    // owns blocks [t*PB, (t+1)*PB)), so the two reads overlap
+    const int nb = a.nblk;
+    const int PB = (nb + NT - 1) / NT;
+    const int32_t* cnt = a.blk_count + (int64_t)seg * nb;
+    int mine = 0;
+    for (int q = 0; q < PB; ++q) {
+        const int bi = tid * PB + q;
+        if (bi < nb) mine += cnt[bi];
+    }
+    find_boundary<NT>(g, a.k, sh.scan, s_b);
     const int total = s_b[2];
     const int K = total < a.k ? total : a.k;
     const int bstar = s_b[0];
     const int above = s_b[1];
     int32_t* out_sel = a.sel + (int64_t)seg * a.stride;
 
-    // block offsets: thread t owns blocks [t*PB, (t+1)*PB)
-    const int nb = a.nblk;
-    const int PB = (nb + kNT - 1) / kNT;
-    const int32_t* cnt = a.blk_count + (int64_t)seg * nb;
-    int mine = 0;
-    for (int q = 0; q < PB; ++q) {
-        const int bi = tid * PB + q;
-        if (bi < nb && K > 0) mine += cnt[bi];
-    }
+    // block offsets
+    if (K == 0) mine = 0;
     int n_keep;
-    int off = block_excl_scan<kNT>(mine, sh.scan, &n_keep);
-    if (K > 0 && n_keep <= kSelKeepCap && nb <= kMaxBlocks) {
+    int off = block_excl_scan<NT>(mine, sh.scan, &n_keep);
+    if (K > 0 && n_keep <= kSelKeepCap && nb <= MAXB) {
         // every block's first position in the gathered list
         for (int q = 0; q < PB; ++q) {
             const int bi = tid * PB + q;
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
         if (tid == 0) s_start[nb] = n_keep;
         __syncthreads();
         // all threads copy: entry p belongs to the last block starting at or before p
-        for (int p = tid; p < n_keep; p += kNT) {
+        for (int p = tid; p < n_keep; p += NT) {
             int lo = 0, hi = nb - 1;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
@@ -460,34 +465,34 @@ __global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
         // two radix passes over bits 20..0 of the candidates' keys (bucket b* fixes
         // the rest): bits 20..10, then bits 9..0 of the candidates in the bin found
         const int need = K - above;
-        for (int i = tid; i < 2048; i += kNT) s_h2[i] = 0u;
+        for (int i = tid; i < 2048; i += NT) s_h2[i] = 0u;
         __syncthreads();
-        for (int p0 = 0; p0 < n_keep; p0 += kNT) {
+        for (int p0 = 0; p0 < n_keep; p0 += NT) {
             const int p = p0 + tid;
             const bool act = p < n_keep && s_idx[p] < 0;
             hist_add(s_h2, act, p < n_keep ? (s_key[p] >> 10) & 2047u : 0u);
         }
         __syncthreads();
         int bin, bin_above;
-        find_bin<2048>(s_h2, need, sh.scan, s_b, &bin, &bin_above);
+        find_bin<2048, NT>(s_h2, need, sh.scan, s_b, &bin, &bin_above);
         const uint32_t d1 = (uint32_t)bin;
         int rem = need - bin_above;
-        for (int i = tid; i < 1024; i += kNT) s_h2[i] = 0u;
+        for (int i = tid; i < 1024; i += NT) s_h2[i] = 0u;
         __syncthreads();
-        for (int p0 = 0; p0 < n_keep; p0 += kNT) {
+        for (int p0 = 0; p0 < n_keep; p0 += NT) {
             const int p = p0 + tid;
             const bool act = p < n_keep && s_idx[p] < 0 && ((s_key[p] >> 10) & 2047u) == d1;
             hist_add(s_h2, act, p < n_keep ? s_key[p] & 1023u : 0u);
         }
         __syncthreads();
-        find_bin<1024>(s_h2, rem, sh.scan, s_b, &bin, &bin_above);
+        find_bin<1024, NT>(s_h2, rem, sh.scan, s_b, &bin, &bin_above);
         const uint32_t T = ((uint32_t)bstar << kSelShift) | (d1 << 10) | (uint32_t)bin;
         const int need_eq = rem - bin_above;
         // index-ordered placement with one scan: thread t takes entries [t*E2, t*E2 + E2);
         // an entry above T (every entry above b*, and candidates > T) goes to
         // (entries above T before it) + min(candidates equal to T before it, need_eq),
         // and the first need_eq candidates equal to T fill in between
-        const int E2 = (n_keep + kNT - 1) / kNT;   // <= kSelKeepCap / kNT
+        const int E2 = (n_keep + NT - 1) / NT;   // <= kSelKeepCap / NT
         const int q0 = tid * E2;
         int c_gt = 0, c_eq = 0;
         for (int e = 0; e < E2; ++e) {
@@ -499,7 +504,7 @@ __global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
             else if (k2 == T) ++c_eq;
         }
         int tot;
-        const int packed = block_excl_scan<kNT>(c_gt | (c_eq << 16), sh.scan, &tot);
+        const int packed = block_excl_scan<NT>(c_gt | (c_eq << 16), sh.scan, &tot);
         int n_gt = packed & 0xFFFF, n_eq = packed >> 16;
         for (int e = 0; e < E2; ++e) {
             const int p = q0 + e;
@@ -516,12 +521,16 @@ __global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
             }
         }
     } else if (K > 0) {
-        stream_select(a, a.scores + (int64_t)seg * a.n_keys, seg_valid(a, seg), K, sh, out_sel);
+        stream_select<NT>(a, a.scores + (int64_t)seg * a.n_keys, seg_valid(a, seg), K, sh, out_sel);
     }
-    for (int i = K + tid; i < a.stride; i += kNT) out_sel[i] = -1;
+    for (int i = K + tid; i < a.stride; i += NT) out_sel[i] = -1;
     if (tid == 0) a.count[seg] = K;
     __syncthreads();
-    for (int i = tid; i < kSelBins; i += kNT) g[i] = 0u;
+    for (int i = tid; i < kSelBins; i += NT) g[i] = 0u;
+}
+
+__global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {
+    sel_final_body<kNT>(a, blockIdx.x);
 }
 
 int next_pow2(int x) {

@@ -78,9 +78,9 @@ __device__ inline void copy_rows(const char* cold, char* kv, int row_bytes, int 
     }
 }
 
-__global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
-    const StageLayer& L = a.L[blockIdx.y];
-    const int b = blockIdx.x;
+// One (sequence b, layer) of the stage; a workgroup of kNT threads.
+__device__ __forceinline__ void kv_stage_body(const StageArgs& a, const int b, const int layer) {
+    const StageLayer& L = a.L[layer];
     const int tid = threadIdx.x;
 
     __shared__ int s_scan[kNT / 64 + 1];
@@ -244,6 +244,10 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
     const char* cold = static_cast<const char*>(L.cold) + b * L.cold_stride_b;
     char* kv = static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes;
     copy_rows<kNT>(cold, kv, L.row_bytes, chunks, cpr, s_mlog, s_mslot, L.window);
+}
+
+__global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
+    kv_stage_body(a, blockIdx.x, blockIdx.y);
 }
 
 __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L, int b, int64_t first, int64_t count) {

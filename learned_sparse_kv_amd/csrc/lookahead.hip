@@ -8,19 +8,20 @@
 // One lookahead step t runs on a single stream as five launches:
 //   A  fm_score of step t+1, each workgroup with one extra wave that copies a
 //      share of step t's missed rows into their slots
-//   B  [attention splits of step t                    | select histogram t+1]
-//   C  [attention combine of step t                   | select collect t+1]
-//   D  select of step t+1 (final)
-//   E  stage of step t+1 (LRU; records its misses for the next A)
+//   B  select histogram of step t+1
+//   C  select collect of step t+1
+//   D  [attention splits of step t                    | final select of step t+1]
+//   E  [stage of step t+1 (LRU; records its misses)   | split merge of step t]
 // Design (gfx950): independent work of two steps shares one launch
 // ("horizontal fusion"): in A every score workgroup carries a copy wave, whose
-// PCIe reads run beside the key scan on their own load counter; in B and C the
-// first blocks of the launch run one body and the rest the other.  So the row
-// copies overlap the key scan and the attention overlaps the selection without
-// extra streams, events or host launches.  Every body is the same code the separate kernels run, so the
-// results are those of the synchronous step.  Stage t+1 runs after the
-// attention of step t has finished (stream order), so it may evict any row
-// not selected for t+1.
+// PCIe reads run beside the key scan on their own load counter; in D and E the
+// first blocks of the launch run one body and the rest the other.  The final
+// select (one workgroup per segment) and the stage (one per layer and
+// sequence) leave most CUs idle, so the attention of step t fills them.  Every
+// body is the same code the separate kernels run, so the results are those of
+// the synchronous step.  The stage of step t+1 runs after the attention splits
+// of step t have read their rows (stream order), and the stage itself moves no
+// row (the next A copies them), so it may evict any row not selected for t+1.
 #define LSA_BODIES_ONLY
 #include "fm_score.hip"
 #include "fm_select.hip"
@@ -128,26 +129,33 @@ __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, cons
     score_k::fm_score_body<DK, KT>(sa, blockIdx.x, gridDim.x);
 }
 
+// Launch D: the attention splits of step t beside the final selection of step
+// t+1 (path 1: one 512-thread workgroup per segment).  Both wait long on few
+// dependent memory reads, so neither lengthens the other.
+constexpr int kFinMaxBlocks = 1024;   // collect blocks per segment (1M entries); more take the exact fallback
+
 template <int D, typename KT>
-__global__ __launch_bounds__(512, 2) void la_attend_hist(const AttendArgs aa, const SelectArgs se, const Split sp) {
+__global__ __launch_bounds__(512, 1) void la_final_split(const AttendArgs aa, const SelectArgs se, const Split sp) {
     const int b = blockIdx.x;
     if (b < sp.n0) {
         attend_k::attend_split_body<D, KT>(aa, b % sp.x, (b / sp.x) % sp.y, b / (sp.x * sp.y));
         return;
     }
-    const int h = b - sp.n0;
-    select_k::sel_hist_body<512>(se, h % sp.x2, h / sp.x2);
+    select_k::sel_final_body<512, kFinMaxBlocks>(se, b - sp.n0);
 }
 
+// Launch E: the stage of step t+1 (one 1024-thread workgroup per (layer,
+// sequence)) beside the split merge of step t (four 32-column slices per
+// workgroup).
 template <int D>
-__global__ __launch_bounds__(256) void la_combine_collect(const AttendArgs aa, const SelectArgs se, const Split sp) {
+__global__ __launch_bounds__(1024, 1) void la_stage_combine(const StageArgs ga, const AttendArgs aa, const Split sp) {
     const int b = blockIdx.x;
     if (b < sp.n0) {
-        attend_k::attend_combine_body<D>(aa, b % sp.x, (b / sp.x) % sp.y, b / (sp.x * sp.y));
+        stage_k::kv_stage_body(ga, b % ga.batch, b / ga.batch);
         return;
     }
     const int h = b - sp.n0;
-    select_k::sel_collect_body(se, h % sp.x2, h / sp.x2);
+    attend_k::attend_combine_body<D, 1024>(aa, h % sp.x2, (h / sp.x2) % aa.batch, h / (sp.x2 * aa.batch));
 }
 
 template <int DK, typename KT>
@@ -161,34 +169,40 @@ hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, int n_cu, hipStream
 }
 
 template <int D, typename KT>
-hipError_t launch_b(const AttendArgs& aa, const SelectArgs& se, hipStream_t s) {
+hipError_t launch_d(const AttendArgs& aa, const SelectArgs& se, hipStream_t s) {
     Split sp{};
     sp.x = aa.max_splits;
     sp.y = aa.batch;
     sp.n0 = aa.max_splits * aa.batch * aa.n_layers;
-    int nh = 0;
     if (se.path == 1) {
-        sp.x2 = (int)((se.n_keys + select_k::kBlk - 1) / select_k::kBlk);
-        nh = sp.x2 * se.n_seg;
+        // hist and collect, then the final selection beside the attention splits
+        hipLaunchKernelGGL(select_k::sel_hist_kernel, dim3((unsigned)((se.n_keys + select_k::kBlk - 1) / select_k::kBlk), se.n_seg),
+                           dim3(select_k::kBlkThreads), 0, s, se);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(select_k::sel_collect_kernel, dim3(se.nblk, se.n_seg), dim3(select_k::kBlkThreads), 0, s, se);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((la_final_split<D, KT>), dim3(sp.n0 + se.n_seg), dim3(512), 0, s, aa, se, sp);
+        return hipGetLastError();
     }
-    if (sp.n0 + nh == 0) return hipSuccess;
-    hipLaunchKernelGGL((la_attend_hist<D, KT>), dim3(sp.n0 + nh), dim3(512), 0, s, aa, se, sp);
-    return hipGetLastError();
+    // short segments: the attention splits, then the one-kernel selection
+    if (sp.n0 > 0) {
+        hipLaunchKernelGGL((attend_k::attend_split_kernel<D, KT>), dim3(aa.max_splits, aa.batch, aa.n_layers),
+                           dim3(attend_k::kThreads), 0, s, aa);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_fm_select(se, s);
 }
 
 template <int D>
-hipError_t launch_c(const AttendArgs& aa, const SelectArgs& se, hipStream_t s) {
+hipError_t launch_e(const StageArgs& ga, const AttendArgs& aa, hipStream_t s) {
     Split sp{};
-    sp.x = D / attend_k::kCombCols;
-    sp.y = aa.batch;
-    sp.n0 = sp.x * aa.batch * aa.n_layers;
-    int nc = 0;
-    if (se.path == 1) {
-        sp.x2 = se.nblk;
-        nc = se.nblk * se.n_seg;
-    }
-    if (sp.n0 + nc == 0) return hipSuccess;
-    hipLaunchKernelGGL((la_combine_collect<D>), dim3(sp.n0 + nc), dim3(256), 0, s, aa, se, sp);
+    sp.n0 = ga.batch * ga.n_layers;
+    sp.x2 = (D / attend_k::kCombCols + 3) / 4;
+    const int nc = sp.x2 * aa.batch * aa.n_layers;
+    hipLaunchKernelGGL((la_stage_combine<D>), dim3(sp.n0 + nc), dim3(1024), 0, s, ga, aa, sp);
     return hipGetLastError();
 }
 
@@ -221,24 +235,25 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int p
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_la_attend_hist(const AttendArgs& aa, const SelectArgs& se, hipStream_t s) {
+hipError_t launch_la_select_split(const AttendArgs& aa, const SelectArgs& se, hipStream_t s) {
     if (aa.max_splits == 0) return hipErrorInvalidValue;
     if (aa.dtype == LSA_F32) {
-        if (aa.D == 128) return launch_b<128, float>(aa, se, s);
-        if (aa.D == 256) return launch_b<256, float>(aa, se, s);
-        if (aa.D == 512) return launch_b<512, float>(aa, se, s);
+        if (aa.D == 128) return launch_d<128, float>(aa, se, s);
+        if (aa.D == 256) return launch_d<256, float>(aa, se, s);
+        if (aa.D == 512) return launch_d<512, float>(aa, se, s);
     } else if (aa.dtype == LSA_BF16) {
-        if (aa.D == 128) return launch_b<128, uint16_t>(aa, se, s);
-        if (aa.D == 256) return launch_b<256, uint16_t>(aa, se, s);
-        if (aa.D == 512) return launch_b<512, uint16_t>(aa, se, s);
+        if (aa.D == 128) return launch_d<128, uint16_t>(aa, se, s);
+        if (aa.D == 256) return launch_d<256, uint16_t>(aa, se, s);
+        if (aa.D == 512) return launch_d<512, uint16_t>(aa, se, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_la_combine_collect(const AttendArgs& aa, const SelectArgs& se, hipStream_t s) {
-    if (aa.D == 128) return launch_c<128>(aa, se, s);
-    if (aa.D == 256) return launch_c<256>(aa, se, s);
-    if (aa.D == 512) return launch_c<512>(aa, se, s);
+hipError_t launch_la_stage_combine(const StageArgs& ga, const AttendArgs& aa, hipStream_t s) {
+    if (ga.batch != aa.batch || ga.n_layers != aa.n_layers) return hipErrorInvalidValue;
+    if (aa.D == 128) return launch_e<128>(ga, aa, s);
+    if (aa.D == 256) return launch_e<256>(ga, aa, s);
+    if (aa.D == 512) return launch_e<512>(ga, aa, s);
     return hipErrorInvalidValue;
 }
 

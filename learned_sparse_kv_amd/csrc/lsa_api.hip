@@ -945,24 +945,15 @@ lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t
         t.end();
     }
     {
-        Timed t(ctx, LSA_K_ATTEND, s);
-        HIPTRY(launch_la_attend_hist(P.aa, P.se, s));
-        t.end();
-    }
-    {
-        Timed t(ctx, LSA_K_COMBINE, s);
-        HIPTRY(launch_la_combine_collect(P.aa, P.se, s));
-        t.end();
-    }
-    {
         Timed t(ctx, LSA_K_SELECT, s);
-        HIPTRY(launch_fm_select_final(P.se, s));
+        HIPTRY(launch_la_select_split(P.aa, P.se, s));
         t.end();
     }
+    const AttendArgs attend_cur = P.aa;   // the combine merges step t's splits
     plan_use_buffer(&P, nxt);
     {
         Timed t(ctx, LSA_K_STAGE, s);
-        HIPTRY(launch_kv_stage(P.ga, s));
+        HIPTRY(launch_la_stage_combine(P.ga, attend_cur, s));
         t.end();
     }
     ctx->la_cur = nxt;

@@ -198,14 +198,15 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
     attend_split_body<D, KT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// One workgroup per (layer, sequence, 32-column slice of D): the splits'
-// maxima and denominators are staged in LDS with one parallel load, every
-// thread then merges two outputs over the splits in split order, eight
-// splits' loads in flight at a time.
+// One workgroup of NT threads per (layer, sequence, NT/256 consecutive
+// 32-column slices of D): the splits' maxima and denominators are staged in
+// LDS with one parallel load, every thread then merges two outputs over the
+// splits in split order, eight splits' loads in flight at a time.
 constexpr int kCombCols = 32;
 
-template <int D>
+template <int D, int NT = 256>
 __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const int bx, const int by, const int bz) {
+    static_assert(NT % 256 == 0, "whole slices per workgroup");
     __shared__ float s_ml[kMaxSplits * 32];
     __shared__ float s_w[kMaxSplits][16];   // exp(m_s - M_h)
     __shared__ float s_inv[16];             // 1 / sum_s exp(m_s - M_h) l_s
@@ -216,9 +217,10 @@ __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const i
     n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
     const int ns = (n + kR - 1) / kR;
     const int pair = bz * a.batch + b;
-    const int d0 = bx * kCombCols;
+    const int slice = bx * (NT / 256) + (tid >> 8);
+    const int d0 = slice * kCombCols;
     const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
-    for (int i = tid; i < ns * 32; i += 256) s_ml[i] = ml[i];
+    for (int i = tid; i < ns * 32; i += NT) s_ml[i] = ml[i];
     __syncthreads();
     if (tid < 16) {
         const int hh = tid;
@@ -234,8 +236,8 @@ __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const i
     }
     __syncthreads();
     // thread -> (head h, columns d0 + c and d0 + c + 16)
-    const int h = tid >> 4, c = tid & 15;
-    if (h >= a.hq) return;
+    const int h = (tid & 255) >> 4, c = tid & 15;
+    if (h >= a.hq || d0 >= D) return;
     float* out = L.out + ((int64_t)b * a.hq + h) * D + d0;
     if (ns == 0) {
         out[c] = 0.0f;

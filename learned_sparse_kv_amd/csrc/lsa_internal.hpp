@@ -216,8 +216,11 @@ hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid 
 // stage's output, laid out back to back over (layer, sequence)) into their slots.
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
                                  int n_cu, hipStream_t s);
-hipError_t launch_la_attend_hist(const AttendArgs& aa, const SelectArgs& se, hipStream_t s);
-hipError_t launch_la_combine_collect(const AttendArgs& aa, const SelectArgs& se, hipStream_t s);
+// select histogram and collect of step t+1, then its final selection beside the
+// attention splits of step t (short segments: the splits, then the one-kernel select)
+hipError_t launch_la_select_split(const AttendArgs& aa, const SelectArgs& se, hipStream_t s);
+// the stage of step t+1 beside the split merge of step t
+hipError_t launch_la_stage_combine(const StageArgs& ga, const AttendArgs& aa, hipStream_t s);
 
 }  // namespace lsa
 
