@@ -99,8 +99,12 @@ __device__ inline void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int DK, typename KT>
-__device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, const int gx) {
+// With HIST, every stored score that the select would count (a valid entry;
+// in threshold mode one above t_f) is also added to the LDS histogram `hist`
+// of 11-bit key tops -- the select's first pass -- so a caller can skip it.
+template <int DK, typename KT, bool HIST = false>
+__device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, const int gx, uint32_t* hist = nullptr,
+                                              const int hist_mode = 0, const float hist_t_f = 0.0f) {
     using C = Cfg<DK, KT>;
     constexpr int kPerRead = 16 / (int)sizeof(KT);
     constexpr int kSteps = C::kReads;                     // 16-byte reads per lane per tile
@@ -239,6 +243,11 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
             }
             const uint32_t off = half ? 0x80000000u : (uint32_t)((t - lo) * kTile + col) * 4u;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e + 0.0f), so, off, 0, 0);
+            if (HIST) {
+                const float ev = e + 0.0f;
+                if (half == 0 && (t - lo) * kTile + col < nv && (hist_mode != LSA_SELECT_THRESHOLD || ev > hist_t_f))
+                    atomicAdd(&hist[order_key(ev) >> kSelShift], 1u);
+            }
             cur ^= 1;
         }
     }

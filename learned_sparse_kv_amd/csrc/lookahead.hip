@@ -7,8 +7,9 @@
 //
 // One lookahead step t runs on a single stream as five launches:
 //   A  fm_score of step t+1, each workgroup with one extra wave that copies a
-//      share of step t's missed rows into their slots
-//   B  select histogram of step t+1
+//      share of step t's missed rows into their slots (one segment: the score
+//      waves also build the select's histogram)
+//   B  select histogram of step t+1 (several segments only)
 //   C  select collect of step t+1
 //   D  [attention splits of step t                    | final select of step t+1]
 //   E  [stage of step t+1 (LRU; records its misses)   | split merge of step t]
@@ -117,16 +118,49 @@ __device__ inline void copy_wave(const CopyArgs& ca, const int wg, const int n_w
     }
 }
 
-// Workgroup = 4 score waves (fm_score) + 1 copy wave.
-template <int DK, typename KT>
-__global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, const CopyArgs ca) {
+// The select's histogram, built by the score launch when the step has one
+// segment: hist [kSelBins], zero on entry; mode and t_f as in the select.
+struct HistArgs {
+    uint32_t* hist;
+    int32_t mode;
+    float t_f;
+};
+
+// Workgroup = 4 score waves (fm_score) + 1 copy wave.  With HIST the score
+// waves also count their scores into an LDS histogram; the last of them to
+// finish adds it to the segment's histogram (its PCIe-bound copy wave
+// usually ends later, so the flush costs no time).
+template <int DK, typename KT, bool HIST>
+__global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, const CopyArgs ca, const HistArgs ha) {
     __shared__ int s_pre[LSA_MAX_LAYERS * LSA_MAX_BATCH];
+    __shared__ uint32_t s_hist[HIST ? kSelBins : 1];
+    __shared__ int s_done;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (HIST) {
+        for (int i = threadIdx.x; i < kSelBins; i += 320) s_hist[i] = 0u;
+        if (threadIdx.x == 0) s_done = 0;
+        __syncthreads();
+    }
     if (wave == 4) {
         copy_wave(ca, blockIdx.x, gridDim.x, s_pre);
         return;
     }
-    score_k::fm_score_body<DK, KT>(sa, blockIdx.x, gridDim.x);
+    score_k::fm_score_body<DK, KT, HIST>(sa, blockIdx.x, gridDim.x, s_hist, ha.mode, ha.t_f);
+    if (HIST) {
+        // every score wave's LDS adds are done before it counts itself finished
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        const int lane = threadIdx.x & 63;
+        int prev = 0;
+        if (lane == 0) prev = atomicAdd(&s_done, 1);
+        prev = __shfl(prev, 0, 64);
+        if (prev == score_k::kWaves - 1) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            for (int i = lane; i < kSelBins; i += 64) {
+                const uint32_t c = s_hist[i];
+                if (c) atomicAdd(&ha.hist[i], c);
+            }
+        }
+    }
 }
 
 // Launch D: the attention splits of step t beside the final selection of step
@@ -159,27 +193,35 @@ __global__ __launch_bounds__(1024, 1) void la_stage_combine(const StageArgs ga, 
 }
 
 template <int DK, typename KT>
-hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, int n_cu, hipStream_t s) {
+hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, const HistArgs& ha, int n_cu, hipStream_t s) {
     const int total = sa.tile_start[sa.batch];
     int grid = (total + score_k::kWaves - 1) / score_k::kWaves;
     if (grid > n_cu) grid = n_cu;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((la_score_copy<DK, KT>), dim3(grid), dim3(320), 0, s, sa, ca);
+    if (ha.hist)
+        hipLaunchKernelGGL((la_score_copy<DK, KT, true>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+    else
+        hipLaunchKernelGGL((la_score_copy<DK, KT, false>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
     return hipGetLastError();
 }
 
 template <int D, typename KT>
-hipError_t launch_d(const AttendArgs& aa, const SelectArgs& se, hipStream_t s) {
+hipError_t launch_d(const AttendArgs& aa, const SelectArgs& se, bool hist_done, hipStream_t s) {
     Split sp{};
     sp.x = aa.max_splits;
     sp.y = aa.batch;
     sp.n0 = aa.max_splits * aa.batch * aa.n_layers;
     if (se.path == 1) {
-        // hist and collect, then the final selection beside the attention splits
-        hipLaunchKernelGGL(select_k::sel_hist_kernel, dim3((unsigned)((se.n_keys + select_k::kBlk - 1) / select_k::kBlk), se.n_seg),
-                           dim3(select_k::kBlkThreads), 0, s, se);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        // hist (unless the score launch built it) and collect, then the final
+        // selection beside the attention splits
+        hipError_t e = hipSuccess;
+        if (!hist_done) {
+            hipLaunchKernelGGL(select_k::sel_hist_kernel,
+                               dim3((unsigned)((se.n_keys + select_k::kBlk - 1) / select_k::kBlk), se.n_seg),
+                               dim3(select_k::kBlkThreads), 0, s, se);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(select_k::sel_collect_kernel, dim3(se.nblk, se.n_seg), dim3(select_k::kBlkThreads), 0, s, se);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -209,7 +251,7 @@ hipError_t launch_e(const StageArgs& ga, const AttendArgs& aa, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
-                                 int n_cu, hipStream_t s) {
+                                 int n_cu, const SelectArgs* hist_for, hipStream_t s) {
     // the copy reads the stage's miss lists through one base pointer: they must
     // lie back to back over (layer, sequence), with one row size
     const StageLayer& L0 = ga.L[0];
@@ -223,28 +265,37 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int p
     const int cpr = L0.row_bytes / 16;
     if (L0.row_bytes % 16 != 0 || cpr < 1 || (cpr & (cpr - 1)) != 0) return hipErrorInvalidValue;
     const CopyArgs ca{L0.miss, L0.n_miss, ga.n_layers * ga.batch, phys_stride, L0.row_bytes};
+    HistArgs ha{nullptr, 0, 0.0f};
+    if (hist_for) {
+        if (!la_fused_hist(sa, *hist_for)) return hipErrorInvalidValue;
+        ha = HistArgs{hist_for->hist, hist_for->mode, hist_for->t_f};
+    }
     if (key_dtype == LSA_F32) {
-        if (dk == 32) return launch_a<32, float>(sa, ca, n_cu, s);
-        if (dk == 64) return launch_a<64, float>(sa, ca, n_cu, s);
-        if (dk == 128) return launch_a<128, float>(sa, ca, n_cu, s);
+        if (dk == 32) return launch_a<32, float>(sa, ca, ha, n_cu, s);
+        if (dk == 64) return launch_a<64, float>(sa, ca, ha, n_cu, s);
+        if (dk == 128) return launch_a<128, float>(sa, ca, ha, n_cu, s);
     } else if (key_dtype == LSA_BF16) {
-        if (dk == 32) return launch_a<32, uint16_t>(sa, ca, n_cu, s);
-        if (dk == 64) return launch_a<64, uint16_t>(sa, ca, n_cu, s);
-        if (dk == 128) return launch_a<128, uint16_t>(sa, ca, n_cu, s);
+        if (dk == 32) return launch_a<32, uint16_t>(sa, ca, ha, n_cu, s);
+        if (dk == 64) return launch_a<64, uint16_t>(sa, ca, ha, n_cu, s);
+        if (dk == 128) return launch_a<128, uint16_t>(sa, ca, ha, n_cu, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_la_select_split(const AttendArgs& aa, const SelectArgs& se, hipStream_t s) {
+bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se) {
+    return se.path == 1 && se.n_seg == 1 && sa.batch == 1 && se.hist != nullptr;
+}
+
+hipError_t launch_la_select_split(const AttendArgs& aa, const SelectArgs& se, bool hist_done, hipStream_t s) {
     if (aa.max_splits == 0) return hipErrorInvalidValue;
     if (aa.dtype == LSA_F32) {
-        if (aa.D == 128) return launch_d<128, float>(aa, se, s);
-        if (aa.D == 256) return launch_d<256, float>(aa, se, s);
-        if (aa.D == 512) return launch_d<512, float>(aa, se, s);
+        if (aa.D == 128) return launch_d<128, float>(aa, se, hist_done, s);
+        if (aa.D == 256) return launch_d<256, float>(aa, se, hist_done, s);
+        if (aa.D == 512) return launch_d<512, float>(aa, se, hist_done, s);
     } else if (aa.dtype == LSA_BF16) {
-        if (aa.D == 128) return launch_d<128, uint16_t>(aa, se, s);
-        if (aa.D == 256) return launch_d<256, uint16_t>(aa, se, s);
-        if (aa.D == 512) return launch_d<512, uint16_t>(aa, se, s);
+        if (aa.D == 128) return launch_d<128, uint16_t>(aa, se, hist_done, s);
+        if (aa.D == 256) return launch_d<256, uint16_t>(aa, se, hist_done, s);
+        if (aa.D == 512) return launch_d<512, uint16_t>(aa, se, hist_done, s);
     }
     return hipErrorInvalidValue;
 }

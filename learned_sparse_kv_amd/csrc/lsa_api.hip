@@ -939,14 +939,16 @@ lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t
     hipStream_t s = (hipStream_t)stream;
     plan_use_buffer(&P, cur);
     const StageArgs fetch_cur = P.ga;   // the rows step t reads, and its recorded misses
+    const bool fuse_hist = la_fused_hist(P.sa, P.se);
     {
         Timed t(ctx, LSA_K_SCORE, s);
-        HIPTRY(launch_la_fetch_score(P.sa, fetch_cur, P.phys_stride, d->key_dtype, d->dk, ctx->n_cu, s));
+        HIPTRY(launch_la_fetch_score(P.sa, fetch_cur, P.phys_stride, d->key_dtype, d->dk, ctx->n_cu,
+                                     fuse_hist ? &P.se : nullptr, s));
         t.end();
     }
     {
         Timed t(ctx, LSA_K_SELECT, s);
-        HIPTRY(launch_la_select_split(P.aa, P.se, s));
+        HIPTRY(launch_la_select_split(P.aa, P.se, fuse_hist, s));
         t.end();
     }
     const AttendArgs attend_cur = P.aa;   // the combine merges step t's splits

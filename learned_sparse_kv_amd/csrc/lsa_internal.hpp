@@ -214,11 +214,15 @@ hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid 
 // fused launches of the lookahead schedule.  launch_la_fetch_score scores and,
 // in the same launch, copies the rows in the miss lists of `ga` (a deferring
 // stage's output, laid out back to back over (layer, sequence)) into their slots.
+// With hist_for (a one-segment path-1 select, see la_fused_hist), the score
+// launch also builds that select's histogram.
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
-                                 int n_cu, hipStream_t s);
-// select histogram and collect of step t+1, then its final selection beside the
-// attention splits of step t (short segments: the splits, then the one-kernel select)
-hipError_t launch_la_select_split(const AttendArgs& aa, const SelectArgs& se, hipStream_t s);
+                                 int n_cu, const SelectArgs* hist_for, hipStream_t s);
+bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se);
+// select histogram (unless hist_done) and collect of step t+1, then its final
+// selection beside the attention splits of step t (short segments: the splits,
+// then the one-kernel select)
+hipError_t launch_la_select_split(const AttendArgs& aa, const SelectArgs& se, bool hist_done, hipStream_t s);
 // the stage of step t+1 beside the split merge of step t
 hipError_t launch_la_stage_combine(const StageArgs& ga, const AttendArgs& aa, hipStream_t s);
 
