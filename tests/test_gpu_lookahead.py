@@ -1,8 +1,8 @@
 """GPU parity of the lookahead schedule (lsa_lookahead_prime / lsa_lookahead_step):
-the next step's prediction, staging and row fetch run on a side stream while
-the current step attends.  Step t must give exactly the rows and the output of
-the synchronous decode step t (same selection, same LRU sequence), match the
-oracle within 1e-5, and replay identically from HIP graphs."""
+step t's row copy and attention share launches with the score, selection and
+staging of step t+1.  Step t must give exactly the rows and the output of the
+synchronous decode step t (same selection, same LRU sequence), match the oracle
+within the workload's tolerance, and replay identically from HIP graphs."""
 import numpy as np
 import pytest
 import torch
@@ -108,3 +108,43 @@ def test_lookahead_small_workloads_match_oracle():
                 err = rel_err_rows(out[l, 0], want["out"][l][0])
                 assert err <= RTOL[wl.kv_dtype], f"{name} step {t} layer {l}: rel err {err}"
         say(f"  {name} lookahead ok")
+
+
+@pytest.mark.parametrize("slots", [None, 1024])
+def test_lookahead_batched_threshold_matches_sync(slots):
+    # four sequences of 65536 entries: the separate select histogram, threshold
+    # mode, bf16 rows, and the batched indexing of the fused launches; with 1024
+    # slots both layers also swap (from HBM cold pools), so the copy has misses
+    wl = L.WORKLOADS["thresh_256k"]
+    if slots is not None:
+        wl = wl.replace(gpu_chunks=slots)
+    dw = DeviceWorkload(wl)
+    dw.make_steps(6)
+    n = 4
+    sync_out, sync_phys = [], []
+    dw.reset_pools()
+    for t in range(n):
+        dw.step(t)
+        torch.cuda.synchronize()
+        sync_out.append(bits(dw.out.cpu().numpy()).copy())
+        sync_phys.append((dw.phys.cpu().numpy().copy(), dw.n_rows.cpu().numpy().copy()))
+    sync_stats = [p.stats() for p in dw.pools]
+    dw.reset_pools()
+    dw.lookahead_prime(0)
+    for t in range(n):
+        cur = lsa.lookahead_buffer(dw.ctx)
+        dw.lookahead_step(t)
+        torch.cuda.synchronize()
+        phys, nrows = dw.phys2[cur].cpu().numpy(), dw.n_rows2[cur].cpu().numpy()
+        want_phys, want_nrows = sync_phys[t]
+        assert np.array_equal(nrows, want_nrows), f"step {t}: row counts"
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                m = int(nrows[l, b])
+                assert np.array_equal(phys[l, b, :m], want_phys[l, b, :m]), f"step {t} layer {l} seq {b}: rows"
+        assert np.array_equal(bits(dw.out.cpu().numpy()), sync_out[t]), f"step {t}: lookahead vs sync bits"
+    # the lookahead staged step n as well: its counters are one step ahead
+    if slots is not None:
+        la_stats = [p.stats() for p in dw.pools]
+        assert sum(s["misses"] for s in la_stats) >= sum(s["misses"] for s in sync_stats) > 0
+    say(f"  thresh_256k slots={slots}: lookahead = sync over {n} steps")
