@@ -43,42 +43,45 @@ namespace score_k {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTile = 32;          // keys per wave tile
+constexpr int kSub = 32;           // keys per MFMA block (the B operand's columns)
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// A wave tile is kNSub blocks of 32 keys -- 128 * DK bytes for every key type
+// (16 KB at DK 128), so the load pipeline is the same for fp32, bf16 and fp8.
 template <int DK, typename KT>
 struct Cfg {
+    static constexpr int kNSub = 4 / (int)sizeof(KT);
+    static constexpr int kTile = kSub * kNSub;               // keys per wave tile
     static constexpr int kRowBytes = DK * (int)sizeof(KT);
     static constexpr int kLdsStride = kRowBytes + 16;
     static constexpr int kTileBytes = kTile * kRowBytes;
     static constexpr int kLoads = kTileBytes / (64 * 16);      // 16-byte loads per lane
-    static constexpr int kHalf = DK / 2;                     // MFMA k-steps
+    static constexpr int kHalf = DK / 2;                     // elements of a key row per lane
     static constexpr int kHalfBytes = kHalf * (int)sizeof(KT);
-    static constexpr int kReads = kHalfBytes / 16;           // ds_read_b128 per lane
+    static constexpr int kReads = kHalfBytes / 16;           // ds_read_b128 per lane and block
+    static constexpr int kSteps = kNSub * kReads;            // read steps per tile
     static_assert(kTileBytes % (64 * 16) == 0, "tile must split into 16-byte loads");
     static_assert(kHalfBytes % 16 == 0, "half row must be 16-byte aligned");
+    static_assert(kSteps == kLoads, "one tile load per read step");
 };
 
-template <typename KT>
-__device__ inline void unpack16(const uint4& u, float* out);
-
-template <>
-__device__ inline void unpack16<float>(const uint4& u, float* out) {
-    out[0] = __uint_as_float(u.x);
-    out[1] = __uint_as_float(u.y);
-    out[2] = __uint_as_float(u.z);
-    out[3] = __uint_as_float(u.w);
+// Exact split of an fp32 value into three bf16 parts, x = hi + mid + lo: hi
+// keeps the top 8 significant bits, mid the next 8 of the remainder, and the
+// remainder after that has at most 8 significant bits, so it is exact in bf16.
+__device__ inline void split3(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+    const uint32_t u = __float_as_uint(x);
+    const float r1 = x - __uint_as_float(u & 0xFFFF0000u);
+    const uint32_t u1 = __float_as_uint(r1);
+    const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
+    hi = (uint16_t)(u >> 16);
+    mid = (uint16_t)(u1 >> 16);
+    lo = (uint16_t)(__float_as_uint(r2) >> 16);
 }
 
-template <>
-__device__ inline void unpack16<uint16_t>(const uint4& u, float* out) {
-    out[0] = bf16_lo(u.x);
-    out[1] = bf16_hi(u.x);
-    out[2] = bf16_lo(u.y);
-    out[3] = bf16_hi(u.y);
-    out[4] = bf16_lo(u.z);
-    out[5] = bf16_hi(u.z);
-    out[6] = bf16_lo(u.w);
-    out[7] = bf16_hi(u.w);
+__device__ inline bf16x8 as_bf16x8(const uint4& u) {
+    return __builtin_bit_cast(bf16x8, u);
 }
 
 // max(x, 0) for finite x in one integer max: a set sign bit makes the pattern
@@ -88,7 +91,7 @@ __device__ inline float relu(float x) { return __int_as_float(max(__float_as_int
 // Buffer resource of one tile: base at the tile, records = bytes of the
 // sequence's valid keys from there on, so every read of the tile stays inside
 // the sequence and rows >= n_valid read as zero.  A sequence has
-// ceil(n_valid / 32) tiles, so a tile's first row is valid: tile_off < seq_bytes.
+// ceil(n_valid / keys per tile) tiles, so a tile's first row is valid: tile_off < seq_bytes.
 __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char* seq, uint32_t seq_bytes, uint32_t tile_off) {
     return make_rsrc(seq + tile_off, seq_bytes - tile_off);
 }
@@ -99,6 +102,29 @@ __device__ inline void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The query block as the MFMA's A operand: for fp32 keys the fp32 values for
+// v_mfma_f32_32x32x2f32; for bf16 and fp8 keys each value split exactly into
+// three bf16 parts (hi, mid, lo) for v_mfma_f32_32x32x16_bf16, so every product
+// with a key (exact in bf16) is the exact product with the fp32 query.
+template <int DK, bool F32>
+struct QOperand;
+template <int DK>
+struct QOperand<DK, true> {
+    float v[DK / 2];
+};
+template <int DK>
+struct QOperand<DK, false> {
+    bf16x8 hi[DK / 16], mid[DK / 16], lo[DK / 16];
+};
+
+// Two fp8 (OCP E4M3) codes -> their exact bf16 values, packed: the hardware
+// conversion to fp32 is exact, and every E4M3 value is exact in bf16.
+template <bool HIGH_PAIR>
+__device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH_PAIR);
+    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
 // With HIST, every stored score that the select would count (a valid entry;
 // in threshold mode one above t_f) is also added to the LDS histogram `hist`
 // of 11-bit key tops -- the select's first pass -- so a caller can skip it.
@@ -106,17 +132,18 @@ template <int DK, typename KT, bool HIST = false>
 __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, const int gx, uint32_t* hist = nullptr,
                                               const int hist_mode = 0, const float hist_t_f = 0.0f) {
     using C = Cfg<DK, KT>;
-    constexpr int kPerRead = 16 / (int)sizeof(KT);
-    constexpr int kSteps = C::kReads;                     // 16-byte reads per lane per tile
-    static_assert(C::kReads == C::kLoads, "one tile load per read step");
+    constexpr bool kF32 = sizeof(KT) == 4;
+    constexpr int kSteps = C::kSteps;
+    constexpr int kTile = C::kTile;
     static_assert(1024 % C::kRowBytes == 0, "a 64-lane load covers whole rows");
     constexpr int kBuf = kTile * C::kLdsStride;
     constexpr int kLoadStride = (1024 / C::kRowBytes) * C::kLdsStride;   // LDS bytes per 64-lane load
+    constexpr int kSubBytes = kSub * C::kLdsStride;                     // LDS bytes per 32-key block
     __shared__ __attribute__((aligned(16))) char lds[kWaves][2][kBuf];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps tile state in SGPRs
-    const int col = lane & 31;      // key within the tile (B/D column); query row for A
+    const int col = lane & 31;      // key within a 32-key block (B/D column); query row for A
     const int half = lane >> 5;     // which half of dk this lane feeds
     const int total = a.tile_start[a.batch];
     const int stride = gx * kWaves;
@@ -152,19 +179,39 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
 #pragma unroll
         for (int i = 0; i < kSteps; ++i) pre[i] = buffer_load16(r0, vo[i >> 2] + (uint32_t)(i & 3) * 1024u);
         __builtin_amdgcn_sched_barrier(0);
-        // A operand: query row `col` (indexer col/8, head col%8), elements half*DK/2 + s
-        float qa[C::kHalf];
+        // A operand: query row `col` (indexer col/8, head col%8), elements half*DK/2 + e
+        QOperand<DK, kF32> qa;
         {
             const int g = col >> 3, hd = col & 7;
             const bool qv = g < a.n_idx && hd < a.heads;
             const float* qrow = a.q + (((int64_t)b * a.n_idx + (qv ? g : 0)) * a.heads + (qv ? hd : 0)) * DK + half * C::kHalf;
+            if constexpr (kF32) {
 #pragma unroll
-            for (int e = 0; e < C::kHalf; e += 4) {
-                const f32x4 v = qv ? *reinterpret_cast<const f32x4*>(qrow + e) : f32x4{0.f, 0.f, 0.f, 0.f};
-                qa[e] = v[0];
-                qa[e + 1] = v[1];
-                qa[e + 2] = v[2];
-                qa[e + 3] = v[3];
+                for (int e = 0; e < C::kHalf; e += 4) {
+                    const f32x4 v = qv ? *reinterpret_cast<const f32x4*>(qrow + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    qa.v[e] = v[0];
+                    qa.v[e + 1] = v[1];
+                    qa.v[e + 2] = v[2];
+                    qa.v[e + 3] = v[3];
+                }
+            } else {
+#pragma unroll
+                for (int blk = 0; blk < C::kHalf / 8; ++blk) {
+                    uint32_t wh[4], wm[4], wl[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const f32x2 v = qv ? *reinterpret_cast<const f32x2*>(qrow + 8 * blk + 2 * p) : f32x2{0.f, 0.f};
+                        uint16_t h0, m0, l0, h1, m1, l1;
+                        split3(v[0], h0, m0, l0);
+                        split3(v[1], h1, m1, l1);
+                        wh[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                        wm[p] = (uint32_t)m0 | ((uint32_t)m1 << 16);
+                        wl[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+                    }
+                    qa.hi[blk] = as_bf16x8(make_uint4(wh[0], wh[1], wh[2], wh[3]));
+                    qa.mid[blk] = as_bf16x8(make_uint4(wm[0], wm[1], wm[2], wm[3]));
+                    qa.lo[blk] = as_bf16x8(make_uint4(wl[0], wl[1], wl[2], wl[3]));
+                }
             }
         }
         // epilogue weights: accumulator r is query row 8*(r/4) + 4*half + r%4
@@ -198,55 +245,85 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
             const char* rd = my0 + cur * kBuf + roff;
             char* wrb = my0 + (cur ^ 1) * kBuf + woff;
 
-            f32x16 acc = {};
+            f32x16 acc[C::kNSub];
+#pragma unroll
+            for (int j = 0; j < C::kNSub; ++j) acc[j] = f32x16{};
             uint4 u = *reinterpret_cast<const uint4*>(rd);
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
-                const uint4 un = s + 1 < kSteps ? *reinterpret_cast<const uint4*>(rd + (s + 1) * 16) : u;
+                // step s reads 16 bytes of key block j = s / kReads at read rr = s % kReads
+                const int j = s / C::kReads, rr = s % C::kReads;
+                const int sn = s + 1;
+                const uint4 un = sn < kSteps
+                    ? *reinterpret_cast<const uint4*>(rd + (sn / C::kReads) * kSubBytes + (sn % C::kReads) * 16)
+                    : u;
                 *reinterpret_cast<uint4*>(wrb + s * kLoadStride) = pre[s];
                 pre[s] = buffer_load16(r2, vo[s >> 2] + (uint32_t)(s & 3) * 1024u);
-                float kb[kPerRead];
-                unpack16<KT>(u, kb);
+                if constexpr (kF32) {
+                    const float kb[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                         __uint_as_float(u.w)};
 #pragma unroll
-                for (int e = 0; e < kPerRead; ++e)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[s * kPerRead + e], kb[e], acc, 0, 0, 0);
+                    for (int e = 0; e < 4; ++e)
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.v[rr * 4 + e], kb[e], acc[j], 0, 0, 0);
+                } else if constexpr (sizeof(KT) == 2) {
+                    const bf16x8 kb = as_bf16x8(u);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.hi[rr], kb, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.mid[rr], kb, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.lo[rr], kb, acc[j], 0, 0, 0);
+                } else {
+                    // 16 fp8 codes: elements of blocks 2*rr and 2*rr + 1
+                    const bf16x8 k0 = as_bf16x8(make_uint4(fp8x2_to_bf16x2<false>(u.x), fp8x2_to_bf16x2<true>(u.x),
+                                                           fp8x2_to_bf16x2<false>(u.y), fp8x2_to_bf16x2<true>(u.y)));
+                    const bf16x8 k1 = as_bf16x8(make_uint4(fp8x2_to_bf16x2<false>(u.z), fp8x2_to_bf16x2<true>(u.z),
+                                                           fp8x2_to_bf16x2<false>(u.w), fp8x2_to_bf16x2<true>(u.w)));
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.hi[2 * rr], k0, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.mid[2 * rr], k0, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.lo[2 * rr], k0, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.hi[2 * rr + 1], k1, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.mid[2 * rr + 1], k1, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.lo[2 * rr + 1], k1, acc[j], 0, 0, 0);
+                }
                 u = un;
                 __builtin_amdgcn_sched_barrier(0);
             }
             // the other buffer is complete and this one's reads are done
             wave_sync();
 
-            // epilogue: per indexer, this lane's 4 heads; then the other half's 4 heads
-            float sv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {
-                if (gi >= a.n_idx) break;   // uniform
-                float v = 0.0f;
+            for (int j = 0; j < C::kNSub; ++j) {
+                // epilogue: per indexer, this lane's 4 heads; then the other half's 4 heads
+                float sv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int c = 0; c < 4; ++c) v += wr[4 * gi + c] * relu(acc[4 * gi + c]);
-                // lanes 0..31 receive lane l+32's value in r[1]
-                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-                sv[gi] = (v + __uint_as_float(r[1])) + 0.0f;
-            }
-            float e;
-            if (a.ensemble == LSA_ENSEMBLE_MAX) {
-                e = sv[0];
-                if (a.n_idx > 1) e = fmaxf(e, sv[1]);
-                if (a.n_idx > 2) e = fmaxf(e, sv[2]);
-                if (a.n_idx > 3) e = fmaxf(e, sv[3]);
-            } else {
-                float sum = sv[0];
-                if (a.n_idx > 1) sum += sv[1];
-                if (a.n_idx > 2) sum += sv[2];
-                if (a.n_idx > 3) sum += sv[3];
-                e = sum / (float)a.n_idx;
-            }
-            const uint32_t off = half ? 0x80000000u : (uint32_t)((t - lo) * kTile + col) * 4u;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e + 0.0f), so, off, 0, 0);
-            if (HIST) {
-                const float ev = e + 0.0f;
-                if (half == 0 && (t - lo) * kTile + col < nv && (hist_mode != LSA_SELECT_THRESHOLD || ev > hist_t_f))
-                    atomicAdd(&hist[order_key(ev) >> kSelShift], 1u);
+                for (int gi = 0; gi < 4; ++gi) {
+                    if (gi >= a.n_idx) break;   // uniform
+                    float v = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) v += wr[4 * gi + c] * relu(acc[j][4 * gi + c]);
+                    // lanes 0..31 receive lane l+32's value in r[1]
+                    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                    sv[gi] = (v + __uint_as_float(r[1])) + 0.0f;
+                }
+                float e;
+                if (a.ensemble == LSA_ENSEMBLE_MAX) {
+                    e = sv[0];
+                    if (a.n_idx > 1) e = fmaxf(e, sv[1]);
+                    if (a.n_idx > 2) e = fmaxf(e, sv[2]);
+                    if (a.n_idx > 3) e = fmaxf(e, sv[3]);
+                } else {
+                    float sum = sv[0];
+                    if (a.n_idx > 1) sum += sv[1];
+                    if (a.n_idx > 2) sum += sv[2];
+                    if (a.n_idx > 3) sum += sv[3];
+                    e = sum / (float)a.n_idx;
+                }
+                const int key = (t - lo) * kTile + j * kSub + col;
+                const uint32_t off = half ? 0x80000000u : (uint32_t)key * 4u;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e + 0.0f), so, off, 0, 0);
+                if (HIST) {
+                    const float ev = e + 0.0f;
+                    if (half == 0 && key < nv && (hist_mode != LSA_SELECT_THRESHOLD || ev > hist_t_f))
+                        atomicAdd(&hist[order_key(ev) >> kSelShift], 1u);
+                }
             }
             cur ^= 1;
         }

@@ -321,13 +321,15 @@ lsa_status score_args(const void* keys, lsa_dtype key_dtype, int32_t batch, int6
     a->n_idx = n_idx;
     a->heads = heads;
     a->ensemble = ens;
+    // a wave tile is 128 * dk bytes of keys: 32 fp32, 64 bf16 or 128 fp8 keys
+    const int64_t tile_keys = 32 * (4 / elem_bytes(key_dtype));
     int tiles = 0;
     for (int b = 0; b < batch; ++b) {
         const int64_t nv = n_valid ? n_valid[b] : n_keys;
         if (nv < 0 || nv > n_keys) return fail(LSA_ERR_INVALID_ARG, "n_valid[%d] = %lld not in [0, n_keys]", b, (long long)nv);
         a->n_valid[b] = (int32_t)nv;
         a->tile_start[b] = tiles;
-        tiles += (int)((nv + 31) / 32);
+        tiles += (int)((nv + tile_keys - 1) / tile_keys);
     }
     a->tile_start[batch] = tiles;
     return LSA_OK;
