@@ -15,7 +15,7 @@ Prints ONE JSON line.  Per-kernel times come from HIP events recorded on the
 launch stream inside the timed region; the CPU baseline is the plain oracle
 timed on a bounded sample of the same steps.
 
-    python bench.py [--steps K] [--warmup W] [--workload swap_1m|thresh_256k|ens_8k|tiny_8k]
+    python bench.py [--steps K] [--warmup W] [--workload swap_1m|swap_1m_fp8|thresh_256k|ens_8k|tiny_8k]
                     [--no-cpu-baseline] [--copy-calibration]
 """
 import argparse
@@ -213,8 +213,8 @@ def main():
     del flush
 
     # ---- algorithmic bytes (per launch)
-    key_b = 4 if wl.key_dtype == "f32" else 2
-    kv_b = 4 if wl.kv_dtype == "f32" else 2
+    key_b = L.DTYPE_BYTES[wl.key_dtype]
+    kv_b = L.DTYPE_BYTES[wl.kv_dtype]
     score_bytes = wl.batch * wl.n_src * (wl.dk * key_b + 4)
     avg = {k: (ktimes[k][0] / ktimes[k][1] if ktimes[k][1] else 0.0) for k in KERNELS}
     score_gbs = score_bytes / (score_ms * 1e-3) / 1e9

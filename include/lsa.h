@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LSA_ABI_VERSION 3
+#define LSA_ABI_VERSION 4
 #define LSA_MAX_LAYERS 16
 #define LSA_MAX_BATCH 64
 
@@ -61,7 +61,11 @@ typedef enum lsa_status {
     LSA_ERR_UNSUPPORTED = 7      /* a valid shape this build has no kernel for */
 } lsa_status;
 
-typedef enum lsa_dtype { LSA_F32 = 0, LSA_BF16 = 1, LSA_F16 = 2 } lsa_dtype;
+/* LSA_FP8_E4M3 (OCP E4M3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals, no infinities, codes 0x7F / 0xFF NaN) is accepted for indexer keys
+ * only: [P1] technical details (memory layout and known limits) names fp8/int8
+ * indexer keys as the way to shrink the resident key cache. */
+typedef enum lsa_dtype { LSA_F32 = 0, LSA_BF16 = 1, LSA_F16 = 2, LSA_FP8_E4M3 = 3 } lsa_dtype;
 typedef enum lsa_ensemble { LSA_ENSEMBLE_MAX = 0, LSA_ENSEMBLE_MEAN = 1 } lsa_ensemble;
 typedef enum lsa_select_mode { LSA_SELECT_TOPK = 0, LSA_SELECT_THRESHOLD = 1 } lsa_select_mode;
 typedef enum lsa_cold_kind { LSA_COLD_HBM = 0, LSA_COLD_HOST = 1 } lsa_cold_kind;
@@ -120,8 +124,12 @@ lsa_status lsa_ctx_timing_read(lsa_ctx* ctx, double* ms /* host [LSA_K_COUNT] */
  *     score[j] = max_i s_i[j]                (LSA_ENSEMBLE_MAX), or
  *                (sum_i s_i[j]) / n_idx      (LSA_ENSEMBLE_MEAN, one IEEE division)
  * with -0 written as +0.  Accumulation is fp32 in an unspecified order, so the
- * result is exact whenever every partial sum is representable in fp32.
- *   keys   device [batch][n_keys][dk], key_dtype LSA_F32 or LSA_BF16, rows contiguous
+ * result is exact whenever every partial sum is representable in fp32.  Keys
+ * of every dtype enter as their exact values (an fp8 code decodes exactly),
+ * and each product with the fp32 query is exact before the accumulation.
+ *   keys   device [batch][n_keys][dk], key_dtype LSA_F32, LSA_BF16 or
+ *          LSA_FP8_E4M3 (one byte per element), rows contiguous; NaN codes
+ *          are not allowed
  *   n_valid host [batch] (0 <= n_valid[b] <= n_keys) or NULL for n_keys each
  *   q      device f32 [batch][n_idx][heads][dk]
  *   w      device f32 [batch][n_idx][heads]

@@ -32,8 +32,8 @@
 // epilogue: integer-max ReLU, head weights, a permlane32 swap for the other
 // half's heads, and the ensemble.  Tiles are taken per sequence, so the
 // queries, weights and buffer resources stay fixed in the inner loop.  The
-// grid is one 4-wave workgroup per CU (fewer when the scan is short), which
-// keeps every wave's share of tiles equal.
+// grid is one 4-wave workgroup per CU (two for fp8 keys; fewer when the scan
+// is short), which keeps every wave's share of tiles equal.
 #include "lsa_internal.hpp"
 
 namespace lsa {
@@ -48,11 +48,15 @@ constexpr int kSub = 32;           // keys per MFMA block (the B operand's colum
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// A wave tile is kNSub blocks of 32 keys -- 128 * DK bytes for every key type
-// (16 KB at DK 128), so the load pipeline is the same for fp32, bf16 and fp8.
+// A wave tile is kNSub blocks of 32 keys: 128 * DK bytes for fp32 and bf16
+// keys (16 KB at DK 128), 64 * DK bytes for fp8 keys.  The smaller fp8 tile
+// halves the load registers and accumulators, so an fp8 wave fits in 256
+// registers: two waves share a SIMD and one's fp8 decode (VALU) runs under
+// the other's MFMAs, and the score waves of the fused score+copy launch
+// (five waves per workgroup) need no spills.
 template <int DK, typename KT>
 struct Cfg {
-    static constexpr int kNSub = 4 / (int)sizeof(KT);
+    static constexpr int kNSub = sizeof(KT) == 1 ? 2 : 4 / (int)sizeof(KT);
     static constexpr int kTile = kSub * kNSub;               // keys per wave tile
     static constexpr int kRowBytes = DK * (int)sizeof(KT);
     static constexpr int kLdsStride = kRowBytes + 16;
@@ -330,8 +334,12 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
     }
 }
 
+// workgroups per CU: two for fp8 keys (registers and LDS fit two), else one
+template <typename KT>
+constexpr int kWgPerCu = sizeof(KT) == 1 ? 2 : 1;
+
 template <int DK, typename KT>
-__global__ __launch_bounds__(kThreads, 1) void fm_score_kernel(const ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, kWgPerCu<KT>) void fm_score_kernel(const ScoreArgs a) {
     fm_score_body<DK, KT>(a, blockIdx.x, gridDim.x);
 }
 
@@ -340,7 +348,7 @@ hipError_t launch_t(const ScoreArgs& a, int n_cu, hipStream_t s) {
     const int total = a.tile_start[a.batch];
     if (total == 0) return hipSuccess;
     int grid = (total + kWaves - 1) / kWaves;
-    if (grid > n_cu) grid = n_cu;
+    if (grid > n_cu * kWgPerCu<KT>) grid = n_cu * kWgPerCu<KT>;
     hipLaunchKernelGGL((fm_score_kernel<DK, KT>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
@@ -361,6 +369,10 @@ hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, 
         if (dk == 32) return launch_t<32, uint16_t>(a, n_cu, s);
         if (dk == 64) return launch_t<64, uint16_t>(a, n_cu, s);
         if (dk == 128) return launch_t<128, uint16_t>(a, n_cu, s);
+    } else if (key_dtype == LSA_FP8_E4M3) {
+        if (dk == 32) return launch_t<32, uint8_t>(a, n_cu, s);
+        if (dk == 64) return launch_t<64, uint8_t>(a, n_cu, s);
+        if (dk == 128) return launch_t<128, uint8_t>(a, n_cu, s);
     }
     return hipErrorInvalidValue;
 }

@@ -278,6 +278,10 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int p
         if (dk == 32) return launch_a<32, uint16_t>(sa, ca, ha, n_cu, s);
         if (dk == 64) return launch_a<64, uint16_t>(sa, ca, ha, n_cu, s);
         if (dk == 128) return launch_a<128, uint16_t>(sa, ca, ha, n_cu, s);
+    } else if (key_dtype == LSA_FP8_E4M3) {
+        if (dk == 32) return launch_a<32, uint8_t>(sa, ca, ha, n_cu, s);
+        if (dk == 64) return launch_a<64, uint8_t>(sa, ca, ha, n_cu, s);
+        if (dk == 128) return launch_a<128, uint8_t>(sa, ca, ha, n_cu, s);
     }
     return hipErrorInvalidValue;
 }

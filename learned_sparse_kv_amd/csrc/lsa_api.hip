@@ -35,7 +35,7 @@ lsa_status fail(lsa_status s, const char* fmt, ...) {
         if (e_ != hipSuccess) return fail(LSA_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
     } while (0)
 
-int elem_bytes(lsa_dtype d) { return d == LSA_F32 ? 4 : 2; }
+int elem_bytes(lsa_dtype d) { return d == LSA_F32 ? 4 : d == LSA_FP8_E4M3 ? 1 : 2; }
 bool row_dtype_ok(lsa_dtype d) { return d == LSA_F32 || d == LSA_BF16 || d == LSA_F16; }
 
 int n_cu_current() {
@@ -306,7 +306,8 @@ lsa_status score_args(const void* keys, lsa_dtype key_dtype, int32_t batch, int6
     if (!keys || !q || !w || !scores) return fail(LSA_ERR_INVALID_ARG, "lsa_score: NULL pointer");
     if (ens != LSA_ENSEMBLE_MAX && ens != LSA_ENSEMBLE_MEAN) return fail(LSA_ERR_INVALID_ARG, "ensemble %d", (int)ens);
     if (dk <= 0 || n_idx <= 0 || heads <= 0) return fail(LSA_ERR_INVALID_ARG, "dk, n_idx and heads must be positive");
-    if (key_dtype != LSA_F32 && key_dtype != LSA_BF16) return fail(LSA_ERR_UNSUPPORTED, "key dtype %d", (int)key_dtype);
+    if (key_dtype != LSA_F32 && key_dtype != LSA_BF16 && key_dtype != LSA_FP8_E4M3)
+        return fail(LSA_ERR_UNSUPPORTED, "key dtype %d (supported: F32, BF16, FP8_E4M3)", (int)key_dtype);
     if (dk != 32 && dk != 64 && dk != 128) return fail(LSA_ERR_UNSUPPORTED, "dk %d (supported: 32, 64, 128)", dk);
     if (n_idx > 4 || heads > 8) return fail(LSA_ERR_UNSUPPORTED, "n_idx %d x heads %d (supported: <= 4 x <= 8)", n_idx, heads);
     if ((uint64_t)n_keys * (uint64_t)dk * (uint64_t)elem_bytes(key_dtype) >= ((uint64_t)1 << 32))
@@ -321,8 +322,8 @@ lsa_status score_args(const void* keys, lsa_dtype key_dtype, int32_t batch, int6
     a->n_idx = n_idx;
     a->heads = heads;
     a->ensemble = ens;
-    // a wave tile is 128 * dk bytes of keys: 32 fp32, 64 bf16 or 128 fp8 keys
-    const int64_t tile_keys = 32 * (4 / elem_bytes(key_dtype));
+    // keys per wave tile: 32 fp32 keys, 64 bf16 or fp8 keys
+    const int64_t tile_keys = key_dtype == LSA_F32 ? 32 : 64;
     int tiles = 0;
     for (int b = 0; b < batch; ++b) {
         const int64_t nv = n_valid ? n_valid[b] : n_keys;

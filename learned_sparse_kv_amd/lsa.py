@@ -17,11 +17,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblsa.so")
 
-F32, BF16, F16 = 0, 1, 2
+F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
 ENS = {"max": 0, "mean": 1}
 MODE = {"topk": 0, "threshold": 1}
 COLD = {"hbm": 0, "host": 1}
-DTYPE = {"f32": F32, "bf16": BF16, "f16": F16}
+DTYPE = {"f32": F32, "bf16": BF16, "f16": F16, "fp8": FP8_E4M3}
 K_NAMES = ["score", "select", "stage", "gather", "attend", "combine"]
 MAX_LAYERS = 16
 
@@ -67,7 +67,7 @@ class KVSwapDesc(ctypes.Structure):
                 ("phys", P), ("n_rows", P), ("scale", f32), ("out", P)]
 
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _SIGS = {
     "lsa_compressed_cap": (i64, [i64, i32]),
@@ -165,6 +165,8 @@ def row_dtype_code(t) -> int:
         return BF16
     if t.dtype == torch.float16:
         return F16
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 

@@ -19,15 +19,18 @@ from . import lsa
 
 
 def to_device(x: np.ndarray, dtype: str, dev) -> torch.Tensor:
-    """Upload values already encoded for `dtype` (f32 array, or bf16/f16 16-bit codes)."""
+    """Upload values already encoded for `dtype` (f32 array, bf16/f16 16-bit codes
+    or fp8 E4M3 byte codes)."""
     if dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(dev).view(torch.float8_e4m3fn)
     t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
     return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
 
 
 def torch_dtype(dtype: str):
-    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.float8_e4m3fn}[dtype]
 
 
 class DeviceWorkload:

@@ -89,18 +89,40 @@ def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
     return h.view(np.uint16)
 
 
-DTYPE_CODES = {"f32": 0, "bf16": 1, "f16": 2}
-DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+def f32_to_fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """OCP E4M3 byte codes (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent field 0 is subnormal, m * 2^-9) of values that the format holds
+    exactly: every grid value here does.  Refuses anything else."""
+    x = np.asarray(x, dtype=np.float32)
+    sign = np.signbit(x).astype(np.uint8) << 7
+    a = np.abs(x).astype(np.float64)
+    m, e = np.frexp(a)                 # a = m * 2^e, 0.5 <= m < 1 (m = e = 0 for a = 0)
+    biased = e + 6                     # a = (2m) * 2^(e - 1), exponent field e - 1 + 7
+    normal = a >= 2.0 ** -6            # below: the subnormal range, zero included
+    frac = np.where(normal, (2.0 * m - 1.0) * 8.0, a * 512.0)
+    field = np.where(normal, biased, 0)
+    ok = (frac == np.round(frac)) & (frac >= 0) & (frac < 8) & (field <= 15) & np.isfinite(a)
+    ok &= ~((field == 15) & (frac == 7))          # 0x7F / 0xFF are NaN
+    if not np.all(ok):
+        raise ValueError("value not exactly representable in fp8 e4m3")
+    return (sign | (field.astype(np.uint8) << 3) | frac.astype(np.uint8)).astype(np.uint8)
+
+
+DTYPE_CODES = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3}
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
 
 
 def encode(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Store float32 grid values in the named storage dtype (f32 / bf16 / f16 bits)."""
+    """Store float32 grid values in the named storage dtype (f32 / bf16 / f16 bits /
+    fp8 E4M3 bytes)."""
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
     if dtype == "bf16":
         return f32_to_bf16_bits(x)
     if dtype == "f16":
         return f32_to_f16_bits(x)
+    if dtype == "fp8":
+        return f32_to_fp8_e4m3_bits(x)
     raise ValueError(dtype)
 
 
@@ -188,6 +210,10 @@ WORKLOADS = {
         gpu_chunks=1024, cold="host", dk=128, n_idx=3, heads=8, key_dtype="f32", kv_dtype="f32",
         mode="topk", k=512, ensemble="max", steps=256, drift=SWAP_1M_DRIFT),
 }
+# the 1M swap workload with its indexer keys stored as OCP fp8 E4M3 bytes: the
+# same grid values (exact in E4M3), so the same selections, at a quarter of the
+# key bytes
+WORKLOADS["swap_1m_fp8"] = WORKLOADS["swap_1m"].replace(name="swap_1m_fp8", key_dtype="fp8")
 
 
 # --------------------------------------------------------------------------

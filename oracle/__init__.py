@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "lsa_oracle.cpp")
 _BUILD = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD, "liblsa_oracle.so")
 
-DT = {"f32": 0, "bf16": 1, "f16": 2}
+DT = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3}
 ENS = {"max": 0, "mean": 1}
 MODE = {"topk": 0, "threshold": 1}
 ST_NOT_STORED = 4
@@ -84,7 +84,7 @@ def _c(a, dtype) -> np.ndarray:
 
 
 def _kv(a: np.ndarray, dtype: str) -> np.ndarray:
-    return _c(a, np.float32 if dtype == "f32" else np.uint16)
+    return _c(a, {"f32": np.float32, "fp8": np.uint8}.get(dtype, np.uint16))
 
 
 # ------------------------------------------------------------------ sizing --

@@ -30,7 +30,7 @@
 
 namespace {
 
-enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8_E4M3 = 3 };
 enum { ENS_MAX = 0, ENS_MEAN = 1 };
 enum { SEL_TOPK = 0, SEL_THRESHOLD = 1 };
 enum { ST_OK = 0, ST_NOT_STORED = 4 };
@@ -60,7 +60,27 @@ double bf16_to_double(uint16_t b) {
     return f;
 }
 
+// OCP 8-bit E4M3 -> double, from the format's definition (1 sign, 4 exponent
+// bits with bias 7, 3 fraction bits; exponent 0 = subnormal, frac * 2^-9; no
+// infinities, and exponent 15 with fraction 7 is NaN).  [P1] technical details
+// (known limits) names fp8 indexer keys as the next step after fp4.
+double fp8_e4m3_to_double(uint8_t c) {
+    const int sign = c >> 7;
+    const int expo = (c >> 3) & 15;
+    const int frac = c & 7;
+    double v;
+    if (expo == 0) {
+        v = std::ldexp((double)frac, -9);
+    } else if (expo == 15 && frac == 7) {
+        v = NAN;
+    } else {
+        v = std::ldexp((double)(8 + frac), expo - 10);
+    }
+    return sign ? -v : v;
+}
+
 double elem(const void* base, int dtype, int64_t i) {
+    if (dtype == DT_FP8_E4M3) return fp8_e4m3_to_double(((const uint8_t*)base)[i]);
     if (dtype == DT_F32) {
         float f;
         std::memcpy(&f, (const char*)base + 4 * i, 4);

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(lsa.EXPORTS)
-    assert L.lsa_abi_version() == lsa.ABI_VERSION == 3
+    assert L.lsa_abi_version() == lsa.ABI_VERSION == 4
 
 
 def test_closed_forms_match_oracle():
@@ -88,6 +88,7 @@ def test_pool_validation_errors_before_any_device_call():
     assert _create(_desc(topk=2000))[0] == 1
     assert _create(_desc(batch=0))[0] == 1
     assert _create(_desc(dtype=9))[0] == 7
+    assert _create(_desc(dtype=lsa.FP8_E4M3))[0] == 7   # fp8 is for indexer keys only
     # a caller-owned cold store must be device memory and hold every sequence
     assert _create(_desc(cold=1, cold_buf=0x2000))[0] == 1
     st, msg = _create(_desc(batch=2, kv_stride_b=1 << 20, cold_buf=0x2000, cold_stride_b=1024))
@@ -139,4 +140,9 @@ def test_score_and_select_argument_checks():
     assert L.lsa_score(0x10, 0, 1, 100, None, 64, 0x10, 0x10, 1, 9, 0, 0x10, None) == 7
     assert L.lsa_score(0x10, 0, 1, 100, None, 64, 0x10, 0x10, 1, 4, 5, 0x10, None) == 1
     assert L.lsa_score(None, 0, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 1
+    # key dtypes: f32, bf16 and fp8 E4M3; f16 keys and unknown codes are unsupported
+    assert L.lsa_score(0x10, lsa.F16, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
+    assert L.lsa_score(0x10, 9, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
+    # a sequence's keys must stay under 4 GiB: 2^25 keys x 128 bytes is the limit for fp8
+    assert L.lsa_score(0x10, lsa.FP8_E4M3, 1, 1 << 25, None, 128, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
     assert L.lsa_select(None, 0x10, 1, 100, None, 0, 8, 0.5, 0x10, 0x10, None) == 1

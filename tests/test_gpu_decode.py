@@ -62,6 +62,12 @@ def test_decode_mean_ensemble():
     run_decode(L.WORKLOADS["ens_8k"].replace(ensemble="mean"), 4)
 
 
+@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+def test_decode_quantized_keys(kd):
+    # indexer keys stored as bf16 or OCP fp8 E4M3 (exact for the grid values)
+    run_decode(L.WORKLOADS["ens_8k"].replace(key_dtype=kd), 4)
+
+
 def test_decode_forced_swap_tiny():
     # page 1 troubleshooting: 64-token context, ratio 4 -> 16 entries; 8 slots force swapping
     wl = L.WORKLOADS["tiny_8k"].replace(ctx=64, gpu_chunks=8, k=8)

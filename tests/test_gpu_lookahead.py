@@ -90,6 +90,34 @@ def test_lookahead_graph_replay_matches_eager(dw1m):
         say(f"  replay {rep} ok")
 
 
+def test_lookahead_fp8_keys_give_the_f32_bits(dw1m):
+    # the same grid keys stored as fp8 E4M3 score to the same bits on the bf16
+    # MFMA path, so the schedule stages the same rows and attends identically
+    fp8 = DeviceWorkload(L.WORKLOADS["swap_1m_fp8"])
+    fp8.make_steps(STEPS + 2)
+    runs = []
+    for dw in (dw1m, fp8):
+        dw.reset_pools()
+        dw.lookahead_prime(0)
+        res = []
+        for t in range(4):
+            cur = lsa.lookahead_buffer(dw.ctx)
+            dw.lookahead_step(t)
+            torch.cuda.synchronize()
+            phys, nr = dw.phys2[cur].cpu().numpy(), dw.n_rows2[cur].cpu().numpy()
+            # a row list is defined up to its count; entries past it are stale
+            rows = [phys[l, 0, :nr[l, 0]].copy() for l in range(phys.shape[0])]
+            res.append((rows, nr.copy(), bits(dw.out.cpu().numpy()).copy(), bits(dw.scores.cpu().numpy()).copy()))
+        runs.append(res)
+    for t in range(4):
+        a, b = runs[0][t], runs[1][t]
+        assert np.array_equal(a[1], b[1]), f"step {t}: row counts"
+        assert all(np.array_equal(x, y) for x, y in zip(a[0], b[0])), f"step {t}: rows"
+        assert np.array_equal(a[2], b[2]), f"step {t}: output"
+        assert np.array_equal(a[3], b[3]), f"step {t}: scores"
+    say("  fp8 lookahead ok")
+
+
 def test_lookahead_small_workloads_match_oracle():
     # 512 slots for top-512 (the stage of t+1 runs after step t's attention) and the
     # single-workgroup select path; the tiny workload is fully resident

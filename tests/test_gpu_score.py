@@ -37,6 +37,11 @@ CASES = [
     (3, 300, 64, 2, 5, "bf16", "mean"),
     (1, 1, 128, 1, 1, "f32", "max"),
     (1, 129, 128, 3, 8, "f32", "max"),
+    (2, 4133, 128, 3, 8, "fp8", "max"),     # fp8 keys, ragged tail
+    (3, 300, 64, 2, 5, "fp8", "mean"),
+    (1, 777, 32, 4, 8, "fp8", "max"),
+    (1, 1, 128, 1, 1, "fp8", "max"),
+    (1, 129, 128, 3, 8, "fp8", "mean"),
 ]
 
 
@@ -51,13 +56,63 @@ def test_score_matches_oracle(case):
     run(keys, kd, q, w, ens)
 
 
-def test_ragged_n_valid_per_sequence():
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
+def test_ragged_n_valid_per_sequence(kd):
     rng = np.random.default_rng(5)
     B, N, dk = 4, 300, 128
     keys = L.grid_uniform(rng, (B, N, dk))
     q = L.grid_uniform(rng, (B, 3, 8, dk))
     w = L.grid_uniform(rng, (B, 3, 8))
-    run(keys, "f32", q, w, "max", n_valid=[0, 1, 129, 300])
+    run(keys, kd, q, w, "max", n_valid=[0, 1, 129, 300])
+
+
+@pytest.mark.parametrize("dk", [32, 128])
+def test_fp8_every_code_in_every_column(dk):
+    """Each finite E4M3 code in each key column, alone in its key: with the
+    query all ones in two heads of weight +1 and -1 (second query negated),
+    score = ReLU(k) - ReLU(-k) = the decoded code, +0 for either zero."""
+    import torch as _t
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    n = codes.size * dk
+    keys = np.zeros((1, n, dk), np.uint8)
+    idx = np.arange(n)
+    keys[0, idx, idx % dk] = codes[idx // dk]
+    q = np.stack([np.ones(dk, np.float32), -np.ones(dk, np.float32)])[None, None]
+    w = np.array([[[1.0, -1.0]]], np.float32)
+    kt = torch.from_numpy(keys).to(DEV).view(torch.float8_e4m3fn)
+    s = torch.full((1, n), float("nan"), device=DEV)
+    lsa.score(kt, torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV), s, "max")
+    got = s.cpu().numpy()[0]
+    want = oracle.score(keys[0], "fp8", q[0], w[0], "max")
+    assert np.array_equal(bits(got), bits(want))
+    dec = _t.from_numpy(codes[idx // dk]).view(_t.float8_e4m3fn).float().numpy() + np.float32(0)
+    assert np.array_equal(got, dec)
+
+
+@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+def test_general_fp32_query_split_is_exact_per_product(kd):
+    """bf16 and fp8 keys meet a query of arbitrary fp32 values (not grid values),
+    which the kernel splits into three bf16 parts: every product is exact, so the
+    result differs from the exact score only by fp32 accumulation rounding."""
+    rng = np.random.default_rng(8)
+    B, N, dk, n_idx, H = 1, 1000, 128, 3, 8
+    keys = L.grid_uniform(rng, (B, N, dk))
+    q = rng.standard_normal((B, n_idx, H, dk)).astype(np.float32)
+    w = rng.random((B, n_idx, H)).astype(np.float32)
+    enc = L.encode(keys[0], kd)
+    kt = to_device(enc[None], kd, DEV)
+    s = torch.zeros((B, N), device=DEV)
+    lsa.score(kt, torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV), s, "max")
+    got = s.cpu().numpy()[0].astype(np.float64)
+    want = oracle.score(enc, kd, q[0], w[0], "max").astype(np.float64)
+    # bound: 2 * dk ulps of the absolute-value score, per indexer
+    absum = oracle.score(np.abs(keys[0]), "f32", np.abs(q[0]), w[0], "max").astype(np.float64)
+    assert np.all(np.abs(got - want) <= 2 * dk * 2.0 ** -24 * absum + 1e-30)
+    # and grid queries and weights (exact split: mid = lo = 0; exact sums) are bit-exact
+    qg = L.grid_uniform(rng, (B, n_idx, H, dk))
+    wg = L.grid_uniform(rng, (B, n_idx, H))
+    lsa.score(kt, torch.from_numpy(qg).to(DEV), torch.from_numpy(wg).to(DEV), s, "max")
+    assert np.array_equal(bits(s.cpu().numpy()[0]), bits(oracle.score(enc, kd, qg[0], wg[0], "max")))
 
 
 def test_all_negative_dots_give_positive_zero():
@@ -72,7 +127,7 @@ def test_all_negative_dots_give_positive_zero():
         assert np.all(bits(s.cpu().numpy()) == 0)
 
 
-@pytest.mark.parametrize("name", ["thresh_256k", "swap_1m"])
+@pytest.mark.parametrize("name", ["thresh_256k", "swap_1m", "swap_1m_fp8"])
 def test_full_size_workload_scores(name):
     wl = L.WORKLOADS[name]
     say(f"full-size score {name}: B={wl.batch} N={wl.n_src}")

@@ -156,6 +156,29 @@ def test_bf16_and_f16_storage_decode():
     assert np.array_equal(e, vals.astype(np.float32))
 
 
+def test_fp8_e4m3_storage_decode():
+    """Every finite OCP E4M3 code decodes to torch's float8_e4m3fn value and to
+    the format's defining values; grid keys stored as fp8 score as in fp32."""
+    import torch
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    one = np.ones((1, 1), np.float32)
+    pos = oracle.score(codes.reshape(-1, 1), "fp8", np.ones((1, 1, 1), np.float32), one)
+    neg = oracle.score(codes.reshape(-1, 1), "fp8", -np.ones((1, 1, 1), np.float32), one)
+    dec = (pos - neg).astype(np.float64)          # ReLU(k) - ReLU(-k) = k
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(dec, want)
+    by_code = dict(zip(codes.tolist(), dec.tolist()))
+    # subnormals m * 2^-9, smallest normal 2^-6, 1.0, the largest finite 448
+    assert by_code[0x01] == 2.0 ** -9 and by_code[0x07] == 7 * 2.0 ** -9
+    assert by_code[0x08] == 2.0 ** -6 and by_code[0x38] == 1.0 and by_code[0xB8] == -1.0
+    assert by_code[0x7E] == 448.0 and by_code[0x33] == 0.6875
+    rng = np.random.default_rng(15)
+    keys = L.grid_uniform(rng, (64, 16))
+    q = L.grid_uniform(rng, (3, 8, 16))
+    w = L.grid_uniform(rng, (3, 8))
+    assert np.array_equal(oracle.score(L.f32_to_fp8_e4m3_bits(keys), "fp8", q, w), oracle.score(keys, "f32", q, w))
+
+
 def test_n_valid_prefix():
     rng = np.random.default_rng(14)
     keys = L.grid_uniform(rng, (100, 16))
