@@ -115,6 +115,26 @@ lsa_status lsa_ctx_set_timing(lsa_ctx* ctx, int32_t on);
 lsa_status lsa_ctx_timing_read(lsa_ctx* ctx, double* ms /* host [LSA_K_COUNT] */,
                                int64_t* launches /* host [LSA_K_COUNT] */);
 
+/* ------------------------------------------------------------- projection --
+ * [P1] architecture overview: the decode token's hidden state (hidden[4096])
+ * feeds the three scorers.  Each indexer i maps it linearly to its query heads
+ * and head weights, the (q, w) that lsa_score takes:
+ *     q[b,i,h,t] = sum_c wq[i,h,t,c] * hidden[b,c]
+ *     w[b,i,h]   = sum_c ww[i,h,c]   * hidden[b,c]
+ * Accumulation is fp32 in an unspecified order, so the result is exact
+ * whenever every partial sum is representable in fp32.
+ *   hidden  device f32 [batch][d_model], finite, 16-byte aligned
+ *   wq      device [n_idx][heads][dk][d_model], w_dtype LSA_F32 or LSA_BF16
+ *   ww      device [n_idx][heads][d_model], same dtype
+ *   q       device f32 [batch][n_idx][heads][dk]
+ *   w       device f32 [batch][n_idx][heads]
+ * Supported: d_model a multiple of 8 and at most 16384; 1 <= batch <=
+ * LSA_MAX_BATCH; n_idx * heads * (dk + 1) < 2^31.  Weight rows are read once
+ * per four sequences. */
+lsa_status lsa_project(const float* hidden, int32_t batch, int32_t d_model, const void* wq, const void* ww,
+                       lsa_dtype w_dtype, int32_t n_idx, int32_t heads, int32_t dk, float* q, float* w,
+                       lsa_stream_t stream);
+
 /* ------------------------------------------------------------------ score --
  * [P1] architecture: 3 scorers read the shared indexer keys and are combined
  * by an ensemble (FLASHMEMORY_ENSEMBLE=max|mean); [P2] LSA section: memory

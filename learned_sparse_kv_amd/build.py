@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblsa.so")
 SOURCES = ["fm_score.hip", "fm_select.hip", "kv_stage.hip", "lsa_attend.hip", "lowrank.hip", "attend_kv.hip",
-           "lookahead.hip", "lsa_api.hip"]
+           "lookahead.hip", "lsa_project.hip", "lsa_api.hip"]
 ARCH = "gfx950"
 # packed-fp32 instructions are switched off for every HIP source
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

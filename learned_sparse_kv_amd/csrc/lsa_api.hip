@@ -448,6 +448,32 @@ lsa_status attend_timed(lsa_ctx* ctx, const AttendArgs& a, hipStream_t s) {
 
 extern "C" {
 
+lsa_status lsa_project(const float* hidden, int32_t batch, int32_t d_model, const void* wq, const void* ww,
+                       lsa_dtype w_dtype, int32_t n_idx, int32_t heads, int32_t dk, float* q, float* w,
+                       lsa_stream_t stream) {
+    if (!hidden || !wq || !ww || !q || !w) return fail(LSA_ERR_INVALID_ARG, "lsa_project: NULL pointer");
+    if (batch < 1 || batch > LSA_MAX_BATCH) return fail(LSA_ERR_INVALID_ARG, "batch %d not in [1, %d]", batch, LSA_MAX_BATCH);
+    if (n_idx < 1 || heads < 1 || dk < 1) return fail(LSA_ERR_INVALID_ARG, "n_idx, heads and dk must be positive");
+    if (w_dtype != LSA_F32 && w_dtype != LSA_BF16)
+        return fail(LSA_ERR_UNSUPPORTED, "weight dtype %d (supported: F32, BF16)", (int)w_dtype);
+    if (d_model < 8 || d_model % 8 != 0 || d_model > 16384)
+        return fail(LSA_ERR_UNSUPPORTED, "d_model %d (supported: multiples of 8 up to 16384)", d_model);
+    if ((int64_t)n_idx * heads * (dk + 1) >= ((int64_t)1 << 31))
+        return fail(LSA_ERR_UNSUPPORTED, "too many projection rows");
+    if (((uintptr_t)hidden & 15) != 0) return fail(LSA_ERR_INVALID_ARG, "hidden must be 16-byte aligned");
+    ProjectArgs a;
+    a.hidden = hidden;
+    a.wq = wq;
+    a.ww = ww;
+    a.q = q;
+    a.w = w;
+    a.d_model = d_model;
+    a.q_rows = n_idx * heads * dk;
+    a.w_rows = n_idx * heads;
+    HIPTRY(launch_project(a, w_dtype, batch, n_cu_current(), (hipStream_t)stream));
+    return LSA_OK;
+}
+
 lsa_status lsa_score(const void* keys, lsa_dtype key_dtype, int32_t batch, int64_t n_keys,
                      const int64_t* n_valid, int32_t dk, const float* q, const float* w, int32_t n_idx,
                      int32_t heads, lsa_ensemble ensemble, float* scores, lsa_stream_t stream) {

@@ -103,6 +103,17 @@ constexpr int kSelShift = 21;         // bin = order_key(score) >> kSelShift
 constexpr int kSelKeepCap = 8192;     // entries (above + in the boundary bucket) resolved in LDS
 constexpr int kSelSingle = 32768;     // segments up to this length use one workgroup
 
+// Query/weight projection of the hidden state (lsa_project.hip).
+struct ProjectArgs {
+    const float* hidden;    // [batch][d_model]
+    const void* wq;         // [q_rows][d_model]
+    const void* ww;         // [w_rows][d_model]
+    float* q;               // [batch][q_rows]
+    float* w;               // [batch][w_rows]
+    int32_t d_model, q_rows, w_rows;
+};
+hipError_t launch_project(const ProjectArgs& a, int w_dtype, int batch, int n_cu, hipStream_t s);
+
 struct ScoreArgs {
     const void* keys;
     const float* q;

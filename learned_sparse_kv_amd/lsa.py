@@ -83,6 +83,7 @@ _SIGS = {
     "lsa_ctx_reserve": (i32, [P, u64]),
     "lsa_ctx_set_timing": (i32, [P, i32]),
     "lsa_ctx_timing_read": (i32, [P, P, P]),
+    "lsa_project": (i32, [P, i32, i32, P, P, i32, i32, i32, i32, P, P, P]),
     "lsa_score": (i32, [P, i32, i32, i64, P, i32, P, P, i32, i32, i32, P, P]),
     "lsa_select": (i32, [P, P, i32, i64, P, i32, i32, f64, P, P, P]),
     "lsa_pool_rows": (i64, [ctypes.POINTER(PoolDesc)]),
@@ -222,6 +223,22 @@ class Ctx:
         n = (i64 * 6)()
         _check(lib().lsa_ctx_timing_read(self.h, ctypes.cast(ms, P), ctypes.cast(n, P)))
         return {K_NAMES[i]: (ms[i], n[i]) for i in range(6)}
+
+
+# ----------------------------------------------------------- projection
+def project(hidden, wq, ww, q, w, stream=None) -> None:
+    """hidden [B][d_model] f32, wq [n_idx][H][dk][d_model] and ww [n_idx][H][d_model]
+    (f32/bf16) -> q [B][n_idx][H][dk] f32, w [B][n_idx][H] f32."""
+    for t, n in ((hidden, "hidden"), (wq, "wq"), (ww, "ww"), (q, "q"), (w, "w")):
+        _dev(t, n)
+    B, d_model = hidden.shape
+    n_idx, H, dk, d2 = wq.shape
+    if d2 != d_model or tuple(ww.shape) != (n_idx, H, d_model) or ww.dtype != wq.dtype:
+        raise ValueError("projection weight shapes or dtypes do not match")
+    if tuple(q.shape) != (B, n_idx, H, dk) or tuple(w.shape) != (B, n_idx, H):
+        raise ValueError("projection output shapes do not match")
+    _check(lib().lsa_project(_ptr(hidden), B, d_model, _ptr(wq), _ptr(ww), row_dtype_code(wq), n_idx, H, dk,
+                             _ptr(q), _ptr(w), _stream(stream)))
 
 
 # ---------------------------------------------------------------- score

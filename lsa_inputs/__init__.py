@@ -302,6 +302,29 @@ def attn_query(wl: Workload, layer: int, b: int, step: int) -> np.ndarray:
     return grid_uniform(rng_for(wl.base_seed, "aq", layer, b, step), (wl.hq, wl.kv_dim))
 
 
+# the decode token's hidden state and the indexers' projection weights: the
+# hidden width of the pages' model (hidden[4096]); weights on a 1/512 grid in
+# [-1/64, 1/64], so every product is a multiple of 2^-12 and every partial sum
+# of a projected value (at most 64 in magnitude) is exact in fp32
+D_MODEL = 4096
+PROJ_STEP = 1.0 / 512
+PROJ_MAX = 1.0 / 64
+
+
+def projection_weights(wl: Workload, d_model: int = D_MODEL):
+    """wq [n_idx][H][dk][d_model] and ww [n_idx][H][d_model], float32 grid values."""
+    wq = grid_uniform(rng_for(wl.base_seed, "wq"), (wl.n_idx, wl.heads, wl.dk, d_model),
+                      lo=-PROJ_MAX, hi=PROJ_MAX, step=PROJ_STEP)
+    ww = grid_uniform(rng_for(wl.base_seed, "ww"), (wl.n_idx, wl.heads, d_model),
+                      lo=-PROJ_MAX, hi=PROJ_MAX, step=PROJ_STEP)
+    return wq, ww
+
+
+def hidden_state(wl: Workload, b: int, step: int, d_model: int = D_MODEL) -> np.ndarray:
+    """The decode token's hidden state [d_model] of sequence b at a step, on the 1/8 grid."""
+    return grid_uniform(rng_for(wl.base_seed, "hidden", b, step), (d_model,))
+
+
 def indexer_query_steps(wl: Workload, b: int, steps: int):
     """Indexer queries of steps 0..steps-1, as (q [steps][n_idx][H][dk], w [steps][n_idx][H])."""
     qs, ws = [], []

@@ -55,6 +55,7 @@ def lib():
             "oracle_max_capacity": (i32, [i32, i32]),
             "oracle_swap_enabled": (i32, [i64, i32]),
             "oracle_score": (None, [P, i32, i64, i32, P, P, i32, i32, i32, P]),
+            "oracle_project": (None, [P, i32, i32, P, P, i32, i32, i32, i32, P, P]),
             "oracle_threshold_float": (f32, [f64]),
             "oracle_select": (i32, [P, i64, i32, i32, f64, P]),
             "oracle_ratio_map": (i32, [P, i32, i32, i32, P]),
@@ -117,6 +118,23 @@ def score(keys: np.ndarray, key_dtype: str, q: np.ndarray, w: np.ndarray,
     e = np.zeros(n, np.float32)
     lib().oracle_score(_p(keys), DT[key_dtype], n, dk, _p(q), _p(w), n_idx, H, ENS[ensemble], _p(e))
     return e
+
+
+# -------------------------------------------------------------- projection --
+def project(hidden: np.ndarray, wq: np.ndarray, ww: np.ndarray, w_dtype: str = "f32"):
+    """hidden [B][d_model] f32, wq [n_idx][H][dk][d_model] and ww [n_idx][H][d_model]
+    (f32 or 16-bit codes) -> q [B][n_idx][H][dk], w [B][n_idx][H] (f32)."""
+    hidden = _c(hidden, np.float32)
+    wq = _kv(wq, w_dtype)
+    ww = _kv(ww, w_dtype)
+    B, d_model = hidden.shape
+    n_idx, H, dk, d2 = wq.shape
+    if d2 != d_model or ww.shape != (n_idx, H, d_model):
+        raise ValueError("projection shapes do not match")
+    q = np.zeros((B, n_idx, H, dk), np.float32)
+    w = np.zeros((B, n_idx, H), np.float32)
+    lib().oracle_project(_p(hidden), B, d_model, _p(wq), _p(ww), DT[w_dtype], n_idx, H, dk, _p(q), _p(w))
+    return q, w
 
 
 # ------------------------------------------------------------------ select --

@@ -130,6 +130,33 @@ int32_t oracle_max_capacity(int32_t window, int32_t gpu_chunks) { return window 
 // a layer whose compressed_cap <= gpu_chunks is kept fully resident (no swap).
 int32_t oracle_swap_enabled(int64_t cap, int32_t gpu_chunks) { return cap > gpu_chunks ? 1 : 0; }
 
+// ------------------------------------------------------------ projection ---
+// [P1] architecture overview: the decode token's hidden state (hidden[4096])
+// feeds the three scorers.  Reading (the pages give no formula): every
+// indexer i maps the hidden vector linearly to its H query heads and its H
+// head weights,
+//     q[i,h,t] = sum_c Wq[i,h,t,c] * hidden[c],   w[i,h] = sum_c Ww[i,h,c] * hidden[c],
+// summed in double and rounded once to float.
+// hidden: [B][d_model] f32; wq: [n_idx][H][dk][d_model] and ww: [n_idx][H][d_model]
+// in w_dtype; q: [B][n_idx][H][dk]; w: [B][n_idx][H].
+void oracle_project(const float* hidden, int32_t B, int32_t d_model, const void* wq, const void* ww,
+                    int32_t w_dtype, int32_t n_idx, int32_t H, int32_t dk, float* q, float* w) {
+    const int64_t q_rows = (int64_t)n_idx * H * dk, w_rows = (int64_t)n_idx * H;
+    for (int32_t b = 0; b < B; ++b) {
+        const float* x = hidden + (int64_t)b * d_model;
+        for (int64_t r = 0; r < q_rows; ++r) {
+            double acc = 0.0;
+            for (int32_t c = 0; c < d_model; ++c) acc += elem(wq, w_dtype, r * d_model + c) * (double)x[c];
+            q[(int64_t)b * q_rows + r] = (float)acc;
+        }
+        for (int64_t r = 0; r < w_rows; ++r) {
+            double acc = 0.0;
+            for (int32_t c = 0; c < d_model; ++c) acc += elem(ww, w_dtype, r * d_model + c) * (double)x[c];
+            w[(int64_t)b * w_rows + r] = (float)acc;
+        }
+    }
+}
+
 // ----------------------------------------------------------------- score ---
 // [P1] architecture overview: the hidden state feeds 3 scorers which read the
 // shared indexer_kv_cache and are combined by an ensemble (max or mean).

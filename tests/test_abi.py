@@ -140,6 +140,12 @@ def test_score_and_select_argument_checks():
     assert L.lsa_score(0x10, 0, 1, 100, None, 64, 0x10, 0x10, 1, 9, 0, 0x10, None) == 7
     assert L.lsa_score(0x10, 0, 1, 100, None, 64, 0x10, 0x10, 1, 4, 5, 0x10, None) == 1
     assert L.lsa_score(None, 0, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 1
+    # projection: d_model a multiple of 8, batch in range, f32/bf16 weights, aligned hidden
+    assert L.lsa_project(0x10, 1, 4100, 0x10, 0x10, 1, 3, 8, 128, 0x10, 0x10, None) == 7
+    assert L.lsa_project(0x10, 0, 4096, 0x10, 0x10, 1, 3, 8, 128, 0x10, 0x10, None) == 1
+    assert L.lsa_project(0x10, 1, 4096, 0x10, 0x10, lsa.FP8_E4M3, 3, 8, 128, 0x10, 0x10, None) == 7
+    assert L.lsa_project(0x14, 1, 4096, 0x10, 0x10, 1, 3, 8, 128, 0x10, 0x10, None) == 1
+    assert L.lsa_project(None, 1, 4096, 0x10, 0x10, 1, 3, 8, 128, 0x10, 0x10, None) == 1
     # key dtypes: f32, bf16 and fp8 E4M3; f16 keys and unknown codes are unsupported
     assert L.lsa_score(0x10, lsa.F16, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
     assert L.lsa_score(0x10, 9, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
