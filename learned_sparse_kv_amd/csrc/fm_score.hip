@@ -121,12 +121,13 @@ struct QOperand<DK, false> {
     bf16x8 hi[DK / 16], mid[DK / 16], lo[DK / 16];
 };
 
-// Two fp8 (OCP E4M3) codes -> their exact bf16 values, packed: the hardware
-// conversion to fp32 is exact, and every E4M3 value is exact in bf16.
+// Two fp8 (OCP E4M3) codes -> their exact bf16 values, packed, in one
+// instruction (scale 1): every E4M3 value, subnormals included, is a bf16
+// normal or zero, so the conversion does not round.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <bool HIGH_PAIR>
 __device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
-    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH_PAIR);
-    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH_PAIR));
 }
 
 // With HIST, every stored score that the select would count (a valid entry;
