@@ -15,7 +15,7 @@ Prints ONE JSON line.  Per-kernel times come from HIP events recorded on the
 launch stream inside the timed region; the CPU baseline is the plain oracle
 timed on a bounded sample of the same steps.
 
-    python bench.py [--steps K] [--warmup W] [--workload swap_1m|swap_1m_fp8|thresh_256k|ens_8k|tiny_8k]
+    python bench.py [--steps K] [--warmup W] [--workload swap_1m|swap_1m_fp8|swap_1m_mxfp4|swap_1m_mxint8|thresh_256k|ens_8k|tiny_8k]
                     [--no-cpu-baseline] [--copy-calibration]
 """
 import argparse
@@ -187,10 +187,10 @@ def main():
     st = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_last = Wm + K - 1
-    lsa.score(dw.keys, dw.q_idx[t_last], dw.w_idx[t_last], dw.scores, ensemble=wl.ensemble)
+    lsa.score(dw.keys, dw.q_idx[t_last], dw.w_idx[t_last], dw.scores, ensemble=wl.ensemble, key_scales=dw.key_scales)
     ev0.record(st)
     for _ in range(R):
-        lsa.score(dw.keys, dw.q_idx[t_last], dw.w_idx[t_last], dw.scores, ensemble=wl.ensemble)
+        lsa.score(dw.keys, dw.q_idx[t_last], dw.w_idx[t_last], dw.scores, ensemble=wl.ensemble, key_scales=dw.key_scales)
     ev1.record(st)
     torch.cuda.synchronize()
     score_ms = ev0.elapsed_time(ev1) / R
@@ -206,7 +206,7 @@ def main():
     for e0, e1 in evs:
         flush.sum()
         e0.record(st)
-        lsa.score(dw.keys, dw.q_idx[t_last], dw.w_idx[t_last], dw.scores, ensemble=wl.ensemble)
+        lsa.score(dw.keys, dw.q_idx[t_last], dw.w_idx[t_last], dw.scores, ensemble=wl.ensemble, key_scales=dw.key_scales)
         e1.record(st)
     torch.cuda.synchronize()
     cold_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)[RC // 2]
@@ -218,9 +218,10 @@ def main():
     del flush
 
     # ---- algorithmic bytes (per launch)
-    key_b = L.DTYPE_BYTES[wl.key_dtype]
+    # a key row (plus its E8M0 block scales for the MX dtypes) read, a score written
+    key_row = wl.dk * L.DTYPE_BYTES[wl.key_dtype] + (wl.dk // 32 if wl.key_dtype in L.MX_DTYPES else 0)
     kv_b = L.DTYPE_BYTES[wl.kv_dtype]
-    score_bytes = wl.batch * wl.n_src * (wl.dk * key_b + 4)
+    score_bytes = int(wl.batch * wl.n_src * (key_row + 4))
     avg = {k: (ktimes[k][0] / ktimes[k][1] if ktimes[k][1] else 0.0) for k in KERNELS}
     score_gbs = score_bytes / (score_ms * 1e-3) / 1e9
     hits = sum(s1["hits"] - s0["hits"] for s0, s1 in zip(stats0, stats1))

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LSA_ABI_VERSION 4
+#define LSA_ABI_VERSION 5
 #define LSA_MAX_LAYERS 16
 #define LSA_MAX_BATCH 64
 
@@ -61,11 +61,21 @@ typedef enum lsa_status {
     LSA_ERR_UNSUPPORTED = 7      /* a valid shape this build has no kernel for */
 } lsa_status;
 
-/* LSA_FP8_E4M3 (OCP E4M3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
- * subnormals, no infinities, codes 0x7F / 0xFF NaN) is accepted for indexer keys
- * only: [P1] technical details (memory layout and known limits) names fp8/int8
- * indexer keys as the way to shrink the resident key cache. */
-typedef enum lsa_dtype { LSA_F32 = 0, LSA_BF16 = 1, LSA_F16 = 2, LSA_FP8_E4M3 = 3 } lsa_dtype;
+/* Key-only formats.  [P1] technical details (memory layout and known limits):
+ * the indexer keys are fp4 today, and fp8/int8 keys are the way to shrink the
+ * resident key cache.
+ *   LSA_FP8_E4M3  OCP E4M3: 1 sign, 4 exponent bits with bias 7, 3 mantissa
+ *                 bits, subnormals, no infinities, codes 0x7F / 0xFF NaN.
+ *   LSA_MXFP4     OCP MX FP4: E2M1 codes (1 sign, 2 exponent bits with bias 1,
+ *                 1 mantissa bit: +-{0, .5, 1, 1.5, 2, 3, 4, 6}), two per byte,
+ *                 element 2i in bits 0-3 of byte i.
+ *   LSA_MXINT8    OCP MX INT8: two's-complement int8 codes with an implicit
+ *                 scale of 2^-6 (value code/64).
+ * The MX formats carry one E8M0 scale (unsigned byte s, value 2^(s-127); 255
+ * is NaN and not allowed) per 32 consecutive elements of a key. */
+typedef enum lsa_dtype {
+    LSA_F32 = 0, LSA_BF16 = 1, LSA_F16 = 2, LSA_FP8_E4M3 = 3, LSA_MXFP4 = 4, LSA_MXINT8 = 5
+} lsa_dtype;
 typedef enum lsa_ensemble { LSA_ENSEMBLE_MAX = 0, LSA_ENSEMBLE_MEAN = 1 } lsa_ensemble;
 typedef enum lsa_select_mode { LSA_SELECT_TOPK = 0, LSA_SELECT_THRESHOLD = 1 } lsa_select_mode;
 typedef enum lsa_cold_kind { LSA_COLD_HBM = 0, LSA_COLD_HOST = 1 } lsa_cold_kind;
@@ -145,18 +155,23 @@ lsa_status lsa_project(const float* hidden, int32_t batch, int32_t d_model, cons
  *                (sum_i s_i[j]) / n_idx      (LSA_ENSEMBLE_MEAN, one IEEE division)
  * with -0 written as +0.  Accumulation is fp32 in an unspecified order, so the
  * result is exact whenever every partial sum is representable in fp32.  Keys
- * of every dtype enter as their exact values (an fp8 code decodes exactly),
- * and each product with the fp32 query is exact before the accumulation.
- *   keys   device [batch][n_keys][dk], key_dtype LSA_F32, LSA_BF16 or
- *          LSA_FP8_E4M3 (one byte per element), rows contiguous; NaN codes
- *          are not allowed
+ * of every dtype enter as their exact values (an fp8 code decodes exactly, an
+ * MX element is its code times its block scale), and each product with the
+ * fp32 query is exact before the accumulation.
+ *   keys   device [batch][n_keys][dk] elements, rows contiguous, key_dtype
+ *          LSA_F32, LSA_BF16, LSA_FP8_E4M3 (one byte per element), LSA_MXFP4
+ *          (dk/2 bytes per key) or LSA_MXINT8 (dk bytes); NaN codes are not
+ *          allowed
+ *   key_scales  device u8 [batch][n_keys][dk/32] E8M0 block scales for the MX
+ *          dtypes, with 2 <= s <= 252 (every scaled element then is a bf16
+ *          normal or zero); ignored (may be NULL) otherwise
  *   n_valid host [batch] (0 <= n_valid[b] <= n_keys) or NULL for n_keys each
  *   q      device f32 [batch][n_idx][heads][dk]
  *   w      device f32 [batch][n_idx][heads]
  *   scores device f32 [batch][n_keys]; entries j >= n_valid[b] are not written
- * Supported: dk in {32, 64, 128}; 1 <= n_idx <= 4; 1 <= heads <= 8;
+ * Supported: dk in {32, 64, 128} (64 or 128 for LSA_MXFP4); 1 <= n_idx <= 4; 1 <= heads <= 8;
  * 1 <= batch <= LSA_MAX_BATCH; n_keys * dk * sizeof(key) < 2^32 per sequence. */
-lsa_status lsa_score(const void* keys, lsa_dtype key_dtype, int32_t batch, int64_t n_keys,
+lsa_status lsa_score(const void* keys, lsa_dtype key_dtype, const uint8_t* key_scales, int32_t batch, int64_t n_keys,
                      const int64_t* n_valid, int32_t dk, const float* q, const float* w,
                      int32_t n_idx, int32_t heads, lsa_ensemble ensemble, float* scores,
                      lsa_stream_t stream);
@@ -304,7 +319,8 @@ lsa_status lsa_attend(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dt
  * over window + selected.  All layers' pools must share `batch`. */
 typedef struct lsa_step_desc {
     /* scoring of the shared source layer (see lsa_score) */
-    const void* keys; lsa_dtype key_dtype; int64_t n_keys; const int64_t* n_valid; int32_t dk;
+    const void* keys; lsa_dtype key_dtype; const uint8_t* key_scales; int64_t n_keys; const int64_t* n_valid;
+    int32_t dk;
     const float* q_idx; const float* w_idx; int32_t n_idx; int32_t heads; lsa_ensemble ensemble;
     /* selection (see lsa_select); k is lowered to the smallest swapping pool's
        gpu_chunks when that pool allows top-k reduction */

@@ -48,22 +48,43 @@ constexpr int kSub = 32;           // keys per MFMA block (the B operand's colum
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// A wave tile is kNSub blocks of 32 keys: 128 * DK bytes for fp32 and bf16
-// keys (16 KB at DK 128), 64 * DK bytes for fp8 keys.  The smaller fp8 tile
-// halves the load registers and accumulators, so an fp8 wave fits in 256
-// registers: two waves share a SIMD and one's fp8 decode (VALU) runs under
-// the other's MFMAs, and the score waves of the fused score+copy launch
-// (five waves per workgroup) need no spills.
+// Key storage formats: float, uint16_t (bf16 bits), uint8_t (fp8 E4M3), and
+// the two OCP MX formats, which carry one E8M0 scale per 32 elements of a key.
+struct mxfp4_tag {};    // E2M1 codes, two per byte, element 2i in the low nibble
+struct mxint8_tag {};   // int8 codes with an implicit 2^-6
+template <typename KT>
+struct KeyFmt {
+    static constexpr int kBits = 8 * (int)sizeof(KT);
+    static constexpr bool kMX = false;
+};
+template <>
+struct KeyFmt<mxfp4_tag> {
+    static constexpr int kBits = 4;
+    static constexpr bool kMX = true;
+};
+template <>
+struct KeyFmt<mxint8_tag> {
+    static constexpr int kBits = 8;
+    static constexpr bool kMX = true;
+};
+
+// A wave tile is kNSub blocks of 32 keys: 32 fp32 keys (128 * DK bytes), 64
+// keys of every narrower format.  The 64-key tile of the one-byte and fp4
+// formats keeps a wave within 256 registers, so two waves share a SIMD (one's
+// decode VALU runs under the other's MFMAs) and the score waves of the fused
+// score+copy launch (five waves per workgroup) need no spills.
 template <int DK, typename KT>
 struct Cfg {
-    static constexpr int kNSub = sizeof(KT) == 1 ? 2 : 4 / (int)sizeof(KT);
+    static constexpr int kBits = KeyFmt<KT>::kBits;
+    static constexpr bool kMX = KeyFmt<KT>::kMX;
+    static constexpr int kNSub = kBits == 32 ? 1 : 2;
     static constexpr int kTile = kSub * kNSub;               // keys per wave tile
-    static constexpr int kRowBytes = DK * (int)sizeof(KT);
+    static constexpr int kRowBytes = DK * kBits / 8;
     static constexpr int kLdsStride = kRowBytes + 16;
     static constexpr int kTileBytes = kTile * kRowBytes;
     static constexpr int kLoads = kTileBytes / (64 * 16);      // 16-byte loads per lane
     static constexpr int kHalf = DK / 2;                     // elements of a key row per lane
-    static constexpr int kHalfBytes = kHalf * (int)sizeof(KT);
+    static constexpr int kHalfBytes = kRowBytes / 2;
     static constexpr int kReads = kHalfBytes / 16;           // ds_read_b128 per lane and block
     static constexpr int kSteps = kNSub * kReads;            // read steps per tile
     static_assert(kTileBytes % (64 * 16) == 0, "tile must split into 16-byte loads");
@@ -130,6 +151,38 @@ __device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH_PAIR));
 }
 
+// Two fp4 (E2M1) codes of byte SEL of w, times the scale, as packed bf16: exact
+// while the scaled values are bf16 normals or zero.
+template <int SEL>
+__device__ inline uint32_t fp4x2_to_bf16x2(uint32_t w, float scale) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
+}
+
+// Two int8 codes (bytes 2K and 2K+1 of w) times sf, as packed bf16.  A code c
+// is taken as the unsigned byte of c + 128 (the sign bit flipped), so
+// (c + 128) * sf - 128 * sf = c * sf in one fused multiply-add with no
+// rounding (sf is a power of two); the product has at most 8 significant bits
+// and so is exact in bf16.
+template <int K>
+__device__ inline uint32_t i8x2_to_bf16x2(uint32_t w, float sf, float off) {
+    const uint32_t x = w ^ 0x80808080u;
+    const float f0 = fmaf((float)((x >> (16 * K)) & 0xFFu), sf, off);
+    const float f1 = fmaf((float)((x >> (16 * K + 8)) & 0xFFu), sf, off);
+    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+// The E8M0 scale bytes of one key (DK/32 of them), as the low bytes of a word.
+template <int DK>
+__device__ inline uint32_t load_scales(__amdgpu_buffer_rsrc_t r, int key) {
+    const uint32_t off = (uint32_t)key * (DK / 32);
+    if constexpr (DK == 128) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    else if constexpr (DK == 64) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    else return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// 2^(s-127) for an E8M0 byte s >= 1
+__device__ inline float e8m0(uint32_t s) { return __uint_as_float(s << 23); }
+
 // With HIST, every stored score that the select would count (a valid entry;
 // in threshold mode one above t_f) is also added to the LDS histogram `hist`
 // of 11-bit key tops -- the select's first pass -- so a caller can skip it.
@@ -137,7 +190,7 @@ template <int DK, typename KT, bool HIST = false>
 __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, const int gx, uint32_t* hist = nullptr,
                                               const int hist_mode = 0, const float hist_t_f = 0.0f) {
     using C = Cfg<DK, KT>;
-    constexpr bool kF32 = sizeof(KT) == 4;
+    constexpr bool kF32 = C::kBits == 32;
     constexpr int kSteps = C::kSteps;
     constexpr int kTile = C::kTile;
     static_assert(1024 % C::kRowBytes == 0, "a 64-lane load covers whole rows");
@@ -176,6 +229,18 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
         const uint32_t seq_bytes = (uint32_t)nv * (uint32_t)C::kRowBytes;
         // scores of keys >= n_valid, and every store of lane half 1 (offset 2^31), are dropped
         const __amdgpu_buffer_rsrc_t so = make_rsrc(a.scores + (int64_t)b * a.n_keys, (uint32_t)nv * 4u);
+        // MX keys: the scale words of this lane's key in each 32-key block of tile t
+        // (sc_cur) and of tile t + stride (sc_nxt); keys >= n_valid read zero
+        __amdgpu_buffer_rsrc_t srs = zero_r;
+        uint32_t sc_cur[C::kNSub], sc_nxt[C::kNSub];
+        if constexpr (C::kMX) {
+            srs = make_rsrc(a.scales + (int64_t)b * a.n_keys * (DK / 32), (uint32_t)nv * (uint32_t)(DK / 32));
+#pragma unroll
+            for (int j = 0; j < C::kNSub; ++j) {
+                sc_cur[j] = load_scales<DK>(srs, (t - lo) * kTile + j * kSub + col);
+                sc_nxt[j] = load_scales<DK>(srs, (t + stride - lo) * kTile + j * kSub + col);
+            }
+        }
 
         // prologue: tile t into LDS buffer 0, tile t + stride in flight in registers; the
         // queries and weights load behind the first tile
@@ -249,6 +314,11 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
                 t2 < hi ? tile_rsrc(seq, seq_bytes, (uint32_t)(t2 - lo) * (uint32_t)C::kTileBytes) : zero_r;
             const char* rd = my0 + cur * kBuf + roff;
             char* wrb = my0 + (cur ^ 1) * kBuf + woff;
+            uint32_t sc_n2[C::kNSub];
+            if constexpr (C::kMX) {
+#pragma unroll
+                for (int j = 0; j < C::kNSub; ++j) sc_n2[j] = load_scales<DK>(srs, (t2 - lo) * kTile + j * kSub + col);
+            }
 
             f32x16 acc[C::kNSub];
 #pragma unroll
@@ -270,11 +340,39 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.v[rr * 4 + e], kb[e], acc[j], 0, 0, 0);
-                } else if constexpr (sizeof(KT) == 2) {
+                } else if constexpr (C::kBits == 16) {
                     const bf16x8 kb = as_bf16x8(u);
                     acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.hi[rr], kb, acc[j], 0, 0, 0);
                     acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.mid[rr], kb, acc[j], 0, 0, 0);
                     acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.lo[rr], kb, acc[j], 0, 0, 0);
+                } else if constexpr (__is_same(KT, mxfp4_tag)) {
+                    // 32 fp4 codes of one MX block (index half*DK/64 + rr): elements of
+                    // blocks 4*rr .. 4*rr + 3
+                    const float sf = e8m0((sc_cur[j] >> (8 * (half * (DK / 64) + rr))) & 0xFFu);
+                    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const bf16x8 km = as_bf16x8(make_uint4(fp4x2_to_bf16x2<0>(uw[m], sf), fp4x2_to_bf16x2<1>(uw[m], sf),
+                                                               fp4x2_to_bf16x2<2>(uw[m], sf), fp4x2_to_bf16x2<3>(uw[m], sf)));
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.hi[4 * rr + m], km, acc[j], 0, 0, 0);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.mid[4 * rr + m], km, acc[j], 0, 0, 0);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.lo[4 * rr + m], km, acc[j], 0, 0, 0);
+                    }
+                } else if constexpr (__is_same(KT, mxint8_tag)) {
+                    // 16 int8 codes, half of MX block (half*DK/2 + 16*rr) / 32: elements of
+                    // blocks 2*rr and 2*rr + 1
+                    const float sf = e8m0((sc_cur[j] >> (8 * ((half * (DK / 2) + 16 * rr) / 32))) & 0xFFu) * (1.0f / 64.0f);
+                    const float off = -128.0f * sf;
+                    const bf16x8 k0 = as_bf16x8(make_uint4(i8x2_to_bf16x2<0>(u.x, sf, off), i8x2_to_bf16x2<1>(u.x, sf, off),
+                                                           i8x2_to_bf16x2<0>(u.y, sf, off), i8x2_to_bf16x2<1>(u.y, sf, off)));
+                    const bf16x8 k1 = as_bf16x8(make_uint4(i8x2_to_bf16x2<0>(u.z, sf, off), i8x2_to_bf16x2<1>(u.z, sf, off),
+                                                           i8x2_to_bf16x2<0>(u.w, sf, off), i8x2_to_bf16x2<1>(u.w, sf, off)));
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.hi[2 * rr], k0, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.mid[2 * rr], k0, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.lo[2 * rr], k0, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.hi[2 * rr + 1], k1, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.mid[2 * rr + 1], k1, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.lo[2 * rr + 1], k1, acc[j], 0, 0, 0);
                 } else {
                     // 16 fp8 codes: elements of blocks 2*rr and 2*rr + 1
                     const bf16x8 k0 = as_bf16x8(make_uint4(fp8x2_to_bf16x2<false>(u.x), fp8x2_to_bf16x2<true>(u.x),
@@ -331,13 +429,21 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
                 }
             }
             cur ^= 1;
+            if constexpr (C::kMX) {
+#pragma unroll
+                for (int j = 0; j < C::kNSub; ++j) {
+                    sc_cur[j] = sc_nxt[j];
+                    sc_nxt[j] = sc_n2[j];
+                }
+            }
         }
     }
 }
 
-// workgroups per CU: two for fp8 keys (registers and LDS fit two), else one
+// workgroups per CU: two for the one-byte and fp4 formats (registers and LDS
+// fit two), else one
 template <typename KT>
-constexpr int kWgPerCu = sizeof(KT) == 1 ? 2 : 1;
+constexpr int kWgPerCu = KeyFmt<KT>::kBits <= 8 ? 2 : 1;
 
 template <int DK, typename KT>
 __global__ __launch_bounds__(kThreads, kWgPerCu<KT>) void fm_score_kernel(const ScoreArgs a) {
@@ -374,6 +480,13 @@ hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, 
         if (dk == 32) return launch_t<32, uint8_t>(a, n_cu, s);
         if (dk == 64) return launch_t<64, uint8_t>(a, n_cu, s);
         if (dk == 128) return launch_t<128, uint8_t>(a, n_cu, s);
+    } else if (key_dtype == LSA_MXFP4) {
+        if (dk == 64) return launch_t<64, mxfp4_tag>(a, n_cu, s);
+        if (dk == 128) return launch_t<128, mxfp4_tag>(a, n_cu, s);
+    } else if (key_dtype == LSA_MXINT8) {
+        if (dk == 32) return launch_t<32, mxint8_tag>(a, n_cu, s);
+        if (dk == 64) return launch_t<64, mxint8_tag>(a, n_cu, s);
+        if (dk == 128) return launch_t<128, mxint8_tag>(a, n_cu, s);
     }
     return hipErrorInvalidValue;
 }

@@ -282,6 +282,13 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int p
         if (dk == 32) return launch_a<32, uint8_t>(sa, ca, ha, n_cu, s);
         if (dk == 64) return launch_a<64, uint8_t>(sa, ca, ha, n_cu, s);
         if (dk == 128) return launch_a<128, uint8_t>(sa, ca, ha, n_cu, s);
+    } else if (key_dtype == LSA_MXFP4) {
+        if (dk == 64) return launch_a<64, score_k::mxfp4_tag>(sa, ca, ha, n_cu, s);
+        if (dk == 128) return launch_a<128, score_k::mxfp4_tag>(sa, ca, ha, n_cu, s);
+    } else if (key_dtype == LSA_MXINT8) {
+        if (dk == 32) return launch_a<32, score_k::mxint8_tag>(sa, ca, ha, n_cu, s);
+        if (dk == 64) return launch_a<64, score_k::mxint8_tag>(sa, ca, ha, n_cu, s);
+        if (dk == 128) return launch_a<128, score_k::mxint8_tag>(sa, ca, ha, n_cu, s);
     }
     return hipErrorInvalidValue;
 }

@@ -298,22 +298,35 @@ lsa_status lsa_ctx_timing_read(lsa_ctx* c, double* ms, int64_t* launches) {
 // ------------------------------------------------------------------ score
 namespace {
 
-lsa_status score_args(const void* keys, lsa_dtype key_dtype, int32_t batch, int64_t n_keys,
-                      const int64_t* n_valid, int32_t dk, const float* q, const float* w, int32_t n_idx,
-                      int32_t heads, lsa_ensemble ens, float* scores, ScoreArgs* a) {
+bool mx_dtype(lsa_dtype d) { return d == LSA_MXFP4 || d == LSA_MXINT8; }
+
+// bytes of one key row of dk elements
+uint64_t key_row_bytes(lsa_dtype d, int32_t dk) {
+    if (d == LSA_MXFP4) return (uint64_t)dk / 2;
+    if (d == LSA_MXINT8) return (uint64_t)dk;
+    return (uint64_t)dk * (uint64_t)elem_bytes(d);
+}
+
+lsa_status score_args(const void* keys, lsa_dtype key_dtype, const uint8_t* key_scales, int32_t batch,
+                      int64_t n_keys, const int64_t* n_valid, int32_t dk, const float* q, const float* w,
+                      int32_t n_idx, int32_t heads, lsa_ensemble ens, float* scores, ScoreArgs* a) {
     if (batch < 1 || batch > LSA_MAX_BATCH) return fail(LSA_ERR_INVALID_ARG, "batch %d not in [1, %d]", batch, LSA_MAX_BATCH);
     if (n_keys < 0 || n_keys > INT32_MAX) return fail(LSA_ERR_INVALID_ARG, "n_keys %lld out of range", (long long)n_keys);
     if (!keys || !q || !w || !scores) return fail(LSA_ERR_INVALID_ARG, "lsa_score: NULL pointer");
     if (ens != LSA_ENSEMBLE_MAX && ens != LSA_ENSEMBLE_MEAN) return fail(LSA_ERR_INVALID_ARG, "ensemble %d", (int)ens);
     if (dk <= 0 || n_idx <= 0 || heads <= 0) return fail(LSA_ERR_INVALID_ARG, "dk, n_idx and heads must be positive");
-    if (key_dtype != LSA_F32 && key_dtype != LSA_BF16 && key_dtype != LSA_FP8_E4M3)
-        return fail(LSA_ERR_UNSUPPORTED, "key dtype %d (supported: F32, BF16, FP8_E4M3)", (int)key_dtype);
+    if (key_dtype != LSA_F32 && key_dtype != LSA_BF16 && key_dtype != LSA_FP8_E4M3 && !mx_dtype(key_dtype))
+        return fail(LSA_ERR_UNSUPPORTED, "key dtype %d (supported: F32, BF16, FP8_E4M3, MXFP4, MXINT8)",
+                    (int)key_dtype);
     if (dk != 32 && dk != 64 && dk != 128) return fail(LSA_ERR_UNSUPPORTED, "dk %d (supported: 32, 64, 128)", dk);
+    if (key_dtype == LSA_MXFP4 && dk == 32) return fail(LSA_ERR_UNSUPPORTED, "MXFP4 keys need dk 64 or 128");
+    if (mx_dtype(key_dtype) && !key_scales) return fail(LSA_ERR_INVALID_ARG, "MX keys need key_scales");
     if (n_idx > 4 || heads > 8) return fail(LSA_ERR_UNSUPPORTED, "n_idx %d x heads %d (supported: <= 4 x <= 8)", n_idx, heads);
-    if ((uint64_t)n_keys * (uint64_t)dk * (uint64_t)elem_bytes(key_dtype) >= ((uint64_t)1 << 32))
+    if ((uint64_t)n_keys * key_row_bytes(key_dtype, dk) >= ((uint64_t)1 << 32))
         return fail(LSA_ERR_UNSUPPORTED, "a sequence's keys exceed 4 GiB");
     memset(a, 0, sizeof(*a));
     a->keys = keys;
+    a->scales = mx_dtype(key_dtype) ? key_scales : nullptr;
     a->q = q;
     a->w = w;
     a->scores = scores;
@@ -322,7 +335,7 @@ lsa_status score_args(const void* keys, lsa_dtype key_dtype, int32_t batch, int6
     a->n_idx = n_idx;
     a->heads = heads;
     a->ensemble = ens;
-    // keys per wave tile: 32 fp32 keys, 64 bf16 or fp8 keys
+    // keys per wave tile: 32 fp32 keys, 64 of every narrower format
     const int64_t tile_keys = key_dtype == LSA_F32 ? 32 : 64;
     int tiles = 0;
     for (int b = 0; b < batch; ++b) {
@@ -474,11 +487,12 @@ lsa_status lsa_project(const float* hidden, int32_t batch, int32_t d_model, cons
     return LSA_OK;
 }
 
-lsa_status lsa_score(const void* keys, lsa_dtype key_dtype, int32_t batch, int64_t n_keys,
+lsa_status lsa_score(const void* keys, lsa_dtype key_dtype, const uint8_t* key_scales, int32_t batch, int64_t n_keys,
                      const int64_t* n_valid, int32_t dk, const float* q, const float* w, int32_t n_idx,
                      int32_t heads, lsa_ensemble ensemble, float* scores, lsa_stream_t stream) {
     ScoreArgs a;
-    lsa_status st = score_args(keys, key_dtype, batch, n_keys, n_valid, dk, q, w, n_idx, heads, ensemble, scores, &a);
+    lsa_status st = score_args(keys, key_dtype, key_scales, batch, n_keys, n_valid, dk, q, w, n_idx, heads, ensemble,
+                               scores, &a);
     if (st != LSA_OK) return st;
     HIPTRY(launch_fm_score(a, key_dtype, dk, n_cu_current(), (hipStream_t)stream));
     return LSA_OK;
@@ -813,8 +827,8 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
             k_eff = p->d.gpu_chunks;
         }
     }
-    lsa_status st = score_args(d->keys, d->key_dtype, B, d->n_keys, d->n_valid, d->dk, d->q_idx, d->w_idx, d->n_idx,
-                               d->heads, d->ensemble, d->scores, &P->sa);
+    lsa_status st = score_args(d->keys, d->key_dtype, d->key_scales, B, d->n_keys, d->n_valid, d->dk, d->q_idx,
+                               d->w_idx, d->n_idx, d->heads, d->ensemble, d->scores, &P->sa);
     if (st != LSA_OK) return st;
     size_t sel_need = 0;
     st = select_setup(ctx, d->scores, B, d->n_keys, d->n_valid, d->mode, k_eff, d->k, d->tau, d->sel, d->count, &P->se,

@@ -116,6 +116,7 @@ hipError_t launch_project(const ProjectArgs& a, int w_dtype, int batch, int n_cu
 
 struct ScoreArgs {
     const void* keys;
+    const uint8_t* scales;    // MX keys: E8M0 per 32 elements, [batch][n_keys][dk/32]
     const float* q;
     const float* w;
     float* scores;

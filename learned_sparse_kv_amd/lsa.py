@@ -17,11 +17,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblsa.so")
 
-F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
+F32, BF16, F16, FP8_E4M3, MXFP4, MXINT8 = 0, 1, 2, 3, 4, 5
 ENS = {"max": 0, "mean": 1}
 MODE = {"topk": 0, "threshold": 1}
 COLD = {"hbm": 0, "host": 1}
-DTYPE = {"f32": F32, "bf16": BF16, "f16": F16, "fp8": FP8_E4M3}
+DTYPE = {"f32": F32, "bf16": BF16, "f16": F16, "fp8": FP8_E4M3, "mxfp4": MXFP4, "mxint8": MXINT8}
 K_NAMES = ["score", "select", "stage", "gather", "attend", "combine"]
 MAX_LAYERS = 16
 
@@ -52,7 +52,7 @@ class PoolStats(ctypes.Structure):
 
 
 class StepDesc(ctypes.Structure):
-    _fields_ = [("keys", P), ("key_dtype", i32), ("n_keys", i64), ("n_valid", P), ("dk", i32),
+    _fields_ = [("keys", P), ("key_dtype", i32), ("key_scales", P), ("n_keys", i64), ("n_valid", P), ("dk", i32),
                 ("q_idx", P), ("w_idx", P), ("n_idx", i32), ("heads", i32), ("ensemble", i32),
                 ("mode", i32), ("k", i32), ("tau", f64), ("src_ratio", i32),
                 ("scores", P), ("sel", P), ("count", P),
@@ -67,7 +67,7 @@ class KVSwapDesc(ctypes.Structure):
                 ("phys", P), ("n_rows", P), ("scale", f32), ("out", P)]
 
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _SIGS = {
     "lsa_compressed_cap": (i64, [i64, i32]),
@@ -84,7 +84,7 @@ _SIGS = {
     "lsa_ctx_set_timing": (i32, [P, i32]),
     "lsa_ctx_timing_read": (i32, [P, P, P]),
     "lsa_project": (i32, [P, i32, i32, P, P, i32, i32, i32, i32, P, P, P]),
-    "lsa_score": (i32, [P, i32, i32, i64, P, i32, P, P, i32, i32, i32, P, P]),
+    "lsa_score": (i32, [P, i32, P, i32, i64, P, i32, P, P, i32, i32, i32, P, P]),
     "lsa_select": (i32, [P, P, i32, i64, P, i32, i32, f64, P, P, P]),
     "lsa_pool_rows": (i64, [ctypes.POINTER(PoolDesc)]),
     "lsa_pool_create": (i32, [ctypes.POINTER(P), ctypes.POINTER(PoolDesc)]),
@@ -168,6 +168,10 @@ def row_dtype_code(t) -> int:
         return F16
     if t.dtype == torch.float8_e4m3fn:
         return FP8_E4M3
+    if t.dtype == torch.float4_e2m1fn_x2:
+        return MXFP4
+    if t.dtype == torch.int8:
+        return MXINT8
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
@@ -242,13 +246,33 @@ def project(hidden, wq, ww, q, w, stream=None) -> None:
 
 
 # ---------------------------------------------------------------- score
-def score(keys, q, w, scores, ensemble: str = "max", n_valid=None, stream=None) -> None:
-    """keys [B][N][dk] f32/bf16, q [B][n_idx][H][dk] f32, w [B][n_idx][H] f32 -> scores [B][N] f32."""
+def _keys_args(keys, key_scales, dk: int):
+    """(dtype code, key_scales pointer) after checking the key and scale shapes: keys
+    [B][N][dk] (f32, bf16, fp8 e4m3fn or int8 = MX INT8) or [B][N][dk/2]
+    (float4_e2m1fn_x2 = MX FP4); MX keys need key_scales [B][N][dk/32] (one byte each)."""
+    code = row_dtype_code(keys)
+    B, N, width = keys.shape
+    if width != (dk // 2 if code == MXFP4 else dk):
+        raise ValueError(f"keys' last dimension {width} does not match dk {dk}")
+    if code in (MXFP4, MXINT8):
+        if key_scales is None:
+            raise ValueError("MX keys need key_scales")
+        _dev(key_scales, "key_scales")
+        if tuple(key_scales.shape) != (B, N, dk // 32) or key_scales.element_size() != 1:
+            raise ValueError("key_scales must be one byte per 32 key elements, [B][N][dk/32]")
+        return code, _ptr(key_scales)
+    return code, None
+
+
+def score(keys, q, w, scores, ensemble: str = "max", n_valid=None, stream=None, key_scales=None) -> None:
+    """keys [B][N][dk] (or [B][N][dk/2] MX FP4), q [B][n_idx][H][dk] f32, w [B][n_idx][H] f32
+    -> scores [B][N] f32."""
     _dev(keys, "keys"), _dev(q, "q"), _dev(w, "w"), _dev(scores, "scores")
-    B, N, dk = keys.shape
-    _, n_idx, H, _ = q.shape
+    B, n_idx, H, dk = q.shape
+    N = keys.shape[1]
+    code, sp = _keys_args(keys, key_scales, dk)
     nv = _host_i64(n_valid)
-    _check(lib().lsa_score(_ptr(keys), row_dtype_code(keys), B, N, ctypes.cast(nv, P) if nv else None, dk,
+    _check(lib().lsa_score(_ptr(keys), code, sp, B, N, ctypes.cast(nv, P) if nv else None, dk,
                            _ptr(q), _ptr(w), n_idx, H, ENS[ensemble], _ptr(scores), _stream(stream)))
 
 
@@ -381,19 +405,20 @@ def attend(ctx: Ctx, q, kv, phys, n_rows, out, scale: float, kv_rows: Optional[i
 
 
 def _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble="max",
-               mode="topk", tau=0.5, n_valid=None, phys=None, n_rows=None):
+               mode="topk", tau=0.5, n_valid=None, phys=None, n_rows=None, key_scales=None):
     for t, n in ((keys, "keys"), (q_idx, "q_idx"), (w_idx, "w_idx"), (q_attn, "q_attn"), (out, "out"),
                  (scores, "scores"), (sel, "sel"), (count, "count")):
         _dev(t, n)
-    B, N, dk = keys.shape
-    _, n_idx, H, _ = q_idx.shape
+    B, n_idx, H, dk = q_idx.shape
+    N = keys.shape[1]
+    code, sp = _keys_args(keys, key_scales, dk)
     L, _, hq, D = q_attn.shape
     if L != len(pools):
         raise ValueError("q_attn's first dimension must equal the number of pools")
     d = StepDesc()
     nv = _host_i64(n_valid)
     pool_arr = (P * len(pools))(*[p.h for p in pools])
-    d.keys, d.key_dtype, d.n_keys, d.n_valid, d.dk = _ptr(keys), row_dtype_code(keys), N, \
+    d.keys, d.key_dtype, d.key_scales, d.n_keys, d.n_valid, d.dk = _ptr(keys), code, sp, N, \
         (ctypes.cast(nv, P) if nv else None), dk
     d.q_idx, d.w_idx, d.n_idx, d.heads, d.ensemble = _ptr(q_idx), _ptr(w_idx), n_idx, H, ENS[ensemble]
     d.mode, d.k, d.tau, d.src_ratio = MODE[mode], k, float(tau), src_ratio
@@ -407,21 +432,21 @@ def _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, sr
 
 def lookahead_prime(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,
                     k: int, src_ratio: int, scale: float, ensemble: str = "max", mode: str = "topk",
-                    tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None) -> None:
+                    tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None, key_scales=None) -> None:
     """Stage the rows of the first lookahead step (lsa_lookahead_prime); arguments as decode_step,
     with phys [2][L][B][window + k] and n_rows [2][L][B] when given."""
     d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
-                         mode, tau, n_valid, phys, n_rows)
+                         mode, tau, n_valid, phys, n_rows, key_scales)
     _check(lib().lsa_lookahead_prime(ctx.h, ctypes.byref(d), _stream(stream)))
 
 
 def lookahead_step(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,
                    k: int, src_ratio: int, scale: float, ensemble: str = "max", mode: str = "topk",
-                   tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None) -> None:
+                   tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None, key_scales=None) -> None:
     """Attend this step (q_attn -> out) while predicting and staging the next one from q_idx / w_idx
     (lsa_lookahead_step)."""
     d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
-                         mode, tau, n_valid, phys, n_rows)
+                         mode, tau, n_valid, phys, n_rows, key_scales)
     _check(lib().lsa_lookahead_step(ctx.h, ctypes.byref(d), _stream(stream)))
 
 
@@ -446,32 +471,15 @@ def lookahead_buffer(ctx: Ctx) -> int:
 
 def decode_step(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,
                 k: int, src_ratio: int, scale: float, ensemble: str = "max", mode: str = "topk",
-                tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None) -> None:
+                tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None, key_scales=None) -> None:
     """One LSA decode step over len(pools) sparse layers (lsa_decode_step).
 
-    keys [B][N][dk]; q_idx [B][n_idx][H][dk]; w_idx [B][n_idx][H];
-    q_attn / out [L][B][hq][D] f32; scores [B][N] f32; sel [B][k] i32; count [B] i32;
-    phys [L][B][window + k] i32 and n_rows [L][B] i32 optional."""
-    for t, n in ((keys, "keys"), (q_idx, "q_idx"), (w_idx, "w_idx"), (q_attn, "q_attn"), (out, "out"),
-                 (scores, "scores"), (sel, "sel"), (count, "count")):
-        _dev(t, n)
-    B, N, dk = keys.shape
-    _, n_idx, H, _ = q_idx.shape
-    L, _, hq, D = q_attn.shape
-    if L != len(pools):
-        raise ValueError("q_attn's first dimension must equal the number of pools")
-    d = StepDesc()
-    nv = _host_i64(n_valid)
-    pool_arr = (P * len(pools))(*[p.h for p in pools])
-    d.keys, d.key_dtype, d.n_keys, d.n_valid, d.dk = _ptr(keys), row_dtype_code(keys), N, \
-        (ctypes.cast(nv, P) if nv else None), dk
-    d.q_idx, d.w_idx, d.n_idx, d.heads, d.ensemble = _ptr(q_idx), _ptr(w_idx), n_idx, H, ENS[ensemble]
-    d.mode, d.k, d.tau, d.src_ratio = MODE[mode], k, float(tau), src_ratio
-    d.scores, d.sel, d.count = _ptr(scores), _ptr(sel), _ptr(count)
-    d.n_layers, d.pools, d.q_attn, d.out = len(pools), ctypes.cast(pool_arr, P), _ptr(q_attn), _ptr(out)
-    d.phys = _ptr(phys) if phys is not None else None
-    d.n_rows = _ptr(n_rows) if n_rows is not None else None
-    d.hq, d.scale, d.batch = hq, float(scale), B
+    keys [B][N][dk] (MX FP4: [B][N][dk/2]) with key_scales [B][N][dk/32] for the MX dtypes;
+    q_idx [B][n_idx][H][dk]; w_idx [B][n_idx][H]; q_attn / out [L][B][hq][D] f32;
+    scores [B][N] f32; sel [B][k] i32; count [B] i32; phys [L][B][window + k] i32 and
+    n_rows [L][B] i32 optional."""
+    d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
+                         mode, tau, n_valid, phys, n_rows, key_scales)
     _check(lib().lsa_decode_step(ctx.h, ctypes.byref(d), _stream(stream)))
 
 

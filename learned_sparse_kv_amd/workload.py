@@ -18,9 +18,16 @@ import lsa_inputs as L
 from . import lsa
 
 
-def to_device(x: np.ndarray, dtype: str, dev) -> torch.Tensor:
+def to_device(x, dtype: str, dev):
     """Upload values already encoded for `dtype` (f32 array, bf16/f16 16-bit codes
-    or fp8 E4M3 byte codes)."""
+    or fp8 E4M3 byte codes); for the MX dtypes an MXKeys becomes (codes, scales)
+    tensors (float4_e2m1fn_x2 or int8 codes, float8_e8m0fnu scales)."""
+    if dtype in L.MX_DTYPES:
+        codes = torch.from_numpy(np.ascontiguousarray(x.codes)).to(dev)
+        if dtype == "mxfp4":
+            codes = codes.view(torch.float4_e2m1fn_x2)
+        scales = torch.from_numpy(np.ascontiguousarray(x.scales, dtype=np.uint8)).to(dev).view(torch.float8_e8m0fnu)
+        return codes, scales
     if dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
     if dtype == "fp8":
@@ -43,7 +50,10 @@ class DeviceWorkload:
         say = log or (lambda *_: None)
         B, D, W = wl.batch, wl.kv_dim, wl.window
         keys_np = [L.indexer_keys(wl, b) for b in range(B)]
-        self.keys = to_device(np.stack(keys_np), wl.key_dtype, self.dev)
+        self.keys = to_device(L.stack_keys(keys_np, wl.key_dtype), wl.key_dtype, self.dev)
+        self.key_scales = None
+        if wl.key_dtype in L.MX_DTYPES:
+            self.keys, self.key_scales = self.keys
         self.keys_np = keys_np if keep_host else None
         say(f"keys {tuple(self.keys.shape)} {wl.key_dtype}")
         self.pools: List[lsa.Pool] = []
@@ -112,7 +122,7 @@ class DeviceWorkload:
                         q_attn=self.q_attn[t], out=self.out, scores=self.scores, sel=self.sel, count=self.count,
                         k=wl.k, src_ratio=wl.src_ratio, scale=wl.scale, ensemble=wl.ensemble, mode=wl.mode,
                         tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys, n_rows=self.n_rows,
-                        stream=stream)
+                        stream=stream, key_scales=self.key_scales)
 
     # ---- lookahead schedule: step t attends with the rows staged during step
     # t-1 (or by prime) and predicts step t+1 from q_idx[t+1]
@@ -128,7 +138,8 @@ class DeviceWorkload:
         return dict(keys=self.keys, q_idx=self.q_idx[t_idx], w_idx=self.w_idx[t_idx], pools=self.pools,
                     q_attn=self.q_attn[t_attn], out=self.out, scores=self.scores, sel=self.sel, count=self.count,
                     k=wl.k, src_ratio=wl.src_ratio, scale=wl.scale, ensemble=wl.ensemble, mode=wl.mode,
-                    tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys2, n_rows=self.n_rows2)
+                    tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys2, n_rows=self.n_rows2,
+                    key_scales=self.key_scales)
 
     def lookahead_prime(self, t: int = 0, stream=None) -> None:
         lsa.lookahead_prime(self.ctx, stream=stream, **self._la_args(t, t))

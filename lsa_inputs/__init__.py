@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import dataclasses
 import zlib
-from typing import Optional, Tuple
+from typing import NamedTuple, Optional, Tuple
 
 import numpy as np
 
@@ -108,8 +108,39 @@ def f32_to_fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
     return (sign | (field.astype(np.uint8) << 3) | frac.astype(np.uint8)).astype(np.uint8)
 
 
-DTYPE_CODES = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3}
-DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
+DTYPE_CODES = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3, "mxfp4": 4, "mxint8": 5}
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "mxfp4": 0.5, "mxint8": 1}
+MX_DTYPES = ("mxfp4", "mxint8")
+
+
+class MXKeys(NamedTuple):
+    """Keys in an OCP MX format: codes ([N][dk/2] bytes of two E2M1 codes, or
+    [N][dk] int8) and one E8M0 scale byte per 32 elements ([N][dk/32])."""
+    codes: np.ndarray
+    scales: np.ndarray
+
+
+def mx_keys(rng: np.random.Generator, n: int, dk: int, dtype: str) -> MXKeys:
+    """Random MX keys whose every dot product with 1/8-grid queries and weights
+    stays exact in fp32: fp4 codes uniform over all 16, scales 2^-3..2^-1 (values
+    up to 3 on a 1/16 grid); int8 codes uniform in [-64, 64] (values c/64), scales
+    2^-2..1 (values up to 1 on a 1/256 grid)."""
+    if dtype == "mxfp4":
+        codes = rng.integers(0, 256, size=(n, dk // 2), dtype=np.uint8)
+        scales = (127 + rng.integers(-3, 0, size=(n, dk // 32))).astype(np.uint8)
+    elif dtype == "mxint8":
+        codes = rng.integers(-64, 65, size=(n, dk), dtype=np.int8)
+        scales = (127 + rng.integers(-2, 1, size=(n, dk // 32))).astype(np.uint8)
+    else:
+        raise ValueError(dtype)
+    return MXKeys(codes, scales)
+
+
+def stack_keys(keys: list, dtype: str):
+    """Per-sequence keys -> one batch array (an MXKeys of stacked codes and scales)."""
+    if dtype in MX_DTYPES:
+        return MXKeys(np.stack([k.codes for k in keys]), np.stack([k.scales for k in keys]))
+    return np.stack(keys)
 
 
 def encode(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -214,6 +245,10 @@ WORKLOADS = {
 # same grid values (exact in E4M3), so the same selections, at a quarter of the
 # key bytes
 WORKLOADS["swap_1m_fp8"] = WORKLOADS["swap_1m"].replace(name="swap_1m_fp8", key_dtype="fp8")
+# ... and in the OCP MX formats (codes and block scales drawn in the format:
+# 17.8 and 34.6 MB of keys)
+WORKLOADS["swap_1m_mxfp4"] = WORKLOADS["swap_1m"].replace(name="swap_1m_mxfp4", key_dtype="mxfp4")
+WORKLOADS["swap_1m_mxint8"] = WORKLOADS["swap_1m"].replace(name="swap_1m_mxint8", key_dtype="mxint8")
 
 
 # --------------------------------------------------------------------------
@@ -251,7 +286,13 @@ def indexer_keys_f32(wl: Workload, b: int) -> np.ndarray:
     return keys
 
 
-def indexer_keys(wl: Workload, b: int) -> np.ndarray:
+def indexer_keys(wl: Workload, b: int):
+    """Keys of sequence b in the workload's key dtype (an MXKeys for the MX dtypes,
+    drawn in that format; every other dtype encodes the grid values exactly)."""
+    if wl.key_dtype in MX_DTYPES:
+        if wl.dist != "uniform":
+            raise ValueError("MX keys are drawn for the uniform workloads only")
+        return mx_keys(rng_for(wl.base_seed, "keys", b), wl.n_src, wl.dk, wl.key_dtype)
     return encode(indexer_keys_f32(wl, b), wl.key_dtype)
 
 

@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "lsa_oracle.cpp")
 _BUILD = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_BUILD, "liblsa_oracle.so")
 
-DT = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3}
+DT = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3, "mxfp4": 4, "mxint8": 5}
 ENS = {"max": 0, "mean": 1}
 MODE = {"topk": 0, "threshold": 1}
 ST_NOT_STORED = 4
@@ -54,7 +54,7 @@ def lib():
             "oracle_pinned_bytes": (u64, [i64, P, i32, i32, i32]),
             "oracle_max_capacity": (i32, [i32, i32]),
             "oracle_swap_enabled": (i32, [i64, i32]),
-            "oracle_score": (None, [P, i32, i64, i32, P, P, i32, i32, i32, P]),
+            "oracle_score": (None, [P, i32, P, i64, i32, P, P, i32, i32, i32, P]),
             "oracle_project": (None, [P, i32, i32, P, P, i32, i32, i32, i32, P, P]),
             "oracle_threshold_float": (f32, [f64]),
             "oracle_select": (i32, [P, i64, i32, i32, f64, P]),
@@ -85,7 +85,7 @@ def _c(a, dtype) -> np.ndarray:
 
 
 def _kv(a: np.ndarray, dtype: str) -> np.ndarray:
-    return _c(a, {"f32": np.float32, "fp8": np.uint8}.get(dtype, np.uint16))
+    return _c(a, {"f32": np.float32, "fp8": np.uint8, "mxfp4": np.uint8, "mxint8": np.int8}.get(dtype, np.uint16))
 
 
 # ------------------------------------------------------------------ sizing --
@@ -107,16 +107,23 @@ def swap_enabled(cap: int, gpu_chunks: int) -> bool:
 
 
 # ------------------------------------------------------------------- score --
-def score(keys: np.ndarray, key_dtype: str, q: np.ndarray, w: np.ndarray,
+def score(keys, key_dtype: str, q: np.ndarray, w: np.ndarray,
           ensemble: str = "max", n_valid: Optional[int] = None) -> np.ndarray:
-    """keys [N][dk] (f32 or 16-bit codes), q [n_idx][H][dk], w [n_idx][H] -> e [n_valid] f32."""
+    """keys [N][dk] (f32, 16-bit or fp8 codes; for the MX dtypes a (codes, scales)
+    pair: codes [N][dk/2] (fp4) or [N][dk] (int8), E8M0 scales [N][dk/32]),
+    q [n_idx][H][dk], w [n_idx][H] -> e [n_valid] f32."""
+    scales = None
+    if key_dtype in ("mxfp4", "mxint8"):
+        keys, scales = keys
+        scales = _c(scales, np.uint8)
     keys = _kv(keys, key_dtype)
     q = _c(q, np.float32)
     w = _c(w, np.float32)
     n_idx, H, dk = q.shape
     n = keys.shape[0] if n_valid is None else int(n_valid)
     e = np.zeros(n, np.float32)
-    lib().oracle_score(_p(keys), DT[key_dtype], n, dk, _p(q), _p(w), n_idx, H, ENS[ensemble], _p(e))
+    lib().oracle_score(_p(keys), DT[key_dtype], _p(scales) if scales is not None else None, n, dk, _p(q), _p(w),
+                       n_idx, H, ENS[ensemble], _p(e))
     return e
 
 

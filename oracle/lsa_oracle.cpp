@@ -30,7 +30,7 @@
 
 namespace {
 
-enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8_E4M3 = 3 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8_E4M3 = 3, DT_MXFP4 = 4, DT_MXINT8 = 5 };
 enum { ENS_MAX = 0, ENS_MEAN = 1 };
 enum { SEL_TOPK = 0, SEL_THRESHOLD = 1 };
 enum { ST_OK = 0, ST_NOT_STORED = 4 };
@@ -77,6 +77,39 @@ double fp8_e4m3_to_double(uint8_t c) {
         v = std::ldexp((double)(8 + frac), expo - 10);
     }
     return sign ? -v : v;
+}
+
+// OCP MX FP4 element (E2M1) -> double, from the format's definition: 1 sign,
+// 2 exponent bits with bias 1, 1 mantissa bit; exponent 0 is subnormal
+// (mantissa * 0.5); no infinities or NaN.
+double e2m1_to_double(uint8_t nib) {
+    const int sign = (nib >> 3) & 1;
+    const int expo = (nib >> 1) & 3;
+    const int man = nib & 1;
+    const double v = expo == 0 ? 0.5 * man : std::ldexp(1.0 + 0.5 * man, expo - 1);
+    return sign ? -v : v;
+}
+
+// OCP MX scale (E8M0) -> double: 2^(s - 127); 255 is NaN.
+double e8m0_to_double(uint8_t s) { return s == 255 ? NAN : std::ldexp(1.0, (int)s - 127); }
+
+double elem(const void* base, int dtype, int64_t i);
+
+// Element t of key j (a row of dk elements) in key_dtype.  The MX formats
+// ([P1] technical details: the reference's own keys are fp4) multiply each
+// code by the E8M0 scale of its block of 32 consecutive elements
+// (scales [.][dk/32]); MX INT8 codes carry an implicit 2^-6.
+double key_elem(const void* keys, const uint8_t* scales, int dtype, int32_t dk, int64_t j, int32_t t) {
+    if (dtype == DT_MXFP4) {
+        const uint8_t byte = static_cast<const uint8_t*>(keys)[j * (dk / 2) + t / 2];
+        const uint8_t nib = (t & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+        return e2m1_to_double(nib) * e8m0_to_double(scales[j * (dk / 32) + t / 32]);
+    }
+    if (dtype == DT_MXINT8) {
+        const int8_t c = static_cast<const int8_t*>(keys)[j * dk + t];
+        return (double)c / 64.0 * e8m0_to_double(scales[j * (dk / 32) + t / 32]);
+    }
+    return elem(keys, dtype, j * dk + t);
 }
 
 double elem(const void* base, int dtype, int64_t i) {
@@ -168,14 +201,15 @@ void oracle_project(const float* hidden, int32_t B, int32_t d_model, const void*
 // rounds the sum of the float s_i[j] to float and divides once by n_idx in
 // IEEE single precision.  -0 is written as +0.
 //
-// keys: [n_valid][dk] in key_dtype; q: [n_idx][H][dk]; w: [n_idx][H]; e: [n_valid].
-void oracle_score(const void* keys, int32_t key_dtype, int64_t n_valid, int32_t dk,
+// keys: [n_valid][dk] elements in key_dtype (with key_scales [n_valid][dk/32]
+// for the MX formats, else unused); q: [n_idx][H][dk]; w: [n_idx][H]; e: [n_valid].
+void oracle_score(const void* keys, int32_t key_dtype, const uint8_t* key_scales, int64_t n_valid, int32_t dk,
                   const float* q, const float* w, int32_t n_idx, int32_t H,
                   int32_t ensemble, float* e) {
     std::vector<double> key(dk);
     std::vector<float> s(n_idx);
     for (int64_t j = 0; j < n_valid; ++j) {
-        for (int32_t t = 0; t < dk; ++t) key[t] = elem(keys, key_dtype, j * dk + t);
+        for (int32_t t = 0; t < dk; ++t) key[t] = key_elem(keys, key_scales, key_dtype, dk, j, t);
         for (int32_t i = 0; i < n_idx; ++i) {
             double acc = 0.0;
             for (int32_t h = 0; h < H; ++h) {

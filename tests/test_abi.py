@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(lsa.EXPORTS)
-    assert L.lsa_abi_version() == lsa.ABI_VERSION == 4
+    assert L.lsa_abi_version() == lsa.ABI_VERSION == 5
 
 
 def test_closed_forms_match_oracle():
@@ -136,10 +136,10 @@ def test_pool_rows_swap_auto_disable():
 def test_score_and_select_argument_checks():
     L = lsa.lib()
     # dk unsupported / heads too many / bad ensemble: rejected on the host
-    assert L.lsa_score(0x10, 0, 1, 100, None, 48, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
-    assert L.lsa_score(0x10, 0, 1, 100, None, 64, 0x10, 0x10, 1, 9, 0, 0x10, None) == 7
-    assert L.lsa_score(0x10, 0, 1, 100, None, 64, 0x10, 0x10, 1, 4, 5, 0x10, None) == 1
-    assert L.lsa_score(None, 0, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 1
+    assert L.lsa_score(0x10, 0, None, 1, 100, None, 48, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
+    assert L.lsa_score(0x10, 0, None, 1, 100, None, 64, 0x10, 0x10, 1, 9, 0, 0x10, None) == 7
+    assert L.lsa_score(0x10, 0, None, 1, 100, None, 64, 0x10, 0x10, 1, 4, 5, 0x10, None) == 1
+    assert L.lsa_score(None, 0, None, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 1
     # projection: d_model a multiple of 8, batch in range, f32/bf16 weights, aligned hidden
     assert L.lsa_project(0x10, 1, 4100, 0x10, 0x10, 1, 3, 8, 128, 0x10, 0x10, None) == 7
     assert L.lsa_project(0x10, 0, 4096, 0x10, 0x10, 1, 3, 8, 128, 0x10, 0x10, None) == 1
@@ -147,8 +147,13 @@ def test_score_and_select_argument_checks():
     assert L.lsa_project(0x14, 1, 4096, 0x10, 0x10, 1, 3, 8, 128, 0x10, 0x10, None) == 1
     assert L.lsa_project(None, 1, 4096, 0x10, 0x10, 1, 3, 8, 128, 0x10, 0x10, None) == 1
     # key dtypes: f32, bf16 and fp8 E4M3; f16 keys and unknown codes are unsupported
-    assert L.lsa_score(0x10, lsa.F16, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
-    assert L.lsa_score(0x10, 9, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
+    assert L.lsa_score(0x10, lsa.F16, None, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
+    assert L.lsa_score(0x10, 9, None, 1, 100, None, 64, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
+    # MX keys need their block scales, and MX FP4 needs dk >= 64
+    assert L.lsa_score(0x10, lsa.MXFP4, None, 1, 100, None, 128, 0x10, 0x10, 1, 4, 0, 0x10, None) == 1
+    assert L.lsa_score(0x10, lsa.MXINT8, None, 1, 100, None, 128, 0x10, 0x10, 1, 4, 0, 0x10, None) == 1
+    assert L.lsa_score(0x10, lsa.MXFP4, 0x10, 1, 100, None, 32, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
+    assert L.lsa_score(0x10, 6, 0x10, 1, 100, None, 128, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
     # a sequence's keys must stay under 4 GiB: 2^25 keys x 128 bytes is the limit for fp8
-    assert L.lsa_score(0x10, lsa.FP8_E4M3, 1, 1 << 25, None, 128, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
+    assert L.lsa_score(0x10, lsa.FP8_E4M3, None, 1, 1 << 25, None, 128, 0x10, 0x10, 1, 4, 0, 0x10, None) == 7
     assert L.lsa_select(None, 0x10, 1, 100, None, 0, 8, 0.5, 0x10, 0x10, None) == 1

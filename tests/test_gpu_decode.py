@@ -62,9 +62,10 @@ def test_decode_mean_ensemble():
     run_decode(L.WORKLOADS["ens_8k"].replace(ensemble="mean"), 4)
 
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8", "mxfp4", "mxint8"])
 def test_decode_quantized_keys(kd):
-    # indexer keys stored as bf16 or OCP fp8 E4M3 (exact for the grid values)
+    # indexer keys stored as bf16 or OCP fp8 E4M3 (exact for the grid values), or
+    # drawn in the OCP MX formats (codes and block scales)
     run_decode(L.WORKLOADS["ens_8k"].replace(key_dtype=kd), 4)
 
 

@@ -121,8 +121,9 @@ def test_lookahead_fp8_keys_give_the_f32_bits(dw1m):
 def test_lookahead_small_workloads_match_oracle():
     # 512 slots for top-512 (the stage of t+1 runs after step t's attention) and the
     # single-workgroup select path; the tiny workload is fully resident
-    for name in ("ens_8k", "tiny_8k"):
-        wl = L.WORKLOADS[name]
+    for wl in (L.WORKLOADS["ens_8k"], L.WORKLOADS["tiny_8k"], L.WORKLOADS["ens_8k"].replace(key_dtype="mxfp4"),
+               L.WORKLOADS["ens_8k"].replace(key_dtype="mxint8")):
+        name = f"{wl.name}/{wl.key_dtype}"
         dw = DeviceWorkload(wl, keep_host=True)
         dw.make_steps(6)
         ref = oracle.DecodeState(wl, dw.windows, dw.stores)

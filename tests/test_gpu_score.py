@@ -127,7 +127,75 @@ def test_all_negative_dots_give_positive_zero():
         assert np.all(bits(s.cpu().numpy()) == 0)
 
 
-@pytest.mark.parametrize("name", ["thresh_256k", "swap_1m", "swap_1m_fp8"])
+def run_mx(keys, dtype, q, w, ens, n_valid=None):
+    """keys: per-sequence MXKeys; compares every sequence with the oracle, bit for bit."""
+    B = len(keys)
+    N = keys[0].codes.shape[0]
+    codes, scales = to_device(L.stack_keys(keys, dtype), dtype, DEV)
+    out = torch.full((B, N), float("nan"), device=DEV)
+    lsa.score(codes, torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV), out, ens, n_valid, key_scales=scales)
+    got = out.cpu().numpy()
+    for b in range(B):
+        nv = N if n_valid is None else n_valid[b]
+        want = oracle.score(keys[b], dtype, q[b], w[b], ens, n_valid=nv)
+        assert np.array_equal(bits(got[b, :nv]), bits(want)), f"seq {b}: first diff at {np.argmax(bits(got[b,:nv]) != bits(want))}"
+        assert np.all(np.isnan(got[b, nv:]))
+
+
+MX_CASES = [
+    # (B, N, dk, n_idx, H, dtype, ensemble)
+    (2, 4133, 128, 3, 8, "mxfp4", "max"),
+    (3, 300, 64, 2, 5, "mxfp4", "mean"),
+    (2, 4133, 128, 3, 8, "mxint8", "max"),
+    (1, 777, 32, 4, 8, "mxint8", "mean"),
+    (3, 300, 64, 1, 1, "mxint8", "max"),
+    (1, 1, 128, 1, 1, "mxfp4", "max"),
+]
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=[str(c) for c in MX_CASES])
+def test_mx_score_matches_oracle(case):
+    B, N, dk, n_idx, H, kd, ens = case
+    say(f"mx score case {case}")
+    rng = np.random.default_rng(hash(case) & 0xFFFF)
+    keys = [L.mx_keys(rng, N, dk, kd) for _ in range(B)]
+    q = L.grid_uniform(rng, (B, n_idx, H, dk))
+    w = L.grid_uniform(rng, (B, n_idx, H))
+    run_mx(keys, kd, q, w, ens)
+    if B > 1:
+        run_mx(keys, kd, q, w, ens, n_valid=[N - 1] + [max(0, N // (b + 2)) for b in range(1, B)])
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_mxfp4_every_code_in_every_nibble_and_block(dk):
+    """Each E2M1 code alone in each element position, with its block's scale
+    varied, decoded through the kernel (score = the element, +0 for zeros)."""
+    n = 16 * dk
+    codes = np.zeros((n, dk // 2), np.uint8)
+    scales = np.full((n, dk // 32), 127, np.uint8)
+    idx = np.arange(n)
+    pos, code = idx % dk, idx // dk
+    codes[idx, pos // 2] = (code << (4 * (pos % 2))).astype(np.uint8)
+    scales[idx, pos // 32] = (120 + (idx % 9)).astype(np.uint8)
+    q = np.stack([np.ones(dk, np.float32), -np.ones(dk, np.float32)])[None, None]
+    w = np.array([[[1.0, -1.0]]], np.float32)
+    run_mx([L.MXKeys(codes, scales)], "mxfp4", q, w, "max")
+
+
+def test_mxint8_every_code_in_every_column():
+    dk = 128
+    c = np.arange(-128, 128)
+    n = c.size * dk
+    idx = np.arange(n)
+    codes = np.zeros((n, dk), np.int8)
+    codes[idx, idx % dk] = c[idx // dk].astype(np.int8)
+    scales = (124 + (idx % 5)).astype(np.uint8)[:, None].repeat(dk // 32, axis=1)
+    q = np.stack([np.ones(dk, np.float32), -np.ones(dk, np.float32)])[None, None]
+    w = np.array([[[1.0, -1.0]]], np.float32)
+    run_mx([L.MXKeys(codes, scales)], "mxint8", q, w, "max")
+
+
+@pytest.mark.parametrize("name", ["thresh_256k", "swap_1m", "swap_1m_fp8", "swap_1m_mxfp4", "swap_1m_mxint8"])
 def test_full_size_workload_scores(name):
     wl = L.WORKLOADS[name]
     say(f"full-size score {name}: B={wl.batch} N={wl.n_src}")
@@ -136,9 +204,12 @@ def test_full_size_workload_scores(name):
     qw = [L.indexer_query(wl, b, 0) for b in range(B)]
     q = np.stack([x[0] for x in qw])
     w = np.stack([x[1] for x in qw])
-    kt = to_device(np.stack(keys), wl.key_dtype, DEV)
+    kt = to_device(L.stack_keys(keys, wl.key_dtype), wl.key_dtype, DEV)
+    ks = None
+    if wl.key_dtype in L.MX_DTYPES:
+        kt, ks = kt
     s = torch.zeros((B, wl.n_src), device=DEV)
-    lsa.score(kt, torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV), s, wl.ensemble)
+    lsa.score(kt, torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV), s, wl.ensemble, key_scales=ks)
     got = s.cpu().numpy()
     for b in range(B):
         want = oracle.score(keys[b], wl.key_dtype, q[b], w[b], wl.ensemble)

@@ -179,6 +179,76 @@ def test_fp8_e4m3_storage_decode():
     assert np.array_equal(oracle.score(L.f32_to_fp8_e4m3_bits(keys), "fp8", q, w), oracle.score(keys, "f32", q, w))
 
 
+# OCP MX specification: the E2M1 magnitudes of codes 0..7 (code 8..15: the negatives)
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _element_values(keys, dtype, dk):
+    """Every key holds one nonzero element: with two heads (q = +1 and -1 everywhere,
+    w = +1 and -1) the score is ReLU(x) - ReLU(-x) = x, the decoded element."""
+    q = np.stack([np.ones(dk, np.float32), -np.ones(dk, np.float32)])[None]
+    w = np.array([[1.0, -1.0]], np.float32)
+    return oracle.score(keys, dtype, q, w).astype(np.float64)
+
+
+def test_mxfp4_decode_every_code_nibble_and_block():
+    dk = 64
+    codes, scales, want = [], [], []
+    for code in range(16):
+        for pos in (0, 1, 33, 63):             # low and high nibble; first and second block
+            for s in (1, 120, 127, 131, 250):
+                row = np.zeros(dk // 2, np.uint8)
+                row[pos // 2] = code << (4 * (pos % 2))
+                sc = np.full(dk // 32, 127, np.uint8)
+                sc[pos // 32] = s
+                codes.append(row)
+                scales.append(sc)
+                want.append((-1.0 if code & 8 else 1.0) * E2M1[code & 7] * 2.0 ** (s - 127))
+    got = _element_values((np.array(codes), np.array(scales)), "mxfp4", dk)
+    assert np.array_equal(got, np.array(want, np.float32).astype(np.float64))
+
+
+def test_e8m0_scale_decode_against_torch():
+    import torch
+    s = np.arange(0, 255, dtype=np.uint8)
+    codes = np.zeros((s.size, 16), np.uint8)
+    codes[:, 0] = 2                            # E2M1 code 2 is 1.0
+    got = _element_values((codes, s.reshape(-1, 1)), "mxfp4", 32)
+    want = torch.from_numpy(s.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.array_equal(got, want.astype(np.float32).astype(np.float64))
+
+
+def test_mxint8_decode_every_code():
+    dk = 32
+    c = np.arange(-128, 128, dtype=np.int64)
+    codes = np.zeros((c.size * 2, dk), np.int8)
+    codes[:c.size, 5] = c
+    codes[c.size:, 31] = c
+    scales = np.concatenate([np.full((c.size, 1), 127), np.full((c.size, 1), 124)]).astype(np.uint8)
+    got = _element_values((codes, scales), "mxint8", dk)
+    want = np.concatenate([c / 64.0, c / 64.0 * 2.0 ** -3])
+    assert np.array_equal(got, want)
+
+
+def test_mx_encodings_of_grid_values_score_as_f32():
+    rng = np.random.default_rng(16)
+    dk = 128
+    q = L.grid_uniform(rng, (3, 8, dk))
+    w = L.grid_uniform(rng, (3, 8))
+    # MX INT8 with scale 1: code = 64 * value for every 1/8-grid value in [-1, 1]
+    v = L.grid_uniform(rng, (50, dk))
+    i8 = (v * 64).astype(np.int8)
+    ref = oracle.score(v, "f32", q, w)
+    assert np.array_equal(oracle.score((i8, np.full((50, dk // 32), 127, np.uint8)), "mxint8", q, w), ref)
+    # MX FP4 with scale 1/4: the grid values 4 * E2M1 covers
+    mags = np.array([0.0, 0.125, 0.25, 0.375, 0.5, 0.75, 1.0])
+    v = (mags[rng.integers(0, mags.size, (50, dk))] * rng.choice([-1.0, 1.0], (50, dk))).astype(np.float32)
+    nib = np.array([E2M1.index(abs(x) * 4) | (8 if x < 0 else 0) for x in v.ravel()], np.uint8).reshape(50, dk)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    ref = oracle.score(v, "f32", q, w)
+    assert np.array_equal(oracle.score((packed, np.full((50, dk // 32), 125, np.uint8)), "mxfp4", q, w), ref)
+
+
 def test_n_valid_prefix():
     rng = np.random.default_rng(14)
     keys = L.grid_uniform(rng, (100, 16))
