@@ -260,6 +260,37 @@ lsa_status lsa_pool_mark_stored(lsa_pool* pool, int32_t b, int64_t first, int64_
                                 lsa_stream_t stream);
 /* empty every slot (stored rows stay stored) and zero hits/misses/h2d. */
 lsa_status lsa_pool_reset(lsa_pool* pool, lsa_stream_t stream);
+/* Adaptive GPU_CHUNKS ([P1] limitations, future work: the staging capacity
+ * adjusted from the runtime LRU hit rate; [P1] troubleshooting: a miss rate
+ * above 50 % or more than 10 MB of H2D per step calls for more GPU_CHUNKS).
+ * The capacity is the number of slots a swapping pool may use, 1..gpu_chunks
+ * (gpu_chunks: the slots its kv_buf holds; a new pool uses all of them).
+ * Growing makes the next slots usable (a miss takes the lowest unused slot).
+ * Shrinking to C evicts the least recently used entries until at most C
+ * remain, then moves every remaining entry whose slot is >= C, with its row,
+ * to the lowest vacated slot below C (both in ascending slot order); the LRU
+ * order is kept.  Enqueued on `stream`.  Call it between lsa_decode_step
+ * calls, or re-prime the lookahead schedule after it (staged steps and
+ * captured graphs keep the old slots).  A capacity below topk returns
+ * LSA_ERR_SLOTS_LT_TOPK unless the pool allows top-k reduction.  Resident
+ * pools keep every row and ignore the capacity. */
+lsa_status lsa_pool_set_capacity(lsa_pool* pool, int32_t capacity, lsa_stream_t stream);
+int32_t    lsa_pool_capacity(const lsa_pool* pool);
+/* The adaptive policy, over the steps since the previous call (or reset):
+ * with h hits, m misses and x bytes of H2D in `steps` steps, grow by `step`
+ * slots (up to max_capacity) when m/(h+m) > grow_miss_rate or x/steps >
+ * grow_h2d_bytes_per_step; else shrink by `step` (down to min_capacity) when
+ * m/(h+m) < shrink_miss_rate; no lookups, no change.  Synchronises `stream`
+ * (it reads the counters); writes the resulting capacity to *capacity. */
+typedef struct lsa_adapt_policy {
+    double grow_miss_rate;            /* [P1]: 0.5 */
+    double grow_h2d_bytes_per_step;   /* [P1]: 10 MB */
+    double shrink_miss_rate;          /* 0 never shrinks */
+    int32_t step;
+    int32_t min_capacity, max_capacity;
+} lsa_adapt_policy;
+lsa_status lsa_pool_adapt(lsa_pool* pool, const lsa_adapt_policy* policy, int32_t steps, int32_t* capacity,
+                          lsa_stream_t stream);
 /* Synchronises `stream`, then reports counters.  Returns LSA_ERR_NOT_STORED
  * ([P1] error 4) if a step since the last call selected an entry that was never
  * stored (such an entry is staged from whatever its cold row holds). */

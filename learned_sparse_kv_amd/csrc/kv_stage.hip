@@ -175,7 +175,7 @@ __device__ __forceinline__ void kv_stage_body(const StageArgs& a, const int b, c
     const int packed = block_excl_scan<kNT>((hit ? 1 : 0) | (miss ? 1 << 16 : 0), s_scan, &tot);
     const int hit_rank = packed & 0xFFFF, miss_rank = packed >> 16;
     const int n_hit = tot & 0xFFFF, n_miss = tot >> 16;
-    const int free_slots = S - n_used;
+    const int free_slots = L.cap_slots - n_used;   // slots [n_used, capacity) are unused
     const int n_evict = n_miss > free_slots ? n_miss - free_slots : 0;
 
     // 3. untouched used slots in old list order; the last n_evict are evicted
@@ -263,6 +263,103 @@ __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L,
         *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(src + off);
 }
 
+// Shrink of a swapping pool to C usable slots ([P1] future work: adaptive
+// GPU_CHUNKS; the procedure is the oracle's reading).  The first C entries of
+// the LRU list (the most recent) stay and the rest leave the slot table; every
+// staying entry in a slot >= C moves, with its row, to the lowest vacated slot
+// below C, both taken in ascending slot order; the LRU list keeps its order
+// with the new slot ids.  Used slots are always 0..n_used-1, so afterwards
+// they are 0..C-1.  One workgroup per sequence; thread t ranks slots
+// kPer*t .. kPer*t + kPer - 1.
+__global__ __launch_bounds__(kNT) void pool_shrink_kernel(const StageLayer L, const int C) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    int32_t* slot_of = L.slot_of + (int64_t)b * L.cap;
+    int32_t* logical_of = L.logical_of + (int64_t)b * L.S;
+    int32_t* lru = L.lru + (int64_t)b * L.S;
+    const int n_used = L.meta[b * 4 + 0];
+    if (n_used <= C || n_used > L.S) return;   // uniform: every thread read the same count
+    __shared__ int s_scan[kNT / 64 + 1];
+    __shared__ int s_lru[kMaxSlots];     // LRU list before (slot ids)
+    __shared__ int s_log[kMaxSlots];     // occupant of each slot before
+    __shared__ int s_new[kMaxSlots];     // new slot of each old slot, -1 if it leaves
+    __shared__ uint8_t s_keep[kMaxSlots];
+    __shared__ int s_vac[kMaxSlots];     // vacated slots below C, by rank
+    __shared__ int s_high[kMaxSlots];    // staying slots >= C, by rank
+    for (int i = tid; i < n_used; i += kNT) {
+        s_keep[i] = 0;
+        s_log[i] = logical_of[i];
+    }
+    __syncthreads();
+    for (int p = tid; p < n_used; p += kNT) {
+        const int sl = lru[p];
+        s_lru[p] = sl;
+        if (p < C && sl >= 0 && sl < n_used) s_keep[sl] = 1;
+    }
+    __syncthreads();
+    constexpr int kPer = kMaxSlots / kNT;
+    int c_vac = 0, c_high = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int sl = tid * kPer + q;
+        if (sl < n_used) {
+            c_vac += (sl < C && !s_keep[sl]) ? 1 : 0;
+            c_high += (sl >= C && s_keep[sl]) ? 1 : 0;
+        }
+    }
+    int n_vac, n_high;
+    int r_vac = block_excl_scan<kNT>(c_vac, s_scan, &n_vac);
+    int r_high = block_excl_scan<kNT>(c_high, s_scan, &n_high);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int sl = tid * kPer + q;
+        if (sl >= n_used) continue;
+        s_new[sl] = (sl < C && s_keep[sl]) ? sl : -1;
+        if (sl < C && !s_keep[sl]) s_vac[r_vac++] = sl;
+        if (sl >= C && s_keep[sl]) s_high[r_high++] = sl;
+    }
+    __syncthreads();
+    // n_high == n_vac (C entries stay, C - n_vac of them below C); the min only
+    // keeps a damaged table from indexing past the ranked lists
+    const int n_move = n_high < n_vac ? n_high : n_vac;
+    for (int r = tid; r < n_move; r += kNT) s_new[s_high[r]] = s_vac[r];
+    __syncthreads();
+    for (int sl = tid; sl < n_used; sl += kNT) {
+        const int l = s_log[sl];
+        if (l >= 0 && l < L.cap) slot_of[l] = s_new[sl];
+        if (sl >= C) logical_of[sl] = -1;
+    }
+    for (int r = tid; r < n_move; r += kNT) logical_of[s_vac[r]] = s_log[s_high[r]];
+    for (int p = tid; p < n_used; p += kNT) {
+        const int sl = s_lru[p];
+        lru[p] = (p < C && sl >= 0 && sl < n_used) ? s_new[sl] : -1;
+    }
+    // rows of the moved entries: slot row s_high[r] -> slot row s_vac[r]
+    const int cpr = L.row_bytes / 16;
+    char* kv = static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes;
+    // eight 16-byte chunks per thread in flight before their stores
+    const int n_chunks = n_move * cpr;
+    for (int i0 = 0; i0 < n_chunks; i0 += 8 * kNT) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kNT + tid;
+            if (i < n_chunks) {
+                const int r = i / cpr, c = i - r * cpr;
+                v[u] = *reinterpret_cast<const uint4*>(kv + (int64_t)(L.window + s_high[r]) * L.row_bytes + c * 16);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kNT + tid;
+            if (i < n_chunks) {
+                const int r = i / cpr, c = i - r * cpr;
+                *reinterpret_cast<uint4*>(kv + (int64_t)(L.window + s_vac[r]) * L.row_bytes + c * 16) = v[u];
+            }
+        }
+    }
+    if (tid == 0) L.meta[b * 4 + 0] = C;
+}
+
 // Copies the rows a stage recorded as missed (src[b][r] >= 0: cold entry of
 // list row r) from the cold pool into their slots.  One workgroup per 32 list
 // rows of one (layer, sequence); every load of a batch is issued before any
@@ -317,6 +414,12 @@ hipError_t launch_fetch_missed(const StageArgs& a, int phys_stride, hipStream_t 
 
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(kv_stage_kernel, dim3(a.batch, a.n_layers), dim3(kNT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_shrink(const StageLayer& L, int batch, int capacity, hipStream_t s) {
+    if (L.S > kMaxSlots || capacity < 1 || capacity > L.S) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pool_shrink_kernel, dim3(batch), dim3(kNT), 0, s, L, capacity);
     return hipGetLastError();
 }
 

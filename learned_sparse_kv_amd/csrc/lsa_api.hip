@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -171,6 +172,8 @@ struct lsa_pool {
     int64_t cold_stride_b = 0;  // bytes
     bool cold_owned = false;    // false: the caller's cold_buf
     uint64_t d2h_bytes = 0;
+    int32_t capacity = 0;       // slots a swapping pool may use (adaptive GPU_CHUNKS), <= gpu_chunks
+    uint64_t last_hits = 0, last_misses = 0, last_h2d = 0;   // counters at the last lsa_pool_adapt
 };
 
 extern "C" {
@@ -417,6 +420,7 @@ StageLayer stage_layer(const lsa_pool* p, const int32_t* sel, const int32_t* cou
     L.ratio = p->d.ratio;
     L.src_ratio = src_ratio;
     L.S = p->d.gpu_chunks;
+    L.cap_slots = p->capacity;
     L.window = p->d.window;
     L.swap = p->swap;
     L.sel_stride = sel_stride;
@@ -427,9 +431,9 @@ StageLayer stage_layer(const lsa_pool* p, const int32_t* sel, const int32_t* cou
 
 lsa_status stage_check(const lsa_pool* p, int32_t sel_stride, int32_t src_ratio, int32_t phys_stride) {
     if (sel_stride < 1 || sel_stride > 1024) return fail(LSA_ERR_INVALID_ARG, "sel_stride %d not in [1, 1024]", sel_stride);
-    if (p->swap && sel_stride > p->d.gpu_chunks)
-        return fail(LSA_ERR_SLOTS_LT_TOPK, "a step may select %d chunks but the pool has %d gpu_chunks",
-                    sel_stride, p->d.gpu_chunks);
+    if (p->swap && sel_stride > p->capacity)
+        return fail(LSA_ERR_SLOTS_LT_TOPK, "a step may select %d chunks but the pool uses %d slots",
+                    sel_stride, p->capacity);
     if (src_ratio < 1 || p->d.ratio % src_ratio != 0)
         return fail(LSA_ERR_INVALID_ARG, "pool ratio %d is not a multiple of src_ratio %d", p->d.ratio, src_ratio);
     if (phys_stride < p->d.window + sel_stride)
@@ -575,6 +579,7 @@ lsa_status lsa_pool_create(lsa_pool** out, const lsa_pool_desc* d) {
     p->swap = swap;
     p->row_bytes = row_bytes;
     p->rows_per_seq = rows;
+    p->capacity = d->gpu_chunks;
     const int64_t B = d->batch, S = swap ? d->gpu_chunks : 1, C = cap;
     const size_t sz_slot = align_up((size_t)(swap ? B * C : 1) * 4, 256);
     const size_t sz_lo = align_up((size_t)(B * S) * 4, 256);
@@ -680,6 +685,64 @@ lsa_status lsa_pool_reset(lsa_pool* p, lsa_stream_t stream) {
     }
     HIPTRY(hipMemsetAsync(p->meta, 0, (size_t)B * 16, s));
     HIPTRY(hipMemsetAsync(p->stats, 0, (size_t)B * 32, s));
+    p->last_hits = p->last_misses = p->last_h2d = 0;
+    return LSA_OK;
+}
+
+lsa_status lsa_pool_set_capacity(lsa_pool* p, int32_t capacity, lsa_stream_t stream) {
+    if (!p) return fail(LSA_ERR_INVALID_ARG, "pool is NULL");
+    if (capacity < 1 || capacity > p->d.gpu_chunks)
+        return fail(LSA_ERR_INVALID_ARG, "capacity %d not in [1, gpu_chunks = %d]", capacity, p->d.gpu_chunks);
+    if (p->swap && capacity < p->d.topk && !p->d.allow_topk_reduction)
+        return fail(LSA_ERR_SLOTS_LT_TOPK, "capacity (%d) must be >= index_topk (%d)", capacity, p->d.topk);
+    if (p->swap && capacity < p->capacity) {
+        const StageLayer L = stage_layer(p, nullptr, nullptr, 1, 1, nullptr, 0, nullptr);
+        HIPTRY(launch_pool_shrink(L, p->d.batch, capacity, (hipStream_t)stream));
+    }
+    p->capacity = capacity;
+    return LSA_OK;
+}
+
+int32_t lsa_pool_capacity(const lsa_pool* p) { return p ? p->capacity : -1; }
+
+lsa_status lsa_pool_adapt(lsa_pool* p, const lsa_adapt_policy* pol, int32_t steps, int32_t* capacity,
+                          lsa_stream_t stream) {
+    if (!p || !pol) return fail(LSA_ERR_INVALID_ARG, "lsa_pool_adapt: NULL argument");
+    if (pol->step < 1 || pol->min_capacity < 1 || pol->max_capacity > p->d.gpu_chunks ||
+        pol->min_capacity > pol->max_capacity || steps < 0)
+        return fail(LSA_ERR_INVALID_ARG, "policy: step %d, capacity bounds [%d, %d] (gpu_chunks %d), steps %d",
+                    pol->step, pol->min_capacity, pol->max_capacity, p->d.gpu_chunks, steps);
+    if (p->swap && pol->min_capacity < p->d.topk && !p->d.allow_topk_reduction)
+        return fail(LSA_ERR_SLOTS_LT_TOPK, "policy min_capacity (%d) must be >= index_topk (%d)", pol->min_capacity,
+                    p->d.topk);
+    HIPTRY(hipStreamSynchronize((hipStream_t)stream));
+    const int B = p->d.batch;
+    std::vector<uint64_t> st((size_t)B * 4);
+    HIPTRY(hipMemcpy(st.data(), p->stats, st.size() * 8, hipMemcpyDeviceToHost));
+    uint64_t hits = 0, misses = 0, h2d = 0;
+    for (int b = 0; b < B; ++b) {
+        hits += st[b * 4 + 0];
+        misses += st[b * 4 + 1];
+        h2d += st[b * 4 + 2];
+    }
+    const uint64_t h = hits - p->last_hits, m = misses - p->last_misses, x = h2d - p->last_h2d;
+    p->last_hits = hits;
+    p->last_misses = misses;
+    p->last_h2d = h2d;
+    int32_t c = p->capacity;
+    if (h + m > 0) {
+        const double miss_rate = (double)m / (double)(h + m);
+        const double h2d_per_step = (double)x / (double)(steps > 0 ? steps : 1);
+        if (miss_rate > pol->grow_miss_rate || h2d_per_step > pol->grow_h2d_bytes_per_step)
+            c = std::min(pol->max_capacity, c + pol->step);
+        else if (miss_rate < pol->shrink_miss_rate)
+            c = std::max(pol->min_capacity, c - pol->step);
+    }
+    if (c != p->capacity) {
+        lsa_status r = lsa_pool_set_capacity(p, c, stream);
+        if (r != LSA_OK) return r;
+    }
+    if (capacity) *capacity = p->capacity;
     return LSA_OK;
 }
 
@@ -820,11 +883,11 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
         if (!p) return fail(LSA_ERR_INVALID_ARG, "pool %d is NULL", l);
         if (p->d.batch != B || p->d.kv_dim != D || p->d.window != W || p->d.dtype != dt)
             return fail(LSA_ERR_INVALID_ARG, "pool %d: batch, kv_dim, window and dtype must match the step", l);
-        if (p->swap && p->d.gpu_chunks < k_eff) {
+        if (p->swap && p->capacity < k_eff) {
             if (!p->d.allow_topk_reduction)
                 return fail(LSA_ERR_SLOTS_LT_TOPK, "pool %d: gpu_chunks (%d) must be >= index_topk (%d)", l,
-                            p->d.gpu_chunks, d->k);
-            k_eff = p->d.gpu_chunks;
+                            p->capacity, d->k);
+            k_eff = p->capacity;
         }
     }
     lsa_status st = score_args(d->keys, d->key_dtype, d->key_scales, B, d->n_keys, d->n_valid, d->dk, d->q_idx,
@@ -1127,8 +1190,8 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
                         "batch, dtype, gpu_chunks and kv_stride_b of pool 0", i);
         const char* want = static_cast<const char*>(p0->d.kv_buf) + (int64_t)i * B * p0->d.kv_stride_b * eb;
         if (p->d.kv_buf != want) return fail(LSA_ERR_INVALID_ARG, "pool %d: kv_buf is not pool 0's + %d * batch * kv_stride_b", i, i);
-        if (p->swap && p->d.gpu_chunks < d->k)
-            return fail(LSA_ERR_SLOTS_LT_TOPK, "pool %d: gpu_chunks (%d) must be >= k (%d)", i, p->d.gpu_chunks, d->k);
+        if (p->swap && p->capacity < d->k)
+            return fail(LSA_ERR_SLOTS_LT_TOPK, "pool %d: gpu_chunks (%d) must be >= k (%d)", i, p->capacity, d->k);
     }
     LowrankArgs la;
     lsa_status st = lowrank_args(d->U, d->factor_dtype, n_seg, d->T, d->rank, d->S, d->V, d->heads * d->head_dim, d->q,

@@ -167,6 +167,7 @@ struct StageLayer {
     void* kv;                   // kv_buf
     int64_t cap, cold_stride_b, kv_stride_b_bytes;
     int32_t ratio, src_ratio, S, window, swap, sel_stride, phys_stride, row_bytes;
+    int32_t cap_slots;          // slots the pool may use (adaptive capacity), <= S
     // defer_copy: instead of copying missed rows, write src[b][r] = cold entry
     // of list row r for a miss, -1 otherwise; the attention then reads the
     // missed rows from the cold pool and fills their slots
@@ -192,6 +193,8 @@ hipError_t launch_fetch_missed(const StageArgs& a, int phys_stride, hipStream_t 
 hipError_t launch_fm_select_final(const SelectArgs& a, hipStream_t s);
 // copy the rows of entries [first, first+count) of sequence b that are staged
 // from the cold pool into their slots
+// shrink every sequence of a swapping pool to `capacity` slots (tables + rows)
+hipError_t launch_pool_shrink(const StageLayer& L, int batch, int capacity, hipStream_t s);
 hipError_t launch_refresh_staged(const StageLayer& L, int b, int64_t first, int64_t count,
                                  hipStream_t s);
 

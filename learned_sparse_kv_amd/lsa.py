@@ -51,6 +51,11 @@ class PoolStats(ctypes.Structure):
                 ("compressed_cap", i64), ("swap_enabled", i32), ("resident", i32)]
 
 
+class AdaptPolicy(ctypes.Structure):
+    _fields_ = [("grow_miss_rate", f64), ("grow_h2d_bytes_per_step", f64), ("shrink_miss_rate", f64),
+                ("step", i32), ("min_capacity", i32), ("max_capacity", i32)]
+
+
 class StepDesc(ctypes.Structure):
     _fields_ = [("keys", P), ("key_dtype", i32), ("key_scales", P), ("n_keys", i64), ("n_valid", P), ("dk", i32),
                 ("q_idx", P), ("w_idx", P), ("n_idx", i32), ("heads", i32), ("ensemble", i32),
@@ -93,6 +98,9 @@ _SIGS = {
     "lsa_pool_host_rows": (P, [P, i32]),
     "lsa_pool_mark_stored": (i32, [P, i32, i64, i64, P]),
     "lsa_pool_reset": (i32, [P, P]),
+    "lsa_pool_set_capacity": (i32, [P, i32, P]),
+    "lsa_pool_capacity": (i32, [P]),
+    "lsa_pool_adapt": (i32, [P, P, i32, P, P]),
     "lsa_pool_stats": (i32, [P, ctypes.POINTER(PoolStats), P]),
     "lsa_pool_state": (i32, [P, i32, P, P, ctypes.POINTER(i32), P]),
     "lsa_stage": (i32, [P, P, P, i32, i32, P, i32, P, P]),
@@ -364,6 +372,22 @@ class Pool:
 
     def mark_stored(self, b: int, first: int, count: int, stream=None) -> None:
         _check(lib().lsa_pool_mark_stored(self.h, b, first, count, _stream(stream)))
+
+    def set_capacity(self, capacity: int, stream=None) -> None:
+        """Slots the pool may use (lsa_pool_set_capacity): grow, or shrink keeping the most recent entries."""
+        _check(lib().lsa_pool_set_capacity(self.h, int(capacity), _stream(stream)))
+
+    def capacity(self) -> int:
+        return int(lib().lsa_pool_capacity(self.h))
+
+    def adapt(self, steps: int, min_capacity: int, max_capacity: int, step: int, grow_miss_rate: float = 0.5,
+              grow_h2d_bytes_per_step: float = 10e6, shrink_miss_rate: float = 0.0, stream=None) -> int:
+        """Adaptive capacity from the counters since the last call (lsa_pool_adapt); -> the new capacity."""
+        pol = AdaptPolicy(float(grow_miss_rate), float(grow_h2d_bytes_per_step), float(shrink_miss_rate), int(step),
+                          int(min_capacity), int(max_capacity))
+        out = ctypes.c_int32(0)
+        _check(lib().lsa_pool_adapt(self.h, ctypes.byref(pol), int(steps), ctypes.byref(out), _stream(stream)))
+        return int(out.value)
 
     def reset(self, stream=None) -> None:
         _check(lib().lsa_pool_reset(self.h, _stream(stream)))

@@ -64,6 +64,9 @@ def lib():
             "oracle_pool_store": (None, [P, i64, i64]),
             "oracle_pool_stage": (i32, [P, P, i32, P, P, P, P]),
             "oracle_pool_stats": (None, [P, P]),
+            "oracle_pool_set_capacity": (None, [P, i32]),
+            "oracle_pool_capacity": (i32, [P]),
+            "oracle_pool_adapt": (i32, [P, f64, f64, f64, i32, i32, i32, i32]),
             "oracle_pool_state": (i32, [P, P, P]),
             "oracle_attend": (None, [P, i32, i32, P, i32, P, i32, P, i32, f32, P]),
             "oracle_lowrank_score": (None, [P, i64, i32, P, P, i32, P, P]),
@@ -192,6 +195,18 @@ class Pool:
         nm = ctypes.c_int32(0)
         st = lib().oracle_pool_stage(self._h, _p(sel), n, _p(phys), _p(ml), _p(ms), ctypes.byref(nm))
         return int(st), phys, list(zip(ml[:nm.value].tolist(), ms[:nm.value].tolist()))
+
+    def set_capacity(self, capacity: int) -> None:
+        lib().oracle_pool_set_capacity(self._h, int(capacity))
+
+    def capacity(self) -> int:
+        return int(lib().oracle_pool_capacity(self._h))
+
+    def adapt(self, grow_miss: float, grow_h2d: float, shrink_miss: float, step: int, min_c: int, max_c: int,
+              steps: int) -> int:
+        """Adaptive capacity decision over the steps since the last call; -> the new capacity."""
+        return int(lib().oracle_pool_adapt(self._h, float(grow_miss), float(grow_h2d), float(shrink_miss),
+                                           int(step), int(min_c), int(max_c), int(steps)))
 
     def stats(self) -> dict:
         out = np.zeros(4, np.uint64)

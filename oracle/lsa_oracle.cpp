@@ -313,6 +313,8 @@ struct OracleSwapLayerState {
     std::unordered_map<int, int> slot_by_logical;
     std::list<int> slot_lru;                  // slot ids, front = most recently used
     uint64_t hits = 0, misses = 0, h2d_bytes = 0, d2h_bytes = 0;
+    int32_t capacity;                         // slots in use at most (adaptive GPU_CHUNKS)
+    uint64_t last_hits = 0, last_misses = 0, last_h2d = 0;   // counters at the last adapt
 };
 
 void* oracle_pool_new(int64_t cap, int32_t gpu_chunks, int32_t window, int64_t row_bytes) {
@@ -323,6 +325,7 @@ void* oracle_pool_new(int64_t cap, int32_t gpu_chunks, int32_t window, int64_t r
     p->row_bytes = row_bytes;
     p->host_ready.assign(cap, 0);
     p->gpu_slot_logical.assign(gpu_chunks, -1);
+    p->capacity = gpu_chunks;
     return p;
 }
 
@@ -364,7 +367,7 @@ int32_t oracle_pool_stage(void* pool, const int32_t* sel, int32_t n, int32_t* ph
     }
     for (int32_t l : missed) {                  // misses, ascending
         int slot = -1;
-        for (int s = 0; s < p->gpu_chunks; ++s)
+        for (int s = 0; s < p->capacity; ++s)
             if (p->gpu_slot_logical[s] < 0) { slot = s; break; }
         if (slot < 0) {
             slot = p->slot_lru.back();
@@ -382,6 +385,70 @@ int32_t oracle_pool_stage(void* pool, const int32_t* sel, int32_t n, int32_t* ph
     }
     for (int32_t i = 0; i < n; ++i) phys[p->window + i] = p->window + p->slot_by_logical[sel[i]];
     return ST_OK;
+}
+
+// [P1] limitations, future work: adaptive GPU_CHUNKS, the staging capacity
+// adjusted from the runtime LRU hit rate.  The pages give no procedure.
+// Reading: the capacity is the number of slots the pool may use (at most
+// gpu_chunks).  Growing makes more slots available (a miss still takes the
+// lowest unused slot).  Shrinking to C evicts least recently used entries
+// (pop_back) until at most C remain, then moves every remaining entry whose
+// slot is >= C to the lowest vacated slot below C, taking both lists in
+// ascending slot order; its row moves with it and the LRU order is unchanged.
+// A pool whose swap is disabled ignores the capacity.
+void oracle_pool_set_capacity(void* pool, int32_t C) {
+    auto* p = static_cast<OracleSwapLayerState*>(pool);
+    p->capacity = C;
+    if (p->compressed_cap <= p->gpu_chunks) return;
+    while ((int32_t)p->slot_lru.size() > C) {
+        const int slot = p->slot_lru.back();
+        p->slot_lru.pop_back();
+        p->slot_by_logical.erase(p->gpu_slot_logical[slot]);
+        p->gpu_slot_logical[slot] = -1;
+    }
+    std::vector<int> high, vacated;
+    for (int s = C; s < p->gpu_chunks; ++s)
+        if (p->gpu_slot_logical[s] >= 0) high.push_back(s);
+    for (int s = 0; s < C; ++s)
+        if (p->gpu_slot_logical[s] < 0) vacated.push_back(s);
+    for (size_t i = 0; i < high.size(); ++i) {
+        const int from = high[i], to = vacated[i];
+        const int l = p->gpu_slot_logical[from];
+        p->gpu_slot_logical[to] = l;
+        p->gpu_slot_logical[from] = -1;
+        p->slot_by_logical[l] = to;
+        for (int& e : p->slot_lru)
+            if (e == from) e = to;
+    }
+}
+
+int32_t oracle_pool_capacity(void* pool) { return static_cast<OracleSwapLayerState*>(pool)->capacity; }
+
+// [P1] troubleshooting: a miss rate above 50 % or more than 10 MB of H2D per
+// step calls for a larger GPU_CHUNKS; [P1] tuning: a smaller one saves memory
+// at more misses.  Reading of the adaptive policy: over the steps since the
+// last call, grow by `step` slots (up to max_c) when the miss rate exceeds
+// grow_miss or the H2D bytes per step exceed grow_h2d; otherwise shrink by
+// `step` (down to min_c) when the miss rate is below shrink_miss; no lookups,
+// no change.  Returns the new capacity.
+int32_t oracle_pool_adapt(void* pool, double grow_miss, double grow_h2d, double shrink_miss, int32_t step,
+                          int32_t min_c, int32_t max_c, int32_t steps) {
+    auto* p = static_cast<OracleSwapLayerState*>(pool);
+    const uint64_t h = p->hits - p->last_hits, m = p->misses - p->last_misses, x = p->h2d_bytes - p->last_h2d;
+    p->last_hits = p->hits;
+    p->last_misses = p->misses;
+    p->last_h2d = p->h2d_bytes;
+    int32_t C = p->capacity;
+    if (h + m > 0) {
+        const double miss_rate = (double)m / (double)(h + m);
+        const double h2d_per_step = (double)x / (double)(steps > 0 ? steps : 1);
+        if (miss_rate > grow_miss || h2d_per_step > grow_h2d)
+            C = std::min(max_c, C + step);
+        else if (miss_rate < shrink_miss)
+            C = std::max(min_c, C - step);
+    }
+    if (C != p->capacity) oracle_pool_set_capacity(pool, C);
+    return C;
 }
 
 // stats: hits, misses, h2d_bytes, d2h_bytes

@@ -154,3 +154,97 @@ def test_swap_disabled_is_identity():
     assert st == 0 and moved == []
     assert phys.tolist() == list(range(W)) + [W + 0, W + 5, W + 15]
     assert pool.stats()["hits"] == 0 and pool.stats()["misses"] == 0
+
+
+class CapacityLRU(TimestampLRU):
+    """The timestamp LRU with a usable-slot capacity: misses take unused slots
+    below it; shrinking drops the oldest stamps until the capacity holds the
+    rest, then relocates entries above it, lowest first, to the freed slots
+    below it, lowest first (stamps move with their entries)."""
+
+    def __init__(self, S):
+        super().__init__(S)
+        self.C = S
+
+    def step(self, sel):
+        full = self.S
+        self.S = self.C          # unused slots and victims only below the capacity
+        try:
+            return super().step(sel)
+        finally:
+            self.S = full
+
+    def set_capacity(self, C):
+        self.C = C
+        used = [s for s in range(self.S) if self.owner[s] is not None]
+        for s in sorted(used, key=lambda x: self.stamp[x])[:max(0, len(used) - C)]:
+            self.owner[s] = None
+        high = [s for s in range(C, self.S) if self.owner[s] is not None]
+        free = [s for s in range(C) if self.owner[s] is None]
+        for a, b in zip(high, free):
+            self.owner[b], self.stamp[b] = self.owner[a], self.stamp[a]
+            self.owner[a] = None
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_capacity_changes_match_the_timestamp_model(seed):
+    rng = np.random.default_rng(100 + seed)
+    cap, S = int(rng.integers(60, 300)), int(rng.integers(12, 40))
+    pool = oracle.Pool(cap, S, W, 2048)
+    pool.store(0, cap)
+    ref = CapacityLRU(S)
+    c_min = 4
+    for t, sel in enumerate(random_selections(rng, cap, c_min, 60)):
+        if t % 5 == 4:
+            C = int(rng.integers(c_min, S + 1))
+            pool.set_capacity(C)
+            ref.set_capacity(C)
+            sl, lru = pool.state()
+            # shrinking keeps exactly the C most recent entries, in slots 0..n-1
+            assert sorted(s for s in range(S) if sl[s] >= 0) == list(range(min(C, len(lru))))
+        st, phys, moved = pool.stage(np.array(sel, np.int32))
+        assert st == 0
+        r_phys, r_moved, r_lru = ref.step(sel)
+        assert phys.tolist() == r_phys and moved == r_moved
+        sl, lru = pool.state()
+        assert lru.tolist() == r_lru
+        assert [sl[s] for s in range(S)] == [(-1 if o is None else o) for o in ref.owner]
+        assert all(s < pool.capacity() for s in lru)
+
+
+def test_shrink_keeps_most_recent_and_grow_reuses_lowest_slots():
+    pool = oracle.Pool(100, 8, W, 2048)
+    pool.store(0, 100)
+    pool.stage(np.arange(0, 8, dtype=np.int32))          # slots 0..7 hold 0..7
+    pool.stage(np.array([6, 7], np.int32))                # most recent: 7, 6
+    pool.stage(np.array([1], np.int32))                   # then 1
+    pool.set_capacity(3)                                  # keep 1, 7, 6; 6 and 7 move to slots 0 and 2
+    sl, lru = pool.state()
+    assert sl.tolist() == [6, 1, 7, -1, -1, -1, -1, -1]
+    assert lru.tolist() == [1, 2, 0]                      # LRU order of 1, 7, 6 kept
+    st, phys, moved = pool.stage(np.array([50], np.int32))
+    assert moved == [(50, 0)]                             # full at 3: the LRU back (6, slot 0) goes
+    pool.set_capacity(5)
+    st, phys, moved = pool.stage(np.array([60, 61], np.int32))
+    assert moved == [(60, 3), (61, 4)]                    # grown: the lowest unused slots first
+
+
+def test_adapt_policy_decisions():
+    pool = oracle.Pool(1000, 64, W, 2048)
+    pool.store(0, 1000)
+    pool.set_capacity(16)
+    pool.stage(np.arange(0, 16, dtype=np.int32))          # 16 misses: miss rate 1
+    assert pool.adapt(0.5, 10e6, 0.1, 8, 16, 64, 1) == 24
+    pool.stage(np.arange(0, 16, dtype=np.int32))          # all hits: miss rate 0 -> shrink
+    assert pool.adapt(0.5, 10e6, 0.1, 8, 16, 64, 1) == 16
+    pool.stage(np.arange(0, 16, dtype=np.int32))
+    assert pool.adapt(0.5, 10e6, 0.1, 8, 16, 64, 1) == 16  # floor
+    assert pool.adapt(0.5, 10e6, 0.1, 8, 16, 64, 1) == 16  # no lookups, no change
+    pool.stage(np.arange(8, 24, dtype=np.int32))          # 8 hits, 8 misses: 0.5 is not above 0.5
+    assert pool.adapt(0.5, 10e6, 0.1, 8, 16, 64, 1) == 16
+    pool.stage(np.arange(100, 116, dtype=np.int32))       # 16 misses = 32 KB of H2D in 4 steps
+    assert pool.adapt(1.1, 4096, 0.0, 8, 16, 64, 4) == 24  # the H2D rule alone grows
+    for _ in range(6):
+        pool.stage(np.arange(200 + 16 * _, 216 + 16 * _, dtype=np.int32))
+        pool.adapt(0.5, 10e6, 0.1, 32, 16, 64, 1)
+    assert pool.capacity() == 64                          # ceiling
