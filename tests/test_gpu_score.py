@@ -89,6 +89,32 @@ def test_fp8_every_code_in_every_column(dk):
     assert np.array_equal(got, dec)
 
 
+@pytest.mark.parametrize("mix", ["all", "some"])
+def test_fp32_keys_beyond_bf16_precision(mix):
+    """fp32 keys with full 24-bit significands (all keys, or a few scattered among
+    grid keys): within the fp32 accumulation bound of the exact score, and the
+    grid keys around them stay bit-exact."""
+    rng = np.random.default_rng(9 if mix == "all" else 10)
+    B, N, dk, n_idx, H = 1, 3000, 128, 3, 8
+    keys = L.grid_uniform(rng, (N, dk))
+    if mix == "all":
+        keys = rng.standard_normal((N, dk)).astype(np.float32)
+    else:
+        rows = rng.choice(N, size=40, replace=False)
+        keys[rows, rng.integers(0, dk, size=40)] = rng.standard_normal(40).astype(np.float32)
+    q = L.grid_uniform(rng, (B, n_idx, H, dk))
+    w = L.grid_uniform(rng, (B, n_idx, H))
+    s = torch.zeros((B, N), device=DEV)
+    lsa.score(torch.from_numpy(keys[None]).to(DEV), torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV), s)
+    got = s.cpu().numpy()[0].astype(np.float64)
+    want = oracle.score(keys, "f32", q[0], w[0], "max").astype(np.float64)
+    absum = oracle.score(np.abs(keys), "f32", np.abs(q[0]), np.abs(w[0]), "max").astype(np.float64)
+    assert np.all(np.abs(got - want) <= 2 * dk * 2.0 ** -24 * absum + 1e-30)
+    if mix == "some":
+        grid_rows = np.setdiff1d(np.arange(N), rows)
+        assert np.array_equal(bits(got.astype(np.float32)[grid_rows]), bits(want.astype(np.float32)[grid_rows]))
+
+
 @pytest.mark.parametrize("kd", ["bf16", "fp8"])
 def test_general_fp32_query_split_is_exact_per_product(kd):
     """bf16 and fp8 keys meet a query of arbitrary fp32 values (not grid values),
