@@ -77,17 +77,22 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int
     const AttendLayer& L = a.L[bz];
     const int b = by, split = bx;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = split * kR;
+    // the row count and this split's row list load together (one memory round trip)
+    int p = -1, sr = -1;
+    if (tid < kR && r0 + tid < L.phys_stride) {
+        p = L.phys[(int64_t)b * L.phys_stride + r0 + tid];
+        if (L.src) sr = L.src[(int64_t)b * L.phys_stride + r0 + tid];
+    }
     int n = L.n_rows[b];
     n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
-    const int r0 = split * kR;
-    if (r0 >= n) return;
+    if (r0 >= n) return;   // uniform
     const int cnt = n - r0 < kR ? n - r0 : kR;
     const int pair = bz * a.batch + b;
 
     if (tid < kR) {
-        int p = tid < cnt ? L.phys[(int64_t)b * L.phys_stride + r0 + tid] : -1;
+        if (tid >= cnt) p = sr = -1;
         s_ph[tid] = (p >= 0 && p < L.kv_rows) ? p : -1;
-        int sr = (L.src && tid < cnt) ? L.src[(int64_t)b * L.phys_stride + r0 + tid] : -1;
         s_src[tid] = (sr >= 0 && sr < L.cold_rows && s_ph[tid] >= 0) ? sr : -1;
     }
     __syncthreads();
@@ -201,8 +206,9 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
 // One workgroup of NT threads per (layer, sequence, NT/256 consecutive
 // 32-column slices of D): the splits' maxima and denominators are staged in
 // LDS with one parallel load, every thread then merges two outputs over the
-// splits in split order, eight splits' loads in flight at a time.
+// splits in split order.
 constexpr int kCombCols = 32;
+constexpr int kSpec = 24;   // splits whose outputs are loaded before the row count is known (768 rows)
 
 template <int D, int NT = 256>
 __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const int bx, const int by, const int bz) {
@@ -213,14 +219,29 @@ __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const i
     const AttendLayer& L = a.L[bz];
     const int b = by;
     const int tid = threadIdx.x;
-    int n = L.n_rows[b];
-    n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
-    const int ns = (n + kR - 1) / kR;
     const int pair = bz * a.batch + b;
     const int slice = bx * (NT / 256) + (tid >> 8);
     const int d0 = slice * kCombCols;
+    // thread -> (head h, columns d0 + c and d0 + c + 16)
+    const int h = (tid & 255) >> 4, c = tid & 15;
+    const bool mine = h < a.hq && d0 < D;
+    // the row count, every split's maxima and denominators, and this thread's
+    // outputs of the first kSpec splits are loaded at once (entries past the
+    // row count are read but not used), so a list of up to kSpec splits merges
+    // in one memory round trip
     const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
-    for (int i = tid; i < ns * 32; i += NT) s_ml[i] = ml[i];
+    for (int i = tid; i < a.max_splits * 32; i += NT) s_ml[i] = ml[i];
+    const float* po = a.part_acc + (int64_t)pair * a.max_splits * 16 * D + (int64_t)(mine ? h : 0) * D + (mine ? d0 : 0);
+    float x0[kSpec], x1[kSpec];
+#pragma unroll
+    for (int j = 0; j < kSpec; ++j) {
+        const bool in = mine && j < a.max_splits;
+        x0[j] = in ? po[(int64_t)j * 16 * D + c] : 0.0f;
+        x1[j] = in ? po[(int64_t)j * 16 * D + c + 16] : 0.0f;
+    }
+    int n = L.n_rows[b];
+    n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
+    const int ns = (n + kR - 1) / kR;
     __syncthreads();
     if (tid < 16) {
         const int hh = tid;
@@ -235,31 +256,37 @@ __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const i
         s_inv[hh] = 1.0f / den;
     }
     __syncthreads();
-    // thread -> (head h, columns d0 + c and d0 + c + 16)
-    const int h = (tid & 255) >> 4, c = tid & 15;
-    if (h >= a.hq || d0 >= D) return;
+    if (!mine) return;
     float* out = L.out + ((int64_t)b * a.hq + h) * D + d0;
     if (ns == 0) {
         out[c] = 0.0f;
         out[c + 16] = 0.0f;
         return;
     }
-    const float* po = a.part_acc + (int64_t)pair * a.max_splits * 16 * D + (int64_t)h * D + d0;
     float n0 = 0.0f, n1 = 0.0f;
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-        float x0[8], x1[8];
+#pragma unroll
+    for (int j = 0; j < kSpec; ++j) {
+        if (j < ns) {
+            const float f = s_w[j][h];
+            n0 += f * x0[j];
+            n1 += f * x1[j];
+        }
+    }
+    // longer lists: the remaining splits, eight loads in flight at a time
+    for (int s0 = kSpec; s0 < ns; s0 += 8) {
+        float y0[8], y1[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const bool in = s0 + j < ns;
-            x0[j] = in ? po[(int64_t)(s0 + j) * 16 * D + c] : 0.0f;
-            x1[j] = in ? po[(int64_t)(s0 + j) * 16 * D + c + 16] : 0.0f;
+            y0[j] = in ? po[(int64_t)(s0 + j) * 16 * D + c] : 0.0f;
+            y1[j] = in ? po[(int64_t)(s0 + j) * 16 * D + c + 16] : 0.0f;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             if (s0 + j < ns) {
                 const float f = s_w[s0 + j][h];
-                n0 += f * x0[j];
-                n1 += f * x1[j];
+                n0 += f * y0[j];
+                n1 += f * y1[j];
             }
         }
     }
