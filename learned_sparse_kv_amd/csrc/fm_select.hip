@@ -423,11 +423,16 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
     // owns blocks [t*PB, (t+1)*PB)), so the two reads overlap
     const int nb = a.nblk;
     const int PB = (nb + NT - 1) / NT;
+    constexpr int kPB = (MAXB + NT - 1) / NT;   // PB <= kPB whenever nb <= MAXB
     const int32_t* cnt = a.blk_count + (int64_t)seg * nb;
+    // counts stay in registers for the block offsets below (no second read)
+    int c_own[kPB];
     int mine = 0;
-    for (int q = 0; q < PB; ++q) {
+#pragma unroll
+    for (int q = 0; q < kPB; ++q) {
         const int bi = tid * PB + q;
-        if (bi < nb) mine += cnt[bi];
+        c_own[q] = (q < PB && bi < nb) ? cnt[bi] : 0;
+        mine += c_own[q];
     }
     find_boundary<NT>(g, a.k, sh.scan, s_b);
     const int total = s_b[2];
@@ -442,24 +447,41 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
     int off = block_excl_scan<NT>(mine, sh.scan, &n_keep);
     if (K > 0 && n_keep <= kSelKeepCap && nb <= MAXB) {
         // every block's first position in the gathered list
-        for (int q = 0; q < PB; ++q) {
+#pragma unroll
+        for (int q = 0; q < kPB; ++q) {
             const int bi = tid * PB + q;
-            if (bi >= nb) break;
-            s_start[bi] = off;
-            off += cnt[bi];
+            if (q < PB && bi < nb) s_start[bi] = off;
+            off += c_own[q];
         }
         if (tid == 0) s_start[nb] = n_keep;
         __syncthreads();
-        // all threads copy: entry p belongs to the last block starting at or before p
-        for (int p = tid; p < n_keep; p += NT) {
-            int lo = 0, hi = nb - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_start[mid] <= p) lo = mid; else hi = mid - 1;
+        // all threads copy: entry p belongs to the last block starting at or before p.
+        // A thread's entries are all loaded before any is stored, so the gather
+        // costs one memory round trip however many entries each thread takes.
+        constexpr int kGather = (kSelKeepCap + NT - 1) / NT;
+        int32_t g_idx[kGather];
+        uint32_t g_key[kGather];
+#pragma unroll
+        for (int i = 0; i < kGather; ++i) {
+            const int p = tid + i * NT;
+            if (p < n_keep) {
+                int lo = 0, hi = nb - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_start[mid] <= p) lo = mid; else hi = mid - 1;
+                }
+                const int64_t src = ((int64_t)seg * nb + lo) * kColBlk + (p - s_start[lo]);
+                g_idx[i] = a.blk_idx[src];
+                g_key[i] = a.blk_key[src];
             }
-            const int64_t src = ((int64_t)seg * nb + lo) * kColBlk + (p - s_start[lo]);
-            s_idx[p] = a.blk_idx[src];
-            s_key[p] = a.blk_key[src];
+        }
+#pragma unroll
+        for (int i = 0; i < kGather; ++i) {
+            const int p = tid + i * NT;
+            if (p < n_keep) {
+                s_idx[p] = g_idx[i];
+                s_key[p] = g_key[i];
+            }
         }
         __syncthreads();
         // two radix passes over bits 20..0 of the candidates' keys (bucket b* fixes

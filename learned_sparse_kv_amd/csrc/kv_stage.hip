@@ -133,6 +133,10 @@ __device__ __forceinline__ void kv_stage_body(const StageArgs& a, const int b, c
     }
     int n_l;
     const int pos = block_excl_scan<kNT>(keep ? 1 : 0, s_scan, &n_l);
+    // wait for the two table loads here, on every lane: consumed only under
+    // `keep`, they would otherwise leave the compiler waiting for all memory
+    // operations (the stores below included) before each later store
+    asm volatile("" ::"v"(my_slot), "v"((int)my_rdy));
     if (keep) {
         s_sel[pos] = m;
         s_slot[pos] = my_slot;

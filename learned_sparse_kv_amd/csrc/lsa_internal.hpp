@@ -40,14 +40,17 @@ __device__ inline uint32_t order_key(float x) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, in six DPP adds: shifts by
+// 1, 2, 4 and 8 lanes within each 16-lane row (a lane with no source adds 0),
+// then lane 15's total into rows 1 and 3 and lane 31's total into rows 2 and
+// 3.  No LDS permute, so a scan costs a few VALU latencies.
 __device__ inline int wave_incl_scan(int v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
     return v;
 }
 
@@ -73,28 +76,23 @@ __device__ inline void hist_add(uint32_t* hist, bool act, uint32_t dg) {
 }
 
 // Exclusive block-wide prefix sum for blockDim.x == NT (multiple of 64);
-// `smem` needs NT/64 + 1 ints.  Returns the exclusive prefix; *total = sum.
+// `smem` needs NT/64 ints.  Returns the exclusive prefix; *total = sum.
 template <int NT>
 __device__ inline int block_excl_scan(int v, int* smem, int* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    static_assert(NT % 64 == 0 && NT <= 4096, "whole waves, at most 64");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     constexpr int NW = NT / 64;
     const int incl = wave_incl_scan(v);
     if (lane == 63) smem[wave] = incl;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int w = 0; w < NW; ++w) {
-            const int t = smem[w];
-            smem[w] = run;
-            run += t;
-        }
-        smem[NW] = run;
-    }
-    __syncthreads();
-    const int res = smem[wave] + incl - v;
-    *total = smem[NW];
-    __syncthreads();
-    return res;
+    // every wave scans the wave totals itself (one LDS read per lane), so the
+    // block needs no serial pass and no third barrier phase
+    const int wt = wave_incl_scan(lane < NW ? smem[lane] : 0);
+    const int before = __builtin_amdgcn_readlane(wt, wave > 0 ? wave - 1 : 0);
+    *total = __builtin_amdgcn_readlane(wt, NW - 1);
+    __syncthreads();   // smem is free again for the caller's next scan
+    return (wave > 0 ? before : 0) + incl - v;
 }
 
 // ------------------------------------------------------------------ launchers
