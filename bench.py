@@ -469,9 +469,11 @@ def bench_kvswap(args):
     # per-kernel times: the same steps again with HIP events on the launch stream
     dw.ctx.set_timing(True)
     dw.ctx.timing_read()
+    stats_e0 = [p.stats() for p in dw.pools]
     for t in range(Wm, Wm + K):
         dw.step(t)
     kt = dw.ctx.timing_read()
+    stats_e1 = [p.stats() for p in dw.pools]
     dw.ctx.set_timing(False)
     names = ["score", "select", "stage", "attend"]
     avg = {k: (kt[k][0] / kt[k][1] if kt[k][1] else 0.0) for k in names}
@@ -481,8 +483,14 @@ def bench_kvswap(args):
     attend_bytes = float(n_rows.sum()) * wl.row_elems * 2
     hits = sum(b["hits"] - a["hits"] for a, b in zip(stats0, stats1))
     misses = sum(b["misses"] - a["misses"] for a, b in zip(stats0, stats1))
+    # rows that missed in the event-timed steps are read from the cold store and
+    # also written into their slots: that write is part of the attention's traffic
+    misses_ev = sum(b["misses"] - a["misses"] for a, b in zip(stats_e0, stats_e1)) / K
+    attend_written = misses_ev * wl.row_elems * 2
     score_gbs = scan_bytes / (avg["score"] * 1e-3) / 1e9
     attend_gbs = attend_bytes / (avg["attend"] * 1e-3) / 1e9
+    attend_rw_gbs = (attend_bytes + attend_written) / (avg["attend"] * 1e-3) / 1e9
+    sa_frac = (scan_bytes + attend_bytes + attend_written) / ((avg["score"] + avg["attend"]) * 1e-3) / 1e9 / HBM_PEAK_GBS
     roofline = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "lowrank_p + lowrank_scan",
                 "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(avg["score"] * 1e3, 2)}
@@ -523,7 +531,9 @@ def bench_kvswap(args):
                    "slots": wl.slots, "segments": n_seg, "launch": "eager"},
         "roofline": roofline,
         "attend": {"achieved_gbs": round(attend_gbs, 1), "bytes_per_launch": attend_bytes,
+                   "bytes_written_per_launch": round(attend_written), "achieved_gbs_read_and_written": round(attend_rw_gbs, 1),
                    "avg_launch_us": round(avg["attend"] * 1e3, 2)},
+        "score_attend_hbm_frac": round(sa_frac, 4),
         "cpu_baseline": cpu,
         "kernels_us": {k: round(avg[k] * 1e3, 2) for k in names},
         "hit_rate": round(hits / max(1, hits + misses), 4),
