@@ -9,7 +9,9 @@ Default workload: 1M-token context, ratio-4 source layer of 262144 entries,
 Two schedules are timed: "lookahead" (lsa_lookahead_step: the current step's
 row copy and attention share launches with the next step's score and
 selection) and "sync" (lsa_decode_step: all of it in order).  `value` is the
---schedule one (default lookahead); the other is reported beside it.
+--schedule one (default lookahead); the other is reported beside it.  With a
+1M workload the run also times the 256K threshold workload (batch 4, bf16
+rows) in both schedules, reported as `ctx_256k`.
 
 Prints ONE JSON line.  Per-kernel times come from HIP events recorded on the
 launch stream inside the timed region; the CPU baseline is the plain oracle
@@ -233,6 +235,10 @@ def main():
     # workload); and the time of one shrink of every swapping pool
     adaptive = adaptive_capacity(dw, wl, Wm + K)
 
+    # ---- the metric's other context length: the 256K threshold workload (batch 4,
+    # bf16 rows), both schedules launched eagerly, K steps each
+    ctx256 = other_context("thresh_256k", K, Wm) if wl.name.startswith("swap_1m") else None
+
     # ---- algorithmic bytes (per launch)
     # a key row (plus its E8M0 block scales for the MX dtypes) read, a score written
     key_row = wl.dk * L.DTYPE_BYTES[wl.key_dtype] + (wl.dk // 32 if wl.key_dtype in L.MX_DTYPES else 0)
@@ -335,6 +341,7 @@ def main():
         "cpu_baseline": cpu,
         "project": proj,
         "adaptive_capacity": adaptive,
+        "ctx_256k": ctx256,
         "kernels_us_events": {k: round(avg[k] * 1e3, 2) for k in KERNELS},
         "score_attend_hbm_frac": round(sa_frac, 4),
         "attend_resident": {"us": round(att_res_ms * 1e3, 2), "bytes": int(attend_bytes),
@@ -346,6 +353,44 @@ def main():
         "fm_score_src": src_hash,
     }
     print(json.dumps(res), flush=True)
+
+
+def other_context(name, K, Wm):
+    """Decode steps/s of another workload (its own set-up; pools start empty; eager
+    launches; the lookahead schedule with descriptors marshalled beforehand)."""
+    import torch
+
+    import lsa_inputs as L
+    from learned_sparse_kv_amd.workload import DeviceWorkload
+
+    wl = L.WORKLOADS[name]
+    dw = DeviceWorkload(wl, keep_host=False, log=log)
+    dw.make_steps(Wm + K + 2)
+    res = {"workload": name, "ctx": wl.ctx, "batch": wl.batch, "src_entries": wl.n_src,
+           "sparse_layer_ratios": list(wl.layer_ratios), "select": f"{wl.mode} cap {wl.k}", "kv_dtype": wl.kv_dtype,
+           "key_dtype": wl.key_dtype, "cold_pool": wl.cold}
+    for schedule in ("lookahead", "sync"):
+        dw.reset_pools()
+        la = schedule == "lookahead"
+        if la:
+            dw.lookahead_prime(0)
+        eager = dw.lookahead_step if la else dw.step
+        for t in range(Wm):
+            eager(t)
+        if la:
+            dw.prepare_lookahead(range(Wm, Wm + K))
+            eager = dw.run_prepared
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(Wm, Wm + K):
+            eager(t)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / K
+        res[schedule] = {"value": round(1e3 / ms, 2), "unit": "steps/s", "ms_per_step": round(ms, 5)}
+        log(f"{name} {schedule} (eager): {ms * 1e3:.1f} us/step")
+    del dw
+    torch.cuda.empty_cache()
+    return res
 
 
 def adaptive_capacity(dw, wl, n_steps):

@@ -12,11 +12,13 @@
 //
 // * Segments of at most 32768 entries: one 1024-thread workgroup holds the
 //   keys in registers (contiguous indices per thread, so thread order is index
-//   order), finds the K-th largest key T with four 8-bit radix passes over an
-//   LDS histogram, and compacts {key > T} plus the lowest-indexed keys equal to
-//   T with two block scans.  Histogram atomics are pre-aggregated per wave:
-//   the lanes sharing the first active lane's digit add with one atomic, which
-//   removes the contention of clustered high digits.
+//   order), finds the K-th largest key T with three radix passes (12, 10 and
+//   10 bits) over LDS histograms -- the last two over the first pass's
+//   boundary bin, compacted into LDS -- and compacts {key > T} plus the
+//   lowest-indexed keys equal to T with two block scans.  The atomics of the
+//   last two passes are pre-aggregated per wave (the lanes sharing the first
+//   active lane's digit add with one atomic), which removes the contention of
+//   clustered digits.
 //
 // * Longer segments: (1) every 4096-entry block builds an 11-bit key histogram
 //   in LDS and adds it to a per-segment global histogram; (2) every 1024-entry
@@ -77,42 +79,135 @@ __device__ inline void find_digit(const uint32_t* hist, int rem, KthShared& sh) 
     __syncthreads();
 }
 
-// K-th largest key among the valid ones (1 <= K <= #valid).  Returns T and the
-// number of keys equal to T that belong to the top K.
+// Over hist[0, NB) taken from the top bin down: the bin holding the rem-th
+// largest entry (1 <= rem <= the histogram's total); *bin = it, *above =
+// entries in the bins above it.  Thread t of the NT owns bins NB-1-PER*t-i.
+template <int NB, int NT>
+__device__ void find_bin(const uint32_t* hist, int rem, int* scan, int* out, int* bin, int* above) {
+    constexpr int PER = NB / NT;
+    static_assert(PER >= 1 && NB % NT == 0, "bins per thread");
+    const int t = threadIdx.x;
+    int c[PER];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        c[i] = (int)hist[NB - 1 - PER * t - i];
+        local += c[i];
+    }
+    int tot;
+    int run = block_excl_scan<NT>(local, scan, &tot);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (run < rem && run + c[i] >= rem) {
+            out[0] = NB - 1 - PER * t - i;
+            out[1] = run;
+        }
+        run += c[i];
+    }
+    __syncthreads();
+    *bin = out[0];
+    *above = out[1];
+    __syncthreads();
+}
+
+constexpr int kWideBins = 4096;   // first digit: key bits 31..20 (sign, exponent, 3 mantissa bits)
+constexpr int kWideCand = 4096;   // keys of the first digit's boundary bin resolved from LDS
+
+struct KthWide {
+    uint32_t hist[kWideBins];
+    uint32_t cand[kWideCand];
+    int scan[kNW + 1];
+    int out[2];
+};
+
+// K-th largest key among the valid ones (1 <= K <= #valid): T, and the number
+// of keys equal to T that belong to the top K.  Three radix passes of 12, 10
+// and 10 bits.  The first runs over every entry with 4096 bins, which spread
+// float keys far better than the top byte (sign and 7 exponent bits: a dozen
+// bins, so the histogram atomics serialised).  The keys of its boundary bin
+// are then compacted into LDS (when they fit) and the last two passes run over
+// them alone.
 template <int E>
-__device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int K, KthShared& sh,
+__device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int K, KthWide& sh,
                           uint32_t* T_out, int* need_eq_out) {
-    uint32_t prefix = 0, mask = 0;
-    int rem = K;
-#pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0u;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kWideBins; i += kNT) sh.hist[i] = 0u;
+    __syncthreads();
+    // plain atomics: over 4096 bins a wave's lanes rarely share one, so the
+    // per-wave pre-aggregation (a cross-lane read per entry) costs more than
+    // the collisions it saves (304 against 352 us for 4096 x 32768 entries);
+    // all-equal keys are the worst case, about twice as slow as pre-aggregated
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (valid[e]) atomicAdd(&sh.hist[key[e] >> 20], 1u);
+    __syncthreads();
+    int bin, above;
+    find_bin<kWideBins, kNT>(sh.hist, K, sh.scan, sh.out, &bin, &above);
+    const uint32_t d0 = (uint32_t)bin;
+    const int c0 = (int)sh.hist[d0];
+    int rem = K - above;
+    __syncthreads();   // every thread has read c0 before the histogram is cleared
+    uint32_t d1;
+    if (c0 <= kWideCand) {
+        int mine = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) mine += (valid[e] && (key[e] >> 20) == d0) ? 1 : 0;
+        int tot;
+        int off = block_excl_scan<kNT>(mine, sh.scan, &tot);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (valid[e] && (key[e] >> 20) == d0) sh.cand[off++] = key[e] & 0xFFFFFu;
+        for (int i = tid; i < 1024; i += kNT) sh.hist[i] = 0u;
+        __syncthreads();
+        for (int p0 = 0; p0 < c0; p0 += kNT) {
+            const int p = p0 + tid;
+            const bool act = p < c0;
+            hist_add(sh.hist, act, act ? sh.cand[p] >> 10 : 0u);
+        }
+        __syncthreads();
+        find_bin<1024, kNT>(sh.hist, rem, sh.scan, sh.out, &bin, &above);
+        d1 = (uint32_t)bin;
+        rem -= above;
+        for (int i = tid; i < 1024; i += kNT) sh.hist[i] = 0u;
+        __syncthreads();
+        for (int p0 = 0; p0 < c0; p0 += kNT) {
+            const int p = p0 + tid;
+            const bool act = p < c0 && (sh.cand[p] >> 10) == d1;
+            hist_add(sh.hist, act, act ? sh.cand[p] & 1023u : 0u);
+        }
+        __syncthreads();
+    } else {
+        // too many keys in the boundary bin: the same two passes over the registers
+        for (int i = tid; i < 1024; i += kNT) sh.hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) hist_add(sh.hist, valid[e] && (key[e] >> 20) == d0, (key[e] >> 10) & 1023u);
+        __syncthreads();
+        find_bin<1024, kNT>(sh.hist, rem, sh.scan, sh.out, &bin, &above);
+        d1 = (uint32_t)bin;
+        rem -= above;
+        for (int i = tid; i < 1024; i += kNT) sh.hist[i] = 0u;
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            hist_add(sh.hist, valid[e] && (key[e] & mask) == prefix, (key[e] >> shift) & 255u);
-        __syncthreads();
-        find_digit(sh.hist, rem, sh);
-        prefix |= sh.digit << shift;
-        mask |= 255u << shift;
-        rem -= sh.above;
+            hist_add(sh.hist, valid[e] && (key[e] >> 10) == ((d0 << 10) | d1), key[e] & 1023u);
         __syncthreads();
     }
-    *T_out = prefix;
-    *need_eq_out = rem;
+    find_bin<1024, kNT>(sh.hist, rem, sh.scan, sh.out, &bin, &above);
+    *T_out = (d0 << 20) | (d1 << 10) | (uint32_t)bin;
+    *need_eq_out = rem - above;
 }
 
 // Marks the chosen keys (all > T, plus the first need_eq equal to T in thread
 // order = index order) and returns the first output position of this thread.
 template <int E>
 __device__ void block_choose(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t T, int need_eq,
-                             KthShared& sh, bool (&take)[E], int* pos0) {
+                             int* scan, bool (&take)[E], int* pos0) {
     int c_eq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) c_eq += (valid[e] && key[e] == T) ? 1 : 0;
     int tot;
-    int r = block_excl_scan<kNT>(c_eq, sh.scan, &tot);
+    int r = block_excl_scan<kNT>(c_eq, scan, &tot);
     int c_sel = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -122,7 +217,7 @@ __device__ void block_choose(const uint32_t (&key)[E], const bool (&valid)[E], u
         r += eq ? 1 : 0;
         c_sel += take[e] ? 1 : 0;
     }
-    *pos0 = block_excl_scan<kNT>(c_sel, sh.scan, &tot);
+    *pos0 = block_excl_scan<kNT>(c_sel, scan, &tot);
 }
 
 template <int E>
@@ -151,7 +246,7 @@ __device__ inline void load_scores(const float* sc, int64_t base, int n_valid, f
 // ---------------------------------------------------------------- path 0
 template <int E>
 __global__ __launch_bounds__(kNT) void select_single(const SelectArgs a) {
-    __shared__ KthShared sh;
+    __shared__ KthWide sh;
     const int tid = threadIdx.x;
     const int seg = blockIdx.x;
     const int n_valid = seg_valid(a, seg);
@@ -183,7 +278,7 @@ __global__ __launch_bounds__(kNT) void select_single(const SelectArgs a) {
     block_kth<E>(key, valid, K, sh, &T, &need_eq);
     bool take[E];
     int pos;
-    block_choose<E>(key, valid, T, need_eq, sh, take, &pos);
+    block_choose<E>(key, valid, T, need_eq, sh.scan, take, &pos);
 #pragma unroll
     for (int e = 0; e < E; ++e)
         if (take[e] && pos < a.stride) out_sel[pos++] = (int32_t)(base + e);
@@ -373,37 +468,6 @@ __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid,
         run_eq += tot_eq;
         run_out += tot_take;
     }
-}
-
-// Over hist[0, NB) taken from the top bin down: the bin holding the rem-th
-// largest entry (1 <= rem <= the histogram's total); *bin = it, *above =
-// entries in the bins above it.  Thread t of the NT owns bins NB-1-PER*t-i.
-template <int NB, int NT>
-__device__ void find_bin(const uint32_t* hist, int rem, int* scan, int* out, int* bin, int* above) {
-    constexpr int PER = NB / NT;
-    static_assert(PER >= 1 && NB % NT == 0, "bins per thread");
-    const int t = threadIdx.x;
-    int c[PER];
-    int local = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        c[i] = (int)hist[NB - 1 - PER * t - i];
-        local += c[i];
-    }
-    int tot;
-    int run = block_excl_scan<NT>(local, scan, &tot);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        if (run < rem && run + c[i] >= rem) {
-            out[0] = NB - 1 - PER * t - i;
-            out[1] = run;
-        }
-        run += c[i];
-    }
-    __syncthreads();
-    *bin = out[0];
-    *above = out[1];
-    __syncthreads();
 }
 
 // One workgroup of NT threads per segment: gathers the blocks' kept entries (global index
