@@ -31,7 +31,9 @@
 // adds its issue time to the chain), so the loop keeps VALU work to the
 // epilogue: integer-max ReLU, head weights, a permlane32 swap for the other
 // half's heads, and the ensemble.  Tiles are taken per sequence, so the
-// queries, weights and buffer resources stay fixed in the inner loop.  The
+// queries, weights and buffer resources stay fixed in the inner loop; with
+// several sequences the waves split into one group per sequence, so each
+// wave's pipeline and query set-up start once.  The
 // grid is one 4-wave workgroup per CU (two for fp8 keys; fewer when the scan
 // is short), which keeps every wave's share of tiles equal.
 #include "lsa_internal.hpp"
@@ -203,9 +205,20 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps tile state in SGPRs
     const int col = lane & 31;      // key within a 32-key block (B/D column); query row for A
     const int half = lane >> 5;     // which half of dk this lane feeds
-    const int total = a.tile_start[a.batch];
-    const int stride = gx * kWaves;
+    int total = a.tile_start[a.batch];
+    int stride = gx * kWaves;
     int t = bx * kWaves + wave;
+    if (a.batch > 1 && stride >= a.batch) {
+        // several sequences: the waves split into one equal group per sequence, so
+        // a wave's tiles all lie in one sequence and its load pipeline (and query
+        // set-up) starts once, not once per sequence; the waves left over idle
+        const int per = stride / a.batch;
+        const int bq = t / per;
+        if (bq >= a.batch) return;
+        t = a.tile_start[bq] + (t - bq * per);
+        total = a.tile_start[bq + 1];
+        stride = per;
+    }
 
     const char* kbase = static_cast<const char*>(a.keys);
     const __amdgpu_buffer_rsrc_t zero_r = make_rsrc(kbase, 0u);     // every read returns zero
