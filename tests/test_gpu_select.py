@@ -85,3 +85,19 @@ def test_many_segments_kvswap_shape():
     rng = np.random.default_rng(9)
     e = L.grid_uniform(rng, (64, 32768), lo=-64, hi=64, step=1 / 16)
     run(e, 400)
+
+
+@pytest.mark.parametrize("N", [5000, 32768])
+def test_single_workgroup_crowded_boundary_bin(N):
+    # segments of one workgroup whose K-th largest key shares its top 12 bits with
+    # more than 4096 others: the last two radix passes then run over the registers
+    rng = np.random.default_rng(N + 7)
+    e = np.zeros((4, N), np.float32)
+    e[1, ::3] = 1.0                                     # a third equal, the rest below
+    # distinct values in [1, 1.125): one 12-bit bin, they differ only in lower bits
+    e[2] = (1.0 + rng.permutation(N).astype(np.float64) * 2.0 ** -20).astype(np.float32)
+    e[3] = e[2]
+    e[3, ::5] = 2.0                                     # some above the crowded bin
+    for k in (1, 400, 512):
+        say(f"select crowded boundary bin N={N} k={k}")
+        run(e, k)
