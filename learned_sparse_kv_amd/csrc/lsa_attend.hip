@@ -78,6 +78,19 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int
     const int b = by, split = bx;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r0 = split * kR;
+    // scores: S[h][r] = q[h] . row[r]; wave = (row block nb, quarter kq of D).  The
+    // query loads go first, unconditionally (a head past hq reads head 0 and is
+    // zeroed after), so they overlap the row-list round trip instead of waiting
+    // behind the row loads
+    const int nb = wave & 1, kq = wave >> 1;
+    const int h = lane & 15, g = lane >> 4;
+    const int e0 = kq * (D / 4) + g * QK_STEPS;
+    f32x4 q4[QK_STEPS / 4];
+    {
+        const float* qp = L.q + ((int64_t)b * a.hq + (h < a.hq ? h : 0)) * D + e0;
+#pragma unroll
+        for (int s = 0; s < QK_STEPS; s += 4) q4[s / 4] = *reinterpret_cast<const f32x4*>(qp + s);
+    }
     // the row count and this split's row list load together (one memory round trip)
     int p = -1, sr = -1;
     if (tid < kR && r0 + tid < L.phys_stride) {
@@ -89,6 +102,10 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int
     if (r0 >= n) return;   // uniform
     const int cnt = n - r0 < kR ? n - r0 : kR;
     const int pair = bz * a.batch + b;
+    // wait for the row list here, on every lane: loaded under a branch, it would
+    // otherwise make the compiler wait for every outstanding load before each
+    // row load that reuses its registers, one round trip per row load
+    asm volatile("" ::"v"(p), "v"(sr));
 
     if (tid < kR) {
         if (tid >= cnt) p = sr = -1;
@@ -117,22 +134,9 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int
             if (s_src[r] >= 0) *reinterpret_cast<uint4*>(kvw + (int64_t)s_ph[r] * RB + cc * 16) = v[i];
         }
     }
-    // scores: S[h][r] = q[h] . row[r]; wave = (row block nb, quarter kq of D)
-    const int nb = wave & 1, kq = wave >> 1;
-    const int h = lane & 15, g = lane >> 4;
-    const int e0 = kq * (D / 4) + g * QK_STEPS;
     float qa[QK_STEPS];
-    {
-        const float* qp = L.q + ((int64_t)b * a.hq + (h < a.hq ? h : 0)) * D + e0;
 #pragma unroll
-        for (int s = 0; s < QK_STEPS; s += 4) {
-            f32x4 q4 = h < a.hq ? *reinterpret_cast<const f32x4*>(qp + s) : f32x4{0.f, 0.f, 0.f, 0.f};
-            qa[s] = q4[0];
-            qa[s + 1] = q4[1];
-            qa[s + 2] = q4[2];
-            qa[s + 3] = q4[3];
-        }
-    }
+    for (int s = 0; s < QK_STEPS; ++s) qa[s] = h < a.hq ? q4[s / 4][s % 4] : 0.0f;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) *reinterpret_cast<uint4*>(tile + (rr + i * RSTEP) * LS + cc * 16) = v[i];
     __syncthreads();
@@ -229,15 +233,34 @@ __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const i
     // outputs of the first kSpec splits are loaded at once (entries past the
     // row count are read but not used), so a list of up to kSpec splits merges
     // in one memory round trip
-    const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
-    for (int i = tid; i < a.max_splits * 32; i += NT) s_ml[i] = ml[i];
+    // (every load below is unconditional, on a clamped index, and all are issued
+    // before the first is used: a load under a branch would make the compiler
+    // wait for everything outstanding at the join)
     const float* po = a.part_acc + (int64_t)pair * a.max_splits * 16 * D + (int64_t)(mine ? h : 0) * D + (mine ? d0 : 0);
     float x0[kSpec], x1[kSpec];
 #pragma unroll
     for (int j = 0; j < kSpec; ++j) {
+        const int jj = j < a.max_splits ? j : a.max_splits - 1;
+        x0[j] = po[(int64_t)jj * 16 * D + c];
+        x1[j] = po[(int64_t)jj * 16 * D + c + 16];
+    }
+    const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
+    constexpr int kMlPer = (kMaxSplits * 32 + NT - 1) / NT;
+    const int n_ml = a.max_splits * 32;
+    float mlv[kMlPer];
+#pragma unroll
+    for (int q = 0; q < kMlPer; ++q) {
+        const int i = tid + q * NT;
+        mlv[q] = ml[i < n_ml ? i : n_ml - 1];
+    }
+#pragma unroll
+    for (int q = 0; q < kMlPer; ++q)
+        if (tid + q * NT < n_ml) s_ml[tid + q * NT] = mlv[q];
+#pragma unroll
+    for (int j = 0; j < kSpec; ++j) {
         const bool in = mine && j < a.max_splits;
-        x0[j] = in ? po[(int64_t)j * 16 * D + c] : 0.0f;
-        x1[j] = in ? po[(int64_t)j * 16 * D + c + 16] : 0.0f;
+        x0[j] = in ? x0[j] : 0.0f;
+        x1[j] = in ? x1[j] : 0.0f;
     }
     int n = L.n_rows[b];
     n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
