@@ -25,8 +25,9 @@
 //   block finds the boundary bucket b* holding the K-th largest key from that
 //   histogram and keeps, in index order (block scan, no atomics), its entries
 //   in buckets >= b*; (3) one workgroup per segment gathers the kept entries in
-//   block order -- which is global index order -- resolves b* with two radix
-//   passes (11 + 10 bits) over the 21 key bits below the bucket, and places {above b*} +
+//   block order -- which is global index order -- resolves b* over the 21 key
+//   bits below the bucket (a radix pass over 11 bits, then the last 10 by ranking
+//   the few keys of the bin found, or by a second radix pass), and places {above b*} +
 //   {candidates > T} + {the first candidates equal to T}: ties fall to the
 //   lowest index because the list is in index order, and the output is
 //   already ascending.  If more than 8192 entries are kept, step (3) falls back
@@ -471,8 +472,11 @@ __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid,
 }
 
 // One workgroup of NT threads per segment: gathers the blocks' kept entries (global index
-// order), resolves the boundary bucket with two radix passes over the 21 key
-// bits below it, and writes the chosen indices (already ascending).
+// order), resolves the boundary bucket with a radix pass over key bits 20..10
+// and then bits 9..0 -- by ranking the members of the bin found when they are
+// few, else by a second radix pass -- and writes the chosen indices (already
+// ascending).
+constexpr int kFewMembers = 64;
 template <int NT, int MAXB = kMaxBlocks>
 __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int seg) {
     __shared__ KthShared sh;
@@ -481,6 +485,8 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
     __shared__ uint32_t s_key[kSelKeepCap];
     __shared__ int s_start[MAXB + 1];
     __shared__ uint32_t s_h2[2048];
+    __shared__ uint32_t s_few[kFewMembers];
+    __shared__ int s_few_n, s_few_t[2];
     const int tid = threadIdx.x;
     uint32_t* g = a.hist + (int64_t)seg * kSelBins;
     // the blocks' counts are loaded before the histogram is scanned (thread t
@@ -548,32 +554,68 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
             }
         }
         __syncthreads();
-        // two radix passes over bits 20..0 of the candidates' keys (bucket b* fixes
-        // the rest): bits 20..10, then bits 9..0 of the candidates in the bin found
+        // bits 20..0 of the candidates' keys (bucket b* fixes the rest): a radix
+        // pass over bits 20..10, then bits 9..0 of the candidates in the bin found
         const int need = K - above;
         for (int i = tid; i < 2048; i += NT) s_h2[i] = 0u;
         __syncthreads();
+        // (plain atomics: 2048 bins spread these digits; see select_single)
         for (int p0 = 0; p0 < n_keep; p0 += NT) {
             const int p = p0 + tid;
-            const bool act = p < n_keep && s_idx[p] < 0;
-            hist_add(s_h2, act, p < n_keep ? (s_key[p] >> 10) & 2047u : 0u);
+            if (p < n_keep && s_idx[p] < 0) atomicAdd(&s_h2[(s_key[p] >> 10) & 2047u], 1u);
         }
         __syncthreads();
         int bin, bin_above;
         find_bin<2048, NT>(s_h2, need, sh.scan, s_b, &bin, &bin_above);
         const uint32_t d1 = (uint32_t)bin;
-        int rem = need - bin_above;
-        for (int i = tid; i < 1024; i += NT) s_h2[i] = 0u;
-        __syncthreads();
-        for (int p0 = 0; p0 < n_keep; p0 += NT) {
-            const int p = p0 + tid;
-            const bool act = p < n_keep && s_idx[p] < 0 && ((s_key[p] >> 10) & 2047u) == d1;
-            hist_add(s_h2, act, p < n_keep ? s_key[p] & 1023u : 0u);
+        const int rem = need - bin_above;
+        const int c_d1 = (int)s_h2[d1];   // candidates in bin d1; 1 <= rem <= c_d1
+        uint32_t low_T;
+        int need_eq;
+        __syncthreads();   // every thread has read c_d1 before s_h2 or the counter changes
+        if (c_d1 <= kFewMembers) {   // uniform
+            // few keys share bin d1 (the usual case): rank them against each other
+            // instead of a second histogram pass.  Each member counts the members
+            // above and equal to it; the one whose range holds rank rem gives T's
+            // low bits and how many keys equal to T are taken.
+            if (tid == 0) s_few_n = 0;
+            __syncthreads();
+            for (int p0 = 0; p0 < n_keep; p0 += NT) {
+                const int p = p0 + tid;
+                if (p < n_keep && s_idx[p] < 0 && ((s_key[p] >> 10) & 2047u) == d1)
+                    s_few[atomicAdd(&s_few_n, 1)] = s_key[p] & 1023u;
+            }
+            __syncthreads();
+            if (tid < c_d1) {
+                const uint32_t me = s_few[tid];
+                int gt = 0, eq = 0;
+                for (int i = 0; i < c_d1; ++i) {
+                    const uint32_t o = s_few[i];
+                    gt += o > me ? 1 : 0;
+                    eq += o == me ? 1 : 0;
+                }
+                if (gt < rem && rem <= gt + eq) {   // every such member writes the same pair
+                    s_few_t[0] = (int)me;
+                    s_few_t[1] = rem - gt;
+                }
+            }
+            __syncthreads();
+            low_T = (uint32_t)s_few_t[0];
+            need_eq = s_few_t[1];
+        } else {
+            for (int i = tid; i < 1024; i += NT) s_h2[i] = 0u;
+            __syncthreads();
+            for (int p0 = 0; p0 < n_keep; p0 += NT) {
+                const int p = p0 + tid;
+                const bool act = p < n_keep && s_idx[p] < 0 && ((s_key[p] >> 10) & 2047u) == d1;
+                hist_add(s_h2, act, p < n_keep ? s_key[p] & 1023u : 0u);
+            }
+            __syncthreads();
+            find_bin<1024, NT>(s_h2, rem, sh.scan, s_b, &bin, &bin_above);
+            low_T = (uint32_t)bin;
+            need_eq = rem - bin_above;
         }
-        __syncthreads();
-        find_bin<1024, NT>(s_h2, rem, sh.scan, s_b, &bin, &bin_above);
-        const uint32_t T = ((uint32_t)bstar << kSelShift) | (d1 << 10) | (uint32_t)bin;
-        const int need_eq = rem - bin_above;
+        const uint32_t T = ((uint32_t)bstar << kSelShift) | (d1 << 10) | low_T;
         // index-ordered placement with one scan: thread t takes entries [t*E2, t*E2 + E2);
         // an entry above T (every entry above b*, and candidates > T) goes to
         // (entries above T before it) + min(candidates equal to T before it, need_eq),
