@@ -82,7 +82,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="swap_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-steps", type=int, default=12)
+    ap.add_argument("--cpu-sample-steps", type=int, default=28)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--graph", type=int, default=0,
                     help="time eager launches (0, the default: faster here, the host keeps ahead of the GPU) "
