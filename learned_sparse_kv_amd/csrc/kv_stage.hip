@@ -79,8 +79,7 @@ __device__ inline void copy_rows(const char* cold, char* kv, int row_bytes, int 
 }
 
 // One (sequence b, layer) of the stage; a workgroup of kNT threads.
-__device__ __forceinline__ void kv_stage_body(const StageArgs& a, const int b, const int layer) {
-    const StageLayer& L = a.L[layer];
+__device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b) {
     const int tid = threadIdx.x;
 
     __shared__ int s_scan[kNT / 64 + 1];
@@ -251,7 +250,14 @@ __device__ __forceinline__ void kv_stage_body(const StageArgs& a, const int b, c
 }
 
 __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
-    kv_stage_body(a, blockIdx.x, blockIdx.y);
+    kv_stage_body(a.L[blockIdx.y], blockIdx.x);
+}
+
+// Any number of layers in one launch: their descriptors come from device
+// memory (copied to registers once, so the body's stores cannot alias them).
+__global__ __launch_bounds__(kNT) void kv_stage_table_kernel(const StageLayer* Ls) {
+    const StageLayer L = Ls[blockIdx.y];
+    kv_stage_body(L, blockIdx.x);
 }
 
 __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L, int b, int64_t first, int64_t count) {
@@ -418,6 +424,12 @@ hipError_t launch_fetch_missed(const StageArgs& a, int phys_stride, hipStream_t 
 
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(kv_stage_kernel, dim3(a.batch, a.n_layers), dim3(kNT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_stage_table(const StageLayer* layers, int n_layers, int batch, hipStream_t s) {
+    if (n_layers < 1 || n_layers > 65535 || batch < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kv_stage_table_kernel, dim3(batch, n_layers), dim3(kNT), 0, s, layers);
     return hipGetLastError();
 }
 

@@ -185,7 +185,7 @@ template <int D>
 __global__ __launch_bounds__(1024, 1) void la_stage_combine(const StageArgs ga, const AttendArgs aa, const Split sp) {
     const int b = blockIdx.x;
     if (b < sp.n0) {
-        stage_k::kv_stage_body(ga, b % ga.batch, b / ga.batch);
+        stage_k::kv_stage_body(ga.L[b / ga.batch], b % ga.batch);
         return;
     }
     const int h = b - sp.n0;

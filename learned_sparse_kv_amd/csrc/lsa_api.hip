@@ -73,9 +73,48 @@ struct lsa_ctx {
     // lookahead schedule: which of the two row-list buffers holds the rows of
     // the coming step
     int la_cur = 0;
+    // KVSwap stage: every pool's stage descriptor goes to the device in one copy
+    // (from one of two pinned host buffers, each reused only after its previous
+    // copy has completed) and the stage of all pools runs as one launch
+    StageLayer* kv_layers_dev = nullptr;
+    StageLayer* kv_layers_host[2] = {nullptr, nullptr};
+    hipEvent_t kv_layers_done[2] = {nullptr, nullptr};
+    int kv_layers_cap = 0;
+    int kv_layers_next = 0;
 };
 
 namespace {
+
+// The pinned host buffer the next KVSwap stage table is written into (n
+// descriptors), grown on first use.  The device table is written by a stream-
+// ordered copy, so every step's stage reads its own descriptors; a host buffer is
+// reused only once the copy from it two steps before has completed.
+lsa_status kv_layer_buffer(lsa_ctx* c, int n, StageLayer** out) {
+    if (n > c->kv_layers_cap) {
+        HIPTRY(hipDeviceSynchronize());
+        if (c->kv_layers_dev) (void)hipFree(c->kv_layers_dev);
+        c->kv_layers_dev = nullptr;
+        for (int i = 0; i < 2; ++i) {
+            if (c->kv_layers_host[i]) (void)hipHostFree(c->kv_layers_host[i]);
+            c->kv_layers_host[i] = nullptr;
+        }
+        c->kv_layers_cap = 0;
+        const size_t bytes = (size_t)n * sizeof(StageLayer);
+        if (hipMalloc(reinterpret_cast<void**>(&c->kv_layers_dev), bytes) != hipSuccess)
+            return fail(LSA_ERR_NO_MEMORY, "KVSwap stage table: hipMalloc of %zu bytes failed", bytes);
+        for (int i = 0; i < 2; ++i) {
+            if (hipHostMalloc(reinterpret_cast<void**>(&c->kv_layers_host[i]), bytes, hipHostMallocDefault) != hipSuccess)
+                return fail(LSA_ERR_NO_MEMORY, "KVSwap stage table: hipHostMalloc of %zu bytes failed", bytes);
+            if (!c->kv_layers_done[i]) HIPTRY(hipEventCreateWithFlags(&c->kv_layers_done[i], hipEventDisableTiming));
+            HIPTRY(hipEventRecord(c->kv_layers_done[i], nullptr));
+        }
+        c->kv_layers_cap = n;
+    }
+    const int slot = c->kv_layers_next;
+    HIPTRY(hipEventSynchronize(c->kv_layers_done[slot]));
+    *out = c->kv_layers_host[slot];
+    return LSA_OK;
+}
 
 lsa_status ws_ensure(lsa_ctx* c, size_t bytes) {
     if (bytes <= c->ws_bytes) return LSA_OK;
@@ -263,6 +302,11 @@ void lsa_ctx_destroy(lsa_ctx* c) {
         (void)hipEventDestroy(p.b);
     }
     for (auto e : c->spare) (void)hipEventDestroy(e);
+    if (c->kv_layers_dev) (void)hipFree(c->kv_layers_dev);
+    for (int i = 0; i < 2; ++i) {
+        if (c->kv_layers_host[i]) (void)hipHostFree(c->kv_layers_host[i]);
+        if (c->kv_layers_done[i]) (void)hipEventDestroy(c->kv_layers_done[i]);
+    }
     delete c;
 }
 
@@ -1240,23 +1284,23 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
         t.end();
     }
     {
-        Timed t(ctx, LSA_K_STAGE, s);
-        for (int i0 = 0; i0 < d->n_pools; i0 += LSA_MAX_LAYERS) {
-            StageArgs ga;
-            memset(&ga, 0, sizeof(ga));
-            ga.batch = B;
-            ga.n_layers = d->n_pools - i0 < LSA_MAX_LAYERS ? d->n_pools - i0 : LSA_MAX_LAYERS;
-            for (int j = 0; j < ga.n_layers; ++j) {
-                const int i = i0 + j;
-                const size_t seg0 = (size_t)i * B;
-                ga.L[j] = stage_layer(d->pools[i], d->sel + seg0 * d->k, d->count + seg0, d->k, 1,
-                                      d->phys + seg0 * d->k, d->k, d->n_rows + seg0);
-                ga.L[j].defer_copy = 1;
-                ga.L[j].src = srcs + seg0 * d->k;
-                ga.L[j].seg_cold = seg_cold + seg0;
-            }
-            HIPTRY(launch_kv_stage(ga, s));
+        StageLayer* host = nullptr;
+        st = kv_layer_buffer(ctx, d->n_pools, &host);
+        if (st != LSA_OK) return st;
+        for (int i = 0; i < d->n_pools; ++i) {
+            const size_t seg0 = (size_t)i * B;
+            host[i] = stage_layer(d->pools[i], d->sel + seg0 * d->k, d->count + seg0, d->k, 1, d->phys + seg0 * d->k,
+                                  d->k, d->n_rows + seg0);
+            host[i].defer_copy = 1;
+            host[i].src = srcs + seg0 * d->k;
+            host[i].seg_cold = seg_cold + seg0;
         }
+        const int slot = ctx->kv_layers_next;
+        HIPTRY(hipMemcpyAsync(ctx->kv_layers_dev, host, (size_t)d->n_pools * sizeof(StageLayer), hipMemcpyHostToDevice, s));
+        HIPTRY(hipEventRecord(ctx->kv_layers_done[slot], s));
+        ctx->kv_layers_next = slot ^ 1;
+        Timed t(ctx, LSA_K_STAGE, s);
+        HIPTRY(launch_kv_stage_table(ctx->kv_layers_dev, d->n_pools, B, s));
         t.end();
     }
     {
