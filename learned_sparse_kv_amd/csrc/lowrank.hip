@@ -76,8 +76,13 @@ __global__ __launch_bounds__(kThreads) void lowrank_scan_kernel(const LowrankArg
                 d += p[2 * e] * f16_to_f32((uint16_t)(w[e] & 0xFFFF));
                 d += p[2 * e + 1] * f16_to_f32((uint16_t)(w[e] >> 16));
             }
-#pragma unroll
-            for (int o = 1; o < kLpr; o <<= 1) d += __shfl_xor(d, o, 64);
+            // sum over the row's kLpr lanes: DPP quad permutes for lane distances 1
+            // and 2 (no LDS permute), a shuffle for 4
+            if constexpr (kLpr >= 2)
+                d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+            if constexpr (kLpr >= 4)
+                d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+            if constexpr (kLpr >= 8) d += __shfl_xor(d, 4, 64);
             const int64_t row = base + u * kRpb + wave * kRpw + lane / kLpr;
             // one lane per row stores; rows past the end and the other lanes are dropped
             const uint32_t off = (sub == 0 && row < last) ? (uint32_t)row * 4u : 0xFFFFFFF0u;
