@@ -444,7 +444,12 @@ lsa_status lsa_attend_kv(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype
  * used as entries directly), then lsa_attend_kv over the staged rows.
  * Every pool must have window 0, ratio 1, compressed_cap == T, the same batch,
  * dtype and kv_dim == 2 * heads * head_dim, and their kv_buf must be laid out
- * back to back: pool p's kv_buf == pool 0's + p * batch * kv_stride_b elements. */
+ * back to back: pool p's kv_buf == pool 0's + p * batch * kv_stride_b elements.
+ * The stage of all pools is one launch: each call copies the pools' stage
+ * descriptors to the device (a stream-ordered copy from one of two pinned host
+ * buffers of the context) and first waits on the host until the copy from that
+ * buffer two calls back has completed; the first call allocates them.  The call
+ * is therefore not meant for stream capture. */
 typedef struct lsa_kvswap_desc {
     const void* U; const float* S; const void* V; lsa_dtype factor_dtype;
     int64_t T; int32_t rank;
