@@ -7,9 +7,10 @@
 //
 // One lookahead step t runs on a single stream as five launches:
 //   A  fm_score of step t+1, each workgroup with one extra wave that copies a
-//      share of step t's missed rows into their slots (one segment: the score
-//      waves also build the select's histogram)
-//   B  select histogram of step t+1 (several segments only)
+//      share of step t's missed rows into their slots (the score waves also
+//      build the select's histogram)
+//   B  select histogram of step t+1 (only when A cannot: segments that are
+//      not one per sequence, or fewer score workgroups than sequences)
 //   C  select collect of step t+1
 //   D  [attention splits of step t                    | final select of step t+1]
 //   E  [stage of step t+1 (LRU; records its misses)   | split merge of step t]
@@ -155,9 +156,13 @@ __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, cons
         prev = __shfl(prev, 0, 64);
         if (prev == score_k::kWaves - 1) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            // several sequences: the grid is a multiple of the batch, so all waves of
+            // a workgroup score the same sequence (fm_score's per-sequence groups)
+            const int seg = sa.batch > 1 ? blockIdx.x / (gridDim.x / sa.batch) : 0;
+            uint32_t* gh = ha.hist + (size_t)seg * kSelBins;
             for (int i = lane; i < kSelBins; i += 64) {
                 const uint32_t c = s_hist[i];
-                if (c) atomicAdd(&ha.hist[i], c);
+                if (c) atomicAdd(&gh[i], c);
             }
         }
     }
@@ -198,6 +203,9 @@ hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, const HistArgs& ha,
     int grid = (total + score_k::kWaves - 1) / score_k::kWaves;
     if (grid > n_cu) grid = n_cu;
     if (grid < 1) grid = 1;
+    // with the histogram and several sequences, whole workgroups per sequence
+    if (ha.hist && sa.batch > 1) grid -= grid % sa.batch;
+    if (grid < 1) return hipErrorInvalidValue;
     if (ha.hist)
         hipLaunchKernelGGL((la_score_copy<DK, KT, true>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
     else
@@ -294,7 +302,11 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int p
 }
 
 bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se) {
-    return se.path == 1 && se.n_seg == 1 && sa.batch == 1 && se.hist != nullptr;
+    // one select segment per sequence, and at least one workgroup of score waves
+    // per sequence (the grid is rounded down to a multiple of the batch)
+    const int tiles = sa.tile_start[sa.batch];
+    return se.path == 1 && se.n_seg == sa.batch && se.hist != nullptr &&
+           (tiles + score_k::kWaves - 1) / score_k::kWaves >= sa.batch;
 }
 
 hipError_t launch_la_select_split(const AttendArgs& aa, const SelectArgs& se, bool hist_done, hipStream_t s) {
