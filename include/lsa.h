@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LSA_ABI_VERSION 5
+#define LSA_ABI_VERSION 6
 #define LSA_MAX_LAYERS 16
 #define LSA_MAX_BATCH 64
 
@@ -152,7 +152,9 @@ lsa_status lsa_project(const float* hidden, int32_t batch, int32_t d_model, cons
  * product.  For every sequence b and valid entry j < n_valid[b]:
  *     s_i[j]   = sum_h w[b,i,h] * ReLU( q[b,i,h,:] . keys[b,j,:] )   (fp32)
  *     score[j] = max_i s_i[j]                (LSA_ENSEMBLE_MAX), or
- *                (sum_i s_i[j]) / n_idx      (LSA_ENSEMBLE_MEAN, one IEEE division)
+ *                fl(sum_i s_i[j]) / n_idx    (LSA_ENSEMBLE_MEAN: the float s_i added
+ *                                             in double in indexer order, rounded
+ *                                             once to float, one IEEE division)
  * with -0 written as +0.  Accumulation is fp32 in an unspecified order, so the
  * result is exact whenever every partial sum is representable in fp32.  Keys
  * of every dtype enter as their exact values (an fp8 code decodes exactly, an
@@ -292,8 +294,13 @@ typedef struct lsa_adapt_policy {
 lsa_status lsa_pool_adapt(lsa_pool* pool, const lsa_adapt_policy* policy, int32_t steps, int32_t* capacity,
                           lsa_stream_t stream);
 /* Synchronises `stream`, then reports counters.  Returns LSA_ERR_NOT_STORED
- * ([P1] error 4) if a step since the last call selected an entry that was never
- * stored (such an entry is staged from whatever its cold row holds). */
+ * ([P1] error 4) if a stage since the last call found an entry that was never
+ * stored in a sequence's list (that stage left the sequence's slot table, LRU
+ * order and counters unchanged and wrote an empty row list, so its attention
+ * output is zero), and LSA_ERR_INVALID_ARG if a list held an entry outside
+ * [0, compressed_cap).  The flags are cleared once reported.  The stage runs on
+ * the device and the step calls return before it does, so this is where the
+ * error surfaces. */
 lsa_status lsa_pool_stats(lsa_pool* pool, lsa_pool_stats_t* out, lsa_stream_t stream);
 /* Test hook ([P1] KV_SWAP_VALIDATE): copies the slot table of sequence b to
  * host: slot_logical [gpu_chunks] (-1 = unused) and lru [gpu_chunks] (slot ids
@@ -305,22 +312,28 @@ lsa_status lsa_pool_state(lsa_pool* pool, int32_t b, int32_t* slot_logical, int3
 /* ------------------------------------------------------------------ stage --
  * [P1] swap-in flow: for the chunks selected on the ratio-src_ratio source
  * layer, map them to this pool's ratio (entry j -> floor(j * src_ratio /
- * ratio), duplicates removed, ascending), then per entry: a hit moves it to
- * the LRU front; a miss takes the lowest unused slot, else evicts the least
- * recently used one, and its row is copied cold -> slot.  Hits are handled
+ * ratio), duplicates removed, ascending), keep the complete ones (entry m with
+ * m < floor(n_valid[b] * src_ratio / ratio): the tokens of a chunk that is not
+ * complete yet all lie in the sliding window), then per entry: a hit moves it
+ * to the LRU front; a miss takes the lowest unused slot, else evicts the least
+ * recently used one, and its row is copied cold -> slot.  [P1] error 4: if the
+ * list of sequence b holds an entry that was never stored, nothing of b
+ * changes, n_rows[b] = 0 and the pool's error flag is set (lsa_pool_stats).  Hits are handled
  * before misses, each in ascending order, so no selected chunk is evicted in
  * the step that selects it.  Writes the physical row list the attention reads:
  * phys[b][0..window-1] = 0..window-1, then window + slot of each entry in
  * ascending entry order; n_rows[b] = window + entries.
  *   sel   device i32 [batch][sel_stride] ascending source-layer indices
  *   count device i32 [batch]
+ *   n_valid host [batch] valid source-layer entries per sequence, or NULL
+ *         (every chunk complete)
  *   phys  device i32 [batch][phys_stride], phys_stride >= window + sel_stride
  *   n_rows device i32 [batch]
  * sel_stride must not exceed the pool's gpu_chunks when it swaps (it is the
  * most entries a step can stage), nor 1024. */
 lsa_status lsa_stage(lsa_pool* pool, const int32_t* sel, const int32_t* count, int32_t sel_stride,
-                     int32_t src_ratio, int32_t* phys, int32_t phys_stride, int32_t* n_rows,
-                     lsa_stream_t stream);
+                     int32_t src_ratio, const int64_t* n_valid, int32_t* phys, int32_t phys_stride,
+                     int32_t* n_rows, lsa_stream_t stream);
 
 /* ----------------------------------------------------------------- attend --
  * [P1] overview "Two-tier KV cache" and indexed_cached_attention (window +
@@ -370,6 +383,19 @@ typedef struct lsa_step_desc {
 } lsa_step_desc;
 lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
 
+/* [P2] LSA section: the memory indexer is triggered periodically, and each
+ * prediction covers the chunks of the coming short decoding window.  A step of
+ * that window on which the indexer does not fire attends over the rows the
+ * last lsa_decode_step staged: no scoring, selection or staging (the indexer
+ * query and weights of `step` are not read), and the pools' counters and LRU
+ * order stay as they are.  `step` must have the shapes of that lsa_decode_step
+ * (its q_attn and out are this step's); when it passed no phys / n_rows, the
+ * rows live in the context workspace, and a call in between on the same
+ * context that needs a larger workspace loses them (pass phys / n_rows then).
+ * A (layer, sequence) whose last stage failed with [P1] error 4 has an empty
+ * row list and gets a zero output. */
+lsa_status lsa_decode_attend(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
+
 /* ------------------------------------------------------ lookahead schedule --
  * [P2] LSA section: the memory indexer predicts, ahead of time, which chunks
  * the coming decoding window will use, and only those are recalled to the GPU;
@@ -397,6 +423,15 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t
 lsa_status lsa_lookahead_prime(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
 lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
 int32_t    lsa_lookahead_buffer(const lsa_ctx* ctx);
+/* The periodic indexer in the lookahead schedule ([P2] LSA section): with a
+ * period of D steps, steps D*j .. D*j + D-1 attend over the rows of prediction
+ * j.  The last step of a window calls lsa_lookahead_step, which attends and
+ * predicts the next window (its q_idx / w_idx are the indexer query of that
+ * window); the other steps call lsa_lookahead_attend, which only attends (and,
+ * on the first step of a window, copies the window's missed rows into their
+ * slots).  The outputs equal lsa_decode_step on the first step of each window
+ * and lsa_decode_attend on the others. */
+lsa_status lsa_lookahead_attend(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
 
 /* ---------------------------------------------------------------- KVSwap --
  * KVSwap article, sections 2.2-2.3 and 3.2: keys of a head group are kept as

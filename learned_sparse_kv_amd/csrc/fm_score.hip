@@ -426,11 +426,15 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
                     if (a.n_idx > 2) e = fmaxf(e, sv[2]);
                     if (a.n_idx > 3) e = fmaxf(e, sv[3]);
                 } else {
-                    float sum = sv[0];
-                    if (a.n_idx > 1) sum += sv[1];
-                    if (a.n_idx > 2) sum += sv[2];
-                    if (a.n_idx > 3) sum += sv[3];
-                    e = sum / (float)a.n_idx;
+                    // mean ensemble: the float indexer scores are added in
+                    // double, in indexer order (exact unless their exponents
+                    // lie more than 27 apart), rounded once to float, and
+                    // divided once by n_idx in IEEE single precision
+                    double sum = (double)sv[0];
+                    if (a.n_idx > 1) sum += (double)sv[1];
+                    if (a.n_idx > 2) sum += (double)sv[2];
+                    if (a.n_idx > 3) sum += (double)sv[3];
+                    e = (float)sum / (float)a.n_idx;
                 }
                 const int key = (t - lo) * kTile + j * kSub + col;
                 const uint32_t off = half ? 0x80000000u : (uint32_t)key * 4u;

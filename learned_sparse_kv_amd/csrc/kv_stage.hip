@@ -9,9 +9,14 @@
 // layer whose compressed_cap <= gpu_chunks does not swap (rows = window + j).
 //
 // Readings shared with the CPU oracle: a source chunk j maps to chunk
-// floor(j * src_ratio / ratio) of this layer (duplicates dropped); hits are
-// handled before misses, each in ascending chunk order; a miss takes the
-// lowest never-used slot before it evicts.
+// floor(j * src_ratio / ratio) of this layer (duplicates dropped), and a layer
+// chunk is only used once it is complete, i.e. once the valid source entries
+// cover all of its tokens (the tokens of an incomplete chunk are all inside
+// the sliding window); hits are handled before misses, each in ascending chunk
+// order; a miss takes the lowest never-used slot before it evicts.  A step
+// whose list holds a chunk that was never stored ([P1] error 4) changes
+// nothing: the pool's tables and counters stay as they were, the row list is
+// empty (so the attention writes zeros) and the pool's error flag is set.
 //
 // Design (gfx950): one 1024-thread workgroup per (layer, sequence) replaces
 // the host-side std::list walk with prefix sums.  The LRU list is kept as an
@@ -79,13 +84,14 @@ __device__ inline void copy_rows(const char* cold, char* kv, int row_bytes, int 
 }
 
 // One (sequence b, layer) of the stage; a workgroup of kNT threads.
-__device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b) {
+// src_valid: valid entries of sequence b in the source layer; this layer's
+// complete chunks are the first floor(src_valid * src_ratio / ratio).
+__device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, const int src_valid) {
     const int tid = threadIdx.x;
 
     __shared__ int s_scan[kNT / 64 + 1];
     __shared__ int s_sel[kNT];
     __shared__ int s_slot[kNT];     // slot of s_sel[i] before this step (-1: none)
-    __shared__ uint8_t s_rdy[kNT];  // ready flag of s_sel[i]
     __shared__ int s_victim[kNT];
     __shared__ int s_order[kMaxSlots];
     __shared__ int s_logical[kMaxSlots];   // logical_of before this step
@@ -118,11 +124,12 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b) 
 
     // 1. source selection -> this layer's ascending unique chunk list
     const int n_src = n_src_raw < 0 ? 0 : (n_src_raw > L.sel_stride ? L.sel_stride : n_src_raw);
+    const int64_t complete = (int64_t)(src_valid < 0 ? 0 : src_valid) * L.src_ratio / L.ratio;
     bool keep = false;
     int m = -1;
     if (tid < n_src) {
         m = (int)((int64_t)sv * L.src_ratio / L.ratio);
-        keep = tid == 0 || m != (int)((int64_t)sp * L.src_ratio / L.ratio);
+        keep = (tid == 0 || m != (int)((int64_t)sp * L.src_ratio / L.ratio)) && m < complete;
     }
     int my_slot = -1;
     uint8_t my_rdy = 1;
@@ -130,16 +137,27 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b) 
         my_rdy = L.ready[(int64_t)b * L.cap + m];
         if (sw) my_slot = slot_of[m];
     }
-    int n_l;
-    const int pos = block_excl_scan<kNT>(keep ? 1 : 0, s_scan, &n_l);
     // wait for the two table loads here, on every lane: consumed only under
     // `keep`, they would otherwise leave the compiler waiting for all memory
     // operations (the stores below included) before each later store
     asm volatile("" ::"v"(my_slot), "v"((int)my_rdy));
+    // one scan counts the kept chunks and the never-stored ones among them
+    const bool unstored = keep && my_rdy == 0;
+    int tot0;
+    const int packed0 = block_excl_scan<kNT>((keep ? 1 : 0) | (unstored ? 1 << 16 : 0), s_scan, &tot0);
+    const int pos = packed0 & 0xFFFF;
+    const int n_l = tot0 & 0xFFFF;
+    if ((tot0 >> 16) != 0) {   // uniform: [P1] error 4, the step changes nothing
+        if (tid == 0) {
+            atomicOr(&L.meta[b * 4 + 1], 1);
+            L.n_rows[b] = 0;
+            if (L.n_miss) L.n_miss[b] = 0;
+        }
+        return;
+    }
     if (keep) {
         s_sel[pos] = m;
         s_slot[pos] = my_slot;
-        s_rdy[pos] = my_rdy;
     }
     __syncthreads();
 
@@ -154,7 +172,6 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b) 
         phys[L.window + tid] = 0;
         l = -1;
     }
-    if (l >= 0 && !s_rdy[tid]) atomicOr(&L.meta[b * 4 + 1], 1);
 
     if (L.seg_cold && tid == 0)
         L.seg_cold[b] = (uint64_t)(static_cast<const char*>(L.cold) + b * L.cold_stride_b);
@@ -250,14 +267,14 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b) 
 }
 
 __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
-    kv_stage_body(a.L[blockIdx.y], blockIdx.x);
+    kv_stage_body(a.L[blockIdx.y], blockIdx.x, a.src_valid[blockIdx.x]);
 }
 
 // Any number of layers in one launch: their descriptors come from device
 // memory (copied to registers once, so the body's stores cannot alias them).
 __global__ __launch_bounds__(kNT) void kv_stage_table_kernel(const StageLayer* Ls) {
     const StageLayer L = Ls[blockIdx.y];
-    kv_stage_body(L, blockIdx.x);
+    kv_stage_body(L, blockIdx.x, 0x7FFFFFFF);
 }
 
 __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L, int b, int64_t first, int64_t count) {

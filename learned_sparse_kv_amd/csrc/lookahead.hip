@@ -190,7 +190,7 @@ template <int D>
 __global__ __launch_bounds__(1024, 1) void la_stage_combine(const StageArgs ga, const AttendArgs aa, const Split sp) {
     const int b = blockIdx.x;
     if (b < sp.n0) {
-        stage_k::kv_stage_body(ga.L[b / ga.batch], b % ga.batch);
+        stage_k::kv_stage_body(ga.L[b / ga.batch], b % ga.batch, ga.src_valid[b % ga.batch]);
         return;
     }
     const int h = b - sp.n0;
@@ -259,7 +259,7 @@ hipError_t launch_e(const StageArgs& ga, const AttendArgs& aa, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
-                                 int n_cu, const SelectArgs* hist_for, hipStream_t s) {
+                                 int n_cu, const SelectArgs* hist_for, bool copy, hipStream_t s) {
     // the copy reads the stage's miss lists through one base pointer: they must
     // lie back to back over (layer, sequence), with one row size
     const StageLayer& L0 = ga.L[0];
@@ -272,10 +272,11 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int p
     }
     const int cpr = L0.row_bytes / 16;
     if (L0.row_bytes % 16 != 0 || cpr < 1 || (cpr & (cpr - 1)) != 0) return hipErrorInvalidValue;
-    const CopyArgs ca{L0.miss, L0.n_miss, ga.n_layers * ga.batch, phys_stride, L0.row_bytes};
+    // no segments: the copy waves find nothing to copy
+    const CopyArgs ca{L0.miss, L0.n_miss, copy ? ga.n_layers * ga.batch : 0, phys_stride, L0.row_bytes};
     HistArgs ha{nullptr, 0, 0.0f};
     if (hist_for) {
-        if (!la_fused_hist(sa, *hist_for)) return hipErrorInvalidValue;
+        if (!la_fused_hist(sa, *hist_for, n_cu)) return hipErrorInvalidValue;
         ha = HistArgs{hist_for->hist, hist_for->mode, hist_for->t_f};
     }
     if (key_dtype == LSA_F32) {
@@ -301,12 +302,14 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int p
     return hipErrorInvalidValue;
 }
 
-bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se) {
+bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se, int n_cu) {
     // one select segment per sequence, and at least one workgroup of score waves
-    // per sequence (the grid is rounded down to a multiple of the batch)
+    // per sequence: the grid (capped at one workgroup per CU, then rounded down
+    // to a multiple of the batch, as launch_a does) must keep one per sequence
     const int tiles = sa.tile_start[sa.batch];
-    return se.path == 1 && se.n_seg == sa.batch && se.hist != nullptr &&
-           (tiles + score_k::kWaves - 1) / score_k::kWaves >= sa.batch;
+    int grid = (tiles + score_k::kWaves - 1) / score_k::kWaves;
+    if (grid > n_cu) grid = n_cu;
+    return se.path == 1 && se.n_seg == sa.batch && se.hist != nullptr && grid >= sa.batch;
 }
 
 hipError_t launch_la_select_split(const AttendArgs& aa, const SelectArgs& se, bool hist_done, hipStream_t s) {

@@ -73,10 +73,14 @@ struct lsa_ctx {
     // lookahead schedule: which of the two row-list buffers holds the rows of
     // the coming step
     int la_cur = 0;
+    // whether the missed rows of buffer la_cur have been copied into their
+    // slots (by an attention of the window the last prediction serves)
+    bool la_fetched = false;
     // KVSwap stage: every pool's stage descriptor goes to the device in one copy
-    // (from one of two pinned host buffers, each reused only after its previous
-    // copy has completed) and the stage of all pools runs as one launch
-    StageLayer* kv_layers_dev = nullptr;
+    // and the stage of all pools runs as one launch.  Two (pinned host, device)
+    // table pairs alternate; a pair is reused only once the stage launch that
+    // read it two calls back has completed
+    StageLayer* kv_layers_dev[2] = {nullptr, nullptr};
     StageLayer* kv_layers_host[2] = {nullptr, nullptr};
     hipEvent_t kv_layers_done[2] = {nullptr, nullptr};
     int kv_layers_cap = 0;
@@ -85,24 +89,25 @@ struct lsa_ctx {
 
 namespace {
 
-// The pinned host buffer the next KVSwap stage table is written into (n
-// descriptors), grown on first use.  The device table is written by a stream-
-// ordered copy, so every step's stage reads its own descriptors; a host buffer is
-// reused only once the copy from it two steps before has completed.
-lsa_status kv_layer_buffer(lsa_ctx* c, int n, StageLayer** out) {
+// The table pair the next KVSwap stage uses (n descriptors), grown on first
+// use.  The device table is written by a stream-ordered copy from the pinned
+// host table, so every step's stage reads its own descriptors; the host waits
+// until the stage that read the pair two calls back has completed, so neither
+// table is overwritten while a launch may still read it (also across streams).
+lsa_status kv_layer_buffer(lsa_ctx* c, int n, StageLayer** host, StageLayer** dev) {
     if (n > c->kv_layers_cap) {
         HIPTRY(hipDeviceSynchronize());
-        if (c->kv_layers_dev) (void)hipFree(c->kv_layers_dev);
-        c->kv_layers_dev = nullptr;
         for (int i = 0; i < 2; ++i) {
+            if (c->kv_layers_dev[i]) (void)hipFree(c->kv_layers_dev[i]);
             if (c->kv_layers_host[i]) (void)hipHostFree(c->kv_layers_host[i]);
+            c->kv_layers_dev[i] = nullptr;
             c->kv_layers_host[i] = nullptr;
         }
         c->kv_layers_cap = 0;
         const size_t bytes = (size_t)n * sizeof(StageLayer);
-        if (hipMalloc(reinterpret_cast<void**>(&c->kv_layers_dev), bytes) != hipSuccess)
-            return fail(LSA_ERR_NO_MEMORY, "KVSwap stage table: hipMalloc of %zu bytes failed", bytes);
         for (int i = 0; i < 2; ++i) {
+            if (hipMalloc(reinterpret_cast<void**>(&c->kv_layers_dev[i]), bytes) != hipSuccess)
+                return fail(LSA_ERR_NO_MEMORY, "KVSwap stage table: hipMalloc of %zu bytes failed", bytes);
             if (hipHostMalloc(reinterpret_cast<void**>(&c->kv_layers_host[i]), bytes, hipHostMallocDefault) != hipSuccess)
                 return fail(LSA_ERR_NO_MEMORY, "KVSwap stage table: hipHostMalloc of %zu bytes failed", bytes);
             if (!c->kv_layers_done[i]) HIPTRY(hipEventCreateWithFlags(&c->kv_layers_done[i], hipEventDisableTiming));
@@ -112,7 +117,8 @@ lsa_status kv_layer_buffer(lsa_ctx* c, int n, StageLayer** out) {
     }
     const int slot = c->kv_layers_next;
     HIPTRY(hipEventSynchronize(c->kv_layers_done[slot]));
-    *out = c->kv_layers_host[slot];
+    *host = c->kv_layers_host[slot];
+    *dev = c->kv_layers_dev[slot];
     return LSA_OK;
 }
 
@@ -302,8 +308,8 @@ void lsa_ctx_destroy(lsa_ctx* c) {
         (void)hipEventDestroy(p.b);
     }
     for (auto e : c->spare) (void)hipEventDestroy(e);
-    if (c->kv_layers_dev) (void)hipFree(c->kv_layers_dev);
     for (int i = 0; i < 2; ++i) {
+        if (c->kv_layers_dev[i]) (void)hipFree(c->kv_layers_dev[i]);
         if (c->kv_layers_host[i]) (void)hipHostFree(c->kv_layers_host[i]);
         if (c->kv_layers_done[i]) (void)hipEventDestroy(c->kv_layers_done[i]);
     }
@@ -398,7 +404,7 @@ lsa_status score_args(const void* keys, lsa_dtype key_dtype, const uint8_t* key_
 
 lsa_status select_setup(lsa_ctx* c, const float* scores, int32_t n_seg, int64_t n_keys, const int64_t* n_valid,
                         lsa_select_mode mode, int32_t k, int32_t stride, double tau, int32_t* sel, int32_t* count,
-                        SelectArgs* a, size_t* ws_need) {
+                        SelectArgs* a, size_t* zero_need, size_t* ws_need) {
     if (!scores || !sel || !count) return fail(LSA_ERR_INVALID_ARG, "lsa_select: NULL pointer");
     if (n_seg < 1) return fail(LSA_ERR_INVALID_ARG, "n_seg %d", n_seg);
     if (n_keys < 0 || n_keys > INT32_MAX) return fail(LSA_ERR_INVALID_ARG, "n_keys out of range");
@@ -433,12 +439,8 @@ lsa_status select_setup(lsa_ctx* c, const float* scores, int32_t n_seg, int64_t 
             for (int s = 0; s < n_seg; ++s) a->n_valid[s] = (int32_t)n_valid[s];
         }
     }
-    size_t zero_bytes = 0;
-    if (!select_plan(a, &zero_bytes, ws_need)) return fail(LSA_ERR_UNSUPPORTED, "selection shape out of range");
-    if (zero_bytes) {
-        lsa_status st = zero_ensure(c, zero_bytes);
-        if (st != LSA_OK) return st;
-    }
+    (void)c;
+    if (!select_plan(a, zero_need, ws_need)) return fail(LSA_ERR_UNSUPPORTED, "selection shape out of range");
     return LSA_OK;
 }
 
@@ -471,6 +473,16 @@ StageLayer stage_layer(const lsa_pool* p, const int32_t* sel, const int32_t* cou
     L.phys_stride = phys_stride;
     L.row_bytes = p->row_bytes;
     return L;
+}
+
+// valid source entries per sequence (NULL: unbounded, every chunk complete)
+lsa_status fill_src_valid(StageArgs* a, const int64_t* n_valid) {
+    for (int b = 0; b < a->batch; ++b) {
+        const int64_t v = n_valid ? n_valid[b] : (int64_t)INT32_MAX;
+        if (v < 0) return fail(LSA_ERR_INVALID_ARG, "n_valid[%d] = %lld < 0", b, (long long)v);
+        a->src_valid[b] = (int32_t)(v > INT32_MAX ? INT32_MAX : v);
+    }
+    return LSA_OK;
 }
 
 lsa_status stage_check(const lsa_pool* p, int32_t sel_stride, int32_t src_ratio, int32_t phys_stride) {
@@ -551,8 +563,10 @@ lsa_status lsa_select(lsa_ctx* ctx, const float* scores, int32_t n_seg, int64_t 
                       lsa_stream_t stream) {
     if (!ctx) return fail(LSA_ERR_INVALID_ARG, "ctx is NULL");
     SelectArgs a;
-    size_t need = 0;
-    lsa_status st = select_setup(ctx, scores, n_seg, n_keys, n_valid, mode, k, k, tau, sel, count, &a, &need);
+    size_t need = 0, zneed = 0;
+    lsa_status st = select_setup(ctx, scores, n_seg, n_keys, n_valid, mode, k, k, tau, sel, count, &a, &zneed, &need);
+    if (st != LSA_OK) return st;
+    st = zero_ensure(ctx, zneed);
     if (st != LSA_OK) return st;
     st = ws_ensure(ctx, need);
     if (st != LSA_OK) return st;
@@ -840,7 +854,7 @@ lsa_status lsa_pool_state(lsa_pool* p, int32_t b, int32_t* slot_logical, int32_t
 
 // ------------------------------------------------------------------- stage
 lsa_status lsa_stage(lsa_pool* p, const int32_t* sel, const int32_t* count, int32_t sel_stride, int32_t src_ratio,
-                     int32_t* phys, int32_t phys_stride, int32_t* n_rows, lsa_stream_t stream) {
+                     const int64_t* n_valid, int32_t* phys, int32_t phys_stride, int32_t* n_rows, lsa_stream_t stream) {
     if (!p || !sel || !count || !phys || !n_rows) return fail(LSA_ERR_INVALID_ARG, "lsa_stage: NULL argument");
     lsa_status st = stage_check(p, sel_stride, src_ratio, phys_stride);
     if (st != LSA_OK) return st;
@@ -848,6 +862,8 @@ lsa_status lsa_stage(lsa_pool* p, const int32_t* sel, const int32_t* count, int3
     memset(&a, 0, sizeof(a));
     a.n_layers = 1;
     a.batch = p->d.batch;
+    st = fill_src_valid(&a, n_valid);
+    if (st != LSA_OK) return st;
     a.L[0] = stage_layer(p, sel, count, sel_stride, src_ratio, phys, phys_stride, n_rows);
     hipStream_t s = (hipStream_t)stream;
     HIPTRY(launch_kv_stage(a, s));
@@ -895,6 +911,10 @@ namespace {
 // Everything one decode step launches, validated and bound to the workspace.
 // n_buf row-list buffers are laid out (2 for the lookahead schedule).
 struct StepPlan {
+    // with a fixed scratch buffer (the allocation-free entry point) the select's
+    // zero region is cleared by a fill kernel at the start of every call
+    uint32_t* zero_clear = nullptr;
+    size_t zero_clear_words = 0;
     ScoreArgs sa;
     SelectArgs se;
     StageArgs ga;           // per layer; phys / n_rows / src point at buffer 0
@@ -907,7 +927,10 @@ struct StepPlan {
     int32_t* n_miss = nullptr;   // [n_buf][L][B]
 };
 
-lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* P) {
+// fixed / fixed_bytes: bind the workspace to this buffer instead of the
+// context's (nothing is allocated; too small a buffer is an error)
+lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* P, char* fixed = nullptr,
+                     size_t fixed_bytes = 0) {
     if (!ctx || !d) return fail(LSA_ERR_INVALID_ARG, "decode step: NULL argument");
     if (d->n_layers < 1 || d->n_layers > LSA_MAX_LAYERS)
         return fail(LSA_ERR_INVALID_ARG, "n_layers %d not in [1, %d]", d->n_layers, LSA_MAX_LAYERS);
@@ -937,9 +960,9 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
     lsa_status st = score_args(d->keys, d->key_dtype, d->key_scales, B, d->n_keys, d->n_valid, d->dk, d->q_idx,
                                d->w_idx, d->n_idx, d->heads, d->ensemble, d->scores, &P->sa);
     if (st != LSA_OK) return st;
-    size_t sel_need = 0;
+    size_t sel_need = 0, sel_zero = 0;
     st = select_setup(ctx, d->scores, B, d->n_keys, d->n_valid, d->mode, k_eff, d->k, d->tau, d->sel, d->count, &P->se,
-                      &sel_need);
+                      &sel_zero, &sel_need);
     if (st != LSA_OK) return st;
     const int phys_stride = W + d->k;
     if (phys_stride > kAttendMaxRows)
@@ -962,10 +985,27 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
     const size_t miss_bytes = align_up((size_t)n_buf * L * B * phys_stride * 16, 256);
     const size_t off_nmiss = off_miss + miss_bytes;
     const size_t nmiss_bytes = align_up((size_t)n_buf * L * B * 4, 256);
-    st = ws_ensure(ctx, off_nmiss + nmiss_bytes);
-    if (st != LSA_OK) return st;
-    char* ws = static_cast<char*>(ctx->ws);
-    select_bind(&P->se, ctx->zero, ws);
+    const size_t ws_total = off_nmiss + nmiss_bytes;
+    char* ws;
+    void* zero;
+    if (fixed) {
+        const size_t zero_al = align_up(sel_zero, 256);
+        if (zero_al + ws_total > fixed_bytes)
+            return fail(LSA_ERR_UNSUPPORTED, "the step needs %zu bytes of scratch; the static scratch holds %zu",
+                        zero_al + ws_total, fixed_bytes);
+        zero = fixed;
+        ws = fixed + zero_al;
+        P->zero_clear = reinterpret_cast<uint32_t*>(fixed);
+        P->zero_clear_words = sel_zero / 4;
+    } else {
+        st = zero_ensure(ctx, sel_zero);
+        if (st != LSA_OK) return st;
+        st = ws_ensure(ctx, ws_total);
+        if (st != LSA_OK) return st;
+        ws = static_cast<char*>(ctx->ws);
+        zero = ctx->zero;
+    }
+    select_bind(&P->se, zero, ws);
     P->phys = d->phys ? d->phys : reinterpret_cast<int32_t*>(ws + off_phys);
     P->n_rows = d->n_rows ? d->n_rows : reinterpret_cast<int32_t*>(ws + off_nrows);
     P->srcs = reinterpret_cast<int32_t*>(ws + off_src);
@@ -981,6 +1021,7 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
     memset(&P->ga, 0, sizeof(P->ga));
     P->ga.n_layers = L;
     P->ga.batch = B;
+    for (int b = 0; b < B; ++b) P->ga.src_valid[b] = P->sa.n_valid[b];
     memset(&P->aa, 0, sizeof(P->aa));
     P->aa.n_layers = L;
     P->aa.batch = B;
@@ -1067,13 +1108,38 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
     return attend_timed(ctx, P.aa, s);
 }
 
+lsa_status lsa_decode_attend(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
+    StepPlan P;
+    lsa_status st = step_plan(ctx, d, 1, &P);
+    if (st != LSA_OK) return st;
+    // the rows lsa_decode_step staged: its attention already filled the slots
+    return attend_timed(ctx, P.aa, (hipStream_t)stream);
+}
+
 int32_t lsa_lookahead_buffer(const lsa_ctx* ctx) { return ctx ? ctx->la_cur : 0; }
+
+lsa_status lsa_lookahead_attend(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
+    StepPlan P;
+    lsa_status st = step_plan(ctx, d, 2, &P);
+    if (st != LSA_OK) return st;
+    plan_use_buffer(&P, ctx->la_cur);
+    // the first attention over a prediction's rows reads its missed rows from
+    // the cold pools and fills their slots
+    if (!ctx->la_fetched)
+        for (int l = 0; l < P.L; ++l)
+            if (d->pools[l]->swap) P.aa.L[l].src = P.ga.L[l].src;
+    st = attend_timed(ctx, P.aa, (hipStream_t)stream);
+    if (st != LSA_OK) return st;
+    ctx->la_fetched = true;
+    return LSA_OK;
+}
 
 lsa_status lsa_lookahead_prime(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
     StepPlan P;
     lsa_status st = step_plan(ctx, d, 2, &P);
     if (st != LSA_OK) return st;
     ctx->la_cur = 0;
+    ctx->la_fetched = false;
     plan_use_buffer(&P, 0);
     // the first step's rows are staged; its lookahead step copies the missed ones
     return launch_predict(ctx, P, d, (hipStream_t)stream, false);
@@ -1089,11 +1155,11 @@ lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t
     hipStream_t s = (hipStream_t)stream;
     plan_use_buffer(&P, cur);
     const StageArgs fetch_cur = P.ga;   // the rows step t reads, and its recorded misses
-    const bool fuse_hist = la_fused_hist(P.sa, P.se);
+    const bool fuse_hist = la_fused_hist(P.sa, P.se, ctx->n_cu);
     {
         Timed t(ctx, LSA_K_SCORE, s);
         HIPTRY(launch_la_fetch_score(P.sa, fetch_cur, P.phys_stride, d->key_dtype, d->dk, ctx->n_cu,
-                                     fuse_hist ? &P.se : nullptr, s));
+                                     fuse_hist ? &P.se : nullptr, !ctx->la_fetched, s));
         t.end();
     }
     {
@@ -1109,6 +1175,7 @@ lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t
         t.end();
     }
     ctx->la_cur = nxt;
+    ctx->la_fetched = false;
     return LSA_OK;
 }
 
@@ -1244,9 +1311,11 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     if (d->T > INT32_MAX || (uint64_t)d->T * (uint64_t)row_elems * (uint64_t)eb >= ((uint64_t)1 << 32))
         return fail(LSA_ERR_UNSUPPORTED, "T %lld: a sequence's cold rows must stay below 4 GiB", (long long)d->T);
     SelectArgs se;
-    size_t sel_need = 0;
+    size_t sel_need = 0, sel_zero = 0;
     st = select_setup(ctx, d->scores, n_seg, d->T, nullptr, LSA_SELECT_TOPK, d->k, d->k, 0.5, d->sel, d->count, &se,
-                      &sel_need);
+                      &sel_zero, &sel_need);
+    if (st != LSA_OK) return st;
+    st = zero_ensure(ctx, sel_zero);
     if (st != LSA_OK) return st;
     for (int i = 0; i < d->n_pools; ++i) {
         st = stage_check(d->pools[i], d->k, 1, d->k);
@@ -1271,8 +1340,24 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     ka.src = srcs;
     ka.seg_cold = seg_cold;
     ka.cold_rows = d->T;
+    // the stage descriptors: the tables (and any allocation or wait they need)
+    // are settled before the first launch, so a failure enqueues nothing
+    StageLayer* host = nullptr;
+    StageLayer* dev = nullptr;
+    st = kv_layer_buffer(ctx, d->n_pools, &host, &dev);
+    if (st != LSA_OK) return st;
+    for (int i = 0; i < d->n_pools; ++i) {
+        const size_t seg0 = (size_t)i * B;
+        host[i] = stage_layer(d->pools[i], d->sel + seg0 * d->k, d->count + seg0, d->k, 1, d->phys + seg0 * d->k,
+                              d->k, d->n_rows + seg0);
+        host[i].defer_copy = 1;
+        host[i].src = srcs + seg0 * d->k;
+        host[i].seg_cold = seg_cold + seg0;
+    }
 
     hipStream_t s = (hipStream_t)stream;
+    const int slot = ctx->kv_layers_next;
+    HIPTRY(hipMemcpyAsync(dev, host, (size_t)d->n_pools * sizeof(StageLayer), hipMemcpyHostToDevice, s));
     {
         Timed t(ctx, LSA_K_SCORE, s);
         HIPTRY(launch_lowrank_score(la, s));
@@ -1284,24 +1369,12 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
         t.end();
     }
     {
-        StageLayer* host = nullptr;
-        st = kv_layer_buffer(ctx, d->n_pools, &host);
-        if (st != LSA_OK) return st;
-        for (int i = 0; i < d->n_pools; ++i) {
-            const size_t seg0 = (size_t)i * B;
-            host[i] = stage_layer(d->pools[i], d->sel + seg0 * d->k, d->count + seg0, d->k, 1, d->phys + seg0 * d->k,
-                                  d->k, d->n_rows + seg0);
-            host[i].defer_copy = 1;
-            host[i].src = srcs + seg0 * d->k;
-            host[i].seg_cold = seg_cold + seg0;
-        }
-        const int slot = ctx->kv_layers_next;
-        HIPTRY(hipMemcpyAsync(ctx->kv_layers_dev, host, (size_t)d->n_pools * sizeof(StageLayer), hipMemcpyHostToDevice, s));
+        Timed t(ctx, LSA_K_STAGE, s);
+        HIPTRY(launch_kv_stage_table(dev, d->n_pools, B, s));
+        t.end();
+        // the pair is free again once this stage has run
         HIPTRY(hipEventRecord(ctx->kv_layers_done[slot], s));
         ctx->kv_layers_next = slot ^ 1;
-        Timed t(ctx, LSA_K_STAGE, s);
-        HIPTRY(launch_kv_stage_table(ctx->kv_layers_dev, d->n_pools, B, s));
-        t.end();
     }
     {
         Timed t(ctx, LSA_K_ATTEND, s);

@@ -182,6 +182,9 @@ struct StageLayer {
 };
 struct StageArgs {
     int32_t n_layers, batch;
+    // valid source entries per sequence: a layer uses its chunks below
+    // floor(src_valid[b] * src_ratio / ratio), the complete ones
+    int32_t src_valid[LSA_MAX_BATCH];
     StageLayer L[LSA_MAX_LAYERS];
 };
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s);
@@ -231,9 +234,10 @@ hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid 
 // stage's output, laid out back to back over (layer, sequence)) into their slots.
 // With hist_for (a one-segment path-1 select, see la_fused_hist), the score
 // launch also builds that select's histogram.
+// copy = false: the rows were copied already (the launch only scores).
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
-                                 int n_cu, const SelectArgs* hist_for, hipStream_t s);
-bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se);
+                                 int n_cu, const SelectArgs* hist_for, bool copy, hipStream_t s);
+bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se, int n_cu);
 // select histogram (unless hist_done) and collect of step t+1, then its final
 // selection beside the attention splits of step t (short segments: the splits,
 // then the one-kernel select)

@@ -72,7 +72,7 @@ class KVSwapDesc(ctypes.Structure):
                 ("phys", P), ("n_rows", P), ("scale", f32), ("out", P)]
 
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _SIGS = {
     "lsa_compressed_cap": (i64, [i64, i32]),
@@ -103,12 +103,14 @@ _SIGS = {
     "lsa_pool_adapt": (i32, [P, P, i32, P, P]),
     "lsa_pool_stats": (i32, [P, ctypes.POINTER(PoolStats), P]),
     "lsa_pool_state": (i32, [P, i32, P, P, ctypes.POINTER(i32), P]),
-    "lsa_stage": (i32, [P, P, P, i32, i32, P, i32, P, P]),
+    "lsa_stage": (i32, [P, P, P, i32, i32, P, P, i32, P, P]),
     "lsa_attend": (i32, [P, P, P, i32, i64, i64, P, i32, P, i32, i32, i32, f32, P, P]),
     "lsa_decode_step": (i32, [P, ctypes.POINTER(StepDesc), P]),
     "lsa_lookahead_prime": (i32, [P, ctypes.POINTER(StepDesc), P]),
     "lsa_lookahead_step": (i32, [P, ctypes.POINTER(StepDesc), P]),
     "lsa_lookahead_buffer": (i32, [P]),
+    "lsa_decode_attend": (i32, [P, ctypes.POINTER(StepDesc), P]),
+    "lsa_lookahead_attend": (i32, [P, ctypes.POINTER(StepDesc), P]),
     "lsa_score_lowrank": (i32, [P, P, i32, i32, i64, i32, P, P, i32, P, P, P]),
     "lsa_attend_kv": (i32, [P, P, P, i32, i64, i64, i32, i32, P, i32, P, i32, f32, P, P]),
     "lsa_kvswap_step": (i32, [P, ctypes.POINTER(KVSwapDesc), P]),
@@ -410,11 +412,14 @@ class Pool:
         return sl, lr[:n.value].copy()
 
 
-def stage(pool: Pool, sel, count, src_ratio: int, phys, n_rows, stream=None) -> None:
-    """sel [B][k] i32, count [B] i32 -> phys [B][window + k] i32, n_rows [B] i32."""
+def stage(pool: Pool, sel, count, src_ratio: int, phys, n_rows, n_valid=None, stream=None) -> None:
+    """sel [B][k] i32, count [B] i32 -> phys [B][window + k] i32, n_rows [B] i32; n_valid:
+    valid source entries per sequence (None: every chunk complete)."""
     _dev(sel, "sel"), _dev(count, "count"), _dev(phys, "phys"), _dev(n_rows, "n_rows")
-    _check(lib().lsa_stage(pool.h, _ptr(sel), _ptr(count), sel.shape[1], src_ratio, _ptr(phys), phys.shape[1],
-                           _ptr(n_rows), _stream(stream)))
+    nv = _host_i64(n_valid)
+    _check(lib().lsa_stage(pool.h, _ptr(sel), _ptr(count), sel.shape[1], src_ratio,
+                           ctypes.cast(nv, P) if nv else None, _ptr(phys), phys.shape[1], _ptr(n_rows),
+                           _stream(stream)))
 
 
 def attend(ctx: Ctx, q, kv, phys, n_rows, out, scale: float, kv_rows: Optional[int] = None,
@@ -489,6 +494,15 @@ class PreparedStep:
         _check(self._fn(self._ctx, self._ref, self._stream))
 
 
+def lookahead_attend(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,
+                     k: int, src_ratio: int, scale: float, ensemble: str = "max", mode: str = "topk",
+                     tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None, key_scales=None) -> None:
+    """Attend this step over the current prediction's rows without predicting (lsa_lookahead_attend)."""
+    d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
+                         mode, tau, n_valid, phys, n_rows, key_scales)
+    _check(lib().lsa_lookahead_attend(ctx.h, ctypes.byref(d), _stream(stream)))
+
+
 def lookahead_buffer(ctx: Ctx) -> int:
     return int(lib().lsa_lookahead_buffer(ctx.h))
 
@@ -505,6 +519,16 @@ def decode_step(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, 
     d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
                          mode, tau, n_valid, phys, n_rows, key_scales)
     _check(lib().lsa_decode_step(ctx.h, ctypes.byref(d), _stream(stream)))
+
+
+def decode_attend(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,
+                  k: int, src_ratio: int, scale: float, ensemble: str = "max", mode: str = "topk",
+                  tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None, key_scales=None) -> None:
+    """Attend over the rows the last decode_step staged (lsa_decode_attend): a step of the
+    decoding window a periodic prediction serves."""
+    d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
+                         mode, tau, n_valid, phys, n_rows, key_scales)
+    _check(lib().lsa_decode_attend(ctx.h, ctypes.byref(d), _stream(stream)))
 
 
 # ---------------------------------------------------------------- KVSwap

@@ -41,8 +41,12 @@ def torch_dtype(dtype: str):
 
 
 class DeviceWorkload:
+    """stored: optional per-layer count of leading entries stored at set-up (the
+    rest are stored later with store(); default all).  n_valid: optional valid
+    source entries per sequence, passed to every step (default all)."""
+
     def __init__(self, wl: L.Workload, device: int = 0, keep_host: bool = False, ctx: Optional[lsa.Ctx] = None,
-                 log=None):
+                 log=None, stored: Optional[List[int]] = None):
         self.wl = wl
         self.dev = torch.device(f"cuda:{device}")
         self.ctx = ctx if ctx is not None else lsa.Ctx(device)
@@ -70,17 +74,18 @@ class DeviceWorkload:
                 win = L.encode(L.window_rows(wl, l, b), wl.kv_dtype)
                 kv[b, :W] = to_device(win, wl.kv_dtype, self.dev)
                 host = pool.host_rows(b, np_row)
+                n0 = pool.cap if stored is None else int(stored[l])
                 if host is not None and wl.kv_dtype == "f32":
                     L.cold_rows(wl, l, b, out=host)
-                    pool.mark_stored(b, 0, pool.cap)
+                    pool.mark_stored(b, 0, n0)
                     store = host
                 elif host is not None:
                     host[:] = L.encode(L.cold_rows(wl, l, b), wl.kv_dtype)
-                    pool.mark_stored(b, 0, pool.cap)
+                    pool.mark_stored(b, 0, n0)
                     store = host
                 else:
                     store = L.encode(L.cold_rows(wl, l, b), wl.kv_dtype)
-                    pool.store(b, 0, store)
+                    pool.store(b, 0, store[:n0])
                 wins.append(win)
                 stores.append(store if keep_host else None)
             self.pools.append(pool)
@@ -98,6 +103,14 @@ class DeviceWorkload:
         self.n_rows = torch.zeros((nL, B), dtype=torch.int32, device=self.dev)
         self.q_idx = self.w_idx = self.q_attn = None
         self.q_idx_np = self.w_idx_np = self.q_attn_np = None
+        self.n_valid = None
+
+    def store(self, l: int, b: int, first: int, rows: np.ndarray) -> None:
+        """Store rows (encoded in the row dtype) into entries first.. of layer l,
+        sequence b (lsa_pool_store), keeping the host copy in step."""
+        self.pools[l].store(b, first, np.ascontiguousarray(rows))
+        if self.keep_host and self.stores[l][b] is not None and self.pools[l].host_rows(b) is None:
+            self.stores[l][b][first:first + rows.shape[0]] = rows
 
     def make_steps(self, steps: int) -> None:
         """Draw the indexer and attention queries of `steps` steps and upload them."""
@@ -116,13 +129,20 @@ class DeviceWorkload:
         self.w_idx = torch.from_numpy(self.w_idx_np).to(self.dev)
         self.q_attn = torch.from_numpy(self.q_attn_np).to(self.dev)
 
-    def step(self, t: int, stream=None) -> None:
+    def _step_args(self, t: int):
         wl = self.wl
-        lsa.decode_step(self.ctx, keys=self.keys, q_idx=self.q_idx[t], w_idx=self.w_idx[t], pools=self.pools,
-                        q_attn=self.q_attn[t], out=self.out, scores=self.scores, sel=self.sel, count=self.count,
-                        k=wl.k, src_ratio=wl.src_ratio, scale=wl.scale, ensemble=wl.ensemble, mode=wl.mode,
-                        tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys, n_rows=self.n_rows,
-                        stream=stream, key_scales=self.key_scales)
+        return dict(keys=self.keys, q_idx=self.q_idx[t], w_idx=self.w_idx[t], pools=self.pools,
+                    q_attn=self.q_attn[t], out=self.out, scores=self.scores, sel=self.sel, count=self.count,
+                    k=wl.k, src_ratio=wl.src_ratio, scale=wl.scale, ensemble=wl.ensemble, mode=wl.mode,
+                    tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys, n_rows=self.n_rows,
+                    key_scales=self.key_scales, n_valid=self.n_valid)
+
+    def step(self, t: int, stream=None) -> None:
+        lsa.decode_step(self.ctx, stream=stream, **self._step_args(t))
+
+    def attend(self, t: int, stream=None) -> None:
+        """Step t of the window the last prediction serves (lsa_decode_attend)."""
+        lsa.decode_attend(self.ctx, stream=stream, **self._step_args(t))
 
     # ---- lookahead schedule: step t attends with the rows staged during step
     # t-1 (or by prime) and predicts step t+1 from q_idx[t+1]
@@ -139,14 +159,19 @@ class DeviceWorkload:
                     q_attn=self.q_attn[t_attn], out=self.out, scores=self.scores, sel=self.sel, count=self.count,
                     k=wl.k, src_ratio=wl.src_ratio, scale=wl.scale, ensemble=wl.ensemble, mode=wl.mode,
                     tau=wl.tau if wl.tau is not None else 0.5, phys=self.phys2, n_rows=self.n_rows2,
-                    key_scales=self.key_scales)
+                    key_scales=self.key_scales, n_valid=self.n_valid)
 
     def lookahead_prime(self, t: int = 0, stream=None) -> None:
         lsa.lookahead_prime(self.ctx, stream=stream, **self._la_args(t, t))
 
-    def lookahead_step(self, t: int, stream=None) -> None:
-        """Attend step t and stage step t+1 (needs the queries of step t+1)."""
-        lsa.lookahead_step(self.ctx, stream=stream, **self._la_args(t + 1, t))
+    def lookahead_step(self, t: int, stream=None, t_next: Optional[int] = None) -> None:
+        """Attend step t and stage the next prediction from the indexer query of step
+        t_next (default t+1)."""
+        lsa.lookahead_step(self.ctx, stream=stream, **self._la_args(t + 1 if t_next is None else t_next, t))
+
+    def lookahead_attend(self, t: int, stream=None) -> None:
+        """Attend step t over the current prediction's rows (lsa_lookahead_attend)."""
+        lsa.lookahead_attend(self.ctx, stream=stream, **self._la_args(t, t))
 
     def prepare_lookahead(self, steps) -> None:
         """Marshal the descriptors of the listed lookahead steps once (launch with run_prepared)."""

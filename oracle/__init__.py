@@ -33,7 +33,8 @@ ST_NOT_STORED = 4
 def build(force: bool = False) -> str:
     """Compile the oracle with g++ (no HIP headers, no GPU)."""
     os.makedirs(_BUILD, exist_ok=True)
-    if force or not os.path.exists(_LIB_PATH):
+    stale = not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    if force or stale:
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
         subprocess.check_call(["g++", "-std=c++17", "-O2", "-shared", "-fPIC", _SRC, "-o", tmp])
         os.replace(tmp, _LIB_PATH)
@@ -58,7 +59,7 @@ def lib():
             "oracle_project": (None, [P, i32, i32, P, P, i32, i32, i32, i32, P, P]),
             "oracle_threshold_float": (f32, [f64]),
             "oracle_select": (i32, [P, i64, i32, i32, f64, P]),
-            "oracle_ratio_map": (i32, [P, i32, i32, i32, P]),
+            "oracle_ratio_map": (i32, [P, i32, i32, i32, i64, P]),
             "oracle_pool_new": (P, [i64, i32, i32, i64]),
             "oracle_pool_free": (None, [P]),
             "oracle_pool_store": (None, [P, i64, i64]),
@@ -161,10 +162,13 @@ def select(e: np.ndarray, mode: str, k: int, tau: float = 0.5,
     return out[:c].copy()
 
 
-def ratio_map(sel: np.ndarray, src_ratio: int, layer_ratio: int) -> np.ndarray:
+def ratio_map(sel: np.ndarray, src_ratio: int, layer_ratio: int, src_valid: Optional[int] = None) -> np.ndarray:
+    """Source-layer selection -> this layer's ascending complete entries (src_valid: valid
+    source entries; None = unbounded)."""
     sel = _c(sel, np.int32)
     out = np.zeros(max(1, sel.size), np.int32)
-    c = lib().oracle_ratio_map(_p(sel), sel.size, src_ratio, layer_ratio, _p(out))
+    sv = (1 << 62) // max(1, src_ratio) if src_valid is None else int(src_valid)
+    c = lib().oracle_ratio_map(_p(sel), sel.size, src_ratio, layer_ratio, sv, _p(out))
     return out[:c].copy()
 
 
@@ -267,51 +271,94 @@ def attend_kv(q: np.ndarray, K: np.ndarray, V: np.ndarray, kv_dtype: str, row_st
 # ------------------------------------------------------------- decode step --
 class DecodeState:
     """Oracle of whole decode steps for one workload: per sparse layer and
-    sequence an LRU pool; all rows stored up front."""
+    sequence an LRU pool over a store of rows.
 
-    def __init__(self, wl, window_rows: List[List[np.ndarray]], store_rows: List[List[np.ndarray]]):
+    store_rows[l][b] [cap][D] is the content of every entry; the first
+    stored[l][b] entries (all of them by default) are stored up front, the rest
+    by store() during decoding ([P1] store flow).
+
+    step(predict=True) is a step on which the memory indexer fires: score the
+    valid keys, select, then per layer map the selection to the layer's complete
+    entries, stage them and attend.  step(predict=False) is a step of the
+    decoding window the last prediction covers ([P2] LSA section: the indexer is
+    triggered periodically and predicts the chunks of the coming short decoding
+    window): no scoring, no staging; each layer attends over the entries it
+    staged at the last prediction.  A stage that finds a never-stored entry
+    ([P1] error 4) leaves its pool unchanged; that (layer, sequence) then has an
+    empty list and attends to nothing (output 0) until the next prediction."""
+
+    def __init__(self, wl, window_rows: List[List[np.ndarray]], store_rows: List[List[np.ndarray]],
+                 stored: Optional[List[List[int]]] = None):
         # window_rows[layer][b] : [W][D]; store_rows[layer][b] : [cap][D] (kv dtype storage)
         self.wl = wl
         self.window_rows = window_rows
-        self.store_rows = store_rows
+        self.store_rows = [[np.array(r, copy=True) for r in per_b] for per_b in store_rows]
         row_bytes = wl.kv_dim * (4 if wl.kv_dtype == "f32" else 2)
         self.pools = []
+        # the entries each (layer, sequence) staged at the last prediction, and
+        # whether that stage failed (then the list is empty, window included)
+        self.held = [[np.zeros(0, np.int32) for _ in range(wl.batch)] for _ in range(wl.n_layers)]
+        self.failed = [[False] * wl.batch for _ in range(wl.n_layers)]
         for l in range(wl.n_layers):
             cap = wl.layer_cap(l)
             per_b = []
             for b in range(wl.batch):
                 p = Pool(cap, wl.gpu_chunks, wl.window, row_bytes)
-                p.store(0, cap)
+                n0 = cap if stored is None else int(stored[l][b])
+                if n0 > 0:
+                    p.store(0, n0)
                 per_b.append(p)
             self.pools.append(per_b)
 
+    def store(self, l: int, b: int, first: int, rows: np.ndarray) -> None:
+        """[P1] store flow: entries first.. of layer l, sequence b get `rows` and are marked stored."""
+        rows = np.asarray(rows)
+        self.store_rows[l][b][first:first + rows.shape[0]] = rows
+        self.pools[l][b].store(first, rows.shape[0])
+
     def step(self, keys: Sequence[np.ndarray], q_idx: np.ndarray, w_idx: np.ndarray,
-             q_attn: np.ndarray, k: Optional[int] = None) -> dict:
-        """keys[b] [N][dk]; q_idx [B][n_idx][H][dk]; w_idx [B][n_idx][H]; q_attn [L][B][Hq][D]."""
+             q_attn: np.ndarray, k: Optional[int] = None, n_valid: Optional[Sequence[int]] = None,
+             predict: bool = True) -> dict:
+        """keys[b] [N][dk]; q_idx [B][n_idx][H][dk]; w_idx [B][n_idx][H]; q_attn [L][B][Hq][D];
+        n_valid[b]: valid source entries (default: all of keys[b])."""
         wl = self.wl
         k = wl.k if k is None else k
-        res = dict(scores=[], sel=[], layer_sel=[], phys=[], misses=[], out=[])
-        for b in range(wl.batch):
-            e = score(keys[b], wl.key_dtype, q_idx[b], w_idx[b], wl.ensemble)
-            s = select(e, wl.mode, k, wl.tau if wl.tau is not None else 0.5)
-            res["scores"].append(e)
-            res["sel"].append(s)
-        for l in range(wl.n_layers):
-            lsel, lphys, lmiss, lout = [], [], [], []
+        res = dict(scores=[], sel=[], layer_sel=[], phys=[], misses=[], status=[], out=[])
+        if predict:
             for b in range(wl.batch):
-                sl = ratio_map(res["sel"][b], wl.src_ratio, wl.layer_ratios[l])
-                st, phys, miss = self.pools[l][b].stage(sl)
-                if st != 0:
-                    raise RuntimeError(f"oracle stage status {st}")
-                out = attend(q_attn[l][b], self.window_rows[l][b], self.store_rows[l][b],
-                             wl.kv_dtype, sl, wl.scale)
+                nv = None if n_valid is None else int(n_valid[b])
+                e = score(keys[b], wl.key_dtype, q_idx[b], w_idx[b], wl.ensemble, n_valid=nv)
+                s = select(e, wl.mode, k, wl.tau if wl.tau is not None else 0.5)
+                res["scores"].append(e)
+                res["sel"].append(s)
+        for l in range(wl.n_layers):
+            lsel, lphys, lmiss, lst, lout = [], [], [], [], []
+            for b in range(wl.batch):
+                st, phys, miss = 0, None, []
+                if predict:
+                    nv = keys[b].shape[0] if n_valid is None else int(n_valid[b])
+                    sl = ratio_map(res["sel"][b], wl.src_ratio, wl.layer_ratios[l], nv)
+                    st, phys, miss = self.pools[l][b].stage(sl)
+                    if st != 0:
+                        sl, phys, miss = np.zeros(0, np.int32), np.zeros(0, np.int32), []
+                    self.held[l][b] = sl
+                    self.failed[l][b] = st != 0
+                sl = self.held[l][b]
+                if self.failed[l][b]:
+                    out = np.zeros((wl.hq, wl.kv_dim), np.float32)
+                else:
+                    out = attend(q_attn[l][b], self.window_rows[l][b], self.store_rows[l][b],
+                                 wl.kv_dtype, sl, wl.scale)
                 lsel.append(sl)
                 lphys.append(phys)
                 lmiss.append(miss)
+                # on a window step, the status of the prediction it serves
+                lst.append(ST_NOT_STORED if self.failed[l][b] else 0)
                 lout.append(out)
             res["layer_sel"].append(lsel)
             res["phys"].append(lphys)
             res["misses"].append(lmiss)
+            res["status"].append(lst)
             res["out"].append(lout)
         return res
 

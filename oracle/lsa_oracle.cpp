@@ -283,10 +283,21 @@ int32_t oracle_select(const float* e, int64_t n_valid, int32_t mode, int32_t k, 
 // source entry j covers tokens [j*r_src, (j+1)*r_src), which lie in entry
 // floor(j*r_src / r_layer) of a layer whose ratio is a multiple of r_src; the
 // layer's list is the ascending set of those entries, duplicates removed.
+// [P1] store flow: the compressor emits a layer's chunk once its r_layer
+// tokens exist.  Reading: with src_valid source entries (tokens
+// [0, src_valid*r_src) compressed), a layer entry m whose last token
+// (m+1)*r_layer - 1 lies beyond them does not exist yet and is left out of the
+// list; its tokens are all among the newest r_layer - 1 and so inside the
+// 128-row sliding window.
 int32_t oracle_ratio_map(const int32_t* sel, int32_t count, int32_t src_ratio,
-                         int32_t layer_ratio, int32_t* out) {
+                         int32_t layer_ratio, int64_t src_valid, int32_t* out) {
     std::set<int64_t> s;
-    for (int32_t i = 0; i < count; ++i) s.insert((int64_t)sel[i] * src_ratio / layer_ratio);
+    const int64_t tokens = src_valid * (int64_t)src_ratio;
+    for (int32_t i = 0; i < count; ++i) {
+        const int64_t m = (int64_t)sel[i] * src_ratio / layer_ratio;
+        const int64_t last_token = (m + 1) * (int64_t)layer_ratio - 1;
+        if (last_token < tokens) s.insert(m);
+    }
     int32_t n = 0;
     for (int64_t v : s) out[n++] = (int32_t)v;
     return n;

@@ -99,3 +99,175 @@ def test_swap_on_and_off_give_identical_bits():
         assert torch.equal(on.sel, off.sel)
         assert torch.equal(on.out.view(torch.int32), off.out.view(torch.int32)), f"step {t}"
     assert on.pools[0].stats()["misses"] > 0
+
+
+def check_step(t, wl, dw, want, cur=None, check_sel=True):
+    """Compare the GPU step outputs with the oracle's step `want` (rows, counts,
+    attention); cur: the lookahead row-list buffer, or None for the sync one."""
+    W = wl.window
+    if check_sel:
+        cnt = dw.count.cpu().numpy()
+        sel = dw.sel.cpu().numpy()
+        for b in range(wl.batch):
+            assert np.array_equal(sel[b, :cnt[b]], want["sel"][b]), f"step {t} seq {b}: selected set"
+    phys = (dw.phys if cur is None else dw.phys2[cur]).cpu().numpy()
+    nrows = (dw.n_rows if cur is None else dw.n_rows2[cur]).cpu().numpy()
+    out = dw.out.cpu().numpy()
+    for l in range(wl.n_layers):
+        for b in range(wl.batch):
+            if want["status"][l][b] != 0:
+                assert nrows[l, b] == 0, f"step {t} layer {l} seq {b}: a failed stage lists no rows"
+                assert np.all(out[l, b] == 0), f"step {t} layer {l} seq {b}: failed stage attends to nothing"
+                continue
+            n = W + want["layer_sel"][l][b].size
+            assert nrows[l, b] == n, f"step {t} layer {l} seq {b}: row count {nrows[l, b]} vs {n}"
+            if want["phys"][l][b] is not None:
+                assert np.array_equal(phys[l, b, :n], want["phys"][l][b]), f"step {t} layer {l} seq {b}: rows"
+            err = rel_err_rows(out[l, b], want["out"][l][b])
+            assert err <= RTOL[wl.kv_dtype], f"step {t} layer {l} seq {b}: rel err {err}"
+    return out
+
+
+def check_pools(wl, dw, ref):
+    for l, pool in enumerate(dw.pools):
+        st = pool.stats()
+        want = [ref.pools[l][b].stats() for b in range(wl.batch)]
+        for key in ("hits", "misses", "h2d_bytes", "d2h_bytes"):
+            assert st[key] == sum(x[key] for x in want), f"layer {l} {key}: {st[key]}"
+        if pool.swap:
+            for b in range(wl.batch):
+                sl, lru = pool.state(b)
+                rsl, rlru = ref.pools[l][b].state()
+                assert np.array_equal(sl, rsl) and np.array_equal(lru, rlru), f"layer {l} seq {b}: slot table"
+
+
+def growing_run(schedule: str, steps: int = 24):
+    """The stored prefix grows while decoding ([P1] store flow): before step t one
+    more source entry exists (its key counts in n_valid, its ratio-4 rows are
+    stored) and each ratio-128 chunk is stored once its 128 tokens exist; at
+    step 6 a chunk the ratio-4 layer has staged is stored again with new
+    content.  Every step is compared with the oracle, and the pools' slot
+    tables and counters (d2h bytes included) after every step."""
+    wl = L.WORKLOADS["ens_8k"].replace(name="ens_8k_grow")
+    N = wl.n_src
+    n0 = N - steps - 8                       # 8 more entries than the run will need
+    stored = [n0 if r == 4 else n0 * 4 // r for r in wl.layer_ratios]
+    say(f"growing {schedule}: n_valid {n0} -> {n0 + steps}, stored {stored}")
+    dw = DeviceWorkload(wl, keep_host=True, stored=stored)
+    dw.make_steps(steps + 1)
+    ref = oracle.DecodeState(wl, dw.windows, dw.stores, stored=[[s] for s in stored])
+    rng = np.random.default_rng(77)
+
+    def grow(t):
+        j = n0 + t                           # the entry that completes before step t
+        for l, r in enumerate(wl.layer_ratios):
+            if r == 4:
+                rows = dw.stores[l][0][j:j + 1].copy()
+                dw.store(l, 0, j, rows)
+                ref.store(l, 0, j, rows)
+            elif (j + 1) * 4 % r == 0:
+                m = (j + 1) * 4 // r - 1
+                rows = dw.stores[l][0][m:m + 1].copy()
+                dw.store(l, 0, m, rows)
+                ref.store(l, 0, m, rows)
+        dw.n_valid = [j + 1]
+        return [j + 1]
+
+    nv = grow(0)
+    if schedule == "lookahead":
+        dw.lookahead_prime(0)
+    for t in range(steps):
+        if t == 6:
+            # store again a chunk that is staged in the ratio-4 layer, with new content
+            staged = ref.held[0][0]
+            m = int(staged[len(staged) // 2])
+            rows = L.grid_uniform(rng, (1, wl.kv_dim))
+            say(f"  re-store of staged entry {m}")
+            sl0, lru0 = dw.pools[0].state(0)
+            dw.store(0, 0, m, rows)
+            ref.store(0, 0, m, rows)
+            torch.cuda.synchronize()
+            sl1, lru1 = dw.pools[0].state(0)
+            # [P1] store flow: a staged chunk stays staged (no eviction, same LRU order) ...
+            assert np.array_equal(sl0, sl1) and np.array_equal(lru0, lru1)
+            if m in sl1.tolist():
+                # ... and its slot holds the new content
+                slot = sl1.tolist().index(m)
+                assert np.array_equal(dw.kv[0][0, wl.window + slot].cpu().numpy(), rows[0])
+        want = ref.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t], n_valid=nv)
+        if schedule == "sync":
+            dw.step(t)
+            torch.cuda.synchronize()
+            check_step(t, wl, dw, want)
+            check_pools(wl, dw, ref)
+        else:
+            cur = lsa.lookahead_buffer(dw.ctx)
+            nv = grow(t + 1) if t + 1 < steps else nv
+            dw.lookahead_step(t)
+            torch.cuda.synchronize()
+            check_step(t, wl, dw, want, cur=cur, check_sel=False)
+        if schedule == "sync" and t + 1 < steps:
+            nv = grow(t + 1)
+    say(f"growing {schedule}: ok")
+
+
+def test_store_while_decoding_sync():
+    growing_run("sync")
+
+
+def test_not_stored_step_matches_oracle():
+    """A step whose selection reaches entries that were never stored: the failing
+    layers keep their pools unchanged and output zeros (the oracle's reading of
+    [P1] error 4), lsa_pool_stats reports it once, and after the entries are
+    stored the next steps agree with the oracle again."""
+    wl = L.WORKLOADS["ens_8k"].replace(name="ens_8k_unstored")
+    N = wl.n_src
+    stored = [N - 600 if r == 4 else (N - 600) * 4 // r for r in wl.layer_ratios]
+    dw = DeviceWorkload(wl, keep_host=True, stored=stored)
+    dw.make_steps(4)
+    ref = oracle.DecodeState(wl, dw.windows, dw.stores, stored=[[s] for s in stored])
+    saw_error = False
+    for t in range(4):
+        if t == 2:
+            for l, r in enumerate(wl.layer_ratios):
+                first = stored[l]
+                rows = dw.stores[l][0][first:].copy()
+                dw.store(l, 0, first, rows)
+                ref.store(l, 0, first, rows)
+        want = ref.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t])
+        dw.step(t)
+        torch.cuda.synchronize()
+        check_step(t, wl, dw, want)
+        failed = [l for l in range(wl.n_layers) if want["status"][l][0] != 0]
+        say(f"  step {t}: failed layers {failed}")
+        for l, pool in enumerate(dw.pools):
+            if l in failed:
+                saw_error = True
+                with pytest.raises(lsa.LsaError) as e:
+                    pool.stats()
+                assert e.value.status == 4
+        check_pools(wl, dw, ref)
+    assert saw_error, "the workload never selected an unstored entry"
+
+
+@pytest.mark.parametrize("period", [1, 2, 4])
+def test_periodic_indexer_sync(period):
+    """[P2] the indexer fires every `period` steps and its prediction serves the
+    coming window: lsa_decode_step on the first step of each window,
+    lsa_decode_attend on the others; outputs, rows and counters equal the
+    oracle's periodic chain."""
+    wl = L.WORKLOADS["ens_8k"]
+    steps = 8
+    dw = DeviceWorkload(wl, keep_host=True)
+    dw.make_steps(steps)
+    ref = oracle.DecodeState(wl, dw.windows, dw.stores)
+    for t in range(steps):
+        predict = t % period == 0
+        want = ref.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t], predict=predict)
+        if predict:
+            dw.step(t)
+        else:
+            dw.attend(t)
+        torch.cuda.synchronize()
+        check_step(t, wl, dw, want, check_sel=predict)
+    check_pools(wl, dw, ref)

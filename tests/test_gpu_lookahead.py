@@ -141,9 +141,10 @@ def test_lookahead_small_workloads_match_oracle():
 
 @pytest.mark.parametrize("slots", [None, 1024])
 def test_lookahead_batched_threshold_matches_sync(slots):
-    # four sequences of 65536 entries: the separate select histogram, threshold
-    # mode, bf16 rows, and the batched indexing of the fused launches; with 1024
-    # slots both layers also swap (from HBM cold pools), so the copy has misses
+    # four sequences of 65536 entries: the select histogram built by the score
+    # launch for several sequences, threshold mode, bf16 rows, and the batched
+    # indexing of the fused launches; with 1024 slots both layers also swap (from
+    # HBM cold pools), so the copy has misses
     wl = L.WORKLOADS["thresh_256k"]
     if slots is not None:
         wl = wl.replace(gpu_chunks=slots)
@@ -177,3 +178,82 @@ def test_lookahead_batched_threshold_matches_sync(slots):
         la_stats = [p.stats() for p in dw.pools]
         assert sum(s["misses"] for s in la_stats) >= sum(s["misses"] for s in sync_stats) > 0
     say(f"  thresh_256k slots={slots}: lookahead = sync over {n} steps")
+
+
+def test_lookahead_separate_histogram_matches_sync():
+    """Four sequences of a 65536-entry key array with only a few dozen valid
+    entries each: the score launch has fewer workgroups than sequences, so the
+    select histogram runs as its own launch; rows and output bits equal the
+    synchronous steps'."""
+    wl = L.WORKLOADS["thresh_256k"].replace(mode="topk", k=32)
+    dw = DeviceWorkload(wl)
+    dw.make_steps(6)
+    dw.n_valid = [40, 64, 100, 33]
+    sync = []
+    for t in range(4):
+        dw.step(t)
+        torch.cuda.synchronize()
+        sync.append((bits(dw.out.cpu().numpy()).copy(), dw.phys.cpu().numpy().copy(), dw.n_rows.cpu().numpy().copy()))
+    dw.lookahead_prime(0)
+    for t in range(4):
+        cur = lsa.lookahead_buffer(dw.ctx)
+        dw.lookahead_step(t)
+        torch.cuda.synchronize()
+        out, phys, nrows = sync[t]
+        got_n = dw.n_rows2[cur].cpu().numpy()
+        assert np.array_equal(got_n, nrows), f"step {t}: row counts"
+        got_p = dw.phys2[cur].cpu().numpy()
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                m = int(nrows[l, b])
+                assert np.array_equal(got_p[l, b, :m], phys[l, b, :m]), f"step {t} layer {l} seq {b}"
+        assert np.array_equal(bits(dw.out.cpu().numpy()), out), f"step {t}: lookahead vs sync bits"
+    say("  separate-histogram lookahead = sync")
+
+
+@pytest.mark.parametrize("period", [1, 2, 4])
+def test_lookahead_periodic_indexer(period):
+    """[P2] periodic indexer in the lookahead schedule: the last step of each
+    window attends and predicts the next window (lsa_lookahead_step with the
+    next window's indexer query), the other steps only attend
+    (lsa_lookahead_attend).  Rows and outputs equal the oracle's periodic chain
+    and, bit for bit, the synchronous periodic schedule."""
+    wl = L.WORKLOADS["ens_8k"]
+    steps = 8
+    dw = DeviceWorkload(wl, keep_host=True)
+    dw.make_steps(steps + 1)
+    ref = oracle.DecodeState(wl, dw.windows, dw.stores)
+    la = []
+    dw.lookahead_prime(0)
+    for t in range(steps):
+        want = ref.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t], predict=t % period == 0)
+        cur = lsa.lookahead_buffer(dw.ctx)
+        if (t + 1) % period == 0:
+            dw.lookahead_step(t, t_next=t + 1)
+        else:
+            dw.lookahead_attend(t)
+        torch.cuda.synchronize()
+        phys, nrows, out = dw.phys2[cur].cpu().numpy(), dw.n_rows2[cur].cpu().numpy(), dw.out.cpu().numpy()
+        for l in range(wl.n_layers):
+            n = wl.window + want["layer_sel"][l][0].size
+            assert nrows[l, 0] == n, f"step {t} layer {l}: row count"
+            if want["phys"][l][0] is not None:
+                assert np.array_equal(phys[l, 0, :n], want["phys"][l][0]), f"step {t} layer {l}: rows"
+            err = rel_err_rows(out[l, 0], want["out"][l][0])
+            assert err <= RTOL[wl.kv_dtype], f"step {t} layer {l}: rel err {err}"
+        la.append(bits(out).copy())
+    # the synchronous periodic schedule from fresh pools gives the same bits
+    dw.reset_pools()
+    for t in range(steps):
+        if t % period == 0:
+            dw.step(t)
+        else:
+            dw.attend(t)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(dw.out.cpu().numpy()), la[t]), f"step {t}: sync vs lookahead bits"
+    say(f"  periodic lookahead, period {period}: ok")
+
+
+def test_store_while_decoding_lookahead():
+    from test_gpu_decode import growing_run
+    growing_run("lookahead")

@@ -1,4 +1,6 @@
 """GPU parity of fm_score (lsa_score) with oracle.score: bit-exact on grid inputs."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -49,7 +51,7 @@ CASES = [
 def test_score_matches_oracle(case):
     B, N, dk, n_idx, H, kd, ens = case
     say(f"score case {case}")
-    rng = np.random.default_rng(hash(case) & 0xFFFF)
+    rng = np.random.default_rng(zlib.crc32(str(case).encode()))
     keys = L.grid_uniform(rng, (B, N, dk))
     q = L.grid_uniform(rng, (B, n_idx, H, dk))
     w = L.grid_uniform(rng, (B, n_idx, H))
@@ -141,6 +143,57 @@ def test_general_fp32_query_split_is_exact_per_product(kd):
     assert np.array_equal(bits(s.cpu().numpy()[0]), bits(oracle.score(enc, kd, qg[0], wg[0], "max")))
 
 
+def test_mean_ensemble_rounds_the_indexer_sum_once():
+    """Indexer scores 1, 2^-24 and 2^-24 (one head each, exact products): the
+    float sum taken once is 1 + 2^-23, while two float adds in a row would give
+    1; the mean is that sum divided once by 3, exactly as the oracle computes
+    it (and not fl(fl(1 + 2^-24) + 2^-24) / 3)."""
+    dk, N = 128, 64
+    keys = np.zeros((1, N, dk), np.float32)
+    keys[0, :, 0] = 1.0
+    keys[0, 1::2, 0] = 0.5
+    q = np.zeros((1, 3, 1, dk), np.float32)
+    q[0, 0, 0, 0] = 1.0
+    q[0, 1, 0, 0] = 2.0 ** -24
+    q[0, 2, 0, 0] = 2.0 ** -24
+    w = np.ones((1, 3, 1), np.float32)
+    s = torch.zeros((1, N), device=DEV)
+    lsa.score(torch.from_numpy(keys).to(DEV), torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV), s, "mean")
+    got = s.cpu().numpy()[0]
+    want = oracle.score(keys[0], "f32", q[0], w[0], "mean")
+    assert np.array_equal(bits(got), bits(want))
+    assert got[0] == np.float32(np.float32(1 + 2.0 ** -23) / np.float32(3))
+    assert got[0] != np.float32(np.float32(np.float32(1 + 2.0 ** -24) + np.float32(2.0 ** -24)) / np.float32(3))
+
+
+@pytest.mark.parametrize("kd", ["f32", "bf16"])
+def test_mean_ensemble_off_grid(kd):
+    """Mean ensemble with arbitrary fp32 queries and weights (and full-precision
+    fp32 keys): within the fp32 accumulation bound of the oracle's score, per
+    indexer, with the sum of the indexer scores rounded once."""
+    rng = np.random.default_rng(21 if kd == "f32" else 22)
+    B, N, dk, n_idx, H = 1, 2000, 128, 3, 8
+    if kd == "f32":
+        keys = rng.standard_normal((N, dk)).astype(np.float32)
+        enc = keys
+    else:
+        keys = L.grid_uniform(rng, (N, dk))
+        enc = L.encode(keys, "bf16")
+    q = rng.standard_normal((B, n_idx, H, dk)).astype(np.float32)
+    w = rng.random((B, n_idx, H)).astype(np.float32)
+    kt = to_device(enc[None], kd, DEV)
+    s = torch.zeros((B, N), device=DEV)
+    lsa.score(kt, torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV), s, "mean")
+    got = s.cpu().numpy()[0].astype(np.float64)
+    want = oracle.score(enc, kd, q[0], w[0], "mean").astype(np.float64)
+    # each indexer score is within 2*dk ulps of its absolute-value score; the mean
+    # of three such errors plus the two roundings of the mean itself
+    absum = oracle.score(np.abs(keys), "f32", np.abs(q[0]), np.abs(w[0]), "max").astype(np.float64)
+    bound = 2 * dk * 2.0 ** -24 * absum + 2 * np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - want) <= bound + 1e-30)
+    assert np.mean(got == want) > 0.05     # not a vacuous bound: many agree exactly
+
+
 def test_all_negative_dots_give_positive_zero():
     rng = np.random.default_rng(6)
     keys = L.grid_uniform(rng, (1, 256, 64), lo=0.125, hi=1.0)
@@ -183,7 +236,7 @@ MX_CASES = [
 def test_mx_score_matches_oracle(case):
     B, N, dk, n_idx, H, kd, ens = case
     say(f"mx score case {case}")
-    rng = np.random.default_rng(hash(case) & 0xFFFF)
+    rng = np.random.default_rng(zlib.crc32(str(case).encode()))
     keys = [L.mx_keys(rng, N, dk, kd) for _ in range(B)]
     q = L.grid_uniform(rng, (B, n_idx, H, dk))
     w = L.grid_uniform(rng, (B, n_idx, H))

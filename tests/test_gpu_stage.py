@@ -105,18 +105,90 @@ def test_swap_disabled_is_identity_and_rows_resident():
     assert pool.stats()["misses"] == 0
 
 
-def test_not_stored_is_reported():
-    pool, kv = make_pool(1024, 4, 16, 8, 1, "hbm")
-    pool.store(0, 0, np.zeros((100, 128), np.float32))
-    sel = torch.tensor([[3, 150, -1, -1, -1, -1, -1, -1]], dtype=torch.int32, device=DEV)
-    cnt = torch.tensor([2], dtype=torch.int32, device=DEV)
-    phys = torch.zeros((1, W + 8), dtype=torch.int32, device=DEV)
-    nrows = torch.zeros((1,), dtype=torch.int32, device=DEV)
-    lsa.stage(pool, sel, cnt, 4, phys, nrows)
-    with pytest.raises(lsa.LsaError) as e:
-        pool.stats()
-    assert e.value.status == 4
-    assert pool.stats()["misses"] == 2          # the flag is cleared once reported
+def test_not_stored_leaves_the_pool_as_the_oracle_does():
+    """[P1] error 4: a list holding a never-stored entry changes nothing of that
+    sequence (slot table, LRU order and counters equal the oracle's, which
+    returns status 4 and keeps its state), writes an empty row list, and is
+    reported once by the pool's stats; the other sequence of the pool stages as
+    usual, and the failing one continues from its unchanged state."""
+    B, S, k, D = 2, 16, 8, 128
+    pool, kv = make_pool(1024, 4, S, k, B, "hbm", D)
+    rng = np.random.default_rng(12)
+    rows = [L.grid_uniform(rng, (pool.cap, D)) for _ in range(B)]
+    refs = []
+    for b in range(B):
+        pool.store(b, 0, rows[b][:100])
+        r = oracle.Pool(pool.cap, S, W, D * 4)
+        r.store(0, 100)
+        refs.append(r)
+    sel = torch.zeros((B, k), dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    phys = torch.zeros((B, W + k), dtype=torch.int32, device=DEV)
+    nrows = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    steps = [[[3, 7, 9], [1, 2]], [[3, 150], [2, 60, 99]], [[7, 11, 12], [5]], [[150], [3, 4]]]
+    for t, lists in enumerate(steps):
+        sel_np = np.full((B, k), -1, np.int32)
+        for b in range(B):
+            sel_np[b, :len(lists[b])] = lists[b]
+        sel.copy_(torch.from_numpy(sel_np))
+        cnt.copy_(torch.tensor([len(x) for x in lists], dtype=torch.int32))
+        lsa.stage(pool, sel, cnt, 4, phys, nrows)
+        torch.cuda.synchronize()
+        bad = False
+        for b in range(B):
+            st, want_phys, _ = refs[b].stage(np.array(lists[b], np.int32))
+            if st != 0:
+                bad = True
+                assert st == oracle.ST_NOT_STORED
+                assert int(nrows[b]) == 0, f"step {t} seq {b}: a failed stage lists no rows"
+            else:
+                assert int(nrows[b]) == W + len(lists[b])
+                assert np.array_equal(phys[b, :W + len(lists[b])].cpu().numpy(), want_phys)
+            sl, lru = pool.state(b)
+            rsl, rlru = refs[b].state()
+            assert np.array_equal(sl, rsl) and np.array_equal(lru, rlru), f"step {t} seq {b}: slot table"
+        if bad:
+            with pytest.raises(lsa.LsaError) as e:
+                pool.stats()
+            assert e.value.status == 4
+        st = pool.stats()                               # the flag is cleared once reported
+        assert st["hits"] == sum(r.stats()["hits"] for r in refs)
+        assert st["misses"] == sum(r.stats()["misses"] for r in refs)
+        assert st["h2d_bytes"] == sum(r.stats()["h2d_bytes"] for r in refs)
+
+
+def test_incomplete_chunks_are_not_staged():
+    """A ratio-128 layer only lists chunks whose 128 tokens are all covered by the
+    valid source entries (oracle.ratio_map with src_valid); the incomplete last
+    chunk is neither staged nor reported as not stored."""
+    B, S, k, D = 2, 8, 8, 128
+    pool, kv = make_pool(65536, 128, S, k, B, "hbm", D)     # cap 512 > 8 slots: swaps
+    rng = np.random.default_rng(13)
+    refs = []
+    n_valid = [33, 100]                                     # chunks 0 / 0..2 complete
+    for b in range(B):
+        n_st = n_valid[b] * 4 // 128
+        pool.store(b, 0, L.grid_uniform(rng, (n_st, D)))
+        r = oracle.Pool(pool.cap, S, W, D * 4)
+        r.store(0, n_st)
+        refs.append(r)
+    lists = [[0, 31, 32], [5, 40, 64, 96, 99]]
+    sel_np = np.full((B, k), -1, np.int32)
+    for b in range(B):
+        sel_np[b, :len(lists[b])] = lists[b]
+    sel = torch.from_numpy(sel_np).to(DEV)
+    cnt = torch.tensor([len(x) for x in lists], dtype=torch.int32, device=DEV)
+    phys = torch.zeros((B, W + k), dtype=torch.int32, device=DEV)
+    nrows = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    lsa.stage(pool, sel, cnt, 4, phys, nrows, n_valid=n_valid)
+    torch.cuda.synchronize()
+    for b in range(B):
+        lsel = oracle.ratio_map(np.array(lists[b], np.int32), 4, 128, n_valid[b])
+        st, want_phys, _ = refs[b].stage(lsel)
+        assert st == 0
+        assert int(nrows[b]) == W + lsel.size
+        assert np.array_equal(phys[b, :W + lsel.size].cpu().numpy(), want_phys)
+    assert pool.stats()["misses"] == sum(r.stats()["misses"] for r in refs) == 4
 
 
 def test_topk_reduction_override():

@@ -103,3 +103,29 @@ def test_ratio_map_stays_in_layer_capacity():
         lay_cap = oracle.compressed_cap(ctx, 128)
         m = oracle.ratio_map(np.array([0, src_cap - 1]), 4, 128)
         assert m[-1] == lay_cap - 1 and m[0] == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ratio_map_keeps_only_complete_chunks_by_token_enumeration(seed):
+    """Brute force over tokens: a layer chunk is listed iff some selected source
+    entry maps to it and every token of the chunk is covered by the valid source
+    entries (tokens [0, src_valid * r_src))."""
+    rng = np.random.default_rng(300 + seed)
+    r_src = 4
+    for r_l in (4, 8, 128):
+        src_valid = int(rng.integers(0, 200))
+        if src_valid == 0:
+            sel = np.zeros(0, np.int32)
+        else:
+            sel = np.sort(rng.choice(src_valid, size=int(rng.integers(1, src_valid + 1)), replace=False))
+        tokens = set(range(src_valid * r_src))
+        want = []
+        for m in sorted({int(j) * r_src // r_l for j in sel}):
+            if all(t in tokens for t in range(m * r_l, (m + 1) * r_l)):
+                want.append(m)
+        got = oracle.ratio_map(sel.astype(np.int32), r_src, r_l, src_valid)
+        assert got.tolist() == want, (r_l, src_valid)
+    # the hand case of a ratio-128 layer: 33 source entries = 132 tokens: chunk 0
+    # (tokens 0..127) exists, chunk 1 (128..255) does not yet
+    assert oracle.ratio_map(np.array([0, 31, 32], np.int32), 4, 128, 33).tolist() == [0]
+    assert oracle.ratio_map(np.array([0, 31, 32], np.int32), 4, 128, 64).tolist() == [0, 1]
