@@ -336,7 +336,7 @@ class DecodeState:
             for b in range(wl.batch):
                 st, phys, miss = 0, None, []
                 if predict:
-                    nv = keys[b].shape[0] if n_valid is None else int(n_valid[b])
+                    nv = res["scores"][b].size      # the valid entries that were scored
                     sl = ratio_map(res["sel"][b], wl.src_ratio, wl.layer_ratios[l], nv)
                     st, phys, miss = self.pools[l][b].stage(sl)
                     if st != 0:

@@ -8,6 +8,7 @@ import torch
 
 import lsa_inputs as L
 import oracle
+from learned_sparse_kv_amd import lsa
 from learned_sparse_kv_amd.workload import DeviceWorkload
 
 from gpu_util import RTOL, bits, rel_err_rows, say
