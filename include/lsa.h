@@ -383,6 +383,22 @@ typedef struct lsa_step_desc {
 } lsa_step_desc;
 lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same step
+ * as lsa_decode_step (same kernels, same results, bit for bit), but its scratch
+ * (select histogram and candidates, attention partials, row lists, miss lists)
+ * lives in a static device array of LSA_STATIC_SCRATCH_BYTES that every GPU
+ * the library runs on holds until the process ends; the call allocates and
+ * frees nothing (no hipMalloc / hipFree, no events, no timing).  A step needing
+ * more scratch than that returns LSA_ERR_UNSUPPORTED and enqueues nothing.
+ * ctx's device must be current.  Every call on one GPU shares that GPU's
+ * array and it keeps the last call's contents (the call clears what must start
+ * at zero), so calls that overlap on one GPU -- on different streams or from
+ * different threads -- race; the row lists are those of the last call (pass
+ * phys / n_rows to keep them elsewhere). */
+#define LSA_STATIC_SCRATCH_BYTES (32u << 20)
+lsa_status lsa_decode_step_noalloc(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream_t stream);
+
 /* [P2] LSA section: the memory indexer is triggered periodically, and each
  * prediction covers the chunks of the coming short decoding window.  A step of
  * that window on which the indexer does not fire attends over the rows the

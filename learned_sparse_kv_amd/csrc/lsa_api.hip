@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -53,11 +54,50 @@ int n_cu_current() {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// ------------------------------------------------------ static scratch
+// The scratch of lsa_decode_step_noalloc: one static device array, of which
+// every GPU the library runs on holds its own copy (at its own address) until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on
+// the host the name is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in g_scratch_addr.
+static __device__ __align__(256) char scratch[LSA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 128;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch` (device `dev` must
+// be current).  NULL with an error when the lookup fails.
+lsa_status scratch_address(int dev, void** out) {
+    *out = nullptr;
+    if (dev < 0 || dev >= kMaxDevices) return LSA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return LSA_ERR_HIP;
+        }
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return LSA_OK;
+}
+
+// Clears n words (a plain fill kernel, so a captured step records no memset).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ context
 struct lsa_ctx {
     int device = 0;
+    void* scratch = nullptr;    // this device's copy of the static scratch (device address)
+    lsa_status scratch_status = LSA_OK;
     int n_cu = 256;
     void* ws = nullptr;
     size_t ws_bytes = 0;
@@ -294,6 +334,9 @@ lsa_status lsa_ctx_create(lsa_ctx** out, int32_t device) {
     lsa_ctx* c = new lsa_ctx;
     c->device = device;
     c->n_cu = n_cu_current();
+    // the static scratch's device address, looked up once per device (only the
+    // allocation-free step needs it, so a failed lookup fails only that call)
+    c->scratch_status = scratch_address(device, &c->scratch);
     *out = c;
     return LSA_OK;
 }
@@ -1114,6 +1157,36 @@ lsa_status lsa_decode_attend(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t 
     if (st != LSA_OK) return st;
     // the rows lsa_decode_step staged: its attention already filled the slots
     return attend_timed(ctx, P.aa, (hipStream_t)stream);
+}
+
+lsa_status lsa_decode_step_noalloc(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
+    if (!ctx) return fail(LSA_ERR_INVALID_ARG, "ctx is NULL");
+    if (!ctx->scratch)
+        return fail(LSA_ERR_HIP, "device %d: the static scratch has no device address (lookup status %d)",
+                    ctx->device, (int)ctx->scratch_status);
+    int cur = -1;
+    HIPTRY(hipGetDevice(&cur));
+    if (cur != ctx->device)
+        return fail(LSA_ERR_INVALID_ARG, "the context belongs to device %d but device %d is current", ctx->device, cur);
+    StepPlan P;
+    lsa_status st = step_plan(ctx, d, 1, &P, static_cast<char*>(ctx->scratch), LSA_STATIC_SCRATCH_BYTES);
+    if (st != LSA_OK) return st;
+    for (int l = 0; l < P.L; ++l)
+        if (d->pools[l]->swap) P.aa.L[l].src = P.ga.L[l].src;
+    hipStream_t s = (hipStream_t)stream;
+    // the select's histogram region must start at zero; the array keeps whatever
+    // the previous call on this device left in it
+    if (P.zero_clear_words) {
+        const size_t n = P.zero_clear_words;
+        const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
+        hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, s, P.zero_clear, n);
+        HIPTRY(hipGetLastError());
+    }
+    HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s));
+    HIPTRY(launch_fm_select(P.se, s));
+    HIPTRY(launch_kv_stage(P.ga, s));
+    HIPTRY(launch_lsa_attend(P.aa, s));
+    return LSA_OK;
 }
 
 int32_t lsa_lookahead_buffer(const lsa_ctx* ctx) { return ctx ? ctx->la_cur : 0; }

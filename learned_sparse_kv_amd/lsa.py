@@ -106,6 +106,7 @@ _SIGS = {
     "lsa_stage": (i32, [P, P, P, i32, i32, P, P, i32, P, P]),
     "lsa_attend": (i32, [P, P, P, i32, i64, i64, P, i32, P, i32, i32, i32, f32, P, P]),
     "lsa_decode_step": (i32, [P, ctypes.POINTER(StepDesc), P]),
+    "lsa_decode_step_noalloc": (i32, [P, ctypes.POINTER(StepDesc), P]),
     "lsa_lookahead_prime": (i32, [P, ctypes.POINTER(StepDesc), P]),
     "lsa_lookahead_step": (i32, [P, ctypes.POINTER(StepDesc), P]),
     "lsa_lookahead_buffer": (i32, [P]),
@@ -519,6 +520,16 @@ def decode_step(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, 
     d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
                          mode, tau, n_valid, phys, n_rows, key_scales)
     _check(lib().lsa_decode_step(ctx.h, ctypes.byref(d), _stream(stream)))
+
+
+def decode_step_noalloc(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,
+                        k: int, src_ratio: int, scale: float, ensemble: str = "max", mode: str = "topk",
+                        tau: float = 0.5, n_valid=None, phys=None, n_rows=None, stream=None,
+                        key_scales=None) -> None:
+    """decode_step with its scratch in the library's static device array (lsa_decode_step_noalloc)."""
+    d, keep = _step_desc(keys, q_idx, w_idx, pools, q_attn, out, scores, sel, count, k, src_ratio, scale, ensemble,
+                         mode, tau, n_valid, phys, n_rows, key_scales)
+    _check(lib().lsa_decode_step_noalloc(ctx.h, ctypes.byref(d), _stream(stream)))
 
 
 def decode_attend(ctx: Ctx, *, keys, q_idx, w_idx, pools: Sequence[Pool], q_attn, out, scores, sel, count,
