@@ -9,9 +9,16 @@ Default workload: 1M-token context, ratio-4 source layer of 262144 entries,
 Two schedules are timed: "lookahead" (lsa_lookahead_step: the current step's
 row copy and attention share launches with the next step's score and
 selection) and "sync" (lsa_decode_step: all of it in order).  `value` is the
---schedule one (default lookahead); the other is reported beside it.  With a
-1M workload the run also times the 256K threshold workload (batch 4, bf16
-rows) in both schedules, reported as `ctx_256k`.
+--schedule one (default lookahead); the other is reported beside it, and so is
+the lookahead schedule with a periodic indexer (one prediction per window of
+2, 4 or 8 steps).  With a 1M workload the run also times the 256K threshold
+workload (batch 4, bf16 rows) in both schedules with a sampled parity check
+(`ctx_256k`) and the KVSwap step at its 32K shape (`kvswap_32k`).
+
+`roofline` is fm_score's: each launch timed alone after a read that evicts the
+keys from every cache (HBM-bound); the back-to-back figure, where part of the
+134 MB of keys comes from the 256 MiB last-level cache, is reported beside it
+as `cache_assisted`.
 
 Prints ONE JSON line.  Per-kernel times come from HIP events recorded on the
 launch stream inside the timed region; the CPU baseline is the plain oracle
@@ -63,6 +70,51 @@ def stored_traffic(workload, score_src_hash):
     return float(m_bytes.group(1))
 
 
+def cpu_info():
+    """(CPU model from /proc/cpuinfo, logical CPUs, CPUs this process may run on)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, os.cpu_count(), avail
+
+
+def oracle_threads():
+    """Threads for the CPU baseline: the CPUs this process may use, at most 16 (the
+    host share of one GPU on the box)."""
+    return max(1, min(16, cpu_info()[2]))
+
+
+def run_threads(fn, n):
+    """Runs fn(i) on n threads (the oracle's ctypes calls release the GIL); returns wall seconds."""
+    import threading
+    errs = []
+
+    def body(i):
+        try:
+            fn(i)
+        except BaseException as e:   # re-raised in the caller
+            errs.append(e)
+    ths = [threading.Thread(target=body, args=(i,)) for i in range(n)]
+    t0 = time.perf_counter()
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    if errs:
+        raise errs[0]
+    return time.perf_counter() - t0
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -84,6 +136,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=28)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-kvswap", action="store_true", help="skip the KVSwap leg of the 1M run")
     ap.add_argument("--graph", type=int, default=0,
                     help="time eager launches (0, the default: faster here, the host keeps ahead of the GPU) "
                          "or HIP-graph replays, one graph per step (1)")
@@ -122,6 +175,29 @@ def main():
     dw = DeviceWorkload(wl, keep_host=not args.no_cpu_baseline, log=log)
     dw.make_steps(Wm + K + 2)
     log(f"set-up {time.time() - t0:.1f}s")
+
+    def periodic_region(period):
+        """The lookahead schedule with one prediction per window of `period` steps:
+        lsa_lookahead_step on the last step of a window, lsa_lookahead_attend on the
+        others (eager launches, pools start empty).  Returns ms per step."""
+        dw.reset_pools()
+        dw.lookahead_prime(0)
+
+        def run(t):
+            if (t + 1) % period == 0:
+                dw.lookahead_step(t, t_next=t + 1)
+            else:
+                dw.lookahead_attend(t)
+        for t in range(Wm):
+            run(t)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for t in range(Wm, Wm + K):
+            run(t)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t_start) * 1e3 / K
+        log(f"lookahead, period {period} (eager): {ms * 1e3:.1f} us/step")
+        return ms
 
     def timed_region(schedule, use_graph):
         """Warm up, then time K steps of the schedule, launched eagerly or as HIP-graph
@@ -169,6 +245,8 @@ def main():
     alt_ms, _, _ = timed_region(args.schedule, not use_graph)
     ms_per_step, stats0, stats1 = timed_region(args.schedule, use_graph)
     value = 1e3 / ms_per_step
+    periodic = {str(d): {"value": round(1e3 / m, 2), "ms_per_step": round(m, 5)}
+                for d, m in ((d, periodic_region(d)) for d in (2, 4, 8))}
 
     # ---- kernel-timed region: the same K steps of the synchronous schedule
     # launched eagerly with HIP events around every kernel on the launch stream
@@ -213,7 +291,7 @@ def main():
     # so the keys come from HBM rather than from the cache they stay in across
     # back-to-back launches
     flush = torch.zeros(64 << 20, dtype=torch.int64, device="cuda")
-    RC = 16
+    RC = 32
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(RC)]
     for e0, e1 in evs:
         flush.sum()
@@ -221,7 +299,9 @@ def main():
         lsa.score(dw.keys, dw.q_idx[t_last], dw.w_idx[t_last], dw.scores, ensemble=wl.ensemble, key_scales=dw.key_scales)
         e1.record(st)
     torch.cuda.synchronize()
-    cold_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)[RC // 2]
+    cold_all = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    cold_ms = sum(cold_all) / RC
+    cold_median_ms = cold_all[RC // 2]
 
     # ---- the indexers' query/weight projection (hidden[4096] -> q, w) at this
     # workload's indexer shape, bf16 weights: back to back behind a GPU sleep that
@@ -237,7 +317,16 @@ def main():
 
     # ---- the metric's other context length: the 256K threshold workload (batch 4,
     # bf16 rows), both schedules launched eagerly, K steps each
-    ctx256 = other_context("thresh_256k", K, Wm) if wl.name.startswith("swap_1m") else None
+    ctx256 = other_context("thresh_256k", K, Wm, parity_steps=0 if args.no_cpu_baseline else 2) \
+        if wl.name.startswith("swap_1m") else None
+    kvs = kvswap_measure(L.KVSWAP_WORKLOADS["kvswap_32k"], min(K, 32), min(Wm, 8),
+                         parity_steps=0 if args.no_cpu_baseline else 2) \
+        if wl.name.startswith("swap_1m") and not args.no_kvswap else None
+    # the rolling buffer of the KVSwap article's section 3.2 (400 slots, top 200,
+    # recency and importance weighed equally, 70 % high-water mark)
+    kvs_wr = kvswap_measure(L.KVSWAP_WORKLOADS["kvswap_32k_wr"], min(K, 32), min(Wm, 8),
+                            parity_steps=0 if args.no_cpu_baseline else 2) \
+        if wl.name.startswith("swap_1m") and not args.no_kvswap else None
 
     # ---- algorithmic bytes (per launch)
     # a key row (plus its E8M0 block scales for the MX dtypes) read, a score written
@@ -257,15 +346,17 @@ def main():
 
     src_hash = kernel_source_hash("fm_score.hip", "lsa_internal.hpp")
     traffic = stored_traffic(wl.name, src_hash)
-    roofline = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "fm_score",
-                "algorithmic_bytes_per_launch": score_bytes, "avg_launch_us": round(score_ms * 1e3, 2),
-                "timing": f"{R} back-to-back launches between HIP events on the launch stream",
-                "cold_cache": {"avg_launch_us": round(cold_ms * 1e3, 2),
-                               "achieved": round(score_bytes / (cold_ms * 1e-3) / 1e9, 1),
-                               "frac": round(score_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                               "timing": f"median of {RC} launches, each bracketed by HIP events after a "
-                                         "512 MiB read that evicts the keys from every cache"}}
+    cold_gbs = score_bytes / (cold_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(cold_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(cold_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "fm_score",
+                "algorithmic_bytes_per_launch": score_bytes, "avg_launch_us": round(cold_ms * 1e3, 2),
+                "median_launch_us": round(cold_median_ms * 1e3, 2),
+                "timing": f"average of {RC} launches, each bracketed by HIP events on the launch stream after a "
+                          "512 MiB read that evicts the keys from every cache (the keys come from HBM)",
+                "cache_assisted": {"avg_launch_us": round(score_ms * 1e3, 2), "achieved": round(score_gbs, 1),
+                                   "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                                   "timing": f"{R} back-to-back launches between HIP events: part of the keys "
+                                             "stay in the 256 MiB last-level cache between launches"}}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same steps, and a
     # parity check of the GPU on those steps (pools reset on both sides)
@@ -316,11 +407,26 @@ def main():
         parity = {"steps": n_s, "selected_sets_and_rows_identical": sel_ok, "max_rel_err": max_err,
                   "lookahead_max_rel_err": la_err, "tolerance": tol,
                   "pass": bool(sel_ok and max_err <= tol and la_err <= tol)}
-        cpu = {"value": round(n_s / cpu_s, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n_s} full decode steps (steps 0..{n_s - 1}) of {wl.name}: score of all "
-                         f"{wl.batch}x{wl.n_src} entries, select, {wl.n_layers} layers of stage + attend; "
-                         f"single-threaded C++ oracle, {cpu_s:.1f}s"}
-        log(f"cpu baseline {cpu['value']} steps/s over {n_s} steps ({time.perf_counter() - tc0:.1f}s incl. GPU replay)")
+        log(f"cpu baseline (1 thread) {n_s / cpu_s:.3f} steps/s over {n_s} steps "
+            f"({time.perf_counter() - tc0:.1f}s incl. GPU replay)")
+        # throughput on the host's cores: independent oracle instances (fresh pools,
+        # the same steps), one per thread
+        T = oracle_threads()
+        n_t = 3
+
+        def one(i):
+            st = oracle.DecodeState(wl, dw.windows, dw.stores)
+            for t in range(n_t):
+                st.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t])
+        wall = run_threads(one, T)
+        model, n_cpu, avail = cpu_info()
+        cpu = {"value": round(T * n_t / wall, 4), "unit": "steps/s", "cores": T, "kind": "oracle",
+               "sample": f"{T} threads, each an independent oracle over steps 0..{n_t - 1} of {wl.name} (score of "
+                         f"all {wl.batch}x{wl.n_src} entries, select, {wl.n_layers} layers of stage + attend), "
+                         f"{wall:.1f}s wall; unchanged C++ oracle, its calls release the GIL",
+               "single_thread": {"value": round(n_s / cpu_s, 4), "steps": n_s, "seconds": round(cpu_s, 1)},
+               "cpu_model": model, "cpus": n_cpu, "cpus_available": avail}
+        log(f"cpu baseline ({T} threads) {cpu['value']} steps/s, {wall:.1f}s wall")
 
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": Wm,
@@ -342,6 +448,11 @@ def main():
         "project": proj,
         "adaptive_capacity": adaptive,
         "ctx_256k": ctx256,
+        "kvswap_32k": kvs,
+        "kvswap_32k_wr": kvs_wr,
+        "periodic_indexer": {"schedule": "lookahead, eager; one prediction per window of `period` steps "
+                                         "(lsa_lookahead_step on a window's last step, lsa_lookahead_attend "
+                                         "on the others)", "by_period": periodic},
         "kernels_us_events": {k: round(avg[k] * 1e3, 2) for k in KERNELS},
         "score_attend_hbm_frac": round(sa_frac, 4),
         "attend_resident": {"us": round(att_res_ms * 1e3, 2), "bytes": int(attend_bytes),
@@ -355,16 +466,18 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def other_context(name, K, Wm):
+def other_context(name, K, Wm, parity_steps=0):
     """Decode steps/s of another workload (its own set-up; pools start empty; eager
-    launches; the lookahead schedule with descriptors marshalled beforehand)."""
+    launches; the lookahead schedule with descriptors marshalled beforehand), and a
+    parity check of `parity_steps` synchronous steps against the oracle."""
+    import numpy as np
     import torch
 
     import lsa_inputs as L
     from learned_sparse_kv_amd.workload import DeviceWorkload
 
     wl = L.WORKLOADS[name]
-    dw = DeviceWorkload(wl, keep_host=False, log=log)
+    dw = DeviceWorkload(wl, keep_host=parity_steps > 0, log=log)
     dw.make_steps(Wm + K + 2)
     res = {"workload": name, "ctx": wl.ctx, "batch": wl.batch, "src_entries": wl.n_src,
            "sparse_layer_ratios": list(wl.layer_ratios), "select": f"{wl.mode} cap {wl.k}", "kv_dtype": wl.kv_dtype,
@@ -388,6 +501,28 @@ def other_context(name, K, Wm):
         ms = (time.perf_counter() - t0) * 1e3 / K
         res[schedule] = {"value": round(1e3 / ms, 2), "unit": "steps/s", "ms_per_step": round(ms, 5)}
         log(f"{name} {schedule} (eager): {ms * 1e3:.1f} us/step")
+    if parity_steps:
+        import oracle
+        ref = oracle.DecodeState(wl, dw.windows, dw.stores)
+        dw.reset_pools()
+        ok, err = True, 0.0
+        for t in range(parity_steps):
+            dw.step(t)
+            torch.cuda.synchronize()
+            want = ref.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t])
+            cnt, sel, out = dw.count.cpu().numpy(), dw.sel.cpu().numpy(), dw.out.cpu().numpy()
+            for b in range(wl.batch):
+                ok &= bool(np.array_equal(sel[b, :cnt[b]], want["sel"][b]))
+                for l in range(wl.n_layers):
+                    w_ = want["out"][l][b]
+                    den = np.maximum(np.abs(w_).max(axis=1), 1e-30)
+                    err = max(err, float((np.abs(out[l, b] - w_).max(axis=1) / den).max()))
+        tol = 1e-5 if wl.kv_dtype == "f32" else 2e-2
+        res["parity"] = {"steps": parity_steps, "selected_sets_identical": ok, "max_rel_err": err,
+                         "tolerance": tol, "pass": bool(ok and err <= tol),
+                         "note": "both sides read the same bf16 rows and accumulate in fp32 / double; the "
+                                 "tolerance is the bf16 storage bound, max_rel_err the observed difference"}
+        log(f"{name} parity over {parity_steps} steps: sets {ok}, max rel err {err:.3g}")
     del dw
     torch.cuda.empty_cache()
     return res
@@ -482,22 +617,37 @@ def project_timing(wl, flush):
                       "cold: median of 8 single launches after the 512 MiB read"}
 
 
-def bench_kvswap(args):
-    """KVSwap variant: one step = low-rank score of every group over all
-    positions, top-k per group, LRU staging of every pool, per-head attention."""
+def kvswap_segments(wl, n=16):
+    """n segments spread over layers, groups and sequences (distinct; pool indices
+    l * groups + g above 16 included)."""
+    segs = []
+    i = 0
+    while len(segs) < min(n, wl.n_seg):
+        l = (i * 7 + 3) % wl.layers
+        g = (i * 3 + 1) % wl.groups
+        b = (i * 5 + 2) % wl.batch
+        s_ = wl.seg(l, g, b)
+        if s_ not in segs:
+            segs.append(s_)
+        i += 1
+    return sorted(segs)
+
+
+def kvswap_measure(wl, K, Wm, parity_steps=2, n_parity_segs=16):
+    """KVSwap step at its workload: eager steps/s, per-kernel event times, the
+    score+attention HBM fraction, and (parity_steps > 0) the GPU's selections and
+    outputs of n_parity_segs sampled segments against the oracle, one thread per
+    segment, which also gives the CPU baseline."""
     import numpy as np
     import torch
 
-    import lsa_inputs as L
     from learned_sparse_kv_amd.kvswap_workload import DeviceKVSwap
 
-    wl = L.KVSWAP_WORKLOADS[args.workload]
-    K, Wm = args.steps, args.warmup
     log(f"workload {wl.name}: ctx={wl.ctx} B={wl.batch} layers={wl.layers} groups={wl.groups}x{wl.group_heads}x"
         f"{wl.head_dim} rank={wl.rank} k={wl.k} slots={wl.slots} segments={wl.n_seg}")
     t0 = time.time()
     dw = DeviceKVSwap(wl, log=log)
-    dw.make_steps(Wm + K)
+    dw.make_steps(max(Wm + K, parity_steps))
     log(f"set-up {time.time() - t0:.1f}s")
     for t in range(Wm):
         dw.step(t)
@@ -540,40 +690,58 @@ def bench_kvswap(args):
                 "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "lowrank_p + lowrank_scan",
                 "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(avg["score"] * 1e3, 2)}
     cpu = parity = None
-    if not args.no_cpu_baseline:
+    if parity_steps:
         import oracle
-        segs = [0, wl.n_seg // 2, wl.n_seg - 1]
+        segs = kvswap_segments(wl, n_parity_segs)
         ref = oracle.KVSwapState(wl, segs)
         dw.reset_pools()
-        inputs = {s: dw.host_inputs(s, 0) for s in segs}
-        ok, max_err, cpu_s, n_s = True, 0.0, 0.0, max(1, min(args.cpu_sample_steps, 3))
-        for t in range(n_s):
+        inputs = {}
+
+        def load(i):
+            inputs[segs[i]] = dw.host_inputs(segs[i], 0)
+        run_threads(load, len(segs))
+        ok, max_err, cpu_wall, seg_steps = True, 0.0, 0.0, 0
+        errs = {}
+        for t in range(parity_steps):
             dw.step(t)
             torch.cuda.synchronize()
             sel, cnt, out = dw.sel.cpu().numpy(), dw.count.cpu().numpy(), dw.out.cpu().numpy()
-            for sgi in segs:
-                U, S, V, _, cold = inputs[sgi]
-                c0 = time.perf_counter()
-                want = ref.step(sgi, U, S, V, dw.q_np[t, sgi], cold)
-                cpu_s += time.perf_counter() - c0
-                ok &= bool(cnt[sgi] == want["sel"].size and np.array_equal(sel[sgi, :cnt[sgi]], want["sel"]))
+            wants = {}
+
+            def one(i):
+                sg = segs[i]
+                U, S, V, _, cold = inputs[sg]
+                wants[sg] = ref.step(sg, U, S, V, dw.q_np[t, sg], cold)
+            cpu_wall += run_threads(one, len(segs))
+            seg_steps += len(segs)
+            for sg in segs:
+                want = wants[sg]
+                ok &= bool(cnt[sg] == want["sel"].size and np.array_equal(sel[sg, :cnt[sg]], want["sel"]))
                 den = np.maximum(np.abs(want["out"]).max(axis=1), 1e-30)
-                max_err = max(max_err, float((np.abs(out[sgi] - want["out"]).max(axis=1) / den).max()))
-        per_seg = cpu_s / (n_s * len(segs))
-        parity = {"steps": n_s, "segments": segs, "selected_sets_identical": ok, "max_rel_err": max_err,
-                  "tolerance": 1e-5, "pass": bool(ok and max_err <= 1e-5)}
-        cpu = {"value": round(1.0 / (per_seg * wl.n_seg), 6), "unit": "steps/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n_s} steps x {len(segs)} of the {wl.n_seg} group segments (score over {T} positions, "
-                         f"top-{wl.k}, LRU, {wl.group_heads}-head attention), {per_seg * 1e3:.1f} ms per "
-                         f"segment-step, scaled to a whole step; single-threaded C++ oracle"}
+                errs[sg] = max(errs.get(sg, 0.0), float((np.abs(out[sg] - want["out"]).max(axis=1) / den).max()))
+        max_err = max(errs.values())
+        pool_ids = sorted({sg // wl.batch for sg in segs})
+        parity = {"steps": parity_steps, "segments": segs, "pools": pool_ids, "selected_sets_identical": ok,
+                  "max_rel_err": max_err, "tolerance": 2e-2, "pass": bool(ok and max_err <= 2e-2),
+                  "note": "f16 K/V on both sides; the tolerance is the f16 storage bound, max_rel_err the "
+                          "observed difference"}
+        model, n_cpu, avail = cpu_info()
+        per_seg = cpu_wall / seg_steps * len(segs)   # seconds per segment-step on one thread
+        cpu = {"value": round(len(segs) / (per_seg * wl.n_seg), 6), "unit": "steps/s", "cores": len(segs),
+               "kind": "oracle",
+               "sample": f"{parity_steps} steps x {len(segs)} of the {wl.n_seg} group segments (score over {T} "
+                         f"positions, top-{wl.k}, LRU, {wl.group_heads}-head attention), one thread per segment, "
+                         f"{cpu_wall:.1f}s wall; scaled to a whole step; unchanged C++ oracle",
+               "cpu_model": model, "cpus": n_cpu, "cpus_available": avail}
+        log(f"{wl.name} parity over {parity_steps} steps x {len(segs)} segments: sets {ok}, max rel err {max_err:.3g}")
     res = {
-        "metric": "KVSwap decode steps/s (32K ctx, batch 16, 32 layers x 8 groups of 4 heads, top-400)",
-        "value": round(1e3 / ms_per_step, 3), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": Wm,
-        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16", "data": "synthetic (seeded 1/8-grid values)",
+        "metric": f"KVSwap decode steps/s (32K ctx, batch 16, 32 layers x 8 groups of 4 heads, top-{wl.k})",
+        "value": round(1e3 / ms_per_step, 3), "unit": "steps/s", "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 4),
         "config": {"workload": wl.name, "ctx": T, "batch": wl.batch, "layers": wl.layers, "groups": wl.groups,
                    "group_heads": wl.group_heads, "head_dim": wl.head_dim, "rank": r, "k": wl.k,
-                   "slots": wl.slots, "segments": n_seg, "launch": "eager"},
+                   "slots": wl.slots, "segments": n_seg, "launch": "eager",
+                   "replacement": {"recency_weight": wl.recency_w, "high_water": wl.high_water}},
         "roofline": roofline,
         "attend": {"achieved_gbs": round(attend_gbs, 1), "bytes_per_launch": attend_bytes,
                    "bytes_written_per_launch": round(attend_written), "achieved_gbs_read_and_written": round(attend_rw_gbs, 1),
@@ -584,7 +752,24 @@ def bench_kvswap(args):
         "hit_rate": round(hits / max(1, hits + misses), 4),
         "parity": parity,
     }
-    print(json.dumps(res), flush=True)
+    log(f"{wl.name}: {ms_per_step:.3f} ms/step")
+    del dw
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_kvswap(args):
+    """KVSwap variant as the headline: one step = low-rank score of every group over
+    all positions, top-k per group, LRU staging of every pool, per-head attention."""
+    import lsa_inputs as L
+    wl = L.KVSWAP_WORKLOADS[args.workload]
+    res = kvswap_measure(wl, args.steps, args.warmup, parity_steps=0 if args.no_cpu_baseline else 2)
+    line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1}
+    line.update({"steps": res.pop("steps"), "warmup": res.pop("warmup"), "ms_per_step": res.pop("ms_per_step"),
+                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+                 "data": "synthetic (seeded 1/8-grid values)"})
+    line.update(res)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -278,6 +278,26 @@ lsa_status lsa_pool_reset(lsa_pool* pool, lsa_stream_t stream);
  * pools keep every row and ignore the capacity. */
 lsa_status lsa_pool_set_capacity(lsa_pool* pool, int32_t capacity, lsa_stream_t stream);
 int32_t    lsa_pool_capacity(const lsa_pool* pool);
+/* KVSwap article §3.2 (rolling buffer): replacement by LRU weighted with the
+ * entries' importance scores, and a prefetch trigger at 70 % buffer
+ * utilisation.  For a swapping pool:
+ *   recency_weight w (percent, 0..100): the eviction candidates of a step
+ *     (entries resident when it starts and not selected by it) are evicted in
+ *     ascending w*a + (100-w)*c, ties to the smaller a, where a is the
+ *     candidate's recency rank (0 = least recently used) and c its importance
+ *     rank (0 = lowest score of the step's scorer for that entry, equal scores
+ *     ranked by a).  100 is plain LRU.  Below 100 the stage needs the step's
+ *     scores of the pool's own entries: the pool's ratio must be the scored
+ *     source ratio (lsa_decode_step passes its scores, lsa_kvswap_step its
+ *     low-rank scores, lsa_stage its `importance`).
+ *   high_water h (percent, 1..100): after a step the pool keeps at most
+ *     max(floor(h * capacity / 100), the step's entries) slots in use,
+ *     evicting further candidates in the same order, so the next step's misses
+ *     first take the freed slots (the lowest free slot first).  100 is off.
+ * Policies beyond plain LRU need gpu_chunks <= 1024.  Takes effect from the
+ * next stage; a pool that used them keeps taking free slots from anywhere
+ * below its capacity. */
+lsa_status lsa_pool_set_replacement(lsa_pool* pool, int32_t recency_weight, int32_t high_water);
 /* The adaptive policy, over the steps since the previous call (or reset):
  * with h hits, m misses and x bytes of H2D in `steps` steps, grow by `step`
  * slots (up to max_capacity) when m/(h+m) > grow_miss_rate or x/steps >
@@ -327,13 +347,16 @@ lsa_status lsa_pool_state(lsa_pool* pool, int32_t b, int32_t* slot_logical, int3
  *   count device i32 [batch]
  *   n_valid host [batch] valid source-layer entries per sequence, or NULL
  *         (every chunk complete)
+ *   importance device f32 [batch][compressed_cap]: the step's score of every
+ *         entry, for a pool whose replacement weighs importance (its ratio must
+ *         equal src_ratio); NULL otherwise
  *   phys  device i32 [batch][phys_stride], phys_stride >= window + sel_stride
  *   n_rows device i32 [batch]
  * sel_stride must not exceed the pool's gpu_chunks when it swaps (it is the
  * most entries a step can stage), nor 1024. */
 lsa_status lsa_stage(lsa_pool* pool, const int32_t* sel, const int32_t* count, int32_t sel_stride,
-                     int32_t src_ratio, const int64_t* n_valid, int32_t* phys, int32_t phys_stride,
-                     int32_t* n_rows, lsa_stream_t stream);
+                     int32_t src_ratio, const int64_t* n_valid, const float* importance, int32_t* phys,
+                     int32_t phys_stride, int32_t* n_rows, lsa_stream_t stream);
 
 /* ----------------------------------------------------------------- attend --
  * [P1] overview "Two-tier KV cache" and indexed_cached_attention (window +

@@ -195,41 +195,117 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
     const int packed = block_excl_scan<kNT>((hit ? 1 : 0) | (miss ? 1 << 16 : 0), s_scan, &tot);
     const int hit_rank = packed & 0xFFFF, miss_rank = packed >> 16;
     const int n_hit = tot & 0xFFFF, n_miss = tot >> 16;
-    const int free_slots = L.cap_slots - n_used;   // slots [n_used, capacity) are unused
-    const int n_evict = n_miss > free_slots ? n_miss - free_slots : 0;
+    int new_used;
+    if (!L.general) {
+        const int free_slots = L.cap_slots - n_used;   // slots [n_used, capacity) are unused
+        const int n_evict = n_miss > free_slots ? n_miss - free_slots : 0;
 
-    // 3. untouched used slots in old list order; the last n_evict are evicted
-    constexpr int kPer = kMaxSlots / kNT;
-    bool untouched[kPer];
-    int c_untouched = 0;
+        // 3. untouched used slots in old list order; the last n_evict are evicted
+        constexpr int kPer = kMaxSlots / kNT;
+        bool untouched[kPer];
+        int c_untouched = 0;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int p = tid * kPer + q;
-        untouched[q] = p < n_used && s_hit[s_order[p]] == 0;
-        c_untouched += untouched[q] ? 1 : 0;
-    }
-    int n_untouched;
-    int before = block_excl_scan<kNT>(c_untouched, s_scan, &n_untouched);
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        if (!untouched[q]) continue;
-        const int p = tid * kPer + q;
-        const int after = n_untouched - before - 1;
-        if (after < n_evict) {
-            s_victim[after] = s_order[p];           // victim 0 = least recently used
-        } else {
-            lru[n_miss + n_hit + before] = s_order[p];
+        for (int q = 0; q < kPer; ++q) {
+            const int p = tid * kPer + q;
+            untouched[q] = p < n_used && s_hit[s_order[p]] == 0;
+            c_untouched += untouched[q] ? 1 : 0;
         }
-        ++before;
-    }
-    __syncthreads();
+        int n_untouched;
+        int before = block_excl_scan<kNT>(c_untouched, s_scan, &n_untouched);
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            if (!untouched[q]) continue;
+            const int p = tid * kPer + q;
+            const int after = n_untouched - before - 1;
+            if (after < n_evict) {
+                s_victim[after] = s_order[p];           // victim 0 = least recently used
+            } else {
+                lru[n_miss + n_hit + before] = s_order[p];
+            }
+            ++before;
+        }
+        __syncthreads();
 
-    // 4. slots for the misses; the evicted chunks leave the table
-    if (miss) slot = miss_rank < free_slots ? n_used + miss_rank : s_victim[miss_rank - free_slots];
-    int old = -1;
-    if (tid < n_evict) old = s_logical[s_victim[tid]];
-    __syncthreads();
-    if (old >= 0) slot_of[old] = -1;
+        // 4. slots for the misses; the evicted chunks leave the table
+        if (miss) slot = miss_rank < free_slots ? n_used + miss_rank : s_victim[miss_rank - free_slots];
+        int old = -1;
+        if (tid < n_evict) old = s_logical[s_victim[tid]];
+        __syncthreads();
+        if (old >= 0) slot_of[old] = -1;
+        new_used = n_used + (n_miss < free_slots ? n_miss : free_slots);
+    } else {
+        // [P4] rolling-buffer reading (gpu_chunks <= kNT): free slots may lie
+        // anywhere below the capacity; the candidates (untouched used slots) are
+        // evicted in ascending recency_w * a + (100 - recency_w) * c, a = recency
+        // rank (0 = least recent), c = importance rank (0 = lowest score, ties by
+        // a), ties by a; then the high-water mark frees the next candidates down
+        // to max(hw_slots, this step's entries).  Thread t handles LRU position t,
+        // slot t and candidate t.
+        __shared__ int s_free[kNT];
+        __shared__ int s_cand[kNT];     // candidate slots by recency rank
+        __shared__ float s_cimp[kNT];
+        __shared__ int s_cprio[kNT];
+        const bool fr = tid < L.cap_slots && tid < S && s_logical[tid] < 0;
+        int n_free;
+        const int fpos = block_excl_scan<kNT>(fr ? 1 : 0, s_scan, &n_free);
+        if (fr) s_free[fpos] = tid;
+        const int uslot = tid < n_used ? s_order[tid] : -1;
+        const bool cand = uslot >= 0 && s_hit[uslot] == 0;
+        int n_cand;
+        const int cpos = block_excl_scan<kNT>(cand ? 1 : 0, s_scan, &n_cand);
+        if (cand) s_cand[n_cand - cpos - 1] = uslot;
+        __syncthreads();
+        if (L.recency_w < 100) {
+            // an entry past the complete ones (valid entries shrank) ranks lowest
+            float my_imp = 0.0f;
+            if (tid < n_cand) {
+                const int e = s_logical[s_cand[tid]];
+                my_imp = e < complete ? L.imp[(int64_t)b * L.imp_stride + e] : -INFINITY;
+            }
+            s_cimp[tid] = my_imp;
+            __syncthreads();
+            int c = 0;
+            if (tid < n_cand)
+                for (int j = 0; j < n_cand; ++j) {
+                    const float o = s_cimp[j];
+                    c += (o < my_imp || (o == my_imp && j < tid)) ? 1 : 0;
+                }
+            const int prio = L.recency_w * tid + (100 - L.recency_w) * c;
+            s_cprio[tid] = prio;
+            __syncthreads();
+            int v = 0;
+            if (tid < n_cand)
+                for (int j = 0; j < n_cand; ++j) {
+                    const int o = s_cprio[j];
+                    v += (o < prio || (o == prio && j < tid)) ? 1 : 0;
+                }
+            if (tid < n_cand) s_victim[v] = s_cand[tid];
+        } else if (tid < n_cand) {
+            s_victim[tid] = s_cand[tid];
+        }
+        __syncthreads();
+        const int n_ev_miss = n_miss > n_free ? n_miss - n_free : 0;
+        const int kept = n_hit + n_miss + (n_cand - n_ev_miss);
+        const int limit = L.hw_slots > n_hit + n_miss ? L.hw_slots : n_hit + n_miss;
+        int n_extra = kept > limit ? kept - limit : 0;
+        if (n_extra > n_cand - n_ev_miss) n_extra = n_cand - n_ev_miss;
+        const int n_ev = n_ev_miss + n_extra;
+        int old = -1;
+        if (tid < n_ev) {
+            old = s_logical[s_victim[tid]];
+            s_hit[s_victim[tid]] = 2;                  // evicted
+        }
+        if (miss) slot = miss_rank < n_free ? s_free[miss_rank] : s_victim[miss_rank - n_free];
+        __syncthreads();
+        if (old >= 0) slot_of[old] = -1;
+        if (tid >= n_ev_miss && tid < n_ev) logical_of[s_victim[tid]] = -1;
+        // the candidates that stay, in their old order, after the misses and hits
+        const bool stays = cand && s_hit[uslot] != 2;
+        int n_stay;
+        const int spos = block_excl_scan<kNT>(stays ? 1 : 0, s_scan, &n_stay);
+        if (stays) lru[n_miss + n_hit + spos] = uslot;
+        new_used = n_hit + n_miss + n_stay;
+    }
     if (miss) {
         slot_of[l] = slot;
         logical_of[slot] = l;
@@ -247,7 +323,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
     if (hit) lru[n_miss + n_hit - 1 - hit_rank] = slot;
     if (l >= 0) phys[L.window + tid] = L.window + slot;
     if (tid == 0) {
-        L.meta[b * 4 + 0] = n_used + (n_miss < free_slots ? n_miss : free_slots);
+        L.meta[b * 4 + 0] = new_used;
         uint64_t* st = L.stats + (int64_t)b * 4;
         st[0] += (uint64_t)n_hit;
         st[1] += (uint64_t)n_miss;
@@ -294,17 +370,18 @@ __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L,
 // GPU_CHUNKS; the procedure is the oracle's reading).  The first C entries of
 // the LRU list (the most recent) stay and the rest leave the slot table; every
 // staying entry in a slot >= C moves, with its row, to the lowest vacated slot
-// below C, both taken in ascending slot order; the LRU list keeps its order
-// with the new slot ids.  Used slots are always 0..n_used-1, so afterwards
-// they are 0..C-1.  One workgroup per sequence; thread t ranks slots
-// kPer*t .. kPer*t + kPer - 1.
+// below C (a free slot or one whose entry left), both taken in ascending slot
+// order; the LRU list keeps its order with the new slot ids.  Used slots may
+// lie anywhere below S (a high-water mark leaves free slots between them).
+// One workgroup per sequence; thread t ranks slots kPer*t .. kPer*t + kPer - 1.
 __global__ __launch_bounds__(kNT) void pool_shrink_kernel(const StageLayer L, const int C) {
     const int b = blockIdx.x, tid = threadIdx.x;
     int32_t* slot_of = L.slot_of + (int64_t)b * L.cap;
     int32_t* logical_of = L.logical_of + (int64_t)b * L.S;
     int32_t* lru = L.lru + (int64_t)b * L.S;
     const int n_used = L.meta[b * 4 + 0];
-    if (n_used <= C || n_used > L.S) return;   // uniform: every thread read the same count
+    const int S = L.S;
+    if (n_used > S) return;   // uniform: every thread read the same count
     __shared__ int s_scan[kNT / 64 + 1];
     __shared__ int s_lru[kMaxSlots];     // LRU list before (slot ids)
     __shared__ int s_log[kMaxSlots];     // occupant of each slot before
@@ -312,7 +389,7 @@ __global__ __launch_bounds__(kNT) void pool_shrink_kernel(const StageLayer L, co
     __shared__ uint8_t s_keep[kMaxSlots];
     __shared__ int s_vac[kMaxSlots];     // vacated slots below C, by rank
     __shared__ int s_high[kMaxSlots];    // staying slots >= C, by rank
-    for (int i = tid; i < n_used; i += kNT) {
+    for (int i = tid; i < S; i += kNT) {
         s_keep[i] = 0;
         s_log[i] = logical_of[i];
     }
@@ -320,7 +397,7 @@ __global__ __launch_bounds__(kNT) void pool_shrink_kernel(const StageLayer L, co
     for (int p = tid; p < n_used; p += kNT) {
         const int sl = lru[p];
         s_lru[p] = sl;
-        if (p < C && sl >= 0 && sl < n_used) s_keep[sl] = 1;
+        if (p < C && sl >= 0 && sl < S) s_keep[sl] = 1;
     }
     __syncthreads();
     constexpr int kPer = kMaxSlots / kNT;
@@ -328,7 +405,7 @@ __global__ __launch_bounds__(kNT) void pool_shrink_kernel(const StageLayer L, co
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int sl = tid * kPer + q;
-        if (sl < n_used) {
+        if (sl < S) {
             c_vac += (sl < C && !s_keep[sl]) ? 1 : 0;
             c_high += (sl >= C && s_keep[sl]) ? 1 : 0;
         }
@@ -339,26 +416,27 @@ __global__ __launch_bounds__(kNT) void pool_shrink_kernel(const StageLayer L, co
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int sl = tid * kPer + q;
-        if (sl >= n_used) continue;
+        if (sl >= S) continue;
         s_new[sl] = (sl < C && s_keep[sl]) ? sl : -1;
         if (sl < C && !s_keep[sl]) s_vac[r_vac++] = sl;
         if (sl >= C && s_keep[sl]) s_high[r_high++] = sl;
     }
     __syncthreads();
-    // n_high == n_vac (C entries stay, C - n_vac of them below C); the min only
-    // keeps a damaged table from indexing past the ranked lists
+    // at most C entries stay, so n_high <= n_vac; the min only keeps a damaged
+    // table from indexing past the ranked lists
     const int n_move = n_high < n_vac ? n_high : n_vac;
     for (int r = tid; r < n_move; r += kNT) s_new[s_high[r]] = s_vac[r];
     __syncthreads();
-    for (int sl = tid; sl < n_used; sl += kNT) {
+    for (int sl = tid; sl < S; sl += kNT) {
         const int l = s_log[sl];
         if (l >= 0 && l < L.cap) slot_of[l] = s_new[sl];
-        if (sl >= C) logical_of[sl] = -1;
+        if (!s_keep[sl] || sl >= C) logical_of[sl] = -1;
     }
+    __syncthreads();
     for (int r = tid; r < n_move; r += kNT) logical_of[s_vac[r]] = s_log[s_high[r]];
     for (int p = tid; p < n_used; p += kNT) {
         const int sl = s_lru[p];
-        lru[p] = (p < C && sl >= 0 && sl < n_used) ? s_new[sl] : -1;
+        lru[p] = (p < C && sl >= 0 && sl < S) ? s_new[sl] : -1;
     }
     // rows of the moved entries: slot row s_high[r] -> slot row s_vac[r]
     const int cpr = L.row_bytes / 16;
@@ -384,7 +462,7 @@ __global__ __launch_bounds__(kNT) void pool_shrink_kernel(const StageLayer L, co
             }
         }
     }
-    if (tid == 0) L.meta[b * 4 + 0] = C;
+    if (tid == 0) L.meta[b * 4 + 0] = n_used < C ? n_used : C;
 }
 
 // Copies the rows a stage recorded as missed (src[b][r] >= 0: cold entry of

@@ -258,6 +258,9 @@ struct lsa_pool {
     bool cold_owned = false;    // false: the caller's cold_buf
     uint64_t d2h_bytes = 0;
     int32_t capacity = 0;       // slots a swapping pool may use (adaptive GPU_CHUNKS), <= gpu_chunks
+    int32_t recency_w = 100;    // replacement weighting, percent (100 = plain LRU)
+    int32_t high_water = 100;   // percent of the capacity kept in use at most after a step
+    bool general = false;       // set once a policy beyond plain LRU was used: free slots may have holes
     uint64_t last_hits = 0, last_misses = 0, last_h2d = 0;   // counters at the last lsa_pool_adapt
 };
 
@@ -488,7 +491,8 @@ lsa_status select_setup(lsa_ctx* c, const float* scores, int32_t n_seg, int64_t 
 }
 
 StageLayer stage_layer(const lsa_pool* p, const int32_t* sel, const int32_t* count, int32_t sel_stride,
-                       int32_t src_ratio, int32_t* phys, int32_t phys_stride, int32_t* n_rows) {
+                       int32_t src_ratio, int32_t* phys, int32_t phys_stride, int32_t* n_rows,
+                       const float* imp = nullptr, int64_t imp_stride = 0) {
     StageLayer L;
     memset(&L, 0, sizeof(L));
     L.slot_of = p->slot_of;
@@ -515,7 +519,24 @@ StageLayer stage_layer(const lsa_pool* p, const int32_t* sel, const int32_t* cou
     L.sel_stride = sel_stride;
     L.phys_stride = phys_stride;
     L.row_bytes = p->row_bytes;
+    L.general = p->general ? 1 : 0;
+    L.recency_w = p->recency_w;
+    L.hw_slots = p->high_water < 100 ? (int32_t)((int64_t)p->high_water * p->capacity / 100) : INT32_MAX;
+    L.imp = imp;
+    L.imp_stride = imp_stride;
     return L;
+}
+
+// A pool that weighs its replacement needs the step's scores of its own entries:
+// its ratio must be the source ratio (entries = scored entries).
+lsa_status stage_importance_check(const lsa_pool* p, const float* imp, int32_t src_ratio, int l) {
+    if (!p->swap || p->recency_w >= 100) return LSA_OK;
+    if (!imp) return fail(LSA_ERR_INVALID_ARG, "pool %d weighs importance in its replacement: the step's scores "
+                                               "are needed", l);
+    if (p->d.ratio != src_ratio)
+        return fail(LSA_ERR_UNSUPPORTED, "pool %d weighs importance in its replacement but its ratio %d is not the "
+                                         "scored source ratio %d", l, p->d.ratio, src_ratio);
+    return LSA_OK;
 }
 
 // valid source entries per sequence (NULL: unbounded, every chunk complete)
@@ -806,6 +827,20 @@ lsa_status lsa_pool_set_capacity(lsa_pool* p, int32_t capacity, lsa_stream_t str
 
 int32_t lsa_pool_capacity(const lsa_pool* p) { return p ? p->capacity : -1; }
 
+lsa_status lsa_pool_set_replacement(lsa_pool* p, int32_t recency_weight, int32_t high_water) {
+    if (!p) return fail(LSA_ERR_INVALID_ARG, "pool is NULL");
+    if (recency_weight < 0 || recency_weight > 100 || high_water < 1 || high_water > 100)
+        return fail(LSA_ERR_INVALID_ARG, "recency_weight %d not in [0, 100] or high_water %d not in [1, 100]",
+                    recency_weight, high_water);
+    if (p->swap && (recency_weight < 100 || high_water < 100) && p->d.gpu_chunks > 1024)
+        return fail(LSA_ERR_UNSUPPORTED, "a replacement beyond plain LRU needs gpu_chunks <= 1024 (got %d)",
+                    p->d.gpu_chunks);
+    p->recency_w = recency_weight;
+    p->high_water = high_water;
+    if (recency_weight < 100 || high_water < 100) p->general = true;
+    return LSA_OK;
+}
+
 lsa_status lsa_pool_adapt(lsa_pool* p, const lsa_adapt_policy* pol, int32_t steps, int32_t* capacity,
                           lsa_stream_t stream) {
     if (!p || !pol) return fail(LSA_ERR_INVALID_ARG, "lsa_pool_adapt: NULL argument");
@@ -897,9 +932,12 @@ lsa_status lsa_pool_state(lsa_pool* p, int32_t b, int32_t* slot_logical, int32_t
 
 // ------------------------------------------------------------------- stage
 lsa_status lsa_stage(lsa_pool* p, const int32_t* sel, const int32_t* count, int32_t sel_stride, int32_t src_ratio,
-                     const int64_t* n_valid, int32_t* phys, int32_t phys_stride, int32_t* n_rows, lsa_stream_t stream) {
+                     const int64_t* n_valid, const float* importance, int32_t* phys, int32_t phys_stride,
+                     int32_t* n_rows, lsa_stream_t stream) {
     if (!p || !sel || !count || !phys || !n_rows) return fail(LSA_ERR_INVALID_ARG, "lsa_stage: NULL argument");
     lsa_status st = stage_check(p, sel_stride, src_ratio, phys_stride);
+    if (st != LSA_OK) return st;
+    st = stage_importance_check(p, importance, src_ratio, 0);
     if (st != LSA_OK) return st;
     StageArgs a;
     memset(&a, 0, sizeof(a));
@@ -907,7 +945,7 @@ lsa_status lsa_stage(lsa_pool* p, const int32_t* sel, const int32_t* count, int3
     a.batch = p->d.batch;
     st = fill_src_valid(&a, n_valid);
     if (st != LSA_OK) return st;
-    a.L[0] = stage_layer(p, sel, count, sel_stride, src_ratio, phys, phys_stride, n_rows);
+    a.L[0] = stage_layer(p, sel, count, sel_stride, src_ratio, phys, phys_stride, n_rows, importance, p->cap);
     hipStream_t s = (hipStream_t)stream;
     HIPTRY(launch_kv_stage(a, s));
     return LSA_OK;
@@ -1013,6 +1051,8 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
     for (int l = 0; l < d->n_layers; ++l) {
         st = stage_check(d->pools[l], k_eff, d->src_ratio, phys_stride);
         if (st != LSA_OK) return st;
+        st = stage_importance_check(d->pools[l], d->scores, d->src_ratio, l);
+        if (st != LSA_OK) return st;
     }
     const int L = d->n_layers;
     // workspace: select candidates | attend partials | phys | n_rows | src | miss lists | miss counts
@@ -1080,7 +1120,7 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
         int32_t* ph = P->phys + (size_t)l * B * phys_stride;
         int32_t* nr = P->n_rows + (size_t)l * B;
         int32_t* sr = P->srcs + (size_t)l * B * phys_stride;
-        P->ga.L[l] = stage_layer(p, d->sel, d->count, d->k, d->src_ratio, ph, phys_stride, nr);
+        P->ga.L[l] = stage_layer(p, d->sel, d->count, d->k, d->src_ratio, ph, phys_stride, nr, d->scores, d->n_keys);
         P->ga.L[l].defer_copy = 1;
         P->ga.L[l].src = sr;
         P->ga.L[l].miss = P->miss + (size_t)l * B * phys_stride * 2;
@@ -1422,7 +1462,7 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     for (int i = 0; i < d->n_pools; ++i) {
         const size_t seg0 = (size_t)i * B;
         host[i] = stage_layer(d->pools[i], d->sel + seg0 * d->k, d->count + seg0, d->k, 1, d->phys + seg0 * d->k,
-                              d->k, d->n_rows + seg0);
+                              d->k, d->n_rows + seg0, d->scores + seg0 * d->T, d->T);
         host[i].defer_copy = 1;
         host[i].src = srcs + seg0 * d->k;
         host[i].seg_cold = seg_cold + seg0;

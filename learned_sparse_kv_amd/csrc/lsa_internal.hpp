@@ -179,6 +179,14 @@ struct StageLayer {
     // n_miss[b] = their number (0 for a resident layer)
     uint64_t* miss;             // [batch][phys_stride][2]
     int32_t* n_miss;            // [batch]
+    // replacement beyond plain LRU (S <= 1024 only): general = 1 takes free
+    // slots from anywhere below cap_slots, evicts candidates in the order that
+    // weighs recency (recency_w percent) against importance (imp[b][entry],
+    // the step's scores; read when recency_w < 100), and frees slots down to
+    // max(hw_slots, the step's entries) after the step
+    int32_t general, recency_w, hw_slots;
+    int64_t imp_stride;
+    const float* imp;
 };
 struct StageArgs {
     int32_t n_layers, batch;

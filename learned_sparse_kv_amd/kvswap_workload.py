@@ -70,6 +70,8 @@ class DeviceKVSwap:
                             kv_stride_b=S * 2 * C, cold_buf=self.cold[g], cold_stride_b=T * row_bytes)
             for b in range(B):
                 pool.mark_stored(b, 0, T)
+            if wl.recency_w < 100 or wl.high_water < 100:
+                pool.set_replacement(wl.recency_w, wl.high_water)
             self.pools.append(pool)
         torch.cuda.synchronize()
         say(f"{P} pools of {S} slots x batch {B}, swap={self.pools[0].swap}")

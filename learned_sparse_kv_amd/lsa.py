@@ -100,10 +100,11 @@ _SIGS = {
     "lsa_pool_reset": (i32, [P, P]),
     "lsa_pool_set_capacity": (i32, [P, i32, P]),
     "lsa_pool_capacity": (i32, [P]),
+    "lsa_pool_set_replacement": (i32, [P, i32, i32]),
     "lsa_pool_adapt": (i32, [P, P, i32, P, P]),
     "lsa_pool_stats": (i32, [P, ctypes.POINTER(PoolStats), P]),
     "lsa_pool_state": (i32, [P, i32, P, P, ctypes.POINTER(i32), P]),
-    "lsa_stage": (i32, [P, P, P, i32, i32, P, P, i32, P, P]),
+    "lsa_stage": (i32, [P, P, P, i32, i32, P, P, P, i32, P, P]),
     "lsa_attend": (i32, [P, P, P, i32, i64, i64, P, i32, P, i32, i32, i32, f32, P, P]),
     "lsa_decode_step": (i32, [P, ctypes.POINTER(StepDesc), P]),
     "lsa_decode_step_noalloc": (i32, [P, ctypes.POINTER(StepDesc), P]),
@@ -383,6 +384,10 @@ class Pool:
     def capacity(self) -> int:
         return int(lib().lsa_pool_capacity(self.h))
 
+    def set_replacement(self, recency_weight: int = 100, high_water: int = 100) -> None:
+        """Replacement weighing recency against importance, and the high-water mark (lsa_pool_set_replacement)."""
+        _check(lib().lsa_pool_set_replacement(self.h, int(recency_weight), int(high_water)))
+
     def adapt(self, steps: int, min_capacity: int, max_capacity: int, step: int, grow_miss_rate: float = 0.5,
               grow_h2d_bytes_per_step: float = 10e6, shrink_miss_rate: float = 0.0, stream=None) -> int:
         """Adaptive capacity from the counters since the last call (lsa_pool_adapt); -> the new capacity."""
@@ -413,14 +418,18 @@ class Pool:
         return sl, lr[:n.value].copy()
 
 
-def stage(pool: Pool, sel, count, src_ratio: int, phys, n_rows, n_valid=None, stream=None) -> None:
+def stage(pool: Pool, sel, count, src_ratio: int, phys, n_rows, n_valid=None, importance=None,
+          stream=None) -> None:
     """sel [B][k] i32, count [B] i32 -> phys [B][window + k] i32, n_rows [B] i32; n_valid:
-    valid source entries per sequence (None: every chunk complete)."""
+    valid source entries per sequence (None: every chunk complete); importance [B][cap] f32
+    for a pool that weighs importance in its replacement."""
     _dev(sel, "sel"), _dev(count, "count"), _dev(phys, "phys"), _dev(n_rows, "n_rows")
+    if importance is not None:
+        _dev(importance, "importance")
     nv = _host_i64(n_valid)
     _check(lib().lsa_stage(pool.h, _ptr(sel), _ptr(count), sel.shape[1], src_ratio,
-                           ctypes.cast(nv, P) if nv else None, _ptr(phys), phys.shape[1], _ptr(n_rows),
-                           _stream(stream)))
+                           ctypes.cast(nv, P) if nv else None, _ptr(importance), _ptr(phys), phys.shape[1],
+                           _ptr(n_rows), _stream(stream)))
 
 
 def attend(ctx: Ctx, q, kv, phys, n_rows, out, scale: float, kv_rows: Optional[int] = None,

@@ -69,6 +69,8 @@ class DeviceWorkload:
             rows = lsa.Pool.rows_needed(wl.ctx, wl.layer_ratios[l], W, wl.gpu_chunks)
             kv = torch.zeros((B, rows, D), dtype=torch_dtype(wl.kv_dtype), device=self.dev)
             pool = lsa.Pool(wl.ctx, wl.layer_ratios[l], kv, W, wl.gpu_chunks, wl.k, D, B, cold=wl.cold)
+            if pool.swap and (wl.recency_w < 100 or wl.high_water < 100):
+                pool.set_replacement(wl.recency_w if wl.layer_ratios[l] == wl.src_ratio else 100, wl.high_water)
             wins, stores = [], []
             for b in range(B):
                 win = L.encode(L.window_rows(wl, l, b), wl.kv_dtype)

@@ -191,6 +191,11 @@ class Workload:
     hq: int = 16
     dist: str = "uniform"     # "uniform" or "planted"
     drift: Optional[float] = None  # fraction of indexer-query coordinates redrawn per step
+    # replacement of the swapping pools (KVSwap article §3.2 reading): recency
+    # weight in percent for the layers whose ratio is the source ratio (100 =
+    # plain LRU), and the high-water mark in percent of the capacity (100 = off)
+    recency_w: int = 100
+    high_water: int = 100
 
     @property
     def n_src(self) -> int:
@@ -249,6 +254,12 @@ WORKLOADS["swap_1m_fp8"] = WORKLOADS["swap_1m"].replace(name="swap_1m_fp8", key_
 # 17.8 and 34.6 MB of keys)
 WORKLOADS["swap_1m_mxfp4"] = WORKLOADS["swap_1m"].replace(name="swap_1m_mxfp4", key_dtype="mxfp4")
 WORKLOADS["swap_1m_mxint8"] = WORKLOADS["swap_1m"].replace(name="swap_1m_mxint8", key_dtype="mxint8")
+# the 1M workload with the rolling-buffer replacement: recency and importance
+# weighed equally, and at most 70 % of the 1024 slots kept in use after a step
+WORKLOADS["swap_1m_wr"] = WORKLOADS["swap_1m"].replace(name="swap_1m_wr", recency_w=50, high_water=70)
+# a small one for parity: 8K context, 1024 slots for top-512 (the ratio-4 layer swaps)
+WORKLOADS["ens_8k_wr"] = WORKLOADS["ens_8k"].replace(name="ens_8k_wr", gpu_chunks=1024, recency_w=50,
+                                                    high_water=70, drift=0.05)
 
 
 # --------------------------------------------------------------------------
@@ -407,6 +418,8 @@ class KVSwapWorkload:
     kv_dtype: str = "f16"
     steps: int = 8
     drift: Optional[float] = None
+    recency_w: int = 100      # replacement weighting, percent (100 = plain LRU)
+    high_water: int = 100     # slots kept in use after a step, percent of the 400 (100 = off)
 
     @property
     def C(self) -> int:
@@ -443,6 +456,14 @@ KVSWAP_WORKLOADS = {
     "kvswap_32k": KVSwapWorkload(name="kvswap_32k", base_seed=1006, ctx=32768, batch=16, layers=32, groups=8,
                                  k=400, slots=400, steps=16, drift=0.05),
 }
+# the rolling buffer of the article's section 3.2: 400 slots per group, the
+# replacement weighing recency and importance equally, at most 70 % of the
+# slots in use after a step; each step keeps its top 200, so the buffer holds
+# earlier entries too and the weighting decides which of them stay
+KVSWAP_WORKLOADS["kvswap_small_wr"] = dataclasses.replace(KVSWAP_WORKLOADS["kvswap_small"], name="kvswap_small_wr",
+                                                          k=200, recency_w=50, high_water=70)
+KVSWAP_WORKLOADS["kvswap_32k_wr"] = dataclasses.replace(KVSWAP_WORKLOADS["kvswap_32k"], name="kvswap_32k_wr",
+                                                        k=200, recency_w=50, high_water=70)
 
 HALF = 0.5
 

@@ -63,7 +63,8 @@ def lib():
             "oracle_pool_new": (P, [i64, i32, i32, i64]),
             "oracle_pool_free": (None, [P]),
             "oracle_pool_store": (None, [P, i64, i64]),
-            "oracle_pool_stage": (i32, [P, P, i32, P, P, P, P]),
+            "oracle_pool_stage": (i32, [P, P, i32, P, P, P, P, P]),
+            "oracle_pool_set_replacement": (None, [P, i32, i32]),
             "oracle_pool_stats": (None, [P, P]),
             "oracle_pool_set_capacity": (None, [P, i32]),
             "oracle_pool_capacity": (i32, [P]),
@@ -189,15 +190,23 @@ class Pool:
     def store(self, first: int, count: int) -> None:
         lib().oracle_pool_store(self._h, first, count)
 
-    def stage(self, sel: np.ndarray):
-        """-> (status, phys [W+n], misses [(logical, slot)] in processing order)."""
+    def set_replacement(self, recency_weight: int = 100, high_water: int = 100) -> None:
+        """[P4] §3.2 reading: replacement order weighing recency against importance
+        (percent; 100 = plain LRU), and the high-water mark (percent of the capacity)."""
+        lib().oracle_pool_set_replacement(self._h, int(recency_weight), int(high_water))
+
+    def stage(self, sel: np.ndarray, importance: Optional[np.ndarray] = None):
+        """-> (status, phys [W+n], misses [(logical, slot)] in processing order);
+        importance [cap] f32: the step's score of every entry (weighted pools only)."""
         sel = _c(sel, np.int32)
         n = sel.size
         phys = np.zeros(self.window + n, np.int32)
         ml = np.zeros(max(1, n), np.int32)
         ms = np.zeros(max(1, n), np.int32)
         nm = ctypes.c_int32(0)
-        st = lib().oracle_pool_stage(self._h, _p(sel), n, _p(phys), _p(ml), _p(ms), ctypes.byref(nm))
+        imp = None if importance is None else _c(importance, np.float32)
+        st = lib().oracle_pool_stage(self._h, _p(sel), n, _p(imp) if imp is not None else None, _p(phys), _p(ml),
+                                     _p(ms), ctypes.byref(nm))
         return int(st), phys, list(zip(ml[:nm.value].tolist(), ms[:nm.value].tolist()))
 
     def set_capacity(self, capacity: int) -> None:
@@ -292,7 +301,9 @@ class DecodeState:
         # window_rows[layer][b] : [W][D]; store_rows[layer][b] : [cap][D] (kv dtype storage)
         self.wl = wl
         self.window_rows = window_rows
-        self.store_rows = [[np.array(r, copy=True) for r in per_b] for per_b in store_rows]
+        # the caller's arrays, copied only when store() first changes one
+        self.store_rows = [list(per_b) for per_b in store_rows]
+        self._own = [[False] * len(per_b) for per_b in store_rows]
         row_bytes = wl.kv_dim * (4 if wl.kv_dtype == "f32" else 2)
         self.pools = []
         # the entries each (layer, sequence) staged at the last prediction, and
@@ -304,15 +315,25 @@ class DecodeState:
             per_b = []
             for b in range(wl.batch):
                 p = Pool(cap, wl.gpu_chunks, wl.window, row_bytes)
+                p.set_replacement(self._weight(l), getattr(wl, "high_water", 100))
                 n0 = cap if stored is None else int(stored[l][b])
                 if n0 > 0:
                     p.store(0, n0)
                 per_b.append(p)
             self.pools.append(per_b)
 
+    def _weight(self, l: int) -> int:
+        """Recency weight of layer l's pools: the workload's, for layers whose entries
+        are the scored source entries; plain LRU elsewhere."""
+        wl = self.wl
+        return getattr(wl, "recency_w", 100) if wl.layer_ratios[l] == wl.src_ratio else 100
+
     def store(self, l: int, b: int, first: int, rows: np.ndarray) -> None:
         """[P1] store flow: entries first.. of layer l, sequence b get `rows` and are marked stored."""
         rows = np.asarray(rows)
+        if not self._own[l][b]:
+            self.store_rows[l][b] = np.array(self.store_rows[l][b], copy=True)
+            self._own[l][b] = True
         self.store_rows[l][b][first:first + rows.shape[0]] = rows
         self.pools[l][b].store(first, rows.shape[0])
 
@@ -338,7 +359,12 @@ class DecodeState:
                 if predict:
                     nv = res["scores"][b].size      # the valid entries that were scored
                     sl = ratio_map(res["sel"][b], wl.src_ratio, wl.layer_ratios[l], nv)
-                    st, phys, miss = self.pools[l][b].stage(sl)
+                    imp = None
+                    if self._weight(l) < 100:
+                        # the step's score of every entry; entries not scored rank lowest
+                        imp = np.full(self.pools[l][b].cap, -np.inf, np.float32)
+                        imp[:res["scores"][b].size] = res["scores"][b]
+                    st, phys, miss = self.pools[l][b].stage(sl, imp)
                     if st != 0:
                         sl, phys, miss = np.zeros(0, np.int32), np.zeros(0, np.int32), []
                     self.held[l][b] = sl
@@ -379,6 +405,7 @@ class KVSwapState:
         for seg in self.segs:
             p = Pool(wl.ctx, wl.slots, 0, row_bytes)
             p.store(0, wl.ctx)
+            p.set_replacement(getattr(wl, "recency_w", 100), getattr(wl, "high_water", 100))
             self.pools[seg] = p
 
     def step(self, seg, U, S, V, q, cold) -> dict:
@@ -387,7 +414,7 @@ class KVSwapState:
         wl = self.wl
         e = lowrank_score(U, S, V, q)
         sel = select(e, "topk", wl.k)
-        st, phys, miss = self.pools[seg].stage(sel)
+        st, phys, miss = self.pools[seg].stage(sel, e)
         if st != 0:
             raise RuntimeError(f"oracle stage status {st}")
         flat = np.ascontiguousarray(cold, dtype=np.uint16).reshape(-1)

@@ -326,6 +326,8 @@ struct OracleSwapLayerState {
     uint64_t hits = 0, misses = 0, h2d_bytes = 0, d2h_bytes = 0;
     int32_t capacity;                         // slots in use at most (adaptive GPU_CHUNKS)
     uint64_t last_hits = 0, last_misses = 0, last_h2d = 0;   // counters at the last adapt
+    int32_t recency_weight = 100;             // replacement weighting, percent (100 = plain LRU)
+    int32_t high_water = 100;                 // percent of the capacity kept in use at most after a step
 };
 
 void* oracle_pool_new(int64_t cap, int32_t gpu_chunks, int32_t window, int64_t row_bytes) {
@@ -349,11 +351,34 @@ void oracle_pool_store(void* pool, int64_t first, int64_t count) {
     p->d2h_bytes += (uint64_t)count * (uint64_t)p->row_bytes;
 }
 
+// [P4] §3.2 (rolling buffer): the replacement weighs LRU order with the
+// entries' importance scores, and a prefetch is triggered at 70 % buffer
+// utilisation.  The page gives neither formula.  Readings:
+//  * the candidates for eviction are the entries resident when the step starts
+//    and not selected by it.  Each gets a recency rank a (0 = least recently
+//    used, in LRU order) and an importance rank c (0 = lowest importance -- the
+//    step's prediction score of that entry --, equal scores ranked by a), and
+//    candidates are evicted in ascending order of w*a + (100-w)*c, equal values
+//    by a, where w is the recency weight in percent (100 = plain LRU);
+//  * with a high-water mark h percent below 100, a step that leaves more than
+//    max(floor(h * capacity / 100), its own entries) slots in use evicts the
+//    next candidates in the same order down to that count: the freed slots are
+//    where the next step's misses land, without an eviction.
+// w and h are set per pool; with both at 100 the stage below is the page's
+// plain LRU loop.
+void oracle_pool_set_replacement(void* pool, int32_t recency_weight, int32_t high_water) {
+    auto* p = static_cast<OracleSwapLayerState*>(pool);
+    p->recency_weight = recency_weight;
+    p->high_water = high_water;
+}
+
 // sel: ascending unique logical IDs of this layer (n of them).
+// importance: the step's score of every logical ID ([compressed_cap]); read
+// only when the pool weighs its replacement (may be NULL otherwise).
 // phys: [window + n]; rows 0..window-1 are the window, then one row per ID.
 // miss_logical / miss_slot: [n]; the misses in processing order.
 // Returns 0, or 4 when a selected ID was never stored (nothing is changed then).
-int32_t oracle_pool_stage(void* pool, const int32_t* sel, int32_t n, int32_t* phys,
+int32_t oracle_pool_stage(void* pool, const int32_t* sel, int32_t n, const float* importance, int32_t* phys,
                           int32_t* miss_logical, int32_t* miss_slot, int32_t* n_miss) {
     auto* p = static_cast<OracleSwapLayerState*>(pool);
     for (int32_t i = 0; i < n; ++i)
@@ -364,6 +389,27 @@ int32_t oracle_pool_stage(void* pool, const int32_t* sel, int32_t n, int32_t* ph
         for (int32_t i = 0; i < n; ++i) phys[p->window + i] = p->window + sel[i];
         return ST_OK;
     }
+    // eviction order of this step's candidates (resident and not selected)
+    std::set<int32_t> selected(sel, sel + n);
+    std::vector<int> cand;                      // slots, least recently used first
+    for (auto it = p->slot_lru.rbegin(); it != p->slot_lru.rend(); ++it)
+        if (!selected.count(p->gpu_slot_logical[*it])) cand.push_back(*it);
+    std::vector<int> evict_order(cand.size());
+    std::iota(evict_order.begin(), evict_order.end(), 0);   // indices into cand = recency ranks
+    if (p->recency_weight < 100) {
+        std::vector<int> by_imp(cand.size());
+        std::iota(by_imp.begin(), by_imp.end(), 0);
+        std::stable_sort(by_imp.begin(), by_imp.end(), [&](int x, int y) {
+            return importance[p->gpu_slot_logical[cand[x]]] < importance[p->gpu_slot_logical[cand[y]]];
+        });
+        std::vector<int64_t> prio(cand.size());
+        for (size_t c = 0; c < by_imp.size(); ++c) {
+            const int a = by_imp[c];
+            prio[a] = (int64_t)p->recency_weight * a + (int64_t)(100 - p->recency_weight) * (int64_t)c;
+        }
+        std::stable_sort(evict_order.begin(), evict_order.end(), [&](int x, int y) { return prio[x] < prio[y]; });
+    }
+    size_t next_victim = 0;
     std::vector<int32_t> missed;
     for (int32_t i = 0; i < n; ++i) {           // hits, ascending
         auto it = p->slot_by_logical.find(sel[i]);
@@ -381,8 +427,8 @@ int32_t oracle_pool_stage(void* pool, const int32_t* sel, int32_t n, int32_t* ph
         for (int s = 0; s < p->capacity; ++s)
             if (p->gpu_slot_logical[s] < 0) { slot = s; break; }
         if (slot < 0) {
-            slot = p->slot_lru.back();
-            p->slot_lru.pop_back();
+            slot = cand[evict_order[next_victim++]];
+            p->slot_lru.remove(slot);
             p->slot_by_logical.erase(p->gpu_slot_logical[slot]);
         }
         p->gpu_slot_logical[slot] = l;
@@ -393,6 +439,16 @@ int32_t oracle_pool_stage(void* pool, const int32_t* sel, int32_t n, int32_t* ph
         miss_logical[*n_miss] = l;
         miss_slot[*n_miss] = slot;
         (*n_miss)++;
+    }
+    // the high-water mark: free slots for the next step's misses
+    if (p->high_water < 100) {
+        const int64_t limit = std::max<int64_t>((int64_t)p->high_water * p->capacity / 100, n);
+        while ((int64_t)p->slot_lru.size() > limit && next_victim < cand.size()) {
+            const int slot = cand[evict_order[next_victim++]];
+            p->slot_lru.remove(slot);
+            p->slot_by_logical.erase(p->gpu_slot_logical[slot]);
+            p->gpu_slot_logical[slot] = -1;
+        }
     }
     for (int32_t i = 0; i < n; ++i) phys[p->window + i] = p->window + p->slot_by_logical[sel[i]];
     return ST_OK;

@@ -272,3 +272,20 @@ def test_periodic_indexer_sync(period):
         torch.cuda.synchronize()
         check_step(t, wl, dw, want, check_sel=predict)
     check_pools(wl, dw, ref)
+
+
+def test_decode_weighted_replacement():
+    """KVSwap §3.2 reading in the decode step: the ratio-4 layer (1024 slots, top
+    512) evicts by recency and importance (the step's scores) and keeps 70 % of
+    its slots in use; every step and the slot tables equal the oracle's."""
+    wl = L.WORKLOADS["ens_8k_wr"]
+    dw = DeviceWorkload(wl, keep_host=True)
+    dw.make_steps(10)
+    ref = oracle.DecodeState(wl, dw.windows, dw.stores)
+    for t in range(10):
+        want = ref.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t])
+        dw.step(t)
+        torch.cuda.synchronize()
+        check_step(t, wl, dw, want)
+        check_pools(wl, dw, ref)
+    assert dw.pools[0].stats()["hits"] > 0

@@ -79,22 +79,53 @@ def test_attend_kv_matches_oracle(ctx, heads, dh, dtype):
             assert err <= TOL, f"segment {s} head {h}: rel err {err}"
 
 
+def run_threads(fn, n):
+    """fn(i) for i < n on n threads (the oracle's ctypes calls release the GIL)."""
+    import threading
+    errs = []
+
+    def body(i):
+        try:
+            fn(i)
+        except BaseException as e:
+            errs.append(e)
+    ths = [threading.Thread(target=body, args=(i,)) for i in range(n)]
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    if errs:
+        raise errs[0]
+
+
 def run_kvswap(wl, steps, segs=None):
     say(f"kvswap {wl.name}: {steps} steps, n_seg={wl.n_seg}, T={wl.ctx}, k={wl.k}, slots={wl.slots}")
     dw = DeviceKVSwap(wl, log=say)
     dw.make_steps(steps)
-    segs = list(range(wl.n_seg)) if segs is None else segs
+    segs = list(range(wl.n_seg)) if segs is None else sorted(segs)
     ref = oracle.KVSwapState(wl, segs)
-    inputs = {s: dw.host_inputs(s, 0) for s in segs}
+    inputs = {}
+
+    def load(i):
+        inputs[segs[i]] = dw.host_inputs(segs[i], 0)
+    run_threads(load, len(segs))
     misses = {s: 0 for s in segs}
+    hits = {s: 0 for s in segs}
+    T_threads = 16
     for t in range(steps):
         dw.step(t)
         torch.cuda.synchronize()
         sc, sel, cnt = dw.scores.cpu().numpy(), dw.sel.cpu().numpy(), dw.count.cpu().numpy()
         phys, nrows, out = dw.phys.cpu().numpy(), dw.n_rows.cpu().numpy(), dw.out.cpu().numpy()
+        wants = {}
+
+        def one(i):
+            for s in segs[i::T_threads]:
+                U, S, V, _, cold = inputs[s]
+                wants[s] = ref.step(s, U, S, V, dw.q_np[t, s], cold)
+        run_threads(one, min(T_threads, len(segs)))
         for s in segs:
-            U, S, V, _, cold = inputs[s]
-            want = ref.step(s, U, S, V, dw.q_np[t, s], cold)
+            want = wants[s]
             assert np.array_equal(bits(sc[s]), bits(want["score"])), f"step {t} seg {s}: scores"
             n = want["sel"].size
             assert cnt[s] == n and np.array_equal(sel[s, :n], want["sel"]), f"step {t} seg {s}: selection"
@@ -102,21 +133,59 @@ def run_kvswap(wl, steps, segs=None):
             err = rel_err_rows(out[s], want["out"])
             assert err <= TOL, f"step {t} seg {s}: rel err {err}"
             misses[s] += len(want["misses"])
-        say(f"  step {t} ok")
+            hits[s] += n - len(want["misses"])
+        say(f"  step {t} ok ({len(segs)} segments)")
     B = wl.batch
+    full = 0
     for p, pool in enumerate(dw.pools):
-        st = pool.stats()
         covered = [s for s in range(p * B, (p + 1) * B) if s in misses]
         if len(covered) == B:
+            st = pool.stats()
             assert st["misses"] == sum(misses[s] for s in covered), f"pool {p} misses"
-    return dw
+            assert st["hits"] == sum(hits[s] for s in covered), f"pool {p} hits"
+            full += 1
+    return dw, full
 
 
 def test_kvswap_small_all_segments():
-    run_kvswap(L.KVSWAP_WORKLOADS["kvswap_small"], 6)
+    _, full = run_kvswap(L.KVSWAP_WORKLOADS["kvswap_small"], 6)
+    assert full == L.KVSWAP_WORKLOADS["kvswap_small"].n_pools
 
 
 def test_kvswap_32k_full_size_sampled_segments():
+    """The pages' shape (4096 segments, one stage launch over 256 pools): 16
+    segments spread over layers, groups and sequences, plus every sequence of
+    pool 171 (layer 21, group 3), whose counters are then compared too; 4 steps."""
     wl = L.KVSWAP_WORKLOADS["kvswap_32k"]
-    segs = [0, 1, wl.seg(13, 5, 7), wl.n_seg - 1]
-    run_kvswap(wl, 2, segs)
+    spread = []
+    i = 0
+    while len(spread) < 16:
+        s_ = wl.seg((i * 7 + 3) % wl.layers, (i * 3 + 1) % wl.groups, (i * 5 + 2) % wl.batch)
+        if s_ not in spread:
+            spread.append(s_)
+        i += 1
+    pool = 21 * wl.groups + 3
+    segs = sorted(set(spread) | set(range(pool * wl.batch, (pool + 1) * wl.batch)))
+    assert max(s // wl.batch for s in spread) > 16
+    _, full = run_kvswap(wl, 4, segs)
+    assert full >= 1
+
+
+def test_kvswap_small_weighted_all_segments():
+    """KVSwap §3.2 rolling buffer: 400 slots, top 200 per step, replacement by
+    recency and importance (the step's low-rank scores) and a 70 % high-water
+    mark; every segment, slot rows and counters equal the oracle's."""
+    wl = L.KVSWAP_WORKLOADS["kvswap_small_wr"]
+    dw, full = run_kvswap(wl, 6)
+    assert full == wl.n_pools
+    for p in dw.pools:
+        assert p.stats()["hits"] > 0
+
+
+def test_kvswap_32k_weighted_sampled_segments():
+    wl = L.KVSWAP_WORKLOADS["kvswap_32k_wr"]
+    pool = 9 * wl.groups + 6
+    segs = sorted({wl.seg((i * 11 + 2) % wl.layers, (i * 5 + 3) % wl.groups, (i * 7) % wl.batch) for i in range(16)}
+                  | set(range(pool * wl.batch, (pool + 1) * wl.batch)))
+    _, full = run_kvswap(wl, 3, segs)
+    assert full >= 1

@@ -257,3 +257,24 @@ def test_lookahead_periodic_indexer(period):
 def test_store_while_decoding_lookahead():
     from test_gpu_decode import growing_run
     growing_run("lookahead")
+
+
+def test_lookahead_weighted_replacement():
+    """The rolling-buffer replacement in the lookahead schedule (the stage of step
+    t+1 reads the scores that predict it): rows and outputs equal the oracle's."""
+    wl = L.WORKLOADS["ens_8k_wr"]
+    dw = DeviceWorkload(wl, keep_host=True)
+    dw.make_steps(8)
+    ref = oracle.DecodeState(wl, dw.windows, dw.stores)
+    dw.lookahead_prime(0)
+    for t in range(6):
+        want = ref.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t])
+        cur = lsa.lookahead_buffer(dw.ctx)
+        dw.lookahead_step(t)
+        torch.cuda.synchronize()
+        phys, nrows, out = dw.phys2[cur].cpu().numpy(), dw.n_rows2[cur].cpu().numpy(), dw.out.cpu().numpy()
+        for l in range(wl.n_layers):
+            n = wl.window + want["layer_sel"][l][0].size
+            assert nrows[l, 0] == n and np.array_equal(phys[l, 0, :n], want["phys"][l][0]), f"step {t} layer {l}"
+            err = rel_err_rows(out[l, 0], want["out"][l][0])
+            assert err <= RTOL[wl.kv_dtype], f"step {t} layer {l}: rel err {err}"

@@ -199,3 +199,66 @@ def test_topk_reduction_override():
     assert e.value.status == 2
     pool = lsa.Pool(64, 4, kv, W, 8, 64, 128, 1, allow_topk_reduction=True)
     assert pool.swap and pool.cap == 16
+
+
+@pytest.mark.parametrize("w,h,cold", [(50, 100, "hbm"), (0, 100, "host"), (100, 70, "hbm"), (50, 70, "host"),
+                                      (20, 40, "hbm")])
+def test_weighted_replacement_matches_oracle(w, h, cold):
+    """KVSwap §3.2 reading: eviction order weighing recency against the step's
+    importance scores, and the high-water mark; slot tables, LRU order, rows and
+    counters equal the oracle's after every step, then a shrink of the capacity
+    (free slots in the middle of the range) equals the oracle's too."""
+    say(f"weighted replacement w={w} h={h} cold={cold}")
+    rng = np.random.default_rng(w * 13 + h + (cold == "host"))
+    B, S, k, D, ctx_len = 2, 64, 40, 128, 4096
+    pool, kv = make_pool(ctx_len, 4, S, k, B, cold, D)
+    pool.set_replacement(w, h)
+    stores, refs = [], []
+    for b in range(B):
+        rows = L.grid_uniform(rng, (pool.cap, D))
+        pool.store(b, 0, rows)
+        stores.append(rows)
+        r = oracle.Pool(pool.cap, S, W, D * 4)
+        r.store(0, pool.cap)
+        r.set_replacement(w, h)
+        refs.append(r)
+    seqs = [selections(rng, pool.cap, k, 24, overlap=0.6) for _ in range(B)]
+    sel = torch.zeros((B, k), dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    phys = torch.zeros((B, W + k), dtype=torch.int32, device=DEV)
+    nrows = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    imp = torch.zeros((B, pool.cap), dtype=torch.float32, device=DEV)
+    for t in range(24):
+        sel_np = np.full((B, k), -1, np.int32)
+        imp_np = (rng.integers(0, 9, size=(B, pool.cap)) / 8).astype(np.float32)   # many ties
+        for b in range(B):
+            sel_np[b, :seqs[b][t].size] = seqs[b][t]
+        sel.copy_(torch.from_numpy(sel_np))
+        cnt.copy_(torch.tensor([seqs[b][t].size for b in range(B)], dtype=torch.int32))
+        imp.copy_(torch.from_numpy(imp_np))
+        lsa.stage(pool, sel, cnt, 4, phys, nrows, importance=imp if w < 100 else None)
+        torch.cuda.synchronize()
+        ph = phys.cpu().numpy()
+        kvh = kv.cpu().numpy()
+        for b in range(B):
+            st, want_phys, _ = refs[b].stage(seqs[b][t], imp_np[b])
+            assert st == 0
+            assert np.array_equal(ph[b, :W + seqs[b][t].size], want_phys), f"step {t} seq {b}: rows"
+            sl, lru = pool.state(b)
+            rsl, rlru = refs[b].state()
+            assert np.array_equal(sl, rsl) and np.array_equal(lru, rlru), f"step {t} seq {b}: slot table"
+            assert np.array_equal(kvh[b, want_phys[W:]], stores[b][seqs[b][t]])
+    st = pool.stats()
+    assert st["misses"] == sum(r.stats()["misses"] for r in refs)
+    assert st["hits"] == sum(r.stats()["hits"] for r in refs)
+    # shrink below the used count: the oracle's reading, with free slots in the middle
+    pool.set_capacity(k)
+    torch.cuda.synchronize()
+    kvh = kv.cpu().numpy()
+    for b in range(B):
+        refs[b].set_capacity(k)
+        sl, lru = pool.state(b)
+        rsl, rlru = refs[b].state()
+        assert np.array_equal(sl, rsl) and np.array_equal(lru, rlru), f"shrink seq {b}"
+        for slot in np.nonzero(rsl >= 0)[0]:
+            assert np.array_equal(kvh[b, W + slot], stores[b][rsl[slot]]), f"shrink seq {b} slot {slot}: row"

@@ -6,6 +6,7 @@ import pytest
 
 import oracle
 
+
 W = 128
 
 
@@ -248,3 +249,108 @@ def test_adapt_policy_decisions():
         pool.stage(np.arange(200 + 16 * _, 216 + 16 * _, dtype=np.int32))
         pool.adapt(0.5, 10e6, 0.1, 32, 16, 64, 1)
     assert pool.capacity() == 64                          # ceiling
+
+
+class WeightedTimestampLRU:
+    """An independent model of the [P4] §3.2 reading: recency from last-use
+    stamps; the step's candidates (resident, not selected) ranked by recency a and
+    importance c, evicted in ascending w*a + (100-w)*c (ties: less recent first);
+    misses take the lowest free slot below the capacity first; then the
+    high-water mark frees slots down to max(h*C/100, |sel|)."""
+
+    def __init__(self, S, C=None):
+        self.S, self.C = S, S if C is None else C
+        self.owner = [None] * S
+        self.stamp = [0] * S
+        self.clock = 0
+
+    def step(self, sel, imp, w, h):
+        chosen = set(sel)
+        cand = sorted((s for s in range(self.S) if self.owner[s] is not None and self.owner[s] not in chosen),
+                      key=lambda s: self.stamp[s])
+        a = {s: i for i, s in enumerate(cand)}
+        c = {s: i for i, s in enumerate(sorted(cand, key=lambda s: (imp[self.owner[s]], a[s])))}
+        order = sorted(cand, key=lambda s: (w * a[s] + (100 - w) * c[s], a[s]))
+        slot_of = {l: s for s, l in enumerate(self.owner) if l is not None}
+        for l in sel:
+            if l in slot_of:
+                self.clock += 1
+                self.stamp[slot_of[l]] = self.clock
+        nxt = 0
+        moved = []
+        for l in sel:
+            if l in slot_of:
+                continue
+            free = [s for s in range(self.C) if self.owner[s] is None]
+            if free:
+                s = free[0]
+            else:
+                s = order[nxt]
+                nxt += 1
+            self.owner[s] = l
+            self.clock += 1
+            self.stamp[s] = self.clock
+            moved.append((l, s))
+        limit = max(h * self.C // 100, len(sel))
+        while sum(o is not None for o in self.owner) > limit and nxt < len(order):
+            self.owner[order[nxt]] = None
+            nxt += 1
+        slot_of = {l: s for s, l in enumerate(self.owner) if l is not None}
+        lru = sorted(slot_of.values(), key=lambda s: -self.stamp[s])
+        return [W + slot_of[l] for l in sel], moved, lru
+
+
+@pytest.mark.parametrize("w,h", [(100, 100), (50, 100), (0, 100), (100, 70), (50, 70), (20, 40)])
+def test_weighted_replacement_matches_independent_model(w, h):
+    rng = np.random.default_rng(w * 7 + h)
+    for run in range(4):
+        cap, S = int(rng.integers(30, 120)), int(rng.integers(6, 20))
+        pool = oracle.Pool(cap, S, W, 2048)
+        pool.store(0, cap)
+        pool.set_replacement(w, h)
+        ref = WeightedTimestampLRU(S)
+        for sel in random_selections(rng, cap, S, 25, overlap=0.6):
+            imp = L_grid(rng, cap)
+            st, phys, moved = pool.stage(np.array(sel, np.int32), imp)
+            want_phys, want_moved, want_lru = ref.step(sel, imp, w, h)
+            assert st == 0
+            assert phys[W:].tolist() == want_phys, (run, sel)
+            assert moved == want_moved
+            sl, lru = pool.state()
+            assert lru.tolist() == want_lru
+            assert sl.tolist() == [o if o is not None else -1 for o in ref.owner]
+
+
+def L_grid(rng, n):
+    """Importance scores with many ties (1/8 grid in [0, 1])."""
+    return (rng.integers(0, 9, size=n) / 8).astype(np.float32)
+
+
+def test_importance_only_evicts_the_least_important():
+    """w = 0: the evicted entries are the candidates of lowest importance (ties to
+    the less recent), whatever their recency."""
+    pool = oracle.Pool(100, 4, W, 8)
+    pool.store(0, 100)
+    pool.set_replacement(0, 100)
+    imp = np.zeros(100, np.float32)
+    imp[[10, 11, 12, 13]] = [0.9, 0.1, 0.5, 0.3]
+    pool.stage(np.array([10, 11, 12, 13], np.int32), imp)     # fills slots 0..3
+    # touch 11 last so that it is the most recent, yet the least important
+    pool.stage(np.array([11], np.int32), imp)
+    st, phys, moved = pool.stage(np.array([50, 51], np.int32), imp)
+    assert st == 0 and moved == [(50, 1), (51, 3)]             # 11 (0.1) then 13 (0.3) leave
+
+
+def test_high_water_keeps_room_for_the_next_misses():
+    """h = 50 with 8 slots: after every step at most max(4, |sel|) slots are in
+    use, and every selected entry is resident."""
+    pool = oracle.Pool(1000, 8, W, 8)
+    pool.store(0, 1000)
+    pool.set_replacement(100, 50)
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        sel = np.sort(rng.choice(1000, size=int(rng.integers(1, 7)), replace=False)).astype(np.int32)
+        st, _, _ = pool.stage(sel)
+        sl, lru = pool.state()
+        assert st == 0 and len(lru) <= max(4, sel.size)
+        assert set(sel.tolist()) <= set(sl.tolist())
