@@ -77,7 +77,7 @@ def test_decode_forced_swap_tiny():
 
 
 def test_decode_256k_threshold_full_size():
-    run_decode(L.WORKLOADS["thresh_256k"], 2)
+    run_decode(L.WORKLOADS["thresh_256k"], 8)
 
 
 def test_decode_1m_host_swap_full_size():
