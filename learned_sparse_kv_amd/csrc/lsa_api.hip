@@ -1071,17 +1071,19 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
     const size_t ws_total = off_nmiss + nmiss_bytes;
     char* ws;
     void* zero;
+    // zero region: the select's histogram
+    const size_t zero_need = align_up(sel_zero, 256);
     if (fixed) {
-        const size_t zero_al = align_up(sel_zero, 256);
+        const size_t zero_al = zero_need;
         if (zero_al + ws_total > fixed_bytes)
             return fail(LSA_ERR_UNSUPPORTED, "the step needs %zu bytes of scratch; the static scratch holds %zu",
                         zero_al + ws_total, fixed_bytes);
         zero = fixed;
         ws = fixed + zero_al;
         P->zero_clear = reinterpret_cast<uint32_t*>(fixed);
-        P->zero_clear_words = sel_zero / 4;
+        P->zero_clear_words = zero_need / 4;
     } else {
-        st = zero_ensure(ctx, sel_zero);
+        st = zero_ensure(ctx, zero_need);
         if (st != LSA_OK) return st;
         st = ws_ensure(ctx, ws_total);
         if (st != LSA_OK) return st;
