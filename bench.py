@@ -319,6 +319,10 @@ def main():
     # bf16 rows), both schedules launched eagerly, K steps each
     ctx256 = other_context("thresh_256k", K, Wm, parity_steps=0 if args.no_cpu_baseline else 2) \
         if wl.name.startswith("swap_1m") else None
+    # the pages' whole sparse-layer stack at 1M: 41 layers (20 ratio-4, 21 ratio-128)
+    # on one selection per step, 11.1 GB of pinned-host cold pools
+    stack41 = other_context("stack_1m_41", min(K, 64), min(Wm, 16), parity_steps=0 if args.no_cpu_baseline else 1) \
+        if wl.name == "swap_1m" else None
     kvs = kvswap_measure(L.KVSWAP_WORKLOADS["kvswap_32k"], min(K, 32), min(Wm, 8),
                          parity_steps=0 if args.no_cpu_baseline else 2) \
         if wl.name.startswith("swap_1m") and not args.no_kvswap else None
@@ -448,6 +452,7 @@ def main():
         "project": proj,
         "adaptive_capacity": adaptive,
         "ctx_256k": ctx256,
+        "stack_41_layers": stack41,
         "kvswap_32k": kvs,
         "kvswap_32k_wr": kvs_wr,
         "periodic_indexer": {"schedule": "lookahead, eager; one prediction per window of `period` steps "
@@ -520,8 +525,8 @@ def other_context(name, K, Wm, parity_steps=0):
         tol = 1e-5 if wl.kv_dtype == "f32" else 2e-2
         res["parity"] = {"steps": parity_steps, "selected_sets_identical": ok, "max_rel_err": err,
                          "tolerance": tol, "pass": bool(ok and err <= tol),
-                         "note": "both sides read the same bf16 rows and accumulate in fp32 / double; the "
-                                 "tolerance is the bf16 storage bound, max_rel_err the observed difference"}
+                         "note": f"both sides read the same {wl.kv_dtype} rows and accumulate in fp32 / double; "
+                                 "max_rel_err is the observed difference"}
         log(f"{name} parity over {parity_steps} steps: sets {ok}, max rel err {err:.3g}")
     del dw
     torch.cuda.empty_cache()

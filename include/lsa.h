@@ -47,7 +47,7 @@ extern "C" {
 #endif
 
 #define LSA_ABI_VERSION 6
-#define LSA_MAX_LAYERS 16
+#define LSA_MAX_LAYERS 64
 #define LSA_MAX_BATCH 64
 
 typedef enum lsa_status {
@@ -396,7 +396,8 @@ typedef struct lsa_step_desc {
     int32_t* sel;               /* device i32 [batch][k] */
     int32_t* count;             /* device i32 [batch] */
     /* sparse layers */
-    int32_t n_layers;           /* 1..LSA_MAX_LAYERS */
+    int32_t n_layers;           /* 1..LSA_MAX_LAYERS ([P1]: 41 sparse layers share one selection);
+                                   the lookahead schedule needs n_layers * batch <= 1024 */
     lsa_pool* const* pools;     /* host [n_layers] */
     const float* q_attn;        /* device f32 [n_layers][batch][hq][kv_dim] */
     float* out;                 /* device f32 [n_layers][batch][hq][kv_dim] */
@@ -447,10 +448,10 @@ lsa_status lsa_decode_attend(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream
  *   lsa_lookahead_step(ctx, d, s): for the current step, copy its missed rows
  *     into their slots and attend d->q_attn over its staged rows (writing
  *     d->out); for the NEXT step, score d->q_idx / d->w_idx (the indexer query
- *     that predicts it), select and stage.  Five launches on s, each pairing
- *     independent work of the two steps (row copy with the key scan, attention
- *     with the selection histogram, attention combine with the selection's
- *     candidate pass), then the select's last pass and the stage.
+ *     that predicts it), select and stage.  Four launches on s: the row copy
+ *     beside the key scan (and the selection histogram), the selection's
+ *     candidate pass, the attention splits beside the selection's final pass,
+ *     the attention merge beside the stage.
  * The outputs equal lsa_decode_step's when step t's call carries the indexer
  * query of step t+1: every kernel body is the same, and the stage of step t+1
  * runs after step t's attention has finished.

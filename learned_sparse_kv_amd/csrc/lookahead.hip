@@ -5,12 +5,12 @@
 // limitations / future work: the reference scores synchronously, and
 // overlapping the global scoring is listed as the way to remove that cost.
 //
-// One lookahead step t runs on a single stream as five launches:
+// One lookahead step t runs on a single stream as four launches:
 //   A  fm_score of step t+1, each workgroup with one extra wave that copies a
 //      share of step t's missed rows into their slots (the score waves also
 //      build the select's histogram)
-//   B  select histogram of step t+1 (only when A cannot: segments that are
-//      not one per sequence, or fewer score workgroups than sequences)
+//   (B select histogram of step t+1, only when A cannot: segments that are not
+//      one per sequence, or fewer score workgroups than sequences)
 //   C  select collect of step t+1
 //   D  [attention splits of step t                    | final select of step t+1]
 //   E  [stage of step t+1 (LRU; records its misses)   | split merge of step t]
@@ -39,15 +39,6 @@ struct Split {
     int n0;        // blocks of the first body
     int x, y;      // its grid (x fastest), z = n0 / (x * y)
     int x2;        // second body's x extent (y = rest)
-};
-
-// The missed rows a deferring stage listed for the step, as the copy wave reads
-// them: the lists and counts of every (layer, sequence) segment lie back to
-// back, segment s = layer * batch + b.
-struct CopyArgs {
-    const uint64_t* miss;     // [n_seg][phys_stride][2]: cold row address, slot row address
-    const int32_t* n_miss;    // [n_seg]
-    int32_t n_seg, phys_stride, row_bytes;
 };
 
 typedef __attribute__((address_space(1))) u32x4 global_u32x4;
@@ -101,7 +92,7 @@ __device__ inline void copy_wave(const CopyArgs& ca, const int wg, const int n_w
             // last segment starting at or before m: a fixed-step binary search
             int lo = 0;
 #pragma clang loop unroll(full)
-            for (int step = LSA_MAX_LAYERS * LSA_MAX_BATCH / 2; step > 0; step >>= 1)
+            for (int step = kCopyMaxSegs / 2; step > 0; step >>= 1)
                 if (lo + step < ca.n_seg && s_pre[lo + step] <= m) lo += step;
             const uint64_t* e = ca.miss + ((int64_t)lo * ca.phys_stride + (m - s_pre[lo])) * 2;
             const uint64_t off = (uint64_t)(c & cpr_mask) * 16u;
@@ -133,7 +124,7 @@ struct HistArgs {
 // usually ends later, so the flush costs no time).
 template <int DK, typename KT, bool HIST>
 __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, const CopyArgs ca, const HistArgs ha) {
-    __shared__ int s_pre[LSA_MAX_LAYERS * LSA_MAX_BATCH];
+    __shared__ int s_pre[kCopyMaxSegs];
     __shared__ uint32_t s_hist[HIST ? kSelBins : 1];
     __shared__ int s_done;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -175,9 +166,10 @@ constexpr int kFinMaxBlocks = 1024;   // collect blocks per segment (1M entries)
 
 template <int D, typename KT>
 __global__ __launch_bounds__(512, 1) void la_final_split(const AttendArgs aa, const SelectArgs se, const Split sp) {
+    __shared__ __attribute__((aligned(16))) char tile[attend_k::tile_bytes<D, KT>()];
     const int b = blockIdx.x;
     if (b < sp.n0) {
-        attend_k::attend_split_body<D, KT>(aa, b % sp.x, (b / sp.x) % sp.y, b / (sp.x * sp.y));
+        attend_k::attend_split_body<D, KT>(aa, b % sp.x, (b / sp.x) % sp.y, b / (sp.x * sp.y), tile);
         return;
     }
     select_k::sel_final_body<512, kFinMaxBlocks>(se, b - sp.n0);
@@ -258,22 +250,12 @@ hipError_t launch_e(const StageArgs& ga, const AttendArgs& aa, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
-                                 int n_cu, const SelectArgs* hist_for, bool copy, hipStream_t s) {
-    // the copy reads the stage's miss lists through one base pointer: they must
-    // lie back to back over (layer, sequence), with one row size
-    const StageLayer& L0 = ga.L[0];
-    if (!L0.miss || !L0.n_miss || ga.n_layers < 1 || ga.batch < 1) return hipErrorInvalidValue;
-    for (int l = 0; l < ga.n_layers; ++l) {
-        const StageLayer& L = ga.L[l];
-        if (L.miss != L0.miss + (size_t)l * ga.batch * phys_stride * 2 || L.n_miss != L0.n_miss + (size_t)l * ga.batch ||
-            L.row_bytes != L0.row_bytes || L.phys_stride != phys_stride)
-            return hipErrorInvalidValue;
-    }
-    const int cpr = L0.row_bytes / 16;
-    if (L0.row_bytes % 16 != 0 || cpr < 1 || (cpr & (cpr - 1)) != 0) return hipErrorInvalidValue;
-    // no segments: the copy waves find nothing to copy
-    const CopyArgs ca{L0.miss, L0.n_miss, copy ? ga.n_layers * ga.batch : 0, phys_stride, L0.row_bytes};
+hipError_t launch_la_fetch_score(const ScoreArgs& sa, const CopyArgs& ca, int key_dtype, int dk, int n_cu,
+                                 const SelectArgs* hist_for, hipStream_t s) {
+    const int cpr = ca.row_bytes / 16;
+    if (ca.n_seg < 0 || ca.n_seg > kCopyMaxSegs || (ca.n_seg && (!ca.miss || !ca.n_miss)) || ca.row_bytes % 16 != 0 ||
+        cpr < 1 || (cpr & (cpr - 1)) != 0)
+        return hipErrorInvalidValue;
     HistArgs ha{nullptr, 0, 0.0f};
     if (hist_for) {
         if (!la_fused_hist(sa, *hist_for, n_cu)) return hipErrorInvalidValue;

@@ -998,9 +998,15 @@ struct StepPlan {
     size_t zero_clear_words = 0;
     ScoreArgs sa;
     SelectArgs se;
-    StageArgs ga;           // per layer; phys / n_rows / src point at buffer 0
-    AttendArgs aa;
+    // the layers in groups of kLaunchLayers, one stage / attention launch each;
+    // phys / n_rows / src point at buffer 0
+    static constexpr int kMaxGroups = (LSA_MAX_LAYERS + kLaunchLayers - 1) / kLaunchLayers;
+    StageArgs ga[kMaxGroups];
+    AttendArgs aa[kMaxGroups];
+    int n_groups = 0;
     int B = 0, D = 0, W = 0, L = 0, k_eff = 0, phys_stride = 0;
+    StageLayer& stage(int l) { return ga[l / kLaunchLayers].L[l % kLaunchLayers]; }
+    AttendLayer& attend(int l) { return aa[l / kLaunchLayers].L[l % kLaunchLayers]; }
     int32_t* phys = nullptr;     // [n_buf][L][B][phys_stride]
     int32_t* n_rows = nullptr;   // [n_buf][L][B]
     int32_t* srcs = nullptr;     // [n_buf][L][B][phys_stride]
@@ -1103,33 +1109,67 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
     P->k_eff = k_eff;
     P->phys_stride = phys_stride;
 
-    memset(&P->ga, 0, sizeof(P->ga));
-    P->ga.n_layers = L;
-    P->ga.batch = B;
-    for (int b = 0; b < B; ++b) P->ga.src_valid[b] = P->sa.n_valid[b];
-    memset(&P->aa, 0, sizeof(P->aa));
-    P->aa.n_layers = L;
-    P->aa.batch = B;
-    P->aa.hq = d->hq;
-    P->aa.D = D;
-    P->aa.dtype = dt;
-    P->aa.max_splits = (phys_stride + kAttendRows - 1) / kAttendRows;
-    P->aa.scale = d->scale;
-    P->aa.part_acc = reinterpret_cast<float*>(ws + off_att);
-    P->aa.part_ml = P->aa.part_acc + (size_t)L * B * P->aa.max_splits * 16 * D;
+    P->n_groups = (L + kLaunchLayers - 1) / kLaunchLayers;
+    const int max_splits = (phys_stride + kAttendRows - 1) / kAttendRows;
+    float* acc_base = reinterpret_cast<float*>(ws + off_att);
+    float* ml_base = acc_base + (size_t)L * B * max_splits * 16 * D;
+    for (int g = 0; g < P->n_groups; ++g) {
+        const int l0 = g * kLaunchLayers;
+        const int nl = std::min(kLaunchLayers, L - l0);
+        StageArgs& ga = P->ga[g];
+        memset(&ga, 0, sizeof(ga));
+        ga.n_layers = nl;
+        ga.batch = B;
+        for (int b = 0; b < B; ++b) ga.src_valid[b] = P->sa.n_valid[b];
+        AttendArgs& aa = P->aa[g];
+        memset(&aa, 0, sizeof(aa));
+        aa.n_layers = nl;
+        aa.batch = B;
+        aa.hq = d->hq;
+        aa.D = D;
+        aa.dtype = dt;
+        aa.max_splits = max_splits;
+        aa.scale = d->scale;
+        aa.part_acc = acc_base + (size_t)l0 * B * max_splits * 16 * D;
+        aa.part_ml = ml_base + (size_t)l0 * B * max_splits * 32;
+    }
     for (int l = 0; l < L; ++l) {
         const lsa_pool* p = d->pools[l];
         int32_t* ph = P->phys + (size_t)l * B * phys_stride;
         int32_t* nr = P->n_rows + (size_t)l * B;
         int32_t* sr = P->srcs + (size_t)l * B * phys_stride;
-        P->ga.L[l] = stage_layer(p, d->sel, d->count, d->k, d->src_ratio, ph, phys_stride, nr, d->scores, d->n_keys);
-        P->ga.L[l].defer_copy = 1;
-        P->ga.L[l].src = sr;
-        P->ga.L[l].miss = P->miss + (size_t)l * B * phys_stride * 2;
-        P->ga.L[l].n_miss = P->n_miss + (size_t)l * B;
-        P->aa.L[l] = AttendLayer{d->q_attn + (size_t)l * B * d->hq * D, p->d.kv_buf, ph, nr,
-                                 d->out + (size_t)l * B * d->hq * D, p->d.kv_stride_b, p->rows_per_seq, phys_stride,
-                                 nullptr, p->d.kv_buf, p->cold_dev, p->cold_stride_b, p->cap};
+        StageLayer& sl = P->stage(l);
+        sl = stage_layer(p, d->sel, d->count, d->k, d->src_ratio, ph, phys_stride, nr, d->scores, d->n_keys);
+        sl.defer_copy = 1;
+        sl.src = sr;
+        sl.miss = P->miss + (size_t)l * B * phys_stride * 2;
+        sl.n_miss = P->n_miss + (size_t)l * B;
+        P->attend(l) = AttendLayer{d->q_attn + (size_t)l * B * d->hq * D, p->d.kv_buf, ph, nr,
+                                   d->out + (size_t)l * B * d->hq * D, p->d.kv_stride_b, p->rows_per_seq, phys_stride,
+                                   nullptr, p->d.kv_buf, p->cold_dev, p->cold_stride_b, p->cap};
+    }
+    return LSA_OK;
+}
+
+// The missed rows of row-list buffer `buf` as the lookahead copy reads them
+// (n_seg = 0: nothing to copy).
+CopyArgs plan_copy(const StepPlan& P, int buf, bool copy) {
+    const size_t per_buf = (size_t)P.L * P.B;
+    return CopyArgs{P.miss + buf * per_buf * P.phys_stride * 2, P.n_miss + buf * per_buf,
+                    copy ? P.L * P.B : 0, P.phys_stride, P.D * (P.aa[0].dtype == LSA_F32 ? 4 : 2)};
+}
+
+// a swapping layer's missed rows are read from the cold pool by the attention,
+// which also fills their slots
+void plan_attention_fetches(StepPlan* P, const lsa_step_desc* d) {
+    for (int l = 0; l < P->L; ++l)
+        if (d->pools[l]->swap) P->attend(l).src = P->stage(l).src;
+}
+
+lsa_status attend_groups(lsa_ctx* ctx, const StepPlan& P, hipStream_t s) {
+    for (int g = 0; g < P.n_groups; ++g) {
+        lsa_status st = attend_timed(ctx, P.aa[g], s);
+        if (st != LSA_OK) return st;
     }
     return LSA_OK;
 }
@@ -1140,13 +1180,14 @@ void plan_use_buffer(StepPlan* P, int buf) {
     for (int l = 0; l < P->L; ++l) {
         int32_t* ph = P->phys + (buf * per_buf + (size_t)l * P->B) * P->phys_stride;
         int32_t* nr = P->n_rows + buf * per_buf + (size_t)l * P->B;
-        P->ga.L[l].phys = ph;
-        P->ga.L[l].n_rows = nr;
-        P->ga.L[l].src = P->srcs + (buf * per_buf + (size_t)l * P->B) * P->phys_stride;
-        P->ga.L[l].miss = P->miss + (buf * per_buf + (size_t)l * P->B) * P->phys_stride * 2;
-        P->ga.L[l].n_miss = P->n_miss + buf * per_buf + (size_t)l * P->B;
-        P->aa.L[l].phys = ph;
-        P->aa.L[l].n_rows = nr;
+        StageLayer& sl = P->stage(l);
+        sl.phys = ph;
+        sl.n_rows = nr;
+        sl.src = P->srcs + (buf * per_buf + (size_t)l * P->B) * P->phys_stride;
+        sl.miss = P->miss + (buf * per_buf + (size_t)l * P->B) * P->phys_stride * 2;
+        sl.n_miss = P->n_miss + buf * per_buf + (size_t)l * P->B;
+        P->attend(l).phys = ph;
+        P->attend(l).n_rows = nr;
     }
 }
 
@@ -1161,15 +1202,17 @@ lsa_status launch_predict(lsa_ctx* ctx, const StepPlan& P, const lsa_step_desc* 
         HIPTRY(launch_fm_select(P.se, s));
         t.end();
     }
-    {
+    for (int g = 0; g < P.n_groups; ++g) {
         Timed t(ctx, LSA_K_STAGE, s);
-        HIPTRY(launch_kv_stage(P.ga, s));
+        HIPTRY(launch_kv_stage(P.ga[g], s));
         t.end();
     }
     if (fetch) {
-        Timed t(ctx, LSA_K_GATHER, s);
-        HIPTRY(launch_fetch_missed(P.ga, P.phys_stride, s));
-        t.end();
+        for (int g = 0; g < P.n_groups; ++g) {
+            Timed t(ctx, LSA_K_GATHER, s);
+            HIPTRY(launch_fetch_missed(P.ga[g], P.phys_stride, s));
+            t.end();
+        }
     }
     return LSA_OK;
 }
@@ -1183,14 +1226,11 @@ lsa_status lsa_decode_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t st
     StepPlan P;
     lsa_status st = step_plan(ctx, d, 1, &P);
     if (st != LSA_OK) return st;
-    // a swapping layer's missed rows are read from the cold pool by the
-    // attention, which also fills their slots
-    for (int l = 0; l < P.L; ++l)
-        if (d->pools[l]->swap) P.aa.L[l].src = P.ga.L[l].src;
+    plan_attention_fetches(&P, d);
     hipStream_t s = (hipStream_t)stream;
     st = launch_predict(ctx, P, d, s, false);
     if (st != LSA_OK) return st;
-    return attend_timed(ctx, P.aa, s);
+    return attend_groups(ctx, P, s);
 }
 
 lsa_status lsa_decode_attend(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
@@ -1198,7 +1238,7 @@ lsa_status lsa_decode_attend(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t 
     lsa_status st = step_plan(ctx, d, 1, &P);
     if (st != LSA_OK) return st;
     // the rows lsa_decode_step staged: its attention already filled the slots
-    return attend_timed(ctx, P.aa, (hipStream_t)stream);
+    return attend_groups(ctx, P, (hipStream_t)stream);
 }
 
 lsa_status lsa_decode_step_noalloc(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
@@ -1213,8 +1253,7 @@ lsa_status lsa_decode_step_noalloc(lsa_ctx* ctx, const lsa_step_desc* d, lsa_str
     StepPlan P;
     lsa_status st = step_plan(ctx, d, 1, &P, static_cast<char*>(ctx->scratch), LSA_STATIC_SCRATCH_BYTES);
     if (st != LSA_OK) return st;
-    for (int l = 0; l < P.L; ++l)
-        if (d->pools[l]->swap) P.aa.L[l].src = P.ga.L[l].src;
+    plan_attention_fetches(&P, d);
     hipStream_t s = (hipStream_t)stream;
     // the select's histogram region must start at zero; the array keeps whatever
     // the previous call on this device left in it
@@ -1226,8 +1265,8 @@ lsa_status lsa_decode_step_noalloc(lsa_ctx* ctx, const lsa_step_desc* d, lsa_str
     }
     HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s));
     HIPTRY(launch_fm_select(P.se, s));
-    HIPTRY(launch_kv_stage(P.ga, s));
-    HIPTRY(launch_lsa_attend(P.aa, s));
+    for (int g = 0; g < P.n_groups; ++g) HIPTRY(launch_kv_stage(P.ga[g], s));
+    for (int g = 0; g < P.n_groups; ++g) HIPTRY(launch_lsa_attend(P.aa[g], s));
     return LSA_OK;
 }
 
@@ -1240,10 +1279,8 @@ lsa_status lsa_lookahead_attend(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream
     plan_use_buffer(&P, ctx->la_cur);
     // the first attention over a prediction's rows reads its missed rows from
     // the cold pools and fills their slots
-    if (!ctx->la_fetched)
-        for (int l = 0; l < P.L; ++l)
-            if (d->pools[l]->swap) P.aa.L[l].src = P.ga.L[l].src;
-    st = attend_timed(ctx, P.aa, (hipStream_t)stream);
+    if (!ctx->la_fetched) plan_attention_fetches(&P, d);
+    st = attend_groups(ctx, P, (hipStream_t)stream);
     if (st != LSA_OK) return st;
     ctx->la_fetched = true;
     return LSA_OK;
@@ -1253,6 +1290,9 @@ lsa_status lsa_lookahead_prime(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_
     StepPlan P;
     lsa_status st = step_plan(ctx, d, 2, &P);
     if (st != LSA_OK) return st;
+    if (P.L * P.B > kCopyMaxSegs)
+        return fail(LSA_ERR_UNSUPPORTED, "the lookahead schedule handles n_layers * batch <= %d (got %d)", kCopyMaxSegs,
+                    P.L * P.B);
     ctx->la_cur = 0;
     ctx->la_fetched = false;
     plan_use_buffer(&P, 0);
@@ -1266,27 +1306,33 @@ lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t
     StepPlan P;
     lsa_status st = step_plan(ctx, d, 2, &P);
     if (st != LSA_OK) return st;
+    if (P.L * P.B > kCopyMaxSegs)
+        return fail(LSA_ERR_UNSUPPORTED, "the lookahead schedule handles n_layers * batch <= %d (got %d)", kCopyMaxSegs,
+                    P.L * P.B);
     const int cur = ctx->la_cur, nxt = cur ^ 1;
     hipStream_t s = (hipStream_t)stream;
     plan_use_buffer(&P, cur);
-    const StageArgs fetch_cur = P.ga;   // the rows step t reads, and its recorded misses
+    // the rows step t reads: its recorded misses are copied by the score launch
+    // (unless an attention of the window already did)
+    const CopyArgs ca = plan_copy(P, cur, !ctx->la_fetched);
     const bool fuse_hist = la_fused_hist(P.sa, P.se, ctx->n_cu);
     {
         Timed t(ctx, LSA_K_SCORE, s);
-        HIPTRY(launch_la_fetch_score(P.sa, fetch_cur, P.phys_stride, d->key_dtype, d->dk, ctx->n_cu,
-                                     fuse_hist ? &P.se : nullptr, !ctx->la_fetched, s));
+        HIPTRY(launch_la_fetch_score(P.sa, ca, d->key_dtype, d->dk, ctx->n_cu, fuse_hist ? &P.se : nullptr, s));
         t.end();
     }
     {
         Timed t(ctx, LSA_K_SELECT, s);
-        HIPTRY(launch_la_select_split(P.aa, P.se, fuse_hist, s));
+        HIPTRY(launch_la_select_split(P.aa[0], P.se, fuse_hist, s));
+        for (int g = 1; g < P.n_groups; ++g) HIPTRY(launch_attend_splits(P.aa[g], s));
         t.end();
     }
-    const AttendArgs attend_cur = P.aa;   // the combine merges step t's splits
+    AttendArgs attend_cur[StepPlan::kMaxGroups];   // the merges of step t's splits
+    for (int g = 0; g < P.n_groups; ++g) attend_cur[g] = P.aa[g];
     plan_use_buffer(&P, nxt);
     {
         Timed t(ctx, LSA_K_STAGE, s);
-        HIPTRY(launch_la_stage_combine(P.ga, attend_cur, s));
+        for (int g = 0; g < P.n_groups; ++g) HIPTRY(launch_la_stage_combine(P.ga[g], attend_cur[g], s));
         t.end();
     }
     ctx->la_cur = nxt;

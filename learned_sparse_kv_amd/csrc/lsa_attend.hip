@@ -57,7 +57,12 @@ __device__ inline void unpack<uint16_t>(const uint4& u, float* out) {
 }
 
 template <int D, typename KT>
-__device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int bx, const int by, const int bz) {
+constexpr int tile_bytes() { return kR * (D * (int)sizeof(KT) + 16); }
+
+// tile: LDS of tile_bytes<D, KT>() bytes, 16-byte aligned, from the caller
+template <int D, typename KT>
+__device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int bx, const int by, const int bz,
+                                                  char* tile) {
     constexpr int RB = D * (int)sizeof(KT);          // row bytes
     constexpr int LS = RB + 16;                      // LDS row stride
     constexpr int CPR = RB / 16;                     // 16-byte chunks per row
@@ -68,7 +73,6 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int
     constexpr int NB = D / 128;                      // 16-wide output blocks per wave in PV
     static_assert(LOADS >= 1 && (kR * CPR) % kThreads == 0, "tile must split evenly");
 
-    __shared__ __attribute__((aligned(16))) char tile[kR * LS];
     __shared__ float sS[4][16][kR];
     __shared__ float sP[16][kR];
     __shared__ int s_ph[kR];
@@ -204,7 +208,8 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int
 
 template <int D, typename KT>
 __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendArgs a) {
-    attend_split_body<D, KT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    __shared__ __attribute__((aligned(16))) char tile[tile_bytes<D, KT>()];
+    attend_split_body<D, KT>(a, blockIdx.x, blockIdx.y, blockIdx.z, tile);
 }
 
 // One workgroup of NT threads per (layer, sequence, NT/256 consecutive
@@ -347,6 +352,26 @@ using namespace attend_k;
 size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows) {
     const size_t splits = (size_t)((max_rows + kR - 1) / kR);
     return (size_t)n_layers * batch * splits * (16 * (size_t)D + 32) * sizeof(float);
+}
+
+template <int D, typename KT>
+hipError_t launch_splits_t(const AttendArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((attend_split_kernel<D, KT>), dim3(a.max_splits, a.batch, a.n_layers), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_splits(const AttendArgs& a, hipStream_t s) {
+    if (a.max_splits == 0) return hipSuccess;
+    if (a.dtype == LSA_F32) {
+        if (a.D == 128) return launch_splits_t<128, float>(a, s);
+        if (a.D == 256) return launch_splits_t<256, float>(a, s);
+        if (a.D == 512) return launch_splits_t<512, float>(a, s);
+    } else if (a.dtype == LSA_BF16) {
+        if (a.D == 128) return launch_splits_t<128, uint16_t>(a, s);
+        if (a.D == 256) return launch_splits_t<256, uint16_t>(a, s);
+        if (a.D == 512) return launch_splits_t<512, uint16_t>(a, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid) {

@@ -100,6 +100,11 @@ constexpr int kSelBins = 2048;        // 11-bit key histogram of the long-segmen
 constexpr int kSelShift = 21;         // bin = order_key(score) >> kSelShift
 constexpr int kSelKeepCap = 8192;     // entries (above + in the boundary bucket) resolved in LDS
 constexpr int kSelSingle = 32768;     // segments up to this length use one workgroup
+// sparse layers per stage / attention launch: a step with more layers issues
+// these launches per group of this many layers (their arguments stay small)
+constexpr int kLaunchLayers = 16;
+// (layer, sequence) segments the lookahead schedule's row copy handles in one launch
+constexpr int kCopyMaxSegs = 1024;
 
 // Query/weight projection of the hidden state (lsa_project.hip).
 struct ProjectArgs {
@@ -193,7 +198,7 @@ struct StageArgs {
     // valid source entries per sequence: a layer uses its chunks below
     // floor(src_valid[b] * src_ratio / ratio), the complete ones
     int32_t src_valid[LSA_MAX_BATCH];
-    StageLayer L[LSA_MAX_LAYERS];
+    StageLayer L[kLaunchLayers];
 };
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s);
 // the stage of n_layers layers (descriptors in device memory) as one launch
@@ -231,20 +236,29 @@ struct AttendArgs {
     float scale;
     float* part_acc;            // [layer][b][split][16][D]
     float* part_ml;             // [layer][b][split][2][16]
-    AttendLayer L[LSA_MAX_LAYERS];
+    AttendLayer L[kLaunchLayers];
 };
 constexpr int kAttendRows = 32;
 constexpr int kAttendMaxRows = 5120;    // longest row list (window + entries) of one attention
 size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows);
 hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid = nullptr);
+// the split launch alone (its merge runs elsewhere)
+hipError_t launch_attend_splits(const AttendArgs& a, hipStream_t s);
 // fused launches of the lookahead schedule.  launch_la_fetch_score scores and,
 // in the same launch, copies the rows in the miss lists of `ga` (a deferring
 // stage's output, laid out back to back over (layer, sequence)) into their slots.
 // With hist_for (a one-segment path-1 select, see la_fused_hist), the score
 // launch also builds that select's histogram.
-// copy = false: the rows were copied already (the launch only scores).
-hipError_t launch_la_fetch_score(const ScoreArgs& sa, const StageArgs& ga, int phys_stride, int key_dtype, int dk,
-                                 int n_cu, const SelectArgs* hist_for, bool copy, hipStream_t s);
+// The missed rows a deferring stage listed for a step: the lists and counts of
+// every (layer, sequence) segment lie back to back, segment s = layer * batch + b.
+struct CopyArgs {
+    const uint64_t* miss;     // [n_seg][phys_stride][2]: cold row address, slot row address
+    const int32_t* n_miss;    // [n_seg]
+    int32_t n_seg, phys_stride, row_bytes;
+};
+// n_seg = 0: the rows were copied already (the launch only scores).
+hipError_t launch_la_fetch_score(const ScoreArgs& sa, const CopyArgs& ca, int key_dtype, int dk, int n_cu,
+                                 const SelectArgs* hist_for, hipStream_t s);
 bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se, int n_cu);
 // select histogram (unless hist_done) and collect of step t+1, then its final
 // selection beside the attention splits of step t (short segments: the splits,

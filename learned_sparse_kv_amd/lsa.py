@@ -23,7 +23,7 @@ MODE = {"topk": 0, "threshold": 1}
 COLD = {"hbm": 0, "host": 1}
 DTYPE = {"f32": F32, "bf16": BF16, "f16": F16, "fp8": FP8_E4M3, "mxfp4": MXFP4, "mxint8": MXINT8}
 K_NAMES = ["score", "select", "stage", "gather", "attend", "combine"]
-MAX_LAYERS = 16
+MAX_LAYERS = 64
 
 STATUS = {0: "LSA_OK", 1: "LSA_ERR_INVALID_ARG", 2: "LSA_ERR_SLOTS_LT_TOPK", 3: "LSA_ERR_PINNED_CAP",
           4: "LSA_ERR_NOT_STORED", 5: "LSA_ERR_HIP", 6: "LSA_ERR_NO_MEMORY", 7: "LSA_ERR_UNSUPPORTED"}

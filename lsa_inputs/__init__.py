@@ -254,6 +254,15 @@ WORKLOADS["swap_1m_fp8"] = WORKLOADS["swap_1m"].replace(name="swap_1m_fp8", key_
 # 17.8 and 34.6 MB of keys)
 WORKLOADS["swap_1m_mxfp4"] = WORKLOADS["swap_1m"].replace(name="swap_1m_mxfp4", key_dtype="mxfp4")
 WORKLOADS["swap_1m_mxint8"] = WORKLOADS["swap_1m"].replace(name="swap_1m_mxint8", key_dtype="mxint8")
+# the pages' whole sparse-layer stack (FlashMemory 1M doc, PINNED_MIB worked
+# examples and the expected log sparse_layers=41): 20 ratio-4 and 21 ratio-128
+# layers, alternating, all served by one selection per step; at 64K context for
+# parity (the ratio-4 layers swap from HBM, the ratio-128 ones are resident) and
+# at 1M with pinned-host cold pools (11.1 GB)
+STACK_41 = tuple([128, 4] * 20 + [128])
+WORKLOADS["stack_64k_41"] = WORKLOADS["ens_8k"].replace(name="stack_64k_41", base_seed=1007, ctx=65536,
+                                                       layer_ratios=STACK_41, gpu_chunks=1024, drift=0.05)
+WORKLOADS["stack_1m_41"] = WORKLOADS["swap_1m"].replace(name="stack_1m_41", layer_ratios=STACK_41)
 # the 1M workload with the rolling-buffer replacement: recency and importance
 # weighed equally, and at most 70 % of the 1024 slots kept in use after a step
 WORKLOADS["swap_1m_wr"] = WORKLOADS["swap_1m"].replace(name="swap_1m_wr", recency_w=50, high_water=70)

@@ -289,3 +289,10 @@ def test_decode_weighted_replacement():
         check_step(t, wl, dw, want)
         check_pools(wl, dw, ref)
     assert dw.pools[0].stats()["hits"] > 0
+
+
+def test_decode_41_layer_stack():
+    """The pages' 41 sparse layers (20 ratio-4, 21 ratio-128) served by one
+    selection per step: stages and attentions run in groups of layers; every
+    layer's rows and output equal the oracle's."""
+    run_decode(L.WORKLOADS["stack_64k_41"], 3)

@@ -278,3 +278,60 @@ def test_lookahead_weighted_replacement():
             assert nrows[l, 0] == n and np.array_equal(phys[l, 0, :n], want["phys"][l][0]), f"step {t} layer {l}"
             err = rel_err_rows(out[l, 0], want["out"][l][0])
             assert err <= RTOL[wl.kv_dtype], f"step {t} layer {l}: rel err {err}"
+
+
+def test_lookahead_41_layer_stack_matches_sync():
+    """The 41-layer stack in the lookahead schedule (the row copy covers every
+    layer, attention and stage run per group of layers): rows and output bits
+    equal the synchronous schedule's."""
+    wl = L.WORKLOADS["stack_64k_41"]
+    dw = DeviceWorkload(wl)
+    dw.make_steps(6)
+    sync = []
+    for t in range(4):
+        dw.step(t)
+        torch.cuda.synchronize()
+        sync.append((bits(dw.out.cpu().numpy()).copy(), dw.phys.cpu().numpy().copy(), dw.n_rows.cpu().numpy().copy()))
+    dw.reset_pools()
+    dw.lookahead_prime(0)
+    for t in range(4):
+        cur = lsa.lookahead_buffer(dw.ctx)
+        dw.lookahead_step(t)
+        torch.cuda.synchronize()
+        out, phys, nrows = sync[t]
+        assert np.array_equal(dw.n_rows2[cur].cpu().numpy(), nrows), f"step {t}: row counts"
+        got_p = dw.phys2[cur].cpu().numpy()
+        for l in range(wl.n_layers):
+            m = int(nrows[l, 0])
+            assert np.array_equal(got_p[l, 0, :m], phys[l, 0, :m]), f"step {t} layer {l}"
+        assert np.array_equal(bits(dw.out.cpu().numpy()), out), f"step {t}: lookahead vs sync bits"
+
+
+def test_lookahead_batched_topk_matches_sync_over_16_steps():
+    """Four sequences of 65536 entries (64 select collect blocks each), top-512,
+    over 16 steps: the final selection of every sequence runs beside the
+    attention splits; rows and output bits equal the synchronous schedule's."""
+    wl = L.WORKLOADS["thresh_256k"].replace(mode="topk", k=512)
+    n = 16
+    dw = DeviceWorkload(wl)
+    dw.make_steps(n + 2)
+    sync = []
+    for t in range(n):
+        dw.step(t)
+        torch.cuda.synchronize()
+        sync.append((bits(dw.out.cpu().numpy()).copy(), dw.phys.cpu().numpy().copy(), dw.n_rows.cpu().numpy().copy()))
+    dw.reset_pools()
+    dw.lookahead_prime(0)
+    for t in range(n):
+        cur = lsa.lookahead_buffer(dw.ctx)
+        dw.lookahead_step(t)
+        torch.cuda.synchronize()
+        out, phys, nrows = sync[t]
+        assert np.array_equal(dw.n_rows2[cur].cpu().numpy(), nrows), f"step {t}: row counts"
+        got_p = dw.phys2[cur].cpu().numpy()
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                m = int(nrows[l, b])
+                assert np.array_equal(got_p[l, b, :m], phys[l, b, :m]), f"step {t} layer {l} seq {b}"
+        assert np.array_equal(bits(dw.out.cpu().numpy()), out), f"step {t}: lookahead vs sync bits"
+    say(f"  batched top-512: lookahead = sync over {n} steps")
