@@ -180,6 +180,10 @@ class DeviceWorkload:
         self.prepared = {t: lsa.PreparedStep("lsa_lookahead_step", self.ctx, **self._la_args(t + 1, t))
                          for t in steps}
 
+    def prepare_steps(self, steps) -> None:
+        """Marshal the descriptors of the listed synchronous steps once (launch with run_prepared)."""
+        self.prepared = {t: lsa.PreparedStep("lsa_decode_step", self.ctx, **self._step_args(t)) for t in steps}
+
     def run_prepared(self, t: int) -> None:
         self.prepared[t]()
 
