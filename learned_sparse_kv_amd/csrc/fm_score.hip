@@ -188,9 +188,42 @@ __device__ inline float e8m0(uint32_t s) { return __uint_as_float(s << 23); }
 // With HIST, every stored score that the select would count (a valid entry;
 // in threshold mode one above t_f) is also added to the LDS histogram `hist`
 // of 11-bit key tops -- the select's first pass -- so a caller can skip it.
-template <int DK, typename KT, bool HIST = false>
+// Candidate lists written by the score launch (the lookahead schedule's
+// select): per sub-block of kCandSub consecutive entries, in index order, the
+// entries of bin >= guess[seq] that pass the threshold, with their order keys.
+// The workgroups split evenly over the sequences (the grid is a multiple of the
+// batch) and each takes whole 1024-entry blocks; its waves take one quarter of
+// them each, a run of consecutive tiles, so each wave writes the lists of its
+// own sub-blocks as it goes.
+constexpr int kCandSub = kSelColBlk / kWaves;   // 256
+struct CandOut {
+    int32_t* idx;            // [n_seg][nsb][kCandSub]
+    uint32_t* key;           // [n_seg][nsb][kCandSub]
+    int32_t* count;          // [n_seg][nsb]
+    const int32_t* guess;    // [n_seg]
+    int32_t nblk;            // 1024-entry blocks per sequence
+    int32_t thr;             // threshold mode: an entry also needs score > t_f
+    float t_f;
+};
+
+// The 1024-entry blocks of workgroup bx of gx: returns the first, *seq the
+// sequence and *n their number (0 when the sequence has fewer blocks than
+// workgroups).
+__device__ inline int cand_blocks(const ScoreArgs& a, const int bx, const int gx, const int nblk, int* seq, int* n) {
+    const int G = gx / a.batch;
+    *seq = bx / G;
+    const int j = bx - *seq * G;
+    const int per = (nblk + G - 1) / G;
+    const int first = j * per;
+    const int last = first + per < nblk ? first + per : nblk;
+    *n = last > first ? last - first : 0;
+    return first;
+}
+
+template <int DK, typename KT, bool HIST = false, bool CAND = false>
 __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, const int gx, uint32_t* hist = nullptr,
-                                              const int hist_mode = 0, const float hist_t_f = 0.0f) {
+                                              const int hist_mode = 0, const float hist_t_f = 0.0f,
+                                              const CandOut* co = nullptr) {
     using C = Cfg<DK, KT>;
     constexpr bool kF32 = C::kBits == 32;
     constexpr int kSteps = C::kSteps;
@@ -208,7 +241,26 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
     int total = a.tile_start[a.batch];
     int stride = gx * kWaves;
     int t = bx * kWaves + wave;
-    if (a.batch > 1 && stride >= a.batch) {
+    // CAND: this wave's sequence, first sub-block and sub-block count, the list
+    // bin and key threshold, and the running list of the current sub-block
+    int c_seq = 0, c_sb = 0, c_nsb = 0, c_guess = 0, c_run = 0, c_cur = 0;
+    uint32_t c_tkey = 0;
+    if constexpr (CAND) {
+        int nb;
+        const int b0 = cand_blocks(a, bx, gx, co->nblk, &c_seq, &nb);
+        c_guess = co->guess[c_seq];
+        c_tkey = co->thr ? order_key(co->t_f) : 0u;
+        constexpr int kTpb = kSelColBlk / kTile;    // tiles per block
+        const int tw = nb * (kTpb / kWaves);        // tiles per wave: nb sub-blocks
+        const int ts = a.tile_start[c_seq], te = a.tile_start[c_seq + 1];
+        const int lo_w = ts + b0 * kTpb + wave * tw;
+        t = lo_w < te ? lo_w : te;
+        total = lo_w + tw < te ? lo_w + tw : te;
+        stride = 1;
+        c_sb = b0 * kWaves + wave * nb;
+        c_nsb = nb;
+        c_cur = c_sb;
+    } else if (a.batch > 1 && stride >= a.batch) {
         // several sequences: the waves split into one equal group per sequence, so
         // a wave's tiles all lie in one sequence and its load pipeline (and query
         // set-up) starts once, not once per sequence; the waves left over idle
@@ -236,7 +288,8 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
     while (t < total) {
         // one run of this wave's tiles that belong to sequence b
         while (t >= a.tile_start[b + 1]) ++b;
-        const int lo = a.tile_start[b], hi = a.tile_start[b + 1];
+        // a run ends at the sequence's last tile, or at the workgroup's (CAND)
+        const int lo = a.tile_start[b], hi = a.tile_start[b + 1] < total ? a.tile_start[b + 1] : total;
         const int nv = a.n_valid[b];
         const char* const seq = kbase + (int64_t)b * a.n_keys * C::kRowBytes;
         const uint32_t seq_bytes = (uint32_t)nv * (uint32_t)C::kRowBytes;
@@ -444,6 +497,28 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
                     if (half == 0 && key < nv && (hist_mode != LSA_SELECT_THRESHOLD || ev > hist_t_f))
                         atomicAdd(&hist[order_key(ev) >> kSelShift], 1u);
                 }
+                if (CAND) {
+                    // the 32 keys of this block lie in one sub-block; a new one
+                    // closes the list of the last (its count written by lane 0)
+                    const int sb = key / kCandSub;   // uniform over the lanes that matter
+                    const int sbu = __builtin_amdgcn_readfirstlane(sb);
+                    if (sbu != c_cur) {
+                        if (lane == 0) co->count[(int64_t)c_seq * (co->nblk * kWaves) + c_cur] = c_run;
+                        c_cur = sbu;
+                        c_run = 0;
+                    }
+                    const uint32_t ok = order_key(e);
+                    const bool cand = half == 0 && key < nv && (int)(ok >> kSelShift) >= c_guess && (!co->thr || ok > c_tkey);
+                    const uint64_t bal = __ballot(cand);
+                    if (cand) {
+                        const int pos = c_run + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                        const int64_t at = ((int64_t)c_seq * (co->nblk * kWaves) + sbu) * kCandSub + pos;
+                        co->idx[at] = key;
+                        co->key[at] = ok;
+                    }
+                    c_run += __popcll(bal);
+                }
             }
             cur ^= 1;
             if constexpr (C::kMX) {
@@ -453,6 +528,14 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
                     sc_nxt[j] = sc_n2[j];
                 }
             }
+        }
+    }
+    if constexpr (CAND) {
+        // the current sub-block's count, and zero for the wave's sub-blocks past
+        // the sequence's valid entries (they had no tile)
+        if (lane == 0) {
+            for (int sb = c_cur; sb < c_sb + c_nsb; ++sb)
+                co->count[(int64_t)c_seq * (co->nblk * kWaves) + sb] = sb == c_cur ? c_run : 0;
         }
     }
 }

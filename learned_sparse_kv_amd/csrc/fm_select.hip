@@ -43,7 +43,7 @@ namespace select_k {
 constexpr int kNT = 1024;
 constexpr int kNW = kNT / 64;
 constexpr int kBlk = 4096;          // entries per block of the histogram kernel
-constexpr int kColBlk = 1024;       // entries per block of the collect kernel
+constexpr int kColBlk = kSelColBlk;   // entries per block of the collect kernel
 constexpr int kMaxBlocks = 4096;    // collect blocks whose lists the final kernel gathers in LDS
 constexpr int kBlkThreads = 256;
 
@@ -492,6 +492,7 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
     // the blocks' counts are loaded before the histogram is scanned (thread t
     // owns blocks [t*PB, (t+1)*PB)), so the two reads overlap
     const int nb = a.nblk;
+    const int stride = a.blk_stride ? a.blk_stride : kColBlk;   // entries per block list
     const int PB = (nb + NT - 1) / NT;
     constexpr int kPB = (MAXB + NT - 1) / NT;   // PB <= kPB whenever nb <= MAXB
     const int32_t* cnt = a.blk_count + (int64_t)seg * nb;
@@ -504,6 +505,7 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
         c_own[q] = (q < PB && bi < nb) ? cnt[bi] : 0;
         mine += c_own[q];
     }
+    const int guess = a.pre ? a.guess_in[seg] : 0;
     find_boundary<NT>(g, a.k, sh.scan, s_b);
     const int total = s_b[2];
     const int K = total < a.k ? total : a.k;
@@ -515,7 +517,9 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
     if (K == 0) mine = 0;
     int n_keep;
     int off = block_excl_scan<NT>(mine, sh.scan, &n_keep);
-    if (K > 0 && n_keep <= kSelKeepCap && nb <= MAXB) {
+    // lists written by the score launch hold every entry of b* and above only
+    // when their first bin is at most b*
+    if (K > 0 && n_keep <= kSelKeepCap && nb <= MAXB && guess <= bstar) {
         // every block's first position in the gathered list
 #pragma unroll
         for (int q = 0; q < kPB; ++q) {
@@ -540,7 +544,7 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
                     const int mid = (lo + hi + 1) >> 1;
                     if (s_start[mid] <= p) lo = mid; else hi = mid - 1;
                 }
-                const int64_t src = ((int64_t)seg * nb + lo) * kColBlk + (p - s_start[lo]);
+                const int64_t src = ((int64_t)seg * nb + lo) * stride + (p - s_start[lo]);
                 g_idx[i] = a.blk_idx[src];
                 g_key[i] = a.blk_key[src];
             }
@@ -549,11 +553,49 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
         for (int i = 0; i < kGather; ++i) {
             const int p = tid + i * NT;
             if (p < n_keep) {
-                s_idx[p] = g_idx[i];
+                // lists from the score launch are unmarked: mark the entries of b*
+                const bool mark = a.pre && (int)(g_key[i] >> kSelShift) == bstar;
+                s_idx[p] = g_idx[i] | (mark ? (int32_t)0x80000000 : 0);
                 s_key[p] = g_key[i];
             }
         }
         __syncthreads();
+        if (a.pre && guess < bstar) {
+            // lists that start below b*: keep the entries of b* and above, in
+            // order; thread t moves [t*E3, t*E3 + E3) once every thread has read its own
+            constexpr int kE3 = (kSelKeepCap + NT - 1) / NT;
+            const int E3 = (n_keep + NT - 1) / NT;
+            int32_t r_idx[kE3];
+            uint32_t r_key[kE3];
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < kE3; ++e) {
+                const int p = tid * E3 + e;
+                const bool in = e < E3 && p < n_keep;
+                r_idx[e] = in ? s_idx[p] : 0;
+                r_key[e] = in ? s_key[p] : 0u;
+                const int bin = (int)(r_key[e] >> kSelShift);
+                if (in && bin >= bstar) {
+                    r_idx[e] |= bin == bstar ? (int32_t)0x80000000 : 0;
+                    ++c;
+                } else {
+                    r_idx[e] = 0x7FFFFFFF;   // dropped
+                }
+            }
+            int kept;
+            int pos = block_excl_scan<NT>(c, sh.scan, &kept);
+            __syncthreads();   // every entry is in registers before any moves
+#pragma unroll
+            for (int e = 0; e < kE3; ++e) {
+                if (r_idx[e] != 0x7FFFFFFF) {
+                    s_idx[pos] = r_idx[e];
+                    s_key[pos] = r_key[e];
+                    ++pos;
+                }
+            }
+            n_keep = kept;
+            __syncthreads();
+        }
         // bits 20..0 of the candidates' keys (bucket b* fixes the rest): a radix
         // pass over bits 20..10, then bits 9..0 of the candidates in the bin found
         const int need = K - above;
@@ -652,7 +694,21 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
         stream_select<NT>(a, a.scores + (int64_t)seg * a.n_keys, seg_valid(a, seg), K, sh, out_sel);
     }
     for (int i = K + tid; i < a.stride; i += NT) out_sel[i] = -1;
-    if (tid == 0) a.count[seg] = K;
+    if (tid == 0) {
+        a.count[seg] = K;
+        if (a.guess_out) {
+            // the next step's lists start at b* when its entries and those above
+            // hold half as many again as are chosen (a small drift keeps b*),
+            // else one bin lower if that fits half the LDS list; no entry: from 0
+            int gn = 0;
+            if (K > 0) {
+                const int at_b = above + (int)g[bstar];
+                gn = bstar;
+                if (2 * at_b < 3 * K && bstar > 0 && at_b + (int)g[bstar - 1] <= kSelKeepCap / 2) gn = bstar - 1;
+            }
+            a.guess_out[seg] = gn;
+        }
+    }
     __syncthreads();
     for (int i = tid; i < kSelBins; i += NT) g[i] = 0u;
 }
@@ -690,7 +746,9 @@ bool select_plan(SelectArgs* a, size_t* zero_bytes, size_t* ws_bytes) {
     a->nblk = (int)((a->n_keys + kColBlk - 1) / kColBlk);
     *zero_bytes = (size_t)a->n_seg * kSelBins * 4;
     const size_t nb = (size_t)a->n_seg * a->nblk;
-    *ws_bytes = nb * 4 + 256 + nb * kColBlk * 8 + 256;
+    // counts for four lists per block: the score launch's lists cover a
+    // quarter block each
+    *ws_bytes = nb * 16 + 256 + nb * kColBlk * 8 + 256;
     return true;
 }
 
@@ -700,7 +758,7 @@ void select_bind(SelectArgs* a, void* zero_region, void* ws) {
     char* w = static_cast<char*>(ws);
     const size_t nb = (size_t)a->n_seg * a->nblk;
     a->blk_count = reinterpret_cast<int32_t*>(w);
-    w += (nb * 4 + 255) / 256 * 256;
+    w += (nb * 16 + 255) / 256 * 256;
     a->blk_idx = reinterpret_cast<int32_t*>(w);
     a->blk_key = reinterpret_cast<uint32_t*>(w + nb * kColBlk * 4);
 }

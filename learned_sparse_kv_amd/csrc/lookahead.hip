@@ -111,19 +111,28 @@ __device__ inline void copy_wave(const CopyArgs& ca, const int wg, const int n_w
 }
 
 // The select's histogram, built by the score launch when the step has one
-// segment: hist [kSelBins], zero on entry; mode and t_f as in the select.
+// segment per sequence: hist [n_seg][kSelBins], zero on entry; mode and t_f as
+// in the select.  With blk_count set the score waves also write the select's
+// candidate lists (score_k::CandOut), which the final selection takes in place
+// of its collect pass.
 struct HistArgs {
     uint32_t* hist;
     int32_t mode;
     float t_f;
+    int32_t* blk_count;         // [n_seg][4 * nblk]
+    int32_t* blk_idx;           // [n_seg][4 * nblk][kCandSub]
+    uint32_t* blk_key;          // [n_seg][4 * nblk][kCandSub]
+    const int32_t* guess;       // [n_seg]
+    int32_t nblk;               // 1024-entry blocks per sequence
 };
 
 // Workgroup = 4 score waves (fm_score) + 1 copy wave.  With HIST the score
 // waves also count their scores into an LDS histogram; the last of them to
 // finish adds it to the segment's histogram (its PCIe-bound copy wave
 // usually ends later, so the flush costs no time).
-template <int DK, typename KT, bool HIST>
+template <int DK, typename KT, bool HIST, bool CAND>
 __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, const CopyArgs ca, const HistArgs ha) {
+    static_assert(HIST || !CAND, "the candidate lists come with the histogram");
     __shared__ int s_pre[kCopyMaxSegs];
     __shared__ uint32_t s_hist[HIST ? kSelBins : 1];
     __shared__ int s_done;
@@ -137,7 +146,9 @@ __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, cons
         copy_wave(ca, blockIdx.x, gridDim.x, s_pre);
         return;
     }
-    score_k::fm_score_body<DK, KT, HIST>(sa, blockIdx.x, gridDim.x, s_hist, ha.mode, ha.t_f);
+    const score_k::CandOut co{ha.blk_idx, ha.blk_key, ha.blk_count, ha.guess, ha.nblk,
+                              ha.mode == LSA_SELECT_THRESHOLD ? 1 : 0, ha.t_f};
+    score_k::fm_score_body<DK, KT, HIST, CAND>(sa, blockIdx.x, gridDim.x, s_hist, ha.mode, ha.t_f, &co);
     if (HIST) {
         // every score wave's LDS adds are done before it counts itself finished
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -189,19 +200,27 @@ __global__ __launch_bounds__(1024, 1) void la_stage_combine(const StageArgs ga, 
     attend_k::attend_combine_body<D, 1024>(aa, h % sp.x2, (h / sp.x2) % aa.batch, h / (sp.x2 * aa.batch));
 }
 
-template <int DK, typename KT>
-hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, const HistArgs& ha, int n_cu, hipStream_t s) {
+// The score launch's grid: one workgroup per CU at most; with the histogram
+// and several sequences, whole workgroups per sequence.
+int la_score_grid(const ScoreArgs& sa, bool hist, int n_cu) {
     const int total = sa.tile_start[sa.batch];
     int grid = (total + score_k::kWaves - 1) / score_k::kWaves;
     if (grid > n_cu) grid = n_cu;
     if (grid < 1) grid = 1;
-    // with the histogram and several sequences, whole workgroups per sequence
-    if (ha.hist && sa.batch > 1) grid -= grid % sa.batch;
+    if (hist && sa.batch > 1) grid -= grid % sa.batch;
+    return grid;
+}
+
+template <int DK, typename KT>
+hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, const HistArgs& ha, int n_cu, hipStream_t s) {
+    const int grid = la_score_grid(sa, ha.hist != nullptr, n_cu);
     if (grid < 1) return hipErrorInvalidValue;
-    if (ha.hist)
-        hipLaunchKernelGGL((la_score_copy<DK, KT, true>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+    if (ha.blk_count)
+        hipLaunchKernelGGL((la_score_copy<DK, KT, true, true>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+    else if (ha.hist)
+        hipLaunchKernelGGL((la_score_copy<DK, KT, true, false>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
     else
-        hipLaunchKernelGGL((la_score_copy<DK, KT, false>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+        hipLaunchKernelGGL((la_score_copy<DK, KT, false, false>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
     return hipGetLastError();
 }
 
@@ -222,9 +241,12 @@ hipError_t launch_d(const AttendArgs& aa, const SelectArgs& se, bool hist_done, 
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(select_k::sel_collect_kernel, dim3(se.nblk, se.n_seg), dim3(select_k::kBlkThreads), 0, s, se);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (!se.pre) {
+            hipLaunchKernelGGL(select_k::sel_collect_kernel, dim3(se.nblk, se.n_seg), dim3(select_k::kBlkThreads), 0, s,
+                               se);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL((la_final_split<D, KT>), dim3(sp.n0 + se.n_seg), dim3(512), 0, s, aa, se, sp);
         return hipGetLastError();
     }
@@ -251,15 +273,29 @@ hipError_t launch_e(const StageArgs& ga, const AttendArgs& aa, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const CopyArgs& ca, int key_dtype, int dk, int n_cu,
-                                 const SelectArgs* hist_for, hipStream_t s) {
+                                 const SelectArgs* hist_for, const int32_t* guess, bool* lists, hipStream_t s) {
     const int cpr = ca.row_bytes / 16;
     if (ca.n_seg < 0 || ca.n_seg > kCopyMaxSegs || (ca.n_seg && (!ca.miss || !ca.n_miss)) || ca.row_bytes % 16 != 0 ||
         cpr < 1 || (cpr & (cpr - 1)) != 0)
         return hipErrorInvalidValue;
-    HistArgs ha{nullptr, 0, 0.0f};
+    HistArgs ha{};
+    *lists = false;
     if (hist_for) {
         if (!la_fused_hist(sa, *hist_for, n_cu)) return hipErrorInvalidValue;
-        ha = HistArgs{hist_for->hist, hist_for->mode, hist_for->t_f};
+        ha.hist = hist_for->hist;
+        ha.mode = hist_for->mode;
+        ha.t_f = hist_for->t_f;
+        // the candidate lists too, when their sub-blocks fit the final
+        // selection's block table
+        const int G = la_score_grid(sa, true, n_cu) / sa.batch;
+        if (guess && G > 0 && hist_for->nblk * score_k::kWaves <= kFinMaxBlocks) {
+            ha.blk_count = hist_for->blk_count;
+            ha.blk_idx = hist_for->blk_idx;
+            ha.blk_key = hist_for->blk_key;
+            ha.guess = guess;
+            ha.nblk = hist_for->nblk;
+            *lists = true;
+        }
     }
     if (key_dtype == LSA_F32) {
         if (dk == 32) return launch_a<32, float>(sa, ca, ha, n_cu, s);

@@ -125,6 +125,10 @@ struct lsa_ctx {
     hipEvent_t kv_layers_done[2] = {nullptr, nullptr};
     int kv_layers_cap = 0;
     int kv_layers_next = 0;
+    // lookahead schedule: per sequence, the select bin from which the next
+    // step's score launch lists candidates (written by each step's final
+    // selection; a wrong guess only costs the exact fallback)
+    int32_t* sel_guess = nullptr;   // device [LSA_MAX_BATCH]
 };
 
 namespace {
@@ -340,6 +344,16 @@ lsa_status lsa_ctx_create(lsa_ctx** out, int32_t device) {
     // the static scratch's device address, looked up once per device (only the
     // allocation-free step needs it, so a failed lookup fails only that call)
     c->scratch_status = scratch_address(device, &c->scratch);
+    if (hipMalloc(reinterpret_cast<void**>(&c->sel_guess), LSA_MAX_BATCH * sizeof(int32_t)) != hipSuccess) {
+        delete c;
+        return fail(LSA_ERR_NO_MEMORY, "lsa_ctx_create: %zu bytes of device memory", LSA_MAX_BATCH * sizeof(int32_t));
+    }
+    if (hipMemset(c->sel_guess, 0, LSA_MAX_BATCH * sizeof(int32_t)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(c->sel_guess);
+        delete c;
+        return fail(LSA_ERR_HIP, "lsa_ctx_create: clearing the select guesses failed");
+    }
     *out = c;
     return LSA_OK;
 }
@@ -349,6 +363,7 @@ void lsa_ctx_destroy(lsa_ctx* c) {
     (void)hipDeviceSynchronize();
     if (c->ws) (void)hipFree(c->ws);
     if (c->zero) (void)hipFree(c->zero);
+    if (c->sel_guess) (void)hipFree(c->sel_guess);
     for (auto& p : c->pending) {
         (void)hipEventDestroy(p.a);
         (void)hipEventDestroy(p.b);
@@ -1296,12 +1311,14 @@ lsa_status lsa_lookahead_prime(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_
     ctx->la_cur = 0;
     ctx->la_fetched = false;
     plan_use_buffer(&P, 0);
+    // the final selection leaves the first step's candidate-list guess
+    P.se.guess_out = ctx->sel_guess;
     // the first step's rows are staged; its lookahead step copies the missed ones
     return launch_predict(ctx, P, d, (hipStream_t)stream, false);
 }
 
 // Step t (rows in buffer cur) and the prediction of step t+1 (into buffer
-// nxt), as five launches on one stream; see lookahead.hip.
+// nxt), as three or four launches on one stream; see lookahead.hip.
 lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t stream) {
     StepPlan P;
     lsa_status st = step_plan(ctx, d, 2, &P);
@@ -1316,14 +1333,27 @@ lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t
     // (unless an attention of the window already did)
     const CopyArgs ca = plan_copy(P, cur, !ctx->la_fetched);
     const bool fuse_hist = la_fused_hist(P.sa, P.se, ctx->n_cu);
+    bool lists = false;
     {
         Timed t(ctx, LSA_K_SCORE, s);
-        HIPTRY(launch_la_fetch_score(P.sa, ca, d->key_dtype, d->dk, ctx->n_cu, fuse_hist ? &P.se : nullptr, s));
+        HIPTRY(launch_la_fetch_score(P.sa, ca, d->key_dtype, d->dk, ctx->n_cu, fuse_hist ? &P.se : nullptr,
+                                     ctx->sel_guess, &lists, s));
         t.end();
     }
     {
         Timed t(ctx, LSA_K_SELECT, s);
-        HIPTRY(launch_la_select_split(P.aa[0], P.se, fuse_hist, s));
+        // with the lists written by the score launch the final selection checks
+        // their guess and takes them in place of the collect pass
+        SelectArgs se = P.se;
+        if (lists) {
+            // one list per quarter block
+            se.pre = 1;
+            se.nblk = P.se.nblk * 4;
+            se.blk_stride = kSelColBlk / 4;
+        }
+        se.guess_in = ctx->sel_guess;
+        se.guess_out = ctx->sel_guess;
+        HIPTRY(launch_la_select_split(P.aa[0], se, fuse_hist, s));
         for (int g = 1; g < P.n_groups; ++g) HIPTRY(launch_attend_splits(P.aa[g], s));
         t.end();
     }

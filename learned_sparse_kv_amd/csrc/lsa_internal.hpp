@@ -99,6 +99,7 @@ __device__ inline int block_excl_scan(int v, int* smem, int* total) {
 constexpr int kSelBins = 2048;        // 11-bit key histogram of the long-segment path
 constexpr int kSelShift = 21;         // bin = order_key(score) >> kSelShift
 constexpr int kSelKeepCap = 8192;     // entries (above + in the boundary bucket) resolved in LDS
+constexpr int kSelColBlk = 1024;      // entries per candidate list block of the histogram path
 constexpr int kSelSingle = 32768;     // segments up to this length use one workgroup
 // sparse layers per stage / attention launch: a step with more layers issues
 // these launches per group of this many layers (their arguments stay small)
@@ -148,6 +149,16 @@ struct SelectArgs {
     int32_t* blk_count;         // [n_seg][nblk] entries each block kept
     int32_t* blk_idx;           // [n_seg][nblk][1024] kept indices (top bit: boundary bucket)
     uint32_t* blk_key;          // [n_seg][nblk][1024] their keys
+    // pre = 1: the score launch wrote the block lists: every entry of bin
+    // >= guess_in[seg] (passing the threshold), unmarked, in index order; the
+    // final selection checks guess_in[seg] <= b* and scans the scores otherwise
+    int32_t pre;
+    int32_t blk_stride;         // entries per block list (0: kSelColBlk)
+    const int32_t* guess_in;    // [n_seg]
+    // when set, the final selection writes the bin the next step's lists start
+    // at: this step's b*, or one bin lower when b* and above hold fewer than
+    // 1.5 times the entries chosen (and the lower bin keeps the lists short)
+    int32_t* guess_out;         // [n_seg]
 };
 // Fills the shape fields; returns false when out of range.  *zero_bytes is the
 // size of the zero-initialised region (hist + counters), *ws_bytes the rest.
@@ -245,10 +256,12 @@ hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid 
 // the split launch alone (its merge runs elsewhere)
 hipError_t launch_attend_splits(const AttendArgs& a, hipStream_t s);
 // fused launches of the lookahead schedule.  launch_la_fetch_score scores and,
-// in the same launch, copies the rows in the miss lists of `ga` (a deferring
+// in the same launch, copies the rows in the miss lists of `ca` (a deferring
 // stage's output, laid out back to back over (layer, sequence)) into their slots.
-// With hist_for (a one-segment path-1 select, see la_fused_hist), the score
-// launch also builds that select's histogram.
+// With hist_for (a path-1 select with one segment per sequence, see
+// la_fused_hist), the score launch also builds that select's histogram, and,
+// when guess is set and the blocks fit, its candidate lists from bin guess[seq]
+// on (*lists = true; the final selection then runs with pre = 1).
 // The missed rows a deferring stage listed for a step: the lists and counts of
 // every (layer, sequence) segment lie back to back, segment s = layer * batch + b.
 struct CopyArgs {
@@ -258,11 +271,11 @@ struct CopyArgs {
 };
 // n_seg = 0: the rows were copied already (the launch only scores).
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const CopyArgs& ca, int key_dtype, int dk, int n_cu,
-                                 const SelectArgs* hist_for, hipStream_t s);
+                                 const SelectArgs* hist_for, const int32_t* guess, bool* lists, hipStream_t s);
 bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se, int n_cu);
-// select histogram (unless hist_done) and collect of step t+1, then its final
-// selection beside the attention splits of step t (short segments: the splits,
-// then the one-kernel select)
+// select histogram (unless hist_done) and collect (unless se.pre) of step t+1,
+// then its final selection beside the attention splits of step t (short
+// segments: the splits, then the one-kernel select)
 hipError_t launch_la_select_split(const AttendArgs& aa, const SelectArgs& se, bool hist_done, hipStream_t s);
 // the stage of step t+1 beside the split merge of step t
 hipError_t launch_la_stage_combine(const StageArgs& ga, const AttendArgs& aa, hipStream_t s);

@@ -335,3 +335,40 @@ def test_lookahead_batched_topk_matches_sync_over_16_steps():
                 assert np.array_equal(got_p[l, b, :m], phys[l, b, :m]), f"step {t} layer {l} seq {b}"
         assert np.array_equal(bits(dw.out.cpu().numpy()), out), f"step {t}: lookahead vs sync bits"
     say(f"  batched top-512: lookahead = sync over {n} steps")
+
+
+@pytest.mark.parametrize("mode", ["topk", "threshold"])
+def test_lookahead_candidate_guess_fallback(mode):
+    """The score launch lists candidates from a bin guessed by the previous
+    step's final selection.  Head weights scaled by 1/16 or 16 between steps move
+    the boundary bin by 16 bins either way: a guess above the new boundary, or
+    one that lists too many entries, must fall back to the exact scan.  Rows
+    and output bits equal the synchronous steps' throughout."""
+    wl = L.WORKLOADS["thresh_256k"]
+    if mode == "topk":
+        wl = wl.replace(mode="topk", k=512)
+    n = 8
+    dw = DeviceWorkload(wl)
+    dw.make_steps(n + 2)
+    for t, f in enumerate([1.0, 1 / 16, 1.0, 16.0, 16.0, 1 / 16, 1.0, 1.0, 16.0, 1.0]):
+        dw.w_idx[t] *= f
+    sync = []
+    for t in range(n):
+        dw.step(t)
+        torch.cuda.synchronize()
+        sync.append((bits(dw.out.cpu().numpy()).copy(), dw.phys.cpu().numpy().copy(), dw.n_rows.cpu().numpy().copy()))
+    dw.reset_pools()
+    dw.lookahead_prime(0)
+    for t in range(n):
+        cur = lsa.lookahead_buffer(dw.ctx)
+        dw.lookahead_step(t)
+        torch.cuda.synchronize()
+        out, phys, nrows = sync[t]
+        assert np.array_equal(dw.n_rows2[cur].cpu().numpy(), nrows), f"step {t}: row counts"
+        got_p = dw.phys2[cur].cpu().numpy()
+        for l in range(wl.n_layers):
+            for b in range(wl.batch):
+                m = int(nrows[l, b])
+                assert np.array_equal(got_p[l, b, :m], phys[l, b, :m]), f"step {t} layer {l} seq {b}"
+        assert np.array_equal(bits(dw.out.cpu().numpy()), out), f"step {t}: lookahead vs sync bits"
+    say(f"  {mode}: guessed candidate lists with scaled steps = sync over {n} steps")
