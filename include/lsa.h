@@ -448,10 +448,10 @@ lsa_status lsa_decode_attend(lsa_ctx* ctx, const lsa_step_desc* step, lsa_stream
  *   lsa_lookahead_step(ctx, d, s): for the current step, copy its missed rows
  *     into their slots and attend d->q_attn over its staged rows (writing
  *     d->out); for the NEXT step, score d->q_idx / d->w_idx (the indexer query
- *     that predicts it), select and stage.  Four launches on s: the row copy
- *     beside the key scan (and the selection histogram), the selection's
- *     candidate pass, the attention splits beside the selection's final pass,
- *     the attention merge beside the stage.
+ *     that predicts it), select and stage.  Three launches on s: the row copy
+ *     beside the key scan (which also builds the selection's histogram and
+ *     candidate lists), the attention splits beside the selection's final
+ *     pass, the attention merge beside the stage.
  * The outputs equal lsa_decode_step's when step t's call carries the indexer
  * query of step t+1: every kernel body is the same, and the stage of step t+1
  * runs after step t's attention has finished.

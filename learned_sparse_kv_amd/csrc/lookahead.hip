@@ -5,13 +5,13 @@
 // limitations / future work: the reference scores synchronously, and
 // overlapping the global scoring is listed as the way to remove that cost.
 //
-// One lookahead step t runs on a single stream as four launches:
+// One lookahead step t runs on a single stream as three launches:
 //   A  fm_score of step t+1, each workgroup with one extra wave that copies a
 //      share of step t's missed rows into their slots (the score waves also
-//      build the select's histogram)
+//      build the select's histogram and write its candidate lists)
 //   (B select histogram of step t+1, only when A cannot: segments that are not
 //      one per sequence, or fewer score workgroups than sequences)
-//   C  select collect of step t+1
+//   (C select collect of step t+1, only when A did not write the lists)
 //   D  [attention splits of step t                    | final select of step t+1]
 //   E  [stage of step t+1 (LRU; records its misses)   | split merge of step t]
 // Design (gfx950): independent work of two steps shares one launch
