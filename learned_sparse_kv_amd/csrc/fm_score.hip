@@ -250,6 +250,9 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
         const int b0 = cand_blocks(a, bx, gx, co->nblk, &c_seq, &nb);
         c_guess = co->guess[c_seq];
         c_tkey = co->thr ? order_key(co->t_f) : 0u;
+        // threshold mode lists every passing entry: the guess goes no higher
+        // than the threshold's own bin
+        if (co->thr && (int)(c_tkey >> kSelShift) < c_guess) c_guess = (int)(c_tkey >> kSelShift);
         constexpr int kTpb = kSelColBlk / kTile;    // tiles per block
         const int tw = nb * (kTpb / kWaves);        // tiles per wave: nb sub-blocks
         const int ts = a.tile_start[c_seq], te = a.tile_start[c_seq + 1];
@@ -540,6 +543,27 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
     }
 }
 
+// The end of a workgroup's score waves that count their scores into s_hist
+// (HIST): each counts itself finished on s_done (zero on entry) after its LDS
+// adds, and the last one adds the non-zero bins to its sequence's histogram
+// (with several sequences the grid is a multiple of the batch and every wave
+// of a workgroup scores one sequence).
+__device__ inline void score_hist_flush(const ScoreArgs& a, const uint32_t* s_hist, int* s_done, uint32_t* hist) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    const int lane = threadIdx.x & 63;
+    int prev = 0;
+    if (lane == 0) prev = atomicAdd(s_done, 1);
+    prev = __shfl(prev, 0, 64);
+    if (prev != kWaves - 1) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const int seg = a.batch > 1 ? (int)(blockIdx.x / (gridDim.x / a.batch)) : 0;
+    uint32_t* gh = hist + (size_t)seg * kSelBins;
+    for (int i = lane; i < kSelBins; i += 64) {
+        const uint32_t c = s_hist[i];
+        if (c) atomicAdd(&gh[i], c);
+    }
+}
+
 // workgroups per CU: two for the one-byte and fp4 formats (registers and LDS
 // fit two), else one
 template <typename KT>
@@ -548,6 +572,22 @@ constexpr int kWgPerCu = KeyFmt<KT>::kBits <= 8 ? 2 : 1;
 template <int DK, typename KT>
 __global__ __launch_bounds__(kThreads, kWgPerCu<KT>) void fm_score_kernel(const ScoreArgs a) {
     fm_score_body<DK, KT>(a, blockIdx.x, gridDim.x);
+}
+
+// fm_score that also writes the select's candidate lists (one workgroup per
+// CU, as the lists' schedule assumes)
+template <int DK, typename KT>
+__global__ __launch_bounds__(kThreads, 1) void fm_score_lists_kernel(const ScoreArgs a, const ScoreHistArgs h) {
+    const CandOut co{h.blk_idx, h.blk_key, h.blk_count, h.guess, h.nblk, h.mode == LSA_SELECT_THRESHOLD ? 1 : 0, h.t_f};
+    fm_score_body<DK, KT, false, true>(a, blockIdx.x, gridDim.x, nullptr, h.mode, h.t_f, &co);
+}
+
+template <int DK, typename KT>
+hipError_t launch_lists_t(const ScoreArgs& a, const ScoreHistArgs& h, int n_cu, hipStream_t s) {
+    const int grid = score_lists_grid(a, n_cu);
+    if (grid < a.batch || grid < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((fm_score_lists_kernel<DK, KT>), dim3(grid), dim3(kThreads), 0, s, a, h);
+    return hipGetLastError();
 }
 
 template <int DK, typename KT>
@@ -567,6 +607,28 @@ using namespace score_k;
 }  // namespace
 
 #ifndef LSA_BODIES_ONLY
+int score_lists_grid(const ScoreArgs& a, int n_cu) {
+    int grid = (a.tile_start[a.batch] + score_k::kWaves - 1) / score_k::kWaves;
+    if (grid > n_cu) grid = n_cu;
+    if (grid < 1) grid = 1;
+    if (a.batch > 1) grid -= grid % a.batch;
+    return grid;
+}
+
+hipError_t launch_fm_score_lists(const ScoreArgs& a, const ScoreHistArgs& h, int key_dtype, int dk, int n_cu,
+                                 hipStream_t s) {
+    if (key_dtype == LSA_F32) {
+        if (dk == 32) return launch_lists_t<32, float>(a, h, n_cu, s);
+        if (dk == 64) return launch_lists_t<64, float>(a, h, n_cu, s);
+        if (dk == 128) return launch_lists_t<128, float>(a, h, n_cu, s);
+    } else if (key_dtype == LSA_BF16) {
+        if (dk == 32) return launch_lists_t<32, uint16_t>(a, h, n_cu, s);
+        if (dk == 64) return launch_lists_t<64, uint16_t>(a, h, n_cu, s);
+        if (dk == 128) return launch_lists_t<128, uint16_t>(a, h, n_cu, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, hipStream_t s) {
     if (key_dtype == LSA_F32) {
         if (dk == 32) return launch_t<32, float>(a, n_cu, s);

@@ -44,7 +44,7 @@ constexpr int kNT = 1024;
 constexpr int kNW = kNT / 64;
 constexpr int kBlk = 4096;          // entries per block of the histogram kernel
 constexpr int kColBlk = kSelColBlk;   // entries per block of the collect kernel
-constexpr int kMaxBlocks = 4096;    // collect blocks whose lists the final kernel gathers in LDS
+constexpr int kMaxBlocks = kSelFinalBlocks;   // collect blocks whose lists the final kernel gathers in LDS
 constexpr int kBlkThreads = 256;
 
 struct KthShared {
@@ -415,8 +415,8 @@ __global__ __launch_bounds__(kBlkThreads) void sel_collect_kernel(const SelectAr
 // over the whole segment, then an index-ordered compaction.  Used when the
 // boundary bucket overflows the candidate list.
 template <int NT>
-__device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid, int K, KthShared& sh,
-                              int32_t* out_sel) {
+__device__ uint32_t stream_select(const SelectArgs& a, const float* sc, int n_valid, int K, KthShared& sh,
+                                  int32_t* out_sel) {
     const int tid = threadIdx.x;
     uint32_t prefix = 0, mask = 0;
     int rem = K;
@@ -469,6 +469,7 @@ __device__ void stream_select(const SelectArgs& a, const float* sc, int n_valid,
         run_eq += tot_eq;
         run_out += tot_take;
     }
+    return T;
 }
 
 // One workgroup of NT threads per segment: gathers the blocks' kept entries (global index
@@ -505,21 +506,31 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
         c_own[q] = (q < PB && bi < nb) ? cnt[bi] : 0;
         mine += c_own[q];
     }
-    const int guess = a.pre ? a.guess_in[seg] : 0;
-    find_boundary<NT>(g, a.k, sh.scan, s_b);
-    const int total = s_b[2];
-    const int K = total < a.k ? total : a.k;
-    const int bstar = s_b[0];
-    const int above = s_b[1];
     int32_t* out_sel = a.sel + (int64_t)seg * a.stride;
-
-    // block offsets
-    if (K == 0) mine = 0;
+    // pre: the lists hold every entry of bin >= the guess (every passing entry
+    // in threshold mode), so the boundary bin b* comes from the listed entries
+    // themselves; otherwise from the segment's histogram
+    const bool pre = a.pre != 0;
+    int K = 0, bstar = 0, above = 0, gn = 0;
+    if (!pre) {
+        find_boundary<NT>(g, a.k, sh.scan, s_b);
+        const int total = s_b[2];
+        K = total < a.k ? total : a.k;
+        bstar = s_b[0];
+        above = s_b[1];
+        if (K == 0) mine = 0;
+    }
+    // block offsets; n_keep = listed entries
     int n_keep;
     int off = block_excl_scan<NT>(mine, sh.scan, &n_keep);
-    // lists written by the score launch hold every entry of b* and above only
-    // when their first bin is at most b*
-    if (K > 0 && n_keep <= kSelKeepCap && nb <= MAXB && guess <= bstar) {
+    if (pre) {
+        const int nv = seg_valid(a, seg);
+        const int avail = a.mode == LSA_SELECT_THRESHOLD ? n_keep : nv;
+        K = avail < a.k ? avail : a.k;
+    }
+    // with lists from the score launch the guess held if they list K entries
+    const bool in_lds = K > 0 && n_keep <= kSelKeepCap && nb <= MAXB && (!pre || n_keep >= K);
+    if (in_lds) {
         // every block's first position in the gathered list
 #pragma unroll
         for (int q = 0; q < kPB; ++q) {
@@ -553,47 +564,63 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
         for (int i = 0; i < kGather; ++i) {
             const int p = tid + i * NT;
             if (p < n_keep) {
-                // lists from the score launch are unmarked: mark the entries of b*
-                const bool mark = a.pre && (int)(g_key[i] >> kSelShift) == bstar;
-                s_idx[p] = g_idx[i] | (mark ? (int32_t)0x80000000 : 0);
+                s_idx[p] = g_idx[i];
                 s_key[p] = g_key[i];
             }
         }
         __syncthreads();
-        if (a.pre && guess < bstar) {
-            // lists that start below b*: keep the entries of b* and above, in
-            // order; thread t moves [t*E3, t*E3 + E3) once every thread has read its own
-            constexpr int kE3 = (kSelKeepCap + NT - 1) / NT;
-            const int E3 = (n_keep + NT - 1) / NT;
-            int32_t r_idx[kE3];
-            uint32_t r_key[kE3];
-            int c = 0;
+        if (pre) {
+            // b* and the count above it from a histogram of the listed bins
+            for (int i = tid; i < kSelBins; i += NT) s_h2[i] = 0u;
+            __syncthreads();
+            for (int p = tid; p < n_keep; p += NT) atomicAdd(&s_h2[s_key[p] >> kSelShift], 1u);
+            __syncthreads();
+            find_boundary<NT>(s_h2, K, sh.scan, s_b);
+            bstar = s_b[0];
+            above = s_b[1];
+            const int at_b = above + (int)s_h2[bstar];
+            // the next step's guess: b*, or one bin lower when b* and above hold
+            // fewer than 1.5 times the entries chosen
+            gn = (2 * at_b < 3 * K && bstar > 0) ? bstar - 1 : bstar;
+            if (at_b == n_keep) {
+                // nothing listed below b*: mark the entries of b* in place
+                for (int p = tid; p < n_keep; p += NT)
+                    if ((int)(s_key[p] >> kSelShift) == bstar) s_idx[p] |= (int32_t)0x80000000;
+            } else {
+                // keep the entries of b* and above, in order, marking those of
+                // b*; thread t moves [t*E3, t*E3 + E3) once every thread has read its own
+                constexpr int kE3 = (kSelKeepCap + NT - 1) / NT;
+                const int E3 = (n_keep + NT - 1) / NT;
+                int32_t r_idx[kE3];
+                uint32_t r_key[kE3];
+                int c = 0;
 #pragma unroll
-            for (int e = 0; e < kE3; ++e) {
-                const int p = tid * E3 + e;
-                const bool in = e < E3 && p < n_keep;
-                r_idx[e] = in ? s_idx[p] : 0;
-                r_key[e] = in ? s_key[p] : 0u;
-                const int bin = (int)(r_key[e] >> kSelShift);
-                if (in && bin >= bstar) {
-                    r_idx[e] |= bin == bstar ? (int32_t)0x80000000 : 0;
-                    ++c;
-                } else {
-                    r_idx[e] = 0x7FFFFFFF;   // dropped
+                for (int e = 0; e < kE3; ++e) {
+                    const int p = tid * E3 + e;
+                    const bool in = e < E3 && p < n_keep;
+                    r_idx[e] = in ? s_idx[p] : 0;
+                    r_key[e] = in ? s_key[p] : 0u;
+                    const int bin = (int)(r_key[e] >> kSelShift);
+                    if (in && bin >= bstar) {
+                        r_idx[e] |= bin == bstar ? (int32_t)0x80000000 : 0;
+                        ++c;
+                    } else {
+                        r_idx[e] = 0x7FFFFFFF;   // dropped
+                    }
+                }
+                int kept;
+                int pos = block_excl_scan<NT>(c, sh.scan, &kept);
+                __syncthreads();   // every entry is in registers before any moves
+#pragma unroll
+                for (int e = 0; e < kE3; ++e) {
+                    if (r_idx[e] != 0x7FFFFFFF) {
+                        s_idx[pos] = r_idx[e];
+                        s_key[pos] = r_key[e];
+                        ++pos;
+                    }
                 }
             }
-            int kept;
-            int pos = block_excl_scan<NT>(c, sh.scan, &kept);
-            __syncthreads();   // every entry is in registers before any moves
-#pragma unroll
-            for (int e = 0; e < kE3; ++e) {
-                if (r_idx[e] != 0x7FFFFFFF) {
-                    s_idx[pos] = r_idx[e];
-                    s_key[pos] = r_key[e];
-                    ++pos;
-                }
-            }
-            n_keep = kept;
+            n_keep = at_b;
             __syncthreads();
         }
         // bits 20..0 of the candidates' keys (bucket b* fixes the rest): a radix
@@ -690,6 +717,12 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
                 ++n_eq;
             }
         }
+    } else if (pre && K > 0) {
+        // the guess failed (too few listed, or too many): the exact scan; the
+        // next step's lists start one bin below this step's K-th key
+        const uint32_t T = stream_select<NT>(a, a.scores + (int64_t)seg * a.n_keys, seg_valid(a, seg), K, sh, out_sel);
+        const int bt = (int)(T >> kSelShift);
+        gn = bt > 0 ? bt - 1 : 0;
     } else if (K > 0) {
         stream_select<NT>(a, a.scores + (int64_t)seg * a.n_keys, seg_valid(a, seg), K, sh, out_sel);
     }
@@ -697,20 +730,21 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
     if (tid == 0) {
         a.count[seg] = K;
         if (a.guess_out) {
-            // the next step's lists start at b* when its entries and those above
-            // hold half as many again as are chosen (a small drift keeps b*),
-            // else one bin lower if that fits half the LDS list; no entry: from 0
-            int gn = 0;
-            if (K > 0) {
+            if (!pre && K > 0) {
+                // from the histogram: b*, or one bin lower when b* and above hold
+                // fewer than 1.5 times the entries chosen and the lower bin
+                // keeps the lists within half the LDS list
                 const int at_b = above + (int)g[bstar];
                 gn = bstar;
                 if (2 * at_b < 3 * K && bstar > 0 && at_b + (int)g[bstar - 1] <= kSelKeepCap / 2) gn = bstar - 1;
             }
-            a.guess_out[seg] = gn;
+            a.guess_out[seg] = gn;   // no entry chosen: the lists start at bin 0
         }
     }
-    __syncthreads();
-    for (int i = tid; i < kSelBins; i += NT) g[i] = 0u;
+    if (!pre) {
+        __syncthreads();
+        for (int i = tid; i < kSelBins; i += NT) g[i] = 0u;
+    }
 }
 
 __global__ __launch_bounds__(kNT) void sel_final_kernel(const SelectArgs a) {

@@ -110,29 +110,14 @@ __device__ inline void copy_wave(const CopyArgs& ca, const int wg, const int n_w
     }
 }
 
-// The select's histogram, built by the score launch when the step has one
-// segment per sequence: hist [n_seg][kSelBins], zero on entry; mode and t_f as
-// in the select.  With blk_count set the score waves also write the select's
-// candidate lists (score_k::CandOut), which the final selection takes in place
-// of its collect pass.
-struct HistArgs {
-    uint32_t* hist;
-    int32_t mode;
-    float t_f;
-    int32_t* blk_count;         // [n_seg][4 * nblk]
-    int32_t* blk_idx;           // [n_seg][4 * nblk][kCandSub]
-    uint32_t* blk_key;          // [n_seg][4 * nblk][kCandSub]
-    const int32_t* guess;       // [n_seg]
-    int32_t nblk;               // 1024-entry blocks per sequence
-};
-
 // Workgroup = 4 score waves (fm_score) + 1 copy wave.  With HIST the score
 // waves also count their scores into an LDS histogram; the last of them to
 // finish adds it to the segment's histogram (its PCIe-bound copy wave
-// usually ends later, so the flush costs no time).
+// usually ends later, so the flush costs no time).  With CAND they also write
+// the select's candidate lists (score_k::CandOut).
 template <int DK, typename KT, bool HIST, bool CAND>
-__global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, const CopyArgs ca, const HistArgs ha) {
-    static_assert(HIST || !CAND, "the candidate lists come with the histogram");
+__global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, const CopyArgs ca, const ScoreHistArgs ha) {
+    static_assert(!(HIST && CAND), "the lists replace the histogram");
     __shared__ int s_pre[kCopyMaxSegs];
     __shared__ uint32_t s_hist[HIST ? kSelBins : 1];
     __shared__ int s_done;
@@ -149,25 +134,7 @@ __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, cons
     const score_k::CandOut co{ha.blk_idx, ha.blk_key, ha.blk_count, ha.guess, ha.nblk,
                               ha.mode == LSA_SELECT_THRESHOLD ? 1 : 0, ha.t_f};
     score_k::fm_score_body<DK, KT, HIST, CAND>(sa, blockIdx.x, gridDim.x, s_hist, ha.mode, ha.t_f, &co);
-    if (HIST) {
-        // every score wave's LDS adds are done before it counts itself finished
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        const int lane = threadIdx.x & 63;
-        int prev = 0;
-        if (lane == 0) prev = atomicAdd(&s_done, 1);
-        prev = __shfl(prev, 0, 64);
-        if (prev == score_k::kWaves - 1) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            // several sequences: the grid is a multiple of the batch, so all waves of
-            // a workgroup score the same sequence (fm_score's per-sequence groups)
-            const int seg = sa.batch > 1 ? blockIdx.x / (gridDim.x / sa.batch) : 0;
-            uint32_t* gh = ha.hist + (size_t)seg * kSelBins;
-            for (int i = lane; i < kSelBins; i += 64) {
-                const uint32_t c = s_hist[i];
-                if (c) atomicAdd(&gh[i], c);
-            }
-        }
-    }
+    if (HIST) score_k::score_hist_flush(sa, s_hist, &s_done, ha.hist);
 }
 
 // Launch D: the attention splits of step t beside the final selection of step
@@ -212,11 +179,11 @@ int la_score_grid(const ScoreArgs& sa, bool hist, int n_cu) {
 }
 
 template <int DK, typename KT>
-hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, const HistArgs& ha, int n_cu, hipStream_t s) {
-    const int grid = la_score_grid(sa, ha.hist != nullptr, n_cu);
+hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, const ScoreHistArgs& ha, int n_cu, hipStream_t s) {
+    const int grid = la_score_grid(sa, ha.hist != nullptr || ha.blk_count != nullptr, n_cu);
     if (grid < 1) return hipErrorInvalidValue;
     if (ha.blk_count)
-        hipLaunchKernelGGL((la_score_copy<DK, KT, true, true>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+        hipLaunchKernelGGL((la_score_copy<DK, KT, false, true>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
     else if (ha.hist)
         hipLaunchKernelGGL((la_score_copy<DK, KT, true, false>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
     else
@@ -234,7 +201,7 @@ hipError_t launch_d(const AttendArgs& aa, const SelectArgs& se, bool hist_done, 
         // hist (unless the score launch built it) and collect, then the final
         // selection beside the attention splits
         hipError_t e = hipSuccess;
-        if (!hist_done) {
+        if (!hist_done && !se.pre) {
             hipLaunchKernelGGL(select_k::sel_hist_kernel,
                                dim3((unsigned)((se.n_keys + select_k::kBlk - 1) / select_k::kBlk), se.n_seg),
                                dim3(select_k::kBlkThreads), 0, s, se);
@@ -278,15 +245,14 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const CopyArgs& ca, int ke
     if (ca.n_seg < 0 || ca.n_seg > kCopyMaxSegs || (ca.n_seg && (!ca.miss || !ca.n_miss)) || ca.row_bytes % 16 != 0 ||
         cpr < 1 || (cpr & (cpr - 1)) != 0)
         return hipErrorInvalidValue;
-    HistArgs ha{};
+    ScoreHistArgs ha{};
     *lists = false;
     if (hist_for) {
         if (!la_fused_hist(sa, *hist_for, n_cu)) return hipErrorInvalidValue;
-        ha.hist = hist_for->hist;
         ha.mode = hist_for->mode;
         ha.t_f = hist_for->t_f;
-        // the candidate lists too, when their sub-blocks fit the final
-        // selection's block table
+        // the candidate lists in place of the histogram when their sub-blocks
+        // fit the final selection's block table
         const int G = la_score_grid(sa, true, n_cu) / sa.batch;
         if (guess && G > 0 && hist_for->nblk * score_k::kWaves <= kFinMaxBlocks) {
             ha.blk_count = hist_for->blk_count;
@@ -295,6 +261,8 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const CopyArgs& ca, int ke
             ha.guess = guess;
             ha.nblk = hist_for->nblk;
             *lists = true;
+        } else {
+            ha.hist = hist_for->hist;
         }
     }
     if (key_dtype == LSA_F32) {

@@ -1206,15 +1206,45 @@ void plan_use_buffer(StepPlan* P, int buf) {
     }
 }
 
+// Whether the score launch can write the select's histogram and candidate
+// lists: the long-segment select with one segment per sequence, fp32 or bf16
+// keys, a workgroup per sequence at least, and list blocks that fit the final
+// selection's table.
+bool score_lists_fit(const ScoreArgs& sa, const SelectArgs& se, lsa_dtype key_dtype, int n_cu) {
+    return (key_dtype == LSA_F32 || key_dtype == LSA_BF16) && se.path == 1 && se.n_seg == sa.batch &&
+           sa.tile_start[sa.batch] > 0 && score_lists_grid(sa, n_cu) >= sa.batch && se.nblk * 4 <= kSelFinalBlocks;
+}
+
 lsa_status launch_predict(lsa_ctx* ctx, const StepPlan& P, const lsa_step_desc* d, hipStream_t s, bool fetch) {
-    {
-        Timed t(ctx, LSA_K_SCORE, s);
-        HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s));
-        t.end();
-    }
-    {
+    if (score_lists_fit(P.sa, P.se, d->key_dtype, ctx->n_cu)) {
+        // score, histogram and candidate lists in one launch (the lists from
+        // the bin the previous step's final selection left), then the final
+        // selection, which checks that bin against this step's boundary
+        const ScoreHistArgs h{nullptr, P.se.mode, P.se.t_f, P.se.blk_count, P.se.blk_idx, P.se.blk_key,
+                              ctx->sel_guess, P.se.nblk};
+        {
+            Timed t(ctx, LSA_K_SCORE, s);
+            HIPTRY(launch_fm_score_lists(P.sa, h, d->key_dtype, d->dk, ctx->n_cu, s));
+            t.end();
+        }
+        SelectArgs se = P.se;
+        se.pre = 1;
+        se.nblk = P.se.nblk * 4;
+        se.blk_stride = kSelColBlk / 4;
+        se.guess_out = ctx->sel_guess;
         Timed t(ctx, LSA_K_SELECT, s);
-        HIPTRY(launch_fm_select(P.se, s));
+        HIPTRY(launch_fm_select_final(se, s));
+        t.end();
+    } else {
+        {
+            Timed t(ctx, LSA_K_SCORE, s);
+            HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s));
+            t.end();
+        }
+        SelectArgs se = P.se;
+        se.guess_out = ctx->sel_guess;
+        Timed t(ctx, LSA_K_SELECT, s);
+        HIPTRY(launch_fm_select(se, s));
         t.end();
     }
     for (int g = 0; g < P.n_groups; ++g) {
@@ -1311,8 +1341,6 @@ lsa_status lsa_lookahead_prime(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_
     ctx->la_cur = 0;
     ctx->la_fetched = false;
     plan_use_buffer(&P, 0);
-    // the final selection leaves the first step's candidate-list guess
-    P.se.guess_out = ctx->sel_guess;
     // the first step's rows are staged; its lookahead step copies the missed ones
     return launch_predict(ctx, P, d, (hipStream_t)stream, false);
 }
@@ -1351,7 +1379,6 @@ lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t
             se.nblk = P.se.nblk * 4;
             se.blk_stride = kSelColBlk / 4;
         }
-        se.guess_in = ctx->sel_guess;
         se.guess_out = ctx->sel_guess;
         HIPTRY(launch_la_select_split(P.aa[0], se, fuse_hist, s));
         for (int g = 1; g < P.n_groups; ++g) HIPTRY(launch_attend_splits(P.aa[g], s));

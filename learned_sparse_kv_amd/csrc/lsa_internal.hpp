@@ -100,6 +100,7 @@ constexpr int kSelBins = 2048;        // 11-bit key histogram of the long-segmen
 constexpr int kSelShift = 21;         // bin = order_key(score) >> kSelShift
 constexpr int kSelKeepCap = 8192;     // entries (above + in the boundary bucket) resolved in LDS
 constexpr int kSelColBlk = 1024;      // entries per candidate list block of the histogram path
+constexpr int kSelFinalBlocks = 4096; // list blocks per segment whose starts the final selection keeps in LDS
 constexpr int kSelSingle = 32768;     // segments up to this length use one workgroup
 // sparse layers per stage / attention launch: a step with more layers issues
 // these launches per group of this many layers (their arguments stay small)
@@ -130,6 +131,27 @@ struct ScoreArgs {
     int32_t tile_start[LSA_MAX_BATCH + 1];   // prefix of 32-key tiles per sequence
 };
 hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, hipStream_t s);
+// What the score waves write for the select as they score: the histogram
+// (hist set: [n_seg][kSelBins], zero on entry), or the candidate lists
+// (blk_count set; see the select's pre = 1): per 256-entry sub-block the
+// entries of bin >= guess[seq] (in threshold mode no higher than the
+// threshold's bin) passing the threshold, in index order, with their order keys.
+struct ScoreHistArgs {
+    uint32_t* hist;
+    int32_t mode;
+    float t_f;
+    int32_t* blk_count;         // [n_seg][4 * nblk]
+    int32_t* blk_idx;           // [n_seg][4 * nblk][256]
+    uint32_t* blk_key;          // [n_seg][4 * nblk][256]
+    const int32_t* guess;       // [n_seg]
+    int32_t nblk;               // 1024-entry blocks per sequence
+};
+// the grid of the list-writing score launch (one workgroup per CU at most,
+// a multiple of the batch)
+int score_lists_grid(const ScoreArgs& a, int n_cu);
+// fm_score with the select's candidate lists: fp32 and bf16 keys
+hipError_t launch_fm_score_lists(const ScoreArgs& a, const ScoreHistArgs& h, int key_dtype, int dk, int n_cu,
+                                 hipStream_t s);
 
 struct SelectArgs {
     const float* scores;
@@ -150,14 +172,15 @@ struct SelectArgs {
     int32_t* blk_idx;           // [n_seg][nblk][1024] kept indices (top bit: boundary bucket)
     uint32_t* blk_key;          // [n_seg][nblk][1024] their keys
     // pre = 1: the score launch wrote the block lists: every entry of bin
-    // >= guess_in[seg] (passing the threshold), unmarked, in index order; the
-    // final selection checks guess_in[seg] <= b* and scans the scores otherwise
+    // >= guess (passing the threshold), unmarked, in index order, and no
+    // histogram; the final selection takes b* from the listed entries when they
+    // number at least the K chosen, and scans the scores otherwise
     int32_t pre;
     int32_t blk_stride;         // entries per block list (0: kSelColBlk)
-    const int32_t* guess_in;    // [n_seg]
     // when set, the final selection writes the bin the next step's lists start
     // at: this step's b*, or one bin lower when b* and above hold fewer than
-    // 1.5 times the entries chosen (and the lower bin keeps the lists short)
+    // 1.5 times the entries chosen (and, from a histogram, the lower bin keeps
+    // the lists short)
     int32_t* guess_out;         // [n_seg]
 };
 // Fills the shape fields; returns false when out of range.  *zero_bytes is the

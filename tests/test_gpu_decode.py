@@ -296,3 +296,28 @@ def test_decode_41_layer_stack():
     selection per step: stages and attentions run in groups of layers; every
     layer's rows and output equal the oracle's."""
     run_decode(L.WORKLOADS["stack_64k_41"], 3)
+
+
+@pytest.mark.parametrize("mode", ["topk", "threshold"])
+def test_sync_candidate_guess_fallback(mode):
+    """The synchronous step's score launch also lists candidates from a bin the
+    previous final selection guessed.  Head weights scaled by 1/16 or 16
+    between steps move the boundary 16 bins either way, so the guess fails
+    both ways (and the first step has none); every step still equals the
+    oracle: selected sets, rows and outputs."""
+    wl = L.WORKLOADS["thresh_256k"]
+    if mode == "topk":
+        wl = wl.replace(mode="topk", k=512)
+    n = 8
+    dw = DeviceWorkload(wl, keep_host=True)
+    dw.make_steps(n)
+    for t, f in enumerate([1.0, 1 / 16, 1.0, 16.0, 16.0, 1 / 16, 1.0, 1.0]):
+        dw.w_idx_np[t] *= np.float32(f)
+        dw.w_idx[t] *= f
+    ref = oracle.DecodeState(wl, dw.windows, dw.stores)
+    for t in range(n):
+        want = ref.step(dw.keys_np, dw.q_idx_np[t], dw.w_idx_np[t], dw.q_attn_np[t])
+        dw.step(t)
+        torch.cuda.synchronize()
+        check_step(t, wl, dw, want)
+    say(f"  {mode}: synchronous steps with failing guesses = oracle over {n} steps")
