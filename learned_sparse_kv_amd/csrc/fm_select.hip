@@ -128,9 +128,9 @@ struct KthWide {
 // bins, so the histogram atomics serialised).  The keys of its boundary bin
 // are then compacted into LDS (when they fit) and the last two passes run over
 // them alone.
+// key[e] == 0 marks an entry that takes no part (no float maps to order key 0)
 template <int E>
-__device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int K, KthWide& sh,
-                          uint32_t* T_out, int* need_eq_out) {
+__device__ void block_kth(const uint32_t (&key)[E], int K, KthWide& sh, uint32_t* T_out, int* need_eq_out) {
     const int tid = threadIdx.x;
     for (int i = tid; i < kWideBins; i += kNT) sh.hist[i] = 0u;
     __syncthreads();
@@ -140,7 +140,7 @@ __device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int 
     // all-equal keys are the worst case, about twice as slow as pre-aggregated
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        if (valid[e]) atomicAdd(&sh.hist[key[e] >> 20], 1u);
+        if ((key[e] != 0u)) atomicAdd(&sh.hist[key[e] >> 20], 1u);
     __syncthreads();
     int bin, above;
     find_bin<kWideBins, kNT>(sh.hist, K, sh.scan, sh.out, &bin, &above);
@@ -152,12 +152,12 @@ __device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int 
     if (c0 <= kWideCand) {
         int mine = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) mine += (valid[e] && (key[e] >> 20) == d0) ? 1 : 0;
+        for (int e = 0; e < E; ++e) mine += ((key[e] != 0u) && (key[e] >> 20) == d0) ? 1 : 0;
         int tot;
         int off = block_excl_scan<kNT>(mine, sh.scan, &tot);
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            if (valid[e] && (key[e] >> 20) == d0) sh.cand[off++] = key[e] & 0xFFFFFu;
+            if ((key[e] != 0u) && (key[e] >> 20) == d0) sh.cand[off++] = key[e] & 0xFFFFFu;
         for (int i = tid; i < 1024; i += kNT) sh.hist[i] = 0u;
         __syncthreads();
         for (int p0 = 0; p0 < c0; p0 += kNT) {
@@ -182,7 +182,7 @@ __device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int 
         for (int i = tid; i < 1024; i += kNT) sh.hist[i] = 0u;
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < E; ++e) hist_add(sh.hist, valid[e] && (key[e] >> 20) == d0, (key[e] >> 10) & 1023u);
+        for (int e = 0; e < E; ++e) hist_add(sh.hist, (key[e] != 0u) && (key[e] >> 20) == d0, (key[e] >> 10) & 1023u);
         __syncthreads();
         find_bin<1024, kNT>(sh.hist, rem, sh.scan, sh.out, &bin, &above);
         d1 = (uint32_t)bin;
@@ -191,7 +191,7 @@ __device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int 
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            hist_add(sh.hist, valid[e] && (key[e] >> 10) == ((d0 << 10) | d1), key[e] & 1023u);
+            hist_add(sh.hist, (key[e] != 0u) && (key[e] >> 10) == ((d0 << 10) | d1), key[e] & 1023u);
         __syncthreads();
     }
     find_bin<1024, kNT>(sh.hist, rem, sh.scan, sh.out, &bin, &above);
@@ -199,26 +199,35 @@ __device__ void block_kth(const uint32_t (&key)[E], const bool (&valid)[E], int 
     *need_eq_out = rem - above;
 }
 
-// Marks the chosen keys (all > T, plus the first need_eq equal to T in thread
-// order = index order) and returns the first output position of this thread.
+// Writes the chosen entries (all keys > T, plus the first need_eq equal to T
+// in thread order = index order) in index order; thread t holds entries
+// base .. base + E - 1.  The choice is made twice (counted, then written) so
+// that no per-entry flags stay live across the scans.
 template <int E>
-__device__ void block_choose(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t T, int need_eq,
-                             int* scan, bool (&take)[E], int* pos0) {
+__device__ void block_choose(const uint32_t (&key)[E], uint32_t T, int need_eq, int* scan, int64_t base,
+                             int32_t* out_sel, int stride) {
     int c_eq = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) c_eq += (valid[e] && key[e] == T) ? 1 : 0;
+    for (int e = 0; e < E; ++e) c_eq += ((key[e] != 0u) && key[e] == T) ? 1 : 0;
     int tot;
-    int r = block_excl_scan<kNT>(c_eq, scan, &tot);
-    int c_sel = 0;
+    const int r0 = block_excl_scan<kNT>(c_eq, scan, &tot);
+    int c_sel = 0, r = r0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const bool gt = valid[e] && key[e] > T;
-        const bool eq = valid[e] && key[e] == T;
-        take[e] = gt || (eq && r < need_eq);
+        const bool gt = (key[e] != 0u) && key[e] > T;
+        const bool eq = (key[e] != 0u) && key[e] == T;
+        c_sel += (gt || (eq && r < need_eq)) ? 1 : 0;
         r += eq ? 1 : 0;
-        c_sel += take[e] ? 1 : 0;
     }
-    *pos0 = block_excl_scan<kNT>(c_sel, scan, &tot);
+    int pos = block_excl_scan<kNT>(c_sel, scan, &tot);
+    r = r0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const bool gt = (key[e] != 0u) && key[e] > T;
+        const bool eq = (key[e] != 0u) && key[e] == T;
+        if ((gt || (eq && r < need_eq)) && pos < stride) out_sel[pos++] = (int32_t)(base + e);
+        r += eq ? 1 : 0;
+    }
 }
 
 template <int E>
@@ -245,8 +254,10 @@ __device__ inline void load_scores(const float* sc, int64_t base, int n_valid, f
 }
 
 // ---------------------------------------------------------------- path 0
+// two workgroups per CU (eight waves per SIMD): one's passes overlap the
+// other's score loads
 template <int E>
-__global__ __launch_bounds__(kNT) void select_single(const SelectArgs a) {
+__global__ __launch_bounds__(kNT, 8) void select_single(const SelectArgs a) {
     __shared__ KthWide sh;
     const int tid = threadIdx.x;
     const int seg = blockIdx.x;
@@ -257,12 +268,13 @@ __global__ __launch_bounds__(kNT) void select_single(const SelectArgs a) {
     float x[E];
     bool valid[E];
     load_scores<E>(sc, base, n_valid, x, valid);
+    // order key 0 (no float has it) marks entries past n_valid or below the threshold
     uint32_t key[E];
     int c_valid = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         if (a.mode == LSA_SELECT_THRESHOLD) valid[e] = valid[e] && (x[e] > a.t_f);
-        key[e] = order_key(x[e]);
+        key[e] = valid[e] ? order_key(x[e]) : 0u;
         c_valid += valid[e] ? 1 : 0;
     }
     int n_ok;
@@ -276,13 +288,8 @@ __global__ __launch_bounds__(kNT) void select_single(const SelectArgs a) {
     }
     uint32_t T;
     int need_eq;
-    block_kth<E>(key, valid, K, sh, &T, &need_eq);
-    bool take[E];
-    int pos;
-    block_choose<E>(key, valid, T, need_eq, sh.scan, take, &pos);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-        if (take[e] && pos < a.stride) out_sel[pos++] = (int32_t)(base + e);
+    block_kth<E>(key, K, sh, &T, &need_eq);
+    block_choose<E>(key, T, need_eq, sh.scan, base, out_sel, a.stride);
     for (int i = K + tid; i < a.stride; i += kNT) out_sel[i] = -1;
     if (tid == 0) a.count[seg] = K;
 }
