@@ -527,6 +527,9 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
         above = s_b[1];
         if (K == 0) mine = 0;
     }
+    // pre: the listed entries' bins are counted as they are gathered
+    if (pre)
+        for (int i = tid; i < kSelBins; i += NT) s_h2[i] = 0u;
     // block offsets; n_keep = listed entries
     int n_keep;
     int off = block_excl_scan<NT>(mine, sh.scan, &n_keep);
@@ -573,15 +576,13 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
             if (p < n_keep) {
                 s_idx[p] = g_idx[i];
                 s_key[p] = g_key[i];
+                if (pre) atomicAdd(&s_h2[g_key[i] >> kSelShift], 1u);
             }
         }
         __syncthreads();
         if (pre) {
-            // b* and the count above it from a histogram of the listed bins
-            for (int i = tid; i < kSelBins; i += NT) s_h2[i] = 0u;
-            __syncthreads();
-            for (int p = tid; p < n_keep; p += NT) atomicAdd(&s_h2[s_key[p] >> kSelShift], 1u);
-            __syncthreads();
+            // b* and the count above it from the listed bins' histogram; entries
+            // listed below b* stay in place (every later pass tests the bin)
             find_boundary<NT>(s_h2, K, sh.scan, s_b);
             bstar = s_b[0];
             above = s_b[1];
@@ -589,46 +590,7 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
             // the next step's guess: b*, or one bin lower when b* and above hold
             // fewer than 1.5 times the entries chosen
             gn = (2 * at_b < 3 * K && bstar > 0) ? bstar - 1 : bstar;
-            if (at_b == n_keep) {
-                // nothing listed below b*: mark the entries of b* in place
-                for (int p = tid; p < n_keep; p += NT)
-                    if ((int)(s_key[p] >> kSelShift) == bstar) s_idx[p] |= (int32_t)0x80000000;
-            } else {
-                // keep the entries of b* and above, in order, marking those of
-                // b*; thread t moves [t*E3, t*E3 + E3) once every thread has read its own
-                constexpr int kE3 = (kSelKeepCap + NT - 1) / NT;
-                const int E3 = (n_keep + NT - 1) / NT;
-                int32_t r_idx[kE3];
-                uint32_t r_key[kE3];
-                int c = 0;
-#pragma unroll
-                for (int e = 0; e < kE3; ++e) {
-                    const int p = tid * E3 + e;
-                    const bool in = e < E3 && p < n_keep;
-                    r_idx[e] = in ? s_idx[p] : 0;
-                    r_key[e] = in ? s_key[p] : 0u;
-                    const int bin = (int)(r_key[e] >> kSelShift);
-                    if (in && bin >= bstar) {
-                        r_idx[e] |= bin == bstar ? (int32_t)0x80000000 : 0;
-                        ++c;
-                    } else {
-                        r_idx[e] = 0x7FFFFFFF;   // dropped
-                    }
-                }
-                int kept;
-                int pos = block_excl_scan<NT>(c, sh.scan, &kept);
-                __syncthreads();   // every entry is in registers before any moves
-#pragma unroll
-                for (int e = 0; e < kE3; ++e) {
-                    if (r_idx[e] != 0x7FFFFFFF) {
-                        s_idx[pos] = r_idx[e];
-                        s_key[pos] = r_key[e];
-                        ++pos;
-                    }
-                }
-            }
-            n_keep = at_b;
-            __syncthreads();
+            __syncthreads();   // s_h2 is read before the passes below reuse it
         }
         // bits 20..0 of the candidates' keys (bucket b* fixes the rest): a radix
         // pass over bits 20..10, then bits 9..0 of the candidates in the bin found
@@ -638,7 +600,7 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
         // (plain atomics: 2048 bins spread these digits; see select_single)
         for (int p0 = 0; p0 < n_keep; p0 += NT) {
             const int p = p0 + tid;
-            if (p < n_keep && s_idx[p] < 0) atomicAdd(&s_h2[(s_key[p] >> 10) & 2047u], 1u);
+            if (p < n_keep && (int)(s_key[p] >> kSelShift) == bstar) atomicAdd(&s_h2[(s_key[p] >> 10) & 2047u], 1u);
         }
         __syncthreads();
         int bin, bin_above;
@@ -658,7 +620,7 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
             __syncthreads();
             for (int p0 = 0; p0 < n_keep; p0 += NT) {
                 const int p = p0 + tid;
-                if (p < n_keep && s_idx[p] < 0 && ((s_key[p] >> 10) & 2047u) == d1)
+                if (p < n_keep && (int)(s_key[p] >> kSelShift) == bstar && ((s_key[p] >> 10) & 2047u) == d1)
                     s_few[atomicAdd(&s_few_n, 1)] = s_key[p] & 1023u;
             }
             __syncthreads();
@@ -683,7 +645,7 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
             __syncthreads();
             for (int p0 = 0; p0 < n_keep; p0 += NT) {
                 const int p = p0 + tid;
-                const bool act = p < n_keep && s_idx[p] < 0 && ((s_key[p] >> 10) & 2047u) == d1;
+                const bool act = p < n_keep && (int)(s_key[p] >> kSelShift) == bstar && ((s_key[p] >> 10) & 2047u) == d1;
                 hist_add(s_h2, act, p < n_keep ? s_key[p] & 1023u : 0u);
             }
             __syncthreads();
@@ -693,7 +655,8 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
         }
         const uint32_t T = ((uint32_t)bstar << kSelShift) | (d1 << 10) | low_T;
         // index-ordered placement with one scan: thread t takes entries [t*E2, t*E2 + E2);
-        // an entry above T (every entry above b*, and candidates > T) goes to
+        // an entry above T (every entry above b*, and candidates > T; listed
+        // entries below b* are below T and take no place) goes to
         // (entries above T before it) + min(candidates equal to T before it, need_eq),
         // and the first need_eq candidates equal to T fill in between
         const int E2 = (n_keep + NT - 1) / NT;   // <= kSelKeepCap / NT
@@ -704,7 +667,7 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
             if (p >= n_keep) break;
             const int32_t raw = s_idx[p];
             const uint32_t k2 = s_key[p];
-            if (raw >= 0 || k2 > T) ++c_gt;
+            if (k2 > T) ++c_gt;
             else if (k2 == T) ++c_eq;
         }
         int tot;
@@ -715,7 +678,7 @@ __device__ __forceinline__ void sel_final_body(const SelectArgs& a, const int se
             if (p >= n_keep) break;
             const int32_t raw = s_idx[p];
             const uint32_t k2 = s_key[p];
-            if (raw >= 0 || k2 > T) {
+            if (k2 > T) {
                 const int pos = n_gt + (n_eq < need_eq ? n_eq : need_eq);
                 if (pos < a.stride) out_sel[pos] = raw & 0x7FFFFFFF;
                 ++n_gt;
