@@ -374,7 +374,12 @@ lsa_status lsa_stage(lsa_pool* pool, const int32_t* sel, const int32_t* count, i
  *   phys device i32 [batch][phys_stride]; n_rows device i32 [batch], values
  *        clamped to [0, phys_stride]
  * Supported: 1 <= hq <= 16, kv_dim in {128, 256, 512}, 1 <= batch <= LSA_MAX_BATCH,
- * phys_stride <= 5120. */
+ * phys_stride <= 5120.
+ * When the whole grid of 32-row splits fits on the GPU at once, the splits
+ * merge in the same launch through counters in the context (calls on one
+ * context must not overlap, as for its workspace); a merge that waits longer
+ * than about a second (a split that never ran) writes NaN, and so does every
+ * later one-launch attention of that context. */
 lsa_status lsa_attend(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dtype,
                       int64_t kv_stride_b, int64_t kv_rows, const int32_t* phys,
                       int32_t phys_stride, const int32_t* n_rows, int32_t batch, int32_t hq,

@@ -129,6 +129,9 @@ struct lsa_ctx {
     // step's score launch lists candidates (written by each step's final
     // selection; a wrong guess only costs the exact fallback)
     int32_t* sel_guess = nullptr;   // device [LSA_MAX_BATCH]
+    // counters of the one-launch attention (AttendArgs::sync), in the same
+    // allocation; zero between launches
+    uint32_t* att_sync = nullptr;
 };
 
 namespace {
@@ -344,15 +347,16 @@ lsa_status lsa_ctx_create(lsa_ctx** out, int32_t device) {
     // the static scratch's device address, looked up once per device (only the
     // allocation-free step needs it, so a failed lookup fails only that call)
     c->scratch_status = scratch_address(device, &c->scratch);
-    if (hipMalloc(reinterpret_cast<void**>(&c->sel_guess), LSA_MAX_BATCH * sizeof(int32_t)) != hipSuccess) {
+    const size_t small = LSA_MAX_BATCH * sizeof(int32_t) + kAttendSyncWords * sizeof(uint32_t);
+    if (hipMalloc(reinterpret_cast<void**>(&c->sel_guess), small) != hipSuccess) {
         delete c;
-        return fail(LSA_ERR_NO_MEMORY, "lsa_ctx_create: %zu bytes of device memory", LSA_MAX_BATCH * sizeof(int32_t));
+        return fail(LSA_ERR_NO_MEMORY, "lsa_ctx_create: %zu bytes of device memory", small);
     }
-    if (hipMemset(c->sel_guess, 0, LSA_MAX_BATCH * sizeof(int32_t)) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
+    c->att_sync = reinterpret_cast<uint32_t*>(c->sel_guess + LSA_MAX_BATCH);
+    if (hipMemset(c->sel_guess, 0, small) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(c->sel_guess);
         delete c;
-        return fail(LSA_ERR_HIP, "lsa_ctx_create: clearing the select guesses failed");
+        return fail(LSA_ERR_HIP, "lsa_ctx_create: clearing the select guesses and attention counters failed");
     }
     *out = c;
     return LSA_OK;
@@ -995,6 +999,8 @@ lsa_status lsa_attend(lsa_ctx* ctx, const float* q, const void* kv, lsa_dtype dt
     if (st != LSA_OK) return st;
     a.part_acc = static_cast<float*>(ctx->ws);
     a.part_ml = a.part_acc + (size_t)batch * a.max_splits * 16 * kv_dim;
+    a.sync = ctx->att_sync;
+    a.n_cu = ctx->n_cu;
     a.L[0] = AttendLayer{q, kv, phys, n_rows, out, kv_stride_b, kv_rows, phys_stride, nullptr, nullptr, nullptr, 0, 0};
     return attend_timed(ctx, a, (hipStream_t)stream);
 }
@@ -1094,15 +1100,19 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
     void* zero;
     // zero region: the select's histogram
     const size_t zero_need = align_up(sel_zero, 256);
+    uint32_t* att_sync = ctx->att_sync;
     if (fixed) {
-        const size_t zero_al = zero_need;
+        // the attention's counters sit in the cleared region too, so every call
+        // starts them at zero whatever an earlier call on the device left
+        const size_t zero_al = zero_need + align_up(kAttendSyncWords * sizeof(uint32_t), 256);
         if (zero_al + ws_total > fixed_bytes)
             return fail(LSA_ERR_UNSUPPORTED, "the step needs %zu bytes of scratch; the static scratch holds %zu",
                         zero_al + ws_total, fixed_bytes);
         zero = fixed;
+        att_sync = reinterpret_cast<uint32_t*>(fixed + zero_need);
         ws = fixed + zero_al;
         P->zero_clear = reinterpret_cast<uint32_t*>(fixed);
-        P->zero_clear_words = zero_need / 4;
+        P->zero_clear_words = zero_al / 4;
     } else {
         st = zero_ensure(ctx, zero_need);
         if (st != LSA_OK) return st;
@@ -1147,6 +1157,8 @@ lsa_status step_plan(lsa_ctx* ctx, const lsa_step_desc* d, int n_buf, StepPlan* 
         aa.scale = d->scale;
         aa.part_acc = acc_base + (size_t)l0 * B * max_splits * 16 * D;
         aa.part_ml = ml_base + (size_t)l0 * B * max_splits * 32;
+        aa.sync = att_sync;
+        aa.n_cu = ctx->n_cu;
     }
     for (int l = 0; l < L; ++l) {
         const lsa_pool* p = d->pools[l];

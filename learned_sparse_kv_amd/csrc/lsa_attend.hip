@@ -59,10 +59,23 @@ __device__ inline void unpack<uint16_t>(const uint4& u, float* out) {
 template <int D, typename KT>
 constexpr int tile_bytes() { return kR * (D * (int)sizeof(KT) + 16); }
 
-// tile: LDS of tile_bytes<D, KT>() bytes, 16-byte aligned, from the caller
-template <int D, typename KT>
-__device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int bx, const int by, const int bz,
-                                                  char* tile) {
+// Stores and loads of data that another workgroup reads or wrote in the same
+// launch: agent-scope relaxed atomics, which the L2 of every XCD passes through
+// to the device's coherence point (no whole-cache write-back or invalidate).
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// tile: LDS of tile_bytes<D, KT>() bytes, 16-byte aligned, from the caller.
+// Returns whether the split holds rows (false: it returned before any work);
+// *n_out is the clamped row count.  COH: the partials are stored with agent
+// scope, for a merge in the same launch.
+template <int D, typename KT, bool COH = false>
+__device__ __forceinline__ bool attend_split_body(const AttendArgs& a, const int bx, const int by, const int bz,
+                                                  char* tile, int* n_out = nullptr) {
     constexpr int RB = D * (int)sizeof(KT);          // row bytes
     constexpr int LS = RB + 16;                      // LDS row stride
     constexpr int CPR = RB / 16;                     // 16-byte chunks per row
@@ -103,7 +116,8 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int
     }
     int n = L.n_rows[b];
     n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
-    if (r0 >= n) return;   // uniform
+    if (n_out) *n_out = n;
+    if (r0 >= n) return false;   // uniform
     const int cnt = n - r0 < kR ? n - r0 : kR;
     const int pair = bz * a.batch + b;
     // wait for the row list here, on every lane: loaded under a branch, it would
@@ -175,8 +189,13 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int
         for (int o = 16; o >= 1; o >>= 1) l += __shfl_xor(l, o, 32);
         sP[hh][r] = p;
         if (r == 0) {
-            ml[hh] = m;
-            ml[16 + hh] = l;
+            if (COH) {
+                st_agent(ml + hh, m);
+                st_agent(ml + 16 + hh, l);
+            } else {
+                ml[hh] = m;
+                ml[16 + hh] = l;
+            }
         }
     }
     __syncthreads();
@@ -202,8 +221,15 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, const int
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) po[(4 * g + r) * D + d0 + 16 * i + h] = acc[i][r];
+            for (int r = 0; r < 4; ++r) {
+                float* dst = po + (4 * g + r) * D + d0 + 16 * i + h;
+                if (COH)
+                    st_agent(dst, acc[i][r]);
+                else
+                    *dst = acc[i][r];
+            }
     }
+    return true;
 }
 
 template <int D, typename KT>
@@ -218,6 +244,46 @@ __global__ __launch_bounds__(kThreads, 2) void attend_split_kernel(const AttendA
 // splits in split order.
 constexpr int kCombCols = 32;
 constexpr int kSpec = 24;   // splits whose outputs are loaded before the row count is known (768 rows)
+
+// The merge weights of every head from the splits' maxima and denominators
+// (s_ml, split s at s * 32: 16 maxima, then 16 denominators):
+// w[s][h] = exp(m_s - M_h) with M_h = max_s m_s, inv[h] = 1 / sum_s w[s][h] l_s,
+// the sum taken in split order.  Every thread of the workgroup (NT) takes part:
+// each finds its head's maximum and the weights of a share of the splits, then
+// 16 threads add the denominators.  Both merges use it, so they agree bit for
+// bit.  Starts and ends with the workgroup in step (s_ml written before).
+// (LDS reads go eight at a time, on clamped indices, so their latencies overlap.)
+template <int NT>
+__device__ __forceinline__ void merge_weights(const float* s_ml, const int ns, float* s_w, float* s_inv) {
+    const int tid = threadIdx.x, hh = tid & 15;
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+        float m[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m[u] = s_ml[(s0 + u < ns ? s0 + u : ns - 1) * 32 + hh];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) M = fmaxf(M, m[u]);
+    }
+    for (int s = tid >> 4; s < ns; s += NT / 16) s_w[s * 16 + hh] = expf(s_ml[s * 32 + hh] - M);
+    __syncthreads();
+    if (tid < 16) {
+        float den = 0.0f;
+        for (int s0 = 0; s0 < ns; s0 += 8) {
+            float w[8], l[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sv = s0 + u < ns ? s0 + u : ns - 1;
+                w[u] = s_w[sv * 16 + tid];
+                l[u] = s_ml[sv * 32 + 16 + tid];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < ns) den = __builtin_fmaf(w[u], l[u], den);
+        }
+        s_inv[tid] = 1.0f / den;
+    }
+    __syncthreads();
+}
 
 template <int D, int NT = 256>
 __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const int bx, const int by, const int bz) {
@@ -271,19 +337,7 @@ __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const i
     n = n < 0 ? 0 : (n > L.phys_stride ? L.phys_stride : n);
     const int ns = (n + kR - 1) / kR;
     __syncthreads();
-    if (tid < 16) {
-        const int hh = tid;
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, s_ml[s * 32 + hh]);
-        float den = 0.0f;
-        for (int s = 0; s < ns; ++s) {
-            const float f = expf(s_ml[s * 32 + hh] - M);
-            s_w[s][hh] = f;
-            den += f * s_ml[s * 32 + 16 + hh];
-        }
-        s_inv[hh] = 1.0f / den;
-    }
-    __syncthreads();
+    merge_weights<NT>(s_ml, ns, &s_w[0][0], s_inv);
     if (!mine) return;
     float* out = L.out + ((int64_t)b * a.hq + h) * D + d0;
     if (ns == 0) {
@@ -296,8 +350,8 @@ __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const i
     for (int j = 0; j < kSpec; ++j) {
         if (j < ns) {
             const float f = s_w[j][h];
-            n0 += f * x0[j];
-            n1 += f * x1[j];
+            n0 = __builtin_fmaf(f, x0[j], n0);
+            n1 = __builtin_fmaf(f, x1[j], n1);
         }
     }
     // longer lists: the remaining splits, eight loads in flight at a time
@@ -313,8 +367,8 @@ __device__ __forceinline__ void attend_combine_body(const AttendArgs& a, const i
         for (int j = 0; j < 8; ++j) {
             if (s0 + j < ns) {
                 const float f = s_w[s0 + j][h];
-                n0 += f * y0[j];
-                n1 += f * y1[j];
+                n0 = __builtin_fmaf(f, y0[j], n0);
+                n1 = __builtin_fmaf(f, y1[j], n1);
             }
         }
     }
@@ -327,8 +381,196 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a)
     attend_combine_body<D>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+// ---- one launch: every split merges a share of the columns once all splits
+// of its (layer, sequence) have stored their partials.
+//
+// The splits of one (layer, sequence) count themselves on an arrival counter
+// and wait for it to reach the number of live splits; the last to leave resets
+// the counters.  Waiting is safe because the host launches this form only when
+// every workgroup of the grid can be resident at once (the ones that wait
+// never keep a missing one from starting).  The wait is bounded: a workgroup
+// that gives up writes NaN to its columns and sets the sticky error word, and
+// from then on every launch on these counters writes NaN (a failed wait leaves
+// them counted).
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+template <int D>
+constexpr int fused_lds_bytes() {
+    return kMaxSplits * 32 * 4 + kMaxSplits * 16 * 4 + 16 * 4;
+}
+
+// 16-byte loads of partials another workgroup of the launch stored: buffer
+// loads with the device-scope cache policy (SC1), which the XCD's L2 does not
+// answer from a line it may hold from before.
+constexpr int kCpolDevice = 16;
+__device__ __forceinline__ f32x4 ld4_agent(__amdgpu_buffer_rsrc_t r, const uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolDevice);
+    return f32x4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+}
+
+// The merge in the launch.  Column slices of 32 go to the live splits in
+// turn: split s merges slices s, s + ns, s + 2 ns, ..., four at a time, one per
+// 128-thread quarter, each thread four columns of one head.  Same arithmetic, in
+// the same order, as attend_combine_body.  A thread's first kPre splits load
+// together with every split's maxima and denominators: one memory round trip
+// for lists of up to kPre splits.
+template <int D>
+__device__ __forceinline__ void attend_merge_share(const AttendArgs& a, const AttendLayer& L, const int b,
+                                                   const int pair, const int split, const int ns, const bool ok,
+                                                   char* lds) {
+    constexpr int NSL = D / kCombCols;
+    constexpr int kPre = 20;
+    float* s_ml = reinterpret_cast<float*>(lds);   // [ns][32]
+    float* s_w = s_ml + kMaxSplits * 32;            // [ns][16]
+    float* s_inv = s_w + kMaxSplits * 16;           // [16]
+    const int tid = threadIdx.x;
+    if (split >= NSL) return;   // uniform: no slice for this split
+    const int quarter = tid >> 7, h = (tid & 127) >> 3, c = (tid & 7) * 4;
+    int j = split + quarter * ns;
+    const bool mine = j < NSL && h < a.hq;
+    const int d0 = (j < NSL ? j : split) * kCombCols;   // clamped: every load stays in range
+    const int hh = h < a.hq ? h : 0;
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(a.part_acc + (int64_t)pair * a.max_splits * 16 * D, (uint32_t)(a.max_splits * 16 * D * 4));
+    f32x4 y[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int sv = u < ns ? u : ns - 1;
+        y[u] = ld4_agent(rp, (uint32_t)(((sv * 16 + hh) * D + d0 + c) * 4));
+    }
+    const float* ml = a.part_ml + (int64_t)pair * a.max_splits * 32;
+    const int n_ml = ns * 32;
+    const float m0 = ld_agent(ml + (tid < n_ml ? tid : 0));
+    const float m1 = ld_agent(ml + (tid + kThreads < n_ml ? tid + kThreads : 0));
+    if (tid < n_ml) s_ml[tid] = m0;
+    if (tid + kThreads < n_ml) s_ml[tid + kThreads] = m1;
+    for (int i = tid + 2 * kThreads; i < n_ml; i += kThreads) s_ml[i] = ld_agent(ml + i);
+    __syncthreads();
+    merge_weights<kThreads>(s_ml, ns, s_w, s_inv);
+    if (!mine) return;
+    const float inv = s_inv[h];
+    float* out = L.out + ((int64_t)b * a.hq + h) * D;
+    f32x4 n = {0.f, 0.f, 0.f, 0.f};
+    float fw[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) fw[u] = s_w[(u < ns ? u : ns - 1) * 16 + h];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        if (u < ns) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) n[e] = __builtin_fmaf(fw[u], y[u][e], n[e]);
+        }
+    }
+    for (int from = kPre;; from = 0) {
+        // the remaining splits of slice j, eight loads in flight
+        for (int s0 = from; s0 < ns; s0 += 8) {
+            f32x4 z[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sv = s0 + u < ns ? s0 + u : ns - 1;
+                z[u] = ld4_agent(rp, (uint32_t)(((sv * 16 + h) * D + j * kCombCols + c) * 4));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (s0 + u < ns) {
+                    const float f = s_w[(s0 + u) * 16 + h];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) n[e] = __builtin_fmaf(f, z[u][e], n[e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[j * kCombCols + c + e] = ok ? n[e] * inv : __builtin_nanf("");
+        // short lists (fewer than NSL / 4 splits): the quarter's further slices
+        j += 4 * ns;
+        if (j >= NSL) break;
+        n = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// sync: [0] sticky error word, then per (layer, sequence) pair p, at word
+// kAttendSyncStride * (1 + p): arrivals, departures; all zero between launches.
+template <int D, typename KT>
+__device__ __forceinline__ void attend_fused_body(const AttendArgs& a, const int bx, const int by, const int bz,
+                                                  char* lds) {
+    int n = 0;
+    if (!attend_split_body<D, KT, true>(a, bx, by, bz, lds, &n)) {
+        // an empty list: split 0 writes the zero output
+        if (n == 0 && bx == 0) {
+            float* out = a.L[bz].out + (int64_t)by * a.hq * D;
+            for (int i = threadIdx.x; i < a.hq * D; i += kThreads) out[i] = 0.0f;
+        }
+        return;
+    }
+    const int ns = (n + kR - 1) / kR;
+    const int pair = bz * a.batch + by;
+    uint32_t* err = a.sync;
+    uint32_t* arrive = a.sync + kAttendSyncStride * (1 + pair);
+    uint32_t* depart = arrive + 1;
+    __shared__ int s_ok;
+    // every partial store of this workgroup has completed before it counts itself
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int ok = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+        if (ok) {
+            __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t spins = 0;
+            while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)ns) {
+                __builtin_amdgcn_s_sleep(8);
+                if (++spins == kSpinLimit) {
+                    ok = 0;
+                    __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+            if (ok && __hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                          (uint32_t)ns - 1) {
+                __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        s_ok = ok;
+    }
+    __syncthreads();
+    attend_merge_share<D>(a, a.L[bz], by, pair, bx, ns, s_ok != 0, lds);
+}
+
+template <int D, typename KT>
+constexpr int fused_kernel_lds() {
+    return tile_bytes<D, KT>() > fused_lds_bytes<D>() ? tile_bytes<D, KT>() : fused_lds_bytes<D>();
+}
+
+template <int D, typename KT>
+__global__ __launch_bounds__(kThreads, 2) void attend_fused_kernel(const AttendArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[fused_kernel_lds<D, KT>()];
+    attend_fused_body<D, KT>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+}
+
+// Workgroups of attend_fused_kernel<D, KT> one CU holds at once (0: unknown).
+template <int D, typename KT>
+int fused_per_cu() {
+    static int per_cu = -1;
+    if (per_cu < 0) {
+        int nb = 0;
+        per_cu = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attend_fused_kernel<D, KT>, kThreads, 0) ==
+                         hipSuccess
+                     ? nb
+                     : 0;
+    }
+    return per_cu;
+}
+
 template <int D, typename KT>
 hipError_t launch_t(const AttendArgs& a, hipStream_t s, hipEvent_t mid) {
+    const int64_t grid = (int64_t)a.max_splits * a.batch * a.n_layers;
+    if (a.sync && grid <= (int64_t)a.n_cu * fused_per_cu<D, KT>()) {
+        hipLaunchKernelGGL((attend_fused_kernel<D, KT>), dim3(a.max_splits, a.batch, a.n_layers), dim3(kThreads), 0,
+                           s, a);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
+        return e;
+    }
     const dim3 g1(a.max_splits, a.batch, a.n_layers);
     hipLaunchKernelGGL((attend_split_kernel<D, KT>), g1, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();

@@ -270,9 +270,19 @@ struct AttendArgs {
     float scale;
     float* part_acc;            // [layer][b][split][16][D]
     float* part_ml;             // [layer][b][split][2][16]
+    // one-launch form (split and merge together): its counters (kAttendSyncWords,
+    // zero between launches; nullptr: always two launches) and the CUs that
+    // decide whether the whole grid can be resident at once
+    uint32_t* sync;
+    int32_t n_cu;
     AttendLayer L[kLaunchLayers];
 };
 constexpr int kAttendRows = 32;
+// counters of the one-launch attention: one 128-byte line per (layer,
+// sequence) pair and one for the error word, so the waits of different pairs
+// never poll the line another pair counts on
+constexpr int kAttendSyncStride = 32;
+constexpr int kAttendSyncWords = kAttendSyncStride * (1 + kLaunchLayers * LSA_MAX_BATCH);
 constexpr int kAttendMaxRows = 5120;    // longest row list (window + entries) of one attention
 size_t attend_workspace_bytes(int n_layers, int batch, int D, int max_rows);
 hipError_t launch_lsa_attend(const AttendArgs& a, hipStream_t s, hipEvent_t mid = nullptr);

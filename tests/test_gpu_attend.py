@@ -107,14 +107,7 @@ def test_all_chunks_is_dense_attention():
     assert rel_err_rows(out[0].cpu().numpy(), want) <= 1e-5
 
 
-def test_attention_repeats_exactly():
-    """200 launches over 8 sequences of 0 to 5120 rows (up to 160 splits merged
-    for one sequence): every launch gives the same bits, within the oracle's
-    tolerance, and a sequence without rows gets zeros."""
-    rng = np.random.default_rng(21)
-    B, hq, D, W = 8, 16, 512, 128
-    n_sel = [4992, 0, 1, 31, 500, 2000, 64, 3333]
-    cap = 5000
+def long_lists(rng, B, hq, D, W, n_sel, cap):
     q = L.grid_uniform(rng, (B, hq, D))
     wins = [L.grid_uniform(rng, (W, D)) for _ in range(B)]
     stores = [L.grid_uniform(rng, (cap, D)) for _ in range(B)]
@@ -127,7 +120,22 @@ def test_attention_repeats_exactly():
         phys[b, :W] = np.arange(W)
         phys[b, W:W + n_sel[b]] = W + sels[b]
     nrows = np.array([W + n for n in n_sel], np.int32)
-    nrows[1] = 0                                   # a sequence with no rows at all
+    return q, wins, stores, sels, kv, phys, nrows
+
+
+@pytest.mark.parametrize("B", [8, 1])
+def test_attention_repeats_exactly(B):
+    """200 launches over sequences of 0 to 5120 rows (up to 160 splits merged
+    for one sequence): every launch gives the same bits, within the oracle's
+    tolerance, and a sequence without rows gets zeros.  At batch 8 the grid
+    (1280 workgroups) is larger than the GPU holds at once and the merge is a
+    second launch; at batch 1 (160) split and merge share one launch."""
+    rng = np.random.default_rng(21)
+    hq, D, W = 16, 512, 128
+    n_sel = [4992, 0, 1, 31, 500, 2000, 64, 3333][:B]
+    q, wins, stores, sels, kv, phys, nrows = long_lists(rng, B, hq, D, W, n_sel, 5000)
+    if B > 1:
+        nrows[1] = 0                               # a sequence with no rows at all                                   # a sequence with no rows at all
     tq, tkv = torch.from_numpy(q).to(DEV), torch.from_numpy(kv).to(DEV)
     tp, tn = torch.from_numpy(phys).to(DEV), torch.from_numpy(nrows).to(DEV)
     outs = torch.zeros((4, B, hq, D), device=DEV)
@@ -144,9 +152,37 @@ def test_attention_repeats_exactly():
             for j in range(4):
                 assert np.array_equal(got[j], first), f"launch {it - 3 + j} differs from the first"
     res = outs[0].cpu().numpy()
-    assert np.all(res[1] == 0)
+    if B > 1:
+        assert np.all(res[1] == 0)
     for b in range(B):
         if b == 1:
             continue
+        want = oracle.attend(q[b], wins[b], stores[b], "f32", sels[b], 1 / np.sqrt(D))
+        assert rel_err_rows(res[b], want) <= 1e-5, f"seq {b}"
+
+
+def test_one_launch_and_two_launch_merges_agree():
+    """The same sequences attended one at a time (split and merge in one
+    launch) and at batch 8 (grid too large to be resident at once: two
+    launches) give the same bits: the two merges take the same steps in the
+    same order."""
+    rng = np.random.default_rng(22)
+    hq, D, W = 16, 512, 128
+    n_sel = [4992, 3000, 2000, 700, 33, 1, 0, 512]
+    q, wins, stores, sels, kv, phys, nrows = long_lists(rng, 8, hq, D, W, n_sel, 5000)
+    nrows[6] = 0
+    tq, tkv = torch.from_numpy(q).to(DEV), torch.from_numpy(kv).to(DEV)
+    tp, tn = torch.from_numpy(phys).to(DEV), torch.from_numpy(nrows).to(DEV)
+    both = torch.full((8, hq, D), float("nan"), device=DEV)
+    lsa.attend(ctx(), tq, tkv, tp, tn, both, 1 / np.sqrt(D))
+    pairs = torch.full((8, hq, D), float("nan"), device=DEV)
+    for b in range(8):
+        lsa.attend(ctx(), tq[b:b + 1].contiguous(), tkv[b:b + 1].contiguous(), tp[b:b + 1].contiguous(),
+                   tn[b:b + 1].contiguous(), pairs[b:b + 1], 1 / np.sqrt(D))
+    torch.cuda.synchronize()
+    assert torch.equal(both.view(torch.int32), pairs.view(torch.int32))
+    res = pairs.cpu().numpy()
+    assert np.all(res[6] == 0)
+    for b in (0, 3, 5):
         want = oracle.attend(q[b], wins[b], stores[b], "f32", sels[b], 1 / np.sqrt(D))
         assert rel_err_rows(res[b], want) <= 1e-5, f"seq {b}"
