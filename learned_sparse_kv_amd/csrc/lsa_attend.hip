@@ -87,7 +87,7 @@ __device__ __forceinline__ bool attend_split_body(const AttendArgs& a, const int
     static_assert(LOADS >= 1 && (kR * CPR) % kThreads == 0, "tile must split evenly");
 
     __shared__ float sS[4][16][kR];
-    __shared__ float sP[16][kR];
+    __shared__ float sP[16][kR + 1];   // padded: the PV reads of one row of P hit 16 banks
     __shared__ int s_ph[kR];
     __shared__ int s_src[kR];
 
@@ -206,9 +206,11 @@ __device__ __forceinline__ bool attend_split_body(const AttendArgs& a, const int
         f32x4 acc[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // step s takes rows (s & 3) + 4 g + 16 (s >> 2): the four k-lanes read rows
+        // four apart, 16 LDS banks apart with the row padding
 #pragma unroll
         for (int s = 0; s < kR / 4; ++s) {
-            const int r = 4 * s + g;
+            const int r = (s & 3) + 4 * g + 16 * (s >> 2);
             const float pa = sP[h][r];
             const char* rp = tile + r * LS;
 #pragma unroll
