@@ -510,13 +510,17 @@ __device__ __forceinline__ void attend_fused_body(const AttendArgs& a, const int
     uint32_t* arrive = a.sync + kAttendSyncStride * (1 + pair);
     uint32_t* depart = arrive + 1;
     __shared__ int s_ok;
-    // every partial store of this workgroup has completed before it counts itself
+    // every partial store of this workgroup has completed before it counts
+    // itself; the count is a release and the wait ends with an acquire, so the
+    // partials are ordered before the merge's loads in the memory model too (the
+    // SC1 accesses leave no dirty line for the release to write back: measured,
+    // the fences cost nothing next to relaxed atomics)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
         int ok = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
         if (ok) {
-            __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             uint32_t spins = 0;
             while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)ns) {
                 __builtin_amdgcn_s_sleep(8);
@@ -532,6 +536,7 @@ __device__ __forceinline__ void attend_fused_body(const AttendArgs& a, const int
                 __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         s_ok = ok;
     }
     __syncthreads();
