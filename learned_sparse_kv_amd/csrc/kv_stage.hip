@@ -134,7 +134,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
     int my_slot = -1;
     uint8_t my_rdy = 1;
     if (keep && m >= 0 && m < L.cap) {
-        my_rdy = L.ready[(int64_t)b * L.cap + m];
+        my_rdy = ((L.all_ready >> b) & 1) ? 1 : L.ready[(int64_t)b * L.cap + m];
         if (sw) my_slot = slot_of[m];
     }
     // wait for the two table loads here, on every lane: consumed only under

@@ -269,6 +269,9 @@ struct lsa_pool {
     int32_t high_water = 100;   // percent of the capacity kept in use at most after a step
     bool general = false;       // set once a policy beyond plain LRU was used: free slots may have holes
     uint64_t last_hits = 0, last_misses = 0, last_h2d = 0;   // counters at the last lsa_pool_adapt
+    // per sequence: entries [0, ready_prefix[b]) are marked stored (host-side
+    // bookkeeping of the ready flags, which are only ever set)
+    int64_t ready_prefix[LSA_MAX_BATCH] = {};
 };
 
 extern "C" {
@@ -520,6 +523,9 @@ StageLayer stage_layer(const lsa_pool* p, const int32_t* sel, const int32_t* cou
     L.meta = p->meta;
     L.stats = p->stats;
     L.ready = p->ready;
+    L.all_ready = 0;
+    for (int b = 0; b < p->d.batch && b < 64; ++b)
+        if (p->ready_prefix[b] >= p->cap) L.all_ready |= 1ull << b;
     L.sel = sel;
     L.count = count;
     L.phys = phys;
@@ -777,6 +783,7 @@ void* lsa_pool_host_rows(lsa_pool* p, int32_t b) {
 
 static lsa_status mark_ready(lsa_pool* p, int32_t b, int64_t first, int64_t count, hipStream_t s) {
     HIPTRY(hipMemsetAsync(p->ready + (int64_t)b * p->cap + first, 1, (size_t)count, s));
+    if (first <= p->ready_prefix[b] && first + count > p->ready_prefix[b]) p->ready_prefix[b] = first + count;
     if (p->swap) {
         StageLayer L = stage_layer(p, nullptr, nullptr, 1, 1, nullptr, 0, nullptr);
         HIPTRY(launch_refresh_staged(L, b, first, count, s));

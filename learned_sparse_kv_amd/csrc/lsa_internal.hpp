@@ -196,6 +196,9 @@ struct StageLayer {
     int32_t* meta;              // [batch][4]: used slots, not-stored flag
     uint64_t* stats;            // [batch][4]: hits, misses, h2d bytes
     const uint8_t* ready;       // [batch][cap]
+    // bit b: every entry of sequence b is marked stored (the stage then skips
+    // its ready lookups; the flags are only ever set, never cleared)
+    uint64_t all_ready;
     const int32_t* sel;         // [batch][sel_stride]
     const int32_t* count;       // [batch]
     int32_t* phys;              // [batch][phys_stride]
