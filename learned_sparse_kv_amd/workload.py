@@ -180,6 +180,15 @@ class DeviceWorkload:
         self.prepared = {t: lsa.PreparedStep("lsa_lookahead_step", self.ctx, **self._la_args(t + 1, t))
                          for t in steps}
 
+    def prepare_periodic(self, steps, period: int) -> None:
+        """Marshal the descriptors of the listed steps of the periodic-indexer schedule once:
+        lsa_lookahead_step on the last step of each window of `period` steps (predicting
+        the next step), lsa_lookahead_attend on the others (launch with run_prepared)."""
+        self.prepared = {t: (lsa.PreparedStep("lsa_lookahead_step", self.ctx, **self._la_args(t + 1, t))
+                             if (t + 1) % period == 0 else
+                             lsa.PreparedStep("lsa_lookahead_attend", self.ctx, **self._la_args(t, t)))
+                         for t in steps}
+
     def prepare_steps(self, steps) -> None:
         """Marshal the descriptors of the listed synchronous steps once (launch with run_prepared)."""
         self.prepared = {t: lsa.PreparedStep("lsa_decode_step", self.ctx, **self._step_args(t)) for t in steps}
