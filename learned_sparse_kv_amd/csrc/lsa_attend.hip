@@ -396,10 +396,9 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const AttendArgs a)
 // them counted).
 constexpr uint32_t kSpinLimit = 1u << 20;
 
-template <int D>
-constexpr int fused_lds_bytes() {
-    return kMaxSplits * 32 * 4 + kMaxSplits * 16 * 4 + 16 * 4;
-}
+// LDS of the merge (maxima and denominators, weights, inverses), in the tile
+// buffer once the split is done with it
+constexpr int kMergeLds = kMaxSplits * 32 * 4 + kMaxSplits * 16 * 4 + 16 * 4;
 
 // 16-byte loads of partials another workgroup of the launch stored: buffer
 // loads with the device-scope cache policy (SC1), which the XCD's L2 does not
@@ -545,7 +544,7 @@ __device__ __forceinline__ void attend_fused_body(const AttendArgs& a, const int
 
 template <int D, typename KT>
 constexpr int fused_kernel_lds() {
-    return tile_bytes<D, KT>() > fused_lds_bytes<D>() ? tile_bytes<D, KT>() : fused_lds_bytes<D>();
+    return tile_bytes<D, KT>() > kMergeLds ? tile_bytes<D, KT>() : kMergeLds;
 }
 
 template <int D, typename KT>
