@@ -376,9 +376,12 @@ def main():
     # attention bytes: window + staged rows of every layer and sequence, read once
     n_rows = dw.n_rows.cpu().numpy()
     attend_bytes = float(n_rows.sum()) * wl.kv_dim * kv_b
-    # fm_score (back to back) + the attention over resident rows (back to back)
-    sa_ms = score_ms + att_res_ms
+    # fm_score with its keys from HBM (the rotating launches) + the attention over
+    # resident rows (back to back); also with the cache-assisted score time (inside a
+    # decode loop one layer's keys stay in the last-level cache from step to step)
+    sa_ms = cold_ms + att_res_ms
     sa_frac = (score_bytes + attend_bytes) / (sa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    sa_frac_warm = (score_bytes + attend_bytes) / ((score_ms + att_res_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS
 
     src_hash = kernel_source_hash("fm_score.hip")
     traffic = stored_traffic(wl.name, src_hash)
@@ -496,6 +499,7 @@ def main():
                                          "on the others)", "by_period": periodic},
         "kernels_us_events": {k: round(avg[k] * 1e3, 2) for k in KERNELS},
         "score_attend_hbm_frac": round(sa_frac, 4),
+        "score_attend_frac_cache_assisted": round(sa_frac_warm, 4),
         "attend_resident": {"us": round(att_res_ms * 1e3, 2), "bytes": int(attend_bytes),
                             "achieved": round(attend_bytes / (att_res_ms * 1e-3) / 1e9, 1),
                             "timing": f"{RA} attention-only calls (lsa_decode_attend) over the last step's "
