@@ -186,3 +186,14 @@ def test_one_launch_and_two_launch_merges_agree():
     for b in (0, 3, 5):
         want = oracle.attend(q[b], wins[b], stores[b], "f32", sels[b], 1 / np.sqrt(D))
         assert rel_err_rows(res[b], want) <= 1e-5, f"seq {b}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [128, 256])
+def test_long_list_one_launch(dtype, D):
+    """A 5117-row list (160 splits, one launch) at D 128 / 256 with 5 heads: the
+    merge takes its first 20 splits with the maxima and the rest eight at a time,
+    on fewer column slices than splits."""
+    say(f"attend long list D={D} {dtype}")
+    rng = np.random.default_rng(31 + D + (dtype == "bf16"))
+    attend_case(rng, 1, 5, D, 128, [4989], 5000, dtype)
