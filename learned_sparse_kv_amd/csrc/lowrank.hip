@@ -64,8 +64,9 @@ __global__ __launch_bounds__(kThreads) void lowrank_scan_kernel(const LowrankArg
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t row = base + u * kRpb + wave * kRpw + lane / kLpr;
-            // rows past the end read as zero (offsets stay below 2^32: T * row_bytes < 4 GiB)
-            v[u] = buffer_load16(ru, (uint32_t)(row < a.T ? row : a.T) * row_bytes + sub * 16);
+            // rows past the end read as zero (offsets stay below 2^32: T * row_bytes < 4 GiB);
+            // U is read once per step, so its lines are not kept
+            v[u] = buffer_load16_nt(ru, (uint32_t)(row < a.T ? row : a.T) * row_bytes + sub * 16);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {

@@ -29,6 +29,14 @@ __device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_of
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// The same with the non-temporal cache policy (NT): for data read once per
+// launch that no later kernel reads again soon, so it does not displace what
+// the caches hold.
+__device__ inline uint4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ inline float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ inline float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
 
