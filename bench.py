@@ -695,15 +695,18 @@ def kvswap_measure(wl, K, Wm, parity_steps=2, n_parity_segs=16):
     t0 = time.time()
     dw = DeviceKVSwap(wl, log=log)
     dw.make_steps(max(Wm + K, parity_steps))
+    # pools that weigh importance read the step's scores; otherwise the step gets
+    # no scores buffer and scores and selects each segment in one launch
+    fused = wl.recency_w >= 100
     log(f"set-up {time.time() - t0:.1f}s")
     for t in range(Wm):
-        dw.step(t)
+        dw.step(t, fused=fused)
     torch.cuda.synchronize()
     stats0 = [p.stats() for p in dw.pools]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for t in range(Wm, Wm + K):
-        dw.step(t)
+        dw.step(t, fused=fused)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / K
@@ -713,14 +716,15 @@ def kvswap_measure(wl, K, Wm, parity_steps=2, n_parity_segs=16):
     dw.ctx.timing_read()
     stats_e0 = [p.stats() for p in dw.pools]
     for t in range(Wm, Wm + K):
-        dw.step(t)
+        dw.step(t, fused=fused)
     kt = dw.ctx.timing_read()
     stats_e1 = [p.stats() for p in dw.pools]
     dw.ctx.set_timing(False)
     names = ["score", "select", "stage", "attend"]
     avg = {k: (kt[k][0] / kt[k][1] if kt[k][1] else 0.0) for k in names}
     n_seg, T, r = wl.n_seg, wl.ctx, wl.rank
-    scan_bytes = n_seg * T * (2 * r + 4) + n_seg * (wl.C * r * 2 + wl.C * 4)
+    # U, V and q read; the scores written (not when fused)
+    scan_bytes = n_seg * T * (2 * r + (0 if fused else 4)) + n_seg * (wl.C * r * 2 + wl.C * 4)
     n_rows = dw.n_rows.cpu().numpy()
     attend_bytes = float(n_rows.sum()) * wl.row_elems * 2
     hits = sum(b["hits"] - a["hits"] for a, b in zip(stats0, stats1))
@@ -734,7 +738,9 @@ def kvswap_measure(wl, K, Wm, parity_steps=2, n_parity_segs=16):
     attend_rw_gbs = (attend_bytes + attend_written) / (avg["attend"] * 1e-3) / 1e9
     sa_frac = (scan_bytes + attend_bytes + attend_written) / ((avg["score"] + avg["attend"]) * 1e-3) / 1e9 / HBM_PEAK_GBS
     roofline = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "lowrank_p + lowrank_scan",
+                "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": ("lowrank_select (p, U scan and top-k in one launch, no scores written)" if fused
+                           else "lowrank_p + lowrank_scan"),
                 "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(avg["score"] * 1e3, 2)}
     cpu = parity = None
     if parity_steps:
@@ -750,7 +756,7 @@ def kvswap_measure(wl, K, Wm, parity_steps=2, n_parity_segs=16):
         ok, max_err, cpu_wall, seg_steps = True, 0.0, 0.0, 0
         errs = {}
         for t in range(parity_steps):
-            dw.step(t)
+            dw.step(t, fused=fused)
             torch.cuda.synchronize()
             sel, cnt, out = dw.sel.cpu().numpy(), dw.count.cpu().numpy(), dw.out.cpu().numpy()
             wants = {}
@@ -788,6 +794,7 @@ def kvswap_measure(wl, K, Wm, parity_steps=2, n_parity_segs=16):
         "config": {"workload": wl.name, "ctx": T, "batch": wl.batch, "layers": wl.layers, "groups": wl.groups,
                    "group_heads": wl.group_heads, "head_dim": wl.head_dim, "rank": r, "k": wl.k,
                    "slots": wl.slots, "segments": n_seg, "launch": "eager",
+                   "score_and_select": "one launch per step, no scores written" if fused else "two launches",
                    "replacement": {"recency_weight": wl.recency_w, "high_water": wl.high_water}},
         "roofline": roofline,
         "attend": {"achieved_gbs": round(attend_gbs, 1), "bytes_per_launch": attend_bytes,

@@ -536,7 +536,11 @@ typedef struct lsa_kvswap_desc {
     const float* q;             /* device f32 [n_seg][heads * head_dim] */
     int32_t heads, head_dim;
     int32_t k;                  /* positions kept per segment, <= 1024 */
-    float* scores;              /* device f32 [n_seg][T] */
+    float* scores;              /* device f32 [n_seg][T], or NULL: then each segment is
+                                   scored and its top-k taken in one workgroup and no
+                                   score is written (T <= 32768, k <= 1024; not with a
+                                   pool whose recency weight is below 100, which reads
+                                   the scores: LSA_ERR_INVALID_ARG) */
     int32_t* sel;               /* device i32 [n_seg][k] */
     int32_t* count;             /* device i32 [n_seg] */
     int32_t n_pools;

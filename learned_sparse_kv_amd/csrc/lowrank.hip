@@ -15,6 +15,9 @@
 // p is computed once per group by a separate small launch rather than being
 // repeated by every block of the scan.
 #include "lsa_internal.hpp"
+#define LSA_BODIES_ONLY
+#include "fm_select.hip"
+#undef LSA_BODIES_ONLY
 
 namespace lsa {
 
@@ -22,24 +25,56 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// p = diag(S) V^T q of segment s: threads t < 256 (every thread of the
+// workgroup calls this) sum rank index t % R over the columns c = t / R +
+// 256/R * i, then the first R threads add the 256/R partial sums in order and
+// write p_out[x].  red: 256 floats of LDS.
 template <int R>
-__global__ __launch_bounds__(kThreads) void lowrank_p_kernel(const LowrankArgs a) {
-    constexpr int kParts = kThreads / R;
-    __shared__ float red[kThreads];
-    const int s = blockIdx.x;
-    const int x = threadIdx.x % R, part = threadIdx.x / R;
-    const uint16_t* V = a.V + (int64_t)s * a.C * R;
-    const float* q = a.q + (int64_t)s * a.C;
-    float acc = 0.0f;
-    for (int c = part; c < a.C; c += kParts) acc += f16_to_f32(V[(int64_t)c * R + x]) * q[c];
-    red[threadIdx.x] = acc;
+__device__ __forceinline__ void lowrank_p_body(const LowrankArgs& a, const int s, float* red, float* p_out) {
+    constexpr int kParts = 256 / R;
+    const int tid = threadIdx.x;
+    const int x = tid % R, part = tid / R;
+    if (tid < 256) {
+        const uint16_t* V = a.V + (int64_t)s * a.C * R;
+        const float* q = a.q + (int64_t)s * a.C;
+        float acc = 0.0f;
+        for (int c = part; c < a.C; c += kParts) acc += f16_to_f32(V[(int64_t)c * R + x]) * q[c];
+        red[tid] = acc;
+    }
     __syncthreads();
-    if (part == 0) {
+    if (tid < R) {
         float t = 0.0f;
 #pragma unroll
         for (int i = 0; i < kParts; ++i) t += red[i * R + x];
-        a.p[(int64_t)s * R + x] = a.S[(int64_t)s * R + x] * t;
+        p_out[x] = a.S[(int64_t)s * R + x] * t;
     }
+}
+
+// One lane's part of a row's score (eight f16 of U against its eight values
+// of p), summed over the row's R/8 lanes: DPP quad permutes for lane
+// distances 1 and 2 (no LDS permute), a shuffle for 4.
+template <int R>
+__device__ __forceinline__ float row_score(const uint4& v, const float (&p)[8]) {
+    constexpr int kLpr = R / 8;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float d = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        d += p[2 * e] * f16_to_f32((uint16_t)(w[e] & 0xFFFF));
+        d += p[2 * e + 1] * f16_to_f32((uint16_t)(w[e] >> 16));
+    }
+    if constexpr (kLpr >= 2)
+        d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    if constexpr (kLpr >= 4)
+        d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    if constexpr (kLpr >= 8) d += __shfl_xor(d, 4, 64);
+    return d;
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void lowrank_p_kernel(const LowrankArgs a) {
+    __shared__ float red[kThreads];
+    lowrank_p_body<R>(a, blockIdx.x, red, a.p + (int64_t)blockIdx.x * R);
 }
 
 template <int R>
@@ -70,26 +105,87 @@ __global__ __launch_bounds__(kThreads) void lowrank_scan_kernel(const LowrankArg
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-            float d = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                d += p[2 * e] * f16_to_f32((uint16_t)(w[e] & 0xFFFF));
-                d += p[2 * e + 1] * f16_to_f32((uint16_t)(w[e] >> 16));
-            }
-            // sum over the row's kLpr lanes: DPP quad permutes for lane distances 1
-            // and 2 (no LDS permute), a shuffle for 4
-            if constexpr (kLpr >= 2)
-                d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-            if constexpr (kLpr >= 4)
-                d += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(d), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-            if constexpr (kLpr >= 8) d += __shfl_xor(d, 4, 64);
+            const float d = row_score<R>(v[u], p);
             const int64_t row = base + u * kRpb + wave * kRpw + lane / kLpr;
             // one lane per row stores; rows past the end and the other lanes are dropped
             const uint32_t off = (sub == 0 && row < last) ? (uint32_t)row * 4u : 0xFFFFFFF0u;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(d + 0.0f), rs, off, 0, 0);
         }
     }
+}
+
+// Score and top-k of one segment in one workgroup, the scores never leaving
+// the CU: p as lowrank_p_kernel, the scan as lowrank_scan_kernel (the same
+// arithmetic, so the same bits), each row's score into LDS (one padding word
+// per 32, so that a thread's E consecutive entries sit in distinct banks), then
+// the top-k of the one-workgroup select (fm_select, select_single) over the
+// E entries each thread takes from LDS: the same choice, ties to the lowest
+// position, output ascending.  T <= kFuseMaxT; the LDS of the scores is
+// reused by the select once they are in registers.
+constexpr int kFuseMaxT = 32768;
+
+template <int R, int E>
+__global__ __launch_bounds__(select_k::kNT) void lowrank_select_kernel(const LowrankArgs a, const int k,
+                                                                       int32_t* sel, int32_t* count) {
+    constexpr int NT = select_k::kNT;
+    constexpr int kLpr = R / 8, kRpw = 64 / kLpr, kRpb = (NT / 64) * kRpw, kUnroll = 8;
+    __shared__ union FuseLds {
+        float sc[kFuseMaxT + kFuseMaxT / 32];
+        select_k::KthWide sh;
+        float red[256];
+    } u;
+    __shared__ float s_p[R];
+    const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = lane % kLpr;
+    const int T = (int)a.T;
+    lowrank_p_body<R>(a, s, u.red, s_p);
+    __syncthreads();   // p is in LDS
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = s_p[sub * 8 + e];
+    __syncthreads();   // red is read before the scores overwrite it
+    const uint32_t row_bytes = R * 2;
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.U + (int64_t)s * a.T * R, (uint32_t)(a.T * row_bytes));
+    for (int base = 0; base < T; base += kRpb * kUnroll) {
+        uint4 v[kUnroll];
+#pragma unroll
+        for (int uu = 0; uu < kUnroll; ++uu) {
+            const int row = base + uu * kRpb + wave * kRpw + lane / kLpr;
+            v[uu] = buffer_load16_nt(ru, (uint32_t)(row < T ? row : T) * row_bytes + sub * 16);
+        }
+#pragma unroll
+        for (int uu = 0; uu < kUnroll; ++uu) {
+            const float d = row_score<R>(v[uu], p);
+            const int row = base + uu * kRpb + wave * kRpw + lane / kLpr;
+            if (sub == 0 && row < T) u.sc[row + (row >> 5)] = d + 0.0f;
+        }
+    }
+    __syncthreads();
+    // thread t takes entries t*E .. t*E + E - 1 (order key 0: past the segment)
+    uint32_t key[E];
+    int c_valid = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = tid * E + e;
+        const bool valid = j < T;
+        key[e] = valid ? order_key(u.sc[j + (j >> 5)]) : 0u;
+        c_valid += valid ? 1 : 0;
+    }
+    __syncthreads();   // the scores are in registers: the LDS is the select's from here
+    int n_ok;
+    block_excl_scan<NT>(c_valid, u.sh.scan, &n_ok);
+    const int K = n_ok < k ? n_ok : k;
+    int32_t* out_sel = sel + (int64_t)s * k;
+    if (K == 0) {
+        for (int i = tid; i < k; i += NT) out_sel[i] = -1;
+        if (tid == 0) count[s] = 0;
+        return;
+    }
+    uint32_t Tk;
+    int need_eq;
+    select_k::block_kth<E>(key, K, u.sh, &Tk, &need_eq);
+    select_k::block_choose<E>(key, Tk, need_eq, u.sh.scan, (int64_t)tid * E, out_sel, k);
+    for (int i = K + tid; i < k; i += NT) out_sel[i] = -1;
+    if (tid == 0) count[s] = K;
 }
 
 template <int R>
@@ -103,7 +199,36 @@ hipError_t launch_r(const LowrankArgs& a, hipStream_t s, hipEvent_t mid) {
     return hipGetLastError();
 }
 
+template <int R>
+hipError_t launch_rs(const LowrankArgs& a, int E, int k, int32_t* sel, int32_t* count, hipStream_t s) {
+    const dim3 grid(a.n_seg), block(select_k::kNT);
+    switch (E) {
+        case 1: hipLaunchKernelGGL((lowrank_select_kernel<R, 1>), grid, block, 0, s, a, k, sel, count); break;
+        case 2: hipLaunchKernelGGL((lowrank_select_kernel<R, 2>), grid, block, 0, s, a, k, sel, count); break;
+        case 4: hipLaunchKernelGGL((lowrank_select_kernel<R, 4>), grid, block, 0, s, a, k, sel, count); break;
+        case 8: hipLaunchKernelGGL((lowrank_select_kernel<R, 8>), grid, block, 0, s, a, k, sel, count); break;
+        case 16: hipLaunchKernelGGL((lowrank_select_kernel<R, 16>), grid, block, 0, s, a, k, sel, count); break;
+        case 32: hipLaunchKernelGGL((lowrank_select_kernel<R, 32>), grid, block, 0, s, a, k, sel, count); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool lowrank_select_fits(int64_t T, int rank, int k) {
+    return T >= 1 && T <= kFuseMaxT && k >= 1 && k <= select_k::kNT && (rank == 16 || rank == 32 || rank == 64);
+}
+
+hipError_t launch_lowrank_select(const LowrankArgs& a, int k, int32_t* sel, int32_t* count, hipStream_t s) {
+    if (a.n_seg == 0) return hipSuccess;
+    if (!lowrank_select_fits(a.T, a.rank, k)) return hipErrorInvalidValue;
+    int E = 1;
+    while ((int64_t)E * select_k::kNT < a.T) E *= 2;
+    if (a.rank == 16) return launch_rs<16>(a, E, k, sel, count, s);
+    if (a.rank == 32) return launch_rs<32>(a, E, k, sel, count, s);
+    return launch_rs<64>(a, E, k, sel, count, s);
+}
 
 hipError_t launch_lowrank_score(const LowrankArgs& a, hipStream_t s, hipEvent_t mid) {
     if (a.T == 0 || a.n_seg == 0) return hipSuccess;

@@ -1422,8 +1422,10 @@ lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t
 namespace {
 
 lsa_status lowrank_args(const void* U, lsa_dtype fdt, int32_t n_seg, int64_t T, int32_t rank, const float* S,
-                        const void* V, int32_t C, const float* q, float* scores, LowrankArgs* a) {
-    if (!U || !S || !V || !q || !scores) return fail(LSA_ERR_INVALID_ARG, "lsa_score_lowrank: NULL pointer");
+                        const void* V, int32_t C, const float* q, float* scores, LowrankArgs* a,
+                        bool scores_optional = false) {
+    if (!U || !S || !V || !q || (!scores && !scores_optional))
+        return fail(LSA_ERR_INVALID_ARG, "lsa_score_lowrank: NULL pointer");
     if (fdt != LSA_F16) return fail(LSA_ERR_UNSUPPORTED, "factor dtype %d (supported: F16)", (int)fdt);
     if (n_seg < 0 || T < 0) return fail(LSA_ERR_INVALID_ARG, "n_seg %d, T %lld", n_seg, (long long)T);
     if (n_seg > 65535) return fail(LSA_ERR_UNSUPPORTED, "n_seg %d > 65535", n_seg);
@@ -1541,19 +1543,36 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
         if (p->swap && p->capacity < d->k)
             return fail(LSA_ERR_SLOTS_LT_TOPK, "pool %d: gpu_chunks (%d) must be >= k (%d)", i, p->capacity, d->k);
     }
+    // no scores buffer: score and top-k in one launch per step, the scores never
+    // written (a pool that weighs importance needs them, so it needs the buffer)
+    const bool fused = d->scores == nullptr;
+    if (fused) {
+        if (!lowrank_select_fits(d->T, d->rank, d->k))
+            return fail(LSA_ERR_UNSUPPORTED, "without a scores buffer the step needs T <= 32768, rank 16/32/64 and "
+                        "k <= 1024 (T %lld, rank %d, k %d)", (long long)d->T, d->rank, d->k);
+        for (int i = 0; i < d->n_pools; ++i)
+            if (d->pools[i]->swap && d->pools[i]->recency_w < 100)
+                return fail(LSA_ERR_INVALID_ARG, "pool %d weighs importance (recency weight %d): the step needs "
+                            "its scores buffer", i, d->pools[i]->recency_w);
+    }
     LowrankArgs la;
     lsa_status st = lowrank_args(d->U, d->factor_dtype, n_seg, d->T, d->rank, d->S, d->V, d->heads * d->head_dim, d->q,
-                                 d->scores, &la);
+                                 d->scores, &la, fused);
     if (st != LSA_OK) return st;
     if (d->T > INT32_MAX || (uint64_t)d->T * (uint64_t)row_elems * (uint64_t)eb >= ((uint64_t)1 << 32))
         return fail(LSA_ERR_UNSUPPORTED, "T %lld: a sequence's cold rows must stay below 4 GiB", (long long)d->T);
     SelectArgs se;
     size_t sel_need = 0, sel_zero = 0;
-    st = select_setup(ctx, d->scores, n_seg, d->T, nullptr, LSA_SELECT_TOPK, d->k, d->k, 0.5, d->sel, d->count, &se,
-                      &sel_zero, &sel_need);
-    if (st != LSA_OK) return st;
-    st = zero_ensure(ctx, sel_zero);
-    if (st != LSA_OK) return st;
+    memset(&se, 0, sizeof(se));
+    if (!fused) {
+        st = select_setup(ctx, d->scores, n_seg, d->T, nullptr, LSA_SELECT_TOPK, d->k, d->k, 0.5, d->sel, d->count,
+                          &se, &sel_zero, &sel_need);
+        if (st != LSA_OK) return st;
+        st = zero_ensure(ctx, sel_zero);
+        if (st != LSA_OK) return st;
+    } else if (!d->sel || !d->count) {
+        return fail(LSA_ERR_INVALID_ARG, "lsa_kvswap_step: NULL sel or count");
+    }
     for (int i = 0; i < d->n_pools; ++i) {
         st = stage_check(d->pools[i], d->k, 1, d->k);
         if (st != LSA_OK) return st;
@@ -1569,7 +1588,7 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     st = ws_ensure(ctx, off_cold + align_up((size_t)n_seg * 8, 256));
     if (st != LSA_OK) return st;
     char* ws = static_cast<char*>(ctx->ws);
-    select_bind(&se, ctx->zero, ws);
+    if (!fused) select_bind(&se, ctx->zero, ws);
     la.p = reinterpret_cast<float*>(ws + off_p);
     int32_t* srcs = reinterpret_cast<int32_t*>(ws + off_src);
     uint64_t* seg_cold = reinterpret_cast<uint64_t*>(ws + off_cold);
@@ -1586,7 +1605,7 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     for (int i = 0; i < d->n_pools; ++i) {
         const size_t seg0 = (size_t)i * B;
         host[i] = stage_layer(d->pools[i], d->sel + seg0 * d->k, d->count + seg0, d->k, 1, d->phys + seg0 * d->k,
-                              d->k, d->n_rows + seg0, d->scores + seg0 * d->T, d->T);
+                              d->k, d->n_rows + seg0, fused ? nullptr : d->scores + seg0 * d->T, d->T);
         host[i].defer_copy = 1;
         host[i].src = srcs + seg0 * d->k;
         host[i].seg_cold = seg_cold + seg0;
@@ -1595,12 +1614,16 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     hipStream_t s = (hipStream_t)stream;
     const int slot = ctx->kv_layers_next;
     HIPTRY(hipMemcpyAsync(dev, host, (size_t)d->n_pools * sizeof(StageLayer), hipMemcpyHostToDevice, s));
-    {
+    if (fused) {
         Timed t(ctx, LSA_K_SCORE, s);
-        HIPTRY(launch_lowrank_score(la, s));
+        HIPTRY(launch_lowrank_select(la, d->k, d->sel, d->count, s));
         t.end();
-    }
-    {
+    } else {
+        {
+            Timed t(ctx, LSA_K_SCORE, s);
+            HIPTRY(launch_lowrank_score(la, s));
+            t.end();
+        }
         Timed t(ctx, LSA_K_SELECT, s);
         HIPTRY(launch_fm_select(se, s));
         t.end();

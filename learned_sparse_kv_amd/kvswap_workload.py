@@ -95,10 +95,12 @@ class DeviceKVSwap:
         self.q_np = q
         self.q = torch.from_numpy(q).to(self.dev)
 
-    def step(self, t: int, stream=None) -> None:
+    def step(self, t: int, stream=None, fused: bool = False) -> None:
+        """Step t; fused: no scores buffer, so score and top-k run as one launch."""
         wl = self.wl
         lsa.kvswap_step(self.ctx, U=self.U, S=self.S, V=self.V, q=self.q[t], pools=self.pools, k=wl.k,
-                        heads=wl.group_heads, head_dim=wl.head_dim, scores=self.scores, sel=self.sel,
+                        heads=wl.group_heads, head_dim=wl.head_dim, scores=None if fused else self.scores,
+                        sel=self.sel,
                         count=self.count, phys=self.phys, n_rows=self.n_rows, out=self.out, scale=wl.scale,
                         stream=stream)
 

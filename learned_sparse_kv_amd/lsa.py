@@ -579,11 +579,14 @@ def kvswap_step(ctx: Ctx, *, U, S, V, q, pools: Sequence[Pool], k: int, heads: i
                 count, phys, n_rows, out, scale: float, stream=None) -> None:
     """One KVSwap decode step (lsa_kvswap_step); segment s = pool * batch + b.
 
-    U [n_seg][T][r] f16; S [n_seg][r]; V [n_seg][C][r] f16; q [n_seg][C] f32; scores [n_seg][T] f32;
-    sel / phys [n_seg][k] i32; count / n_rows [n_seg] i32; out [n_seg][heads][head_dim] f32."""
-    for t, n in ((U, "U"), (S, "S"), (V, "V"), (q, "q"), (scores, "scores"), (sel, "sel"), (count, "count"),
+    U [n_seg][T][r] f16; S [n_seg][r]; V [n_seg][C][r] f16; q [n_seg][C] f32; scores [n_seg][T] f32 or
+    None (score and top-k in one launch, no scores written); sel / phys [n_seg][k] i32; count / n_rows
+    [n_seg] i32; out [n_seg][heads][head_dim] f32."""
+    for t, n in ((U, "U"), (S, "S"), (V, "V"), (q, "q"), (sel, "sel"), (count, "count"),
                  (phys, "phys"), (n_rows, "n_rows"), (out, "out")):
         _dev(t, n)
+    if scores is not None:
+        _dev(scores, "scores")
     n_seg, T, r = U.shape
     d = KVSwapDesc()
     pool_arr = (P * len(pools))(*[p.h for p in pools])

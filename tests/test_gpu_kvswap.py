@@ -98,8 +98,11 @@ def run_threads(fn, n):
         raise errs[0]
 
 
-def run_kvswap(wl, steps, segs=None):
-    say(f"kvswap {wl.name}: {steps} steps, n_seg={wl.n_seg}, T={wl.ctx}, k={wl.k}, slots={wl.slots}")
+def run_kvswap(wl, steps, segs=None, fused=False):
+    """fused: the step gets no scores buffer (score and top-k in one launch), so
+    everything but the scores is compared."""
+    say(f"kvswap {wl.name}: {steps} steps, n_seg={wl.n_seg}, T={wl.ctx}, k={wl.k}, slots={wl.slots}"
+        f"{', score + top-k fused' if fused else ''}")
     dw = DeviceKVSwap(wl, log=say)
     dw.make_steps(steps)
     segs = list(range(wl.n_seg)) if segs is None else sorted(segs)
@@ -113,7 +116,7 @@ def run_kvswap(wl, steps, segs=None):
     hits = {s: 0 for s in segs}
     T_threads = 16
     for t in range(steps):
-        dw.step(t)
+        dw.step(t, fused=fused)
         torch.cuda.synchronize()
         sc, sel, cnt = dw.scores.cpu().numpy(), dw.sel.cpu().numpy(), dw.count.cpu().numpy()
         phys, nrows, out = dw.phys.cpu().numpy(), dw.n_rows.cpu().numpy(), dw.out.cpu().numpy()
@@ -126,7 +129,8 @@ def run_kvswap(wl, steps, segs=None):
         run_threads(one, min(T_threads, len(segs)))
         for s in segs:
             want = wants[s]
-            assert np.array_equal(bits(sc[s]), bits(want["score"])), f"step {t} seg {s}: scores"
+            if not fused:
+                assert np.array_equal(bits(sc[s]), bits(want["score"])), f"step {t} seg {s}: scores"
             n = want["sel"].size
             assert cnt[s] == n and np.array_equal(sel[s, :n], want["sel"]), f"step {t} seg {s}: selection"
             assert nrows[s] == n and np.array_equal(phys[s, :n], want["phys"]), f"step {t} seg {s}: slot rows"
@@ -169,6 +173,34 @@ def test_kvswap_32k_full_size_sampled_segments():
     assert max(s // wl.batch for s in spread) > 16
     _, full = run_kvswap(wl, 4, segs)
     assert full >= 1
+
+
+def test_kvswap_small_all_segments_fused():
+    """Without a scores buffer the step scores and selects each segment in one
+    workgroup (the scores stay in LDS): selections, slot rows, outputs and
+    counters equal the oracle's."""
+    _, full = run_kvswap(L.KVSWAP_WORKLOADS["kvswap_small"], 6, fused=True)
+    assert full == L.KVSWAP_WORKLOADS["kvswap_small"].n_pools
+
+
+def test_kvswap_32k_sampled_segments_fused():
+    wl = L.KVSWAP_WORKLOADS["kvswap_32k"]
+    pool = 37 * 1 + 5
+    segs = sorted({wl.seg((i * 13 + 5) % wl.layers, (i * 3 + 2) % wl.groups, (i * 9 + 1) % wl.batch)
+                   for i in range(16)} | set(range(pool * wl.batch, (pool + 1) * wl.batch)))
+    _, full = run_kvswap(wl, 3, segs, fused=True)
+    assert full >= 1
+
+
+def test_kvswap_fused_refuses_a_weighted_pool(ctx):
+    """A pool that weighs importance reads the step's scores, so a step without a
+    scores buffer is refused before anything is enqueued."""
+    wl = L.KVSWAP_WORKLOADS["kvswap_small_wr"]
+    dw = DeviceKVSwap(wl, log=say)
+    dw.make_steps(1)
+    with pytest.raises(lsa.LsaError) as e:
+        dw.step(0, fused=True)
+    assert "scores buffer" in str(e.value)
 
 
 def test_kvswap_small_weighted_all_segments():
