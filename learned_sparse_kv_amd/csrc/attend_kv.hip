@@ -8,13 +8,14 @@
 // where a row holds the keys of all the group's heads followed by their values.
 //
 // Design (gfx950): one workgroup per segment and one wave per head.  A head's
-// key (and later value) slice of a row is head_dim * 2 bytes; head_dim*2/16
-// lanes load it with 16-byte buffer loads, so a wave load covers 4 (dh 128) or
-// 8 (dh 64) rows and reads each row slice exactly once.  Pass 1 forms the
-// scaled dots into LDS, the softmax is taken over LDS, pass 2 accumulates
-// p_i * V rows per lane group and the groups are combined in a fixed order.
-// The work per row is a few flops per byte: an HBM stream, not a contraction
-// worth MFMA (M = 1 per head).
+// key and value slices of a row are head_dim * 2 bytes each; head_dim*2/16
+// lanes load one with 16-byte buffer loads, so a wave load covers 4 (dh 128)
+// or 8 (dh 64) rows and reads each row slice exactly once.  The K and V slices
+// of a batch of rows are loaded together and the softmax is taken in the same
+// pass with a running maximum per lane group (rescaled once per batch), so a
+// wave waits on memory once per batch instead of once per pass; the lane
+// groups are combined in a fixed order at the end.  The work per row is a few
+// flops per byte: an HBM stream, not a contraction worth MFMA (M = 1 per head).
 #include "lsa_internal.hpp"
 
 namespace lsa {
@@ -49,8 +50,8 @@ template <int DH, typename ET>
 __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
     constexpr int kLpr = DH * 2 / 16;       // lanes per row slice
     constexpr int kRpi = 64 / kLpr;         // rows per wave load
-    constexpr int kUnroll = 4;
-    // LDS: per list row its slot byte offset and cold row (-1: none), then per head the scores
+    constexpr int kUnroll = 4;              // rows per lane group per batch (K and V: 8 loads in flight)
+    // LDS: per list row its slot byte offset and cold row (-1: none)
     extern __shared__ int32_t lds[];
     const int s = blockIdx.x;
     const int lane = threadIdx.x & 63;
@@ -66,7 +67,6 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
     }
     uint32_t* s_off = reinterpret_cast<uint32_t*>(lds);
     int32_t* s_src = lds + a.phys_stride;
-    float* z = reinterpret_cast<float*>(lds + 2 * a.phys_stride) + h * a.phys_stride;
 
     const uint32_t row_bytes = (uint32_t)(2 * a.heads * DH * 2);
     const uint32_t nrec = (uint32_t)a.kv_rows * row_bytes;
@@ -82,14 +82,16 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
     }
     __syncthreads();
 
+    const uint32_t k_off = (uint32_t)(h * DH * 2 + sub * 16);
+    const uint32_t v_off = (uint32_t)((a.heads + h) * DH * 2 + sub * 16);
     // deferred staging: a missed row is read from the cold store and this
-    // head's K (pass 1) or V (pass 2) slice is written into its slot.  Every
-    // lane issues both a slot load and a cold load; the one it does not need
-    // is pointed past its buffer, reads zero and moves no data, so the loads of
-    // a batch stay branch-free and in flight together.
+    // head's K and V slices are written into its slot.  Every lane issues both
+    // the slot loads and the cold loads; the ones it does not need are pointed
+    // past their buffer, read zero and move no data, so the loads of a batch
+    // stay branch-free and in flight together.
     const uint32_t cold_rec = srcs ? (uint32_t)a.cold_rows * row_bytes : 0u;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(srcs ? reinterpret_cast<const void*>(a.seg_cold[s]) : a.kv, cold_rec);
-    auto load_batch = [&](int i0, uint32_t slice, uint4* v) {
+    auto load_batch = [&](int i0, uint4* kk, uint4* vv) {
         int32_t c[kUnroll];
         uint32_t off[kUnroll];
 #pragma unroll
@@ -100,23 +102,34 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
         }
         if (!srcs) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) v[u] = buffer_load16(r, off[u] + slice);
+            for (int u = 0; u < kUnroll; ++u) {
+                kk[u] = buffer_load16(r, off[u] + k_off);
+                vv[u] = buffer_load16(r, off[u] + v_off);
+            }
             return;
         }
-        uint4 w[kUnroll];
+        uint4 wk[kUnroll], wv[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const bool cold = (uint32_t)c[u] < (uint32_t)a.cold_rows;
-            v[u] = buffer_load16(r, (cold ? nrec : off[u]) + slice);
-            w[u] = buffer_load16(rc, cold ? (uint32_t)c[u] * row_bytes + slice : cold_rec);
+            const uint32_t so = cold ? nrec : off[u];
+            const uint32_t co = cold ? (uint32_t)c[u] * row_bytes : cold_rec;
+            kk[u] = buffer_load16(r, so + k_off);
+            vv[u] = buffer_load16(r, so + v_off);
+            wk[u] = buffer_load16(rc, co + k_off);
+            wv[u] = buffer_load16(rc, co + v_off);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const bool cold = (uint32_t)c[u] < (uint32_t)a.cold_rows;
-            v[u] = make_uint4(v[u].x | w[u].x, v[u].y | w[u].y, v[u].z | w[u].z, v[u].w | w[u].w);
-            const u32x4 d = {v[u].x, v[u].y, v[u].z, v[u].w};
-            // the slot write goes past the buffer (dropped) unless this row was missed
-            __builtin_amdgcn_raw_buffer_store_b128(d, r, (cold && off[u] < nrec) ? off[u] + slice : nrec, 0, 0);
+            kk[u] = make_uint4(kk[u].x | wk[u].x, kk[u].y | wk[u].y, kk[u].z | wk[u].z, kk[u].w | wk[u].w);
+            vv[u] = make_uint4(vv[u].x | wv[u].x, vv[u].y | wv[u].y, vv[u].z | wv[u].z, vv[u].w | wv[u].w);
+            // the slot writes go past the buffer (dropped) unless this row was missed
+            const uint32_t wo = (cold && off[u] < nrec) ? off[u] : nrec;
+            const u32x4 dk = {kk[u].x, kk[u].y, kk[u].z, kk[u].w};
+            const u32x4 dv = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+            __builtin_amdgcn_raw_buffer_store_b128(dk, r, wo == nrec ? nrec : wo + k_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(dv, r, wo == nrec ? nrec : wo + v_off, 0, 0);
         }
     };
 
@@ -126,66 +139,62 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[e] = qh[e];
     }
-    const uint32_t k_off = (uint32_t)(h * DH * 2 + sub * 16);
-    const uint32_t v_off = (uint32_t)((a.heads + h) * DH * 2 + sub * 16);
 
-    // pass 1: z_i = scale * q . K_i
+    // one pass with a running maximum: lane group rg takes rows i = rg (mod
+    // kRpi) and keeps its own maximum m, sum l and PV sums acc; each batch
+    // rescales them once by exp(m_old - m_new)
+    float m = -INFINITY, l = 0.0f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int i0 = 0; i0 < n; i0 += kRpi * kUnroll) {
-        uint4 kv[kUnroll];
-        load_batch(i0, k_off, kv);
+        uint4 kk[kUnroll], vv[kUnroll];
+        load_batch(i0, kk, vv);
+        float z[kUnroll];
+        float mb = m;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             float f[8];
-            unpack8<ET>(kv[u], f);
+            unpack8<ET>(kk[u], f);
             float d = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) d += qv[e] * f[e];
 #pragma unroll
             for (int o = 1; o < kLpr; o <<= 1) d += __shfl_xor(d, o, 64);
             const int i = i0 + u * kRpi + rg;
-            if (sub == 0 && i < n) z[i] = a.scale * d;
+            z[u] = i < n ? a.scale * d : -INFINITY;
+            mb = fmaxf(mb, z[u]);
         }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // softmax over the n scores of this head
-    float m = -INFINITY;
-    for (int i = lane; i < n; i += 64) m = fmaxf(m, z[i]);
+        // a group with no row yet keeps m = -inf; 0 then stands in for the
+        // maximum so that every exponent below is -inf (weight 0), not NaN
+        const float mu = mb == -INFINITY ? 0.0f : mb;
+        const float corr = expf(m - mu);
+        l *= corr;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    float l = 0.0f;
-    for (int i = lane; i < n; i += 64) {
-        const float pz = expf(z[i] - m);
-        z[i] = pz;
-        l += pz;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // pass 2: sum_i p_i V_i, rows i = rg (mod kRpi) per lane group
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 < n; i0 += kRpi * kUnroll) {
-        uint4 vv[kUnroll];
-        load_batch(i0, v_off, vv);
+        for (int e = 0; e < 8; ++e) acc[e] *= corr;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int i = i0 + u * kRpi + rg;
-            const float pi = i < n ? z[i] : 0.0f;
+            const float pz = expf(z[u] - mu);
+            l += pz;
             float f[8];
             unpack8<ET>(vv[u], f);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += pi * f[e];
+            for (int e = 0; e < 8; ++e) acc[e] += pz * f[e];
         }
+        m = mb;
     }
+    // combine the lane groups: each to the wave's maximum, then summed
+    float mw = m;
 #pragma unroll
-    for (int o = kLpr; o < 64; o <<= 1)
+    for (int o = kLpr; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o, 64));
+    const float g = expf(m - mw);   // mw is finite (n >= 1); a group with no row has m = -inf, weight 0
+    l *= g;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= g;
+#pragma unroll
+    for (int o = kLpr; o < 64; o <<= 1) {
+        l += __shfl_xor(l, o, 64);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+    }
     if (lane < kLpr) {
         const float inv_l = 1.0f / l;
 #pragma unroll
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
 
 template <int DH>
 hipError_t launch_dh(const AttendKVArgs& a, hipStream_t s) {
-    const size_t lds = (size_t)(a.heads + 2) * a.phys_stride * sizeof(float);
+    const size_t lds = (size_t)2 * a.phys_stride * sizeof(int32_t);
     if (a.dtype == LSA_F16)
         hipLaunchKernelGGL((attend_kv_kernel<DH, uint16_t>), dim3(a.n_seg), dim3(64 * a.heads), lds, s, a);
     else if (a.dtype == LSA_BF16)

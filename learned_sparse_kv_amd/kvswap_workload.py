@@ -73,6 +73,11 @@ class DeviceKVSwap:
             if wl.recency_w < 100 or wl.high_water < 100:
                 pool.set_replacement(wl.recency_w, wl.high_water)
             self.pools.append(pool)
+        if not self.pools[0].swap:
+            # slots for every position: the pools never swap and read row t at slot t,
+            # so the rows are resident from the start
+            for p in range(P):
+                self.kv[p, :, :T] = self.cold[p % G]
         torch.cuda.synchronize()
         say(f"{P} pools of {S} slots x batch {B}, swap={self.pools[0].swap}")
         self.scores = torch.zeros((n_seg, T), dtype=torch.float32, device=dev)

@@ -98,9 +98,11 @@ def run_threads(fn, n):
         raise errs[0]
 
 
-def run_kvswap(wl, steps, segs=None, fused=False):
+def run_kvswap(wl, steps, segs=None, fused=False, period=None):
     """fused: the step gets no scores buffer (score and top-k in one launch), so
-    everything but the scores is compared."""
+    everything but the scores is compared.  period: row j of every U is made
+    row j % period, on both sides, so that each score repeats and the k-th
+    largest is shared by many positions (ties to the lowest position)."""
     say(f"kvswap {wl.name}: {steps} steps, n_seg={wl.n_seg}, T={wl.ctx}, k={wl.k}, slots={wl.slots}"
         f"{', score + top-k fused' if fused else ''}")
     dw = DeviceKVSwap(wl, log=say)
@@ -108,9 +110,14 @@ def run_kvswap(wl, steps, segs=None, fused=False):
     segs = list(range(wl.n_seg)) if segs is None else sorted(segs)
     ref = oracle.KVSwapState(wl, segs)
     inputs = {}
+    fold = None
+    if period is not None:
+        fold = np.arange(wl.ctx) % period
+        dw.U.copy_(dw.U[:, torch.from_numpy(fold).to(DEV)])
 
     def load(i):
-        inputs[segs[i]] = dw.host_inputs(segs[i], 0)
+        U, S, V, q, cold = dw.host_inputs(segs[i], 0)
+        inputs[segs[i]] = (U if fold is None else np.ascontiguousarray(U[fold]), S, V, q, cold)
     run_threads(load, len(segs))
     misses = {s: 0 for s in segs}
     hits = {s: 0 for s in segs}
@@ -146,7 +153,9 @@ def run_kvswap(wl, steps, segs=None, fused=False):
         if len(covered) == B:
             st = pool.stats()
             assert st["misses"] == sum(misses[s] for s in covered), f"pool {p} misses"
-            assert st["hits"] == sum(hits[s] for s in covered), f"pool {p} hits"
+            # a pool with a slot for every position never swaps and keeps no hit count
+            want_hits = sum(hits[s] for s in covered) if pool.swap else 0
+            assert st["hits"] == want_hits, f"pool {p} hits"
             full += 1
     return dw, full
 
@@ -190,6 +199,23 @@ def test_kvswap_32k_sampled_segments_fused():
                    for i in range(16)} | set(range(pool * wl.batch, (pool + 1) * wl.batch)))
     _, full = run_kvswap(wl, 3, segs, fused=True)
     assert full >= 1
+
+
+@pytest.mark.parametrize("T,k,rank,period", [(1, 4, 32, None), (301, 400, 32, None), (1023, 512, 32, None),
+                                              (1024, 512, 16, None), (4097, 513, 32, None), (3001, 100, 16, None),
+                                              (2500, 300, 64, None), (4097, 400, 32, 7), (2048, 512, 32, 3),
+                                              (1500, 400, 32, 1), (5000, 513, 32, 11)])
+def test_kvswap_fused_edge_shapes(T, k, rank, period):
+    """The fused score + top-k at its edges: a single position, fewer positions
+    than k (every position chosen, the pools holding every row), odd and
+    ragged T, k above 512, ranks 16 and 64, and U rows repeating with a period
+    (period 1: every score equal), so that the k-th largest score is shared by
+    many positions and the lowest of them must be the ones chosen."""
+    import dataclasses
+    wl = dataclasses.replace(L.KVSWAP_WORKLOADS["kvswap_small"], name=f"kvswap_edge_{T}_{k}_{rank}",
+                             base_seed=7000 + T + k + rank, ctx=T, k=k, slots=k, rank=rank, layers=1, groups=2)
+    _, full = run_kvswap(wl, 2, fused=True, period=period)
+    assert full == wl.n_pools
 
 
 def test_kvswap_fused_refuses_a_weighted_pool(ctx):
