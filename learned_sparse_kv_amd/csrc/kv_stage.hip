@@ -38,6 +38,7 @@ namespace stage_k {
 
 constexpr int kNT = 1024;
 constexpr int kMaxSlots = 4096;
+constexpr int kSmallNT = 512;   // threads and slots of the small-pool form
 
 // Copies `chunks` 16-byte chunks (cpr per row) of the rows src_row[m] of
 // `cold` to rows dst_row_off + dst_row[m] of `kv`, eight chunks in flight per
@@ -83,21 +84,24 @@ __device__ inline void copy_rows(const char* cold, char* kv, int row_bytes, int 
     }
 }
 
-// One (sequence b, layer) of the stage; a workgroup of kNT threads.
+// One (sequence b, layer) of the stage; a workgroup of NT threads, at most MS
+// slots per sequence (NT >= the selection stride, and >= the slots for the
+// rolling buffer).
 // src_valid: valid entries of sequence b in the source layer; this layer's
 // complete chunks are the first floor(src_valid * src_ratio / ratio).
+template <int NT = kNT, int MS = kMaxSlots>
 __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, const int src_valid) {
     const int tid = threadIdx.x;
 
-    __shared__ int s_scan[kNT / 64 + 1];
-    __shared__ int s_sel[kNT];
-    __shared__ int s_slot[kNT];     // slot of s_sel[i] before this step (-1: none)
-    __shared__ int s_victim[kNT];
-    __shared__ int s_order[kMaxSlots];
-    __shared__ int s_logical[kMaxSlots];   // logical_of before this step
-    __shared__ uint8_t s_hit[kMaxSlots];
-    __shared__ int s_mlog[kNT];     // missed entries and their slots, by miss rank
-    __shared__ int s_mslot[kNT];
+    __shared__ int s_scan[NT / 64 + 1];
+    __shared__ int s_sel[NT];
+    __shared__ int s_slot[NT];     // slot of s_sel[i] before this step (-1: none)
+    __shared__ int s_victim[NT];
+    __shared__ int s_order[MS];
+    __shared__ int s_logical[MS];   // logical_of before this step
+    __shared__ uint8_t s_hit[MS];
+    __shared__ int s_mlog[NT];     // missed entries and their slots, by miss rank
+    __shared__ int s_mslot[NT];
 
     // Loads come in two dependent rounds: the selection together with the LRU
     // state (order, slot occupants, used count), then the slot-table entry and
@@ -115,7 +119,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
     int n_used = 0;
     if (sw) {
         n_used = L.meta[b * 4 + 0];
-        for (int i = tid; i < S; i += kNT) {
+        for (int i = tid; i < S; i += NT) {
             s_order[i] = lru[i];
             s_logical[i] = logical_of[i];
             s_hit[i] = 0;
@@ -144,7 +148,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
     // one scan counts the kept chunks and the never-stored ones among them
     const bool unstored = keep && my_rdy == 0;
     int tot0;
-    const int packed0 = block_excl_scan<kNT>((keep ? 1 : 0) | (unstored ? 1 << 16 : 0), s_scan, &tot0);
+    const int packed0 = block_excl_scan<NT>((keep ? 1 : 0) | (unstored ? 1 << 16 : 0), s_scan, &tot0);
     const int pos = packed0 & 0xFFFF;
     const int n_l = tot0 & 0xFFFF;
     if ((tot0 >> 16) != 0) {   // uniform: [P1] error 4, the step changes nothing
@@ -162,7 +166,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
     __syncthreads();
 
     int32_t* phys = L.phys + (int64_t)b * L.phys_stride;
-    for (int r = tid; r < L.window; r += kNT) phys[r] = r;
+    for (int r = tid; r < L.window; r += NT) phys[r] = r;
     if (tid == 0) L.n_rows[b] = L.window + n_l;
     // entries outside [0, cap) (a malformed selection) are flagged and read
     // window row 0 instead, so no access leaves the pool's buffers
@@ -178,7 +182,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
     if (L.n_miss && tid == 0) L.n_miss[b] = 0;   // a swapping layer overwrites it below
     int32_t* src = L.defer_copy ? L.src + (int64_t)b * L.phys_stride : nullptr;
     if (src) {
-        for (int r = tid; r < L.window; r += kNT) src[r] = -1;
+        for (int r = tid; r < L.window; r += NT) src[r] = -1;
         if (tid < n_l) src[L.window + tid] = -1;
     }
     if (!sw) {
@@ -192,7 +196,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
     const bool miss = l >= 0 && !hit;
     if (hit) s_hit[slot] = 1;
     int tot;
-    const int packed = block_excl_scan<kNT>((hit ? 1 : 0) | (miss ? 1 << 16 : 0), s_scan, &tot);
+    const int packed = block_excl_scan<NT>((hit ? 1 : 0) | (miss ? 1 << 16 : 0), s_scan, &tot);
     const int hit_rank = packed & 0xFFFF, miss_rank = packed >> 16;
     const int n_hit = tot & 0xFFFF, n_miss = tot >> 16;
     int new_used;
@@ -201,7 +205,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
         const int n_evict = n_miss > free_slots ? n_miss - free_slots : 0;
 
         // 3. untouched used slots in old list order; the last n_evict are evicted
-        constexpr int kPer = kMaxSlots / kNT;
+        constexpr int kPer = MS / NT;
         bool untouched[kPer];
         int c_untouched = 0;
 #pragma unroll
@@ -211,7 +215,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
             c_untouched += untouched[q] ? 1 : 0;
         }
         int n_untouched;
-        int before = block_excl_scan<kNT>(c_untouched, s_scan, &n_untouched);
+        int before = block_excl_scan<NT>(c_untouched, s_scan, &n_untouched);
 #pragma unroll
         for (int q = 0; q < kPer; ++q) {
             if (!untouched[q]) continue;
@@ -234,25 +238,25 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
         if (old >= 0) slot_of[old] = -1;
         new_used = n_used + (n_miss < free_slots ? n_miss : free_slots);
     } else {
-        // [P4] rolling-buffer reading (gpu_chunks <= kNT): free slots may lie
+        // [P4] rolling-buffer reading (gpu_chunks <= NT): free slots may lie
         // anywhere below the capacity; the candidates (untouched used slots) are
         // evicted in ascending recency_w * a + (100 - recency_w) * c, a = recency
         // rank (0 = least recent), c = importance rank (0 = lowest score, ties by
         // a), ties by a; then the high-water mark frees the next candidates down
         // to max(hw_slots, this step's entries).  Thread t handles LRU position t,
         // slot t and candidate t.
-        __shared__ int s_free[kNT];
-        __shared__ int s_cand[kNT];     // candidate slots by recency rank
-        __shared__ float s_cimp[kNT];
-        __shared__ int s_cprio[kNT];
+        __shared__ int s_free[NT];
+        __shared__ int s_cand[NT];     // candidate slots by recency rank
+        __shared__ float s_cimp[NT];
+        __shared__ int s_cprio[NT];
         const bool fr = tid < L.cap_slots && tid < S && s_logical[tid] < 0;
         int n_free;
-        const int fpos = block_excl_scan<kNT>(fr ? 1 : 0, s_scan, &n_free);
+        const int fpos = block_excl_scan<NT>(fr ? 1 : 0, s_scan, &n_free);
         if (fr) s_free[fpos] = tid;
         const int uslot = tid < n_used ? s_order[tid] : -1;
         const bool cand = uslot >= 0 && s_hit[uslot] == 0;
         int n_cand;
-        const int cpos = block_excl_scan<kNT>(cand ? 1 : 0, s_scan, &n_cand);
+        const int cpos = block_excl_scan<NT>(cand ? 1 : 0, s_scan, &n_cand);
         if (cand) s_cand[n_cand - cpos - 1] = uslot;
         __syncthreads();
         if (L.recency_w < 100) {
@@ -302,7 +306,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
         // the candidates that stay, in their old order, after the misses and hits
         const bool stays = cand && s_hit[uslot] != 2;
         int n_stay;
-        const int spos = block_excl_scan<kNT>(stays ? 1 : 0, s_scan, &n_stay);
+        const int spos = block_excl_scan<NT>(stays ? 1 : 0, s_scan, &n_stay);
         if (stays) lru[n_miss + n_hit + spos] = uslot;
         new_used = n_hit + n_miss + n_stay;
     }
@@ -339,7 +343,7 @@ __device__ __forceinline__ void kv_stage_body(const StageLayer& L, const int b, 
     const int chunks = n_miss * cpr;
     const char* cold = static_cast<const char*>(L.cold) + b * L.cold_stride_b;
     char* kv = static_cast<char*>(L.kv) + b * L.kv_stride_b_bytes;
-    copy_rows<kNT>(cold, kv, L.row_bytes, chunks, cpr, s_mlog, s_mslot, L.window);
+    copy_rows<NT>(cold, kv, L.row_bytes, chunks, cpr, s_mlog, s_mslot, L.window);
 }
 
 __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
@@ -348,9 +352,13 @@ __global__ __launch_bounds__(kNT) void kv_stage_kernel(const StageArgs a) {
 
 // Any number of layers in one launch: their descriptors come from device
 // memory (copied to registers once, so the body's stores cannot alias them).
-__global__ __launch_bounds__(kNT) void kv_stage_table_kernel(const StageLayer* Ls) {
+// Pools of at most 512 slots with at most 512 entries per selection (KVSwap's
+// 400-slot buffers) take 512-thread workgroups with a quarter of the LDS, so
+// four fit on a CU instead of two.
+template <int NT, int MS>
+__global__ __launch_bounds__(NT) void kv_stage_table_kernel(const StageLayer* Ls) {
     const StageLayer L = Ls[blockIdx.y];
-    kv_stage_body(L, blockIdx.x, 0x7FFFFFFF);
+    kv_stage_body<NT, MS>(L, blockIdx.x, 0x7FFFFFFF);
 }
 
 __global__ __launch_bounds__(256) void refresh_staged_kernel(const StageLayer L, int b, int64_t first, int64_t count) {
@@ -522,9 +530,13 @@ hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_kv_stage_table(const StageLayer* layers, int n_layers, int batch, hipStream_t s) {
+hipError_t launch_kv_stage_table(const StageLayer* layers, int n_layers, int batch, bool small, hipStream_t s) {
     if (n_layers < 1 || n_layers > 65535 || batch < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kv_stage_table_kernel, dim3(batch, n_layers), dim3(kNT), 0, s, layers);
+    if (small)
+        hipLaunchKernelGGL((kv_stage_table_kernel<kSmallNT, kSmallNT>), dim3(batch, n_layers), dim3(kSmallNT), 0, s,
+                           layers);
+    else
+        hipLaunchKernelGGL((kv_stage_table_kernel<kNT, kMaxSlots>), dim3(batch, n_layers), dim3(kNT), 0, s, layers);
     return hipGetLastError();
 }
 

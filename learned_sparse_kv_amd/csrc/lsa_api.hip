@@ -1610,6 +1610,8 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
         host[i].src = srcs + seg0 * d->k;
         host[i].seg_cold = seg_cold + seg0;
     }
+    bool small_pools = d->k <= 512;
+    for (int i = 0; i < d->n_pools; ++i) small_pools = small_pools && host[i].S <= 512;
 
     hipStream_t s = (hipStream_t)stream;
     const int slot = ctx->kv_layers_next;
@@ -1630,7 +1632,7 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     }
     {
         Timed t(ctx, LSA_K_STAGE, s);
-        HIPTRY(launch_kv_stage_table(dev, d->n_pools, B, s));
+        HIPTRY(launch_kv_stage_table(dev, d->n_pools, B, small_pools, s));
         t.end();
         // the pair is free again once this stage has run
         HIPTRY(hipEventRecord(ctx->kv_layers_done[slot], s));

@@ -247,7 +247,8 @@ struct StageArgs {
 };
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t s);
 // the stage of n_layers layers (descriptors in device memory) as one launch
-hipError_t launch_kv_stage_table(const StageLayer* layers, int n_layers, int batch, hipStream_t s);
+// small: every layer has S <= 512 slots and sel_stride <= 512 (512-thread workgroups)
+hipError_t launch_kv_stage_table(const StageLayer* layers, int n_layers, int batch, bool small, hipStream_t s);
 // copy the rows a deferred stage recorded in src[] from the cold pool into their slots
 hipError_t launch_fetch_missed(const StageArgs& a, int phys_stride, hipStream_t s);
 // the select's last launch alone (path 1: the final kernel; path 0: the whole select)
