@@ -128,24 +128,30 @@ struct KthWide {
 // bins, so the histogram atomics serialised).  The keys of its boundary bin
 // are then compacted into LDS (when they fit) and the last two passes run over
 // them alone.
-// key[e] == 0 marks an entry that takes no part (no float maps to order key 0)
+// key[e] == 0 marks an entry that takes no part (no float maps to order key 0).
+// pre: the first pass's histogram (key >> 20 over the valid keys), when the
+// caller has already built it (outside sh); otherwise it is built here.
 template <int E>
-__device__ void block_kth(const uint32_t (&key)[E], int K, KthWide& sh, uint32_t* T_out, int* need_eq_out) {
+__device__ void block_kth(const uint32_t (&key)[E], int K, KthWide& sh, uint32_t* T_out, int* need_eq_out,
+                          const uint32_t* pre = nullptr) {
     const int tid = threadIdx.x;
-    for (int i = tid; i < kWideBins; i += kNT) sh.hist[i] = 0u;
-    __syncthreads();
-    // plain atomics: over 4096 bins a wave's lanes rarely share one, so the
-    // per-wave pre-aggregation (a cross-lane read per entry) costs more than
-    // the collisions it saves (304 against 352 us for 4096 x 32768 entries);
-    // all-equal keys are the worst case, about twice as slow as pre-aggregated
+    if (!pre) {
+        for (int i = tid; i < kWideBins; i += kNT) sh.hist[i] = 0u;
+        __syncthreads();
+        // plain atomics: over 4096 bins a wave's lanes rarely share one, so the
+        // per-wave pre-aggregation (a cross-lane read per entry) costs more than
+        // the collisions it saves (304 against 352 us for 4096 x 32768 entries);
+        // all-equal keys are the worst case, about twice as slow as pre-aggregated
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-        if ((key[e] != 0u)) atomicAdd(&sh.hist[key[e] >> 20], 1u);
-    __syncthreads();
+        for (int e = 0; e < E; ++e)
+            if ((key[e] != 0u)) atomicAdd(&sh.hist[key[e] >> 20], 1u);
+        __syncthreads();
+    }
+    const uint32_t* h0 = pre ? pre : sh.hist;
     int bin, above;
-    find_bin<kWideBins, kNT>(sh.hist, K, sh.scan, sh.out, &bin, &above);
+    find_bin<kWideBins, kNT>(h0, K, sh.scan, sh.out, &bin, &above);
     const uint32_t d0 = (uint32_t)bin;
-    const int c0 = (int)sh.hist[d0];
+    const int c0 = (int)h0[d0];
     int rem = K - above;
     __syncthreads();   // every thread has read c0 before the histogram is cleared
     uint32_t d1;

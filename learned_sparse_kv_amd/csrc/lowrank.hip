@@ -137,8 +137,11 @@ __global__ __launch_bounds__(select_k::kNT) void lowrank_select_kernel(const Low
         float red[256];
     } u;
     __shared__ float s_p[R];
+    // the select's first histogram (key bits 31..20), counted as the scores are made
+    __shared__ uint32_t s_hist[select_k::kWideBins];
     const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = lane % kLpr;
     const int T = (int)a.T;
+    for (int i = tid; i < select_k::kWideBins; i += NT) s_hist[i] = 0u;
     lowrank_p_body<R>(a, s, u.red, s_p);
     __syncthreads();   // p is in LDS
     float p[8];
@@ -158,33 +161,27 @@ __global__ __launch_bounds__(select_k::kNT) void lowrank_select_kernel(const Low
         for (int uu = 0; uu < kUnroll; ++uu) {
             const float d = row_score<R>(v[uu], p);
             const int row = base + uu * kRpb + wave * kRpw + lane / kLpr;
-            if (sub == 0 && row < T) u.sc[row + (row >> 5)] = d + 0.0f;
+            if (sub == 0 && row < T) {
+                u.sc[row + (row >> 5)] = d + 0.0f;
+                atomicAdd(&s_hist[order_key(d + 0.0f) >> 20], 1u);
+            }
         }
     }
     __syncthreads();
     // thread t takes entries t*E .. t*E + E - 1 (order key 0: past the segment)
     uint32_t key[E];
-    int c_valid = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int j = tid * E + e;
-        const bool valid = j < T;
-        key[e] = valid ? order_key(u.sc[j + (j >> 5)]) : 0u;
-        c_valid += valid ? 1 : 0;
+        key[e] = j < T ? order_key(u.sc[j + (j >> 5)]) : 0u;
     }
     __syncthreads();   // the scores are in registers: the LDS is the select's from here
-    int n_ok;
-    block_excl_scan<NT>(c_valid, u.sh.scan, &n_ok);
-    const int K = n_ok < k ? n_ok : k;
+    // every position of the segment is an entry (T >= 1), so K = min(k, T) >= 1
+    const int K = T < k ? T : k;
     int32_t* out_sel = sel + (int64_t)s * k;
-    if (K == 0) {
-        for (int i = tid; i < k; i += NT) out_sel[i] = -1;
-        if (tid == 0) count[s] = 0;
-        return;
-    }
     uint32_t Tk;
     int need_eq;
-    select_k::block_kth<E>(key, K, u.sh, &Tk, &need_eq);
+    select_k::block_kth<E>(key, K, u.sh, &Tk, &need_eq, s_hist);
     select_k::block_choose<E>(key, Tk, need_eq, u.sh.scan, (int64_t)tid * E, out_sel, k);
     for (int i = K + tid; i < k; i += NT) out_sel[i] = -1;
     if (tid == 0) count[s] = K;
