@@ -88,7 +88,10 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
     // head's K and V slices are written into its slot.  Every lane issues both
     // the slot loads and the cold loads; the ones it does not need are pointed
     // past their buffer, read zero and move no data, so the loads of a batch
-    // stay branch-free and in flight together.
+    // stay branch-free and in flight together.  The cold reads and the slot
+    // writes are non-temporal: neither is read again in this step, and kept
+    // lines would only push out what the next launches stream (32K KVSwap
+    // step 2.60 -> 2.58 ms, most of it in the next step's score).
     const uint32_t cold_rec = srcs ? (uint32_t)a.cold_rows * row_bytes : 0u;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(srcs ? reinterpret_cast<const void*>(a.seg_cold[s]) : a.kv, cold_rec);
     auto load_batch = [&](int i0, uint4* kk, uint4* vv) {
@@ -116,8 +119,8 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
             const uint32_t co = cold ? (uint32_t)c[u] * row_bytes : cold_rec;
             kk[u] = buffer_load16(r, so + k_off);
             vv[u] = buffer_load16(r, so + v_off);
-            wk[u] = buffer_load16(rc, co + k_off);
-            wv[u] = buffer_load16(rc, co + v_off);
+            wk[u] = buffer_load16_nt(rc, co + k_off);
+            wv[u] = buffer_load16_nt(rc, co + v_off);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -128,8 +131,8 @@ __global__ __launch_bounds__(512) void attend_kv_kernel(const AttendKVArgs a) {
             const uint32_t wo = (cold && off[u] < nrec) ? off[u] : nrec;
             const u32x4 dk = {kk[u].x, kk[u].y, kk[u].z, kk[u].w};
             const u32x4 dv = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-            __builtin_amdgcn_raw_buffer_store_b128(dk, r, wo == nrec ? nrec : wo + k_off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(dv, r, wo == nrec ? nrec : wo + v_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(dk, r, wo == nrec ? nrec : wo + k_off, 0, 2);
+            __builtin_amdgcn_raw_buffer_store_b128(dv, r, wo == nrec ? nrec : wo + v_off, 0, 2);
         }
     };
 
