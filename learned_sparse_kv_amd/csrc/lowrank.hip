@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void lowrank_scan_kernel(const LowrankArg
     }
 }
 
-// Score and top-k of one segment in one workgroup, the scores never leaving
+// Score and top-k of a segment in one workgroup, the scores never leaving
 // the CU: p as lowrank_p_kernel, the scan as lowrank_scan_kernel (the same
 // arithmetic, so the same bits), each row's score into LDS (one padding word
 // per 32, so that a thread's E consecutive entries sit in distinct banks), then
@@ -122,6 +122,13 @@ __global__ __launch_bounds__(kThreads) void lowrank_scan_kernel(const LowrankArg
 // E entries each thread takes from LDS: the same choice, ties to the lowest
 // position, output ascending.  T <= kFuseMaxT; the LDS of the scores is
 // reused by the select once they are in registers.
+//
+// One workgroup per CU, each taking segments blockIdx.x, blockIdx.x + grid, ...
+// The select reads and writes only the first 33 KB of the LDS, so before it
+// starts, the workgroup has the first batch of its next segment's U rows (64
+// KB) copied from HBM into the LDS above that (buffer loads straight to LDS);
+// the CU's memory traffic then goes on while it selects, and the next scan
+// takes its first batch from the LDS.
 constexpr int kFuseMaxT = 32768;
 
 template <int R, int E>
@@ -131,60 +138,98 @@ __global__ __launch_bounds__(select_k::kNT) void lowrank_select_kernel(const Low
     // four 16-byte loads in flight per lane (16 waves): 2.67 ms per 32K step, against 2.80 / 2.70 /
     // 2.72 / 2.72 with 2 / 3 / 6 / 8
     constexpr int kLpr = R / 8, kRpw = 64 / kLpr, kRpb = (NT / 64) * kRpw, kUnroll = 4;
+    constexpr int kBatch = kRpb * kUnroll;          // rows per batch: NT * kUnroll 16-byte pieces
+    constexpr int kPreBytes = NT * kUnroll * 16;    // 64 KB
+    constexpr int kPreOff = (int)((sizeof(select_k::KthWide) + 1023) / 1024 * 1024);
     __shared__ union FuseLds {
         float sc[kFuseMaxT + kFuseMaxT / 32];
         select_k::KthWide sh;
         float red[256];
     } u;
+    static_assert(kPreOff + kPreBytes <= (int)sizeof(FuseLds), "prefetch region inside the score LDS");
     __shared__ float s_p[R];
     // the select's first histogram (key bits 31..20), counted as the scores are made
     __shared__ uint32_t s_hist[select_k::kWideBins];
-    const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = lane % kLpr;
+    char* const pre = reinterpret_cast<char*>(&u) + kPreOff;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = lane % kLpr;
     const int T = (int)a.T;
-    for (int i = tid; i < select_k::kWideBins; i += NT) s_hist[i] = 0u;
-    lowrank_p_body<R>(a, s, u.red, s_p);
-    __syncthreads();   // p is in LDS
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = s_p[sub * 8 + e];
-    __syncthreads();   // red is read before the scores overwrite it
     const uint32_t row_bytes = R * 2;
-    const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.U + (int64_t)s * a.T * R, (uint32_t)(a.T * row_bytes));
-    for (int base = 0; base < T; base += kRpb * kUnroll) {
-        uint4 v[kUnroll];
+    bool have_pre = false;
+    for (int s = blockIdx.x; s < a.n_seg; s += gridDim.x) {
+        for (int i = tid; i < select_k::kWideBins; i += NT) s_hist[i] = 0u;
+        lowrank_p_body<R>(a, s, u.red, s_p);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's prefetch has landed
+        __syncthreads();   // p is in LDS, and so is every wave's prefetch
+        float p[8];
 #pragma unroll
-        for (int uu = 0; uu < kUnroll; ++uu) {
-            const int row = base + uu * kRpb + wave * kRpw + lane / kLpr;
-            v[uu] = buffer_load16_nt(ru, (uint32_t)(row < T ? row : T) * row_bytes + sub * 16);
-        }
+        for (int e = 0; e < 8; ++e) p[e] = s_p[sub * 8 + e];
+        auto take = [&](const uint4 (&v)[kUnroll], int base) {
 #pragma unroll
-        for (int uu = 0; uu < kUnroll; ++uu) {
-            const float d = row_score<R>(v[uu], p);
-            const int row = base + uu * kRpb + wave * kRpw + lane / kLpr;
-            if (sub == 0 && row < T) {
-                u.sc[row + (row >> 5)] = d + 0.0f;
-                atomicAdd(&s_hist[order_key(d + 0.0f) >> 20], 1u);
+            for (int uu = 0; uu < kUnroll; ++uu) {
+                const float d = row_score<R>(v[uu], p);
+                const int row = base + uu * kRpb + wave * kRpw + lane / kLpr;
+                if (sub == 0 && row < T) {
+                    u.sc[row + (row >> 5)] = d + 0.0f;
+                    atomicAdd(&s_hist[order_key(d + 0.0f) >> 20], 1u);
+                }
             }
-        }
-    }
-    __syncthreads();
-    // thread t takes entries t*E .. t*E + E - 1 (order key 0: past the segment)
-    uint32_t key[E];
+        };
+        int base0 = 0;
+        if (have_pre) {
+            // the first batch from the LDS (rows past T read as zero there and are dropped)
+            uint4 v[kUnroll];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int j = tid * E + e;
-        key[e] = j < T ? order_key(u.sc[j + (j >> 5)]) : 0u;
+            for (int uu = 0; uu < kUnroll; ++uu) {
+                const int row = uu * kRpb + wave * kRpw + lane / kLpr;
+                v[uu] = *reinterpret_cast<const uint4*>(pre + row * row_bytes + sub * 16);
+            }
+            __syncthreads();   // red is read (p) and the prefetched rows are in registers
+            take(v, 0);
+            base0 = kBatch;
+        } else {
+            __syncthreads();   // red is read before the scores overwrite it
+        }
+        const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.U + (int64_t)s * a.T * R, (uint32_t)(a.T * row_bytes));
+        for (int base = base0; base < T; base += kBatch) {
+            uint4 v[kUnroll];
+#pragma unroll
+            for (int uu = 0; uu < kUnroll; ++uu) {
+                const int row = base + uu * kRpb + wave * kRpw + lane / kLpr;
+                // rows past the end read as zero; U is read once per step, so its lines are not kept
+                v[uu] = buffer_load16_nt(ru, (uint32_t)(row < T ? row : T) * row_bytes + sub * 16);
+            }
+            take(v, base);
+        }
+        __syncthreads();
+        // thread t takes entries t*E .. t*E + E - 1 (order key 0: past the segment)
+        uint32_t key[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = tid * E + e;
+            key[e] = j < T ? order_key(u.sc[j + (j >> 5)]) : 0u;
+        }
+        __syncthreads();   // the scores are in registers: the LDS is the select's and the prefetch's from here
+        const int s_next = s + (int)gridDim.x;
+        have_pre = s_next < a.n_seg;
+        if (have_pre) {
+            const __amdgpu_buffer_rsrc_t rn =
+                make_rsrc(a.U + (int64_t)s_next * a.T * R, (uint32_t)(a.T * row_bytes));
+            // wave w copies the 1 KB pieces w, w + 16, ... of the batch, lane l the 16 bytes at 16 l
+            for (int c = wave; c < kPreBytes / 1024; c += NT / 64)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rn, (__attribute__((address_space(3))) void*)(pre + c * 1024), 16, c * 1024 + lane * 16, 0, 0, 2);
+        }
+        // every position of the segment is an entry (T >= 1), so K = min(k, T) >= 1
+        const int K = T < k ? T : k;
+        int32_t* out_sel = sel + (int64_t)s * k;
+        uint32_t Tk;
+        int need_eq;
+        select_k::block_kth<E>(key, K, u.sh, &Tk, &need_eq, s_hist);
+        select_k::block_choose<E>(key, Tk, need_eq, u.sh.scan, (int64_t)tid * E, out_sel, k);
+        for (int i = K + tid; i < k; i += NT) out_sel[i] = -1;
+        if (tid == 0) count[s] = K;
+        __syncthreads();   // the select's LDS is free before the next segment's p
     }
-    __syncthreads();   // the scores are in registers: the LDS is the select's from here
-    // every position of the segment is an entry (T >= 1), so K = min(k, T) >= 1
-    const int K = T < k ? T : k;
-    int32_t* out_sel = sel + (int64_t)s * k;
-    uint32_t Tk;
-    int need_eq;
-    select_k::block_kth<E>(key, K, u.sh, &Tk, &need_eq, s_hist);
-    select_k::block_choose<E>(key, Tk, need_eq, u.sh.scan, (int64_t)tid * E, out_sel, k);
-    for (int i = K + tid; i < k; i += NT) out_sel[i] = -1;
-    if (tid == 0) count[s] = K;
 }
 
 template <int R>
@@ -199,8 +244,8 @@ hipError_t launch_r(const LowrankArgs& a, hipStream_t s, hipEvent_t mid) {
 }
 
 template <int R>
-hipError_t launch_rs(const LowrankArgs& a, int E, int k, int32_t* sel, int32_t* count, hipStream_t s) {
-    const dim3 grid(a.n_seg), block(select_k::kNT);
+hipError_t launch_rs(const LowrankArgs& a, int E, int k, int32_t* sel, int32_t* count, int n_cu, hipStream_t s) {
+    const dim3 grid(a.n_seg < n_cu ? a.n_seg : n_cu), block(select_k::kNT);
     switch (E) {
         case 1: hipLaunchKernelGGL((lowrank_select_kernel<R, 1>), grid, block, 0, s, a, k, sel, count); break;
         case 2: hipLaunchKernelGGL((lowrank_select_kernel<R, 2>), grid, block, 0, s, a, k, sel, count); break;
@@ -219,14 +264,15 @@ bool lowrank_select_fits(int64_t T, int rank, int k) {
     return T >= 1 && T <= kFuseMaxT && k >= 1 && k <= select_k::kNT && (rank == 16 || rank == 32 || rank == 64);
 }
 
-hipError_t launch_lowrank_select(const LowrankArgs& a, int k, int32_t* sel, int32_t* count, hipStream_t s) {
+hipError_t launch_lowrank_select(const LowrankArgs& a, int k, int32_t* sel, int32_t* count, int n_cu,
+                                 hipStream_t s) {
     if (a.n_seg == 0) return hipSuccess;
-    if (!lowrank_select_fits(a.T, a.rank, k)) return hipErrorInvalidValue;
+    if (!lowrank_select_fits(a.T, a.rank, k) || n_cu < 1) return hipErrorInvalidValue;
     int E = 1;
     while ((int64_t)E * select_k::kNT < a.T) E *= 2;
-    if (a.rank == 16) return launch_rs<16>(a, E, k, sel, count, s);
-    if (a.rank == 32) return launch_rs<32>(a, E, k, sel, count, s);
-    return launch_rs<64>(a, E, k, sel, count, s);
+    if (a.rank == 16) return launch_rs<16>(a, E, k, sel, count, n_cu, s);
+    if (a.rank == 32) return launch_rs<32>(a, E, k, sel, count, n_cu, s);
+    return launch_rs<64>(a, E, k, sel, count, n_cu, s);
 }
 
 hipError_t launch_lowrank_score(const LowrankArgs& a, hipStream_t s, hipEvent_t mid) {

@@ -1618,7 +1618,7 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
     HIPTRY(hipMemcpyAsync(dev, host, (size_t)d->n_pools * sizeof(StageLayer), hipMemcpyHostToDevice, s));
     if (fused) {
         Timed t(ctx, LSA_K_SCORE, s);
-        HIPTRY(launch_lowrank_select(la, d->k, d->sel, d->count, s));
+        HIPTRY(launch_lowrank_select(la, d->k, d->sel, d->count, ctx->n_cu, s));
         t.end();
     } else {
         {

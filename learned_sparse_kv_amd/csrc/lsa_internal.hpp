@@ -347,7 +347,9 @@ hipError_t launch_lowrank_score(const LowrankArgs& a, hipStream_t s, hipEvent_t 
 // the score and the top-k of every segment in one launch, no scores written
 // (a.scores and a.p unused): sel [n_seg][k] ascending, count [n_seg]
 bool lowrank_select_fits(int64_t T, int rank, int k);
-hipError_t launch_lowrank_select(const LowrankArgs& a, int k, int32_t* sel, int32_t* count, hipStream_t s);
+// one workgroup per CU (at most n_cu), each taking every grid-th segment
+hipError_t launch_lowrank_select(const LowrankArgs& a, int k, int32_t* sel, int32_t* count, int n_cu,
+                                 hipStream_t s);
 
 struct AttendKVArgs {
     const float* q;         // [n_seg][heads * head_dim]
