@@ -218,6 +218,21 @@ def test_kvswap_fused_edge_shapes(T, k, rank, period):
     assert full == wl.n_pools
 
 
+@pytest.mark.parametrize("T,k,layers", [(1500, 100, 10), (700, 64, 12), (3001, 200, 9)])
+def test_kvswap_fused_more_segments_than_workgroups(T, k, layers):
+    """More segments than CUs (the fused launch has one workgroup per CU, each
+    taking every grid-th segment and copying the next one's first rows into
+    LDS while it selects): 288-384 segments, so most workgroups take two, with
+    T below, at and above one batch of rows (the copy then reads past the
+    segment's end, which must read as zero and be dropped)."""
+    import dataclasses
+    wl = dataclasses.replace(L.KVSWAP_WORKLOADS["kvswap_small"], name=f"kvswap_many_{T}_{k}",
+                             base_seed=8000 + T + k, ctx=T, k=k, slots=k, layers=layers, groups=8, batch=4)
+    assert wl.n_seg > 256
+    _, full = run_kvswap(wl, 2, fused=True)
+    assert full == wl.n_pools
+
+
 def test_kvswap_fused_refuses_a_weighted_pool(ctx):
     """A pool that weighs importance reads the step's scores, so a step without a
     scores buffer is refused before anything is enqueued."""
