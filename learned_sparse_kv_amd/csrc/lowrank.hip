@@ -25,20 +25,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// p = diag(S) V^T q of segment s: threads t < 256 (every thread of the
-// workgroup calls this) sum rank index t % R over the columns c = t / R +
-// 256/R * i, then the first R threads add the 256/R partial sums in order and
-// write p_out[x].  red: 256 floats of LDS.
+// p = diag(S) V^T q of one segment (V [C][R] f16, q [C], S [R], in global
+// memory or LDS): threads t < 256 (every thread of the workgroup calls this)
+// sum rank index t % R over the columns c = t / R + 256/R * i, then the first R
+// threads add the 256/R partial sums in order and write p_out[x].  red: 256
+// floats of LDS.
 template <int R>
-__device__ __forceinline__ void lowrank_p_body(const LowrankArgs& a, const int s, float* red, float* p_out) {
+__device__ __forceinline__ void lowrank_p_from(const uint16_t* V, const float* q, const int C, const float* S,
+                                               float* red, float* p_out) {
     constexpr int kParts = 256 / R;
     const int tid = threadIdx.x;
     const int x = tid % R, part = tid / R;
     if (tid < 256) {
-        const uint16_t* V = a.V + (int64_t)s * a.C * R;
-        const float* q = a.q + (int64_t)s * a.C;
         float acc = 0.0f;
-        for (int c = part; c < a.C; c += kParts) acc += f16_to_f32(V[(int64_t)c * R + x]) * q[c];
+        for (int c = part; c < C; c += kParts) acc += f16_to_f32(V[c * R + x]) * q[c];
         red[tid] = acc;
     }
     __syncthreads();
@@ -46,8 +46,13 @@ __device__ __forceinline__ void lowrank_p_body(const LowrankArgs& a, const int s
         float t = 0.0f;
 #pragma unroll
         for (int i = 0; i < kParts; ++i) t += red[i * R + x];
-        p_out[x] = a.S[(int64_t)s * R + x] * t;
+        p_out[x] = S[x] * t;
     }
+}
+
+template <int R>
+__device__ __forceinline__ void lowrank_p_body(const LowrankArgs& a, const int s, float* red, float* p_out) {
+    lowrank_p_from<R>(a.V + (int64_t)s * a.C * R, a.q + (int64_t)s * a.C, a.C, a.S + (int64_t)s * R, red, p_out);
 }
 
 // One lane's part of a row's score (eight f16 of U against its eight values
@@ -152,14 +157,37 @@ __global__ __launch_bounds__(select_k::kNT) void lowrank_select_kernel(const Low
     __shared__ uint32_t s_hist[select_k::kWideBins];
     char* const pre = reinterpret_cast<char*>(&u) + kPreOff;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = lane % kLpr;
-    const int T = (int)a.T;
+    const int T = (int)a.T, C = a.C;
     const uint32_t row_bytes = R * 2;
+    // V and q of a segment are copied into the LDS above the U copy when they fit
+    // (C <= 525 at rank 32), so p is summed from LDS rather than from 64 rounds
+    // of small loads, each waiting behind the other CUs' U streams
+    constexpr int kVqOff = kPreOff + kPreBytes;
+    const int v_bytes = (C * R * 2 + 1023) / 1024 * 1024, q_bytes = (C * 4 + 1023) / 1024 * 1024;
+    const bool vq_lds = kVqOff + v_bytes + q_bytes <= (int)sizeof(FuseLds);
+    uint16_t* const Vl = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(&u) + kVqOff);
+    float* const ql = reinterpret_cast<float*>(reinterpret_cast<char*>(&u) + kVqOff + v_bytes);
+    auto copy_vq = [&](int seg) {
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.V + (int64_t)seg * C * R, (uint32_t)(C * R * 2));
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (int64_t)seg * C, (uint32_t)(C * 4));
+        for (int c = wave; c < v_bytes / 1024; c += NT / 64)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(
+                reinterpret_cast<char*>(Vl) + c * 1024), 16, c * 1024 + lane * 16, 0, 0, 0);
+        for (int c = wave; c < q_bytes / 1024; c += NT / 64)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void*)(
+                reinterpret_cast<char*>(ql) + c * 1024), 16, c * 1024 + lane * 16, 0, 0, 0);
+    };
     bool have_pre = false;
     for (int s = blockIdx.x; s < a.n_seg; s += gridDim.x) {
+        if (vq_lds && !have_pre) copy_vq(s);   // later segments' were copied during the previous select
         for (int i = tid; i < select_k::kWideBins; i += NT) s_hist[i] = 0u;
-        lowrank_p_body<R>(a, s, u.red, s_p);
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's prefetch has landed
-        __syncthreads();   // p is in LDS, and so is every wave's prefetch
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
+        __syncthreads();   // every wave's copies are in LDS
+        if (vq_lds)
+            lowrank_p_from<R>(Vl, ql, C, a.S + (int64_t)s * R, u.red, s_p);
+        else
+            lowrank_p_body<R>(a, s, u.red, s_p);
+        __syncthreads();   // p is in LDS (red read)
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = s_p[sub * 8 + e];
@@ -218,6 +246,7 @@ __global__ __launch_bounds__(select_k::kNT) void lowrank_select_kernel(const Low
             for (int c = wave; c < kPreBytes / 1024; c += NT / 64)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rn, (__attribute__((address_space(3))) void*)(pre + c * 1024), 16, c * 1024 + lane * 16, 0, 0, 2);
+            if (vq_lds) copy_vq(s_next);
         }
         // every position of the segment is an entry (T >= 1), so K = min(k, T) >= 1
         const int K = T < k ? T : k;
