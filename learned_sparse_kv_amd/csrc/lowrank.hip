@@ -76,10 +76,36 @@ __device__ __forceinline__ float row_score(const uint4& v, const float (&p)[8]) 
     return d;
 }
 
-template <int R>
+// LDS_VQ: V and q of segment blockIdx.x first go into LDS (16-byte buffer loads
+// straight to LDS, one round trip; dynamic LDS of vq_bytes(C)), and p is then
+// summed from there in the same order, instead of from 64 rounds of 2- and
+// 4-byte loads per thread that each wait a full memory latency.
+__host__ __device__ inline int vq_v_bytes(int C, int R) { return (C * R * 2 + 1023) / 1024 * 1024; }
+__host__ __device__ inline int vq_bytes(int C, int R) { return vq_v_bytes(C, R) + (C * 4 + 1023) / 1024 * 1024; }
+
+template <int R, bool LDS_VQ>
 __global__ __launch_bounds__(kThreads) void lowrank_p_kernel(const LowrankArgs a) {
     __shared__ float red[kThreads];
-    lowrank_p_body<R>(a, blockIdx.x, red, a.p + (int64_t)blockIdx.x * R);
+    const int s = blockIdx.x;
+    float* p_out = a.p + (int64_t)s * R;
+    if constexpr (LDS_VQ) {
+        extern __shared__ __attribute__((aligned(1024))) char vq[];
+        const int C = a.C, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int v_bytes = vq_v_bytes(C, R), all = vq_bytes(C, R);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.V + (int64_t)s * C * R, (uint32_t)(C * R * 2));
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (int64_t)s * C, (uint32_t)(C * 4));
+        for (int c = wave; c < all / 1024; c += kThreads / 64) {
+            const bool in_v = c * 1024 < v_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(in_v ? rv : rq, (__attribute__((address_space(3))) void*)(vq + c * 1024),
+                                                     16, (in_v ? c * 1024 : c * 1024 - v_bytes) + lane * 16, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        lowrank_p_from<R>(reinterpret_cast<const uint16_t*>(vq), reinterpret_cast<const float*>(vq + v_bytes), C,
+                          a.S + (int64_t)s * R, red, p_out);
+    } else {
+        lowrank_p_body<R>(a, s, red, p_out);
+    }
 }
 
 template <int R>
@@ -263,7 +289,11 @@ __global__ __launch_bounds__(select_k::kNT) void lowrank_select_kernel(const Low
 
 template <int R>
 hipError_t launch_r(const LowrankArgs& a, hipStream_t s, hipEvent_t mid) {
-    hipLaunchKernelGGL((lowrank_p_kernel<R>), dim3(a.n_seg), dim3(kThreads), 0, s, a);
+    const int vq = vq_bytes(a.C, R);
+    if (vq <= 64 * 1024)
+        hipLaunchKernelGGL((lowrank_p_kernel<R, true>), dim3(a.n_seg), dim3(kThreads), (size_t)vq, s, a);
+    else
+        hipLaunchKernelGGL((lowrank_p_kernel<R, false>), dim3(a.n_seg), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (mid) (void)hipEventRecord(mid, s);

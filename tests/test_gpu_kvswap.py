@@ -27,7 +27,7 @@ def _rand_codes(rng, shape, pts, off):
 
 
 @pytest.mark.parametrize("n_seg,T,rank,C", [(1, 1, 32, 512), (3, 2047, 32, 512), (2, 5000, 16, 256),
-                                            (2, 4096, 64, 128), (5, 2048, 32, 8)])
+                                            (2, 4096, 64, 128), (5, 2048, 32, 8), (2, 300, 64, 600)])
 def test_score_lowrank_bit_identical(ctx, n_seg, T, rank, C):
     say(f"score_lowrank n_seg={n_seg} T={T} rank={rank} C={C}")
     rng = np.random.default_rng(T + rank)
