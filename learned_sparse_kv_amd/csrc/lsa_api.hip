@@ -1630,6 +1630,17 @@ lsa_status lsa_kvswap_step(lsa_ctx* ctx, const lsa_kvswap_desc* d, lsa_stream_t 
         HIPTRY(launch_fm_select(se, s));
         t.end();
     }
+    int max_slots = 0;
+    for (int i = 0; i < d->n_pools; ++i) max_slots = host[i].S > max_slots ? host[i].S : max_slots;
+    if (small_pools && stage_attend_kv_fits(d->heads, d->head_dim, d->k, max_slots)) {
+        // each segment's stage and attention in one workgroup
+        Timed t(ctx, LSA_K_ATTEND, s);
+        HIPTRY(launch_stage_attend_kv(dev, B, ka, s));
+        t.end();
+        HIPTRY(hipEventRecord(ctx->kv_layers_done[slot], s));
+        ctx->kv_layers_next = slot ^ 1;
+        return LSA_OK;
+    }
     {
         Timed t(ctx, LSA_K_STAGE, s);
         HIPTRY(launch_kv_stage_table(dev, d->n_pools, B, small_pools, s));

@@ -370,5 +370,10 @@ struct AttendKVArgs {
 };
 constexpr int kAttendKVMaxRows = 4096;
 hipError_t launch_attend_kv(const AttendKVArgs& a, hipStream_t s);
+// stage (kv_stage's 512-thread form, descriptors layers[n_seg / batch]) and
+// attention of each segment in one workgroup: heads 1, 2, 4 or 8, head_dim 64
+// or 128, phys_stride (the selection stride) and every pool's slots <= 512
+bool stage_attend_kv_fits(int heads, int head_dim, int phys_stride, int max_slots);
+hipError_t launch_stage_attend_kv(const StageLayer* layers, int batch, const AttendKVArgs& a, hipStream_t s);
 
 }  // namespace lsa
