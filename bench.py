@@ -795,6 +795,9 @@ def kvswap_measure(wl, K, Wm, parity_steps=2, n_parity_segs=16):
                    "group_heads": wl.group_heads, "head_dim": wl.head_dim, "rank": r, "k": wl.k,
                    "slots": wl.slots, "segments": n_seg, "launch": "eager",
                    "score_and_select": "one launch per step, no scores written" if fused else "two launches",
+                   "stage_and_attend": ("one launch per step (each segment's stage, then its attention, in one "
+                                        "workgroup); the attend figures include the stage"
+                                        if avg["stage"] == 0.0 else "two launches"),
                    "replacement": {"recency_weight": wl.recency_w, "high_water": wl.high_water}},
         "roofline": roofline,
         "attend": {"achieved_gbs": round(attend_gbs, 1), "bytes_per_launch": attend_bytes,
