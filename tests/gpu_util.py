@@ -4,6 +4,17 @@ import torch
 
 DEV = torch.device("cuda:0")
 RTOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
+# The tolerances above are the stated outer bounds for each row type.  Both sides read the same
+# bf16 or f16 rows and widen them to fp32 exactly; the kernels then compute in fp32 and the oracle
+# in fp64, so only the fp32 path's rounding separates them, as it does for fp32 rows.  Checking
+# that bound as well makes a loss of precision far inside the 2e-2 storage bound fail.
+ARITH_RTOL = 1e-5
+
+
+def check_attn(err: float, dtype: str, what: str) -> None:
+    """Assert an attention relative error against the stated and the arithmetic bound."""
+    assert err <= RTOL[dtype], f"{what}: rel err {err} above the stated {RTOL[dtype]} for {dtype} rows"
+    assert err <= ARITH_RTOL, f"{what}: rel err {err} above the fp32-arithmetic bound {ARITH_RTOL} ({dtype} rows)"
 
 
 def bits(x: np.ndarray) -> np.ndarray:

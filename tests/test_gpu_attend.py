@@ -1,4 +1,5 @@
-"""GPU parity of lsa_attend with oracle.attend (fp32 1e-5, bf16 2e-2 relative),
+"""GPU parity of lsa_attend with oracle.attend (stated bounds fp32 1e-5, bf16 2e-2
+relative; both also within the fp32-arithmetic bound 1e-5, since bf16 rows widen exactly),
 and bit-identical outputs for the same rows in different physical places."""
 import numpy as np
 import pytest
@@ -9,7 +10,7 @@ import oracle
 from learned_sparse_kv_amd import lsa
 from learned_sparse_kv_amd.workload import to_device
 
-from gpu_util import DEV, RTOL, rel_err_rows, say
+from gpu_util import DEV, check_attn, rel_err_rows, say
 
 pytestmark = pytest.mark.gpu
 _CTX = None
@@ -44,7 +45,7 @@ def attend_case(rng, B, hq, D, W, n_sel, cap, dtype, stride_extra=3):
     for b in range(B):
         want = oracle.attend(q[b], wins[b], stores[b], dtype, sels[b], 1 / np.sqrt(D))
         err = rel_err_rows(got[b], want)
-        assert err <= RTOL[dtype], f"seq {b}: rel err {err}"
+        check_attn(err, dtype, f"seq {b}")
     return got
 
 

@@ -1,6 +1,6 @@
 """GPU parity of whole decode steps (lsa_decode_step) with the oracle's step:
 identical selected sets, physical row lists and LRU counters; attention within
-1e-5 (fp32) / 2e-2 (bf16) per row.  Covers every workload at full size, in the
+1e-5 (fp32) / 2e-2 (bf16) per row, and both within the fp32-arithmetic bound 1e-5.  Covers every workload at full size, in the
 launch configuration the benchmark times."""
 import numpy as np
 import pytest
@@ -11,7 +11,7 @@ import oracle
 from learned_sparse_kv_amd import lsa
 from learned_sparse_kv_amd.workload import DeviceWorkload
 
-from gpu_util import RTOL, bits, rel_err_rows, say
+from gpu_util import check_attn, bits, rel_err_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,7 @@ def run_decode(wl, steps, check_scores=True):
                 assert nrows[l, b] == n
                 assert np.array_equal(phys[l, b, :n], want["phys"][l][b]), f"step {t} layer {l} seq {b}: rows"
                 err = rel_err_rows(out[l, b], want["out"][l][b])
-                assert err <= RTOL[wl.kv_dtype], f"step {t} layer {l} seq {b}: rel err {err}"
+                check_attn(err, wl.kv_dtype, f"step {t} layer {l} seq {b}")
         outs.append(out)
     for l, pool in enumerate(dw.pools):
         st = pool.stats()
@@ -125,7 +125,7 @@ def check_step(t, wl, dw, want, cur=None, check_sel=True):
             if want["phys"][l][b] is not None:
                 assert np.array_equal(phys[l, b, :n], want["phys"][l][b]), f"step {t} layer {l} seq {b}: rows"
             err = rel_err_rows(out[l, b], want["out"][l][b])
-            assert err <= RTOL[wl.kv_dtype], f"step {t} layer {l} seq {b}: rel err {err}"
+            check_attn(err, wl.kv_dtype, f"step {t} layer {l} seq {b}")
     return out
 
 
