@@ -172,7 +172,11 @@ lsa_status lsa_project(const float* hidden, int32_t batch, int32_t d_model, cons
  *   w      device f32 [batch][n_idx][heads]
  *   scores device f32 [batch][n_keys]; entries j >= n_valid[b] are not written
  * Supported: dk in {32, 64, 128} (64 or 128 for LSA_MXFP4); 1 <= n_idx <= 4; 1 <= heads <= 8;
- * 1 <= batch <= LSA_MAX_BATCH; n_keys * dk * sizeof(key) < 2^32 per sequence. */
+ * 1 <= batch <= LSA_MAX_BATCH; n_keys * dk * sizeof(key) < 2^32 per sequence.
+ * The keys are read with the non-temporal cache policy (one pass that streams
+ * them); the step calls, which read the same keys at every step, read them with
+ * the default policy so that they may stay in the last-level cache.  The
+ * scores do not depend on the policy. */
 lsa_status lsa_score(const void* keys, lsa_dtype key_dtype, const uint8_t* key_scales, int32_t batch, int64_t n_keys,
                      const int64_t* n_valid, int32_t dk, const float* q, const float* w,
                      int32_t n_idx, int32_t heads, lsa_ensemble ensemble, float* scores,

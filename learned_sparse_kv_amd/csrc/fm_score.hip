@@ -220,7 +220,16 @@ __device__ inline int cand_blocks(const ScoreArgs& a, const int bx, const int gx
     return first;
 }
 
-template <int DK, typename KT, bool HIST = false, bool CAND = false>
+// A 16-byte key load; NT: with the non-temporal cache policy.
+template <bool NT>
+__device__ __forceinline__ uint4 key_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (NT) return buffer_load16_nt(r, off);
+    else return buffer_load16(r, off);
+}
+
+// NT: the keys are loaded with the non-temporal policy (a pass that streams
+// them once); without it they may stay in the caches for the next step's pass.
+template <int DK, typename KT, bool HIST = false, bool CAND = false, bool NT = false>
 __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, const int gx, uint32_t* hist = nullptr,
                                               const int hist_mode = 0, const float hist_t_f = 0.0f,
                                               const CandOut* co = nullptr) {
@@ -316,7 +325,7 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
         uint4 pre[kSteps];
         const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(seq, seq_bytes, (uint32_t)(t - lo) * (uint32_t)C::kTileBytes);
 #pragma unroll
-        for (int i = 0; i < kSteps; ++i) pre[i] = buffer_load16(r0, vo[i >> 2] + (uint32_t)(i & 3) * 1024u);
+        for (int i = 0; i < kSteps; ++i) pre[i] = key_load16<NT>(r0, vo[i >> 2] + (uint32_t)(i & 3) * 1024u);
         __builtin_amdgcn_sched_barrier(0);
         // A operand: query row `col` (indexer col/8, head col%8), elements half*DK/2 + e
         QOperand<DK, kF32> qa;
@@ -369,7 +378,7 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
             const __amdgpu_buffer_rsrc_t rn =
                 tn < hi ? tile_rsrc(seq, seq_bytes, (uint32_t)(tn - lo) * (uint32_t)C::kTileBytes) : zero_r;
 #pragma unroll
-            for (int i = 0; i < kSteps; ++i) pre[i] = buffer_load16(rn, vo[i >> 2] + (uint32_t)(i & 3) * 1024u);
+            for (int i = 0; i < kSteps; ++i) pre[i] = key_load16<NT>(rn, vo[i >> 2] + (uint32_t)(i & 3) * 1024u);
         }
         wave_sync();
 
@@ -402,7 +411,7 @@ __device__ __forceinline__ void fm_score_body(const ScoreArgs& a, const int bx, 
                     ? *reinterpret_cast<const uint4*>(rd + (sn / C::kReads) * kSubBytes + (sn % C::kReads) * 16)
                     : u;
                 *reinterpret_cast<uint4*>(wrb + s * kLoadStride) = pre[s];
-                pre[s] = buffer_load16(r2, vo[s >> 2] + (uint32_t)(s & 3) * 1024u);
+                pre[s] = key_load16<NT>(r2, vo[s >> 2] + (uint32_t)(s & 3) * 1024u);
                 if constexpr (kF32) {
                     const float kb[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
                                          __uint_as_float(u.w)};
@@ -569,9 +578,9 @@ __device__ inline void score_hist_flush(const ScoreArgs& a, const uint32_t* s_hi
 template <typename KT>
 constexpr int kWgPerCu = KeyFmt<KT>::kBits <= 8 ? 2 : 1;
 
-template <int DK, typename KT>
+template <int DK, typename KT, bool NT>
 __global__ __launch_bounds__(kThreads, kWgPerCu<KT>) void fm_score_kernel(const ScoreArgs a) {
-    fm_score_body<DK, KT>(a, blockIdx.x, gridDim.x);
+    fm_score_body<DK, KT, false, false, NT>(a, blockIdx.x, gridDim.x);
 }
 
 // fm_score that also writes the select's candidate lists (one workgroup per
@@ -591,12 +600,15 @@ hipError_t launch_lists_t(const ScoreArgs& a, const ScoreHistArgs& h, int n_cu, 
 }
 
 template <int DK, typename KT>
-hipError_t launch_t(const ScoreArgs& a, int n_cu, hipStream_t s) {
+hipError_t launch_t(const ScoreArgs& a, int n_cu, hipStream_t s, bool stream_keys) {
     const int total = a.tile_start[a.batch];
     if (total == 0) return hipSuccess;
     int grid = (total + kWaves - 1) / kWaves;
     if (grid > n_cu * kWgPerCu<KT>) grid = n_cu * kWgPerCu<KT>;
-    hipLaunchKernelGGL((fm_score_kernel<DK, KT>), dim3(grid), dim3(kThreads), 0, s, a);
+    if (stream_keys)
+        hipLaunchKernelGGL((fm_score_kernel<DK, KT, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((fm_score_kernel<DK, KT, false>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -629,26 +641,26 @@ hipError_t launch_fm_score_lists(const ScoreArgs& a, const ScoreHistArgs& h, int
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, hipStream_t s) {
+hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, hipStream_t s, bool stream_keys) {
     if (key_dtype == LSA_F32) {
-        if (dk == 32) return launch_t<32, float>(a, n_cu, s);
-        if (dk == 64) return launch_t<64, float>(a, n_cu, s);
-        if (dk == 128) return launch_t<128, float>(a, n_cu, s);
+        if (dk == 32) return launch_t<32, float>(a, n_cu, s, stream_keys);
+        if (dk == 64) return launch_t<64, float>(a, n_cu, s, stream_keys);
+        if (dk == 128) return launch_t<128, float>(a, n_cu, s, stream_keys);
     } else if (key_dtype == LSA_BF16) {
-        if (dk == 32) return launch_t<32, uint16_t>(a, n_cu, s);
-        if (dk == 64) return launch_t<64, uint16_t>(a, n_cu, s);
-        if (dk == 128) return launch_t<128, uint16_t>(a, n_cu, s);
+        if (dk == 32) return launch_t<32, uint16_t>(a, n_cu, s, stream_keys);
+        if (dk == 64) return launch_t<64, uint16_t>(a, n_cu, s, stream_keys);
+        if (dk == 128) return launch_t<128, uint16_t>(a, n_cu, s, stream_keys);
     } else if (key_dtype == LSA_FP8_E4M3) {
-        if (dk == 32) return launch_t<32, uint8_t>(a, n_cu, s);
-        if (dk == 64) return launch_t<64, uint8_t>(a, n_cu, s);
-        if (dk == 128) return launch_t<128, uint8_t>(a, n_cu, s);
+        if (dk == 32) return launch_t<32, uint8_t>(a, n_cu, s, stream_keys);
+        if (dk == 64) return launch_t<64, uint8_t>(a, n_cu, s, stream_keys);
+        if (dk == 128) return launch_t<128, uint8_t>(a, n_cu, s, stream_keys);
     } else if (key_dtype == LSA_MXFP4) {
-        if (dk == 64) return launch_t<64, mxfp4_tag>(a, n_cu, s);
-        if (dk == 128) return launch_t<128, mxfp4_tag>(a, n_cu, s);
+        if (dk == 64) return launch_t<64, mxfp4_tag>(a, n_cu, s, stream_keys);
+        if (dk == 128) return launch_t<128, mxfp4_tag>(a, n_cu, s, stream_keys);
     } else if (key_dtype == LSA_MXINT8) {
-        if (dk == 32) return launch_t<32, mxint8_tag>(a, n_cu, s);
-        if (dk == 64) return launch_t<64, mxint8_tag>(a, n_cu, s);
-        if (dk == 128) return launch_t<128, mxint8_tag>(a, n_cu, s);
+        if (dk == 32) return launch_t<32, mxint8_tag>(a, n_cu, s, stream_keys);
+        if (dk == 64) return launch_t<64, mxint8_tag>(a, n_cu, s, stream_keys);
+        if (dk == 128) return launch_t<128, mxint8_tag>(a, n_cu, s, stream_keys);
     }
     return hipErrorInvalidValue;
 }

@@ -643,7 +643,7 @@ lsa_status lsa_score(const void* keys, lsa_dtype key_dtype, const uint8_t* key_s
     lsa_status st = score_args(keys, key_dtype, key_scales, batch, n_keys, n_valid, dk, q, w, n_idx, heads, ensemble,
                                scores, &a);
     if (st != LSA_OK) return st;
-    HIPTRY(launch_fm_score(a, key_dtype, dk, n_cu_current(), (hipStream_t)stream));
+    HIPTRY(launch_fm_score(a, key_dtype, dk, n_cu_current(), (hipStream_t)stream, true));
     return LSA_OK;
 }
 
@@ -1257,7 +1257,7 @@ lsa_status launch_predict(lsa_ctx* ctx, const StepPlan& P, const lsa_step_desc* 
     } else {
         {
             Timed t(ctx, LSA_K_SCORE, s);
-            HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s));
+            HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s, false));
             t.end();
         }
         SelectArgs se = P.se;
@@ -1327,7 +1327,7 @@ lsa_status lsa_decode_step_noalloc(lsa_ctx* ctx, const lsa_step_desc* d, lsa_str
         hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, s, P.zero_clear, n);
         HIPTRY(hipGetLastError());
     }
-    HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s));
+    HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s, false));
     HIPTRY(launch_fm_select(P.se, s));
     for (int g = 0; g < P.n_groups; ++g) HIPTRY(launch_kv_stage(P.ga[g], s));
     for (int g = 0; g < P.n_groups; ++g) HIPTRY(launch_lsa_attend(P.aa[g], s));

@@ -138,7 +138,10 @@ struct ScoreArgs {
     int32_t n_valid[LSA_MAX_BATCH];
     int32_t tile_start[LSA_MAX_BATCH + 1];   // prefix of 32-key tiles per sequence
 };
-hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, hipStream_t s);
+// stream_keys: load the keys with the non-temporal cache policy (lsa_score, a
+// pass that reads them once); the decode steps, which read the same keys at every
+// step, leave them to the caches
+hipError_t launch_fm_score(const ScoreArgs& a, int key_dtype, int dk, int n_cu, hipStream_t s, bool stream_keys);
 // What the score waves write for the select as they score: the histogram
 // (hist set: [n_seg][kSelBins], zero on entry), or the candidate lists
 // (blk_count set; see the select's pre = 1): per 256-entry sub-block the
