@@ -139,18 +139,23 @@ __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, cons
 
 // Launch D: the attention splits of step t beside the final selection of step
 // t+1 (path 1: one 512-thread workgroup per segment).  Both wait long on few
-// dependent memory reads, so neither lengthens the other.
+// dependent memory reads, so neither lengthens the other.  The selection
+// workgroups come first in the grid, so they are dispatched first: the
+// selection is the longer chain, and the splits' workgroups start over a few
+// microseconds.
 constexpr int kFinMaxBlocks = 1024;   // collect blocks per segment (1M entries); more take the exact fallback
 
 template <int D, typename KT>
 __global__ __launch_bounds__(512, 1) void la_final_split(const AttendArgs aa, const SelectArgs se, const Split sp) {
     __shared__ __attribute__((aligned(16))) char tile[attend_k::tile_bytes<D, KT>()];
+    const int n_sel = (int)gridDim.x - sp.n0;   // one workgroup per segment
     const int b = blockIdx.x;
-    if (b < sp.n0) {
-        attend_k::attend_split_body<D, KT>(aa, b % sp.x, (b / sp.x) % sp.y, b / (sp.x * sp.y), tile);
+    if (b < n_sel) {
+        select_k::sel_final_body<512, kFinMaxBlocks>(se, b);
         return;
     }
-    select_k::sel_final_body<512, kFinMaxBlocks>(se, b - sp.n0);
+    const int a = b - n_sel;
+    attend_k::attend_split_body<D, KT>(aa, a % sp.x, (a / sp.x) % sp.y, a / (sp.x * sp.y), tile);
 }
 
 // Launch E: the stage of step t+1 (one 1024-thread workgroup per (layer,
