@@ -57,16 +57,17 @@ def kernel_source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload, score_src_hash):
-    """HBM bytes per fm_score launch from the committed rocprofv3 counter summary,
-    or None when absent or taken on a different fm_score source."""
-    path = os.path.join(ROOT, "profiles", f"fm_score_{workload}_pmc.txt")
+def stored_traffic(profile, src, src_hash):
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3
+    counter summary profiles/<profile>, or None when absent or taken on a
+    different version of its source file `src`."""
+    path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
     txt = open(path).read()
-    m_hash = re.search(r"fm_score\.hip sha256\[:16\]:\s*([0-9a-f]+)", txt)
+    m_hash = re.search(re.escape(src) + r" sha256\[:16\]:\s*([0-9a-f]+)", txt)
     m_bytes = re.search(r"hbm_bytes_per_dispatch:\s*([0-9.eE+]+)", txt)
-    if not m_hash or not m_bytes or m_hash.group(1) != score_src_hash:
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
         return None
     return float(m_bytes.group(1))
 
@@ -384,7 +385,7 @@ def main():
     sa_frac_warm = (score_bytes + attend_bytes) / ((score_ms + att_res_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS
 
     src_hash = kernel_source_hash("fm_score.hip")
-    traffic = stored_traffic(wl.name, src_hash)
+    traffic = stored_traffic(f"fm_score_{wl.name}_pmc.txt", "fm_score.hip", src_hash)
     cold_gbs = score_bytes / (cold_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(cold_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(cold_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": "fm_score",
@@ -738,7 +739,9 @@ def kvswap_measure(wl, K, Wm, parity_steps=2, n_parity_segs=16):
     attend_rw_gbs = (attend_bytes + attend_written) / (avg["attend"] * 1e-3) / 1e9
     sa_frac = (scan_bytes + attend_bytes + attend_written) / ((avg["score"] + avg["attend"]) * 1e-3) / 1e9 / HBM_PEAK_GBS
     roofline = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                "traffic": (stored_traffic(f"{wl.name}_pmc.txt", "lowrank.hip", kernel_source_hash("lowrank.hip"))
+                            if fused else None),
                 "kernel": ("lowrank_select (p, U scan and top-k in one launch, no scores written)" if fused
                            else "lowrank_p + lowrank_scan"),
                 "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(avg["score"] * 1e3, 2)}
