@@ -374,6 +374,9 @@ def main():
     score_gbs = score_bytes / (score_ms * 1e-3) / 1e9
     hits = sum(s1["hits"] - s0["hits"] for s0, s1 in zip(stats0, stats1))
     misses = sum(s1["misses"] - s0["misses"] for s0, s1 in zip(stats0, stats1))
+    # rows copied from the cold pools into slots per timed step (over PCIe when
+    # the cold pools are in pinned host memory)
+    fetch_bytes = sum(s1["h2d_bytes"] - s0["h2d_bytes"] for s0, s1 in zip(stats0, stats1)) / K
     # attention bytes: window + staged rows of every layer and sequence, read once
     n_rows = dw.n_rows.cpu().numpy()
     attend_bytes = float(n_rows.sum()) * wl.kv_dim * kv_b
@@ -506,6 +509,11 @@ def main():
                             "timing": f"{RA} attention-only calls (lsa_decode_attend) over the last step's "
                                       "rows, all resident, back to back between two HIP events"},
         "hit_rate": round(hits / max(1, hits + misses), 4),
+        "fetch": {"bytes_per_step": round(fetch_bytes), "cold_pool": wl.cold,
+                  "gbs_over_the_step": round(fetch_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+                  "note": "missed rows copied from the cold pools into their slots per timed step; in the "
+                          "lookahead schedule the score launch carries the copy, so a step takes at least the "
+                          "copy at the link's rate"},
         "parity": parity,
         "fm_score_src": src_hash,
     }
