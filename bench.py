@@ -256,6 +256,12 @@ def main():
     value = 1e3 / ms_per_step
     periodic = {str(d): {"value": round(1e3 / m, 2), "ms_per_step": round(m, 5)}
                 for d, m in ((d, periodic_region(d)) for d in (2, 4, 8))}
+    # the same steps with the keys loaded non-temporally (lsa_ctx_set_key_policy):
+    # in this loop the one indexer layer's keys would otherwise stay in the
+    # last-level cache from step to step
+    dw.ctx.set_key_policy(True)
+    nt_ms = {sch: timed_region(sch, use_graph)[0] for sch in ("lookahead", "sync")}
+    dw.ctx.set_key_policy(False)
 
     # ---- kernel-timed region: the same K steps of the synchronous schedule
     # launched eagerly with HIP events around every kernel on the launch stream
@@ -498,6 +504,8 @@ def main():
         "stack_41_layers": stack41,
         "kvswap_32k": kvs,
         "kvswap_32k_wr": kvs_wr,
+        "key_policy_non_temporal": {
+            sch: {"value": round(1e3 / m, 2), "ms_per_step": round(m, 5)} for sch, m in nt_ms.items()},
         "periodic_indexer": {"schedule": "lookahead, eager; one prediction per window of `period` steps "
                                          "(lsa_lookahead_step on a window's last step, lsa_lookahead_attend "
                                          "on the others)", "by_period": periodic},

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define LSA_ABI_VERSION 6
+#define LSA_ABI_VERSION 7
 #define LSA_MAX_LAYERS 64
 #define LSA_MAX_BATCH 64
 
@@ -124,6 +124,19 @@ enum { LSA_K_SCORE = 0, LSA_K_SELECT = 1, LSA_K_STAGE = 2, LSA_K_GATHER = 3,
 lsa_status lsa_ctx_set_timing(lsa_ctx* ctx, int32_t on);
 lsa_status lsa_ctx_timing_read(lsa_ctx* ctx, double* ms /* host [LSA_K_COUNT] */,
                                int64_t* launches /* host [LSA_K_COUNT] */);
+
+/* Cache policy of the indexer keys in the step calls of this context
+ * (lsa_decode_step, lsa_decode_step_noalloc, lsa_lookahead_prime,
+ * lsa_lookahead_step).  [P1] limitations and future work, items 1-2: the keys of
+ * the whole context stay in device memory and every step reads all of them.
+ * non_temporal = 0 (the default): the default policy, so that keys read again
+ * at the next step may still be in the last-level cache (a loop over one
+ * indexer layer).  non_temporal != 0: the non-temporal policy, which lsa_score
+ * always uses; it streams keys that other work evicts between steps (a model's
+ * other layers) faster and keeps them from displacing what the caches hold.
+ * Scores, selections and outputs do not depend on it.  Takes effect at the
+ * next call; LSA_ERR_INVALID_ARG for a NULL ctx. */
+lsa_status lsa_ctx_set_key_policy(lsa_ctx* ctx, int32_t non_temporal);
 
 /* ------------------------------------------------------------- projection --
  * [P1] architecture overview: the decode token's hidden state (hidden[4096])

@@ -585,17 +585,20 @@ __global__ __launch_bounds__(kThreads, kWgPerCu<KT>) void fm_score_kernel(const 
 
 // fm_score that also writes the select's candidate lists (one workgroup per
 // CU, as the lists' schedule assumes)
-template <int DK, typename KT>
+template <int DK, typename KT, bool NT>
 __global__ __launch_bounds__(kThreads, 1) void fm_score_lists_kernel(const ScoreArgs a, const ScoreHistArgs h) {
     const CandOut co{h.blk_idx, h.blk_key, h.blk_count, h.guess, h.nblk, h.mode == LSA_SELECT_THRESHOLD ? 1 : 0, h.t_f};
-    fm_score_body<DK, KT, false, true>(a, blockIdx.x, gridDim.x, nullptr, h.mode, h.t_f, &co);
+    fm_score_body<DK, KT, false, true, NT>(a, blockIdx.x, gridDim.x, nullptr, h.mode, h.t_f, &co);
 }
 
 template <int DK, typename KT>
-hipError_t launch_lists_t(const ScoreArgs& a, const ScoreHistArgs& h, int n_cu, hipStream_t s) {
+hipError_t launch_lists_t(const ScoreArgs& a, const ScoreHistArgs& h, int n_cu, hipStream_t s, bool stream_keys) {
     const int grid = score_lists_grid(a, n_cu);
     if (grid < a.batch || grid < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fm_score_lists_kernel<DK, KT>), dim3(grid), dim3(kThreads), 0, s, a, h);
+    if (stream_keys)
+        hipLaunchKernelGGL((fm_score_lists_kernel<DK, KT, true>), dim3(grid), dim3(kThreads), 0, s, a, h);
+    else
+        hipLaunchKernelGGL((fm_score_lists_kernel<DK, KT, false>), dim3(grid), dim3(kThreads), 0, s, a, h);
     return hipGetLastError();
 }
 
@@ -628,15 +631,15 @@ int score_lists_grid(const ScoreArgs& a, int n_cu) {
 }
 
 hipError_t launch_fm_score_lists(const ScoreArgs& a, const ScoreHistArgs& h, int key_dtype, int dk, int n_cu,
-                                 hipStream_t s) {
+                                 hipStream_t s, bool stream_keys) {
     if (key_dtype == LSA_F32) {
-        if (dk == 32) return launch_lists_t<32, float>(a, h, n_cu, s);
-        if (dk == 64) return launch_lists_t<64, float>(a, h, n_cu, s);
-        if (dk == 128) return launch_lists_t<128, float>(a, h, n_cu, s);
+        if (dk == 32) return launch_lists_t<32, float>(a, h, n_cu, s, stream_keys);
+        if (dk == 64) return launch_lists_t<64, float>(a, h, n_cu, s, stream_keys);
+        if (dk == 128) return launch_lists_t<128, float>(a, h, n_cu, s, stream_keys);
     } else if (key_dtype == LSA_BF16) {
-        if (dk == 32) return launch_lists_t<32, uint16_t>(a, h, n_cu, s);
-        if (dk == 64) return launch_lists_t<64, uint16_t>(a, h, n_cu, s);
-        if (dk == 128) return launch_lists_t<128, uint16_t>(a, h, n_cu, s);
+        if (dk == 32) return launch_lists_t<32, uint16_t>(a, h, n_cu, s, stream_keys);
+        if (dk == 64) return launch_lists_t<64, uint16_t>(a, h, n_cu, s, stream_keys);
+        if (dk == 128) return launch_lists_t<128, uint16_t>(a, h, n_cu, s, stream_keys);
     }
     return hipErrorInvalidValue;
 }

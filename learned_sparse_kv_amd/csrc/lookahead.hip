@@ -115,7 +115,7 @@ __device__ inline void copy_wave(const CopyArgs& ca, const int wg, const int n_w
 // finish adds it to the segment's histogram (its PCIe-bound copy wave
 // usually ends later, so the flush costs no time).  With CAND they also write
 // the select's candidate lists (score_k::CandOut).
-template <int DK, typename KT, bool HIST, bool CAND>
+template <int DK, typename KT, bool HIST, bool CAND, bool NT>
 __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, const CopyArgs ca, const ScoreHistArgs ha) {
     static_assert(!(HIST && CAND), "the lists replace the histogram");
     __shared__ int s_pre[kCopyMaxSegs];
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, cons
     }
     const score_k::CandOut co{ha.blk_idx, ha.blk_key, ha.blk_count, ha.guess, ha.nblk,
                               ha.mode == LSA_SELECT_THRESHOLD ? 1 : 0, ha.t_f};
-    score_k::fm_score_body<DK, KT, HIST, CAND>(sa, blockIdx.x, gridDim.x, s_hist, ha.mode, ha.t_f, &co);
+    score_k::fm_score_body<DK, KT, HIST, CAND, NT>(sa, blockIdx.x, gridDim.x, s_hist, ha.mode, ha.t_f, &co);
     if (HIST) score_k::score_hist_flush(sa, s_hist, &s_done, ha.hist);
 }
 
@@ -183,16 +183,25 @@ int la_score_grid(const ScoreArgs& sa, bool hist, int n_cu) {
     return grid;
 }
 
+template <int DK, typename KT, bool NT>
+void launch_a_nt(const ScoreArgs& sa, const CopyArgs& ca, const ScoreHistArgs& ha, int grid, hipStream_t s) {
+    if (ha.blk_count)
+        hipLaunchKernelGGL((la_score_copy<DK, KT, false, true, NT>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+    else if (ha.hist)
+        hipLaunchKernelGGL((la_score_copy<DK, KT, true, false, NT>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+    else
+        hipLaunchKernelGGL((la_score_copy<DK, KT, false, false, NT>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+}
+
 template <int DK, typename KT>
-hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, const ScoreHistArgs& ha, int n_cu, hipStream_t s) {
+hipError_t launch_a(const ScoreArgs& sa, const CopyArgs& ca, const ScoreHistArgs& ha, int n_cu, hipStream_t s,
+                    bool stream_keys) {
     const int grid = la_score_grid(sa, ha.hist != nullptr || ha.blk_count != nullptr, n_cu);
     if (grid < 1) return hipErrorInvalidValue;
-    if (ha.blk_count)
-        hipLaunchKernelGGL((la_score_copy<DK, KT, false, true>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
-    else if (ha.hist)
-        hipLaunchKernelGGL((la_score_copy<DK, KT, true, false>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+    if (stream_keys)
+        launch_a_nt<DK, KT, true>(sa, ca, ha, grid, s);
     else
-        hipLaunchKernelGGL((la_score_copy<DK, KT, false, false>), dim3(grid), dim3(320), 0, s, sa, ca, ha);
+        launch_a_nt<DK, KT, false>(sa, ca, ha, grid, s);
     return hipGetLastError();
 }
 
@@ -245,7 +254,8 @@ hipError_t launch_e(const StageArgs& ga, const AttendArgs& aa, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const CopyArgs& ca, int key_dtype, int dk, int n_cu,
-                                 const SelectArgs* hist_for, const int32_t* guess, bool* lists, hipStream_t s) {
+                                 const SelectArgs* hist_for, const int32_t* guess, bool* lists, hipStream_t s,
+                                 bool stream_keys) {
     const int cpr = ca.row_bytes / 16;
     if (ca.n_seg < 0 || ca.n_seg > kCopyMaxSegs || (ca.n_seg && (!ca.miss || !ca.n_miss)) || ca.row_bytes % 16 != 0 ||
         cpr < 1 || (cpr & (cpr - 1)) != 0)
@@ -271,24 +281,24 @@ hipError_t launch_la_fetch_score(const ScoreArgs& sa, const CopyArgs& ca, int ke
         }
     }
     if (key_dtype == LSA_F32) {
-        if (dk == 32) return launch_a<32, float>(sa, ca, ha, n_cu, s);
-        if (dk == 64) return launch_a<64, float>(sa, ca, ha, n_cu, s);
-        if (dk == 128) return launch_a<128, float>(sa, ca, ha, n_cu, s);
+        if (dk == 32) return launch_a<32, float>(sa, ca, ha, n_cu, s, stream_keys);
+        if (dk == 64) return launch_a<64, float>(sa, ca, ha, n_cu, s, stream_keys);
+        if (dk == 128) return launch_a<128, float>(sa, ca, ha, n_cu, s, stream_keys);
     } else if (key_dtype == LSA_BF16) {
-        if (dk == 32) return launch_a<32, uint16_t>(sa, ca, ha, n_cu, s);
-        if (dk == 64) return launch_a<64, uint16_t>(sa, ca, ha, n_cu, s);
-        if (dk == 128) return launch_a<128, uint16_t>(sa, ca, ha, n_cu, s);
+        if (dk == 32) return launch_a<32, uint16_t>(sa, ca, ha, n_cu, s, stream_keys);
+        if (dk == 64) return launch_a<64, uint16_t>(sa, ca, ha, n_cu, s, stream_keys);
+        if (dk == 128) return launch_a<128, uint16_t>(sa, ca, ha, n_cu, s, stream_keys);
     } else if (key_dtype == LSA_FP8_E4M3) {
-        if (dk == 32) return launch_a<32, uint8_t>(sa, ca, ha, n_cu, s);
-        if (dk == 64) return launch_a<64, uint8_t>(sa, ca, ha, n_cu, s);
-        if (dk == 128) return launch_a<128, uint8_t>(sa, ca, ha, n_cu, s);
+        if (dk == 32) return launch_a<32, uint8_t>(sa, ca, ha, n_cu, s, stream_keys);
+        if (dk == 64) return launch_a<64, uint8_t>(sa, ca, ha, n_cu, s, stream_keys);
+        if (dk == 128) return launch_a<128, uint8_t>(sa, ca, ha, n_cu, s, stream_keys);
     } else if (key_dtype == LSA_MXFP4) {
-        if (dk == 64) return launch_a<64, score_k::mxfp4_tag>(sa, ca, ha, n_cu, s);
-        if (dk == 128) return launch_a<128, score_k::mxfp4_tag>(sa, ca, ha, n_cu, s);
+        if (dk == 64) return launch_a<64, score_k::mxfp4_tag>(sa, ca, ha, n_cu, s, stream_keys);
+        if (dk == 128) return launch_a<128, score_k::mxfp4_tag>(sa, ca, ha, n_cu, s, stream_keys);
     } else if (key_dtype == LSA_MXINT8) {
-        if (dk == 32) return launch_a<32, score_k::mxint8_tag>(sa, ca, ha, n_cu, s);
-        if (dk == 64) return launch_a<64, score_k::mxint8_tag>(sa, ca, ha, n_cu, s);
-        if (dk == 128) return launch_a<128, score_k::mxint8_tag>(sa, ca, ha, n_cu, s);
+        if (dk == 32) return launch_a<32, score_k::mxint8_tag>(sa, ca, ha, n_cu, s, stream_keys);
+        if (dk == 64) return launch_a<64, score_k::mxint8_tag>(sa, ca, ha, n_cu, s, stream_keys);
+        if (dk == 128) return launch_a<128, score_k::mxint8_tag>(sa, ca, ha, n_cu, s, stream_keys);
     }
     return hipErrorInvalidValue;
 }

@@ -104,6 +104,8 @@ struct lsa_ctx {
     void* zero = nullptr;       // select histogram: zero between calls
     size_t zero_bytes = 0;
     bool timing = false;
+    // the step calls load the indexer keys non-temporally (lsa_ctx_set_key_policy)
+    bool stream_keys = false;
     struct Pending {
         int kind;
         hipEvent_t a, b;
@@ -392,6 +394,12 @@ lsa_status lsa_ctx_reserve(lsa_ctx* c, uint64_t bytes) {
 lsa_status lsa_ctx_set_timing(lsa_ctx* c, int32_t on) {
     if (!c) return fail(LSA_ERR_INVALID_ARG, "ctx is NULL");
     c->timing = on != 0;
+    return LSA_OK;
+}
+
+lsa_status lsa_ctx_set_key_policy(lsa_ctx* c, int32_t non_temporal) {
+    if (!c) return fail(LSA_ERR_INVALID_ARG, "ctx is NULL");
+    c->stream_keys = non_temporal != 0;
     return LSA_OK;
 }
 
@@ -1243,7 +1251,7 @@ lsa_status launch_predict(lsa_ctx* ctx, const StepPlan& P, const lsa_step_desc* 
                               ctx->sel_guess, P.se.nblk};
         {
             Timed t(ctx, LSA_K_SCORE, s);
-            HIPTRY(launch_fm_score_lists(P.sa, h, d->key_dtype, d->dk, ctx->n_cu, s));
+            HIPTRY(launch_fm_score_lists(P.sa, h, d->key_dtype, d->dk, ctx->n_cu, s, ctx->stream_keys));
             t.end();
         }
         SelectArgs se = P.se;
@@ -1257,7 +1265,7 @@ lsa_status launch_predict(lsa_ctx* ctx, const StepPlan& P, const lsa_step_desc* 
     } else {
         {
             Timed t(ctx, LSA_K_SCORE, s);
-            HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s, false));
+            HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s, ctx->stream_keys));
             t.end();
         }
         SelectArgs se = P.se;
@@ -1327,7 +1335,7 @@ lsa_status lsa_decode_step_noalloc(lsa_ctx* ctx, const lsa_step_desc* d, lsa_str
         hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, s, P.zero_clear, n);
         HIPTRY(hipGetLastError());
     }
-    HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s, false));
+    HIPTRY(launch_fm_score(P.sa, d->key_dtype, d->dk, ctx->n_cu, s, ctx->stream_keys));
     HIPTRY(launch_fm_select(P.se, s));
     for (int g = 0; g < P.n_groups; ++g) HIPTRY(launch_kv_stage(P.ga[g], s));
     for (int g = 0; g < P.n_groups; ++g) HIPTRY(launch_lsa_attend(P.aa[g], s));
@@ -1384,7 +1392,7 @@ lsa_status lsa_lookahead_step(lsa_ctx* ctx, const lsa_step_desc* d, lsa_stream_t
     {
         Timed t(ctx, LSA_K_SCORE, s);
         HIPTRY(launch_la_fetch_score(P.sa, ca, d->key_dtype, d->dk, ctx->n_cu, fuse_hist ? &P.se : nullptr,
-                                     ctx->sel_guess, &lists, s));
+                                     ctx->sel_guess, &lists, s, ctx->stream_keys));
         t.end();
     }
     {

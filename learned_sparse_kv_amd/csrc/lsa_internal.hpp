@@ -162,7 +162,7 @@ struct ScoreHistArgs {
 int score_lists_grid(const ScoreArgs& a, int n_cu);
 // fm_score with the select's candidate lists: fp32 and bf16 keys
 hipError_t launch_fm_score_lists(const ScoreArgs& a, const ScoreHistArgs& h, int key_dtype, int dk, int n_cu,
-                                 hipStream_t s);
+                                 hipStream_t s, bool stream_keys);
 
 struct SelectArgs {
     const float* scores;
@@ -319,7 +319,8 @@ struct CopyArgs {
 };
 // n_seg = 0: the rows were copied already (the launch only scores).
 hipError_t launch_la_fetch_score(const ScoreArgs& sa, const CopyArgs& ca, int key_dtype, int dk, int n_cu,
-                                 const SelectArgs* hist_for, const int32_t* guess, bool* lists, hipStream_t s);
+                                 const SelectArgs* hist_for, const int32_t* guess, bool* lists, hipStream_t s,
+                                 bool stream_keys);
 bool la_fused_hist(const ScoreArgs& sa, const SelectArgs& se, int n_cu);
 // select histogram (unless hist_done) and collect (unless se.pre) of step t+1,
 // then its final selection beside the attention splits of step t (short

@@ -72,7 +72,7 @@ class KVSwapDesc(ctypes.Structure):
                 ("phys", P), ("n_rows", P), ("scale", f32), ("out", P)]
 
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _SIGS = {
     "lsa_compressed_cap": (i64, [i64, i32]),
@@ -87,6 +87,7 @@ _SIGS = {
     "lsa_ctx_destroy": (None, [P]),
     "lsa_ctx_reserve": (i32, [P, u64]),
     "lsa_ctx_set_timing": (i32, [P, i32]),
+    "lsa_ctx_set_key_policy": (i32, [P, i32]),
     "lsa_ctx_timing_read": (i32, [P, P, P]),
     "lsa_project": (i32, [P, i32, i32, P, P, i32, i32, i32, i32, P, P, P]),
     "lsa_score": (i32, [P, i32, P, i32, i64, P, i32, P, P, i32, i32, i32, P, P]),
@@ -233,6 +234,9 @@ class Ctx:
 
     def set_timing(self, on: bool):
         _check(lib().lsa_ctx_set_timing(self.h, 1 if on else 0))
+
+    def set_key_policy(self, non_temporal: bool):
+        _check(lib().lsa_ctx_set_key_policy(self.h, 1 if non_temporal else 0))
 
     def timing_read(self) -> dict:
         ms = (f64 * 6)()

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(lsa.EXPORTS)
-    assert L.lsa_abi_version() == lsa.ABI_VERSION == 6
+    assert L.lsa_abi_version() == lsa.ABI_VERSION == 7
 
 
 def test_closed_forms_match_oracle():

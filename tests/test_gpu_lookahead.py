@@ -118,6 +118,40 @@ def test_lookahead_fp8_keys_give_the_f32_bits(dw1m):
     say("  fp8 lookahead ok")
 
 
+def test_key_policy_gives_the_same_bits(dw1m):
+    # the non-temporal key loads of the step calls (lsa_ctx_set_key_policy) change
+    # only how the keys pass the caches: scores, rows and outputs keep their bits
+    # in both schedules
+    dw = dw1m
+    runs = []
+    try:
+        for nt in (False, True):
+            dw.ctx.set_key_policy(nt)
+            res = []
+            dw.reset_pools()
+            dw.lookahead_prime(0)
+            for t in range(4):
+                cur = lsa.lookahead_buffer(dw.ctx)
+                dw.lookahead_step(t)
+                torch.cuda.synchronize()
+                phys, nr = dw.phys2[cur].cpu().numpy(), dw.n_rows2[cur].cpu().numpy()
+                rows = [phys[l, 0, :nr[l, 0]].copy() for l in range(phys.shape[0])]
+                res.append((rows, bits(dw.out.cpu().numpy()).copy(), bits(dw.scores.cpu().numpy()).copy()))
+            dw.reset_pools()
+            for t in range(4):
+                dw.step(t)
+                torch.cuda.synchronize()
+                res.append(([], bits(dw.out.cpu().numpy()).copy(), bits(dw.scores.cpu().numpy()).copy()))
+            runs.append(res)
+    finally:
+        dw.ctx.set_key_policy(False)
+    for i, (a, b) in enumerate(zip(*runs)):
+        assert all(np.array_equal(x, y) for x, y in zip(a[0], b[0])), f"call {i}: rows"
+        assert np.array_equal(a[1], b[1]), f"call {i}: output"
+        assert np.array_equal(a[2], b[2]), f"call {i}: scores"
+    say("  key policy: same bits in both schedules")
+
+
 def test_lookahead_small_workloads_match_oracle():
     # 512 slots for top-512 (the stage of t+1 runs after step t's attention) and the
     # single-workgroup select path; the tiny workload is fully resident
