@@ -118,11 +118,9 @@ def test_lookahead_fp8_keys_give_the_f32_bits(dw1m):
     say("  fp8 lookahead ok")
 
 
-def test_key_policy_gives_the_same_bits(dw1m):
-    # the non-temporal key loads of the step calls (lsa_ctx_set_key_policy) change
-    # only how the keys pass the caches: scores, rows and outputs keep their bits
-    # in both schedules
-    dw = dw1m
+def _key_policy_runs(dw, n=4):
+    """n lookahead steps, then n synchronous steps, with the default and with the
+    non-temporal key policy: (rows, output bits, score bits) per call."""
     runs = []
     try:
         for nt in (False, True):
@@ -130,15 +128,15 @@ def test_key_policy_gives_the_same_bits(dw1m):
             res = []
             dw.reset_pools()
             dw.lookahead_prime(0)
-            for t in range(4):
+            for t in range(n):
                 cur = lsa.lookahead_buffer(dw.ctx)
                 dw.lookahead_step(t)
                 torch.cuda.synchronize()
                 phys, nr = dw.phys2[cur].cpu().numpy(), dw.n_rows2[cur].cpu().numpy()
-                rows = [phys[l, 0, :nr[l, 0]].copy() for l in range(phys.shape[0])]
+                rows = [phys[l, b, :nr[l, b]].copy() for l in range(phys.shape[0]) for b in range(phys.shape[1])]
                 res.append((rows, bits(dw.out.cpu().numpy()).copy(), bits(dw.scores.cpu().numpy()).copy()))
             dw.reset_pools()
-            for t in range(4):
+            for t in range(n):
                 dw.step(t)
                 torch.cuda.synchronize()
                 res.append(([], bits(dw.out.cpu().numpy()).copy(), bits(dw.scores.cpu().numpy()).copy()))
@@ -146,10 +144,26 @@ def test_key_policy_gives_the_same_bits(dw1m):
     finally:
         dw.ctx.set_key_policy(False)
     for i, (a, b) in enumerate(zip(*runs)):
-        assert all(np.array_equal(x, y) for x, y in zip(a[0], b[0])), f"call {i}: rows"
+        assert len(a[0]) == len(b[0]) and all(np.array_equal(x, y) for x, y in zip(a[0], b[0])), f"call {i}: rows"
         assert np.array_equal(a[1], b[1]), f"call {i}: output"
         assert np.array_equal(a[2], b[2]), f"call {i}: scores"
-    say("  key policy: same bits in both schedules")
+
+
+def test_key_policy_gives_the_same_bits(dw1m):
+    # the non-temporal key loads of the step calls (lsa_ctx_set_key_policy) change
+    # only how the keys pass the caches: scores, rows and outputs keep their bits
+    # in both schedules (fp32 keys, one sequence, pinned-host cold pools)
+    _key_policy_runs(dw1m)
+    say("  key policy (swap_1m): same bits in both schedules")
+
+
+def test_key_policy_gives_the_same_bits_bf16_batched():
+    # bf16 keys and rows, four sequences, threshold mode, swapping HBM cold pools
+    wl = L.WORKLOADS["thresh_256k"].replace(gpu_chunks=1024)
+    dw = DeviceWorkload(wl)
+    dw.make_steps(6)
+    _key_policy_runs(dw)
+    say("  key policy (thresh_256k, 1024 slots): same bits in both schedules")
 
 
 def test_lookahead_small_workloads_match_oracle():
