@@ -125,6 +125,12 @@ def test_kvswap_argument_checks():
     assert L.lsa_kvswap_step(ctx, ctypes.byref(d), None) == 1   # no pools
 
 
+def test_context_setters_reject_null():
+    L = lsa.lib()
+    assert L.lsa_ctx_set_key_policy(None, 1) == 1
+    assert L.lsa_ctx_set_timing(None, 1) == 1
+
+
 def test_pool_rows_swap_auto_disable():
     # page 1 troubleshooting: 64 tokens at ratio 4 -> cap 16; gpu_chunks >= 16 keeps it resident
     assert lsa.Pool.rows_needed(64, 4, 128, 16) == 128 + 16
