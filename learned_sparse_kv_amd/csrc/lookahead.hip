@@ -140,9 +140,9 @@ __global__ __launch_bounds__(320, 1) void la_score_copy(const ScoreArgs sa, cons
 // Launch D: the attention splits of step t beside the final selection of step
 // t+1 (path 1: one 512-thread workgroup per segment).  Both wait long on few
 // dependent memory reads, so neither lengthens the other.  The selection
-// workgroups come first in the grid, so they are dispatched first: the
-// selection is the longer chain, and the splits' workgroups start over a few
-// microseconds.
+// workgroups come first in the grid, so they are dispatched first: the splits'
+// workgroups start over a few microseconds, and the selection's one long chain
+// of dependent phases should not wait behind them.
 constexpr int kFinMaxBlocks = 1024;   // collect blocks per segment (1M entries); more take the exact fallback
 
 template <int D, typename KT>
